@@ -1,0 +1,392 @@
+/*
+ * CPU oracle for the forward pass of one mixture-of-experts FFN layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow reference that the
+ * HIP path is checked against.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load it; the product path never does.
+ * It shares no code, header, table or helper with the HIP library.
+ *
+ * Everything is computed token by token in double precision from the exact
+ * stored input values (bfloat16 and float32 widen exactly to double).  No
+ * intermediate is rounded to a narrower type.  Loops are plain; the only
+ * parallelism is a static split of independent tokens over threads.
+ *
+ * Sources (pages as titled):
+ *  - "Expert Parallelism (MoE)", section "MoE Layer Structure": the router is a
+ *    Linear d -> N_experts giving per-token expert ids, the top-K experts are
+ *    activated, each expert is Linear(d->4d) -> GELU -> Linear(4d->d), and the
+ *    output is the routing-weighted sum over the selected experts.
+ *  - same page, section "Load Balancing: The Auxiliary Loss": L_aux, f_i, P_i
+ *    and the balancing weight alpha.
+ *  - same page, section "Top-K Routing and Capacity Factor": capacity and the
+ *    dropping of tokens that would push an expert over it, with their routing
+ *    weight zeroed.
+ *  - "Expert Parallelism (EP)", section "Key math / How it works": route,
+ *    dispatch to the expert's owner, expert GEMMs, combine back home.
+ *
+ * Readings where the pages leave a step open (each one is listed with its
+ * reasons in the design notes of the repository):
+ *  - routing probabilities are the softmax over all E logits; the routing
+ *    weight of a selected expert is that probability, not renormalised;
+ *  - top-k orders experts by logit, descending, ties to the lower expert id;
+ *  - f_i = (selections of expert i before any capacity cap) / T and
+ *    P_i = mean over tokens of the softmax probability of expert i;
+ *  - capacity C = floor(T * capacity_factor / E); an expert keeps the first C
+ *    (token, slot) selections in token-index order; the rest are dropped;
+ *  - GELU is the exact erf form;
+ *  - a shared expert, when present, runs on every token with weight 1.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_DT_F32 0
+#define ORACLE_DT_BF16 1
+
+/* Value i of an array stored as float32 or as bfloat16 bit patterns. */
+static double elem(const void *base, int dtype, int64_t i)
+{
+    if (dtype == ORACLE_DT_BF16) {
+        uint32_t bits = ((uint32_t)((const uint16_t *)base)[i]) << 16;
+        float f;
+        memcpy(&f, &bits, sizeof f);
+        return (double)f;
+    }
+    return (double)((const float *)base)[i];
+}
+
+/* ---------------------------------------------------------------------- */
+/* threads                                                                 */
+/* ---------------------------------------------------------------------- */
+
+typedef void (*range_fn)(void *ctx, int64_t begin, int64_t end);
+
+struct range_job {
+    range_fn fn;
+    void *ctx;
+    int64_t begin, end;
+};
+
+static void *run_range(void *p)
+{
+    struct range_job *j = (struct range_job *)p;
+    if (j->begin < j->end)
+        j->fn(j->ctx, j->begin, j->end);
+    return NULL;
+}
+
+/* Split [0, n) into nthreads contiguous pieces and run fn on each. */
+static void parallel_for(int64_t n, int nthreads, range_fn fn, void *ctx)
+{
+    if (nthreads < 1)
+        nthreads = 1;
+    if ((int64_t)nthreads > n)
+        nthreads = (int)(n > 0 ? n : 1);
+    if (nthreads == 1) {
+        fn(ctx, 0, n);
+        return;
+    }
+    pthread_t *th = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    struct range_job *jobs = (struct range_job *)calloc((size_t)nthreads, sizeof(struct range_job));
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i].fn = fn;
+        jobs[i].ctx = ctx;
+        jobs[i].begin = n * i / nthreads;
+        jobs[i].end = n * (i + 1) / nthreads;
+        pthread_create(&th[i], NULL, run_range, &jobs[i]);
+    }
+    for (int i = 0; i < nthreads; ++i)
+        pthread_join(th[i], NULL);
+    free(th);
+    free(jobs);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Router: logits, softmax, top-k, routing weights                         */
+/* ---------------------------------------------------------------------- */
+
+struct route_ctx {
+    const void *x;
+    int x_dtype;
+    const float *w_router, *b_router;
+    int d, E, k;
+    double *logits, *probs, *topk_w;
+    int32_t *topk_idx;
+};
+
+static void route_range(void *p, int64_t t0, int64_t t1)
+{
+    struct route_ctx *c = (struct route_ctx *)p;
+    const int d = c->d, E = c->E, k = c->k;
+    double *lg = (double *)malloc(sizeof(double) * (size_t)E);
+    char *taken = (char *)malloc((size_t)E);
+    for (int64_t t = t0; t < t1; ++t) {
+        /* Router Linear d -> E ("MoE Layer Structure"). */
+        for (int e = 0; e < E; ++e) {
+            double s = 0.0;
+            for (int i = 0; i < d; ++i)
+                s += elem(c->x, c->x_dtype, t * d + i) * (double)c->w_router[(int64_t)e * d + i];
+            if (c->b_router)
+                s += (double)c->b_router[e];
+            lg[e] = s;
+        }
+        /* Softmax over all E experts. */
+        double mx = lg[0];
+        for (int e = 1; e < E; ++e)
+            if (lg[e] > mx)
+                mx = lg[e];
+        double z = 0.0;
+        for (int e = 0; e < E; ++e)
+            z += exp(lg[e] - mx);
+        double *pr = c->probs + t * E;
+        for (int e = 0; e < E; ++e)
+            pr[e] = exp(lg[e] - mx) / z;
+        if (c->logits)
+            memcpy(c->logits + t * E, lg, sizeof(double) * (size_t)E);
+        /* Top-k: repeatedly take the largest remaining logit; scanning ids
+         * upward with a strict comparison keeps the lower id on a tie. */
+        memset(taken, 0, (size_t)E);
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            for (int e = 0; e < E; ++e) {
+                if (taken[e])
+                    continue;
+                if (best < 0 || lg[e] > lg[best])
+                    best = e;
+            }
+            taken[best] = 1;
+            c->topk_idx[t * k + j] = best;
+            c->topk_w[t * k + j] = pr[best];
+        }
+    }
+    free(lg);
+    free(taken);
+}
+
+/* Route T tokens.  x is [T, d] (float32 or bfloat16 bits per x_dtype),
+ * w_router [E, d] float32, b_router [E] float32 or NULL.  Outputs: logits
+ * [T, E] (may be NULL), probs [T, E], topk_idx [T, k], topk_w [T, k].
+ * Returns 0, or -1 on invalid sizes. */
+int oracle_route(const void *x, int x_dtype, const float *w_router, const float *b_router,
+                 int64_t T, int d, int E, int k, double *logits, double *probs,
+                 int32_t *topk_idx, double *topk_w, int nthreads)
+{
+    if (T < 0 || d < 1 || E < 1 || k < 1 || k > E)
+        return -1;
+    struct route_ctx c = {x, x_dtype, w_router, b_router, d, E, k, logits, probs, topk_w, topk_idx};
+    parallel_for(T, nthreads, route_range, &c);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Load statistics ("Load Balancing: The Auxiliary Loss")                   */
+/* ---------------------------------------------------------------------- */
+
+/* count[e]: selections of expert e over all (token, slot), before capacity.
+ * f[e] = count[e] / T.  P[e] = mean over tokens of probs[t, e].
+ * l_aux = alpha * sum_e f[e] * P[e]. */
+int oracle_load_stats(const int32_t *topk_idx, const double *probs, int64_t T, int E, int k,
+                      double alpha, int64_t *count, double *f, double *P, double *l_aux)
+{
+    if (T < 0 || E < 1 || k < 1)
+        return -1;
+    for (int e = 0; e < E; ++e) {
+        count[e] = 0;
+        P[e] = 0.0;
+    }
+    for (int64_t t = 0; t < T; ++t)
+        for (int j = 0; j < k; ++j) {
+            int e = topk_idx[t * k + j];
+            if (e >= 0 && e < E)
+                count[e] += 1;
+        }
+    for (int e = 0; e < E; ++e) {
+        double s = 0.0;
+        for (int64_t t = 0; t < T; ++t)
+            s += probs[t * E + e];
+        P[e] = T > 0 ? s / (double)T : 0.0;
+        f[e] = T > 0 ? (double)count[e] / (double)T : 0.0;
+    }
+    double acc = 0.0;
+    for (int e = 0; e < E; ++e)
+        acc += f[e] * P[e];
+    *l_aux = alpha * acc;
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Capacity, dropping and the expert-contiguous order                       */
+/* ---------------------------------------------------------------------- */
+
+/* Capacity C = floor(T * capacity_factor / E) ("Top-K Routing and Capacity
+ * Factor"); capacity_factor <= 0 means no cap (C is reported as -1).
+ *
+ * Walk the selections in token order (t ascending, then slot j).  A selection
+ * of an expert outside the local range [e0, e0 + E_loc) is remote (-2).  A
+ * local selection is kept while its expert has seen fewer than C selections,
+ * otherwise dropped (-1).  Kept selections are then laid out expert by expert
+ * (experts ascending, tokens ascending inside an expert): seg_offsets is the
+ * exclusive scan of kept_count, slot_row[t*k+j] the row of a kept selection,
+ * and row_src[row] = t*k+j. */
+int oracle_capacity(const int32_t *topk_idx, int64_t T, int E, int k, double capacity_factor,
+                    int e0, int E_loc, int64_t *capacity, int32_t *slot_row, int32_t *row_src,
+                    int32_t *seg_offsets, int32_t *kept_count, int64_t *n_dropped)
+{
+    if (T < 0 || E < 1 || k < 1 || e0 < 0 || E_loc < 1 || e0 + E_loc > E)
+        return -1;
+    int64_t C = -1;
+    if (capacity_factor > 0.0)
+        C = (int64_t)floor((double)T * capacity_factor / (double)E);
+    *capacity = C;
+
+    int64_t *seen = (int64_t *)calloc((size_t)E_loc, sizeof(int64_t));
+    int64_t *rank = (int64_t *)malloc(sizeof(int64_t) * (size_t)(T * k + 1));
+    int64_t dropped = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int j = 0; j < k; ++j) {
+            int64_t s = t * k + j;
+            int e = topk_idx[s];
+            if (e < e0 || e >= e0 + E_loc || e >= E) {
+                slot_row[s] = -2;
+                continue;
+            }
+            int le = e - e0;
+            if (C < 0 || seen[le] < C) {
+                rank[s] = seen[le];
+                slot_row[s] = 0; /* kept; row assigned below */
+            } else {
+                slot_row[s] = -1;
+                dropped += 1;
+            }
+            seen[le] += 1;
+        }
+    }
+    seg_offsets[0] = 0;
+    for (int le = 0; le < E_loc; ++le) {
+        int64_t kept = (C < 0 || seen[le] < C) ? seen[le] : C;
+        kept_count[le] = (int32_t)kept;
+        seg_offsets[le + 1] = seg_offsets[le] + (int32_t)kept;
+    }
+    for (int64_t s = 0; s < T * k; ++s) {
+        if (slot_row[s] < 0)
+            continue;
+        int le = topk_idx[s] - e0;
+        int32_t row = seg_offsets[le] + (int32_t)rank[s];
+        slot_row[s] = row;
+        row_src[row] = (int32_t)s;
+    }
+    *n_dropped = dropped;
+    free(seen);
+    free(rank);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Expert FFN and combine                                                   */
+/* ---------------------------------------------------------------------- */
+
+/* Exact GELU: u * Phi(u) = 0.5 * u * (1 + erf(u / sqrt(2))). */
+double oracle_gelu(double u)
+{
+    return 0.5 * u * (1.0 + erf(u / sqrt(2.0)));
+}
+
+/* One expert on one token: out += weight * (W2 . GELU(W1 . x + b1) + b2).
+ * W1 is [ffn, d], W2 is [d, ffn] (nn.Linear layout, out x in). */
+static void expert_apply(const double *xt, int d, int ffn, int dtype,
+                         const void *w1, const void *b1, const void *w2, const void *b2,
+                         double weight, double *g, double *out)
+{
+    for (int f = 0; f < ffn; ++f) {
+        double u = 0.0;
+        for (int i = 0; i < d; ++i)
+            u += elem(w1, dtype, (int64_t)f * d + i) * xt[i];
+        if (b1)
+            u += elem(b1, dtype, f);
+        g[f] = oracle_gelu(u);
+    }
+    for (int o = 0; o < d; ++o) {
+        double v = 0.0;
+        for (int f = 0; f < ffn; ++f)
+            v += elem(w2, dtype, (int64_t)o * ffn + f) * g[f];
+        if (b2)
+            v += elem(b2, dtype, o);
+        out[o] += weight * v;
+    }
+}
+
+struct combine_ctx {
+    const void *x;
+    int dtype;
+    int d, k, ffn, e0, E_loc;
+    const int64_t *tokens;
+    const int32_t *topk_idx, *slot_row;
+    const double *topk_w;
+    const void *w1, *b1, *w2, *b2, *ws1, *bs1, *ws2, *bs2;
+    double *y;
+};
+
+static void combine_range(void *p, int64_t i0, int64_t i1)
+{
+    struct combine_ctx *c = (struct combine_ctx *)p;
+    const int d = c->d, ffn = c->ffn, k = c->k;
+    double *xt = (double *)malloc(sizeof(double) * (size_t)d);
+    double *g = (double *)malloc(sizeof(double) * (size_t)ffn);
+    for (int64_t i = i0; i < i1; ++i) {
+        int64_t t = c->tokens[i];
+        double *yt = c->y + i * d;
+        for (int o = 0; o < d; ++o)
+            yt[o] = 0.0;
+        for (int q = 0; q < d; ++q)
+            xt[q] = elem(c->x, c->dtype, t * d + q);
+        /* Y = sum over kept selected experts of routing weight * expert output
+         * ("MoE Layer Structure"); a dropped selection contributes nothing
+         * ("Top-K Routing and Capacity Factor"). */
+        for (int j = 0; j < k; ++j) {
+            int64_t s = t * k + j;
+            if (c->slot_row[s] < 0)
+                continue;
+            int le = c->topk_idx[s] - c->e0;
+            int64_t w1o = (int64_t)le * ffn * d, b1o = (int64_t)le * ffn;
+            int64_t w2o = (int64_t)le * d * ffn, b2o = (int64_t)le * d;
+            size_t es = c->dtype == ORACLE_DT_BF16 ? 2 : 4;
+            expert_apply(xt, d, ffn, c->dtype,
+                         (const char *)c->w1 + w1o * es, c->b1 ? (const char *)c->b1 + b1o * es : NULL,
+                         (const char *)c->w2 + w2o * es, c->b2 ? (const char *)c->b2 + b2o * es : NULL,
+                         c->topk_w[s], g, yt);
+        }
+        /* Shared expert: every token, weight 1. */
+        if (c->ws1)
+            expert_apply(xt, d, ffn, c->dtype, c->ws1, c->bs1, c->ws2, c->bs2, 1.0, g, yt);
+    }
+    free(xt);
+    free(g);
+}
+
+/* Layer output for the tokens listed in tokens[0..n_tokens).  The selections
+ * kept are those with slot_row >= 0 (as produced by oracle_capacity); their
+ * expert is topk_idx (global id, local weights indexed by id - e0) and their
+ * weight topk_w.  Expert weights: w1 [E_loc, ffn, d], b1 [E_loc, ffn] or NULL,
+ * w2 [E_loc, d, ffn], b2 [E_loc, d] or NULL; shared expert ws1 [ffn, d],
+ * ws2 [d, ffn] (NULL when absent).  All in the same dtype as x.
+ * y is [n_tokens, d]. */
+int oracle_combine(const void *x, int dtype, int64_t T, int d, int k, int ffn,
+                   const int64_t *tokens, int64_t n_tokens,
+                   const int32_t *topk_idx, const double *topk_w, const int32_t *slot_row,
+                   int e0, int E_loc,
+                   const void *w1, const void *b1, const void *w2, const void *b2,
+                   const void *ws1, const void *bs1, const void *ws2, const void *bs2,
+                   double *y, int nthreads)
+{
+    if (T < 0 || d < 1 || k < 1 || ffn < 1 || n_tokens < 0)
+        return -1;
+    for (int64_t i = 0; i < n_tokens; ++i)
+        if (tokens[i] < 0 || tokens[i] >= T)
+            return -1;
+    struct combine_ctx c = {x, dtype, d, k, ffn, e0, E_loc, tokens, topk_idx, slot_row, topk_w,
+                            w1, b1, w2, b2, ws1, bs1, ws2, bs2, y};
+    parallel_for(n_tokens, nthreads, combine_range, &c);
+    return 0;
+}

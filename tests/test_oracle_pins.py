@@ -1,0 +1,378 @@
+"""Pins of the CPU oracle to what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: brute force
+on tiny inputs, closed forms, invariants stated on the pages, special cases
+that reduce to a library routine, and the pages' worked example.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from top_routing_expert_route_amd import workloads as wl
+from top_routing_expert_route_amd import accounting
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand(shape, seed, scale=1.0):
+    g = np.random.default_rng(seed)
+    return (g.standard_normal(shape) * scale).astype(np.float32)
+
+
+def _brute_topk(logits_row, k):
+    """Among all ordered k-tuples of distinct experts whose logits are
+    non-increasing and >= every unselected logit, the first by key
+    (-l0, id0, -l1, id1, ...)."""
+    E = len(logits_row)
+    best = None
+    for tup in itertools.permutations(range(E), k):
+        sel = [logits_row[i] for i in tup]
+        if any(sel[a] < sel[a + 1] for a in range(k - 1)):
+            continue
+        rest = [logits_row[i] for i in range(E) if i not in tup]
+        if rest and min(sel) < max(rest):
+            continue
+        key = tuple(v for i in tup for v in (-logits_row[i], i))
+        if best is None or key < best[0]:
+            best = (key, tup)
+    return list(best[1])
+
+
+# ---------------------------------------------------------------- route ----
+
+@pytest.mark.parametrize("E,k", [(3, 1), (4, 2), (5, 3), (7, 2), (6, 1)])
+def test_topk_matches_brute_force(E, k):
+    T, d = 40, 6
+    x = _rand((T, d), 10 + E)
+    w = _rand((E, d), 20 + k, 1 / math.sqrt(d))
+    r = oracle.route(x, w, None, k, threads=2)
+    for t in range(T):
+        assert list(r.topk_idx[t]) == _brute_topk(list(r.logits[t]), k)
+    # library cross-check: stable argsort of -logits
+    ref = np.argsort(-r.logits, axis=1, kind="stable")[:, :k]
+    np.testing.assert_array_equal(r.topk_idx, ref)
+
+
+def test_topk_exact_ties_go_to_lower_id():
+    # integer-valued inputs make several logits exactly equal
+    E, k, d, T = 6, 3, 4, 30
+    g = np.random.default_rng(3)
+    x = g.integers(-2, 3, size=(T, d)).astype(np.float32)
+    w = g.integers(-1, 2, size=(E, d)).astype(np.float32)
+    r = oracle.route(x, w, None, k, threads=1)
+    n_ties = 0
+    for t in range(T):
+        l = list(r.logits[t])
+        n_ties += len(l) - len(set(l))
+        assert list(r.topk_idx[t]) == _brute_topk(l, k)
+    assert n_ties > 0
+
+
+def test_uniform_router_closed_form():
+    """W_r = 0, b_r = 0: every logit is 0, so idx = [0..k-1], p = 1/E,
+    f_e = 1 for e < k, P_e = 1/E and L_aux = alpha * k / E."""
+    T, d, E, k, alpha = 17, 8, 8, 2, 0.01
+    x = _rand((T, d), 1)
+    r = oracle.route(x, np.zeros((E, d), np.float32), None, k)
+    assert (r.topk_idx == np.arange(k)[None, :]).all()
+    np.testing.assert_allclose(r.probs, 1.0 / E, rtol=0, atol=1e-15)
+    st = oracle.load_stats(r.topk_idx, r.probs, alpha)
+    np.testing.assert_array_equal(st.f, [1.0] * k + [0.0] * (E - k))
+    np.testing.assert_allclose(st.P, 1.0 / E, atol=1e-15)
+    assert abs(st.l_aux - alpha * k / E) < 1e-15
+
+
+def test_softmax_normalised_and_matches_torch():
+    T, d, E = 50, 16, 12
+    x = _rand((T, d), 5)
+    w = _rand((E, d), 6, 1 / 4)
+    b = _rand((E,), 7)
+    r = oracle.route(x, w, b, 3)
+    np.testing.assert_allclose(r.probs.sum(1), 1.0, atol=1e-12)
+    ref_logits = torch.from_numpy(x).double() @ torch.from_numpy(w).double().T + torch.from_numpy(b).double()
+    np.testing.assert_allclose(r.logits, ref_logits.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(r.probs, torch.softmax(ref_logits, dim=1).numpy(), rtol=1e-12, atol=1e-15)
+    # routing weight = full-softmax probability of the selected expert
+    np.testing.assert_array_equal(r.topk_w, np.take_along_axis(r.probs, r.topk_idx.astype(np.int64), 1))
+
+
+def test_bf16_inputs_widen_exactly():
+    T, d, E = 9, 32, 5
+    xf = _rand((T, d), 8)
+    xb = wl.f32_to_bf16_bits(xf)
+    w = _rand((E, d), 9, 0.2)
+    r1 = oracle.route(xb, w, None, 2)
+    r2 = oracle.route(wl.bf16_bits_to_f32(xb), w, None, 2)
+    np.testing.assert_array_equal(r1.logits, r2.logits)
+
+
+# ---------------------------------------------------------------- stats ----
+
+def test_stats_invariants():
+    T, d, E, k = 300, 24, 10, 3
+    x = _rand((T, d), 11)
+    w = _rand((E, d), 12, 1 / math.sqrt(d))
+    r = oracle.route(x, w, None, k)
+    st = oracle.load_stats(r.topk_idx, r.probs, 0.01)
+    assert st.count.sum() == T * k          # sum f = k exactly
+    assert abs(st.f.sum() - k) < 1e-12
+    assert abs(st.P.sum() - 1.0) < 1e-12    # sum P = 1
+    np.testing.assert_array_equal(st.f, st.count / T)
+
+
+def test_stats_unpicked_expert_contributes_zero():
+    # bias pushes expert 3 far down: nobody picks it, so f_3 = 0 and its
+    # f*P term is zero ("Load Balancing: The Auxiliary Loss").
+    T, d, E, k = 64, 8, 6, 2
+    x = _rand((T, d), 13)
+    w = _rand((E, d), 14, 0.1)
+    b = np.zeros(E, np.float32)
+    b[3] = -50.0
+    r = oracle.route(x, w, b, k)
+    st = oracle.load_stats(r.topk_idx, r.probs, 0.01)
+    assert st.count[3] == 0 and st.f[3] == 0.0 and st.P[3] > 0.0
+    st2 = oracle.load_stats(r.topk_idx, r.probs.copy(), 0.01)
+    terms = st2.f * st2.P
+    assert terms[3] == 0.0
+
+
+def test_uniform_routing_laux_near_alpha_k_over_E():
+    w = wl.scaled(wl.get(1), T=4096, d=256, ffn=8)
+    inp = wl.make_layer(w, seed=0, with_experts=False)
+    r = oracle.route(inp.x, inp.w_router, None, w.k)
+    st = oracle.load_stats(r.topk_idx, r.probs, 0.01)
+    assert abs(st.l_aux - 0.01 * w.k / w.E) / (0.01 * w.k / w.E) < 0.02
+
+
+# ------------------------------------------------------------- capacity ----
+
+def test_capacity_formula_golden():
+    g = _golden("pages_capacity.json")
+    for c in g["cases"]:
+        T, E = c["T"], c["E"]
+        idx = np.zeros((T, 1), np.int32)
+        dp = oracle.capacity(idx, E, c["capacity_factor"])
+        assert dp.capacity == c["capacity"]
+
+
+def _per_expert_brute(idx, E, C, e0, E_loc):
+    """Independent drop rule: for each local expert, sort the token ids that
+    selected it and keep the first C."""
+    T, k = idx.shape
+    kept = set()
+    for e in range(e0, e0 + E_loc):
+        toks = sorted(int(t) for t in range(T) for j in range(k) if idx[t, j] == e)
+        keep = toks if C < 0 else toks[:C]
+        kept.update((t, e) for t in keep)
+    return kept
+
+
+@pytest.mark.parametrize("cf,e0,E_loc", [(1.25, 0, 0), (0.5, 0, 0), (1.0, 2, 3), (0.0, 1, 4)])
+def test_capacity_drops_and_permutation(cf, e0, E_loc):
+    T, d, E, k = 200, 8, 8, 2
+    x = _rand((T, d), 15)
+    w = _rand((E, d), 16, 0.5)
+    b = np.array([2.0, 1.0, 0.5, 0, 0, 0, -1, -2], np.float32)  # skewed load
+    r = oracle.route(x, w, b, k)
+    dp = oracle.capacity(r.topk_idx, E, cf, e0, E_loc)
+    El = E_loc or E
+    C = dp.capacity
+    if cf > 0:
+        assert C == math.floor(T * cf / E)
+    cnt = np.bincount(r.topk_idx.ravel(), minlength=E)[e0:e0 + El]
+    exp_kept = cnt if C < 0 else np.minimum(cnt, C)
+    np.testing.assert_array_equal(dp.kept_count, exp_kept)
+    np.testing.assert_array_equal(dp.seg_offsets, np.concatenate([[0], np.cumsum(exp_kept)]))
+    remote = int(((r.topk_idx < e0) | (r.topk_idx >= e0 + El)).sum())
+    assert dp.kept_count.sum() + dp.n_dropped + remote == T * k
+    assert (dp.slot_row == -2).sum() == remote
+    assert (dp.slot_row == -1).sum() == dp.n_dropped
+    # the kept selections are exactly the C lowest token ids of each expert
+    got = {(t, int(r.topk_idx[t, j])) for t in range(T) for j in range(k) if dp.slot_row[t, j] >= 0}
+    assert got == _per_expert_brute(r.topk_idx, E, C, e0, El)
+    # the row order is a stable sort of the token-major kept list by expert
+    flat = np.flatnonzero(dp.slot_row.ravel() >= 0)
+    order = flat[np.argsort(r.topk_idx.ravel()[flat], kind="stable")]
+    np.testing.assert_array_equal(dp.row_src, order)
+    np.testing.assert_array_equal(dp.slot_row.ravel()[dp.row_src], np.arange(len(dp.row_src)))
+
+
+def test_large_capacity_equals_uncapped():
+    T, d, E, k = 150, 8, 6, 2
+    x = _rand((T, d), 17)
+    w = _rand((E, d), 18, 0.5)
+    r = oracle.route(x, w, None, k)
+    a = oracle.capacity(r.topk_idx, E, float(E))   # cf >= E  =>  C >= T
+    b = oracle.capacity(r.topk_idx, E, 0.0)
+    assert a.n_dropped == 0
+    np.testing.assert_array_equal(a.slot_row, b.slot_row)
+    np.testing.assert_array_equal(a.row_src, b.row_src)
+
+
+def test_pages_dispatch_example():
+    g = _golden("pages_dispatch_example.json")
+    idx = np.array(g["topk_idx"], np.int32)
+    dp = oracle.capacity(idx, g["E"])
+    np.testing.assert_array_equal(dp.row_src, g["expected_row_src"])
+    np.testing.assert_array_equal(dp.kept_count, g["expected_kept_count"])
+    np.testing.assert_array_equal(dp.seg_offsets, g["expected_seg_offsets"])
+    np.testing.assert_array_equal(dp.slot_row, g["expected_slot_row"])
+
+
+# ------------------------------------------------------------ FFN / Y ------
+
+def _dense_ffn_torch(x, w1, b1, w2, b2):
+    X = torch.from_numpy(x).double()
+    h = torch.nn.functional.linear(X, torch.from_numpy(w1).double(),
+                                   None if b1 is None else torch.from_numpy(b1).double())
+    h = torch.nn.functional.gelu(h, approximate="none")
+    return torch.nn.functional.linear(h, torch.from_numpy(w2).double(),
+                                      None if b2 is None else torch.from_numpy(b2).double()).numpy()
+
+
+def _layer(T, d, E, k, ffn, seed, bias=True):
+    x = _rand((T, d), seed)
+    wr = _rand((E, d), seed + 1, 1 / math.sqrt(d))
+    w1 = _rand((E, ffn, d), seed + 2, 1 / math.sqrt(d))
+    w2 = _rand((E, d, ffn), seed + 3, 1 / math.sqrt(ffn))
+    b1 = _rand((E, ffn), seed + 4, 0.1) if bias else None
+    b2 = _rand((E, d), seed + 5, 0.1) if bias else None
+    return x, wr, w1, b1, w2, b2
+
+
+def _oracle_y(x, wr, br, w1, b1, w2, b2, k, cf=0.0, e0=0, E_loc=0, shared=(None, None, None, None)):
+    T = x.shape[0]
+    E = wr.shape[0]
+    r = oracle.route(x, wr, br, k)
+    dp = oracle.capacity(r.topk_idx, E, cf, e0, E_loc)
+    El = E_loc or E
+    y = oracle.combine(x, np.arange(T), r.topk_idx, r.topk_w, dp.slot_row,
+                       np.ascontiguousarray(w1[e0:e0 + El]), None if b1 is None else np.ascontiguousarray(b1[e0:e0 + El]),
+                       np.ascontiguousarray(w2[e0:e0 + El]), None if b2 is None else np.ascontiguousarray(b2[e0:e0 + El]),
+                       e0, *shared)
+    return r, dp, y
+
+
+def test_single_expert_reduces_to_dense_ffn():
+    """E = 1, k = 1: p = 1 and Y is the dense FFN X -> Linear -> GELU ->
+    Linear ("MoE Layer Structure")."""
+    T, d, ffn = 20, 16, 64
+    x, wr, w1, b1, w2, b2 = _layer(T, d, 1, 1, ffn, 30)
+    r, dp, y = _oracle_y(x, wr, None, w1, b1, w2, b2, 1)
+    assert (r.topk_w == 1.0).all()
+    np.testing.assert_allclose(y, _dense_ffn_torch(x, w1[0], b1[0], w2[0], b2[0]), rtol=1e-12, atol=1e-12)
+
+
+def test_gelu_exact_form():
+    for u in [0.0, 0.3, -0.3, 1.0, -2.5, 2.70, 5.0, -7.0]:
+        g = oracle.gelu(u)
+        assert abs(g - oracle.gelu(-u) - u) < 1e-15
+        ref = torch.nn.functional.gelu(torch.tensor([u], dtype=torch.float64), approximate="none").item()
+        assert abs(g - ref) < 1e-15
+    assert oracle.gelu(0.0) == 0.0
+
+
+def test_identical_experts_all_selected_give_the_dense_ffn():
+    """k = E with identical experts and no cap: Y = FFN(x) * sum_e p_e = FFN(x)."""
+    T, d, E, ffn = 25, 12, 4, 32
+    x, wr, w1, b1, w2, b2 = _layer(T, d, 1, 1, ffn, 40)
+    W1 = np.ascontiguousarray(np.repeat(w1, E, 0))
+    B1 = np.ascontiguousarray(np.repeat(b1, E, 0))
+    W2 = np.ascontiguousarray(np.repeat(w2, E, 0))
+    B2 = np.ascontiguousarray(np.repeat(b2, E, 0))
+    wr = _rand((E, d), 41, 0.3)
+    _, _, y = _oracle_y(x, wr, None, W1, B1, W2, B2, E)
+    np.testing.assert_allclose(y, _dense_ffn_torch(x, w1[0], b1[0], w2[0], b2[0]), rtol=1e-12, atol=1e-12)
+
+
+def test_y_is_weighted_sum_of_selected_experts():
+    """Y_t = sum_j w_tj * FFN_{idx_tj}(x_t), each expert checked with torch."""
+    T, d, E, k, ffn = 12, 8, 5, 2, 24
+    x, wr, w1, b1, w2, b2 = _layer(T, d, E, k, ffn, 50)
+    r, dp, y = _oracle_y(x, wr, None, w1, b1, w2, b2, k)
+    ref = np.zeros((T, d))
+    for e in range(E):
+        ye = _dense_ffn_torch(x, w1[e], b1[e], w2[e], b2[e])
+        for t in range(T):
+            for j in range(k):
+                if r.topk_idx[t, j] == e:
+                    ref[t] += r.topk_w[t, j] * ye[t]
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_scaling_w2_b2_scales_y():
+    T, d, E, k, ffn = 16, 8, 4, 2, 16
+    x, wr, w1, b1, w2, b2 = _layer(T, d, E, k, ffn, 60)
+    _, _, y1 = _oracle_y(x, wr, None, w1, b1, w2, b2, k)
+    c = np.float32(4.0)   # a power of two keeps the float32 weights exact
+    _, _, y4 = _oracle_y(x, wr, None, w1, b1, w2 * c, b2 * c, k)
+    np.testing.assert_allclose(y4, 4.0 * y1, rtol=1e-12, atol=1e-13)
+
+
+def test_token_permutation_permutes_y():
+    T, d, E, k, ffn = 30, 8, 6, 2, 16
+    x, wr, w1, b1, w2, b2 = _layer(T, d, E, k, ffn, 70)
+    _, _, y = _oracle_y(x, wr, None, w1, b1, w2, b2, k)
+    perm = np.random.default_rng(1).permutation(T)
+    _, _, yp = _oracle_y(np.ascontiguousarray(x[perm]), wr, None, w1, b1, w2, b2, k)
+    np.testing.assert_allclose(yp, y[perm], rtol=1e-12, atol=1e-13)
+
+
+def test_expert_shares_sum_to_whole_layer():
+    """Splitting the experts into disjoint local shares and summing the
+    partial outputs gives the whole layer (the combine of the expert-parallel
+    plan in the HF page's "DistributedConfig" section, with no cap)."""
+    T, d, E, k, ffn = 40, 8, 8, 2, 16
+    x, wr, w1, b1, w2, b2 = _layer(T, d, E, k, ffn, 80)
+    _, _, y_all = _oracle_y(x, wr, None, w1, b1, w2, b2, k)
+    parts = [_oracle_y(x, wr, None, w1, b1, w2, b2, k, 0.0, e0, 2)[2] for e0 in range(0, E, 2)]
+    np.testing.assert_allclose(sum(parts), y_all, rtol=1e-12, atol=1e-13)
+
+
+def test_fully_dropped_token_gives_zero_and_shared_adds():
+    T, d, E, k, ffn = 64, 8, 4, 2, 16
+    x, wr, w1, b1, w2, b2 = _layer(T, d, E, k, ffn, 90)
+    br = np.array([5.0, 4.0, -5.0, -5.0], np.float32)   # everyone picks 0 and 1
+    r, dp, y = _oracle_y(x, wr, br, w1, b1, w2, b2, k, cf=0.25)  # C = 4
+    assert dp.capacity == 4
+    full = np.all(dp.slot_row < 0, axis=1)
+    assert full.sum() > 0
+    assert np.all(y[full] == 0.0)
+    sw1, sb1, sw2, sb2 = w1[3], b1[3], w2[3], b2[3]
+    _, _, ys = _oracle_y(x, wr, br, w1, b1, w2, b2, k, cf=0.25, shared=(sw1, sb1, sw2, sb2))
+    np.testing.assert_allclose(ys - y, _dense_ffn_torch(x, sw1, sb1, sw2, sb2), rtol=1e-11, atol=1e-12)
+
+
+# ------------------------------------------------------ FLOP accounting ----
+
+def test_active_fraction_golden():
+    for c in _golden("pages_active_fraction.json")["cases"]:
+        assert accounting.active_param_fraction(c["E"], c["k"]) == c["fraction"]
+    # per-token expert flops scale with k, not with E
+    assert accounting.expert_flops_per_token(4096, 16384, 2) * 4 == accounting.expert_flops_per_token(4096, 16384, 8)
+
+
+def test_workload_generation_is_seeded():
+    w = wl.scaled(wl.get(1), T=64, d=128, ffn=256)
+    a = wl.make_layer(w, seed=3)
+    b = wl.make_layer(w, seed=3, threads=1)
+    c = wl.make_layer(w, seed=4)
+    np.testing.assert_array_equal(a.x, b.x)
+    np.testing.assert_array_equal(a.w1, b.w1)
+    assert not np.array_equal(a.x, c.x)
+    assert a.x.dtype == np.uint16 and a.w_router.dtype == np.float32
+    # bf16 round-to-nearest-even of the float32 draws
+    v = np.array([1.0, 1.00390625, 1.005859375, -2.00390625], np.float32)
+    np.testing.assert_array_equal(wl.bf16_bits_to_f32(wl.f32_to_bf16_bits(v)),
+                                  np.array([1.0, 1.0, 1.0078125, -2.0], np.float32))
