@@ -224,7 +224,8 @@ def forward(inp, tokens: Optional[np.ndarray] = None, threads: Optional[int] = N
     idx = r.topk_idx if topk_idx is None else np.ascontiguousarray(topk_idx, dtype=np.int32)
     wts = np.take_along_axis(r.probs, idx.astype(np.int64).clip(0, w.E - 1), axis=1)
     st = load_stats(idx, r.probs, w.alpha)
-    dp = capacity(idx, w.E, w.capacity_factor, w.expert_begin, w.num_local_experts)
+    # the capacity factor is a float32 parameter of the layer
+    dp = capacity(idx, w.E, float(np.float32(w.capacity_factor)), w.expert_begin, w.num_local_experts)
     if tokens is None:
         tokens = np.arange(w.T, dtype=np.int64)
     y = combine(inp.x, tokens, idx, wts, dp.slot_row, inp.w1, inp.b1, inp.w2, inp.b2,

@@ -1,0 +1,360 @@
+"""GPU parity: every step of the HIP path against the fp64 oracle, called
+through the C ABI, on seeded workloads shaped like the pages' layers.
+
+Small cases span several tiles and ragged tails and are compared on every
+element; the full-size workloads (in the launch configuration the benchmark
+times) compare all integers on every token and Y on a seeded token sample.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity import (TOL_ROUTER, TOL_Y_BF16, TOL_Y_F32, check_topk, expected_xperm, near_ties, rel_err)
+from top_routing_expert_route_amd import api
+from top_routing_expert_route_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+SMALL = {
+    "tiny-fp32": wl.get(0),
+    "mixtral-small": wl.scaled(wl.get(1), name="mixtral-small", T=333, d=256, ffn=384),
+    "drop-small": wl.scaled(wl.get(2), name="drop-small", T=1000, d=192, ffn=256),
+    "fine-small": wl.scaled(wl.get(3), name="fine-small", T=700, d=128, ffn=96),
+    "dsv3-small": wl.scaled(wl.get(4), name="dsv3-small", T=500, d=136, ffn=264, expert_begin=32,
+                            expert_bias="gauss"),
+    "bias-f32": wl.scaled(wl.get(0), name="bias-f32", T=301, d=72, ffn=136, router_bias="gauss",
+                          expert_bias="gauss", capacity_factor=1.1),
+}
+
+FULL = {w.name: w for w in wl.WORKLOADS[1:]}
+FULL_SAMPLE = {"mixtral8x7b-layer": 192, "capacity-drop-zipf": 384, "fine-grained-e128-k8": 256,
+               "deepseekv3-share-32of256": 128}
+
+_cache = {}
+
+
+def _inputs(w, seed=0):
+    key = (w, seed)
+    if key not in _cache:
+        if len(_cache) > 2:
+            _cache.clear()
+        inp = wl.make_layer(w, seed=seed)
+        _cache[key] = (inp, wl.device_layer(inp, DEV))
+    return _cache[key]
+
+
+def _torch_dtype(w):
+    return torch.bfloat16 if w.dtype == wl.BF16 else torch.float32
+
+
+def _ytol(w):
+    return TOL_Y_BF16 if w.dtype == wl.BF16 else TOL_Y_F32
+
+
+def _host(t):
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy()
+    return t.cpu().numpy()
+
+
+def _x_f64(inp):
+    return wl.bf16_bits_to_f32(inp.x) if inp.x.dtype == np.uint16 else inp.x
+
+
+def _run_stages(w, inp, t):
+    """Route, dispatch, expert FFN and combine called one by one."""
+    r = api.moe_route(t["x"], t["w_router"], t["b_router"], w.k, w.alpha)
+    dp = api.moe_dispatch(t["x"], r["topk_idx"], w.E, w.capacity_factor, w.expert_begin, w.num_local_experts)
+    h, y_perm = api.moe_expert_ffn(dp["x_perm"], dp["seg_offsets"], t["w1"], t["b1"], t["w2"], t["b2"])
+    y_sh = None
+    if w.shared_expert:
+        hs = api.moe_grouped_gemm(t["x"], None, t["ws1"].unsqueeze(0), None if t["bs1"] is None else t["bs1"].unsqueeze(0), 1)
+        y_sh = api.moe_grouped_gemm(hs, None, t["ws2"].unsqueeze(0), None if t["bs2"] is None else t["bs2"].unsqueeze(0), 0)
+    y = api.moe_combine(y_perm, dp["slot_row"], r["topk_w"], y_sh)
+    torch.cuda.synchronize()
+    return r, dp, y_perm, y_sh, y
+
+
+def _check_route(w, inp, r, ref_route):
+    gidx = r["topk_idx"].cpu().numpy()
+    nt = check_topk(gidx, ref_route.logits, ref_route.topk_idx, w.k)
+    # routing weight = oracle probability at the GPU's selection
+    ref_w = np.take_along_axis(ref_route.probs, gidx.astype(np.int64), 1)
+    assert rel_err(r["topk_w"].cpu().numpy(), ref_w) <= TOL_ROUTER
+    st = oracle.load_stats(gidx, ref_route.probs, w.alpha)
+    cnt = r["expert_count"].cpu().numpy()
+    np.testing.assert_array_equal(cnt, st.count)
+    np.testing.assert_array_equal(r["f"].cpu().numpy(), np.float32(cnt) / np.float32(w.T))
+    assert rel_err(r["P"].cpu().numpy(), st.P) <= TOL_ROUTER
+    assert rel_err(r["l_aux"].cpu().numpy(), [st.l_aux]) <= TOL_ROUTER
+    own = oracle.load_stats(ref_route.topk_idx, ref_route.probs, w.alpha)
+    assert np.abs(own.count - st.count).sum() <= 2 * nt["boundary"]
+    return gidx, nt
+
+
+def _check_dispatch(w, inp, gidx, dp):
+    ref = oracle.capacity(gidx, w.E, np.float32(w.capacity_factor), w.expert_begin, w.num_local_experts)
+    np.testing.assert_array_equal(dp["seg_offsets"].cpu().numpy(), ref.seg_offsets)
+    np.testing.assert_array_equal(dp["kept_count"].cpu().numpy(), ref.kept_count)
+    np.testing.assert_array_equal(dp["slot_row"].cpu().numpy(), ref.slot_row)
+    rows = int(ref.seg_offsets[-1])
+    np.testing.assert_array_equal(dp["row_src"].cpu().numpy()[:rows], ref.row_src)
+    assert int(dp["n_dropped"].item()) == ref.n_dropped
+    xp = dp["x_perm"][:rows]
+    if xp.dtype == torch.bfloat16:
+        got = xp.view(torch.int16).cpu().numpy().view(np.uint16)
+    else:
+        got = xp.cpu().numpy()
+    np.testing.assert_array_equal(got, expected_xperm(inp.x, ref.row_src, w.k))
+    return ref
+
+
+def _oracle_rows(w, inp, gidx, row_src, rows_sel):
+    """Expert output (no routing weight) of each selected dispatched row."""
+    k = w.k
+    out = np.zeros((len(rows_sel), w.d))
+    toks = row_src[rows_sel] // k
+    slots = row_src[rows_sel] % k
+    for j in range(k):
+        sel = np.flatnonzero(slots == j)
+        if sel.size == 0:
+            continue
+        tj = toks[sel]
+        sr = np.full((w.T, k), -1, np.int32)
+        sr[tj, j] = 0
+        wts = np.ones((w.T, k))
+        y = oracle.combine(inp.x, tj, gidx, wts, sr, inp.w1, inp.b1, inp.w2, inp.b2, w.expert_begin)
+        out[sel] = y
+    return out
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_stages_small(name):
+    w = SMALL[name]
+    inp, t = _inputs(w)
+    r, dp, y_perm, y_sh, y = _run_stages(w, inp, t)
+    ref_route = oracle.route(inp.x, inp.w_router, inp.b_router, w.k)
+    gidx, nt = _check_route(w, inp, r, ref_route)
+    ref_dp = _check_dispatch(w, inp, gidx, dp)
+    rows = int(ref_dp.seg_offsets[-1])
+    if rows:
+        ref_rows = _oracle_rows(w, inp, gidx, ref_dp.row_src, np.arange(rows))
+        assert rel_err(_host(y_perm[:rows]), ref_rows) <= _ytol(w)
+    # combine on the GPU's own expert outputs, reference in float64
+    yp = _host(y_perm).astype(np.float64)
+    sr = dp["slot_row"].cpu().numpy()
+    tw = r["topk_w"].cpu().numpy().astype(np.float64)
+    yc = np.zeros((w.T, w.d))
+    for j in range(w.k):
+        ok = sr[:, j] >= 0
+        yc[ok] += tw[ok, j:j + 1] * yp[sr[ok, j]]
+    if y_sh is not None:
+        yc += _host(y_sh)
+    assert rel_err(_host(y), yc) <= (1e-2 if w.dtype == wl.BF16 else 1e-6)
+    # whole layer against the oracle, conditioned on the GPU's selection
+    ref = oracle.forward(inp, topk_idx=gidx)
+    assert rel_err(_host(y), ref.y) <= _ytol(w)
+
+
+def _layer(w, t, **kw):
+    return api.Layer(w.T, w.d, w.E, w.k, w.ffn, _torch_dtype(w), w.capacity_factor, w.expert_begin,
+                     w.num_local_experts, w.alpha, t["w_router"], t["b_router"], t["w1"], t["b1"], t["w2"],
+                     t["b2"], t["ws1"], t["bs1"], t["ws2"], t["bs2"], device=DEV, **kw)
+
+
+def _check_forward(w, inp, t, tokens=None):
+    layer = _layer(w, t)
+    outs = layer.alloc_outputs()
+    y = layer.forward(t["x"])
+    torch.cuda.synchronize()
+    ref_route = oracle.route(inp.x, inp.w_router, inp.b_router, w.k)
+    gidx, nt = _check_route(w, inp, outs, ref_route)
+    ref_dp = oracle.capacity(gidx, w.E, np.float32(w.capacity_factor), w.expert_begin, w.num_local_experts)
+    np.testing.assert_array_equal(outs["slot_row"].cpu().numpy(), ref_dp.slot_row)
+    np.testing.assert_array_equal(outs["seg_offsets"].cpu().numpy(), ref_dp.seg_offsets)
+    rows = int(ref_dp.seg_offsets[-1])
+    np.testing.assert_array_equal(outs["row_src"].cpu().numpy()[:rows], ref_dp.row_src)
+    assert int(outs["n_dropped"].item()) == ref_dp.n_dropped
+    if tokens is not None:
+        b, o = near_ties(ref_route.logits, w.k)
+        ties = np.flatnonzero(b | o)[:32]
+        tokens = wl.token_sample(w.T, tokens, must_include=ties)
+    ref = oracle.forward(inp, tokens=tokens, topk_idx=gidx)
+    yh = _host(y)
+    yg = yh if tokens is None else yh[tokens]
+    err = rel_err(yg, ref.y)
+    assert err <= _ytol(w), err
+    return layer, y, outs, nt, err
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_small(name):
+    w = SMALL[name]
+    inp, t = _inputs(w)
+    _check_forward(w, inp, t)
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_forward_full_size(name):
+    w = FULL[name]
+    inp, t = _inputs(w)
+    layer, y, outs, nt, err = _check_forward(w, inp, t, tokens=FULL_SAMPLE[name])
+    print("%s: near ties boundary %d order %d, Y rel err %.3e" % (name, nt["boundary"], nt["order"], err))
+    # bitwise reproducible
+    y2 = layer.forward(t["x"])
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+def test_forward_is_deterministic_small():
+    w = SMALL["drop-small"]
+    inp, t = _inputs(w)
+    layer = _layer(w, t)
+    layer.alloc_outputs()
+    y1 = layer.forward(t["x"]).clone()
+    o1 = {k: v.clone() for k, v in layer.outputs.items()}
+    y2 = layer.forward(t["x"])
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    for k in o1:
+        assert torch.equal(o1[k], layer.outputs[k]), k
+
+
+# ------------------------------------------------------------ edge cases --
+
+def test_zero_tokens():
+    w = wl.scaled(wl.get(1), T=0, d=64, ffn=128)
+    inp = wl.make_layer(w, seed=1)
+    t = wl.device_layer(inp, DEV)
+    layer = _layer(w, t)
+    outs = layer.alloc_outputs()
+    for v in outs.values():
+        v.fill_(7)
+    y = layer.forward(t["x"])
+    torch.cuda.synchronize()
+    assert y.shape == (0, 64)
+    assert (outs["seg_offsets"] == 0).all() and (outs["kept_count"] == 0).all()
+    assert (outs["expert_count"] == 0).all() and (outs["f"] == 0).all() and (outs["P"] == 0).all()
+    assert outs["l_aux"].item() == 0.0 and outs["n_dropped"].item() == 0
+
+
+@pytest.mark.parametrize("T", [1, 17])
+def test_few_tokens(T):
+    w = wl.scaled(wl.get(1), T=T, d=128, ffn=256, router_bias="gauss", expert_bias="gauss")
+    inp, t = _inputs(w)
+    _check_forward(w, inp, t)
+
+
+def test_single_expert_is_dense_ffn():
+    w = wl.scaled(wl.get(1), T=130, d=128, E=1, k=1, ffn=256, expert_bias="gauss")
+    inp, t = _inputs(w)
+    layer, y, outs, nt, err = _check_forward(w, inp, t)
+    assert (outs["topk_w"] == 1.0).all()
+
+
+def test_all_experts_selected():
+    w = wl.scaled(wl.get(1), T=90, d=64, E=4, k=4, ffn=128)
+    inp, t = _inputs(w)
+    _check_forward(w, inp, t)
+
+
+def test_capacity_zero_drops_everything():
+    # C = floor(64 * 0.05 / 8) = 0
+    w = wl.scaled(wl.get(1), T=64, d=64, ffn=128, capacity_factor=0.05)
+    inp, t = _inputs(w)
+    layer, y, outs, nt, err = _check_forward(w, inp, t)
+    assert (outs["slot_row"] == -1).all() and outs["n_dropped"].item() == 64 * 2
+    assert (y.float() == 0).all()
+
+
+def test_capacity_zero_with_shared_expert():
+    w = wl.scaled(wl.get(4), T=48, d=64, ffn=128, E=16, k=4, num_local_experts=4, expert_begin=4,
+                  capacity_factor=0.05)
+    inp, t = _inputs(w)
+    _check_forward(w, inp, t)
+
+
+def test_max_experts_and_k():
+    w = wl.scaled(wl.get(3), T=200, d=64, E=1024, k=32, ffn=64)
+    inp, t = _inputs(w)
+    _check_forward(w, inp, t)
+
+
+def test_dispatch_ignores_out_of_range_ids():
+    T, k, E = 50, 2, 8
+    idx = np.random.default_rng(0).integers(0, E, size=(T, k)).astype(np.int32)
+    idx[idx[:, 0] == idx[:, 1], 1] = (idx[idx[:, 0] == idx[:, 1], 0] + 1) % E
+    idx[3, 1] = -5
+    idx[7, 0] = 999
+    gi = torch.from_numpy(idx).to(DEV)
+    dp = api.moe_dispatch(None, gi, E, 0.0, 2, 4, with_x_perm=False, dtype=torch.bfloat16, d=64)
+    torch.cuda.synchronize()
+    ref = oracle.capacity(idx, E, 0.0, 2, 4)
+    np.testing.assert_array_equal(dp["slot_row"].cpu().numpy(), ref.slot_row)
+    np.testing.assert_array_equal(dp["seg_offsets"].cpu().numpy(), ref.seg_offsets)
+    assert dp["slot_row"][3, 1].item() == -2 and dp["slot_row"][7, 0].item() == -2
+
+
+def test_pages_dispatch_example_on_gpu():
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_dispatch_example.json")))
+    idx = torch.tensor(g["topk_idx"], dtype=torch.int32, device=DEV)
+    x = torch.arange(4 * 8, dtype=torch.float32, device=DEV).reshape(4, 8)
+    dp = api.moe_dispatch(x, idx, g["E"])
+    torch.cuda.synchronize()
+    assert dp["row_src"][:4].tolist() == g["expected_row_src"]
+    assert dp["seg_offsets"].tolist() == g["expected_seg_offsets"]
+    assert dp["kept_count"].tolist() == g["expected_kept_count"]
+    assert torch.equal(dp["x_perm"][:4], x[torch.tensor(g["expected_row_src"], device=DEV)])
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("act", [0, 1])
+def test_grouped_gemm_segments(dtype, act):
+    """Segments of 0, 1, ragged and multi-tile sizes; K and N with tails."""
+    g = torch.Generator().manual_seed(5)
+    sizes = [0, 1, 130, 0, 257, 64, 3]
+    rows, K, N = sum(sizes) + 9, 200, 136
+    S = len(sizes)
+    a = torch.randn(rows, K, generator=g).to(dtype)
+    w = (torch.randn(S, N, K, generator=g) / K ** 0.5).to(dtype)
+    b = (torch.randn(S, N, generator=g) * 0.1).to(dtype)
+    seg = torch.tensor(np.concatenate([[0], np.cumsum(sizes)]), dtype=torch.int32)
+    out = torch.full((rows, N), 7.0, dtype=dtype)
+    od = api.moe_grouped_gemm(a.to(DEV), seg.to(DEV), w.to(DEV), b.to(DEV), act, out=out.to(DEV))
+    torch.cuda.synchronize()
+    got = od.float().cpu()
+    for s in range(S):
+        lo, hi = int(seg[s]), int(seg[s + 1])
+        ref = a[lo:hi].double() @ w[s].double().T + b[s].double()
+        if act:
+            ref = torch.nn.functional.gelu(ref, approximate="none")
+        if hi > lo:
+            tol = 1e-2 if dtype == torch.bfloat16 else 1e-5
+            assert rel_err(got[lo:hi].numpy(), ref.numpy()) <= tol
+    # rows past the last segment are untouched
+    assert (got[seg[-1]:] == 7.0).all()
+
+
+def test_grouped_gemm_single_segment_null_offsets():
+    g = torch.Generator().manual_seed(6)
+    a = torch.randn(300, 128, generator=g).to(torch.bfloat16)
+    w = (torch.randn(1, 256, 128, generator=g) / 128 ** 0.5).to(torch.bfloat16)
+    od = api.moe_grouped_gemm(a.to(DEV), None, w.to(DEV), None, 0)
+    torch.cuda.synchronize()
+    ref = a.double() @ w[0].double().T
+    assert rel_err(od.float().cpu().numpy(), ref.numpy()) <= 1e-2
+
+
+def test_route_bitwise_reproducible_and_stats_fixed_order():
+    w = SMALL["fine-small"]
+    inp, t = _inputs(w)
+    r1 = api.moe_route(t["x"], t["w_router"], t["b_router"], w.k)
+    r2 = api.moe_route(t["x"], t["w_router"], t["b_router"], w.k)
+    torch.cuda.synchronize()
+    for k in r1:
+        assert torch.equal(r1[k], r2[k]), k

@@ -1,0 +1,259 @@
+"""Thin Python binding over the C ABI in include/moe.h.
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the layer runs in the HIP kernels of libmoe_hip.so.
+There is no fallback: if the library is missing, every call raises.
+
+The low-level functions (``lib().moe_route`` ...) are the C entry points with
+ctypes signatures; the functions of this module with the same names allocate
+outputs and workspaces with torch and call them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_hip.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("%s (status %d)" % (msg, status))
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("ffn", ctypes.c_int32), ("capacity_factor", ctypes.c_float), ("expert_begin", ctypes.c_int32),
+                ("num_local_experts", ctypes.c_int32), ("has_shared", ctypes.c_int32), ("alpha", ctypes.c_float),
+                ("dtype", ctypes.c_int)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("w_router", "b_router", "w1", "b1", "w2", "b2", "ws1", "bs1", "ws2", "bs2")]
+
+
+class Outputs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("topk_idx", "topk_w", "expert_count", "f", "P", "l_aux", "seg_offsets", "kept_count",
+                 "slot_row", "row_src", "n_dropped")]
+
+
+EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_error", "moe_max_rows", "moe_route_workspace_size",
+           "moe_route", "moe_dispatch_workspace_size", "moe_dispatch", "moe_grouped_gemm", "moe_expert_ffn",
+           "moe_combine", "moe_forward_workspace_size", "moe_forward"]
+
+_lib = None
+
+
+def lib():
+    """The loaded C library with ctypes signatures (raises if not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libmoe_hip.so is not built (%s); run __graft_entry__.build() or "
+                           "python top_routing_expert_route_amd/build.py" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, I64, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    L.moe_abi_version.argtypes, L.moe_abi_version.restype = [], I
+    L.moe_status_string.argtypes, L.moe_status_string.restype = [I], ctypes.c_char_p
+    L.moe_last_error.argtypes, L.moe_last_error.restype = [], ctypes.c_char_p
+    L.moe_max_rows.argtypes, L.moe_max_rows.restype = [I64, I, I, F, I], I64
+    L.moe_route_workspace_size.argtypes, L.moe_route_workspace_size.restype = [I64, I], SZ
+    L.moe_route.argtypes = [P, I, P, P, I64, I, I, I, F, P, P, P, P, P, P, P, SZ, P]
+    L.moe_route.restype = I
+    L.moe_dispatch_workspace_size.argtypes, L.moe_dispatch_workspace_size.restype = [I64, I, I], SZ
+    L.moe_dispatch.argtypes = [P, I, P, I64, I, I, I, F, I, I, P, P, P, P, P, I64, P, P, SZ, P]
+    L.moe_dispatch.restype = I
+    L.moe_grouped_gemm.argtypes = [P, P, I, I64, I, I, I, P, P, I, P, P]
+    L.moe_grouped_gemm.restype = I
+    L.moe_expert_ffn.argtypes = [P, P, I, I64, I, I, I, P, P, P, P, P, P, P]
+    L.moe_expert_ffn.restype = I
+    L.moe_combine.argtypes = [P, I64, P, P, P, I64, I, I, I, P, P]
+    L.moe_combine.restype = I
+    L.moe_forward_workspace_size.argtypes = [ctypes.POINTER(Problem)]
+    L.moe_forward_workspace_size.restype = SZ
+    L.moe_forward.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Weights), P, P, ctypes.POINTER(Outputs), P,
+                              SZ, P]
+    L.moe_forward.restype = I
+    _lib = L
+    return L
+
+
+def check(status: int):
+    if status != MOE_OK:
+        raise MoeError(status, lib().moe_last_error().decode() or lib().moe_status_string(status).decode())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise TypeError("activations and expert weights must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ws(nbytes: int, dev) -> torch.Tensor:
+    return torch.empty(max(1, int(nbytes)), dtype=torch.uint8, device=dev)
+
+
+def max_rows(T: int, E: int, k: int, capacity_factor: float = 0.0, num_local_experts: int = 0) -> int:
+    return int(lib().moe_max_rows(T, E, k, capacity_factor, num_local_experts))
+
+
+# ----------------------------------------------------------------- steps --
+
+def moe_route(x: torch.Tensor, w_router: torch.Tensor, b_router: Optional[torch.Tensor], k: int,
+              alpha: float = 0.01) -> dict:
+    T, d = x.shape
+    E = w_router.shape[0]
+    dev = x.device
+    out = dict(topk_idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+               topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
+               expert_count=torch.empty(E, dtype=torch.int32, device=dev),
+               f=torch.empty(E, dtype=torch.float32, device=dev),
+               P=torch.empty(E, dtype=torch.float32, device=dev),
+               l_aux=torch.empty(1, dtype=torch.float32, device=dev))
+    nb = lib().moe_route_workspace_size(T, E)
+    ws = _ws(nb, dev)
+    check(lib().moe_route(_p(x), _dt(x), _p(w_router), _p(b_router), T, d, E, k, alpha,
+                          _p(out["topk_idx"]), _p(out["topk_w"]), _p(out["expert_count"]), _p(out["f"]),
+                          _p(out["P"]), _p(out["l_aux"]), _p(ws), nb, _stream(dev)))
+    return out
+
+
+def moe_dispatch(x: Optional[torch.Tensor], topk_idx: torch.Tensor, E: int, capacity_factor: float = 0.0,
+                 expert_begin: int = 0, num_local_experts: int = 0, with_x_perm: bool = True,
+                 rows: Optional[int] = None, dtype: Optional[torch.dtype] = None, d: Optional[int] = None) -> dict:
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    E_loc = num_local_experts if num_local_experts > 0 else E
+    mr = max_rows(T, E, k, capacity_factor, num_local_experts) if rows is None else rows
+    d = x.shape[1] if x is not None else d
+    dt = _dt(x) if x is not None else (MOE_BF16 if dtype == torch.bfloat16 else MOE_F32)
+    out = dict(seg_offsets=torch.empty(E_loc + 1, dtype=torch.int32, device=dev),
+               kept_count=torch.empty(E_loc, dtype=torch.int32, device=dev),
+               slot_row=torch.empty((T, k), dtype=torch.int32, device=dev),
+               row_src=torch.full((max(1, mr),), -1, dtype=torch.int32, device=dev),
+               n_dropped=torch.empty(1, dtype=torch.int32, device=dev),
+               x_perm=(torch.empty((max(1, mr), d), dtype=x.dtype, device=dev) if (with_x_perm and x is not None)
+                       else None))
+    nb = lib().moe_dispatch_workspace_size(T, k, E_loc)
+    ws = _ws(nb, dev)
+    check(lib().moe_dispatch(_p(x), dt, _p(topk_idx), T, d, E, k, capacity_factor, expert_begin,
+                             num_local_experts, _p(out["seg_offsets"]), _p(out["kept_count"]), _p(out["slot_row"]),
+                             _p(out["row_src"]), _p(out["x_perm"]), mr, _p(out["n_dropped"]), _p(ws), nb,
+                             _stream(dev)))
+    out["max_rows"] = mr
+    return out
+
+
+def moe_grouped_gemm(a: torch.Tensor, seg_offsets: Optional[torch.Tensor], w: torch.Tensor,
+                     bias: Optional[torch.Tensor], activation: int, out: Optional[torch.Tensor] = None
+                     ) -> torch.Tensor:
+    rows, K = a.shape
+    S, N, K2 = w.shape
+    assert K2 == K
+    if out is None:
+        out = torch.empty((rows, N), dtype=a.dtype, device=a.device)
+    nseg = S if seg_offsets is not None else 1
+    check(lib().moe_grouped_gemm(_p(a), _p(seg_offsets), nseg, rows, N, K, _dt(a), _p(w), _p(bias), activation,
+                                 _p(out), _stream(a.device)))
+    return out
+
+
+def moe_expert_ffn(x_perm: torch.Tensor, seg_offsets: torch.Tensor, w1, b1, w2, b2,
+                   h: Optional[torch.Tensor] = None, y_perm: Optional[torch.Tensor] = None):
+    rows, d = x_perm.shape
+    S, ffn, _ = w1.shape
+    if h is None:
+        h = torch.empty((rows, ffn), dtype=x_perm.dtype, device=x_perm.device)
+    if y_perm is None:
+        y_perm = torch.empty((rows, d), dtype=x_perm.dtype, device=x_perm.device)
+    check(lib().moe_expert_ffn(_p(x_perm), _p(seg_offsets), S, rows, d, ffn, _dt(x_perm), _p(w1), _p(b1), _p(w2),
+                               _p(b2), _p(h), _p(y_perm), _stream(x_perm.device)))
+    return h, y_perm
+
+
+def moe_combine(y_perm: torch.Tensor, slot_row: torch.Tensor, topk_w: torch.Tensor,
+                y_shared: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    rows, d = y_perm.shape
+    T, k = slot_row.shape
+    if y is None:
+        y = torch.empty((T, d), dtype=y_perm.dtype, device=y_perm.device)
+    check(lib().moe_combine(_p(y_perm), rows, _p(slot_row), _p(topk_w), _p(y_shared), T, d, k, _dt(y_perm), _p(y),
+                            _stream(y_perm.device)))
+    return y
+
+
+class Layer:
+    """Device tensors of one layer plus a reusable workspace for moe_forward."""
+
+    def __init__(self, T, d, E, k, ffn, dtype, capacity_factor=0.0, expert_begin=0, num_local_experts=0,
+                 alpha=0.01, w_router=None, b_router=None, w1=None, b1=None, w2=None, b2=None,
+                 ws1=None, bs1=None, ws2=None, bs2=None, device="cuda"):
+        self.problem = Problem(T, d, E, k, ffn, capacity_factor, expert_begin, num_local_experts,
+                               1 if ws1 is not None else 0, alpha, MOE_BF16 if dtype == torch.bfloat16 else MOE_F32)
+        self.tensors = dict(w_router=w_router, b_router=b_router, w1=w1, b1=b1, w2=w2, b2=b2,
+                            ws1=ws1, bs1=bs1, ws2=ws2, bs2=bs2)
+        self.weights = Weights(*[_p(self.tensors[n]) for n, _ in Weights._fields_])
+        self.E_loc = num_local_experts if num_local_experts > 0 else E
+        self.max_rows = max_rows(T, E, k, capacity_factor, num_local_experts)
+        self.device = torch.device(device)
+        self.dtype = dtype
+        self.outputs = None
+        self.out_struct = Outputs()
+        self.ws = None
+
+    def alloc_outputs(self):
+        p, dev = self.problem, self.device
+        self.outputs = dict(
+            topk_idx=torch.empty((p.T, p.k), dtype=torch.int32, device=dev),
+            topk_w=torch.empty((p.T, p.k), dtype=torch.float32, device=dev),
+            expert_count=torch.empty(p.E, dtype=torch.int32, device=dev),
+            f=torch.empty(p.E, dtype=torch.float32, device=dev),
+            P=torch.empty(p.E, dtype=torch.float32, device=dev),
+            l_aux=torch.empty(1, dtype=torch.float32, device=dev),
+            seg_offsets=torch.empty(self.E_loc + 1, dtype=torch.int32, device=dev),
+            kept_count=torch.empty(self.E_loc, dtype=torch.int32, device=dev),
+            slot_row=torch.empty((p.T, p.k), dtype=torch.int32, device=dev),
+            row_src=torch.empty(max(1, self.max_rows), dtype=torch.int32, device=dev),
+            n_dropped=torch.empty(1, dtype=torch.int32, device=dev))
+        self.out_struct = Outputs(*[_p(self.outputs[n]) for n, _ in Outputs._fields_])
+        self.ws = None
+        return self.outputs
+
+    def workspace_bytes(self) -> int:
+        return int(lib().moe_forward_workspace_size(ctypes.byref(self.problem)))
+
+    def forward(self, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+        if self.ws is None:
+            self.ws = _ws(self.workspace_bytes(), self.device)
+        if y is None:
+            y = torch.empty((self.problem.T, self.problem.d), dtype=x.dtype, device=x.device)
+        check(lib().moe_forward(ctypes.byref(self.problem), ctypes.byref(self.weights), _p(x), _p(y),
+                                ctypes.byref(self.out_struct), _p(self.ws), self.ws.numel(), _stream(x.device)))
+        return y

@@ -1,0 +1,86 @@
+// Shared device helpers, error state and internal launcher declarations of
+// the MoE layer library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "moe.h"
+
+#define MOE_ABI_VERSION 1
+
+namespace moe {
+
+// ---------------------------------------------------------------- errors --
+moe_status_t fail(moe_status_t s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+// hipGetLastError after a launch; MOE_ERR_HIP with the kernel's name on failure.
+moe_status_t check_launch(const char *what);
+
+// --------------------------------------------------------------- bfloat16 --
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round to nearest even (hardware v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f)
+{
+    __bf16 h = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// Exact GELU, 0.5 u (1 + erf(u / sqrt 2)), with the device library's erff.
+__device__ __forceinline__ float gelu_erf(float u)
+{
+    return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f));
+}
+
+// ------------------------------------------------------------ workspaces --
+constexpr size_t kAlign = 256;
+__host__ __device__ constexpr size_t align_up(size_t n, size_t a = kAlign) { return (n + a - 1) / a * a; }
+
+struct Carver {
+    char *base;
+    size_t off;
+    template <class T> T *take(size_t n)
+    {
+        T *p = reinterpret_cast<T *>(base ? base + off : nullptr);
+        off += align_up(n * sizeof(T));
+        return p;
+    }
+};
+
+// -------------------------------------------------- internal launchers ---
+// These assume validated arguments; the public entry points validate.
+
+size_t route_ws_bytes(int64_t T, int E);
+moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, const float *b_router,
+                          int64_t T, int d, int E, int k, float alpha, int32_t *topk_idx, float *topk_w,
+                          int32_t *expert_count, float *f, float *P, float *l_aux, void *ws,
+                          hipStream_t stream);
+
+size_t dispatch_ws_bytes(int64_t T, int k, int E_loc);
+int64_t capacity_of(int64_t T, int E, float capacity_factor); // -1: no cap
+moe_status_t launch_dispatch(const void *x, moe_dtype_t dt, const int32_t *topk_idx, int64_t T, int d,
+                             int E, int k, float capacity_factor, int e0, int E_loc, int32_t *seg_offsets,
+                             int32_t *kept_count, int32_t *slot_row, int32_t *row_src, void *x_perm,
+                             int64_t max_rows, int32_t *n_dropped, void *ws, hipStream_t stream);
+
+moe_status_t launch_grouped_gemm(const void *a, const int32_t *seg_offsets, int num_segments,
+                                 int64_t max_rows, int N, int K, moe_dtype_t dt, const void *w,
+                                 const void *bias, int activation, void *out, hipStream_t stream);
+
+moe_status_t launch_combine(const void *y_perm, int64_t max_rows, const int32_t *slot_row,
+                            const float *topk_w, const void *y_shared, int64_t T, int d, int k,
+                            moe_dtype_t dt, void *y, hipStream_t stream);
+
+} // namespace moe

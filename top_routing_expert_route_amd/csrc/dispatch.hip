@@ -1,0 +1,288 @@
+// Dispatch of the MoE layer on one GPU: capacity cap, token dropping and the
+// permutation of the kept selections into expert-contiguous rows.
+//
+// Pages: "Expert Parallelism (MoE)", section "Top-K Routing and Capacity
+// Factor" (capacity = tokens_per_batch / N_experts * capacity_factor; the
+// selections over capacity are dropped) and "Expert Parallelism (EP)",
+// section "Key math / How it works" (dispatch routes each token to the owner
+// of its expert - here a permutation into this GPU's expert segments).
+//
+// The selections t*k+j are cut into chunks of `chunk` consecutive items, one
+// chunk per wave, so that the rank of a selection among the earlier
+// selections of its expert is
+//     (selections of that expert in earlier chunks) + (earlier in its chunk).
+//  dispatch_count    per-chunk histogram of local experts (LDS atomics: exact
+//                    integer counts, order-free).
+//  dispatch_scan     one block: per-expert exclusive scan over chunks (one
+//                    wave per expert, shuffle scans), capacity, kept counts,
+//                    the exclusive scan of kept counts (segment offsets) and
+//                    the number of dropped selections.
+//  dispatch_rank     each wave walks its chunk 64 selections at a time; lanes
+//                    holding the same expert find each other with 64-lane
+//                    ballots over the bits of the expert id, so the rank is
+//                    stable (token order) without atomics.  Writes slot_row
+//                    and row_src.
+//  dispatch_scatter  one wave per token: the token's row of x is read once
+//                    and written to each of its kept rows (16-byte accesses).
+#include "common.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kScanCap = 16384; // chunks * local experts kept small for the scan
+
+__device__ __forceinline__ int local_of(int32_t e, int e0, int E_loc)
+{
+    const int l = e - e0;
+    return (l >= 0 && l < E_loc) ? l : -1;
+}
+
+__global__ __launch_bounds__(256) void dispatch_count(const int32_t *__restrict__ topk_idx, int64_t items,
+                                                      int chunk, int nchunks, int e0, int E_loc,
+                                                      int32_t *__restrict__ chunk_count)
+{
+    extern __shared__ int hist[]; // [4][E_loc]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int *h = hist + wave * E_loc;
+    for (int l = lane; l < E_loc; l += 64)
+        h[l] = 0;
+    __syncthreads();
+    const int c = blockIdx.x * 4 + wave;
+    if (c < nchunks) {
+        const int64_t beg = (int64_t)c * chunk;
+        const int64_t end = min(items, beg + chunk);
+        for (int64_t i = beg + lane; i < end; i += 64) {
+            const int l = local_of(topk_idx[i], e0, E_loc);
+            if (l >= 0)
+                atomicAdd(&h[l], 1);
+        }
+    }
+    __syncthreads();
+    if (c < nchunks)
+        for (int l = lane; l < E_loc; l += 64)
+            chunk_count[(int64_t)c * E_loc + l] = h[l];
+}
+
+__device__ __forceinline__ int wave_incl_scan(int v, int lane)
+{
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(v, o, 64);
+        if (lane >= o)
+            v += u;
+    }
+    return v;
+}
+
+// chunk_count [nchunks][E_loc] is turned in place into the per-chunk bases.
+__global__ __launch_bounds__(1024) void dispatch_scan(int32_t *__restrict__ chunk_cb, int nchunks, int E_loc,
+                                                      int64_t cap, int32_t *__restrict__ seg_offsets,
+                                                      int32_t *__restrict__ kept_count,
+                                                      int32_t *__restrict__ n_dropped)
+{
+    __shared__ int tot[1024];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int l = wave; l < E_loc; l += 16) {
+        int carry = 0;
+        for (int c0 = 0; c0 < nchunks; c0 += 64) {
+            const int c = c0 + lane;
+            const int v = c < nchunks ? chunk_cb[(int64_t)c * E_loc + l] : 0;
+            const int inc = wave_incl_scan(v, lane);
+            if (c < nchunks)
+                chunk_cb[(int64_t)c * E_loc + l] = carry + inc - v;
+            carry += __shfl(inc, 63, 64);
+        }
+        if (lane == 0)
+            tot[l] = carry;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        int carry = 0, drop = 0;
+        for (int l0 = 0; l0 < E_loc; l0 += 64) {
+            const int l = l0 + lane;
+            int t = 0, kept = 0;
+            if (l < E_loc) {
+                t = tot[l];
+                kept = (cap >= 0 && (int64_t)t > cap) ? (int)cap : t;
+            }
+            const int inc = wave_incl_scan(kept, lane);
+            int dr = t - kept;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1)
+                dr += __shfl_xor(dr, o, 64);
+            if (l < E_loc) {
+                seg_offsets[l] = carry + inc - kept;
+                kept_count[l] = kept;
+            }
+            carry += __shfl(inc, 63, 64);
+            drop += dr;
+        }
+        if (lane == 0) {
+            seg_offsets[E_loc] = carry;
+            if (n_dropped)
+                n_dropped[0] = drop;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void dispatch_rank(const int32_t *__restrict__ topk_idx, int64_t items,
+                                                     int chunk, int nchunks, int e0, int E_loc, int nbits,
+                                                     int64_t cap, const int32_t *__restrict__ chunk_base,
+                                                     const int32_t *__restrict__ seg_offsets, int64_t max_rows,
+                                                     int32_t *__restrict__ slot_row, int32_t *__restrict__ row_src)
+{
+    extern __shared__ int run_all[]; // [4][E_loc]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int c = blockIdx.x * 4 + wave;
+    if (c >= nchunks)
+        return; // no block-wide barrier below: waves are independent
+    int *run = run_all + wave * E_loc;
+    for (int l = lane; l < E_loc; l += 64)
+        run[l] = chunk_base[(int64_t)c * E_loc + l];
+    const uint64_t below = (1ull << lane) - 1ull;
+    const int64_t beg = (int64_t)c * chunk;
+    const int64_t end = min(items, beg + chunk);
+    for (int64_t i0 = beg; i0 < end; i0 += 64) {
+        const int64_t i = i0 + lane;
+        const bool valid = i < end;
+        const int l = valid ? local_of(topk_idx[i], e0, E_loc) : -1;
+        const bool local = l >= 0;
+        uint64_t m = __ballot(local);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = local && ((l >> b) & 1);
+            const uint64_t bb = __ballot(bit);
+            m &= bit ? bb : ~bb;
+        }
+        if (local) {
+            const int lrank = __popcll(m & below);
+            const int base = run[l];
+            const int64_t r = (int64_t)base + lrank;
+            const bool last = (m >> lane) == 1ull;
+            if (last)
+                run[l] = base + __popcll(m);
+            int32_t out = -1;
+            if (cap < 0 || r < cap) {
+                const int64_t row = (int64_t)seg_offsets[l] + r;
+                if (row < max_rows) {
+                    out = (int32_t)row;
+                    row_src[row] = (int32_t)i;
+                }
+            }
+            slot_row[i] = out;
+        } else if (valid) {
+            slot_row[i] = -2;
+        }
+    }
+}
+
+template <int U>
+__global__ __launch_bounds__(256) void dispatch_scatter(const u32x4 *__restrict__ x, const int32_t *__restrict__ slot_row,
+                                                        int64_t T, int k, int64_t units, u32x4 *__restrict__ x_perm)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= T)
+        return;
+    bool any = false;
+    for (int j = 0; j < k; ++j)
+        any |= slot_row[t * k + j] >= 0;
+    if (!any)
+        return;
+    const u32x4 *src = x + t * units;
+    for (int64_t u0 = 0; u0 < units; u0 += 64 * U) {
+        u32x4 v[U];
+#pragma unroll
+        for (int q = 0; q < U; ++q) {
+            const int64_t u = u0 + q * 64 + lane;
+            if (u < units)
+                v[q] = src[u];
+        }
+        for (int j = 0; j < k; ++j) {
+            const int r = slot_row[t * k + j];
+            if (r < 0)
+                continue;
+            u32x4 *dst = x_perm + (int64_t)r * units;
+#pragma unroll
+            for (int q = 0; q < U; ++q) {
+                const int64_t u = u0 + q * 64 + lane;
+                if (u < units)
+                    dst[u] = v[q];
+            }
+        }
+    }
+}
+
+struct ChunkPlan {
+    int chunk, nchunks;
+};
+
+ChunkPlan plan_chunks(int64_t items, int E_loc)
+{
+    int64_t chunk = 512;
+    while (((items + chunk - 1) / chunk) * (int64_t)E_loc > kScanCap && chunk < (1 << 30))
+        chunk *= 2;
+    ChunkPlan p;
+    p.chunk = (int)chunk;
+    p.nchunks = (int)((items + chunk - 1) / chunk);
+    return p;
+}
+
+} // namespace
+
+int64_t capacity_of(int64_t T, int E, float capacity_factor)
+{
+    if (!(capacity_factor > 0.f))
+        return -1;
+    const double c = floor((double)T * (double)capacity_factor / (double)E);
+    if (c >= (double)T)
+        return T; // never binding: a token selects an expert at most once
+    return (int64_t)c;
+}
+
+size_t dispatch_ws_bytes(int64_t T, int k, int E_loc)
+{
+    const ChunkPlan p = plan_chunks(T * k, E_loc);
+    return align_up((size_t)p.nchunks * E_loc * sizeof(int32_t));
+}
+
+moe_status_t launch_dispatch(const void *x, moe_dtype_t dt, const int32_t *topk_idx, int64_t T, int d, int E,
+                             int k, float capacity_factor, int e0, int E_loc, int32_t *seg_offsets,
+                             int32_t *kept_count, int32_t *slot_row, int32_t *row_src, void *x_perm,
+                             int64_t max_rows, int32_t *n_dropped, void *ws, hipStream_t stream)
+{
+    const int64_t items = T * k;
+    const ChunkPlan p = plan_chunks(items, E_loc);
+    const int64_t cap = capacity_of(T, E, capacity_factor);
+    int32_t *chunk_cb = (int32_t *)ws;
+    const size_t lds = (size_t)4 * E_loc * sizeof(int);
+    const unsigned blocks = (unsigned)((p.nchunks + 3) / 4);
+    if (items > 0) {
+        dispatch_count<<<blocks, 256, lds, stream>>>(topk_idx, items, p.chunk, p.nchunks, e0, E_loc, chunk_cb);
+        if (moe_status_t s = check_launch("dispatch_count"))
+            return s;
+    }
+    dispatch_scan<<<1, 1024, 0, stream>>>(chunk_cb, items > 0 ? p.nchunks : 0, E_loc, cap, seg_offsets, kept_count,
+                                          n_dropped);
+    if (moe_status_t s = check_launch("dispatch_scan"))
+        return s;
+    if (items == 0)
+        return MOE_OK;
+    int nbits = 0;
+    while ((1 << nbits) < E_loc)
+        ++nbits;
+    dispatch_rank<<<blocks, 256, lds, stream>>>(topk_idx, items, p.chunk, p.nchunks, e0, E_loc, nbits, cap,
+                                                chunk_cb, seg_offsets, max_rows, slot_row, row_src);
+    if (moe_status_t s = check_launch("dispatch_rank"))
+        return s;
+    if (x_perm) {
+        const int64_t units = (int64_t)d * (dt == MOE_BF16 ? 2 : 4) / 16;
+        dispatch_scatter<8><<<(unsigned)((T + 3) / 4), 256, 0, stream>>>((const u32x4 *)x, slot_row, T, k, units,
+                                                                         (u32x4 *)x_perm);
+        if (moe_status_t s = check_launch("dispatch_scatter"))
+            return s;
+    }
+    return MOE_OK;
+}
+
+} // namespace moe

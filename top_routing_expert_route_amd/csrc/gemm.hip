@@ -1,0 +1,387 @@
+// Grouped GEMM of the MoE layer: one Linear of every expert over its segment
+// of expert-contiguous rows, with the bias and (for the first Linear) the
+// exact GELU fused into the epilogue.
+//
+// Pages: "Expert Parallelism (MoE)", section "MoE Layer Structure" (each
+// expert applies Linear(d -> 4d) -> GELU -> Linear(4d -> d)) and "Expert
+// Parallelism (EP)", section "Key math / How it works" (the expert GEMMs run
+// locally on the rows dispatched to this GPU).
+//
+// bf16 kernel (gfx950 matrix cores)
+//  - out[r, n] = act(sum_k a[r, k] w[s, n, k] + b[s, n]) is computed as
+//    out^T = W . A^T: the weight rows are the MFMA "A" operand and the token
+//    rows the "B" operand, so each lane's accumulators hold 4 consecutive
+//    output features of one row (8-byte bf16 stores).
+//  - Block tile BN (features) x BM (rows), BK = 64; four waves in a 2 x 2
+//    grid, each owning (BN/2) x (BM/2) as 32x32x16 bf16 MFMAs with fp32
+//    accumulation.  Tiles of A and W are staged through LDS with an XOR
+//    swizzle of the 16-byte chunks (row & 7) and double-buffered: the global
+//    loads of step k+1 are in flight while step k computes.
+//  - Persistent grid.  The tile list is derived on the device from the
+//    segment offsets (no host round trip): segment s contributes
+//    ceil(rows_s / BM) * (N / BN) tiles, ordered (segment, feature tile,
+//    row tile) so that consecutive tiles share one weight tile.  Blocks are
+//    dealt to the 8 XCDs round-robin by the hardware, so each XCD is given one
+//    contiguous range of the tile list: the tiles that share weights run on
+//    the same L2.
+//  - Ragged tails: rows past the segment end are clamped on load and masked
+//    on store; K tails are zero-filled in whole 8-element chunks.
+// fp32 kernel: straightforward LDS-tiled VALU GEMM for the fp32 workloads.
+#include "common.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kBK = 64;
+constexpr int kMaxSeg = 1024;
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int64_t clamp_off(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// Segment bounds with offsets clamped to [0, max_rows] and made non-decreasing.
+__device__ __forceinline__ void seg_bounds(const int32_t *seg, int s, int64_t max_rows, int64_t &lo, int64_t &hi)
+{
+    if (!seg) {
+        lo = 0;
+        hi = max_rows;
+        return;
+    }
+    lo = clamp_off(seg[s], 0, max_rows);
+    hi = clamp_off(seg[s + 1], lo, max_rows);
+}
+
+// Exclusive prefix (in LDS) of the row tiles per segment; tb[S] = total.
+template <int BM>
+__device__ void build_tile_prefix(const int32_t *seg, int S, int64_t max_rows, int *tb)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (wave == 0) {
+        int carry = 0;
+        for (int s0 = 0; s0 < S; s0 += 64) {
+            const int s = s0 + lane;
+            int v = 0;
+            if (s < S) {
+                int64_t lo, hi;
+                seg_bounds(seg, s, max_rows, lo, hi);
+                v = (int)((hi - lo + BM - 1) / BM);
+            }
+            int inc = v;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int u = __shfl_up(inc, o, 64);
+                if (lane >= o)
+                    inc += u;
+            }
+            if (s < S)
+                tb[s] = carry + inc - v;
+            carry += __shfl(inc, 63, 64);
+        }
+        if (lane == 0)
+            tb[S] = carry;
+    }
+    __syncthreads();
+}
+
+// Largest s in [0, S) with tb[s] * NT <= L (tb non-decreasing, L < tb[S]*NT).
+__device__ __forceinline__ int find_segment(const int *tb, int S, int NT, int64_t L)
+{
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)tb[mid] * NT <= L)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+template <int BN, int BM, bool GELU>
+__global__ __launch_bounds__(256, 2) void grouped_gemm_bf16(const uint16_t *__restrict__ A,
+                                                            const int32_t *__restrict__ seg, int S,
+                                                            int64_t max_rows, const uint16_t *__restrict__ W,
+                                                            const uint16_t *__restrict__ bias,
+                                                            uint16_t *__restrict__ C, int N, int K)
+{
+    constexpr int WN = BN / 2, WM = BM / 2;
+    constexpr int FN = WN / 32, FM = WM / 32;
+    constexpr int LW = BN / 32, LA = BM / 32; // 16-byte loads per thread per stage
+    __shared__ __attribute__((aligned(16))) uint16_t sW[2][BN * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * kBK];
+    __shared__ int tb[kMaxSeg + 1];
+
+    build_tile_prefix<BM>(seg, S, max_rows, tb);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wn = wave & 1, wm = wave >> 1;
+    const int NT = (N + BN - 1) / BN;
+    const int64_t total = (int64_t)tb[S] * NT;
+
+    // XCD-contiguous share of the tile list.
+    const int xcd = blockIdx.x % kXcds;
+    const int per = gridDim.x / kXcds;
+    const int j = blockIdx.x / kXcds;
+    const int64_t rlo = total * xcd / kXcds, rhi = total * (xcd + 1) / kXcds;
+
+    const int lr = tid >> 3;  // row within a 32-row load group
+    const int lc = tid & 7;   // 16-byte chunk within the 64-wide K slice
+    const int KT = (K + kBK - 1) / kBK;
+
+    for (int64_t L = rlo + j; L < rhi; L += per) {
+        const int s = find_segment(tb, S, NT, L);
+        const int mt_s = tb[s + 1] - tb[s];
+        const int64_t local = L - (int64_t)tb[s] * NT;
+        const int n_tile = (int)(local / mt_s);
+        const int m_tile = (int)(local % mt_s);
+        int64_t seg_lo, seg_hi;
+        seg_bounds(seg, s, max_rows, seg_lo, seg_hi);
+        const int64_t row0 = seg_lo + (int64_t)m_tile * BM;
+        const int64_t row_end = min(row0 + BM, seg_hi);
+        const int n0 = n_tile * BN;
+
+        const uint16_t *wbase = W + (int64_t)s * N * K;
+        const uint16_t *gw[LW];
+        const uint16_t *ga[LA];
+#pragma unroll
+        for (int q = 0; q < LW; ++q) {
+            const int n = min(n0 + q * 32 + lr, N - 1);
+            gw[q] = wbase + (int64_t)n * K + lc * 8;
+        }
+#pragma unroll
+        for (int q = 0; q < LA; ++q) {
+            const int64_t r = min(row0 + q * 32 + lr, row_end - 1);
+            ga[q] = A + r * K + lc * 8;
+        }
+        const int sw_off = lr * kBK + ((lc ^ (lr & 7)) * 8);
+
+        u32x4 rw[LW], ra[LA];
+        auto gload = [&](int kt) {
+            const int kk = kt * kBK + lc * 8;
+            const bool ok = kk < K;
+#pragma unroll
+            for (int q = 0; q < LW; ++q)
+                rw[q] = ok ? *reinterpret_cast<const u32x4 *>(gw[q] + kt * kBK) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int q = 0; q < LA; ++q)
+                ra[q] = ok ? *reinterpret_cast<const u32x4 *>(ga[q] + kt * kBK) : u32x4{0u, 0u, 0u, 0u};
+        };
+        auto lstore = [&](int buf) {
+#pragma unroll
+            for (int q = 0; q < LW; ++q)
+                *reinterpret_cast<u32x4 *>(&sW[buf][q * 32 * kBK + sw_off]) = rw[q];
+#pragma unroll
+            for (int q = 0; q < LA; ++q)
+                *reinterpret_cast<u32x4 *>(&sA[buf][q * 32 * kBK + sw_off]) = ra[q];
+        };
+
+        f32x16 acc[FN][FM];
+#pragma unroll
+        for (int a = 0; a < FN; ++a)
+#pragma unroll
+            for (int b = 0; b < FM; ++b)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    acc[a][b][v] = 0.f;
+
+        gload(0);
+        lstore(0);
+        __syncthreads();
+        const int r32 = lane & 31, khalf = lane >> 5;
+        for (int kt = 0; kt < KT; ++kt) {
+            if (kt + 1 < KT)
+                gload(kt + 1);
+            const int buf = kt & 1;
+#pragma unroll
+            for (int ks = 0; ks < kBK / 16; ++ks) {
+                const int ch = ks * 2 + khalf;
+                bf16x8 fa[FN], fb[FM];
+#pragma unroll
+                for (int a = 0; a < FN; ++a) {
+                    const int row = wn * WN + a * 32 + r32;
+                    fa[a] = *reinterpret_cast<const bf16x8 *>(&sW[buf][row * kBK + ((ch ^ (row & 7)) * 8)]);
+                }
+#pragma unroll
+                for (int b = 0; b < FM; ++b) {
+                    const int row = wm * WM + b * 32 + r32;
+                    fb[b] = *reinterpret_cast<const bf16x8 *>(&sA[buf][row * kBK + ((ch ^ (row & 7)) * 8)]);
+                }
+#pragma unroll
+                for (int a = 0; a < FN; ++a)
+#pragma unroll
+                    for (int b = 0; b < FM; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fb[b], acc[a][b], 0, 0, 0);
+            }
+            if (kt + 1 < KT)
+                lstore((kt + 1) & 1);
+            __syncthreads();
+        }
+
+        // Epilogue: lane holds out^T[n][m] for m = lane%32 and, for each group
+        // g of 4 registers, n = 8g + 4*(lane/32) + 0..3.
+        const uint16_t *bseg = bias ? bias + (int64_t)s * N : nullptr;
+#pragma unroll
+        for (int b = 0; b < FM; ++b) {
+            const int64_t row = row0 + wm * WM + b * 32 + r32;
+            if (row >= row_end)
+                continue;
+            uint16_t *crow = C + row * N;
+#pragma unroll
+            for (int a = 0; a < FN; ++a) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = n0 + wn * WN + a * 32 + 8 * g + 4 * khalf;
+                    if (n >= N)
+                        continue;
+                    float v0 = acc[a][b][4 * g + 0], v1 = acc[a][b][4 * g + 1];
+                    float v2 = acc[a][b][4 * g + 2], v3 = acc[a][b][4 * g + 3];
+                    if (bseg) {
+                        const uint2 bb = *reinterpret_cast<const uint2 *>(bseg + n);
+                        v0 += bf16_bits_to_f32(bb.x & 0xFFFFu);
+                        v1 += bf16_bits_to_f32(bb.x >> 16);
+                        v2 += bf16_bits_to_f32(bb.y & 0xFFFFu);
+                        v3 += bf16_bits_to_f32(bb.y >> 16);
+                    }
+                    if (GELU) {
+                        v0 = gelu_erf(v0);
+                        v1 = gelu_erf(v1);
+                        v2 = gelu_erf(v2);
+                        v3 = gelu_erf(v3);
+                    }
+                    uint2 o;
+                    o.x = pack_bf16x2(v0, v1);
+                    o.y = pack_bf16x2(v2, v3);
+                    *reinterpret_cast<uint2 *>(crow + n) = o;
+                }
+            }
+        }
+    }
+}
+
+// fp32: 64 x 64 tiles, 4 x 4 per thread, K slices of 16 through LDS.
+template <bool GELU>
+__global__ __launch_bounds__(256) void grouped_gemm_f32(const float *__restrict__ A, const int32_t *__restrict__ seg,
+                                                        int S, int64_t max_rows, const float *__restrict__ W,
+                                                        const float *__restrict__ bias, float *__restrict__ C, int N,
+                                                        int K)
+{
+    constexpr int TM = 64, TN = 64, TK = 16;
+    __shared__ float sa[TK][TM + 4];
+    __shared__ float sw[TK][TN + 4];
+    __shared__ int tb[kMaxSeg + 1];
+    build_tile_prefix<TM>(seg, S, max_rows, tb);
+    const int64_t mt = blockIdx.y;
+    if (mt >= tb[S])
+        return;
+    const int s = find_segment(tb, S, 1, mt);
+    int64_t seg_lo, seg_hi;
+    seg_bounds(seg, s, max_rows, seg_lo, seg_hi);
+    const int64_t row0 = seg_lo + (mt - tb[s]) * TM;
+    const int64_t row_end = min(row0 + TM, seg_hi);
+    const int n0 = blockIdx.x * TN;
+    const float *wbase = W + (int64_t)s * N * K;
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < K; k0 += TK) {
+        for (int q = tid; q < TM * TK; q += 256) {
+            const int r = q / TK, kk = q % TK;
+            const int64_t row = min(row0 + r, row_end - 1);
+            const int n = min(n0 + r, N - 1);
+            sa[kk][r] = (k0 + kk < K) ? A[row * K + k0 + kk] : 0.f;
+            sw[kk][r] = (k0 + kk < K) ? wbase[(int64_t)n * K + k0 + kk] : 0.f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < TK; ++kk) {
+            float av[4], wv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                av[i] = sa[kk][ty * 4 + i];
+                wv[i] = sw[kk][tx * 4 + i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc[i][q] = fmaf(av[i], wv[q], acc[i][q]);
+        }
+        __syncthreads();
+    }
+    for (int i = 0; i < 4; ++i) {
+        const int64_t row = row0 + ty * 4 + i;
+        if (row >= row_end)
+            continue;
+        for (int q = 0; q < 4; ++q) {
+            const int n = n0 + tx * 4 + q;
+            if (n >= N)
+                continue;
+            float v = acc[i][q];
+            if (bias)
+                v += bias[(int64_t)s * N + n];
+            if (GELU)
+                v = gelu_erf(v);
+            C[row * N + n] = v;
+        }
+    }
+}
+
+int device_cus()
+{
+    static thread_local int cached_dev = -1, cached_cus = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 256;
+    if (dev != cached_dev) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cached_dev = dev;
+        cached_cus = cus;
+    }
+    return cached_cus;
+}
+
+template <int BN, int BM>
+moe_status_t run_bf16(const void *a, const int32_t *seg, int S, int64_t max_rows, int N, int K, const void *w,
+                      const void *bias, int act, void *out, hipStream_t stream)
+{
+    const int64_t tiles_bound = ((max_rows + BM - 1) / BM + S) * (int64_t)((N + BN - 1) / BN);
+    int64_t grid = (int64_t)device_cus() * 2;
+    grid = (grid + kXcds - 1) / kXcds * kXcds;
+    const int64_t need = (tiles_bound + kXcds - 1) / kXcds * kXcds;
+    if (need < grid)
+        grid = need;
+    if (grid < kXcds)
+        grid = kXcds;
+    if (act == 1)
+        grouped_gemm_bf16<BN, BM, true><<<(unsigned)grid, 256, 0, stream>>>(
+            (const uint16_t *)a, seg, S, max_rows, (const uint16_t *)w, (const uint16_t *)bias, (uint16_t *)out, N, K);
+    else
+        grouped_gemm_bf16<BN, BM, false><<<(unsigned)grid, 256, 0, stream>>>(
+            (const uint16_t *)a, seg, S, max_rows, (const uint16_t *)w, (const uint16_t *)bias, (uint16_t *)out, N, K);
+    return check_launch("grouped_gemm_bf16");
+}
+
+} // namespace
+
+moe_status_t launch_grouped_gemm(const void *a, const int32_t *seg_offsets, int num_segments, int64_t max_rows,
+                                 int N, int K, moe_dtype_t dt, const void *w, const void *bias, int activation,
+                                 void *out, hipStream_t stream)
+{
+    if (max_rows == 0)
+        return MOE_OK;
+    const int S = seg_offsets ? num_segments : 1;
+    if (dt == MOE_BF16)
+        return run_bf16<128, 128>(a, seg_offsets, S, max_rows, N, K, w, bias, activation, out, stream);
+    const dim3 g((unsigned)((N + 63) / 64), (unsigned)((max_rows + 63) / 64 + S));
+    if (activation == 1)
+        grouped_gemm_f32<true><<<g, 256, 0, stream>>>((const float *)a, seg_offsets, S, max_rows, (const float *)w,
+                                                       (const float *)bias, (float *)out, N, K);
+    else
+        grouped_gemm_f32<false><<<g, 256, 0, stream>>>((const float *)a, seg_offsets, S, max_rows, (const float *)w,
+                                                        (const float *)bias, (float *)out, N, K);
+    return check_launch("grouped_gemm_f32");
+}
+
+} // namespace moe

@@ -1,0 +1,400 @@
+// Router of the MoE layer: logits = x . W_r^T (+ b_r), softmax over the E
+// experts, top-k selection and the load statistics f, P, L_aux.
+//
+// Pages: "Expert Parallelism (MoE)", section "MoE Layer Structure" (router
+// Linear d -> N_experts, top-K experts per token, routing weight in Y) and
+// section "Load Balancing: The Auxiliary Loss" (f_i, P_i, L_aux = alpha *
+// sum f_i P_i).
+//
+// Kernels
+//  route_logits_mfma  bf16 activations.  The fp32 router weight is split
+//                     exactly into three bf16 pieces (hi + mid + lo = w); each
+//                     piece times a bf16 activation is exact in fp32, so three
+//                     bf16 MFMAs accumulating in fp32 give fp32-class logits at
+//                     matrix-core rate.  The four waves of a block split K and
+//                     their partial tiles are summed in LDS in a fixed order.
+//  route_logits_f32   fp32 activations: one thread per (token, expert) fp32
+//                     dot product (the small fp32 workloads).
+//  route_select       one wave per token: softmax, top-k by (logit desc, id
+//                     asc), routing weights, and per-block partial sums of the
+//                     probabilities and selection counts.
+//  route_finalize     one block: fixed-order sums of the partials -> counts,
+//                     f, P and L_aux (bitwise reproducible).
+#include "common.hpp"
+
+#include <math.h>
+
+namespace moe {
+
+namespace {
+
+constexpr int kSelTokensPerWave = 16;
+constexpr int kSelTokensPerBlock = 4 * kSelTokensPerWave;
+
+__device__ __forceinline__ float trunc_bf16(float v) { return __uint_as_float(__float_as_uint(v) & 0xFFFF0000u); }
+
+__device__ __forceinline__ __bf16 bits_bf16(float v)
+{
+    return __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(v) >> 16));
+}
+
+// ET expert tiles and TT token tiles of 16 per block; 4 waves split K.
+template <int ET, int TT>
+__global__ __launch_bounds__(256) void route_logits_mfma(const uint16_t *__restrict__ x,
+                                                         const float *__restrict__ wr, int64_t T, int d,
+                                                         int E, float *__restrict__ logits)
+{
+    constexpr int EB = 16 * ET, TB = 16 * TT;
+    __shared__ float red[3][ET * TT * 256];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t t0 = (int64_t)blockIdx.x * TB;
+    const int e_base = blockIdx.y * EB;
+
+    // K range of this wave, in steps of 32.
+    const int kw = ((d + 3) / 4 + 31) / 32 * 32;
+    const int kbeg = wave * kw;
+    const int kend = min(d, kbeg + kw);
+
+    f32x4 acc[ET][TT];
+#pragma unroll
+    for (int a = 0; a < ET; ++a)
+#pragma unroll
+        for (int b = 0; b < TT; ++b)
+            acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int r16 = lane & 15;
+    const int koff = (lane >> 4) * 8;
+
+    for (int k = kbeg; k < kend; k += 32) {
+        const int kk = k + koff;
+        const bool kval = kk < kend;
+        bf16x8 xb[TT];
+#pragma unroll
+        for (int b = 0; b < TT; ++b) {
+            const int64_t t = t0 + b * 16 + r16;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (kval && t < T)
+                v = *reinterpret_cast<const u32x4 *>(x + t * d + kk);
+            xb[b] = __builtin_bit_cast(bf16x8, v);
+        }
+#pragma unroll
+        for (int a = 0; a < ET; ++a) {
+            const int e = e_base + a * 16 + r16;
+            float wv[8];
+            if (kval && e < E) {
+                const f32x4 *p = reinterpret_cast<const f32x4 *>(wr + (int64_t)e * d + kk);
+                f32x4 w0 = p[0], w1 = p[1];
+                wv[0] = w0[0]; wv[1] = w0[1]; wv[2] = w0[2]; wv[3] = w0[3];
+                wv[4] = w1[0]; wv[5] = w1[1]; wv[6] = w1[2]; wv[7] = w1[3];
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    wv[q] = 0.f;
+            }
+            bf16x8 hi, mid, lo;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float h = trunc_bf16(wv[q]);
+                const float r1 = wv[q] - h;          // exact
+                const float m = trunc_bf16(r1);
+                const float r2 = r1 - m;             // exact, <= 8 significant bits
+                hi[q] = bits_bf16(h);
+                mid[q] = bits_bf16(m);
+                lo[q] = bits_bf16(r2);
+            }
+#pragma unroll
+            for (int b = 0; b < TT; ++b) {
+                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, xb[b], acc[a][b], 0, 0, 0);
+                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, xb[b], acc[a][b], 0, 0, 0);
+                acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, xb[b], acc[a][b], 0, 0, 0);
+            }
+        }
+    }
+
+    // 16x16 MFMA output: lane holds rows (experts) 4*(lane/16)+v, column
+    // (token) lane%16.  Waves 1..3 park their partial tiles; wave 0 adds them
+    // in wave order and stores.
+    if (wave > 0) {
+#pragma unroll
+        for (int a = 0; a < ET; ++a)
+#pragma unroll
+            for (int b = 0; b < TT; ++b)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    red[wave - 1][((a * TT + b) * 4 + v) * 64 + lane] = acc[a][b][v];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int a = 0; a < ET; ++a)
+#pragma unroll
+            for (int b = 0; b < TT; ++b)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int slot = ((a * TT + b) * 4 + v) * 64 + lane;
+                    float s = acc[a][b][v];
+                    s += red[0][slot];
+                    s += red[1][slot];
+                    s += red[2][slot];
+                    const int e = e_base + a * 16 + 4 * (lane >> 4) + v;
+                    const int64_t t = t0 + b * 16 + (lane & 15);
+                    if (e < E && t < T)
+                        logits[t * E + e] = s;
+                }
+    }
+}
+
+__global__ __launch_bounds__(256) void route_logits_f32(const float *__restrict__ x, const float *__restrict__ wr,
+                                                        int64_t T, int d, int E, float *__restrict__ logits)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= T * E)
+        return;
+    const int64_t t = i / E;
+    const int e = (int)(i % E);
+    const f32x4 *xr = reinterpret_cast<const f32x4 *>(x + t * d);
+    const f32x4 *wv = reinterpret_cast<const f32x4 *>(wr + (int64_t)e * d);
+    float s = 0.f;
+    for (int q = 0; q < d / 4; ++q) {
+        const f32x4 a = xr[q], b = wv[q];
+        s = fmaf(a[0], b[0], s);
+        s = fmaf(a[1], b[1], s);
+        s = fmaf(a[2], b[2], s);
+        s = fmaf(a[3], b[3], s);
+    }
+    logits[i] = s;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// EPL = experts held per lane (ceil(E / 64)).
+template <int EPL>
+__global__ __launch_bounds__(256) void route_select(const float *__restrict__ logits,
+                                                    const float *__restrict__ bias, int64_t T, int E, int k,
+                                                    int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
+                                                    float *__restrict__ part_p, int32_t *__restrict__ part_c)
+{
+    __shared__ float sp[4][EPL * 64];
+    __shared__ int sc[4][EPL * 64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+
+    float pacc[EPL];
+    int cacc[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        pacc[i] = 0.f;
+        cacc[i] = 0;
+    }
+
+    const int64_t tw0 = ((int64_t)blockIdx.x * 4 + wave) * kSelTokensPerWave;
+    for (int q = 0; q < kSelTokensPerWave; ++q) {
+        const int64_t t = tw0 + q;
+        if (t >= T)
+            break;
+        float l[EPL];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane + 64 * i;
+            l[i] = -INFINITY;
+            if (e < E)
+                l[i] = logits[t * E + e] + (bias ? bias[e] : 0.f);
+        }
+        float m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            m = fmaxf(m, l[i]);
+        m = wave_max(m);
+        float ex[EPL];
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            ex[i] = (lane + 64 * i < E) ? expf(l[i] - m) : 0.f;
+            s += ex[i];
+        }
+        s = wave_sum(s);
+        const float inv_s = 1.0f / s;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i)
+            pacc[i] += ex[i] * inv_s;
+
+        // top-k: k rounds of a wave arg-max on (logit desc, id asc)
+        uint32_t taken = 0;
+        for (int j = 0; j < k; ++j) {
+            float bv = -INFINITY;
+            int bi = 0x7FFFFFFF;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                const int e = lane + 64 * i;
+                if (e < E && !((taken >> i) & 1u) && (l[i] > bv || bi == 0x7FFFFFFF))
+                    bv = l[i], bi = e;
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const float ov = __shfl_xor(bv, o, 64);
+                const int oi = __shfl_xor(bi, o, 64);
+                if (ov > bv || (ov == bv && oi < bi))
+                    bv = ov, bi = oi;
+            }
+            if ((bi & 63) == lane) {
+                const int slot = bi >> 6;
+#pragma unroll
+                for (int i = 0; i < EPL; ++i)
+                    if (i == slot) {
+                        taken |= 1u << i;
+                        cacc[i] += 1;
+                        topk_idx[t * k + j] = bi;
+                        topk_w[t * k + j] = ex[i] * inv_s;
+                    }
+            }
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+        sp[wave][lane + 64 * i] = pacc[i];
+        sc[wave][lane + 64 * i] = cacc[i];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) {
+        float p = sp[0][e];
+        p += sp[1][e];
+        p += sp[2][e];
+        p += sp[3][e];
+        part_p[(int64_t)blockIdx.x * E + e] = p;
+        part_c[(int64_t)blockIdx.x * E + e] = sc[0][e] + sc[1][e] + sc[2][e] + sc[3][e];
+    }
+}
+
+// One block of 1024 threads; G threads per expert sum the block partials in a
+// fixed strided order, then the G partial sums are added in order.
+__global__ __launch_bounds__(1024) void route_finalize(const float *__restrict__ part_p,
+                                                       const int32_t *__restrict__ part_c, int nblk, int64_t T,
+                                                       int E, float alpha, int32_t *__restrict__ expert_count,
+                                                       float *__restrict__ f, float *__restrict__ P,
+                                                       float *__restrict__ l_aux)
+{
+    __shared__ double rp[1024];
+    __shared__ long long rc[1024];
+    __shared__ double terms[1024];
+    int G = 1;
+    while (G * 2 * E <= 1024)
+        G *= 2;
+    const int tid = threadIdx.x;
+    const int e = tid / G, g = tid % G;
+    double ps = 0.0;
+    long long cs = 0;
+    if (e < E) {
+        for (int b = g; b < nblk; b += G) {
+            ps += (double)part_p[(int64_t)b * E + e];
+            cs += part_c[(int64_t)b * E + e];
+        }
+    }
+    rp[tid] = ps;
+    rc[tid] = cs;
+    __syncthreads();
+    if (tid < E) {
+        double p = 0.0;
+        long long c = 0;
+        for (int q = 0; q < G; ++q) {
+            p += rp[tid * G + q];
+            c += rc[tid * G + q];
+        }
+        const float fe = T > 0 ? (float)c / (float)T : 0.f;
+        const float Pe = T > 0 ? (float)(p / (double)T) : 0.f;
+        if (expert_count)
+            expert_count[tid] = (int32_t)c;
+        if (f)
+            f[tid] = fe;
+        if (P)
+            P[tid] = Pe;
+        terms[tid] = (double)fe * (double)Pe;
+    }
+    __syncthreads();
+    if (tid == 0 && l_aux) {
+        double s = 0.0;
+        for (int q = 0; q < E; ++q)
+            s += terms[q];
+        l_aux[0] = (float)((double)alpha * s);
+    }
+}
+
+} // namespace
+
+static int select_blocks(int64_t T) { return (int)((T + kSelTokensPerBlock - 1) / kSelTokensPerBlock); }
+
+size_t route_ws_bytes(int64_t T, int E)
+{
+    const int nblk = select_blocks(T);
+    return align_up((size_t)T * E * sizeof(float)) + 2 * align_up((size_t)nblk * E * sizeof(float));
+}
+
+moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, const float *b_router,
+                          int64_t T, int d, int E, int k, float alpha, int32_t *topk_idx, float *topk_w,
+                          int32_t *expert_count, float *f, float *P, float *l_aux, void *ws,
+                          hipStream_t stream)
+{
+    const int nblk = select_blocks(T);
+    Carver cv{(char *)ws, 0};
+    float *logits = cv.take<float>((size_t)T * E);
+    float *part_p = cv.take<float>((size_t)nblk * E);
+    int32_t *part_c = cv.take<int32_t>((size_t)nblk * E);
+
+    if (T > 0) {
+        if (dt == MOE_BF16) {
+            const uint16_t *xb = (const uint16_t *)x;
+            if (E <= 16) {
+                dim3 g((unsigned)((T + 15) / 16), 1);
+                route_logits_mfma<1, 1><<<g, 256, 0, stream>>>(xb, w_router, T, d, E, logits);
+            } else if (E <= 32) {
+                dim3 g((unsigned)((T + 15) / 16), 1);
+                route_logits_mfma<2, 1><<<g, 256, 0, stream>>>(xb, w_router, T, d, E, logits);
+            } else if (E <= 64) {
+                dim3 g((unsigned)((T + 15) / 16), 1);
+                route_logits_mfma<4, 1><<<g, 256, 0, stream>>>(xb, w_router, T, d, E, logits);
+            } else {
+                dim3 g((unsigned)((T + 63) / 64), (unsigned)((E + 63) / 64));
+                route_logits_mfma<4, 4><<<g, 256, 0, stream>>>(xb, w_router, T, d, E, logits);
+            }
+        } else {
+            const int64_t n = T * E;
+            route_logits_f32<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>((const float *)x, w_router, T, d,
+                                                                             E, logits);
+        }
+        if (moe_status_t s = check_launch("route_logits"))
+            return s;
+        const int epl = (E + 63) / 64;
+        const dim3 g((unsigned)nblk);
+        switch (epl) {
+        case 1: route_select<1><<<g, 256, 0, stream>>>(logits, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+        case 2: route_select<2><<<g, 256, 0, stream>>>(logits, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+        case 3:
+        case 4: route_select<4><<<g, 256, 0, stream>>>(logits, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+        case 5: case 6: case 7: case 8:
+            route_select<8><<<g, 256, 0, stream>>>(logits, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+        default:
+            route_select<16><<<g, 256, 0, stream>>>(logits, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+        }
+        if (moe_status_t s = check_launch("route_select"))
+            return s;
+    }
+    route_finalize<<<1, 1024, 0, stream>>>(part_p, part_c, T > 0 ? nblk : 0, T, E, alpha, expert_count, f, P,
+                                           l_aux);
+    return check_launch("route_finalize");
+}
+
+} // namespace moe

@@ -233,3 +233,21 @@ def token_sample(T: int, n: int, seed: int = 1234, must_include=()) -> np.ndarra
     pick = g.choice(T, size=n, replace=False)
     pick = np.union1d(pick, np.asarray(list(must_include), dtype=np.int64))
     return np.sort(pick.astype(np.int64))
+
+
+def to_torch(a: Optional[np.ndarray], device=None):
+    """Host array -> torch tensor (uint16 bit patterns become bfloat16)."""
+    import torch
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(device) if device is not None else t
+
+
+def device_layer(inp: LayerInputs, device="cuda") -> dict:
+    """Every tensor of a layer copied to ``device`` (names as in LayerInputs)."""
+    names = ("x", "w_router", "b_router", "w1", "b1", "w2", "b2", "ws1", "bs1", "ws2", "bs2")
+    return {n: to_torch(getattr(inp, n), device) for n in names}
