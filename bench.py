@@ -1,0 +1,267 @@
+"""Benchmark of the MoE layer forward on one MI355X.
+
+A step is one moe_forward over one batch: route (router GEMM, softmax, top-k,
+load statistics), dispatch (capacity, drops, permutation), the expert FFN
+(grouped GEMM + GELU, grouped GEMM) and combine.  Inputs are seeded
+synthetic layers already resident in HBM.  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+The roofline entry covers the dominant kernel (the first grouped GEMM with
+the fused GELU): algorithmic flops of one launch (2 * rows * d * ffn, rows =
+the kept (token, expert) pairs of the run) over its average duration, timed
+with HIP events on the stream the library launches on.  The per-step value is
+timed separately on moe_forward itself, with no events inside the step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+DEFAULT_WORKLOAD = "mixtral8x7b-layer"
+
+
+def _kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "top_routing_expert_route_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or
+    None when the kernel source changed since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        with open(p) as f:
+            t = json.load(f)
+        e = t[workload][kernel]
+        if e.get("source_hash") != _kernel_source_hash():
+            return None
+        return e["bytes_per_launch"]
+    except (KeyError, ValueError, OSError):
+        return None
+
+
+def cpu_baseline(inp, budget_s: float = 15.0) -> dict:
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    routing, statistics and capacity over all T tokens, the expert FFN and
+    combine on a seeded token sample sized to about budget_s seconds."""
+    import numpy as np
+    import oracle
+    from top_routing_expert_route_amd import workloads as wl
+    w = inp.w
+    threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    r = oracle.route(inp.x, inp.w_router, inp.b_router, w.k, threads=threads, want_logits=False)
+    oracle.load_stats(r.topk_idx, r.probs, w.alpha)
+    dp = oracle.capacity(r.topk_idx, w.E, float(np.float32(w.capacity_factor)), w.expert_begin,
+                         w.num_local_experts)
+    t_route = time.perf_counter() - t0
+
+    def ffn(tokens):
+        s = time.perf_counter()
+        oracle.combine(inp.x, tokens, r.topk_idx, r.topk_w, dp.slot_row, inp.w1, inp.b1, inp.w2, inp.b2,
+                       w.expert_begin, inp.ws1, inp.bs1, inp.ws2, inp.bs2, threads=threads)
+        return time.perf_counter() - s
+
+    n = max(1, threads)
+    probe = ffn(wl.token_sample(w.T, n, seed=99))
+    per_tok = probe / n
+    n2 = int(min(w.T, max(n, (budget_s - probe) / max(per_tok, 1e-9))))
+    n2 = max(threads, n2 // threads * threads)
+    tok = wl.token_sample(w.T, n2, seed=100)
+    t_ffn = ffn(tok)
+    sec_per_token = t_route / w.T + t_ffn / len(tok)
+    return {"value": round(1.0 / sec_per_token, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "fp64 oracle: route+stats+capacity over all %d tokens (%.2f s), expert FFN+combine on a "
+                      "seeded sample of %d tokens (%.2f s); tokens/s = 1/(t_route/T + t_ffn/n)"
+                      % (w.T, t_route, len(tok), t_ffn)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (expert-parallel sharding is a "
+              "design note only). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from top_routing_expert_route_amd import accounting as acc
+    from top_routing_expert_route_amd import api
+    from top_routing_expert_route_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_probe:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 5}))
+        return
+
+    api.lib()  # fail loudly if the HIP library is missing
+    w = wl.get(args.workload)
+    inp = wl.make_layer(w, seed=0)
+    t = wl.device_layer(inp, dev)
+    dt = torch.bfloat16 if w.dtype == wl.BF16 else torch.float32
+    layer = api.Layer(w.T, w.d, w.E, w.k, w.ffn, dt, w.capacity_factor, w.expert_begin, w.num_local_experts,
+                      w.alpha, t["w_router"], t["b_router"], t["w1"], t["b1"], t["w2"], t["b2"], t["ws1"],
+                      t["bs1"], t["ws2"], t["bs2"], device=dev)
+    outs = layer.alloc_outputs()
+    x = t["x"]
+    y = torch.empty((w.T, w.d), dtype=dt, device=dev)
+
+    # ---- headline: K whole-layer steps of moe_forward ----
+    for _ in range(args.warmup):
+        layer.forward(x, y)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        layer.forward(x, y)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = w.T * args.steps / elapsed
+
+    # counts of the actual run
+    seg = outs["seg_offsets"].cpu().numpy()
+    rows = int(seg[-1])
+    per_expert = np.diff(seg)
+    slot_row = outs["slot_row"].cpu().numpy()
+    counts = acc.RunCounts(T=w.T, d=w.d, E=w.E, k=w.k, ffn=w.ffn, dtype=w.dtype, rows=rows,
+                           active_experts=int((per_expert > 0).sum()),
+                           tokens_with_rows=int((slot_row >= 0).any(axis=1).sum()), shared=w.shared_expert,
+                           has_router_bias=inp.b_router is not None)
+
+    # ---- per-stage timing with HIP events on the launch stream ----
+    stream = torch.cuda.current_stream(dev)
+    names = ["route", "dispatch", "gemm1_gelu", "gemm2", "shared", "combine"]
+    acc_ms = {n: 0.0 for n in names}
+    r_buf = {}
+    dp_ws = {}
+
+    def staged_step(record):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] if record else None
+        if record:
+            ev[0].record(stream)
+        r = api.moe_route(x, t["w_router"], t["b_router"], w.k, w.alpha)
+        if record:
+            ev[1].record(stream)
+        dp = api.moe_dispatch(x, r["topk_idx"], w.E, w.capacity_factor, w.expert_begin, w.num_local_experts)
+        if record:
+            ev[2].record(stream)
+        h = api.moe_grouped_gemm(dp["x_perm"], dp["seg_offsets"], t["w1"], t["b1"], 1,
+                                 out=dp_ws.setdefault("h", torch.empty((dp["max_rows"], w.ffn), dtype=dt,
+                                                                       device=dev)))
+        if record:
+            ev[3].record(stream)
+        yp = api.moe_grouped_gemm(h, dp["seg_offsets"], t["w2"], t["b2"], 0,
+                                  out=dp_ws.setdefault("yp", torch.empty((dp["max_rows"], w.d), dtype=dt,
+                                                                         device=dev)))
+        if record:
+            ev[4].record(stream)
+        ysh = None
+        if w.shared_expert:
+            hs = api.moe_grouped_gemm(x, None, t["ws1"].unsqueeze(0), None, 1)
+            ysh = api.moe_grouped_gemm(hs, None, t["ws2"].unsqueeze(0), None, 0)
+        if record:
+            ev[5].record(stream)
+        api.moe_combine(yp, dp["slot_row"], r["topk_w"], ysh, y=y)
+        if record:
+            ev[6].record(stream)
+        return ev
+
+    for _ in range(2):
+        staged_step(False)
+    torch.cuda.synchronize()
+    evs = [staged_step(True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for ev in evs:
+        for i, n in enumerate(names):
+            acc_ms[n] += ev[i].elapsed_time(ev[i + 1])
+    avg_us = {n: acc_ms[n] * 1e3 / args.steps for n in names}
+
+    def tflops(flops, us):
+        return flops / (us * 1e-6) / 1e12 if us > 0 else 0.0
+
+    def gbps(b, us):
+        return b / (us * 1e-6) / 1e9 if us > 0 else 0.0
+
+    g1_flops = acc.gemm1_flops(counts)
+    g1_tf = tflops(g1_flops, avg_us["gemm1_gelu"])
+    stages = {
+        "route": {"us": round(avg_us["route"], 2), "bytes": acc.route_bytes(counts),
+                  "hbm_frac": round(gbps(acc.route_bytes(counts), avg_us["route"]) / acc.PEAK_HBM_GBPS, 4)},
+        "dispatch": {"us": round(avg_us["dispatch"], 2), "bytes": acc.dispatch_bytes(counts),
+                     "hbm_frac": round(gbps(acc.dispatch_bytes(counts), avg_us["dispatch"]) / acc.PEAK_HBM_GBPS,
+                                       4)},
+        "gemm1_gelu": {"us": round(avg_us["gemm1_gelu"], 2), "flops": g1_flops,
+                       "mfma_frac": round(g1_tf / acc.PEAK_BF16_TFLOPS, 4)},
+        "gemm2": {"us": round(avg_us["gemm2"], 2), "flops": acc.gemm2_flops(counts),
+                  "mfma_frac": round(tflops(acc.gemm2_flops(counts), avg_us["gemm2"]) / acc.PEAK_BF16_TFLOPS, 4)},
+        "combine": {"us": round(avg_us["combine"], 2), "bytes": acc.combine_bytes(counts),
+                    "hbm_frac": round(gbps(acc.combine_bytes(counts), avg_us["combine"]) / acc.PEAK_HBM_GBPS, 4)},
+    }
+    if w.shared_expert:
+        stages["shared"] = {"us": round(avg_us["shared"], 2), "flops": acc.shared_flops(counts),
+                            "mfma_frac": round(tflops(acc.shared_flops(counts), avg_us["shared"]) /
+                                               acc.PEAK_BF16_TFLOPS, 4)}
+    staged_total = sum(avg_us.values())
+
+    result = {
+        "metric": "MoE layer tokens/sec (1 GPU)",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == wl.BF16 else "f32",
+        "data": "synthetic (seeded Gaussian layer, uniform routing; no trained weights)",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "ffn": w.ffn,
+                   "capacity_factor": w.capacity_factor, "num_local_experts": w.E_loc,
+                   "shared_expert": w.shared_expert, "router": "fp32", "rows": rows,
+                   "active_experts": counts.active_experts},
+        "roofline": {"bound": "mfma", "achieved": round(g1_tf, 2), "peak": acc.PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(g1_tf / acc.PEAK_BF16_TFLOPS, 4),
+                     "traffic": _traffic(w.name, "gemm1_gelu"),
+                     "kernel": "grouped_gemm_bf16 (first Linear + GELU)",
+                     "flops_per_launch": g1_flops, "avg_us": round(avg_us["gemm1_gelu"], 2)},
+        "stages": stages,
+        "staged_step_us": round(staged_total, 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -358,3 +358,30 @@ def test_route_bitwise_reproducible_and_stats_fixed_order():
     torch.cuda.synchronize()
     for k in r1:
         assert torch.equal(r1[k], r2[k]), k
+
+
+def test_gelu_epilogue_matches_fp64_erf():
+    """The first Linear's GELU (erf from Abramowitz & Stegun 7.1.26, |err| <=
+    1.5e-7) against 0.5 u (1 + erf(u / sqrt 2)) in float64: a one-hot weight
+    makes the fp32 GEMM output exactly GELU(u)."""
+    import math
+    u = torch.linspace(-9.0, 9.0, 4001, dtype=torch.float64)
+    rows = u.numel()
+    a = torch.zeros(rows, 8, dtype=torch.float32)
+    a[:, 0] = u.float()
+    w = torch.zeros(1, 8, 8, dtype=torch.float32)
+    w[0, :, 0] = 1.0
+    out = api.moe_grouped_gemm(a.to(DEV), None, w.to(DEV), None, 1)
+    torch.cuda.synchronize()
+    uu = a[:, 0].double()
+    ref = 0.5 * uu * (1.0 + torch.erf(uu / math.sqrt(2.0)))
+    err = (out[:, 0].cpu().double() - ref).abs()
+    assert (err <= 4e-7 * (1.0 + uu.abs())).all(), float(err.max())
+    # bf16 path: same function, output rounded to bf16
+    ab = a.to(torch.bfloat16)
+    wb = w.to(torch.bfloat16)
+    ob = api.moe_grouped_gemm(ab.to(DEV), None, wb.to(DEV), None, 1)
+    torch.cuda.synchronize()
+    ub = ab[:, 0].double()
+    refb = 0.5 * ub * (1.0 + torch.erf(ub / math.sqrt(2.0)))
+    assert ((ob[:, 0].cpu().double() - refb).abs() <= 2.0 ** -8 * refb.abs() + 1e-6).all()

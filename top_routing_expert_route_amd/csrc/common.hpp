@@ -38,10 +38,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
 }
 
-// Exact GELU, 0.5 u (1 + erf(u / sqrt 2)), with the device library's erff.
+// GELU in its erf form, 0.5 u (1 + erf(u / sqrt 2)).  erf comes from
+// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26
+// (|error| <= 1.5e-7 for x >= 0):
+//   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
+//   t = 1 / (1 + p x),
+// with erf(-x) = -erf(x).  With q = erfc(|u| / sqrt 2) / 2 this gives
+// GELU(u) = u - u q for u >= 0 and u q for u < 0.
 __device__ __forceinline__ float gelu_erf(float u)
 {
-    return 0.5f * u * (1.0f + erff(u * 0.70710678118654752f));
+    const float x = fabsf(u) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+    float poly = fmaf(1.061405429f, t, -1.453152027f);
+    poly = fmaf(poly, t, 1.421413741f);
+    poly = fmaf(poly, t, -0.284496736f);
+    poly = fmaf(poly, t, 0.254829592f);
+    poly *= t;
+    const float q = 0.5f * poly * __expf(-x * x);
+    return u >= 0.f ? u - u * q : u * q;
 }
 
 // ------------------------------------------------------------ workspaces --

@@ -259,6 +259,299 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_bf16(const uint16_t *__re
     }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile bf16 kernel: 256 (features) x 256 (rows) per block, four waves
+// of 128 x 128 (4 x 4 MFMA 32x32x16 tiles, 256 fp32 accumulators per lane,
+// held in AGPRs).
+//
+// Global -> LDS copies are buffer_load_dwordx4 ... lds (LDS DMA): each lane's
+// 16 bytes land at M0 + 16 * lane, so a wave fills 1 KB of contiguous LDS per
+// instruction and the XOR swizzle of the 16-byte chunks is applied on the
+// global side.  The copies are issued as inline assembly so that the
+// compiler's conservative wait-for-all-DMA before every LDS read does not
+// serialise them; the kernel keeps its own vmcnt accounting: STAGES-1 K
+// steps are in flight while one computes.  They have no output registers.
+//
+// LDS on gfx950 serves a ds_read_b128 16 lanes at a time over 64 banks
+// (256 bytes): rows of BK bf16 are swizzled so that the 16 rows read by one
+// group of lanes at the same logical chunk hit 16 distinct bank groups.
+// Requires K % BK == 0; rows past the weight matrix or the segment end read
+// as zeros (buffer range checking); row sub-tiles past the segment end skip
+// their MFMAs; stores are masked.
+// ---------------------------------------------------------------------------
+constexpr int kL = 256; // tile edge
+
+typedef __attribute__((address_space(3))) void lds_void;
+// Word 3 of a raw (unformatted, stride 0) buffer resource on gfx9-family GPUs.
+constexpr int kRsrcWord3 = 0x00020000;
+// A scalar offset past every tile's buffer range: such a copy reads zeros.
+constexpr uint32_t kOutOfRange = 0x40000000u;
+
+template <int N> __device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Logical 16-byte chunk stored at physical chunk p of a row: p ^ f(row).
+template <int BK> __device__ __forceinline__ int swz(int row)
+{
+    return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// LDS-DMA copy: 16 bytes per lane from buffer `rsrc` at voff + soff into LDS
+// at m0 + 16 * lane.  Written as inline assembly so that the compiler's
+// wait-count pass does not track it (it would wait for every copy before
+// any LDS read); the kernel keeps the vmcnt accounting itself.  The
+// instruction writes no registers.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t m0)
+{
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                   "{m0}"(__builtin_amdgcn_readfirstlane(m0))
+                 : "memory");
+}
+
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes)
+{
+    const uint64_t a = (uint64_t)base;
+    i32x4 r;
+    r[0] = (int)(uint32_t)a;
+    r[1] = (int)((uint32_t)(a >> 32) & 0xFFFFu);
+    r[2] = (int)bytes;
+    r[3] = kRsrcWord3;
+    return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+// One K step of a 256x256 tile: MFMAs on stage `cur` (already in LDS) while
+// the LDS-DMA copies of a later K step fill the stage at LDS byte address
+// `nxt`.  The step is cut into chunks of 4 MFMAs + 2 LDS reads of the next
+// 16-wide sub-step; one copy is issued after each chunk, so the copies
+// trickle out at the rate the address unit drains them instead of stalling
+// the wave in a burst.
+template <int BK, int NBV>
+__device__ __forceinline__ void k_step(const uint16_t *cur, uint32_t nxt, f32x16 (&acc)[4][4], i32x4 rw, i32x4 ra,
+                                       uint32_t vbase, uint32_t so_k, uint32_t row_bytes, int wave, int wn, int wm,
+                                       int r32, int khalf, int sw)
+{
+    constexpr int CPR = BK / 8, RPI = 64 / CPR, NQ = kL / (4 * RPI), KS = BK / 16;
+    static_assert(2 * NQ == 4 * KS, "one copy per chunk");
+    const uint16_t *sW = cur;
+    const uint16_t *sA = cur + kL * BK;
+    bf16x8 fa[2][4], fb[2][4];
+    auto read_a = [&](int ks, int buf, int a) {
+        const int ch = ((ks * 2 + khalf) ^ sw) * 8;
+        fa[buf][a] = *reinterpret_cast<const bf16x8 *>(sW + (wn * 128 + a * 32 + r32) * BK + ch);
+    };
+    auto read_b = [&](int ks, int buf, int b) {
+        const int ch = ((ks * 2 + khalf) ^ sw) * 8;
+        fb[buf][b] = *reinterpret_cast<const bf16x8 *>(sA + (wm * 128 + b * 32 + r32) * BK + ch);
+    };
+    auto dma = [&](int i) { // copy i of 2*NQ: W rows for even i, A rows for odd i
+        const int q = i >> 1;
+        const uint32_t R = (uint32_t)((4 * q + wave) * RPI);
+        const uint32_t so = (uint32_t)q * (4u * RPI) * row_bytes + so_k;
+        dma16((i & 1) ? ra : rw, vbase, so, nxt + (uint32_t)((i & 1) * (kL * BK) + R * BK) * 2u);
+    };
+    if (NBV > 0) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+            read_a(0, 0, a);
+#pragma unroll
+        for (int b = 0; b < NBV; ++b)
+            read_b(0, 0, b);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if (NBV > 0) {
+#pragma unroll
+                for (int b = 0; b < NBV; ++b)
+                    acc[c][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][c], fb[ks & 1][b], acc[c][b], 0,
+                                                                        0, 0);
+                if (ks + 1 < KS) {
+                    read_a(ks + 1, (ks + 1) & 1, c);
+                    if (c < NBV)
+                        read_b(ks + 1, (ks + 1) & 1, c);
+                }
+                if (NBV == 4) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    if (ks + 1 < KS)
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    if (ks + 1 < KS)
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            dma(ks * 4 + c);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+template <int BK, int STAGES, int NBV, bool GELU, bool BIAS>
+__device__ __forceinline__ void tile_256(const uint16_t *__restrict__ A, const uint16_t *__restrict__ wseg,
+                                         const uint16_t *__restrict__ bseg, uint16_t *__restrict__ C,
+                                         uint16_t *smem, int64_t row0, int64_t row_end, int n0, int N, int K)
+{
+    constexpr int CPR = BK / 8;            // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;          // rows filled per DMA instruction (1 KB)
+    constexpr int NQ = kL / (4 * RPI);     // DMA instructions per operand per wave
+    constexpr int STAGE = 2 * kL * BK;     // bf16 elements per stage (W then A)
+    constexpr int PER_STAGE = 2 * NQ;      // DMA instructions per thread per stage
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wn = wave & 1, wm = wave >> 1;
+    const int r32 = lane & 31, khalf = lane >> 5;
+
+    // Instruction q of this wave fills LDS rows R = (4q + wave) * RPI ..
+    // R + RPI - 1; lane -> row R + lane / CPR, physical chunk lane % CPR,
+    // which holds logical chunk (lane % CPR) ^ swizzle(row).  The byte offset
+    // of that row is vbase + q * 4 * RPI * K * 2 (the q part is scalar).  The
+    // buffer resources cover exactly the tile's valid rows: rows past the
+    // weight matrix or the segment end read as zeros.
+    const uint32_t row_bytes = (uint32_t)K * 2u;
+    const int lrow = lane / CPR;
+    const int prow = wave * RPI + lrow;
+    const int lchunk = (lane % CPR) ^ swz<BK>(prow);
+    const uint32_t vbase = (uint32_t)prow * row_bytes + (uint32_t)lchunk * 16u;
+    const int wrows = min(kL, N - n0);
+    const int arows = (int)(row_end - row0);
+    const i32x4 rw = make_rsrc(wseg + (int64_t)n0 * K, (uint32_t)wrows * row_bytes);
+    const i32x4 ra = make_rsrc(A + row0 * K, (uint32_t)arows * row_bytes);
+    const uint32_t lds0 = lds_addr(smem);
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[a][b][v] = 0.f;
+
+    const int KT = K / BK;
+    const int sw = swz<BK>(r32);
+    // Prologue: stages 0 .. STAGES-2 (a copy past K reads out of range: zeros).
+    for (int p = 0; p < STAGES - 1; ++p) {
+        const uint32_t dst = lds0 + (uint32_t)(p * STAGE) * 2u;
+        const uint32_t so_k = p < KT ? (uint32_t)p * (BK * 2) : kOutOfRange;
+#pragma unroll
+        for (int i = 0; i < 2 * NQ; ++i) {
+            const int q = i >> 1;
+            const uint32_t R = (uint32_t)((4 * q + wave) * RPI);
+            const uint32_t so = (uint32_t)q * (4u * RPI) * row_bytes + so_k;
+            dma16((i & 1) ? ra : rw, vbase, so, dst + (uint32_t)((i & 1) * (kL * BK) + R * BK) * 2u);
+        }
+    }
+    wait_vmcnt<(STAGES - 2) * PER_STAGE>();
+    __syncthreads();
+
+    for (int kt = 0; kt < KT; ++kt) {
+        const int fill = kt + STAGES - 1;
+        const uint32_t so_k = fill < KT ? (uint32_t)fill * (BK * 2) : kOutOfRange;
+        k_step<BK, NBV>(smem + (kt % STAGES) * STAGE, lds0 + (uint32_t)((fill % STAGES) * STAGE) * 2u, acc, rw, ra,
+                        vbase, so_k, row_bytes, wave, wn, wm, r32, khalf, sw);
+        // Stage kt+1 must have landed; the STAGES-2 stages issued after it
+        // may stay in flight.
+        wait_vmcnt<(STAGES - 2) * PER_STAGE>();
+        __syncthreads();
+    }
+    wait_vmcnt<0>(); // the zero-fill copies of the last steps must land before the next tile's copies
+
+    // Epilogue: accumulators are read unconditionally and only the stores are
+    // predicated, so no accumulator has to live outside its AGPR.
+#pragma unroll
+    for (int b = 0; b < NBV; ++b) {
+        const int64_t row = row0 + wm * 128 + b * 32 + r32;
+        const bool row_ok = row < row_end;
+        uint16_t *crow = C + (row_ok ? row : row0) * N;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * 128 + a * 32 + 8 * g + 4 * khalf;
+                const bool ok = row_ok && n < N;
+                float v0 = acc[a][b][4 * g + 0], v1 = acc[a][b][4 * g + 1];
+                float v2 = acc[a][b][4 * g + 2], v3 = acc[a][b][4 * g + 3];
+                if (BIAS) {
+                    const uint2 bb = *reinterpret_cast<const uint2 *>(bseg + (n < N ? n : 0));
+                    v0 += bf16_bits_to_f32(bb.x & 0xFFFFu);
+                    v1 += bf16_bits_to_f32(bb.x >> 16);
+                    v2 += bf16_bits_to_f32(bb.y & 0xFFFFu);
+                    v3 += bf16_bits_to_f32(bb.y >> 16);
+                }
+                if (GELU) {
+                    v0 = gelu_erf(v0);
+                    v1 = gelu_erf(v1);
+                    v2 = gelu_erf(v2);
+                    v3 = gelu_erf(v3);
+                }
+                uint2 o;
+                o.x = pack_bf16x2(v0, v1);
+                o.y = pack_bf16x2(v2, v3);
+                if (ok)
+                    *reinterpret_cast<uint2 *>(crow + n) = o;
+            }
+        }
+    }
+}
+
+template <int BK, int STAGES, bool GELU, bool BIAS>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_256(const uint16_t *__restrict__ A,
+                                                                const int32_t *__restrict__ seg, int S,
+                                                                int64_t max_rows, const uint16_t *__restrict__ W,
+                                                                const uint16_t *__restrict__ bias,
+                                                                uint16_t *__restrict__ C, int N, int K)
+{
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * 2 * kL * BK];
+    __shared__ int tb[kMaxSeg + 1];
+    build_tile_prefix<kL>(seg, S, max_rows, tb);
+
+    const int wm = (threadIdx.x >> 6) >> 1;
+    const int NT = (N + kL - 1) / kL;
+    const int64_t total = (int64_t)tb[S] * NT;
+    const int xcd = blockIdx.x % kXcds;
+    const int per = gridDim.x / kXcds;
+    const int j = blockIdx.x / kXcds;
+    const int64_t rlo = total * xcd / kXcds, rhi = total * (xcd + 1) / kXcds;
+
+    for (int64_t L = rlo + j; L < rhi; L += per) {
+        const int s = find_segment(tb, S, NT, L);
+        const int mt_s = tb[s + 1] - tb[s];
+        const int64_t local = L - (int64_t)tb[s] * NT;
+        const int n_tile = (int)(local / mt_s);
+        const int m_tile = (int)(local % mt_s);
+        int64_t seg_lo, seg_hi;
+        seg_bounds(seg, s, max_rows, seg_lo, seg_hi);
+        const int64_t row0 = seg_lo + (int64_t)m_tile * kL;
+        const int64_t row_end = min(row0 + kL, seg_hi);
+        const int n0 = n_tile * kL;
+        const uint16_t *wseg = W + (int64_t)s * N * K;
+        const uint16_t *bseg = bias ? bias + (int64_t)s * N : nullptr;
+        const int64_t left = row_end - (row0 + wm * 128);
+        const int nbv = left <= 0 ? 0 : (left >= 128 ? 4 : (int)((left + 31) / 32));
+        switch (nbv) {
+        case 4: tile_256<BK, STAGES, 4, GELU, BIAS>(A, wseg, bseg, C, smem, row0, row_end, n0, N, K); break;
+        case 3: tile_256<BK, STAGES, 3, GELU, BIAS>(A, wseg, bseg, C, smem, row0, row_end, n0, N, K); break;
+        case 2: tile_256<BK, STAGES, 2, GELU, BIAS>(A, wseg, bseg, C, smem, row0, row_end, n0, N, K); break;
+        case 1: tile_256<BK, STAGES, 1, GELU, BIAS>(A, wseg, bseg, C, smem, row0, row_end, n0, N, K); break;
+        default: tile_256<BK, STAGES, 0, GELU, BIAS>(A, wseg, bseg, C, smem, row0, row_end, n0, N, K); break;
+        }
+        __syncthreads(); // the next tile's copies overwrite stages still read here
+    }
+}
+
 // fp32: 64 x 64 tiles, 4 x 4 per thread, K slices of 16 through LDS.
 template <bool GELU>
 __global__ __launch_bounds__(256) void grouped_gemm_f32(const float *__restrict__ A, const int32_t *__restrict__ seg,
@@ -342,6 +635,34 @@ int device_cus()
     return cached_cus;
 }
 
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 32
+#endif
+#ifndef MOE_GEMM_STAGES
+#define MOE_GEMM_STAGES 3
+#endif
+constexpr int kLargeBK = MOE_GEMM_BK, kLargeStages = MOE_GEMM_STAGES;
+
+moe_status_t run_bf16_256(const void *a, const int32_t *seg, int S, int64_t max_rows, int N, int K, const void *w,
+                         const void *bias, int act, void *out, hipStream_t stream)
+{
+    const int64_t tiles_bound = ((max_rows + kL - 1) / kL + S) * (int64_t)((N + kL - 1) / kL);
+    int64_t grid = (int64_t)device_cus();
+    grid = (grid + kXcds - 1) / kXcds * kXcds;
+    const int64_t need = (tiles_bound + kXcds - 1) / kXcds * kXcds;
+    if (need < grid)
+        grid = need;
+    if (grid < kXcds)
+        grid = kXcds;
+    auto *k = act == 1 ? (bias ? grouped_gemm_bf16_256<kLargeBK, kLargeStages, true, true>
+                               : grouped_gemm_bf16_256<kLargeBK, kLargeStages, true, false>)
+                       : (bias ? grouped_gemm_bf16_256<kLargeBK, kLargeStages, false, true>
+                               : grouped_gemm_bf16_256<kLargeBK, kLargeStages, false, false>);
+    k<<<(unsigned)grid, 256, 0, stream>>>((const uint16_t *)a, seg, S, max_rows, (const uint16_t *)w,
+                                          (const uint16_t *)bias, (uint16_t *)out, N, K);
+    return check_launch("grouped_gemm_bf16_256");
+}
+
 template <int BN, int BM>
 moe_status_t run_bf16(const void *a, const int32_t *seg, int S, int64_t max_rows, int N, int K, const void *w,
                       const void *bias, int act, void *out, hipStream_t stream)
@@ -372,8 +693,11 @@ moe_status_t launch_grouped_gemm(const void *a, const int32_t *seg_offsets, int 
     if (max_rows == 0)
         return MOE_OK;
     const int S = seg_offsets ? num_segments : 1;
-    if (dt == MOE_BF16)
+    if (dt == MOE_BF16) {
+        if (K % kLargeBK == 0)
+            return run_bf16_256(a, seg_offsets, S, max_rows, N, K, w, bias, activation, out, stream);
         return run_bf16<128, 128>(a, seg_offsets, S, max_rows, N, K, w, bias, activation, out, stream);
+    }
     const dim3 g((unsigned)((N + 63) / 64), (unsigned)((max_rows + 63) / 64 + S));
     if (activation == 1)
         grouped_gemm_f32<true><<<g, 256, 0, stream>>>((const float *)a, seg_offsets, S, max_rows, (const float *)w,
