@@ -158,20 +158,28 @@ moe_status_t moe_dispatch(const void *x, moe_dtype_t dtype, const int32_t *topk_
  * FFN of "MoE Layer Structure".  For each segment s (rows seg_offsets[s] ..
  * seg_offsets[s+1] - 1 of a):
  *   out[r, n] = act( sum_k a[r, k] * w[s, n, k] + bias[s, n] )
- * with act = identity (activation 0) or exact GELU 0.5*u*(1 + erf(u/sqrt 2))
- * (activation 1).  Accumulation is fp32; bf16 outputs are rounded to nearest
- * even.  Rows outside every segment are not written.
+ * with act = identity (activation 0) or GELU 0.5*u*(1 + erf(u/sqrt 2))
+ * (activation 1; erf to within 1.5e-7).  Accumulation is fp32; bf16 outputs
+ * are rounded to nearest even.  Rows outside every segment are not written.
  *
  * a [max_rows, K], w [num_segments, N, K], bias [num_segments, N] or NULL,
  * out [max_rows, N], all in dtype.  seg_offsets [num_segments + 1] on the
  * device, non-decreasing; offsets are clamped to [0, max_rows].
  * seg_offsets = NULL means one segment covering rows 0 .. max_rows - 1.
+ * ws (optional, may be NULL): device scratch of at least
+ * moe_grouped_gemm_workspace_size() bytes.  With it, the tiles of a last,
+ * partly filled round are split along K over the idle compute units and
+ * their fp32 partial sums are added in a fixed order (results stay bitwise
+ * reproducible); without it every tile runs whole.
  * Errors: INVALID_ARG for sizes < 1 (max_rows = 0 is a no-op), NULL a, w or
- * out; UNSUPPORTED for N or K not a multiple of 8, activation not 0 or 1.
+ * out, misaligned buffers; UNSUPPORTED for N or K not a multiple of 8,
+ * activation not 0 or 1, more than 1024 segments.
  * ------------------------------------------------------------------------ */
+size_t moe_grouped_gemm_workspace_size(void);
 moe_status_t moe_grouped_gemm(const void *a, const int32_t *seg_offsets, int num_segments,
                               int64_t max_rows, int N, int K, moe_dtype_t dtype, const void *w,
-                              const void *bias, int activation, void *out, hipStream_t stream);
+                              const void *bias, int activation, void *out, void *ws, size_t ws_bytes,
+                              hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * moe_expert_ffn - the expert FFN of "MoE Layer Structure" on every segment:
@@ -179,13 +187,14 @@ moe_status_t moe_grouped_gemm(const void *a, const int32_t *seg_offsets, int num
  *   y_perm = h . w2[s]^T + b2[s]                [rows, d]
  * x_perm [max_rows, d], w1 [S, ffn, d], b1 [S, ffn] or NULL, w2 [S, d, ffn],
  * b2 [S, d] or NULL, h [max_rows, ffn] (scratch, written), y_perm
- * [max_rows, d]; S = num_segments.  seg_offsets as in moe_grouped_gemm.
+ * [max_rows, d]; S = num_segments.  seg_offsets and ws as in
+ * moe_grouped_gemm (the two layers share ws one after the other).
  * Errors: as moe_grouped_gemm, for both layers.
  * ------------------------------------------------------------------------ */
 moe_status_t moe_expert_ffn(const void *x_perm, const int32_t *seg_offsets, int num_segments,
                             int64_t max_rows, int d, int ffn, moe_dtype_t dtype, const void *w1,
                             const void *b1, const void *w2, const void *b2, void *h, void *y_perm,
-                            hipStream_t stream);
+                            void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * moe_combine - the weighted sum of "MoE Layer Structure", back at each

@@ -108,14 +108,19 @@ def test_dispatch_rejects_bad_arguments(lib):
 def test_gemm_and_combine_reject_bad_arguments(lib):
     from top_routing_expert_route_amd import api
     P = FAKE
-    assert lib.moe_grouped_gemm(P, P, 4, 100, 60, 64, 1, P, None, 1, P, None) == api.MOE_ERR_UNSUPPORTED
-    assert lib.moe_grouped_gemm(P, P, 4, 100, 64, 64, 1, P, None, 2, P, None) == api.MOE_ERR_UNSUPPORTED
-    assert lib.moe_grouped_gemm(P, P, 0, 100, 64, 64, 1, P, None, 0, P, None) == api.MOE_ERR_INVALID_ARG
-    assert lib.moe_grouped_gemm(P, P, 2000, 100, 64, 64, 1, P, None, 0, P, None) == api.MOE_ERR_UNSUPPORTED
-    assert lib.moe_grouped_gemm(None, P, 4, 100, 64, 64, 1, P, None, 0, P, None) == api.MOE_ERR_INVALID_ARG
+    g = lambda *a: lib.moe_grouped_gemm(*a, None, 0, None)
+    assert g(P, P, 4, 100, 60, 64, 1, P, None, 1, P) == api.MOE_ERR_UNSUPPORTED
+    assert g(P, P, 4, 100, 64, 64, 1, P, None, 2, P) == api.MOE_ERR_UNSUPPORTED
+    assert g(P, P, 0, 100, 64, 64, 1, P, None, 0, P) == api.MOE_ERR_INVALID_ARG
+    assert g(P, P, 2000, 100, 64, 64, 1, P, None, 0, P) == api.MOE_ERR_UNSUPPORTED
+    assert g(None, P, 4, 100, 64, 64, 1, P, None, 0, P) == api.MOE_ERR_INVALID_ARG
+    assert lib.moe_grouped_gemm(P, P, 4, 100, 64, 64, 1, P, None, 0, P, P + 4, 1 << 30, None) \
+        == api.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(P, 10, P, P, None, 4, 64, 33, 1, P, None) == api.MOE_ERR_UNSUPPORTED
     assert lib.moe_combine(P, 10, None, P, None, 4, 64, 2, 1, P, None) == api.MOE_ERR_INVALID_ARG
-    assert lib.moe_expert_ffn(P, P, 4, 100, 64, 100, 1, P, None, P, None, P, P, None) == api.MOE_ERR_UNSUPPORTED
+    assert lib.moe_expert_ffn(P, P, 4, 100, 64, 100, 1, P, None, P, None, P, P, None, 0, None) \
+        == api.MOE_ERR_UNSUPPORTED
+    assert lib.moe_grouped_gemm_workspace_size() > 0
 
 
 def test_forward_rejects_bad_arguments(lib):

@@ -385,3 +385,26 @@ def test_gelu_epilogue_matches_fp64_erf():
     ub = ab[:, 0].double()
     refb = 0.5 * ub * (1.0 + torch.erf(ub / math.sqrt(2.0)))
     assert ((ob[:, 0].cpu().double() - refb).abs() <= 2.0 ** -8 * refb.abs() + 1e-6).all()
+
+
+def test_grouped_gemm_split_tail_matches_whole_tiles():
+    """With a workspace, tail tiles are split along K and reduced in a fixed
+    order: equal to the unsplit result within bf16 rounding, and bitwise
+    reproducible."""
+    g = torch.Generator().manual_seed(7)
+    sizes = [700, 300, 1000]           # 3 + 2 + 4 row tiles of 256
+    rows, K, N = sum(sizes), 1024, 512
+    a = torch.randn(rows, K, generator=g).to(torch.bfloat16).to(DEV)
+    w = (torch.randn(3, N, K, generator=g) / K ** 0.5).to(torch.bfloat16).to(DEV)
+    b = (torch.randn(3, N, generator=g) * 0.1).to(torch.bfloat16).to(DEV)
+    seg = torch.tensor(np.concatenate([[0], np.cumsum(sizes)]), dtype=torch.int32, device=DEV)
+    whole = api.moe_grouped_gemm(a, seg, w, b, 1, use_ws=False)
+    split1 = api.moe_grouped_gemm(a, seg, w, b, 1)
+    split2 = api.moe_grouped_gemm(a, seg, w, b, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(split1.view(torch.int16), split2.view(torch.int16))
+    assert rel_err(split1.float().cpu().numpy(), whole.float().cpu().numpy()) <= 1e-2
+    ref = torch.cat([torch.nn.functional.gelu(a[lo:hi].double() @ w[s].double().T + b[s].double(),
+                                              approximate="none")
+                     for s, (lo, hi) in enumerate(zip(seg[:-1].tolist(), seg[1:].tolist()))])
+    assert rel_err(split1.float().cpu().numpy(), ref.cpu().numpy()) <= 1e-2

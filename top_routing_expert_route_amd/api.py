@@ -48,8 +48,8 @@ class Outputs(ctypes.Structure):
 
 
 EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_error", "moe_max_rows", "moe_route_workspace_size",
-           "moe_route", "moe_dispatch_workspace_size", "moe_dispatch", "moe_grouped_gemm", "moe_expert_ffn",
-           "moe_combine", "moe_forward_workspace_size", "moe_forward"]
+           "moe_route", "moe_dispatch_workspace_size", "moe_dispatch", "moe_grouped_gemm_workspace_size",
+           "moe_grouped_gemm", "moe_expert_ffn", "moe_combine", "moe_forward_workspace_size", "moe_forward"]
 
 _lib = None
 
@@ -74,9 +74,10 @@ def lib():
     L.moe_dispatch_workspace_size.argtypes, L.moe_dispatch_workspace_size.restype = [I64, I, I], SZ
     L.moe_dispatch.argtypes = [P, I, P, I64, I, I, I, F, I, I, P, P, P, P, P, I64, P, P, SZ, P]
     L.moe_dispatch.restype = I
-    L.moe_grouped_gemm.argtypes = [P, P, I, I64, I, I, I, P, P, I, P, P]
+    L.moe_grouped_gemm_workspace_size.argtypes, L.moe_grouped_gemm_workspace_size.restype = [], SZ
+    L.moe_grouped_gemm.argtypes = [P, P, I, I64, I, I, I, P, P, I, P, P, SZ, P]
     L.moe_grouped_gemm.restype = I
-    L.moe_expert_ffn.argtypes = [P, P, I, I64, I, I, I, P, P, P, P, P, P, P]
+    L.moe_expert_ffn.argtypes = [P, P, I, I64, I, I, I, P, P, P, P, P, P, P, SZ, P]
     L.moe_expert_ffn.restype = I
     L.moe_combine.argtypes = [P, I64, P, P, P, I64, I, I, I, P, P]
     L.moe_combine.restype = I
@@ -171,30 +172,46 @@ def moe_dispatch(x: Optional[torch.Tensor], topk_idx: torch.Tensor, E: int, capa
     return out
 
 
+_gemm_ws = {}
+
+
+def gemm_workspace(device) -> torch.Tensor:
+    """A cached device scratch buffer for the grouped GEMM's split tail."""
+    dev = torch.device(device)
+    if dev not in _gemm_ws:
+        _gemm_ws[dev] = _ws(lib().moe_grouped_gemm_workspace_size(), dev)
+    return _gemm_ws[dev]
+
+
 def moe_grouped_gemm(a: torch.Tensor, seg_offsets: Optional[torch.Tensor], w: torch.Tensor,
-                     bias: Optional[torch.Tensor], activation: int, out: Optional[torch.Tensor] = None
-                     ) -> torch.Tensor:
+                     bias: Optional[torch.Tensor], activation: int, out: Optional[torch.Tensor] = None,
+                     ws: Optional[torch.Tensor] = None, use_ws: bool = True) -> torch.Tensor:
     rows, K = a.shape
     S, N, K2 = w.shape
     assert K2 == K
     if out is None:
         out = torch.empty((rows, N), dtype=a.dtype, device=a.device)
+    if ws is None and use_ws:
+        ws = gemm_workspace(a.device)
     nseg = S if seg_offsets is not None else 1
     check(lib().moe_grouped_gemm(_p(a), _p(seg_offsets), nseg, rows, N, K, _dt(a), _p(w), _p(bias), activation,
-                                 _p(out), _stream(a.device)))
+                                 _p(out), _p(ws), 0 if ws is None else ws.numel(), _stream(a.device)))
     return out
 
 
 def moe_expert_ffn(x_perm: torch.Tensor, seg_offsets: torch.Tensor, w1, b1, w2, b2,
-                   h: Optional[torch.Tensor] = None, y_perm: Optional[torch.Tensor] = None):
+                   h: Optional[torch.Tensor] = None, y_perm: Optional[torch.Tensor] = None,
+                   use_ws: bool = True):
     rows, d = x_perm.shape
     S, ffn, _ = w1.shape
     if h is None:
         h = torch.empty((rows, ffn), dtype=x_perm.dtype, device=x_perm.device)
     if y_perm is None:
         y_perm = torch.empty((rows, d), dtype=x_perm.dtype, device=x_perm.device)
+    ws = gemm_workspace(x_perm.device) if use_ws else None
     check(lib().moe_expert_ffn(_p(x_perm), _p(seg_offsets), S, rows, d, ffn, _dt(x_perm), _p(w1), _p(b1), _p(w2),
-                               _p(b2), _p(h), _p(y_perm), _stream(x_perm.device)))
+                               _p(b2), _p(h), _p(y_perm), _p(ws), 0 if ws is None else ws.numel(),
+                               _stream(x_perm.device)))
     return h, y_perm
 
 

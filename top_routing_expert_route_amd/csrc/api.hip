@@ -141,7 +141,8 @@ size_t elem_size(moe_dtype_t dt) { return dt == MOE_BF16 ? 2 : 4; }
 struct ForwardWs {
     int32_t *topk_idx, *expert_count, *seg_offsets, *kept_count, *slot_row, *row_src, *n_dropped;
     float *topk_w, *f, *P, *l_aux;
-    void *route_ws, *dispatch_ws, *x_perm, *h, *y_perm, *y_sh;
+    void *route_ws, *dispatch_ws, *gemm_ws, *x_perm, *h, *y_perm, *y_sh;
+    size_t gemm_ws_bytes;
     size_t bytes;
 };
 
@@ -169,6 +170,8 @@ ForwardWs carve_forward(const moe_problem_t *p, const moe_outputs_t *out, void *
     w.row_src = out->row_src ? out->row_src : cv.take<int32_t>((size_t)max_rows);
     w.n_dropped = out->n_dropped;
     w.dispatch_ws = cv.take<char>(dispatch_ws_bytes(p->T, p->k, E_loc));
+    w.gemm_ws_bytes = p->dtype == MOE_BF16 ? gemm_ws_bytes() : 0;
+    w.gemm_ws = cv.take<char>(w.gemm_ws_bytes);
     w.x_perm = cv.take<char>((size_t)max_rows * p->d * es);
     const int64_t h_rows = p->has_shared && p->T > max_rows ? p->T : max_rows;
     w.h = cv.take<char>((size_t)h_rows * p->ffn * es);
@@ -254,20 +257,25 @@ moe_status_t moe_dispatch(const void *x, moe_dtype_t dtype, const int32_t *topk_
                            kept_count, slot_row, row_src, x_perm, max_rows, n_dropped, ws, stream);
 }
 
+size_t moe_grouped_gemm_workspace_size(void) { return gemm_ws_bytes(); }
+
 moe_status_t moe_grouped_gemm(const void *a, const int32_t *seg_offsets, int num_segments, int64_t max_rows, int N,
                               int K, moe_dtype_t dtype, const void *w, const void *bias, int activation, void *out,
-                              hipStream_t stream)
+                              void *ws, size_t ws_bytes, hipStream_t stream)
 {
     clear_error();
     if (moe_status_t s = check_gemm_args(a, seg_offsets, num_segments, max_rows, N, K, dtype, w, bias, activation,
                                          out, "grouped_gemm"))
         return s;
-    return launch_grouped_gemm(a, seg_offsets, num_segments, max_rows, N, K, dtype, w, bias, activation, out, stream);
+    if (!aligned16(ws))
+        return fail(MOE_ERR_INVALID_ARG, "grouped_gemm: ws must be 16-byte aligned");
+    return launch_grouped_gemm(a, seg_offsets, num_segments, max_rows, N, K, dtype, w, bias, activation, out, ws,
+                               ws_bytes, stream);
 }
 
 moe_status_t moe_expert_ffn(const void *x_perm, const int32_t *seg_offsets, int num_segments, int64_t max_rows,
                             int d, int ffn, moe_dtype_t dtype, const void *w1, const void *b1, const void *w2,
-                            const void *b2, void *h, void *y_perm, hipStream_t stream)
+                            const void *b2, void *h, void *y_perm, void *ws, size_t ws_bytes, hipStream_t stream)
 {
     clear_error();
     if (moe_status_t s = check_gemm_args(x_perm, seg_offsets, num_segments, max_rows, ffn, d, dtype, w1, b1, 1, h,
@@ -276,10 +284,13 @@ moe_status_t moe_expert_ffn(const void *x_perm, const int32_t *seg_offsets, int 
     if (moe_status_t s = check_gemm_args(h, seg_offsets, num_segments, max_rows, d, ffn, dtype, w2, b2, 0, y_perm,
                                          "expert_ffn (second Linear)"))
         return s;
+    if (!aligned16(ws))
+        return fail(MOE_ERR_INVALID_ARG, "expert_ffn: ws must be 16-byte aligned");
     if (moe_status_t s = launch_grouped_gemm(x_perm, seg_offsets, num_segments, max_rows, ffn, d, dtype, w1, b1, 1,
-                                             h, stream))
+                                             h, ws, ws_bytes, stream))
         return s;
-    return launch_grouped_gemm(h, seg_offsets, num_segments, max_rows, d, ffn, dtype, w2, b2, 0, y_perm, stream);
+    return launch_grouped_gemm(h, seg_offsets, num_segments, max_rows, d, ffn, dtype, w2, b2, 0, y_perm, ws, ws_bytes,
+                               stream);
 }
 
 moe_status_t moe_combine(const void *y_perm, int64_t max_rows, const int32_t *slot_row, const float *topk_w,
@@ -348,17 +359,17 @@ extern "C" moe_status_t moe_forward(const moe_problem_t *p, const moe_weights_t 
     if (p->T == 0)
         return MOE_OK;
     if (moe_status_t s = launch_grouped_gemm(b.x_perm, b.seg_offsets, E_loc, max_rows, p->ffn, p->d, p->dtype, w->w1,
-                                             w->b1, 1, b.h, stream))
+                                             w->b1, 1, b.h, b.gemm_ws, b.gemm_ws_bytes, stream))
         return s;
     if (moe_status_t s = launch_grouped_gemm(b.h, b.seg_offsets, E_loc, max_rows, p->d, p->ffn, p->dtype, w->w2,
-                                             w->b2, 0, b.y_perm, stream))
+                                             w->b2, 0, b.y_perm, b.gemm_ws, b.gemm_ws_bytes, stream))
         return s;
     if (p->has_shared) {
         if (moe_status_t s = launch_grouped_gemm(x, nullptr, 1, p->T, p->ffn, p->d, p->dtype, w->ws1, w->bs1, 1, b.h,
-                                                 stream))
+                                                 b.gemm_ws, b.gemm_ws_bytes, stream))
             return s;
         if (moe_status_t s = launch_grouped_gemm(b.h, nullptr, 1, p->T, p->d, p->ffn, p->dtype, w->ws2, w->bs2, 0,
-                                                 b.y_sh, stream))
+                                                 b.y_sh, b.gemm_ws, b.gemm_ws_bytes, stream))
             return s;
     }
     return launch_combine(b.y_perm, max_rows, b.slot_row, b.topk_w, b.y_sh, p->T, p->d, p->k, p->dtype, y, stream);

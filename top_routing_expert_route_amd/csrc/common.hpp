@@ -89,9 +89,11 @@ moe_status_t launch_dispatch(const void *x, moe_dtype_t dt, const int32_t *topk_
                              int32_t *kept_count, int32_t *slot_row, int32_t *row_src, void *x_perm,
                              int64_t max_rows, int32_t *n_dropped, void *ws, hipStream_t stream);
 
+size_t gemm_ws_bytes();
 moe_status_t launch_grouped_gemm(const void *a, const int32_t *seg_offsets, int num_segments,
                                  int64_t max_rows, int N, int K, moe_dtype_t dt, const void *w,
-                                 const void *bias, int activation, void *out, hipStream_t stream);
+                                 const void *bias, int activation, void *out, void *ws, size_t ws_bytes,
+                                 hipStream_t stream);
 
 moe_status_t launch_combine(const void *y_perm, int64_t max_rows, const int32_t *slot_row,
                             const float *topk_w, const void *y_shared, int64_t T, int d, int k,

@@ -399,10 +399,59 @@ __device__ __forceinline__ void k_step(const uint16_t *cur, uint32_t nxt, f32x16
     }
 }
 
-template <int BK, int STAGES, int NBV, bool GELU, bool BIAS>
+// Epilogue of a 256x256 tile: bias, activation, bf16 store of the rows
+// inside [row0, row_end) and features < N.  Accumulators are read
+// unconditionally and only the stores are predicated, so no accumulator has
+// to live outside its AGPR.
+template <int NBV, bool GELU, bool BIAS>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], uint16_t *__restrict__ C,
+                                           const uint16_t *__restrict__ bseg, int64_t row0, int64_t row_end, int n0,
+                                           int N, int wn, int wm, int r32, int khalf)
+{
+#pragma unroll
+    for (int b = 0; b < NBV; ++b) {
+        const int64_t row = row0 + wm * 128 + b * 32 + r32;
+        const bool row_ok = row < row_end;
+        uint16_t *crow = C + (row_ok ? row : row0) * N;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * 128 + a * 32 + 8 * g + 4 * khalf;
+                const bool ok = row_ok && n < N;
+                float v0 = acc[a][b][4 * g + 0], v1 = acc[a][b][4 * g + 1];
+                float v2 = acc[a][b][4 * g + 2], v3 = acc[a][b][4 * g + 3];
+                if (BIAS) {
+                    const uint2 bb = *reinterpret_cast<const uint2 *>(bseg + (n < N ? n : 0));
+                    v0 += bf16_bits_to_f32(bb.x & 0xFFFFu);
+                    v1 += bf16_bits_to_f32(bb.x >> 16);
+                    v2 += bf16_bits_to_f32(bb.y & 0xFFFFu);
+                    v3 += bf16_bits_to_f32(bb.y >> 16);
+                }
+                if (GELU) {
+                    v0 = gelu_erf(v0);
+                    v1 = gelu_erf(v1);
+                    v2 = gelu_erf(v2);
+                    v3 = gelu_erf(v3);
+                }
+                uint2 o;
+                o.x = pack_bf16x2(v0, v1);
+                o.y = pack_bf16x2(v2, v3);
+                if (ok)
+                    *reinterpret_cast<uint2 *>(crow + n) = o;
+            }
+        }
+    }
+}
+
+// One 256x256 tile over K steps [kt_lo, kt_hi).  With PART the raw fp32
+// accumulators go to `part` (one 256 KB slab, lane-major per register) for a
+// later fixed-order reduction; otherwise the epilogue stores bf16.
+template <int BK, int STAGES, int NBV, bool GELU, bool BIAS, bool PART>
 __device__ __forceinline__ void tile_256(const uint16_t *__restrict__ A, const uint16_t *__restrict__ wseg,
                                          const uint16_t *__restrict__ bseg, uint16_t *__restrict__ C,
-                                         uint16_t *smem, int64_t row0, int64_t row_end, int n0, int N, int K)
+                                         float *__restrict__ part, uint16_t *smem, int64_t row0, int64_t row_end,
+                                         int n0, int N, int K, int kt_lo, int kt_hi)
 {
     constexpr int CPR = BK / 8;            // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;          // rows filled per DMA instruction (1 KB)
@@ -440,12 +489,12 @@ __device__ __forceinline__ void tile_256(const uint16_t *__restrict__ A, const u
             for (int v = 0; v < 16; ++v)
                 acc[a][b][v] = 0.f;
 
-    const int KT = K / BK;
     const int sw = swz<BK>(r32);
-    // Prologue: stages 0 .. STAGES-2 (a copy past K reads out of range: zeros).
+    // Prologue: stages 0 .. STAGES-2 hold K steps kt_lo .. kt_lo+STAGES-2 (a
+    // copy past kt_hi reads out of range: zeros).
     for (int p = 0; p < STAGES - 1; ++p) {
         const uint32_t dst = lds0 + (uint32_t)(p * STAGE) * 2u;
-        const uint32_t so_k = p < KT ? (uint32_t)p * (BK * 2) : kOutOfRange;
+        const uint32_t so_k = kt_lo + p < kt_hi ? (uint32_t)(kt_lo + p) * (BK * 2) : kOutOfRange;
 #pragma unroll
         for (int i = 0; i < 2 * NQ; ++i) {
             const int q = i >> 1;
@@ -457,11 +506,12 @@ __device__ __forceinline__ void tile_256(const uint16_t *__restrict__ A, const u
     wait_vmcnt<(STAGES - 2) * PER_STAGE>();
     __syncthreads();
 
-    for (int kt = 0; kt < KT; ++kt) {
+    for (int kt = kt_lo; kt < kt_hi; ++kt) {
         const int fill = kt + STAGES - 1;
-        const uint32_t so_k = fill < KT ? (uint32_t)fill * (BK * 2) : kOutOfRange;
-        k_step<BK, NBV>(smem + (kt % STAGES) * STAGE, lds0 + (uint32_t)((fill % STAGES) * STAGE) * 2u, acc, rw, ra,
-                        vbase, so_k, row_bytes, wave, wn, wm, r32, khalf, sw);
+        const uint32_t so_k = fill < kt_hi ? (uint32_t)fill * (BK * 2) : kOutOfRange;
+        k_step<BK, NBV>(smem + ((kt - kt_lo) % STAGES) * STAGE,
+                        lds0 + (uint32_t)(((fill - kt_lo) % STAGES) * STAGE) * 2u, acc, rw, ra, vbase, so_k, row_bytes,
+                        wave, wn, wm, r32, khalf, sw);
         // Stage kt+1 must have landed; the STAGES-2 stages issued after it
         // may stay in flight.
         wait_vmcnt<(STAGES - 2) * PER_STAGE>();
@@ -469,42 +519,85 @@ __device__ __forceinline__ void tile_256(const uint16_t *__restrict__ A, const u
     }
     wait_vmcnt<0>(); // the zero-fill copies of the last steps must land before the next tile's copies
 
-    // Epilogue: accumulators are read unconditionally and only the stores are
-    // predicated, so no accumulator has to live outside its AGPR.
+    if (PART) {
+        float *dst = part + (size_t)wave * (256 * 64) + lane;
 #pragma unroll
-    for (int b = 0; b < NBV; ++b) {
-        const int64_t row = row0 + wm * 128 + b * 32 + r32;
-        const bool row_ok = row < row_end;
-        uint16_t *crow = C + (row_ok ? row : row0) * N;
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
+            for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * 128 + a * 32 + 8 * g + 4 * khalf;
-                const bool ok = row_ok && n < N;
-                float v0 = acc[a][b][4 * g + 0], v1 = acc[a][b][4 * g + 1];
-                float v2 = acc[a][b][4 * g + 2], v3 = acc[a][b][4 * g + 3];
-                if (BIAS) {
-                    const uint2 bb = *reinterpret_cast<const uint2 *>(bseg + (n < N ? n : 0));
-                    v0 += bf16_bits_to_f32(bb.x & 0xFFFFu);
-                    v1 += bf16_bits_to_f32(bb.x >> 16);
-                    v2 += bf16_bits_to_f32(bb.y & 0xFFFFu);
-                    v3 += bf16_bits_to_f32(bb.y >> 16);
-                }
-                if (GELU) {
-                    v0 = gelu_erf(v0);
-                    v1 = gelu_erf(v1);
-                    v2 = gelu_erf(v2);
-                    v3 = gelu_erf(v3);
-                }
-                uint2 o;
-                o.x = pack_bf16x2(v0, v1);
-                o.y = pack_bf16x2(v2, v3);
-                if (ok)
-                    *reinterpret_cast<uint2 *>(crow + n) = o;
-            }
+                for (int v = 0; v < 16; ++v)
+                    dst[((a * 4 + b) * 16 + v) * 64] = acc[a][b][v];
+    } else {
+        store_tile<NBV, GELU, BIAS>(acc, C, bseg, row0, row_end, n0, N, wn, wm, r32, khalf);
+    }
+}
+
+// Split of the tile list over a persistent grid of G blocks.  F whole tiles
+// run in full rounds (each block gets the same number); when the rest
+// (`rem` tiles, at most half a round) would leave CUs idle, each of them is
+// cut into `sk` K ranges, one per block, written as fp32 partials and summed
+// by grouped_gemm_reduce.  Computed identically by both kernels.
+struct TailPlan {
+    int64_t F;   // whole tiles
+    int rem;     // tail tiles split in K (0: none)
+    int sk;      // K ranges per tail tile
+};
+
+__device__ __forceinline__ TailPlan plan_tail(int64_t total, int G, int KT, bool have_ws)
+{
+    TailPlan p{total, 0, 1};
+    const int64_t R = total / G;
+    const int64_t rem = total - R * G;
+    if (have_ws && rem > 0 && 2 * rem <= G) {
+        int sk = (int)(G / rem);
+        sk = sk > 8 ? 8 : sk;
+        sk = sk > KT ? KT : sk;
+        if (sk >= 2) {
+            p.F = R * G;
+            p.rem = (int)rem;
+            p.sk = sk;
         }
     }
+    return p;
+}
+
+template <int BK, int STAGES, bool GELU, bool BIAS, bool PART>
+__device__ __forceinline__ void tile_any(int nbv, const uint16_t *A, const uint16_t *wseg, const uint16_t *bseg,
+                                         uint16_t *C, float *part, uint16_t *smem, int64_t row0, int64_t row_end,
+                                         int n0, int N, int K, int kt_lo, int kt_hi)
+{
+    switch (nbv) {
+    case 4: tile_256<BK, STAGES, 4, GELU, BIAS, PART>(A, wseg, bseg, C, part, smem, row0, row_end, n0, N, K, kt_lo, kt_hi); break;
+    case 3: tile_256<BK, STAGES, 3, GELU, BIAS, PART>(A, wseg, bseg, C, part, smem, row0, row_end, n0, N, K, kt_lo, kt_hi); break;
+    case 2: tile_256<BK, STAGES, 2, GELU, BIAS, PART>(A, wseg, bseg, C, part, smem, row0, row_end, n0, N, K, kt_lo, kt_hi); break;
+    case 1: tile_256<BK, STAGES, 1, GELU, BIAS, PART>(A, wseg, bseg, C, part, smem, row0, row_end, n0, N, K, kt_lo, kt_hi); break;
+    default: tile_256<BK, STAGES, 0, GELU, BIAS, PART>(A, wseg, bseg, C, part, smem, row0, row_end, n0, N, K, kt_lo, kt_hi); break;
+    }
+}
+
+// Location of tile L of the list: segment, rows and first feature.
+struct TileLoc {
+    int s;
+    int64_t row0, row_end;
+    int n0;
+};
+
+__device__ __forceinline__ TileLoc locate(const int *tb, const int32_t *seg, int S, int64_t max_rows, int NT,
+                                          int64_t L)
+{
+    TileLoc t;
+    t.s = find_segment(tb, S, NT, L);
+    const int mt_s = tb[t.s + 1] - tb[t.s];
+    const int64_t local = L - (int64_t)tb[t.s] * NT;
+    const int n_tile = (int)(local / mt_s);
+    const int m_tile = (int)(local % mt_s);
+    int64_t seg_lo, seg_hi;
+    seg_bounds(seg, t.s, max_rows, seg_lo, seg_hi);
+    t.row0 = seg_lo + (int64_t)m_tile * kL;
+    t.row_end = min(t.row0 + kL, seg_hi);
+    t.n0 = n_tile * kL;
+    return t;
 }
 
 template <int BK, int STAGES, bool GELU, bool BIAS>
@@ -512,7 +605,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_256(const uint16_t *
                                                                 const int32_t *__restrict__ seg, int S,
                                                                 int64_t max_rows, const uint16_t *__restrict__ W,
                                                                 const uint16_t *__restrict__ bias,
-                                                                uint16_t *__restrict__ C, int N, int K)
+                                                                uint16_t *__restrict__ C, int N, int K,
+                                                                float *__restrict__ part_ws)
 {
     __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * 2 * kL * BK];
     __shared__ int tb[kMaxSeg + 1];
@@ -520,35 +614,106 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_256(const uint16_t *
 
     const int wm = (threadIdx.x >> 6) >> 1;
     const int NT = (N + kL - 1) / kL;
+    const int KT = K / BK;
     const int64_t total = (int64_t)tb[S] * NT;
+    const TailPlan plan = plan_tail(total, (int)gridDim.x, KT, part_ws != nullptr);
+
+    // Whole tiles: an XCD-contiguous share of tiles [0, F).
     const int xcd = blockIdx.x % kXcds;
     const int per = gridDim.x / kXcds;
     const int j = blockIdx.x / kXcds;
-    const int64_t rlo = total * xcd / kXcds, rhi = total * (xcd + 1) / kXcds;
-
+    const int64_t rlo = plan.F * xcd / kXcds, rhi = plan.F * (xcd + 1) / kXcds;
     for (int64_t L = rlo + j; L < rhi; L += per) {
-        const int s = find_segment(tb, S, NT, L);
-        const int mt_s = tb[s + 1] - tb[s];
-        const int64_t local = L - (int64_t)tb[s] * NT;
-        const int n_tile = (int)(local / mt_s);
-        const int m_tile = (int)(local % mt_s);
-        int64_t seg_lo, seg_hi;
-        seg_bounds(seg, s, max_rows, seg_lo, seg_hi);
-        const int64_t row0 = seg_lo + (int64_t)m_tile * kL;
-        const int64_t row_end = min(row0 + kL, seg_hi);
-        const int n0 = n_tile * kL;
-        const uint16_t *wseg = W + (int64_t)s * N * K;
-        const uint16_t *bseg = bias ? bias + (int64_t)s * N : nullptr;
-        const int64_t left = row_end - (row0 + wm * 128);
+        const TileLoc t = locate(tb, seg, S, max_rows, NT, L);
+        const int64_t left = t.row_end - (t.row0 + wm * 128);
         const int nbv = left <= 0 ? 0 : (left >= 128 ? 4 : (int)((left + 31) / 32));
-        switch (nbv) {
-        case 4: tile_256<BK, STAGES, 4, GELU, BIAS>(A, wseg, bseg, C, smem, row0, row_end, n0, N, K); break;
-        case 3: tile_256<BK, STAGES, 3, GELU, BIAS>(A, wseg, bseg, C, smem, row0, row_end, n0, N, K); break;
-        case 2: tile_256<BK, STAGES, 2, GELU, BIAS>(A, wseg, bseg, C, smem, row0, row_end, n0, N, K); break;
-        case 1: tile_256<BK, STAGES, 1, GELU, BIAS>(A, wseg, bseg, C, smem, row0, row_end, n0, N, K); break;
-        default: tile_256<BK, STAGES, 0, GELU, BIAS>(A, wseg, bseg, C, smem, row0, row_end, n0, N, K); break;
-        }
+        tile_any<BK, STAGES, GELU, BIAS, false>(nbv, A, W + (int64_t)t.s * N * K,
+                                                bias ? bias + (int64_t)t.s * N : nullptr, C, nullptr, smem, t.row0,
+                                                t.row_end, t.n0, N, K, 0, KT);
         __syncthreads(); // the next tile's copies overwrite stages still read here
+    }
+    // Tail: one K range of one tail tile per block.
+    const int u = blockIdx.x;
+    if (plan.rem > 0 && u < plan.rem * plan.sk) {
+        const int64_t L = plan.F + u / plan.sk;
+        const int c = u % plan.sk;
+        const TileLoc t = locate(tb, seg, S, max_rows, NT, L);
+        const int64_t left = t.row_end - (t.row0 + wm * 128);
+        const int nbv = left <= 0 ? 0 : (left >= 128 ? 4 : (int)((left + 31) / 32));
+        const int klo = (int)((int64_t)KT * c / plan.sk), khi = (int)((int64_t)KT * (c + 1) / plan.sk);
+        tile_any<BK, STAGES, GELU, BIAS, true>(nbv, A, W + (int64_t)t.s * N * K, nullptr, C,
+                                               part_ws + (size_t)u * (kL * kL), smem, t.row0, t.row_end, t.n0, N, K,
+                                               klo, khi);
+    }
+}
+
+// Sums the K-range partials of each tail tile in range order and applies the
+// bias, activation and bf16 store; a no-op when the GEMM had no split tail.
+// Block = (tail tile, GEMM wave w, row sub-tile b); its four waves take the
+// four feature sub-tiles a.  Each lane loads its 16 accumulators of every
+// K range up front (all independent loads), then sums them in range order.
+template <bool GELU, bool BIAS>
+__global__ __launch_bounds__(256) void grouped_gemm_reduce(const int32_t *__restrict__ seg, int S, int64_t max_rows,
+                                                           const uint16_t *__restrict__ bias,
+                                                           uint16_t *__restrict__ C, int N, int K, int BKused, int G,
+                                                           const float *__restrict__ part_ws)
+{
+    __shared__ int tb[kMaxSeg + 1];
+    build_tile_prefix<kL>(seg, S, max_rows, tb);
+    const int NT = (N + kL - 1) / kL;
+    const int64_t total = (int64_t)tb[S] * NT;
+    const TailPlan plan = plan_tail(total, G, K / BKused, true);
+    const int tile = blockIdx.x >> 4, wave = (blockIdx.x >> 2) & 3, b = blockIdx.x & 3;
+    if (plan.rem == 0 || tile >= plan.rem)
+        return;
+    const int lane = threadIdx.x & 63, a = threadIdx.x >> 6;
+    const int wn = wave & 1, wm = wave >> 1;
+    const int r32 = lane & 31, khalf = lane >> 5;
+    const TileLoc t = locate(tb, seg, S, max_rows, NT, plan.F + tile);
+    const float *src = part_ws + (size_t)tile * plan.sk * (kL * kL) + (size_t)wave * (256 * 64) +
+                       (size_t)((a * 4 + b) * 16) * 64 + lane;
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        v[r] = src[(size_t)r * 64];
+#pragma unroll
+    for (int c = 1; c < 8; ++c) {
+        if (c < plan.sk) {
+            float w[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                w[r] = src[(size_t)c * (kL * kL) + (size_t)r * 64];
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                v[r] += w[r];
+        }
+    }
+    const int64_t row = t.row0 + wm * 128 + b * 32 + r32;
+    const bool row_ok = row < t.row_end;
+    uint16_t *crow = C + (row_ok ? row : t.row0) * N;
+    const uint16_t *bseg = bias ? bias + (int64_t)t.s * N : nullptr;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int n = t.n0 + wn * 128 + a * 32 + 8 * g + 4 * khalf;
+        float v0 = v[4 * g], v1 = v[4 * g + 1], v2 = v[4 * g + 2], v3 = v[4 * g + 3];
+        if (BIAS) {
+            const uint2 bb = *reinterpret_cast<const uint2 *>(bseg + (n < N ? n : 0));
+            v0 += bf16_bits_to_f32(bb.x & 0xFFFFu);
+            v1 += bf16_bits_to_f32(bb.x >> 16);
+            v2 += bf16_bits_to_f32(bb.y & 0xFFFFu);
+            v3 += bf16_bits_to_f32(bb.y >> 16);
+        }
+        if (GELU) {
+            v0 = gelu_erf(v0);
+            v1 = gelu_erf(v1);
+            v2 = gelu_erf(v2);
+            v3 = gelu_erf(v3);
+        }
+        uint2 o;
+        o.x = pack_bf16x2(v0, v1);
+        o.y = pack_bf16x2(v2, v3);
+        if (row_ok && n < N)
+            *reinterpret_cast<uint2 *>(crow + n) = o;
     }
 }
 
@@ -643,8 +808,7 @@ int device_cus()
 #endif
 constexpr int kLargeBK = MOE_GEMM_BK, kLargeStages = MOE_GEMM_STAGES;
 
-moe_status_t run_bf16_256(const void *a, const int32_t *seg, int S, int64_t max_rows, int N, int K, const void *w,
-                         const void *bias, int act, void *out, hipStream_t stream)
+int large_grid(int64_t max_rows, int S, int N)
 {
     const int64_t tiles_bound = ((max_rows + kL - 1) / kL + S) * (int64_t)((N + kL - 1) / kL);
     int64_t grid = (int64_t)device_cus();
@@ -654,13 +818,28 @@ moe_status_t run_bf16_256(const void *a, const int32_t *seg, int S, int64_t max_
         grid = need;
     if (grid < kXcds)
         grid = kXcds;
+    return (int)grid;
+}
+
+moe_status_t run_bf16_256(const void *a, const int32_t *seg, int S, int64_t max_rows, int N, int K, const void *w,
+                         const void *bias, int act, void *out, float *part_ws, hipStream_t stream)
+{
+    const int grid = large_grid(max_rows, S, N);
     auto *k = act == 1 ? (bias ? grouped_gemm_bf16_256<kLargeBK, kLargeStages, true, true>
                                : grouped_gemm_bf16_256<kLargeBK, kLargeStages, true, false>)
                        : (bias ? grouped_gemm_bf16_256<kLargeBK, kLargeStages, false, true>
                                : grouped_gemm_bf16_256<kLargeBK, kLargeStages, false, false>);
     k<<<(unsigned)grid, 256, 0, stream>>>((const uint16_t *)a, seg, S, max_rows, (const uint16_t *)w,
-                                          (const uint16_t *)bias, (uint16_t *)out, N, K);
-    return check_launch("grouped_gemm_bf16_256");
+                                          (const uint16_t *)bias, (uint16_t *)out, N, K, part_ws);
+    if (moe_status_t st = check_launch("grouped_gemm_bf16_256"))
+        return st;
+    if (!part_ws)
+        return MOE_OK;
+    auto *r = act == 1 ? (bias ? grouped_gemm_reduce<true, true> : grouped_gemm_reduce<true, false>)
+                       : (bias ? grouped_gemm_reduce<false, true> : grouped_gemm_reduce<false, false>);
+    r<<<(unsigned)(grid / 2 * 16), 256, 0, stream>>>(seg, S, max_rows, (const uint16_t *)bias, (uint16_t *)out, N,
+                                                     K, kLargeBK, grid, part_ws);
+    return check_launch("grouped_gemm_reduce");
 }
 
 template <int BN, int BM>
@@ -686,16 +865,25 @@ moe_status_t run_bf16(const void *a, const int32_t *seg, int S, int64_t max_rows
 
 } // namespace
 
+size_t gemm_ws_bytes()
+{
+    int64_t grid = (int64_t)device_cus();
+    grid = (grid + kXcds - 1) / kXcds * kXcds;
+    return (size_t)grid * kL * kL * sizeof(float);
+}
+
 moe_status_t launch_grouped_gemm(const void *a, const int32_t *seg_offsets, int num_segments, int64_t max_rows,
                                  int N, int K, moe_dtype_t dt, const void *w, const void *bias, int activation,
-                                 void *out, hipStream_t stream)
+                                 void *out, void *ws, size_t ws_bytes, hipStream_t stream)
 {
     if (max_rows == 0)
         return MOE_OK;
     const int S = seg_offsets ? num_segments : 1;
     if (dt == MOE_BF16) {
-        if (K % kLargeBK == 0)
-            return run_bf16_256(a, seg_offsets, S, max_rows, N, K, w, bias, activation, out, stream);
+        if (K % kLargeBK == 0) {
+            float *part = (ws && ws_bytes >= gemm_ws_bytes()) ? (float *)ws : nullptr;
+            return run_bf16_256(a, seg_offsets, S, max_rows, N, K, w, bias, activation, out, part, stream);
+        }
         return run_bf16<128, 128>(a, seg_offsets, S, max_rows, N, K, w, bias, activation, out, stream);
     }
     const dim3 g((unsigned)((N + 63) / 64), (unsigned)((max_rows + 63) / 64 + S));

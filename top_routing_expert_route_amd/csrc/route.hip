@@ -28,7 +28,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kSelTokensPerWave = 16;
+constexpr int kSelTokensPerWave = 4;
 constexpr int kSelTokensPerBlock = 4 * kSelTokensPerWave;
 
 __device__ __forceinline__ float trunc_bf16(float v) { return __uint_as_float(__float_as_uint(v) & 0xFFFF0000u); }
@@ -142,6 +142,173 @@ __global__ __launch_bounds__(256) void route_logits_mfma(const uint16_t *__restr
                     if (e < E && t < T)
                         logits[t * E + e] = s;
                 }
+    }
+}
+
+// Fused router for E <= 64 with bf16 activations: one block scores TB = 16*TT
+// tokens against all experts (16*ET >= E) with the split-bf16 MFMAs (the four
+// waves split K, U K-steps of loads in flight per wave), parks the logits in
+// LDS, then one thread per token does softmax and top-k, and the block
+// writes its partial sums of the probabilities and selection counts.
+template <int ET, int TT, int U, int NW>
+__global__ __launch_bounds__(64 * NW) void route_fused_small(const uint16_t *__restrict__ x,
+                                                         const float *__restrict__ wr,
+                                                         const float *__restrict__ bias, int64_t T, int d, int E,
+                                                         int k, int32_t *__restrict__ topk_idx,
+                                                         float *__restrict__ topk_w, float *__restrict__ part_p,
+                                                         int32_t *__restrict__ part_c)
+{
+    constexpr int EB = 16 * ET, TB = 16 * TT;
+    constexpr int LS = EB + 1; // padded LDS row of one token's logits
+    __shared__ float red[NW - 1][ET * TT * 256];
+    __shared__ float lg[TB * LS];
+    __shared__ int cnt[EB];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t t0 = (int64_t)blockIdx.x * TB;
+    const int kw = ((d + NW - 1) / NW + 31) / 32 * 32;
+    const int kbeg = wave * kw;
+    const int kend = min(d, kbeg + kw);
+    const int r16 = lane & 15;
+    const int koff = (lane >> 4) * 8;
+    if (threadIdx.x < EB)
+        cnt[threadIdx.x] = 0;
+
+    f32x4 acc[ET][TT];
+#pragma unroll
+    for (int a = 0; a < ET; ++a)
+#pragma unroll
+        for (int b = 0; b < TT; ++b)
+            acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int k0 = kbeg; k0 < kend; k0 += 32 * U) {
+        u32x4 xv[U][TT];
+        f32x4 wv[U][ET][2];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kk = k0 + u * 32 + koff;
+            const bool kval = kk < kend;
+#pragma unroll
+            for (int b = 0; b < TT; ++b) {
+                const int64_t t = t0 + b * 16 + r16;
+                xv[u][b] = (kval && t < T) ? *reinterpret_cast<const u32x4 *>(x + t * d + kk) : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int a = 0; a < ET; ++a) {
+                const int e = a * 16 + r16;
+                if (kval && e < E) {
+                    const f32x4 *p = reinterpret_cast<const f32x4 *>(wr + (int64_t)e * d + kk);
+                    wv[u][a][0] = p[0];
+                    wv[u][a][1] = p[1];
+                } else {
+                    wv[u][a][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    wv[u][a][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int a = 0; a < ET; ++a) {
+                bf16x8 hi, mid, lo;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const float w = wv[u][a][q >> 2][q & 3];
+                    const float h = trunc_bf16(w);
+                    const float r1 = w - h;
+                    const float m = trunc_bf16(r1);
+                    hi[q] = bits_bf16(h);
+                    mid[q] = bits_bf16(m);
+                    lo[q] = bits_bf16(r1 - m);
+                }
+#pragma unroll
+                for (int b = 0; b < TT; ++b) {
+                    const bf16x8 xb = __builtin_bit_cast(bf16x8, xv[u][b]);
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, xb, acc[a][b], 0, 0, 0);
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, xb, acc[a][b], 0, 0, 0);
+                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, xb, acc[a][b], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    if (wave > 0) {
+#pragma unroll
+        for (int a = 0; a < ET; ++a)
+#pragma unroll
+            for (int b = 0; b < TT; ++b)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    red[wave - 1][((a * TT + b) * 4 + v) * 64 + lane] = acc[a][b][v];
+    }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int a = 0; a < ET; ++a)
+#pragma unroll
+            for (int b = 0; b < TT; ++b)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int slot = ((a * TT + b) * 4 + v) * 64 + lane;
+                    float sum = acc[a][b][v];
+#pragma unroll
+                    for (int q = 0; q < NW - 1; ++q)
+                        sum += red[q][slot];
+                    const int e = a * 16 + 4 * (lane >> 4) + v;
+                    const int tl = b * 16 + (lane & 15);
+                    lg[tl * LS + e] = sum;
+                }
+    }
+    __syncthreads();
+
+    // One thread per token: softmax over E, top-k by (logit desc, id asc).
+    const int tl = threadIdx.x;
+    const int64_t t = t0 + tl;
+    if (tl < TB && t < T) {
+        float *row = lg + tl * LS;
+        float m = -INFINITY;
+        for (int e = 0; e < E; ++e) {
+            const float l = row[e] + (bias ? bias[e] : 0.f);
+            row[e] = l;
+            m = fmaxf(m, l);
+        }
+        float sum = 0.f;
+        for (int e = 0; e < E; ++e)
+            sum += expf(row[e] - m);
+        const float inv = 1.0f / sum;
+        uint64_t taken = 0;
+        for (int j = 0; j < k; ++j) {
+            int best = -1;
+            float bv = 0.f;
+            for (int e = 0; e < E; ++e) {
+                if ((taken >> e) & 1ull)
+                    continue;
+                if (best < 0 || row[e] > bv) {
+                    best = e;
+                    bv = row[e];
+                }
+            }
+            taken |= 1ull << best;
+            topk_idx[t * k + j] = best;
+            topk_w[t * k + j] = expf(bv - m) * inv;
+            atomicAdd(&cnt[best], 1);
+        }
+        for (int e = 0; e < E; ++e)
+            row[e] = expf(row[e] - m) * inv;
+    } else if (tl < TB) {
+        float *row = lg + tl * LS;
+        for (int e = 0; e < E; ++e)
+            row[e] = 0.f;
+    }
+    __syncthreads();
+    // Block partials: probabilities summed in token order.
+    if (threadIdx.x < E) {
+        const int e = threadIdx.x;
+        float ps = 0.f;
+        for (int q = 0; q < TB; ++q)
+            ps += lg[q * LS + e];
+        part_p[(int64_t)blockIdx.x * E + e] = ps;
+        part_c[(int64_t)blockIdx.x * E + e] = cnt[e];
     }
 }
 
@@ -337,9 +504,20 @@ __global__ __launch_bounds__(1024) void route_finalize(const float *__restrict__
 
 static int select_blocks(int64_t T) { return (int)((T + kSelTokensPerBlock - 1) / kSelTokensPerBlock); }
 
+// Tokens per block of the fused small-E path.
+static int fused_tb(int E) { return E <= 16 ? 16 : 32; }
+
+static int route_blocks(int64_t T, int E, moe_dtype_t dt)
+{
+    if (dt == MOE_BF16 && E <= 64)
+        return (int)((T + fused_tb(E) - 1) / fused_tb(E));
+    return select_blocks(T);
+}
+
 size_t route_ws_bytes(int64_t T, int E)
 {
-    const int nblk = select_blocks(T);
+    // enough for either path: logits (two-kernel path) + partials of the larger block count
+    const int nblk = (int)((T + 15) / 16);
     return align_up((size_t)T * E * sizeof(float)) + 2 * align_up((size_t)nblk * E * sizeof(float));
 }
 
@@ -348,49 +526,54 @@ moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, 
                           int32_t *expert_count, float *f, float *P, float *l_aux, void *ws,
                           hipStream_t stream)
 {
-    const int nblk = select_blocks(T);
+    const int nblk = route_blocks(T, E, dt);
+    const int nblk_max = (int)((T + 15) / 16);
     Carver cv{(char *)ws, 0};
     float *logits = cv.take<float>((size_t)T * E);
-    float *part_p = cv.take<float>((size_t)nblk * E);
-    int32_t *part_c = cv.take<int32_t>((size_t)nblk * E);
+    float *part_p = cv.take<float>((size_t)nblk_max * E);
+    int32_t *part_c = cv.take<int32_t>((size_t)nblk_max * E);
 
     if (T > 0) {
-        if (dt == MOE_BF16) {
+        if (dt == MOE_BF16 && E <= 64) {
             const uint16_t *xb = (const uint16_t *)x;
-            if (E <= 16) {
-                dim3 g((unsigned)((T + 15) / 16), 1);
-                route_logits_mfma<1, 1><<<g, 256, 0, stream>>>(xb, w_router, T, d, E, logits);
-            } else if (E <= 32) {
-                dim3 g((unsigned)((T + 15) / 16), 1);
-                route_logits_mfma<2, 1><<<g, 256, 0, stream>>>(xb, w_router, T, d, E, logits);
-            } else if (E <= 64) {
-                dim3 g((unsigned)((T + 15) / 16), 1);
-                route_logits_mfma<4, 1><<<g, 256, 0, stream>>>(xb, w_router, T, d, E, logits);
-            } else {
-                dim3 g((unsigned)((T + 63) / 64), (unsigned)((E + 63) / 64));
-                route_logits_mfma<4, 4><<<g, 256, 0, stream>>>(xb, w_router, T, d, E, logits);
-            }
+            const dim3 g((unsigned)nblk);
+            if (E <= 16)
+                route_fused_small<1, 1, 8, 8><<<g, 512, 0, stream>>>(xb, w_router, b_router, T, d, E, k, topk_idx,
+                                                                  topk_w, part_p, part_c);
+            else if (E <= 32)
+                route_fused_small<2, 2, 4, 8><<<g, 512, 0, stream>>>(xb, w_router, b_router, T, d, E, k, topk_idx,
+                                                                  topk_w, part_p, part_c);
+            else
+                route_fused_small<4, 2, 2, 8><<<g, 512, 0, stream>>>(xb, w_router, b_router, T, d, E, k, topk_idx,
+                                                                  topk_w, part_p, part_c);
+            if (moe_status_t s = check_launch("route_fused_small"))
+                return s;
         } else {
-            const int64_t n = T * E;
-            route_logits_f32<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>((const float *)x, w_router, T, d,
-                                                                             E, logits);
+            if (dt == MOE_BF16) {
+                dim3 g((unsigned)((T + 63) / 64), (unsigned)((E + 63) / 64));
+                route_logits_mfma<4, 4><<<g, 256, 0, stream>>>((const uint16_t *)x, w_router, T, d, E, logits);
+            } else {
+                const int64_t n = T * E;
+                route_logits_f32<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>((const float *)x, w_router, T, d,
+                                                                                 E, logits);
+            }
+            if (moe_status_t s = check_launch("route_logits"))
+                return s;
+            const int epl = (E + 63) / 64;
+            const dim3 g((unsigned)nblk);
+            switch (epl) {
+            case 1: route_select<1><<<g, 256, 0, stream>>>(logits, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+            case 2: route_select<2><<<g, 256, 0, stream>>>(logits, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+            case 3:
+            case 4: route_select<4><<<g, 256, 0, stream>>>(logits, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+            case 5: case 6: case 7: case 8:
+                route_select<8><<<g, 256, 0, stream>>>(logits, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+            default:
+                route_select<16><<<g, 256, 0, stream>>>(logits, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+            }
+            if (moe_status_t s = check_launch("route_select"))
+                return s;
         }
-        if (moe_status_t s = check_launch("route_logits"))
-            return s;
-        const int epl = (E + 63) / 64;
-        const dim3 g((unsigned)nblk);
-        switch (epl) {
-        case 1: route_select<1><<<g, 256, 0, stream>>>(logits, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
-        case 2: route_select<2><<<g, 256, 0, stream>>>(logits, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
-        case 3:
-        case 4: route_select<4><<<g, 256, 0, stream>>>(logits, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
-        case 5: case 6: case 7: case 8:
-            route_select<8><<<g, 256, 0, stream>>>(logits, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
-        default:
-            route_select<16><<<g, 256, 0, stream>>>(logits, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
-        }
-        if (moe_status_t s = check_launch("route_select"))
-            return s;
     }
     route_finalize<<<1, 1024, 0, stream>>>(part_p, part_c, T > 0 ? nblk : 0, T, E, alpha, expert_count, f, P,
                                            l_aux);
