@@ -331,69 +331,88 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p)
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
 }
 
+// Wave grid of a 256x256 tile: WGN waves along the features and WGM along
+// the rows; each wave owns (256/WGN) x (256/WGM) as FA x FB MFMA tiles of
+// 32x32.  Four waves (2x2, 128x128 each, one wave per SIMD) or eight (2x4,
+// 128x64 each, two waves per SIMD so that one wave's MFMAs cover the
+// other's waits).
+template <int WGN, int WGM> struct Grid {
+    static constexpr int WGN_ = WGN, WGM_ = WGM;
+    static constexpr int NW = WGN * WGM;
+    static constexpr int WTN = kL / WGN, WTM = kL / WGM;
+    static constexpr int FA = WTN / 32, FB = WTM / 32;
+};
+
 // One K step of a 256x256 tile: MFMAs on stage `cur` (already in LDS) while
 // the LDS-DMA copies of a later K step fill the stage at LDS byte address
-// `nxt`.  The step is cut into chunks of 4 MFMAs + 2 LDS reads of the next
-// 16-wide sub-step; one copy is issued after each chunk, so the copies
-// trickle out at the rate the address unit drains them instead of stalling
-// the wave in a burst.
-template <int BK, int NBV>
-__device__ __forceinline__ void k_step(const uint16_t *cur, uint32_t nxt, f32x16 (&acc)[4][4], i32x4 rw, i32x4 ra,
-                                       uint32_t vbase, uint32_t so_k, uint32_t row_bytes, int wave, int wn, int wm,
-                                       int r32, int khalf, int sw)
+// `nxt`.  Each 16-wide K sub-step is cut into chunks of MFMAs plus a share of
+// the LDS reads of the next sub-step; one copy is issued after each chunk, so
+// the copies trickle out at the rate the address unit drains them instead of
+// stalling the wave in a burst.
+template <int BK, class G, int NBV>
+__device__ __forceinline__ void k_step(const uint16_t *cur, uint32_t nxt, f32x16 (&acc)[G::FA][G::FB], i32x4 rw,
+                                       i32x4 ra, uint32_t vbase, uint32_t so_k, uint32_t row_bytes, int wave, int wn,
+                                       int wm, int r32, int khalf, int sw)
 {
-    constexpr int CPR = BK / 8, RPI = 64 / CPR, NQ = kL / (4 * RPI), KS = BK / 16;
-    static_assert(2 * NQ == 4 * KS, "one copy per chunk");
+    constexpr int FA = G::FA, FB = G::FB, NW = G::NW;
+    constexpr int CPR = BK / 8, RPI = 64 / CPR, NQ = kL / (NW * RPI), KS = BK / 16;
+    constexpr int DPW = 2 * NQ;         // copies per wave per stage
+    constexpr int DPS = DPW / KS;       // copies (= chunks) per sub-step
+    constexpr int MPC = FA * FB / DPS;  // MFMAs per chunk
+    constexpr int RDS = FA + FB;        // fragment reads per sub-step
+    constexpr int RPC = (RDS + DPS - 1) / DPS;
+    static_assert(DPW % KS == 0 && (FA * FB) % DPS == 0, "chunking");
     const uint16_t *sW = cur;
     const uint16_t *sA = cur + kL * BK;
-    bf16x8 fa[2][4], fb[2][4];
-    auto read_a = [&](int ks, int buf, int a) {
+    bf16x8 fa[2][FA], fb[2][FB];
+    auto read = [&](int ks, int buf, int r) {
         const int ch = ((ks * 2 + khalf) ^ sw) * 8;
-        fa[buf][a] = *reinterpret_cast<const bf16x8 *>(sW + (wn * 128 + a * 32 + r32) * BK + ch);
+        if (r < FA) {
+            fa[buf][r] = *reinterpret_cast<const bf16x8 *>(sW + (wn * G::WTN + r * 32 + r32) * BK + ch);
+        } else if (r - FA < NBV) {
+            const int b = r - FA;
+            fb[buf][b] = *reinterpret_cast<const bf16x8 *>(sA + (wm * G::WTM + b * 32 + r32) * BK + ch);
+        }
     };
-    auto read_b = [&](int ks, int buf, int b) {
-        const int ch = ((ks * 2 + khalf) ^ sw) * 8;
-        fb[buf][b] = *reinterpret_cast<const bf16x8 *>(sA + (wm * 128 + b * 32 + r32) * BK + ch);
-    };
-    auto dma = [&](int i) { // copy i of 2*NQ: W rows for even i, A rows for odd i
+    auto dma = [&](int i) { // copy i of DPW: W rows for even i, A rows for odd i
         const int q = i >> 1;
-        const uint32_t R = (uint32_t)((4 * q + wave) * RPI);
-        const uint32_t so = (uint32_t)q * (4u * RPI) * row_bytes + so_k;
+        const uint32_t R = (uint32_t)((NW * q + wave) * RPI);
+        const uint32_t so = (uint32_t)q * (uint32_t)(NW * RPI) * row_bytes + so_k;
         dma16((i & 1) ? ra : rw, vbase, so, nxt + (uint32_t)((i & 1) * (kL * BK) + R * BK) * 2u);
     };
     if (NBV > 0) {
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-            read_a(0, 0, a);
-#pragma unroll
-        for (int b = 0; b < NBV; ++b)
-            read_b(0, 0, b);
+        for (int r = 0; r < RDS; ++r)
+            read(0, 0, r);
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+        for (int c = 0; c < DPS; ++c) {
             if (NBV > 0) {
 #pragma unroll
-                for (int b = 0; b < NBV; ++b)
-                    acc[c][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][c], fb[ks & 1][b], acc[c][b], 0,
-                                                                        0, 0);
-                if (ks + 1 < KS) {
-                    read_a(ks + 1, (ks + 1) & 1, c);
-                    if (c < NBV)
-                        read_b(ks + 1, (ks + 1) & 1, c);
+                for (int i = c * MPC; i < (c + 1) * MPC; ++i) {
+                    const int a = i / FB, b = i % FB;
+                    if (b < NBV)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][a], fb[ks & 1][b], acc[a][b],
+                                                                            0, 0, 0);
                 }
-                if (NBV == 4) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                    if (ks + 1 < KS)
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                    if (ks + 1 < KS)
-                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (ks + 1 < KS) {
+#pragma unroll
+                    for (int r = c * RPC; r < (c + 1) * RPC && r < RDS; ++r)
+                        read(ks + 1, (ks + 1) & 1, r);
+                }
+                if (NBV == FB) {
+#pragma unroll
+                    for (int m = 0; m < MPC; ++m) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        if (ks + 1 < KS && m < RPC && c * RPC + m < RDS)
+                            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
                 }
             }
             __builtin_amdgcn_sched_barrier(0);
-            dma(ks * 4 + c);
+            dma(ks * DPS + c);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -402,22 +421,22 @@ __device__ __forceinline__ void k_step(const uint16_t *cur, uint32_t nxt, f32x16
 // Epilogue of a 256x256 tile: bias, activation, bf16 store of the rows
 // inside [row0, row_end) and features < N.  Accumulators are read
 // unconditionally and only the stores are predicated, so no accumulator has
-// to live outside its AGPR.
-template <int NBV, bool GELU, bool BIAS>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], uint16_t *__restrict__ C,
+// to live outside its register.
+template <class G, int NBV, bool GELU, bool BIAS>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[G::FA][G::FB], uint16_t *__restrict__ C,
                                            const uint16_t *__restrict__ bseg, int64_t row0, int64_t row_end, int n0,
                                            int N, int wn, int wm, int r32, int khalf)
 {
 #pragma unroll
     for (int b = 0; b < NBV; ++b) {
-        const int64_t row = row0 + wm * 128 + b * 32 + r32;
+        const int64_t row = row0 + wm * G::WTM + b * 32 + r32;
         const bool row_ok = row < row_end;
         uint16_t *crow = C + (row_ok ? row : row0) * N;
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
+        for (int a = 0; a < G::FA; ++a) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * 128 + a * 32 + 8 * g + 4 * khalf;
+                const int n = n0 + wn * G::WTN + a * 32 + 8 * g + 4 * khalf;
                 const bool ok = row_ok && n < N;
                 float v0 = acc[a][b][4 * g + 0], v1 = acc[a][b][4 * g + 1];
                 float v2 = acc[a][b][4 * g + 2], v3 = acc[a][b][4 * g + 3];
@@ -445,28 +464,30 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], uint16_t *
 }
 
 // One 256x256 tile over K steps [kt_lo, kt_hi).  With PART the raw fp32
-// accumulators go to `part` (one 256 KB slab, lane-major per register) for a
-// later fixed-order reduction; otherwise the epilogue stores bf16.
-template <int BK, int STAGES, int NBV, bool GELU, bool BIAS, bool PART>
+// accumulators go to `part` (one 256 KB slab: per wave, per register, lane
+// fastest) for a later fixed-order reduction; otherwise the epilogue stores
+// bf16.
+template <int BK, int STAGES, class G, int NBV, bool GELU, bool BIAS, bool PART>
 __device__ __forceinline__ void tile_256(const uint16_t *__restrict__ A, const uint16_t *__restrict__ wseg,
                                          const uint16_t *__restrict__ bseg, uint16_t *__restrict__ C,
                                          float *__restrict__ part, uint16_t *smem, int64_t row0, int64_t row_end,
                                          int n0, int N, int K, int kt_lo, int kt_hi)
 {
+    constexpr int NW = G::NW, FA = G::FA, FB = G::FB;
     constexpr int CPR = BK / 8;            // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;          // rows filled per DMA instruction (1 KB)
-    constexpr int NQ = kL / (4 * RPI);     // DMA instructions per operand per wave
+    constexpr int NQ = kL / (NW * RPI);    // DMA instructions per operand per wave
     constexpr int STAGE = 2 * kL * BK;     // bf16 elements per stage (W then A)
     constexpr int PER_STAGE = 2 * NQ;      // DMA instructions per thread per stage
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int wn = wave & 1, wm = wave >> 1;
+    const int wn = wave % G::WGN_, wm = wave / G::WGN_;
     const int r32 = lane & 31, khalf = lane >> 5;
 
-    // Instruction q of this wave fills LDS rows R = (4q + wave) * RPI ..
+    // Instruction q of this wave fills LDS rows R = (NW q + wave) * RPI ..
     // R + RPI - 1; lane -> row R + lane / CPR, physical chunk lane % CPR,
     // which holds logical chunk (lane % CPR) ^ swizzle(row).  The byte offset
-    // of that row is vbase + q * 4 * RPI * K * 2 (the q part is scalar).  The
+    // of that row is vbase + q * NW * RPI * K * 2 (the q part is scalar).  The
     // buffer resources cover exactly the tile's valid rows: rows past the
     // weight matrix or the segment end read as zeros.
     const uint32_t row_bytes = (uint32_t)K * 2u;
@@ -480,11 +501,11 @@ __device__ __forceinline__ void tile_256(const uint16_t *__restrict__ A, const u
     const i32x4 ra = make_rsrc(A + row0 * K, (uint32_t)arows * row_bytes);
     const uint32_t lds0 = lds_addr(smem);
 
-    f32x16 acc[4][4];
+    f32x16 acc[FA][FB];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int a = 0; a < FA; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < FB; ++b)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
                 acc[a][b][v] = 0.f;
@@ -498,8 +519,8 @@ __device__ __forceinline__ void tile_256(const uint16_t *__restrict__ A, const u
 #pragma unroll
         for (int i = 0; i < 2 * NQ; ++i) {
             const int q = i >> 1;
-            const uint32_t R = (uint32_t)((4 * q + wave) * RPI);
-            const uint32_t so = (uint32_t)q * (4u * RPI) * row_bytes + so_k;
+            const uint32_t R = (uint32_t)((NW * q + wave) * RPI);
+            const uint32_t so = (uint32_t)q * (uint32_t)(NW * RPI) * row_bytes + so_k;
             dma16((i & 1) ? ra : rw, vbase, so, dst + (uint32_t)((i & 1) * (kL * BK) + R * BK) * 2u);
         }
     }
@@ -509,9 +530,9 @@ __device__ __forceinline__ void tile_256(const uint16_t *__restrict__ A, const u
     for (int kt = kt_lo; kt < kt_hi; ++kt) {
         const int fill = kt + STAGES - 1;
         const uint32_t so_k = fill < kt_hi ? (uint32_t)fill * (BK * 2) : kOutOfRange;
-        k_step<BK, NBV>(smem + ((kt - kt_lo) % STAGES) * STAGE,
-                        lds0 + (uint32_t)(((fill - kt_lo) % STAGES) * STAGE) * 2u, acc, rw, ra, vbase, so_k, row_bytes,
-                        wave, wn, wm, r32, khalf, sw);
+        k_step<BK, G, NBV>(smem + ((kt - kt_lo) % STAGES) * STAGE,
+                           lds0 + (uint32_t)(((fill - kt_lo) % STAGES) * STAGE) * 2u, acc, rw, ra, vbase, so_k,
+                           row_bytes, wave, wn, wm, r32, khalf, sw);
         // Stage kt+1 must have landed; the STAGES-2 stages issued after it
         // may stay in flight.
         wait_vmcnt<(STAGES - 2) * PER_STAGE>();
@@ -520,16 +541,16 @@ __device__ __forceinline__ void tile_256(const uint16_t *__restrict__ A, const u
     wait_vmcnt<0>(); // the zero-fill copies of the last steps must land before the next tile's copies
 
     if (PART) {
-        float *dst = part + (size_t)wave * (256 * 64) + lane;
+        float *dst = part + (size_t)wave * (FA * FB * 16 * 64) + lane;
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < FA; ++a)
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
+            for (int b = 0; b < FB; ++b)
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
-                    dst[((a * 4 + b) * 16 + v) * 64] = acc[a][b][v];
+                    dst[((a * FB + b) * 16 + v) * 64] = acc[a][b][v];
     } else {
-        store_tile<NBV, GELU, BIAS>(acc, C, bseg, row0, row_end, n0, N, wn, wm, r32, khalf);
+        store_tile<G, NBV, GELU, BIAS>(acc, C, bseg, row0, row_end, n0, N, wn, wm, r32, khalf);
     }
 }
 
@@ -562,17 +583,23 @@ __device__ __forceinline__ TailPlan plan_tail(int64_t total, int G, int KT, bool
     return p;
 }
 
-template <int BK, int STAGES, bool GELU, bool BIAS, bool PART>
+template <int BK, int STAGES, class G, bool GELU, bool BIAS, bool PART>
 __device__ __forceinline__ void tile_any(int nbv, const uint16_t *A, const uint16_t *wseg, const uint16_t *bseg,
                                          uint16_t *C, float *part, uint16_t *smem, int64_t row0, int64_t row_end,
                                          int n0, int N, int K, int kt_lo, int kt_hi)
 {
+    if (G::FB == 4) {
+        switch (nbv) {
+        case 4: tile_256<BK, STAGES, G, (G::FB >= 4 ? 4 : G::FB), GELU, BIAS, PART>(A, wseg, bseg, C, part, smem, row0, row_end, n0, N, K, kt_lo, kt_hi); return;
+        case 3: tile_256<BK, STAGES, G, (G::FB >= 3 ? 3 : G::FB), GELU, BIAS, PART>(A, wseg, bseg, C, part, smem, row0, row_end, n0, N, K, kt_lo, kt_hi); return;
+        default: break;
+        }
+    }
     switch (nbv) {
-    case 4: tile_256<BK, STAGES, 4, GELU, BIAS, PART>(A, wseg, bseg, C, part, smem, row0, row_end, n0, N, K, kt_lo, kt_hi); break;
-    case 3: tile_256<BK, STAGES, 3, GELU, BIAS, PART>(A, wseg, bseg, C, part, smem, row0, row_end, n0, N, K, kt_lo, kt_hi); break;
-    case 2: tile_256<BK, STAGES, 2, GELU, BIAS, PART>(A, wseg, bseg, C, part, smem, row0, row_end, n0, N, K, kt_lo, kt_hi); break;
-    case 1: tile_256<BK, STAGES, 1, GELU, BIAS, PART>(A, wseg, bseg, C, part, smem, row0, row_end, n0, N, K, kt_lo, kt_hi); break;
-    default: tile_256<BK, STAGES, 0, GELU, BIAS, PART>(A, wseg, bseg, C, part, smem, row0, row_end, n0, N, K, kt_lo, kt_hi); break;
+    case 2: tile_256<BK, STAGES, G, (G::FB >= 2 ? 2 : G::FB), GELU, BIAS, PART>(A, wseg, bseg, C, part, smem, row0, row_end, n0, N, K, kt_lo, kt_hi); break;
+    case 1: tile_256<BK, STAGES, G, 1, GELU, BIAS, PART>(A, wseg, bseg, C, part, smem, row0, row_end, n0, N, K, kt_lo, kt_hi); break;
+    case 0: tile_256<BK, STAGES, G, 0, GELU, BIAS, PART>(A, wseg, bseg, C, part, smem, row0, row_end, n0, N, K, kt_lo, kt_hi); break;
+    default: break;
     }
 }
 
@@ -600,19 +627,26 @@ __device__ __forceinline__ TileLoc locate(const int *tb, const int32_t *seg, int
     return t;
 }
 
-template <int BK, int STAGES, bool GELU, bool BIAS>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_256(const uint16_t *__restrict__ A,
-                                                                const int32_t *__restrict__ seg, int S,
-                                                                int64_t max_rows, const uint16_t *__restrict__ W,
-                                                                const uint16_t *__restrict__ bias,
-                                                                uint16_t *__restrict__ C, int N, int K,
-                                                                float *__restrict__ part_ws)
+template <class G> __device__ __forceinline__ int valid_b(const TileLoc &t, int wm)
+{
+    const int64_t left = t.row_end - (t.row0 + (int64_t)wm * G::WTM);
+    return left <= 0 ? 0 : (left >= G::WTM ? G::FB : (int)((left + 31) / 32));
+}
+
+template <int BK, int STAGES, class G, bool GELU, bool BIAS>
+__global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_bf16_256(const uint16_t *__restrict__ A,
+                                                                       const int32_t *__restrict__ seg, int S,
+                                                                       int64_t max_rows,
+                                                                       const uint16_t *__restrict__ W,
+                                                                       const uint16_t *__restrict__ bias,
+                                                                       uint16_t *__restrict__ C, int N, int K,
+                                                                       float *__restrict__ part_ws)
 {
     __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * 2 * kL * BK];
     __shared__ int tb[kMaxSeg + 1];
     build_tile_prefix<kL>(seg, S, max_rows, tb);
 
-    const int wm = (threadIdx.x >> 6) >> 1;
+    const int wm = (threadIdx.x >> 6) / G::WGN_;
     const int NT = (N + kL - 1) / kL;
     const int KT = K / BK;
     const int64_t total = (int64_t)tb[S] * NT;
@@ -625,11 +659,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_256(const uint16_t *
     const int64_t rlo = plan.F * xcd / kXcds, rhi = plan.F * (xcd + 1) / kXcds;
     for (int64_t L = rlo + j; L < rhi; L += per) {
         const TileLoc t = locate(tb, seg, S, max_rows, NT, L);
-        const int64_t left = t.row_end - (t.row0 + wm * 128);
-        const int nbv = left <= 0 ? 0 : (left >= 128 ? 4 : (int)((left + 31) / 32));
-        tile_any<BK, STAGES, GELU, BIAS, false>(nbv, A, W + (int64_t)t.s * N * K,
-                                                bias ? bias + (int64_t)t.s * N : nullptr, C, nullptr, smem, t.row0,
-                                                t.row_end, t.n0, N, K, 0, KT);
+        tile_any<BK, STAGES, G, GELU, BIAS, false>(valid_b<G>(t, wm), A, W + (int64_t)t.s * N * K,
+                                                   bias ? bias + (int64_t)t.s * N : nullptr, C, nullptr, smem, t.row0,
+                                                   t.row_end, t.n0, N, K, 0, KT);
         __syncthreads(); // the next tile's copies overwrite stages still read here
     }
     // Tail: one K range of one tail tile per block.
@@ -638,82 +670,82 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_bf16_256(const uint16_t *
         const int64_t L = plan.F + u / plan.sk;
         const int c = u % plan.sk;
         const TileLoc t = locate(tb, seg, S, max_rows, NT, L);
-        const int64_t left = t.row_end - (t.row0 + wm * 128);
-        const int nbv = left <= 0 ? 0 : (left >= 128 ? 4 : (int)((left + 31) / 32));
         const int klo = (int)((int64_t)KT * c / plan.sk), khi = (int)((int64_t)KT * (c + 1) / plan.sk);
-        tile_any<BK, STAGES, GELU, BIAS, true>(nbv, A, W + (int64_t)t.s * N * K, nullptr, C,
-                                               part_ws + (size_t)u * (kL * kL), smem, t.row0, t.row_end, t.n0, N, K,
-                                               klo, khi);
+        tile_any<BK, STAGES, G, GELU, BIAS, true>(valid_b<G>(t, wm), A, W + (int64_t)t.s * N * K, nullptr, C,
+                                                  part_ws + (size_t)u * (kL * kL), smem, t.row0, t.row_end, t.n0, N,
+                                                  K, klo, khi);
     }
 }
 
 // Sums the K-range partials of each tail tile in range order and applies the
 // bias, activation and bf16 store; a no-op when the GEMM had no split tail.
-// Block = (tail tile, GEMM wave w, row sub-tile b); its four waves take the
-// four feature sub-tiles a.  Each lane loads its 16 accumulators of every
-// K range up front (all independent loads), then sums them in range order.
-template <bool GELU, bool BIAS>
-__global__ __launch_bounds__(256) void grouped_gemm_reduce(const int32_t *__restrict__ seg, int S, int64_t max_rows,
-                                                           const uint16_t *__restrict__ bias,
-                                                           uint16_t *__restrict__ C, int N, int K, int BKused, int G,
-                                                           const float *__restrict__ part_ws)
+// Block = (tail tile, GEMM wave w); its FA waves take the feature sub-tiles
+// a and loop over the row sub-tiles b.  Each lane loads its 16 accumulators
+// of every K range up front (independent loads), then sums in range order.
+template <class G, bool GELU, bool BIAS>
+__global__ __launch_bounds__(64 * G::FA) void grouped_gemm_reduce(const int32_t *__restrict__ seg, int S,
+                                                                  int64_t max_rows, const uint16_t *__restrict__ bias,
+                                                                  uint16_t *__restrict__ C, int N, int K, int BKused,
+                                                                  int Gsize, const float *__restrict__ part_ws)
 {
     __shared__ int tb[kMaxSeg + 1];
     build_tile_prefix<kL>(seg, S, max_rows, tb);
     const int NT = (N + kL - 1) / kL;
     const int64_t total = (int64_t)tb[S] * NT;
-    const TailPlan plan = plan_tail(total, G, K / BKused, true);
-    const int tile = blockIdx.x >> 4, wave = (blockIdx.x >> 2) & 3, b = blockIdx.x & 3;
+    const TailPlan plan = plan_tail(total, Gsize, K / BKused, true);
+    const int tile = blockIdx.x / G::NW, wave = blockIdx.x % G::NW;
     if (plan.rem == 0 || tile >= plan.rem)
         return;
     const int lane = threadIdx.x & 63, a = threadIdx.x >> 6;
-    const int wn = wave & 1, wm = wave >> 1;
+    const int wn = wave % G::WGN_, wm = wave / G::WGN_;
     const int r32 = lane & 31, khalf = lane >> 5;
     const TileLoc t = locate(tb, seg, S, max_rows, NT, plan.F + tile);
-    const float *src = part_ws + (size_t)tile * plan.sk * (kL * kL) + (size_t)wave * (256 * 64) +
-                       (size_t)((a * 4 + b) * 16) * 64 + lane;
-    float v[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-        v[r] = src[(size_t)r * 64];
-#pragma unroll
-    for (int c = 1; c < 8; ++c) {
-        if (c < plan.sk) {
-            float w[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                w[r] = src[(size_t)c * (kL * kL) + (size_t)r * 64];
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                v[r] += w[r];
-        }
-    }
-    const int64_t row = t.row0 + wm * 128 + b * 32 + r32;
-    const bool row_ok = row < t.row_end;
-    uint16_t *crow = C + (row_ok ? row : t.row0) * N;
     const uint16_t *bseg = bias ? bias + (int64_t)t.s * N : nullptr;
+    for (int b = 0; b < G::FB; ++b) {
+        const float *src = part_ws + (size_t)tile * plan.sk * (kL * kL) +
+                           (size_t)wave * (G::FA * G::FB * 16 * 64) + (size_t)((a * G::FB + b) * 16) * 64 + lane;
+        float v[16];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const int n = t.n0 + wn * 128 + a * 32 + 8 * g + 4 * khalf;
-        float v0 = v[4 * g], v1 = v[4 * g + 1], v2 = v[4 * g + 2], v3 = v[4 * g + 3];
-        if (BIAS) {
-            const uint2 bb = *reinterpret_cast<const uint2 *>(bseg + (n < N ? n : 0));
-            v0 += bf16_bits_to_f32(bb.x & 0xFFFFu);
-            v1 += bf16_bits_to_f32(bb.x >> 16);
-            v2 += bf16_bits_to_f32(bb.y & 0xFFFFu);
-            v3 += bf16_bits_to_f32(bb.y >> 16);
+        for (int r = 0; r < 16; ++r)
+            v[r] = src[(size_t)r * 64];
+#pragma unroll
+        for (int c = 1; c < 8; ++c) {
+            if (c < plan.sk) {
+                float w[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    w[r] = src[(size_t)c * (kL * kL) + (size_t)r * 64];
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    v[r] += w[r];
+            }
         }
-        if (GELU) {
-            v0 = gelu_erf(v0);
-            v1 = gelu_erf(v1);
-            v2 = gelu_erf(v2);
-            v3 = gelu_erf(v3);
+        const int64_t row = t.row0 + wm * G::WTM + b * 32 + r32;
+        const bool row_ok = row < t.row_end;
+        uint16_t *crow = C + (row_ok ? row : t.row0) * N;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int n = t.n0 + wn * G::WTN + a * 32 + 8 * g + 4 * khalf;
+            float v0 = v[4 * g], v1 = v[4 * g + 1], v2 = v[4 * g + 2], v3 = v[4 * g + 3];
+            if (BIAS) {
+                const uint2 bb = *reinterpret_cast<const uint2 *>(bseg + (n < N ? n : 0));
+                v0 += bf16_bits_to_f32(bb.x & 0xFFFFu);
+                v1 += bf16_bits_to_f32(bb.x >> 16);
+                v2 += bf16_bits_to_f32(bb.y & 0xFFFFu);
+                v3 += bf16_bits_to_f32(bb.y >> 16);
+            }
+            if (GELU) {
+                v0 = gelu_erf(v0);
+                v1 = gelu_erf(v1);
+                v2 = gelu_erf(v2);
+                v3 = gelu_erf(v3);
+            }
+            uint2 o;
+            o.x = pack_bf16x2(v0, v1);
+            o.y = pack_bf16x2(v2, v3);
+            if (row_ok && n < N)
+                *reinterpret_cast<uint2 *>(crow + n) = o;
         }
-        uint2 o;
-        o.x = pack_bf16x2(v0, v1);
-        o.y = pack_bf16x2(v2, v3);
-        if (row_ok && n < N)
-            *reinterpret_cast<uint2 *>(crow + n) = o;
     }
 }
 
@@ -801,12 +833,16 @@ int device_cus()
 }
 
 #ifndef MOE_GEMM_BK
-#define MOE_GEMM_BK 32
+#define MOE_GEMM_BK 64
 #endif
 #ifndef MOE_GEMM_STAGES
-#define MOE_GEMM_STAGES 3
+#define MOE_GEMM_STAGES 2
+#endif
+#ifndef MOE_GEMM_WGM
+#define MOE_GEMM_WGM 4
 #endif
 constexpr int kLargeBK = MOE_GEMM_BK, kLargeStages = MOE_GEMM_STAGES;
+typedef Grid<2, MOE_GEMM_WGM> LargeGrid;
 
 int large_grid(int64_t max_rows, int S, int N)
 {
@@ -824,21 +860,22 @@ int large_grid(int64_t max_rows, int S, int N)
 moe_status_t run_bf16_256(const void *a, const int32_t *seg, int S, int64_t max_rows, int N, int K, const void *w,
                          const void *bias, int act, void *out, float *part_ws, hipStream_t stream)
 {
+    typedef LargeGrid G;
     const int grid = large_grid(max_rows, S, N);
-    auto *k = act == 1 ? (bias ? grouped_gemm_bf16_256<kLargeBK, kLargeStages, true, true>
-                               : grouped_gemm_bf16_256<kLargeBK, kLargeStages, true, false>)
-                       : (bias ? grouped_gemm_bf16_256<kLargeBK, kLargeStages, false, true>
-                               : grouped_gemm_bf16_256<kLargeBK, kLargeStages, false, false>);
-    k<<<(unsigned)grid, 256, 0, stream>>>((const uint16_t *)a, seg, S, max_rows, (const uint16_t *)w,
-                                          (const uint16_t *)bias, (uint16_t *)out, N, K, part_ws);
+    auto *k = act == 1 ? (bias ? grouped_gemm_bf16_256<kLargeBK, kLargeStages, G, true, true>
+                               : grouped_gemm_bf16_256<kLargeBK, kLargeStages, G, true, false>)
+                       : (bias ? grouped_gemm_bf16_256<kLargeBK, kLargeStages, G, false, true>
+                               : grouped_gemm_bf16_256<kLargeBK, kLargeStages, G, false, false>);
+    k<<<(unsigned)grid, 64 * G::NW, 0, stream>>>((const uint16_t *)a, seg, S, max_rows, (const uint16_t *)w,
+                                                 (const uint16_t *)bias, (uint16_t *)out, N, K, part_ws);
     if (moe_status_t st = check_launch("grouped_gemm_bf16_256"))
         return st;
     if (!part_ws)
         return MOE_OK;
-    auto *r = act == 1 ? (bias ? grouped_gemm_reduce<true, true> : grouped_gemm_reduce<true, false>)
-                       : (bias ? grouped_gemm_reduce<false, true> : grouped_gemm_reduce<false, false>);
-    r<<<(unsigned)(grid / 2 * 16), 256, 0, stream>>>(seg, S, max_rows, (const uint16_t *)bias, (uint16_t *)out, N,
-                                                     K, kLargeBK, grid, part_ws);
+    auto *r = act == 1 ? (bias ? grouped_gemm_reduce<G, true, true> : grouped_gemm_reduce<G, true, false>)
+                       : (bias ? grouped_gemm_reduce<G, false, true> : grouped_gemm_reduce<G, false, false>);
+    r<<<(unsigned)(grid / 2 * G::NW), 64 * G::FA, 0, stream>>>(seg, S, max_rows, (const uint16_t *)bias,
+                                                              (uint16_t *)out, N, K, kLargeBK, grid, part_ws);
     return check_launch("grouped_gemm_reduce");
 }
 
