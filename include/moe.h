@@ -98,12 +98,12 @@ int64_t moe_max_rows(int64_t T, int E, int k, float capacity_factor, int num_loc
  * x [T,d] (dtype), w_router [E,d] f32, b_router [E] f32 or NULL (zero bias).
  * topk_idx [T,k] i32 and topk_w [T,k] f32 are required; expert_count [E],
  * f [E], P [E], l_aux [1] may each be NULL (not written).
- * ws: moe_route_workspace_size(T, E) bytes.
+ * ws: moe_route_workspace_size(T, d, E) bytes.
  * Errors: INVALID_ARG for T < 0, d < 1, E < 1, k < 1, k > E, NULL x, w_router,
  * topk_idx or topk_w; UNSUPPORTED for E > 1024, k > 32, d % 8 != 0;
  * WORKSPACE for a small ws.
  * ------------------------------------------------------------------------ */
-size_t moe_route_workspace_size(int64_t T, int E);
+size_t moe_route_workspace_size(int64_t T, int d, int E);
 moe_status_t moe_route(const void *x, moe_dtype_t dtype, const float *w_router,
                        const float *b_router, int64_t T, int d, int E, int k, float alpha,
                        int32_t *topk_idx, float *topk_w, int32_t *expert_count, float *f,

@@ -56,8 +56,8 @@ def test_max_rows(lib):
 
 def test_workspace_sizes(lib):
     from top_routing_expert_route_amd import api
-    assert lib.moe_route_workspace_size(4096, 8) > 4096 * 8 * 4
-    assert lib.moe_route_workspace_size(0, 8) == 0
+    assert lib.moe_route_workspace_size(4096, 4096, 8) > 4096 * 8 * 4
+    assert lib.moe_route_workspace_size(0, 64, 8) == 0
     assert lib.moe_dispatch_workspace_size(4096, 2, 8) > 0
     p = api.Problem(4096, 4096, 8, 2, 16384, 0.0, 0, 0, 0, 0.01, api.MOE_BF16)
     n = lib.moe_forward_workspace_size(ctypes.byref(p))

@@ -68,7 +68,7 @@ def lib():
     L.moe_status_string.argtypes, L.moe_status_string.restype = [I], ctypes.c_char_p
     L.moe_last_error.argtypes, L.moe_last_error.restype = [], ctypes.c_char_p
     L.moe_max_rows.argtypes, L.moe_max_rows.restype = [I64, I, I, F, I], I64
-    L.moe_route_workspace_size.argtypes, L.moe_route_workspace_size.restype = [I64, I], SZ
+    L.moe_route_workspace_size.argtypes, L.moe_route_workspace_size.restype = [I64, I, I], SZ
     L.moe_route.argtypes = [P, I, P, P, I64, I, I, I, F, P, P, P, P, P, P, P, SZ, P]
     L.moe_route.restype = I
     L.moe_dispatch_workspace_size.argtypes, L.moe_dispatch_workspace_size.restype = [I64, I, I], SZ
@@ -138,7 +138,7 @@ def moe_route(x: torch.Tensor, w_router: torch.Tensor, b_router: Optional[torch.
                f=torch.empty(E, dtype=torch.float32, device=dev),
                P=torch.empty(E, dtype=torch.float32, device=dev),
                l_aux=torch.empty(1, dtype=torch.float32, device=dev))
-    nb = lib().moe_route_workspace_size(T, E)
+    nb = lib().moe_route_workspace_size(T, d, E)
     ws = _ws(nb, dev)
     check(lib().moe_route(_p(x), _dt(x), _p(w_router), _p(b_router), T, d, E, k, alpha,
                           _p(out["topk_idx"]), _p(out["topk_w"]), _p(out["expert_count"]), _p(out["f"]),

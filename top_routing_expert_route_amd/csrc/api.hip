@@ -163,7 +163,7 @@ ForwardWs carve_forward(const moe_problem_t *p, const moe_outputs_t *out, void *
     w.f = out->f;
     w.P = out->P;
     w.l_aux = out->l_aux;
-    w.route_ws = cv.take<char>(route_ws_bytes(p->T, p->E));
+    w.route_ws = cv.take<char>(route_ws_bytes(p->T, p->d, p->E));
     w.seg_offsets = out->seg_offsets ? out->seg_offsets : cv.take<int32_t>((size_t)E_loc + 1);
     w.kept_count = out->kept_count ? out->kept_count : cv.take<int32_t>((size_t)E_loc);
     w.slot_row = out->slot_row ? out->slot_row : cv.take<int32_t>((size_t)Tk);
@@ -213,11 +213,11 @@ int64_t moe_max_rows(int64_t T, int E, int k, float capacity_factor, int num_loc
     return rows;
 }
 
-size_t moe_route_workspace_size(int64_t T, int E)
+size_t moe_route_workspace_size(int64_t T, int d, int E)
 {
-    if (T < 0 || E < 1)
+    if (T < 0 || E < 1 || d < 1)
         return 0;
-    return route_ws_bytes(T, E);
+    return route_ws_bytes(T, d, E);
 }
 
 moe_status_t moe_route(const void *x, moe_dtype_t dtype, const float *w_router, const float *b_router, int64_t T,
@@ -227,7 +227,7 @@ moe_status_t moe_route(const void *x, moe_dtype_t dtype, const float *w_router, 
     clear_error();
     if (moe_status_t s = check_route_args(x, dtype, w_router, T, d, E, k, topk_idx, topk_w))
         return s;
-    if (moe_status_t s = check_ws(ws, ws_bytes, route_ws_bytes(T, E), "route"))
+    if (moe_status_t s = check_ws(ws, ws_bytes, route_ws_bytes(T, d, E), "route"))
         return s;
     return launch_route(x, dtype, w_router, b_router, T, d, E, k, alpha, topk_idx, topk_w, expert_count, f, P,
                         l_aux, ws, stream);

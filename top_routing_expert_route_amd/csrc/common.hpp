@@ -76,7 +76,8 @@ struct Carver {
 // -------------------------------------------------- internal launchers ---
 // These assume validated arguments; the public entry points validate.
 
-size_t route_ws_bytes(int64_t T, int E);
+size_t route_ws_bytes(int64_t T, int d, int E);
+size_t gemm_ws_bytes();
 moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, const float *b_router,
                           int64_t T, int d, int E, int k, float alpha, int32_t *topk_idx, float *topk_w,
                           int32_t *expert_count, float *f, float *P, float *l_aux, void *ws,
@@ -89,11 +90,15 @@ moe_status_t launch_dispatch(const void *x, moe_dtype_t dt, const int32_t *topk_
                              int32_t *kept_count, int32_t *slot_row, int32_t *row_src, void *x_perm,
                              int64_t max_rows, int32_t *n_dropped, void *ws, hipStream_t stream);
 
-size_t gemm_ws_bytes();
 moe_status_t launch_grouped_gemm(const void *a, const int32_t *seg_offsets, int num_segments,
                                  int64_t max_rows, int N, int K, moe_dtype_t dt, const void *w,
                                  const void *bias, int activation, void *out, void *ws, size_t ws_bytes,
                                  hipStream_t stream);
+
+// Router logits as a bf16 GEMM: x [T, d] against w3 [E, 3d] = (hi | mid | lo)
+// bf16 pieces of the fp32 router weight; fp32 logits [T, E].  Needs d % 64 == 0.
+moe_status_t launch_router_gemm(const void *x, const void *w3, int64_t T, int d, int E, float *logits, void *ws,
+                                size_t ws_bytes, hipStream_t stream);
 
 moe_status_t launch_combine(const void *y_perm, int64_t max_rows, const int32_t *slot_row,
                             const float *topk_w, const void *y_shared, int64_t T, int d, int k,

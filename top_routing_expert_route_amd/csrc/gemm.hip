@@ -305,10 +305,14 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // at m0 + 16 * lane.  Written as inline assembly so that the compiler's
 // wait-count pass does not track it (it would wait for every copy before
 // any LDS read); the kernel keeps the vmcnt accounting itself.  The
-// instruction writes no registers.
+// instruction writes no registers.  The compiler's hazard recognizer does
+// not look inside inline assembly, so the block carries its own wait states:
+// the M0 write just before it needs one, and a scalar offset that a VALU op
+// wrote (readfirstlane, or a reload of a spilled SGPR with v_readlane) needs
+// five before a vector memory instruction may read it.
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t m0)
 {
-    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                  :
                  : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)),
                    "{m0}"(__builtin_amdgcn_readfirstlane(m0))
@@ -351,8 +355,9 @@ template <int WGN, int WGM> struct Grid {
 // stalling the wave in a burst.
 template <int BK, class G, int NBV>
 __device__ __forceinline__ void k_step(const uint16_t *cur, uint32_t nxt, f32x16 (&acc)[G::FA][G::FB], i32x4 rw,
-                                       i32x4 ra, uint32_t vbase, uint32_t so_k, uint32_t row_bytes, int wave, int wn,
-                                       int wm, int r32, int khalf, int sw)
+                                       i32x4 ra, uint32_t vbase, uint32_t vbase_a, uint32_t so_w, uint32_t so_a,
+                                       uint32_t row_w, uint32_t row_a, int wave, int wn, int wm, int r32, int khalf,
+                                       int sw)
 {
     constexpr int FA = G::FA, FB = G::FB, NW = G::NW;
     constexpr int CPR = BK / 8, RPI = 64 / CPR, NQ = kL / (NW * RPI), KS = BK / 16;
@@ -377,8 +382,9 @@ __device__ __forceinline__ void k_step(const uint16_t *cur, uint32_t nxt, f32x16
     auto dma = [&](int i) { // copy i of DPW: W rows for even i, A rows for odd i
         const int q = i >> 1;
         const uint32_t R = (uint32_t)((NW * q + wave) * RPI);
-        const uint32_t so = (uint32_t)q * (uint32_t)(NW * RPI) * row_bytes + so_k;
-        dma16((i & 1) ? ra : rw, vbase, so, nxt + (uint32_t)((i & 1) * (kL * BK) + R * BK) * 2u);
+        const uint32_t so = (i & 1) ? (uint32_t)q * (uint32_t)(NW * RPI) * row_a + so_a
+                                    : (uint32_t)q * (uint32_t)(NW * RPI) * row_w + so_w;
+        dma16((i & 1) ? ra : rw, (i & 1) ? vbase_a : vbase, so, nxt + (uint32_t)((i & 1) * (kL * BK) + R * BK) * 2u);
     };
     if (NBV > 0) {
 #pragma unroll
@@ -418,12 +424,44 @@ __device__ __forceinline__ void k_step(const uint16_t *cur, uint32_t nxt, f32x16
     }
 }
 
-// Epilogue of a 256x256 tile: bias, activation, bf16 store of the rows
-// inside [row0, row_end) and features < N.  Accumulators are read
-// unconditionally and only the stores are predicated, so no accumulator has
-// to live outside its register.
-template <class G, int NBV, bool GELU, bool BIAS>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[G::FA][G::FB], uint16_t *__restrict__ C,
+// Epilogue of a 256x256 tile: bias, activation and store of the rows inside
+// [row0, row_end) and features < N, as bf16 (rounded to nearest even) or,
+// with F32OUT, as fp32.  Accumulators are read unconditionally and only the
+// stores are predicated, so no accumulator has to live outside its register.
+template <bool GELU, bool BIAS, bool F32OUT>
+__device__ __forceinline__ void store4(void *C, const uint16_t *__restrict__ bseg, int64_t row, bool row_ok, int n,
+                                       int N, float v0, float v1, float v2, float v3)
+{
+    if (BIAS) {
+        const uint2 bb = *reinterpret_cast<const uint2 *>(bseg + (n < N ? n : 0));
+        v0 += bf16_bits_to_f32(bb.x & 0xFFFFu);
+        v1 += bf16_bits_to_f32(bb.x >> 16);
+        v2 += bf16_bits_to_f32(bb.y & 0xFFFFu);
+        v3 += bf16_bits_to_f32(bb.y >> 16);
+    }
+    if (GELU) {
+        v0 = gelu_erf(v0);
+        v1 = gelu_erf(v1);
+        v2 = gelu_erf(v2);
+        v3 = gelu_erf(v3);
+    }
+    const bool ok = row_ok && n < N;
+    const int64_t at = (ok ? row : 0) * N + (ok ? n : 0);
+    if (F32OUT) {
+        const f32x4 o = {v0, v1, v2, v3};
+        if (ok)
+            *reinterpret_cast<f32x4 *>((float *)C + at) = o;
+    } else {
+        uint2 o;
+        o.x = pack_bf16x2(v0, v1);
+        o.y = pack_bf16x2(v2, v3);
+        if (ok)
+            *reinterpret_cast<uint2 *>((uint16_t *)C + at) = o;
+    }
+}
+
+template <class G, int NBV, bool GELU, bool BIAS, bool F32OUT>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[G::FA][G::FB], void *C,
                                            const uint16_t *__restrict__ bseg, int64_t row0, int64_t row_end, int n0,
                                            int N, int wn, int wm, int r32, int khalf)
 {
@@ -431,33 +469,13 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[G::FA][G::FB], ui
     for (int b = 0; b < NBV; ++b) {
         const int64_t row = row0 + wm * G::WTM + b * 32 + r32;
         const bool row_ok = row < row_end;
-        uint16_t *crow = C + (row_ok ? row : row0) * N;
 #pragma unroll
         for (int a = 0; a < G::FA; ++a) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + wn * G::WTN + a * 32 + 8 * g + 4 * khalf;
-                const bool ok = row_ok && n < N;
-                float v0 = acc[a][b][4 * g + 0], v1 = acc[a][b][4 * g + 1];
-                float v2 = acc[a][b][4 * g + 2], v3 = acc[a][b][4 * g + 3];
-                if (BIAS) {
-                    const uint2 bb = *reinterpret_cast<const uint2 *>(bseg + (n < N ? n : 0));
-                    v0 += bf16_bits_to_f32(bb.x & 0xFFFFu);
-                    v1 += bf16_bits_to_f32(bb.x >> 16);
-                    v2 += bf16_bits_to_f32(bb.y & 0xFFFFu);
-                    v3 += bf16_bits_to_f32(bb.y >> 16);
-                }
-                if (GELU) {
-                    v0 = gelu_erf(v0);
-                    v1 = gelu_erf(v1);
-                    v2 = gelu_erf(v2);
-                    v3 = gelu_erf(v3);
-                }
-                uint2 o;
-                o.x = pack_bf16x2(v0, v1);
-                o.y = pack_bf16x2(v2, v3);
-                if (ok)
-                    *reinterpret_cast<uint2 *>(crow + n) = o;
+                store4<GELU, BIAS, F32OUT>(C, bseg, row, row_ok, n, N, acc[a][b][4 * g + 0], acc[a][b][4 * g + 1],
+                                           acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]);
             }
         }
     }
@@ -467,11 +485,11 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[G::FA][G::FB], ui
 // accumulators go to `part` (one 256 KB slab: per wave, per register, lane
 // fastest) for a later fixed-order reduction; otherwise the epilogue stores
 // bf16.
-template <int BK, int STAGES, class G, int NBV, bool GELU, bool BIAS, bool PART>
+template <int BK, int STAGES, class G, int NBV, bool GELU, bool BIAS, bool F32OUT, bool PART>
 __device__ __forceinline__ void tile_256(const uint16_t *__restrict__ A, const uint16_t *__restrict__ wseg,
-                                         const uint16_t *__restrict__ bseg, uint16_t *__restrict__ C,
+                                         const uint16_t *__restrict__ bseg, void *__restrict__ C,
                                          float *__restrict__ part, uint16_t *smem, int64_t row0, int64_t row_end,
-                                         int n0, int N, int K, int kt_lo, int kt_hi)
+                                         int n0, int N, int K, int Ka, int kt_lo, int kt_hi)
 {
     constexpr int NW = G::NW, FA = G::FA, FB = G::FB;
     constexpr int CPR = BK / 8;            // 16-byte chunks per row
@@ -490,15 +508,19 @@ __device__ __forceinline__ void tile_256(const uint16_t *__restrict__ A, const u
     // of that row is vbase + q * NW * RPI * K * 2 (the q part is scalar).  The
     // buffer resources cover exactly the tile's valid rows: rows past the
     // weight matrix or the segment end read as zeros.
-    const uint32_t row_bytes = (uint32_t)K * 2u;
+    // A's rows have Ka elements: its K offset wraps every Ka (Ka = K for a
+    // plain GEMM; the router's split weight repeats the activations thrice).
+    const uint32_t row_bytes = (uint32_t)K * 2u, row_a = (uint32_t)Ka * 2u;
+    const int KTa = Ka / BK;
     const int lrow = lane / CPR;
     const int prow = wave * RPI + lrow;
     const int lchunk = (lane % CPR) ^ swz<BK>(prow);
     const uint32_t vbase = (uint32_t)prow * row_bytes + (uint32_t)lchunk * 16u;
+    const uint32_t vbase_a = (uint32_t)prow * row_a + (uint32_t)lchunk * 16u;
     const int wrows = min(kL, N - n0);
     const int arows = (int)(row_end - row0);
     const i32x4 rw = make_rsrc(wseg + (int64_t)n0 * K, (uint32_t)wrows * row_bytes);
-    const i32x4 ra = make_rsrc(A + row0 * K, (uint32_t)arows * row_bytes);
+    const i32x4 ra = make_rsrc(A + row0 * Ka, (uint32_t)arows * row_a);
     const uint32_t lds0 = lds_addr(smem);
 
     f32x16 acc[FA][FB];
@@ -515,13 +537,17 @@ __device__ __forceinline__ void tile_256(const uint16_t *__restrict__ A, const u
     // copy past kt_hi reads out of range: zeros).
     for (int p = 0; p < STAGES - 1; ++p) {
         const uint32_t dst = lds0 + (uint32_t)(p * STAGE) * 2u;
-        const uint32_t so_k = kt_lo + p < kt_hi ? (uint32_t)(kt_lo + p) * (BK * 2) : kOutOfRange;
+        const bool live = kt_lo + p < kt_hi;
+        const uint32_t so_w = live ? (uint32_t)(kt_lo + p) * (BK * 2) : kOutOfRange;
+        const uint32_t so_a = live ? (uint32_t)((kt_lo + p) % KTa) * (BK * 2) : kOutOfRange;
 #pragma unroll
         for (int i = 0; i < 2 * NQ; ++i) {
             const int q = i >> 1;
             const uint32_t R = (uint32_t)((NW * q + wave) * RPI);
-            const uint32_t so = (uint32_t)q * (uint32_t)(NW * RPI) * row_bytes + so_k;
-            dma16((i & 1) ? ra : rw, vbase, so, dst + (uint32_t)((i & 1) * (kL * BK) + R * BK) * 2u);
+            const uint32_t so = (i & 1) ? (uint32_t)q * (uint32_t)(NW * RPI) * row_a + so_a
+                                        : (uint32_t)q * (uint32_t)(NW * RPI) * row_bytes + so_w;
+            dma16((i & 1) ? ra : rw, (i & 1) ? vbase_a : vbase, so,
+                  dst + (uint32_t)((i & 1) * (kL * BK) + R * BK) * 2u);
         }
     }
     wait_vmcnt<(STAGES - 2) * PER_STAGE>();
@@ -529,10 +555,12 @@ __device__ __forceinline__ void tile_256(const uint16_t *__restrict__ A, const u
 
     for (int kt = kt_lo; kt < kt_hi; ++kt) {
         const int fill = kt + STAGES - 1;
-        const uint32_t so_k = fill < kt_hi ? (uint32_t)fill * (BK * 2) : kOutOfRange;
+        const bool live = fill < kt_hi;
+        const uint32_t so_w = live ? (uint32_t)fill * (BK * 2) : kOutOfRange;
+        const uint32_t so_a = live ? (uint32_t)(fill % KTa) * (BK * 2) : kOutOfRange;
         k_step<BK, G, NBV>(smem + ((kt - kt_lo) % STAGES) * STAGE,
-                           lds0 + (uint32_t)(((fill - kt_lo) % STAGES) * STAGE) * 2u, acc, rw, ra, vbase, so_k,
-                           row_bytes, wave, wn, wm, r32, khalf, sw);
+                           lds0 + (uint32_t)(((fill - kt_lo) % STAGES) * STAGE) * 2u, acc, rw, ra, vbase, vbase_a,
+                           so_w, so_a, row_bytes, row_a, wave, wn, wm, r32, khalf, sw);
         // Stage kt+1 must have landed; the STAGES-2 stages issued after it
         // may stay in flight.
         wait_vmcnt<(STAGES - 2) * PER_STAGE>();
@@ -550,7 +578,7 @@ __device__ __forceinline__ void tile_256(const uint16_t *__restrict__ A, const u
                 for (int v = 0; v < 16; ++v)
                     dst[((a * FB + b) * 16 + v) * 64] = acc[a][b][v];
     } else {
-        store_tile<G, NBV, GELU, BIAS>(acc, C, bseg, row0, row_end, n0, N, wn, wm, r32, khalf);
+        store_tile<G, NBV, GELU, BIAS, F32OUT>(acc, C, bseg, row0, row_end, n0, N, wn, wm, r32, khalf);
     }
 }
 
@@ -583,24 +611,27 @@ __device__ __forceinline__ TailPlan plan_tail(int64_t total, int G, int KT, bool
     return p;
 }
 
-template <int BK, int STAGES, class G, bool GELU, bool BIAS, bool PART>
+template <int BK, int STAGES, class G, bool GELU, bool BIAS, bool F32OUT, bool PART>
 __device__ __forceinline__ void tile_any(int nbv, const uint16_t *A, const uint16_t *wseg, const uint16_t *bseg,
-                                         uint16_t *C, float *part, uint16_t *smem, int64_t row0, int64_t row_end,
-                                         int n0, int N, int K, int kt_lo, int kt_hi)
+                                         void *C, float *part, uint16_t *smem, int64_t row0, int64_t row_end, int n0,
+                                         int N, int K, int Ka, int kt_lo, int kt_hi)
 {
+#define MOE_TILE(V) tile_256<BK, STAGES, G, V, GELU, BIAS, F32OUT, PART>(A, wseg, bseg, C, part, smem, row0, row_end, \
+                                                                     n0, N, K, Ka, kt_lo, kt_hi)
     if (G::FB == 4) {
         switch (nbv) {
-        case 4: tile_256<BK, STAGES, G, (G::FB >= 4 ? 4 : G::FB), GELU, BIAS, PART>(A, wseg, bseg, C, part, smem, row0, row_end, n0, N, K, kt_lo, kt_hi); return;
-        case 3: tile_256<BK, STAGES, G, (G::FB >= 3 ? 3 : G::FB), GELU, BIAS, PART>(A, wseg, bseg, C, part, smem, row0, row_end, n0, N, K, kt_lo, kt_hi); return;
+        case 4: MOE_TILE(G::FB >= 4 ? 4 : G::FB); return;
+        case 3: MOE_TILE(G::FB >= 3 ? 3 : G::FB); return;
         default: break;
         }
     }
     switch (nbv) {
-    case 2: tile_256<BK, STAGES, G, (G::FB >= 2 ? 2 : G::FB), GELU, BIAS, PART>(A, wseg, bseg, C, part, smem, row0, row_end, n0, N, K, kt_lo, kt_hi); break;
-    case 1: tile_256<BK, STAGES, G, 1, GELU, BIAS, PART>(A, wseg, bseg, C, part, smem, row0, row_end, n0, N, K, kt_lo, kt_hi); break;
-    case 0: tile_256<BK, STAGES, G, 0, GELU, BIAS, PART>(A, wseg, bseg, C, part, smem, row0, row_end, n0, N, K, kt_lo, kt_hi); break;
+    case 2: MOE_TILE(G::FB >= 2 ? 2 : G::FB); break;
+    case 1: MOE_TILE(1); break;
+    case 0: MOE_TILE(0); break;
     default: break;
     }
+#undef MOE_TILE
 }
 
 // Location of tile L of the list: segment, rows and first feature.
@@ -633,13 +664,13 @@ template <class G> __device__ __forceinline__ int valid_b(const TileLoc &t, int 
     return left <= 0 ? 0 : (left >= G::WTM ? G::FB : (int)((left + 31) / 32));
 }
 
-template <int BK, int STAGES, class G, bool GELU, bool BIAS>
+template <int BK, int STAGES, class G, bool GELU, bool BIAS, bool F32OUT>
 __global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_bf16_256(const uint16_t *__restrict__ A,
                                                                        const int32_t *__restrict__ seg, int S,
                                                                        int64_t max_rows,
                                                                        const uint16_t *__restrict__ W,
                                                                        const uint16_t *__restrict__ bias,
-                                                                       uint16_t *__restrict__ C, int N, int K,
+                                                                       void *__restrict__ C, int N, int K, int Ka,
                                                                        float *__restrict__ part_ws)
 {
     __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * 2 * kL * BK];
@@ -659,9 +690,9 @@ __global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_bf16_256(const uin
     const int64_t rlo = plan.F * xcd / kXcds, rhi = plan.F * (xcd + 1) / kXcds;
     for (int64_t L = rlo + j; L < rhi; L += per) {
         const TileLoc t = locate(tb, seg, S, max_rows, NT, L);
-        tile_any<BK, STAGES, G, GELU, BIAS, false>(valid_b<G>(t, wm), A, W + (int64_t)t.s * N * K,
-                                                   bias ? bias + (int64_t)t.s * N : nullptr, C, nullptr, smem, t.row0,
-                                                   t.row_end, t.n0, N, K, 0, KT);
+        tile_any<BK, STAGES, G, GELU, BIAS, F32OUT, false>(valid_b<G>(t, wm), A, W + (int64_t)t.s * N * K,
+                                                           bias ? bias + (int64_t)t.s * N : nullptr, C, nullptr, smem,
+                                                           t.row0, t.row_end, t.n0, N, K, Ka, 0, KT);
         __syncthreads(); // the next tile's copies overwrite stages still read here
     }
     // Tail: one K range of one tail tile per block.
@@ -671,9 +702,9 @@ __global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_bf16_256(const uin
         const int c = u % plan.sk;
         const TileLoc t = locate(tb, seg, S, max_rows, NT, L);
         const int klo = (int)((int64_t)KT * c / plan.sk), khi = (int)((int64_t)KT * (c + 1) / plan.sk);
-        tile_any<BK, STAGES, G, GELU, BIAS, true>(valid_b<G>(t, wm), A, W + (int64_t)t.s * N * K, nullptr, C,
-                                                  part_ws + (size_t)u * (kL * kL), smem, t.row0, t.row_end, t.n0, N,
-                                                  K, klo, khi);
+        tile_any<BK, STAGES, G, GELU, BIAS, F32OUT, true>(valid_b<G>(t, wm), A, W + (int64_t)t.s * N * K, nullptr,
+                                                          C, part_ws + (size_t)u * (kL * kL), smem, t.row0, t.row_end,
+                                                          t.n0, N, K, Ka, klo, khi);
     }
 }
 
@@ -682,10 +713,10 @@ __global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_bf16_256(const uin
 // Block = (tail tile, GEMM wave w); its FA waves take the feature sub-tiles
 // a and loop over the row sub-tiles b.  Each lane loads its 16 accumulators
 // of every K range up front (independent loads), then sums in range order.
-template <class G, bool GELU, bool BIAS>
+template <class G, bool GELU, bool BIAS, bool F32OUT>
 __global__ __launch_bounds__(64 * G::FA) void grouped_gemm_reduce(const int32_t *__restrict__ seg, int S,
                                                                   int64_t max_rows, const uint16_t *__restrict__ bias,
-                                                                  uint16_t *__restrict__ C, int N, int K, int BKused,
+                                                                  void *__restrict__ C, int N, int K, int BKused,
                                                                   int Gsize, const float *__restrict__ part_ws)
 {
     __shared__ int tb[kMaxSeg + 1];
@@ -722,29 +753,11 @@ __global__ __launch_bounds__(64 * G::FA) void grouped_gemm_reduce(const int32_t 
         }
         const int64_t row = t.row0 + wm * G::WTM + b * 32 + r32;
         const bool row_ok = row < t.row_end;
-        uint16_t *crow = C + (row_ok ? row : t.row0) * N;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int n = t.n0 + wn * G::WTN + a * 32 + 8 * g + 4 * khalf;
-            float v0 = v[4 * g], v1 = v[4 * g + 1], v2 = v[4 * g + 2], v3 = v[4 * g + 3];
-            if (BIAS) {
-                const uint2 bb = *reinterpret_cast<const uint2 *>(bseg + (n < N ? n : 0));
-                v0 += bf16_bits_to_f32(bb.x & 0xFFFFu);
-                v1 += bf16_bits_to_f32(bb.x >> 16);
-                v2 += bf16_bits_to_f32(bb.y & 0xFFFFu);
-                v3 += bf16_bits_to_f32(bb.y >> 16);
-            }
-            if (GELU) {
-                v0 = gelu_erf(v0);
-                v1 = gelu_erf(v1);
-                v2 = gelu_erf(v2);
-                v3 = gelu_erf(v3);
-            }
-            uint2 o;
-            o.x = pack_bf16x2(v0, v1);
-            o.y = pack_bf16x2(v2, v3);
-            if (row_ok && n < N)
-                *reinterpret_cast<uint2 *>(crow + n) = o;
+            store4<GELU, BIAS, F32OUT>(C, bseg, row, row_ok, n, N, v[4 * g], v[4 * g + 1], v[4 * g + 2],
+                                       v[4 * g + 3]);
         }
     }
 }
@@ -857,26 +870,31 @@ int large_grid(int64_t max_rows, int S, int N)
     return (int)grid;
 }
 
-moe_status_t run_bf16_256(const void *a, const int32_t *seg, int S, int64_t max_rows, int N, int K, const void *w,
-                         const void *bias, int act, void *out, float *part_ws, hipStream_t stream)
+template <bool GELU, bool BIAS, bool F32OUT>
+moe_status_t run_large(const void *a, const int32_t *seg, int S, int64_t max_rows, int N, int K, int Ka,
+                       const void *w, const void *bias, void *out, float *part_ws, hipStream_t stream)
 {
     typedef LargeGrid G;
     const int grid = large_grid(max_rows, S, N);
-    auto *k = act == 1 ? (bias ? grouped_gemm_bf16_256<kLargeBK, kLargeStages, G, true, true>
-                               : grouped_gemm_bf16_256<kLargeBK, kLargeStages, G, true, false>)
-                       : (bias ? grouped_gemm_bf16_256<kLargeBK, kLargeStages, G, false, true>
-                               : grouped_gemm_bf16_256<kLargeBK, kLargeStages, G, false, false>);
-    k<<<(unsigned)grid, 64 * G::NW, 0, stream>>>((const uint16_t *)a, seg, S, max_rows, (const uint16_t *)w,
-                                                 (const uint16_t *)bias, (uint16_t *)out, N, K, part_ws);
+    grouped_gemm_bf16_256<kLargeBK, kLargeStages, G, GELU, BIAS, F32OUT><<<(unsigned)grid, 64 * G::NW, 0, stream>>>(
+        (const uint16_t *)a, seg, S, max_rows, (const uint16_t *)w, (const uint16_t *)bias, out, N, K, Ka, part_ws);
     if (moe_status_t st = check_launch("grouped_gemm_bf16_256"))
         return st;
     if (!part_ws)
         return MOE_OK;
-    auto *r = act == 1 ? (bias ? grouped_gemm_reduce<G, true, true> : grouped_gemm_reduce<G, true, false>)
-                       : (bias ? grouped_gemm_reduce<G, false, true> : grouped_gemm_reduce<G, false, false>);
-    r<<<(unsigned)(grid / 2 * G::NW), 64 * G::FA, 0, stream>>>(seg, S, max_rows, (const uint16_t *)bias,
-                                                              (uint16_t *)out, N, K, kLargeBK, grid, part_ws);
+    grouped_gemm_reduce<G, GELU, BIAS, F32OUT><<<(unsigned)(grid / 2 * G::NW), 64 * G::FA, 0, stream>>>(
+        seg, S, max_rows, (const uint16_t *)bias, out, N, K, kLargeBK, grid, part_ws);
     return check_launch("grouped_gemm_reduce");
+}
+
+moe_status_t run_bf16_256(const void *a, const int32_t *seg, int S, int64_t max_rows, int N, int K, const void *w,
+                         const void *bias, int act, void *out, float *part_ws, hipStream_t stream)
+{
+    if (act == 1)
+        return bias ? run_large<true, true, false>(a, seg, S, max_rows, N, K, K, w, bias, out, part_ws, stream)
+                    : run_large<true, false, false>(a, seg, S, max_rows, N, K, K, w, bias, out, part_ws, stream);
+    return bias ? run_large<false, true, false>(a, seg, S, max_rows, N, K, K, w, bias, out, part_ws, stream)
+                : run_large<false, false, false>(a, seg, S, max_rows, N, K, K, w, bias, out, part_ws, stream);
 }
 
 template <int BN, int BM>
@@ -931,6 +949,14 @@ moe_status_t launch_grouped_gemm(const void *a, const int32_t *seg_offsets, int 
         grouped_gemm_f32<false><<<g, 256, 0, stream>>>((const float *)a, seg_offsets, S, max_rows, (const float *)w,
                                                         (const float *)bias, (float *)out, N, K);
     return check_launch("grouped_gemm_f32");
+}
+
+moe_status_t launch_router_gemm(const void *x, const void *w3, int64_t T, int d, int E, float *logits, void *ws,
+                                size_t ws_bytes, hipStream_t stream)
+{
+    // logits[T, E] = sum over the three bf16 pieces p of x . w3[:, p*d:(p+1)*d]^T
+    float *part = (ws && ws_bytes >= gemm_ws_bytes()) ? (float *)ws : nullptr;
+    return run_large<false, false, true>(x, nullptr, 1, T, E, 3 * d, d, w3, nullptr, logits, part, stream);
 }
 
 } // namespace moe

@@ -312,6 +312,26 @@ __global__ __launch_bounds__(64 * NW) void route_fused_small(const uint16_t *__r
     }
 }
 
+// w3[e, p*d + i] = bf16 piece p of w_router[e, i]: hi = w truncated to bf16,
+// mid = (w - hi) truncated, lo = w - hi - mid (exact); hi + mid + lo = w.
+__global__ __launch_bounds__(256) void route_split_weight(const float *__restrict__ wr, int64_t n, int d,
+                                                          uint16_t *__restrict__ w3)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n)
+        return;
+    const int64_t e = i / d, c = i % d;
+    const float w = wr[i];
+    const float h = trunc_bf16(w);
+    const float r1 = w - h;
+    const float m = trunc_bf16(r1);
+    const float l = r1 - m;
+    uint16_t *row = w3 + e * 3 * (int64_t)d;
+    row[c] = (uint16_t)(__float_as_uint(h) >> 16);
+    row[d + c] = (uint16_t)(__float_as_uint(m) >> 16);
+    row[2 * d + c] = (uint16_t)(__float_as_uint(l) >> 16);
+}
+
 __global__ __launch_bounds__(256) void route_logits_f32(const float *__restrict__ x, const float *__restrict__ wr,
                                                         int64_t T, int d, int E, float *__restrict__ logits)
 {
@@ -514,11 +534,17 @@ static int route_blocks(int64_t T, int E, moe_dtype_t dt)
     return select_blocks(T);
 }
 
-size_t route_ws_bytes(int64_t T, int E)
+static bool router_on_gemm(moe_dtype_t dt, int d, int E) { return dt == MOE_BF16 && E > 64 && d % 64 == 0; }
+
+size_t route_ws_bytes(int64_t T, int d, int E)
 {
-    // enough for either path: logits (two-kernel path) + partials of the larger block count
+    // logits (two-kernel paths) + partials of the larger block count, plus the
+    // split router weight and the grouped GEMM's tail partials for large E
     const int nblk = (int)((T + 15) / 16);
-    return align_up((size_t)T * E * sizeof(float)) + 2 * align_up((size_t)nblk * E * sizeof(float));
+    size_t b = align_up((size_t)T * E * sizeof(float)) + 2 * align_up((size_t)nblk * E * sizeof(float));
+    if (E > 64 && d % 64 == 0)
+        b += align_up((size_t)E * 3 * d * sizeof(uint16_t)) + align_up(gemm_ws_bytes());
+    return b;
 }
 
 moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, const float *b_router,
@@ -532,6 +558,9 @@ moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, 
     float *logits = cv.take<float>((size_t)T * E);
     float *part_p = cv.take<float>((size_t)nblk_max * E);
     int32_t *part_c = cv.take<int32_t>((size_t)nblk_max * E);
+    const bool on_gemm = router_on_gemm(dt, d, E);
+    uint16_t *w3 = on_gemm ? cv.take<uint16_t>((size_t)E * 3 * d) : nullptr;
+    void *gws = on_gemm ? cv.take<char>(gemm_ws_bytes()) : nullptr;
 
     if (T > 0) {
         if (dt == MOE_BF16 && E <= 64) {
@@ -549,7 +578,14 @@ moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, 
             if (moe_status_t s = check_launch("route_fused_small"))
                 return s;
         } else {
-            if (dt == MOE_BF16) {
+            if (on_gemm) {
+                const int64_t n = (int64_t)E * d;
+                route_split_weight<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(w_router, n, d, w3);
+                if (moe_status_t s = check_launch("route_split_weight"))
+                    return s;
+                if (moe_status_t s = launch_router_gemm(x, w3, T, d, E, logits, gws, gemm_ws_bytes(), stream))
+                    return s;
+            } else if (dt == MOE_BF16) {
                 dim3 g((unsigned)((T + 63) / 64), (unsigned)((E + 63) / 64));
                 route_logits_mfma<4, 4><<<g, 256, 0, stream>>>((const uint16_t *)x, w_router, T, d, E, logits);
             } else {
