@@ -312,9 +312,13 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 // five before a vector memory instruction may read it.
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t m0)
 {
+    i32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        r[k] = __builtin_amdgcn_readfirstlane(rsrc[k]);
     asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                  :
-                 : "v"(voff), "s"(rsrc), "s"(__builtin_amdgcn_readfirstlane(soff)),
+                 : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff)),
                    "{m0}"(__builtin_amdgcn_readfirstlane(m0))
                  : "memory");
 }
@@ -328,6 +332,16 @@ __device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes)
     r[2] = (int)bytes;
     r[3] = kRsrcWord3;
     return r;
+}
+
+// Values the whole wave shares, held in scalar registers (the compiler
+// cannot prove that values read from LDS are uniform).
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uni64(int64_t v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void *p)
@@ -353,6 +367,12 @@ template <int WGN, int WGM> struct Grid {
 // the LDS reads of the next sub-step; one copy is issued after each chunk, so
 // the copies trickle out at the rate the address unit drains them instead of
 // stalling the wave in a burst.
+#ifndef MOE_GEMM_CPS
+#define MOE_GEMM_CPS 0 // chunks per 16-wide sub-step; 0: one per copy
+#endif
+#ifndef MOE_GEMM_LEAD
+#define MOE_GEMM_LEAD 8 // copies are spread over LEAD/8 of the K step
+#endif
 template <int BK, class G, int NBV>
 __device__ __forceinline__ void k_step(const uint16_t *cur, uint32_t nxt, f32x16 (&acc)[G::FA][G::FB], i32x4 rw,
                                        i32x4 ra, uint32_t vbase, uint32_t vbase_a, uint32_t so_w, uint32_t so_a,
@@ -361,12 +381,13 @@ __device__ __forceinline__ void k_step(const uint16_t *cur, uint32_t nxt, f32x16
 {
     constexpr int FA = G::FA, FB = G::FB, NW = G::NW;
     constexpr int CPR = BK / 8, RPI = 64 / CPR, NQ = kL / (NW * RPI), KS = BK / 16;
-    constexpr int DPW = 2 * NQ;         // copies per wave per stage
-    constexpr int DPS = DPW / KS;       // copies (= chunks) per sub-step
-    constexpr int MPC = FA * FB / DPS;  // MFMAs per chunk
-    constexpr int RDS = FA + FB;        // fragment reads per sub-step
-    constexpr int RPC = (RDS + DPS - 1) / DPS;
-    static_assert(DPW % KS == 0 && (FA * FB) % DPS == 0, "chunking");
+    constexpr int DPW = 2 * NQ;                                  // copies per wave per stage
+    constexpr int CPS = MOE_GEMM_CPS > 0 ? MOE_GEMM_CPS : DPW / KS; // chunks per sub-step
+    constexpr int NCH = KS * CPS;                                // chunks per K step
+    constexpr int MPC = FA * FB / CPS;                           // MFMAs per chunk
+    constexpr int RDS = FA + FB;                                 // fragment reads per sub-step
+    constexpr int RPC = (RDS + CPS - 1) / CPS;
+    static_assert(DPW % KS == 0 && (FA * FB) % CPS == 0, "chunking");
     const uint16_t *sW = cur;
     const uint16_t *sA = cur + kL * BK;
     bf16x8 fa[2][FA], fb[2][FB];
@@ -394,7 +415,7 @@ __device__ __forceinline__ void k_step(const uint16_t *cur, uint32_t nxt, f32x16
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-        for (int c = 0; c < DPS; ++c) {
+        for (int c = 0; c < CPS; ++c) {
             if (NBV > 0) {
 #pragma unroll
                 for (int i = c * MPC; i < (c + 1) * MPC; ++i) {
@@ -417,9 +438,16 @@ __device__ __forceinline__ void k_step(const uint16_t *cur, uint32_t nxt, f32x16
                     }
                 }
             }
-            __builtin_amdgcn_sched_barrier(0);
-            dma(ks * DPS + c);
-            __builtin_amdgcn_sched_barrier(0);
+            // Copy j goes out after chunk (j * NCH * LEAD) / (8 * DPW).
+            const int g = ks * CPS + c;
+#pragma unroll
+            for (int j = 0; j < DPW; ++j) {
+                if ((j * NCH * MOE_GEMM_LEAD) / (8 * DPW) == g) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    dma(j);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
         }
     }
 }
@@ -593,7 +621,7 @@ struct TailPlan {
     int sk;      // K ranges per tail tile
 };
 
-__device__ __forceinline__ TailPlan plan_tail(int64_t total, int G, int KT, bool have_ws)
+__device__ __forceinline__ TailPlan plan_tail(int64_t total, int G, int KT, bool have_ws, int min_len = 1)
 {
     TailPlan p{total, 0, 1};
     const int64_t R = total / G;
@@ -601,7 +629,7 @@ __device__ __forceinline__ TailPlan plan_tail(int64_t total, int G, int KT, bool
     if (have_ws && rem > 0 && 2 * rem <= G) {
         int sk = (int)(G / rem);
         sk = sk > 8 ? 8 : sk;
-        sk = sk > KT ? KT : sk;
+        sk = sk > KT / min_len ? KT / min_len : sk;
         if (sk >= 2) {
             p.F = R * G;
             p.rem = (int)rem;
@@ -708,6 +736,843 @@ __global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_bf16_256(const uin
     }
 }
 
+// ---------------------------------------------------------------------------
+// Software-pipelined form of the same tiling.  Two LDS stages; within a K
+// step the copies of the next stage go out during the first KS-1 sub-steps,
+// the block synchronises once, before the last sub-step, and the last
+// sub-step's MFMAs cover the LDS reads of the next stage's first sub-step, so
+// the matrix pipe does not drain at K-step boundaries.  The last K step of a
+// tile already copies the first stage of the block's next tile, so that tile
+// starts without a load bubble and its copies overlap this tile's epilogue.
+// ---------------------------------------------------------------------------
+
+// Per-launch copy geometry: per-lane byte offsets (row and swizzled chunk)
+// into a W and an A row, bytes per row, and K steps per A row.
+struct CopyGeo {
+    uint32_t vbase, vbase_a, row_w, row_a;
+    int KTa;
+};
+
+// One stage's source: the tile's buffer resources and the K step's scalar
+// offsets.  A fill with nothing to load uses resources of zero bytes: every
+// copy is then out of range and writes zeros to LDS without touching memory
+// (no branch in the K loop, and the wait counts stay uniform).
+struct Fill {
+    i32x4 rw, ra;
+    uint32_t so_w, so_a;
+};
+
+template <int BK> __device__ __forceinline__ Fill fill_at(i32x4 rw, i32x4 ra, int kt, int KTa)
+{
+    Fill f;
+    f.rw = rw;
+    f.ra = ra;
+    f.so_w = (uint32_t)kt * (BK * 2);
+    f.so_a = (uint32_t)(kt % KTa) * (BK * 2);
+    return f;
+}
+
+template <int BK, class G>
+__device__ __forceinline__ void copy_one(const CopyGeo &cg, const Fill &f, uint32_t dst, int wave, int i)
+{
+    constexpr int CPR = BK / 8, RPI = 64 / CPR, NW = G::NW;
+    const int q = i >> 1;
+    const uint32_t R = (uint32_t)((NW * q + wave) * RPI);
+    const uint32_t so = (i & 1) ? (uint32_t)q * (uint32_t)(NW * RPI) * cg.row_a + f.so_a
+                                : (uint32_t)q * (uint32_t)(NW * RPI) * cg.row_w + f.so_w;
+    dma16((i & 1) ? f.ra : f.rw, (i & 1) ? cg.vbase_a : cg.vbase, so,
+          dst + (uint32_t)((i & 1) * (kL * BK) + R * BK) * 2u);
+}
+
+// This wave's copies except the newest N have landed, every wave got that
+// far, and every wave's LDS reads issued so far have completed.  (Copies
+// complete in issue order.)
+template <int N> __device__ __forceinline__ void stage_barrier()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+#ifndef MOE_PIPE_CPS
+#define MOE_PIPE_CPS 8 // chunks per 16-wide sub-step
+#endif
+#ifndef MOE_PIPE_RCH
+#define MOE_PIPE_RCH 2 // the next sub-step's fragment reads go out in the first RCH chunks
+#endif
+
+// Fragment reads in the order the next sub-step's MFMAs first use them: the
+// MFMA sequence is (a, b) = (i / FB, i % FB), so read r is A fragment a or B
+// fragment b as they first appear in it.  Returns a for A, FA + b for B.
+template <class G> __host__ __device__ constexpr int read_slot(int r)
+{
+    bool ra[G::FA] = {}, rb[G::FB] = {};
+    int n = 0;
+    for (int i = 0; i < G::FA * G::FB; ++i) {
+        const int a = i / G::FB, b = i % G::FB;
+        if (!ra[a]) {
+            ra[a] = true;
+            if (n++ == r)
+                return a;
+        }
+        if (!rb[b]) {
+            rb[b] = true;
+            if (n++ == r)
+                return G::FA + b;
+        }
+    }
+    return -1;
+}
+
+template <int BK, class G, int NBV>
+__device__ __forceinline__ void read_frag(const uint16_t *stage, int ks, bf16x8 (&fa)[G::FA], bf16x8 (&fb)[G::FB],
+                                          int r, int wn, int wm, int r32, int khalf, int sw)
+{
+    const int ch = ((ks * 2 + khalf) ^ sw) * 8;
+    if (r < G::FA) {
+        fa[r] = *reinterpret_cast<const bf16x8 *>(stage + (wn * G::WTN + r * 32 + r32) * BK + ch);
+    } else if (r - G::FA < NBV) {
+        const int b = r - G::FA;
+        fb[b] = *reinterpret_cast<const bf16x8 *>(stage + kL * BK + (wm * G::WTM + b * 32 + r32) * BK + ch);
+    }
+}
+
+// One K step: MFMAs on stage `cur`; the copies of a later stage (`f`, to
+// LDS byte address `fill_lds`) go out during the first KS-1 sub-steps; then
+// one barrier, after which the next stage `nxt` has landed and the last
+// sub-step's MFMAs cover the reads of its first sub-step.
+template <int BK, int STAGES, class G, int NBV>
+__device__ __forceinline__ void k_step_pipe(const uint16_t *cur, const uint16_t *nxt, uint32_t fill_lds,
+                                            const Fill &f, const CopyGeo &cg, f32x16 (&acc)[G::FA][G::FB],
+                                            bf16x8 (&fa)[2][G::FA], bf16x8 (&fb)[2][G::FB], int wave, int wn, int wm,
+                                            int r32, int khalf, int sw)
+{
+    constexpr int FA = G::FA, FB = G::FB;
+    constexpr int CPR = BK / 8, RPI = 64 / CPR, NQ = kL / (G::NW * RPI), KS = BK / 16;
+    constexpr int DPW = 2 * NQ;            // copies per wave per stage
+    constexpr int CPS = MOE_PIPE_CPS < FA * FB ? MOE_PIPE_CPS : FA * FB; // chunks per sub-step
+    constexpr int MPC = FA * FB / CPS;     // MFMAs per chunk
+    constexpr int RDS = FA + FB;           // fragment reads per sub-step
+    constexpr int RCH = MOE_PIPE_RCH < CPS ? MOE_PIPE_RCH : CPS;
+    constexpr int RPC = (RDS + RCH - 1) / RCH; // reads per chunk in the first RCH chunks
+    constexpr int NPRE = (KS - 1) * CPS;   // chunks before the barrier
+    static_assert(KS >= 2 && (FA * FB) % CPS == 0, "chunking");
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const uint16_t *src = ks + 1 < KS ? cur : nxt;
+        const int kn = ks + 1 < KS ? ks + 1 : 0;
+#pragma unroll
+        for (int c = 0; c < CPS; ++c) {
+            if (NBV > 0) {
+#pragma unroll
+                for (int m = 0; m < MPC; ++m) {
+                    const int i = c * MPC + m;
+                    const int a = i / FB, b = i % FB;
+                    if (b < NBV)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][a], fb[ks & 1][b], acc[a][b],
+                                                                            0, 0, 0);
+#pragma unroll
+                    for (int q = 0; q < RPC; ++q) {
+                        const int r = c * RPC + q;
+                        if (c < RCH && r < RDS && (q * MPC) / RPC == m)
+                            read_frag<BK, G, NBV>(src, kn, fa[(ks + 1) & 1], fb[(ks + 1) & 1], read_slot<G>(r), wn,
+                                                  wm, r32, khalf, sw);
+                    }
+                }
+                if (NBV == FB) {
+#pragma unroll
+                    for (int m = 0; m < MPC; ++m) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+                        for (int q = 0; q < RPC; ++q)
+                            if (c < RCH && c * RPC + q < RDS && (q * MPC) / RPC == m)
+                                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+                }
+            }
+            if (ks + 1 < KS) {
+                const int g = ks * CPS + c;
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int j = 0; j < DPW; ++j)
+                    if ((j * NPRE) / DPW == g)
+                        copy_one<BK, G>(cg, f, fill_lds, wave, j);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if (ks == KS - 2) {
+            // the next stage has landed; the STAGES-2 newer ones may be in flight
+            __builtin_amdgcn_sched_barrier(0);
+            stage_barrier<(STAGES - 2) * DPW>();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// Source of the next work item's first stages, for the last K steps of a
+// tile: its resources and K range (len >= STAGES-1), or none.
+struct NextSrc {
+    i32x4 rw, ra;
+    int kt_lo;
+    bool any;
+};
+
+// One tile (or one K range of a tail tile).  On entry ring slot b holds its
+// first K step (landed, behind a barrier) and the next STAGES-2 steps are in
+// flight; on exit the same holds for `next` at the returned slot.
+template <int BK, int STAGES, class G, int NBV, bool GELU, bool BIAS, bool F32OUT, bool PART>
+__device__ __forceinline__ int tile_pipe(const uint16_t *smem, uint32_t lds0, int b, const CopyGeo &cg, i32x4 rw,
+                                         i32x4 ra, int kt_lo, int kt_hi, const NextSrc &next, i32x4 null_w,
+                                         i32x4 null_a, void *C, const uint16_t *bseg, float *part, int64_t row0,
+                                         int64_t row_end, int n0, int N)
+{
+    constexpr int FA = G::FA, FB = G::FB, STAGE = 2 * kL * BK;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wn = wave % G::WGN_, wm = wave / G::WGN_;
+    const int r32 = lane & 31, khalf = lane >> 5;
+    const int sw = swz<BK>(r32);
+
+    f32x16 acc[FA][FB];
+#pragma unroll
+    for (int a = 0; a < FA; ++a)
+#pragma unroll
+        for (int q = 0; q < FB; ++q)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[a][q][v] = 0.f;
+    bf16x8 fa[2][FA], fb[2][FB];
+    if (NBV > 0) {
+#pragma unroll
+        for (int r = 0; r < FA + FB; ++r)
+            read_frag<BK, G, NBV>(smem + b * STAGE, 0, fa[0], fb[0], r, wn, wm, r32, khalf, sw);
+    }
+    for (int kt = kt_lo; kt < kt_hi; ++kt) {
+        const int fs = kt + STAGES - 1; // K step to fill
+        Fill f;
+        if (fs < kt_hi)
+            f = fill_at<BK>(rw, ra, fs, cg.KTa);
+        else if (next.any)
+            f = fill_at<BK>(next.rw, next.ra, next.kt_lo + (fs - kt_hi), cg.KTa);
+        else
+            f = fill_at<BK>(null_w, null_a, 0, cg.KTa);
+        const int bn = b + 1 == STAGES ? 0 : b + 1;
+        const int bf = b == 0 ? STAGES - 1 : b - 1;
+        k_step_pipe<BK, STAGES, G, NBV>(smem + b * STAGE, smem + bn * STAGE, lds0 + (uint32_t)(bf * STAGE) * 2u, f,
+                                        cg, acc, fa, fb, wave, wn, wm, r32, khalf, sw);
+        b = bn;
+    }
+    if (PART) {
+        float *dst = part + (size_t)wave * (FA * FB * 16 * 64) + lane;
+#pragma unroll
+        for (int a = 0; a < FA; ++a)
+#pragma unroll
+            for (int q = 0; q < FB; ++q)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    dst[((a * FB + q) * 16 + v) * 64] = acc[a][q][v];
+    } else {
+        store_tile<G, NBV, GELU, BIAS, F32OUT>(acc, C, bseg, row0, row_end, n0, N, wn, wm, r32, khalf);
+    }
+    return b;
+}
+
+template <int BK, int STAGES, class G, bool GELU, bool BIAS, bool F32OUT, bool PART>
+__device__ __forceinline__ int tile_pipe_any(int nbv, const uint16_t *smem, uint32_t lds0, int b, const CopyGeo &cg,
+                                             i32x4 rw, i32x4 ra, int kt_lo, int kt_hi, const NextSrc &next,
+                                             i32x4 null_w, i32x4 null_a, void *C, const uint16_t *bseg, float *part,
+                                             int64_t row0, int64_t row_end, int n0, int N)
+{
+#define MOE_TP(V)                                                                                                   \
+    tile_pipe<BK, STAGES, G, V, GELU, BIAS, F32OUT, PART>(smem, lds0, b, cg, rw, ra, kt_lo, kt_hi, next, null_w,    \
+                                                          null_a, C, bseg, part, row0, row_end, n0, N)
+    if (G::FB == 4) {
+        switch (nbv) {
+        case 4: return MOE_TP(G::FB >= 4 ? 4 : G::FB);
+        case 3: return MOE_TP(G::FB >= 3 ? 3 : G::FB);
+        default: break;
+        }
+    }
+    switch (nbv) {
+    case 2: return MOE_TP(G::FB >= 2 ? 2 : G::FB);
+    case 1: return MOE_TP(1);
+    default: return MOE_TP(0);
+    }
+#undef MOE_TP
+}
+
+// Work item i of a block: its whole tiles (an XCD-contiguous share of
+// [0, F), as in grouped_gemm_bf16_256), then its tail unit if it has one.
+struct Work {
+    TileLoc t;
+    int kt_lo, kt_hi;
+    int unit; // tail unit, or -1 for a whole tile
+};
+
+// Needs K / BK >= STAGES - 1 (the tail plan keeps every K range that long).
+template <int BK, int STAGES, class G, bool GELU, bool BIAS, bool F32OUT>
+__global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_pipe(const uint16_t *__restrict__ A,
+                                                                   const int32_t *__restrict__ seg, int S,
+                                                                   int64_t max_rows, const uint16_t *__restrict__ W,
+                                                                   const uint16_t *__restrict__ bias,
+                                                                   void *__restrict__ C, int N, int K, int Ka,
+                                                                   float *__restrict__ part_ws)
+{
+    constexpr int CPR = BK / 8, RPI = 64 / CPR, NQ = kL / (G::NW * RPI);
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * 2 * kL * BK];
+    __shared__ int tb[kMaxSeg + 1];
+    build_tile_prefix<kL>(seg, S, max_rows, tb);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / G::WGN_;
+    const int NT = (N + kL - 1) / kL;
+    const int KT = K / BK;
+    const int64_t total = (int64_t)tb[S] * NT;
+    const TailPlan plan = plan_tail(total, (int)gridDim.x, KT, part_ws != nullptr, STAGES - 1);
+
+    const int xcd = blockIdx.x % kXcds;
+    const int per = gridDim.x / kXcds;
+    const int j = blockIdx.x / kXcds;
+    const int64_t rlo = plan.F * xcd / kXcds, rhi = plan.F * (xcd + 1) / kXcds;
+    const int64_t first = rlo + j;
+    const int nw = first < rhi ? (int)((rhi - first + per - 1) / per) : 0;
+    const int unit = blockIdx.x;
+    const bool has_tail = plan.rem > 0 && unit < plan.rem * plan.sk;
+    const int n_work = nw + (has_tail ? 1 : 0);
+    if (n_work == 0)
+        return;
+
+    CopyGeo cg;
+    {
+        const int lrow = lane / CPR;
+        const int prow = wave * RPI + lrow;
+        const int lchunk = (lane % CPR) ^ swz<BK>(prow);
+        cg.row_w = (uint32_t)K * 2u;
+        cg.row_a = (uint32_t)Ka * 2u;
+        cg.vbase = (uint32_t)prow * cg.row_w + (uint32_t)lchunk * 16u;
+        cg.vbase_a = (uint32_t)prow * cg.row_a + (uint32_t)lchunk * 16u;
+        cg.KTa = Ka / BK;
+    }
+    auto work = [&](int i) {
+        Work w;
+        if (i < nw) {
+            w.t = locate(tb, seg, S, max_rows, NT, first + (int64_t)i * per);
+            w.kt_lo = 0;
+            w.kt_hi = KT;
+            w.unit = -1;
+        } else {
+            const int c = unit % plan.sk;
+            w.t = locate(tb, seg, S, max_rows, NT, plan.F + unit / plan.sk);
+            w.kt_lo = (int)((int64_t)KT * c / plan.sk);
+            w.kt_hi = (int)((int64_t)KT * (c + 1) / plan.sk);
+            w.unit = unit;
+        }
+        return w;
+    };
+    auto src_of = [&](const Work &w, i32x4 &rw, i32x4 &ra) {
+        const int wrows = min(kL, N - w.t.n0);
+        const int arows = (int)(w.t.row_end - w.t.row0);
+        rw = make_rsrc(W + (int64_t)w.t.s * N * K + (int64_t)w.t.n0 * K, (uint32_t)wrows * cg.row_w);
+        ra = make_rsrc(A + w.t.row0 * Ka, (uint32_t)arows * cg.row_a);
+    };
+    const i32x4 null_w = make_rsrc(W, 0), null_a = make_rsrc(A, 0);
+
+    const uint32_t lds0 = lds_addr(smem);
+    Work w = work(0);
+    i32x4 rw, ra;
+    src_of(w, rw, ra);
+    // Prologue: the first STAGES-1 K steps of the first work item.
+#pragma unroll
+    for (int p = 0; p < STAGES - 1; ++p) {
+        const Fill f = fill_at<BK>(rw, ra, w.kt_lo + p, cg.KTa);
+#pragma unroll
+        for (int i = 0; i < 2 * NQ; ++i)
+            copy_one<BK, G>(cg, f, lds0 + (uint32_t)(p * 2 * kL * BK) * 2u, wave, i);
+    }
+    stage_barrier<(STAGES - 2) * 2 * NQ>();
+    int b = 0;
+    for (int i = 0; i < n_work; ++i) {
+        Work wn = w;
+        NextSrc next;
+        next.any = i + 1 < n_work;
+        next.rw = null_w;
+        next.ra = null_a;
+        next.kt_lo = 0;
+        if (next.any) {
+            wn = work(i + 1);
+            src_of(wn, next.rw, next.ra);
+            next.kt_lo = wn.kt_lo;
+        }
+        const int nbv = valid_b<G>(w.t, wm);
+        if (w.unit < 0)
+            b = tile_pipe_any<BK, STAGES, G, GELU, BIAS, F32OUT, false>(
+                nbv, smem, lds0, b, cg, rw, ra, w.kt_lo, w.kt_hi, next, null_w, null_a, C,
+                bias ? bias + (int64_t)w.t.s * N : nullptr, nullptr, w.t.row0, w.t.row_end, w.t.n0, N);
+        else
+            b = tile_pipe_any<BK, STAGES, G, GELU, BIAS, F32OUT, true>(
+                nbv, smem, lds0, b, cg, rw, ra, w.kt_lo, w.kt_hi, next, null_w, null_a, C, nullptr,
+                part_ws + (size_t)w.unit * (kL * kL), w.t.row0, w.t.row_end, w.t.n0, N);
+        w = wn;
+        rw = next.rw;
+        ra = next.ra;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Register-staged form: operands marked REG go global -> VGPR two K steps
+// ahead and VGPR -> LDS (ds_write) one step ahead; the others go by LDS-DMA
+// one step ahead.  Two LDS stages plus the staged registers give three
+// stages in flight.  Plain vector loads stream faster into the CU than LDS-DMA
+// copies do, at the cost of the staging registers.
+// ---------------------------------------------------------------------------
+
+template <int BK, class G> struct Staged {
+    static constexpr int DPW = 2 * (kL / (G::NW * (64 / (BK / 8))));
+    u32x4 v[DPW];
+};
+
+// A stage source as plain scalars (base addresses and byte sizes of the
+// tile's W and A rows); the buffer resources are formed where a copy is
+// issued.  Sizes of zero make every copy out of range (zeros, no access).
+struct Src2 {
+    uint64_t wbase, abase;
+    uint32_t wbytes, abytes;
+};
+
+struct Fill2 {
+    Src2 s;
+    uint32_t so_w, so_a;
+};
+
+template <int BK> __device__ __forceinline__ Fill2 fill2_at(const Src2 &s, int kt, int KTa)
+{
+    Fill2 f;
+    f.s = s;
+    f.so_w = (uint32_t)kt * (BK * 2);
+    f.so_a = (uint32_t)(kt % KTa) * (BK * 2);
+    return f;
+}
+
+__device__ __forceinline__ Src2 src2_of(const uint16_t *w, uint32_t wbytes, const uint16_t *a, uint32_t abytes)
+{
+    Src2 s;
+    s.wbase = (uint64_t)uni64((int64_t)(uintptr_t)w);
+    s.abase = (uint64_t)uni64((int64_t)(uintptr_t)a);
+    s.wbytes = (uint32_t)uni((int)wbytes);
+    s.abytes = (uint32_t)uni((int)abytes);
+    return s;
+}
+
+__device__ __forceinline__ i32x4 raw_rsrc(uint64_t base, uint32_t bytes)
+{
+    return make_rsrc((const void *)(uintptr_t)base, bytes);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(uint64_t base, uint32_t bytes, uint32_t voff, uint32_t soff)
+{
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)base, (short)0, (int)bytes, kRsrcWord3);
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Order in which a K step issues its copies: LDS-DMA ones first, then the
+// register loads (so a wait that leaves the register loads in flight has
+// the LDS-DMA copies landed).
+template <bool WREG, bool AREG, int DPW> __device__ __forceinline__ constexpr int copy_order(int n)
+{
+    return (WREG == AREG) ? n : (!WREG ? (n < DPW / 2 ? 2 * n : 2 * (n - DPW / 2) + 1)
+                                       : (n < DPW / 2 ? 2 * n + 1 : 2 * (n - DPW / 2)));
+}
+
+// Copy i of a stage: scalar offset of its rows.
+template <int BK, class G>
+__device__ __forceinline__ uint32_t copy_soff(const CopyGeo &cg, const Fill2 &f, int i)
+{
+    constexpr int CPR = BK / 8, RPI = 64 / CPR, NW = G::NW;
+    const int q = i >> 1;
+    return (i & 1) ? (uint32_t)q * (uint32_t)(NW * RPI) * cg.row_a + f.so_a
+                   : (uint32_t)q * (uint32_t)(NW * RPI) * cg.row_w + f.so_w;
+}
+
+// LDS byte offset (within a stage) of copy i's 16 bytes for this lane.
+template <int BK, class G> __device__ __forceinline__ uint32_t copy_ldsoff(int wave, int lane, int i)
+{
+    constexpr int CPR = BK / 8, RPI = 64 / CPR, NW = G::NW;
+    const int q = i >> 1;
+    const uint32_t R = (uint32_t)((NW * q + wave) * RPI);
+    return (uint32_t)((i & 1) * (kL * BK) + R * BK) * 2u + (uint32_t)lane * 16u;
+}
+
+template <bool WREG, bool AREG> __device__ __forceinline__ constexpr bool in_reg(int i)
+{
+    return (i & 1) ? AREG : WREG;
+}
+
+#ifndef MOE_PIPE_FA1
+#define MOE_PIPE_FA1 0 // 1: single-buffered A fragments (fewer registers, exposed LDS latency)
+#endif
+#ifndef MOE_PIPE_WCH
+#define MOE_PIPE_WCH 1 // the staged registers go to LDS after this many chunks (before any copy)
+#endif
+
+template <int BK, class G, int NBV, bool WREG, bool AREG>
+__device__ __forceinline__ void k_step_pipe2(const uint16_t *cur, uint16_t *nxt, uint32_t nxt_lds, const Fill2 &f1,
+                                             const Fill2 &f2, Staged<BK, G> &stg, const CopyGeo &cg,
+                                             f32x16 (&acc)[G::FA][G::FB], bf16x8 (&fa)[2][G::FA],
+                                             bf16x8 (&fb)[2][G::FB], int wave, int lane, int wn, int wm, int r32,
+                                             int khalf, int sw)
+{
+    constexpr int FA = G::FA, FB = G::FB;
+    constexpr int KS = BK / 16;
+    constexpr int DPW = Staged<BK, G>::DPW;
+    constexpr int NDMA = (WREG ? 0 : DPW / 2) + (AREG ? 0 : DPW / 2);
+    constexpr int NREG = DPW - NDMA;
+    constexpr int CPS = MOE_PIPE_CPS < FA * FB ? MOE_PIPE_CPS : FA * FB;
+    constexpr int MPC = FA * FB / CPS;
+    constexpr int RDS = FA + FB;
+    constexpr int RCH = MOE_PIPE_RCH < CPS ? MOE_PIPE_RCH : CPS;
+    constexpr int RPC = (RDS + RCH - 1) / RCH;
+    constexpr int NPRE = (KS - 1) * CPS;
+    static_assert(KS >= 2 && (FA * FB) % CPS == 0, "chunking");
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const uint16_t *src = ks + 1 < KS ? cur : nxt;
+        const int kn = ks + 1 < KS ? ks + 1 : 0;
+#pragma unroll
+        for (int c = 0; c < CPS; ++c) {
+            if (NBV > 0) {
+#pragma unroll
+                for (int m = 0; m < MPC; ++m) {
+                    const int i = c * MPC + m;
+                    const int a = i / FB, b = i % FB;
+                    if (b < NBV)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[MOE_PIPE_FA1 ? 0 : ks & 1][a],
+                                                                            fb[ks & 1][b], acc[a][b], 0, 0, 0);
+                    if (MOE_PIPE_FA1) {
+                        // A fragment a is single-buffered: its next sub-step's
+                        // value is read once its last MFMA (a, FB-1) has issued;
+                        // B fragments are double-buffered and read first.
+                        if (i < FB)
+                            read_frag<BK, G, NBV>(src, kn, fa[0], fb[(ks + 1) & 1], FA + i, wn, wm, r32, khalf, sw);
+                        if (b == FB - 1)
+                            read_frag<BK, G, NBV>(src, kn, fa[0], fb[(ks + 1) & 1], a, wn, wm, r32, khalf, sw);
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < RPC; ++q) {
+                            const int r = c * RPC + q;
+                            if (c < RCH && r < RDS && (q * MPC) / RPC == m)
+                                read_frag<BK, G, NBV>(src, kn, fa[(ks + 1) & 1], fb[(ks + 1) & 1], read_slot<G>(r),
+                                                      wn, wm, r32, khalf, sw);
+                        }
+                    }
+                }
+                if (NBV == FB) {
+#pragma unroll
+                    for (int m = 0; m < MPC; ++m) {
+                        const int i = c * MPC + m;
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        if (MOE_PIPE_FA1) {
+                            if (i < FB)
+                                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                            if (i % FB == FB - 1)
+                                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                        } else {
+#pragma unroll
+                            for (int q = 0; q < RPC; ++q)
+                                if (c < RCH && c * RPC + q < RDS && (q * MPC) / RPC == m)
+                                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                        }
+                    }
+                }
+            }
+            if (ks + 1 < KS) {
+                const int g = ks * CPS + c;
+                __builtin_amdgcn_sched_barrier(0);
+                if (NREG > 0 && g + 1 == MOE_PIPE_WCH) {
+                    // staged registers (K step kt+1) -> the next stage
+#pragma unroll
+                    for (int j = 0; j < DPW; ++j)
+                        if (in_reg<WREG, AREG>(j))
+                            *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(nxt) + copy_ldsoff<BK, G>(wave, lane, j)) =
+                                stg.v[j];
+                }
+                // copies in order: LDS-DMA ones (step kt+1) first, then the
+                // register loads (step kt+2); copy n goes after chunk n*NPRE/DPW
+#pragma unroll
+                for (int n = 0; n < DPW; ++n) {
+                    if ((n * NPRE) / DPW != g)
+                        continue;
+                    const int j = copy_order<WREG, AREG, DPW>(n);
+                    if (!in_reg<WREG, AREG>(j)) {
+                        const uint32_t so = copy_soff<BK, G>(cg, f1, j);
+                        dma16((j & 1) ? raw_rsrc(f1.s.abase, f1.s.abytes) : raw_rsrc(f1.s.wbase, f1.s.wbytes),
+                              (j & 1) ? cg.vbase_a : cg.vbase, so, nxt_lds + copy_ldsoff<BK, G>(wave, 0, j));
+                    } else {
+                        const uint32_t so = copy_soff<BK, G>(cg, f2, j);
+                        stg.v[j] = (j & 1) ? buf_load16(f2.s.abase, f2.s.abytes, cg.vbase_a, so)
+                                           : buf_load16(f2.s.wbase, f2.s.wbytes, cg.vbase, so);
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        if (ks == KS - 2) {
+            // the next stage is complete (its copies and register writes);
+            // the register loads of the stage after it may be in flight
+            __builtin_amdgcn_sched_barrier(0);
+            stage_barrier<NREG>();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+}
+
+// One tile (or one K range of a tail tile) of the register-staged kernel.
+// On entry LDS stage b holds its first K step (landed, behind a barrier) and
+// the staged registers hold its second; on exit the same holds for the next
+// work item (sw*/sa*: own rows; nw*/na*: the next item's, sizes 0 if none).
+template <int BK, class G, int NBV, bool WREG, bool AREG, bool GELU, bool BIAS, bool F32OUT, bool PART>
+__device__ __forceinline__ int tile_pipe2(uint16_t *smem, uint32_t lds0, int b, const CopyGeo &cg, uint64_t swb,
+                                          uint64_t sab, uint32_t sws, uint32_t sas, int kt_lo, int kt_hi,
+                                          uint64_t nwb, uint64_t nab, uint32_t nws, uint32_t nas, int n_kt_lo,
+                                          Staged<BK, G> &stg, void *C, const uint16_t *bseg, float *part,
+                                          int64_t row0, int64_t row_end, int n0, int N)
+{
+    constexpr int FA = G::FA, FB = G::FB, STAGE = 2 * kL * BK;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wn = wave % G::WGN_, wm = wave / G::WGN_;
+    const int r32 = lane & 31, khalf = lane >> 5;
+    const int sw = swz<BK>(r32);
+
+    f32x16 acc[FA][FB];
+#pragma unroll
+    for (int a = 0; a < FA; ++a)
+#pragma unroll
+        for (int q = 0; q < FB; ++q)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[a][q][v] = 0.f;
+    bf16x8 fa[2][FA], fb[2][FB];
+    if (NBV > 0) {
+#pragma unroll
+        for (int r = 0; r < FA + FB; ++r)
+            read_frag<BK, G, NBV>(smem + b * STAGE, 0, fa[0], fb[0], r, wn, wm, r32, khalf, sw);
+    }
+    for (int kt = kt_lo; kt < kt_hi; ++kt) {
+        // K steps kt+1 (LDS-DMA operands) and kt+2 (register operands): own
+        // rows while inside [kt_lo, kt_hi), else the next item's first steps.
+        Fill2 f1, f2;
+        {
+            const bool own = kt + 1 < kt_hi;
+            f1.s.wbase = own ? swb : nwb;
+            f1.s.abase = own ? sab : nab;
+            f1.s.wbytes = own ? sws : nws;
+            f1.s.abytes = own ? sas : nas;
+            const int k1 = own ? kt + 1 : n_kt_lo + (kt + 1 - kt_hi);
+            f1.so_w = (uint32_t)k1 * (BK * 2);
+            f1.so_a = (uint32_t)(k1 % cg.KTa) * (BK * 2);
+        }
+        {
+            const bool own = kt + 2 < kt_hi;
+            f2.s.wbase = own ? swb : nwb;
+            f2.s.abase = own ? sab : nab;
+            f2.s.wbytes = own ? sws : nws;
+            f2.s.abytes = own ? sas : nas;
+            const int k2 = own ? kt + 2 : n_kt_lo + (kt + 2 - kt_hi);
+            f2.so_w = (uint32_t)k2 * (BK * 2);
+            f2.so_a = (uint32_t)(k2 % cg.KTa) * (BK * 2);
+        }
+        const int bn = b ^ 1;
+        k_step_pipe2<BK, G, NBV, WREG, AREG>(smem + b * STAGE, smem + bn * STAGE, lds0 + (uint32_t)(bn * STAGE) * 2u,
+                                             f1, f2, stg, cg, acc, fa, fb, wave, lane, wn, wm, r32, khalf, sw);
+        b = bn;
+    }
+    if (PART) {
+        float *dst = part + (size_t)wave * (FA * FB * 16 * 64) + lane;
+#pragma unroll
+        for (int a = 0; a < FA; ++a)
+#pragma unroll
+            for (int q = 0; q < FB; ++q)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    dst[((a * FB + q) * 16 + v) * 64] = acc[a][q][v];
+    } else {
+        store_tile<G, NBV, GELU, BIAS, F32OUT>(acc, C, bseg, row0, row_end, n0, N, wn, wm, r32, khalf);
+    }
+    return b;
+}
+
+template <int BK, class G, bool WREG, bool AREG, bool GELU, bool BIAS, bool F32OUT, bool PART>
+__device__ __forceinline__ int tile_pipe2_any(int nbv, uint16_t *smem, uint32_t lds0, int b, const CopyGeo &cg,
+                                              uint64_t swb, uint64_t sab, uint32_t sws, uint32_t sas, int kt_lo,
+                                              int kt_hi, uint64_t nwb, uint64_t nab, uint32_t nws, uint32_t nas,
+                                              int n_kt_lo, Staged<BK, G> &stg, void *C, const uint16_t *bseg,
+                                              float *part, int64_t row0, int64_t row_end, int n0, int N)
+{
+#define MOE_TP2(V)                                                                                                  \
+    tile_pipe2<BK, G, V, WREG, AREG, GELU, BIAS, F32OUT, PART>(smem, lds0, b, cg, swb, sab, sws, sas, kt_lo, kt_hi, \
+                                                               nwb, nab, nws, nas, n_kt_lo, stg, C, bseg, part,     \
+                                                               row0, row_end, n0, N)
+    if (G::FB == 4) {
+        switch (nbv) {
+        case 4: return MOE_TP2(G::FB >= 4 ? 4 : G::FB);
+        case 3: return MOE_TP2(G::FB >= 3 ? 3 : G::FB);
+        default: break;
+        }
+    }
+    switch (nbv) {
+    case 2: return MOE_TP2(G::FB >= 2 ? 2 : G::FB);
+    case 1: return MOE_TP2(1);
+    default: return MOE_TP2(0);
+    }
+#undef MOE_TP2
+}
+
+// Work item i of a block: its whole tiles (an XCD-contiguous share of
+// [0, F)), then its tail unit if it has one; all fields wave-uniform.
+__device__ __forceinline__ Work get_work(int i, int nw, int64_t first, int per, int unit, const TailPlan &plan,
+                                         const int *tb, const int32_t *seg, int S, int64_t max_rows, int NT, int KT)
+{
+    Work w;
+    if (i < nw) {
+        w.t = locate(tb, seg, S, max_rows, NT, first + (int64_t)i * per);
+        w.kt_lo = 0;
+        w.kt_hi = KT;
+        w.unit = -1;
+    } else {
+        const int c = unit % plan.sk;
+        w.t = locate(tb, seg, S, max_rows, NT, plan.F + unit / plan.sk);
+        w.kt_lo = (int)((int64_t)KT * c / plan.sk);
+        w.kt_hi = (int)((int64_t)KT * (c + 1) / plan.sk);
+        w.unit = unit;
+    }
+    w.t.s = uni(w.t.s);
+    w.t.row0 = uni64(w.t.row0);
+    w.t.row_end = uni64(w.t.row_end);
+    w.t.n0 = uni(w.t.n0);
+    w.kt_lo = uni(w.kt_lo);
+    w.kt_hi = uni(w.kt_hi);
+    return w;
+}
+
+// Needs K / BK >= 2 (the tail plan keeps every K range that long).
+template <int BK, class G, bool WREG, bool AREG, bool GELU, bool BIAS, bool F32OUT>
+__global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_pipe2(const uint16_t *__restrict__ A,
+                                                                    const int32_t *__restrict__ seg, int S,
+                                                                    int64_t max_rows, const uint16_t *__restrict__ W,
+                                                                    const uint16_t *__restrict__ bias,
+                                                                    void *__restrict__ C, int N, int K, int Ka,
+                                                                    float *__restrict__ part_ws)
+{
+    constexpr int CPR = BK / 8, RPI = 64 / CPR;
+    constexpr int DPW = Staged<BK, G>::DPW;
+    constexpr int NDMA = (WREG ? 0 : DPW / 2) + (AREG ? 0 : DPW / 2);
+    constexpr int NREG = DPW - NDMA;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * kL * BK];
+    __shared__ int tb[kMaxSeg + 1];
+    build_tile_prefix<kL>(seg, S, max_rows, tb);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / G::WGN_;
+    const int NT = (N + kL - 1) / kL;
+    const int KT = K / BK;
+    const int64_t total = (int64_t)tb[S] * NT;
+    const TailPlan plan = plan_tail(total, (int)gridDim.x, KT, part_ws != nullptr, 2);
+
+    const int xcd = blockIdx.x % kXcds;
+    const int per = gridDim.x / kXcds;
+    const int jb = blockIdx.x / kXcds;
+    const int64_t rlo = plan.F * xcd / kXcds, rhi = plan.F * (xcd + 1) / kXcds;
+    const int64_t first = rlo + jb;
+    const int nw = first < rhi ? (int)((rhi - first + per - 1) / per) : 0;
+    const int unit = blockIdx.x;
+    const bool has_tail = plan.rem > 0 && unit < plan.rem * plan.sk;
+    const int n_work = nw + (has_tail ? 1 : 0);
+    if (n_work == 0)
+        return;
+
+    CopyGeo cg;
+    {
+        const int lrow = lane / CPR;
+        const int prow = wave * RPI + lrow;
+        const int lchunk = (lane % CPR) ^ swz<BK>(prow);
+        cg.row_w = (uint32_t)K * 2u;
+        cg.row_a = (uint32_t)Ka * 2u;
+        cg.vbase = (uint32_t)prow * cg.row_w + (uint32_t)lchunk * 16u;
+        cg.vbase_a = (uint32_t)prow * cg.row_a + (uint32_t)lchunk * 16u;
+        cg.KTa = Ka / BK;
+    }
+    const uint32_t lds0 = lds_addr(smem);
+
+    Work w = get_work(0, nw, first, per, unit, plan, tb, seg, S, max_rows, NT, KT);
+    uint64_t swb = (uint64_t)(uintptr_t)(W + (int64_t)w.t.s * N * K + (int64_t)w.t.n0 * K);
+    uint64_t sab = (uint64_t)(uintptr_t)(A + w.t.row0 * Ka);
+    uint32_t sws = (uint32_t)min(kL, N - w.t.n0) * cg.row_w;
+    uint32_t sas = (uint32_t)(w.t.row_end - w.t.row0) * cg.row_a;
+    Staged<BK, G> stg;
+    // Prologue: K step kt_lo into LDS stage 0, kt_lo+1 into the staged registers.
+    {
+        Fill2 f0;
+        f0.s.wbase = swb;
+        f0.s.abase = sab;
+        f0.s.wbytes = sws;
+        f0.s.abytes = sas;
+        f0.so_w = (uint32_t)w.kt_lo * (BK * 2);
+        f0.so_a = (uint32_t)(w.kt_lo % cg.KTa) * (BK * 2);
+#pragma unroll
+        for (int i = 0; i < DPW; ++i) {
+            const uint32_t so = copy_soff<BK, G>(cg, f0, i);
+            if (in_reg<WREG, AREG>(i))
+                stg.v[i] = (i & 1) ? buf_load16(sab, sas, cg.vbase_a, so) : buf_load16(swb, sws, cg.vbase, so);
+            else
+                dma16((i & 1) ? raw_rsrc(sab, sas) : raw_rsrc(swb, sws), (i & 1) ? cg.vbase_a : cg.vbase, so,
+                      lds0 + copy_ldsoff<BK, G>(wave, 0, i));
+        }
+#pragma unroll
+        for (int i = 0; i < DPW; ++i)
+            if (in_reg<WREG, AREG>(i))
+                *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(smem) + copy_ldsoff<BK, G>(wave, lane, i)) =
+                    stg.v[i];
+        wait_vmcnt<0>();
+        f0.so_w = (uint32_t)(w.kt_lo + 1) * (BK * 2);
+        f0.so_a = (uint32_t)((w.kt_lo + 1) % cg.KTa) * (BK * 2);
+#pragma unroll
+        for (int i = 0; i < DPW; ++i)
+            if (in_reg<WREG, AREG>(i))
+                stg.v[i] = (i & 1) ? buf_load16(sab, sas, cg.vbase_a, copy_soff<BK, G>(cg, f0, i))
+                                   : buf_load16(swb, sws, cg.vbase, copy_soff<BK, G>(cg, f0, i));
+        stage_barrier<NREG>();
+    }
+    int b = 0;
+    for (int i = 0; i < n_work; ++i) {
+        Work wn = w;
+        uint64_t nwb = swb, nab = sab;
+        uint32_t nws = 0, nas = 0;
+        if (i + 1 < n_work) {
+            wn = get_work(i + 1, nw, first, per, unit, plan, tb, seg, S, max_rows, NT, KT);
+            nwb = (uint64_t)(uintptr_t)(W + (int64_t)wn.t.s * N * K + (int64_t)wn.t.n0 * K);
+            nab = (uint64_t)(uintptr_t)(A + wn.t.row0 * Ka);
+            nws = (uint32_t)min(kL, N - wn.t.n0) * cg.row_w;
+            nas = (uint32_t)(wn.t.row_end - wn.t.row0) * cg.row_a;
+        }
+        const int nbv = valid_b<G>(w.t, wm);
+        if (w.unit < 0)
+            b = tile_pipe2_any<BK, G, WREG, AREG, GELU, BIAS, F32OUT, false>(
+                nbv, smem, lds0, b, cg, swb, sab, sws, sas, w.kt_lo, w.kt_hi, nwb, nab, nws, nas, wn.kt_lo, stg, C,
+                bias ? bias + (int64_t)w.t.s * N : nullptr, nullptr, w.t.row0, w.t.row_end, w.t.n0, N);
+        else
+            b = tile_pipe2_any<BK, G, WREG, AREG, GELU, BIAS, F32OUT, true>(
+                nbv, smem, lds0, b, cg, swb, sab, sws, sas, w.kt_lo, w.kt_hi, nwb, nab, nws, nas, wn.kt_lo, stg, C,
+                nullptr, part_ws + (size_t)w.unit * (kL * kL), w.t.row0, w.t.row_end, w.t.n0, N);
+        w = wn;
+        swb = nwb;
+        sab = nab;
+        sws = nws;
+        sas = nas;
+    }
+}
+
 // Sums the K-range partials of each tail tile in range order and applies the
 // bias, activation and bf16 store; a no-op when the GEMM had no split tail.
 // Block = (tail tile, GEMM wave w); its FA waves take the feature sub-tiles
@@ -717,13 +1582,14 @@ template <class G, bool GELU, bool BIAS, bool F32OUT>
 __global__ __launch_bounds__(64 * G::FA) void grouped_gemm_reduce(const int32_t *__restrict__ seg, int S,
                                                                   int64_t max_rows, const uint16_t *__restrict__ bias,
                                                                   void *__restrict__ C, int N, int K, int BKused,
-                                                                  int Gsize, const float *__restrict__ part_ws)
+                                                                  int min_len, int Gsize,
+                                                                  const float *__restrict__ part_ws)
 {
     __shared__ int tb[kMaxSeg + 1];
     build_tile_prefix<kL>(seg, S, max_rows, tb);
     const int NT = (N + kL - 1) / kL;
     const int64_t total = (int64_t)tb[S] * NT;
-    const TailPlan plan = plan_tail(total, Gsize, K / BKused, true);
+    const TailPlan plan = plan_tail(total, Gsize, K / BKused, true, min_len);
     const int tile = blockIdx.x / G::NW, wave = blockIdx.x % G::NW;
     if (plan.rem == 0 || tile >= plan.rem)
         return;
@@ -854,6 +1720,15 @@ int device_cus()
 #ifndef MOE_GEMM_WGM
 #define MOE_GEMM_WGM 4
 #endif
+#ifndef MOE_GEMM_PIPE
+#define MOE_GEMM_PIPE 2
+#endif
+#ifndef MOE_PIPE_WREG
+#define MOE_PIPE_WREG 1
+#endif
+#ifndef MOE_PIPE_AREG
+#define MOE_PIPE_AREG 1
+#endif
 constexpr int kLargeBK = MOE_GEMM_BK, kLargeStages = MOE_GEMM_STAGES;
 typedef Grid<2, MOE_GEMM_WGM> LargeGrid;
 
@@ -876,14 +1751,26 @@ moe_status_t run_large(const void *a, const int32_t *seg, int S, int64_t max_row
 {
     typedef LargeGrid G;
     const int grid = large_grid(max_rows, S, N);
+#if MOE_GEMM_PIPE == 2
+    const int min_len = 2;
+    grouped_gemm_pipe2<kLargeBK, G, MOE_PIPE_WREG, MOE_PIPE_AREG, GELU, BIAS, F32OUT>
+        <<<(unsigned)grid, 64 * G::NW, 0, stream>>>((const uint16_t *)a, seg, S, max_rows, (const uint16_t *)w,
+                                                     (const uint16_t *)bias, out, N, K, Ka, part_ws);
+#elif MOE_GEMM_PIPE
+    const int min_len = kLargeStages - 1;
+    grouped_gemm_pipe<kLargeBK, kLargeStages, G, GELU, BIAS, F32OUT><<<(unsigned)grid, 64 * G::NW, 0, stream>>>(
+        (const uint16_t *)a, seg, S, max_rows, (const uint16_t *)w, (const uint16_t *)bias, out, N, K, Ka, part_ws);
+#else
+    const int min_len = 1;
     grouped_gemm_bf16_256<kLargeBK, kLargeStages, G, GELU, BIAS, F32OUT><<<(unsigned)grid, 64 * G::NW, 0, stream>>>(
         (const uint16_t *)a, seg, S, max_rows, (const uint16_t *)w, (const uint16_t *)bias, out, N, K, Ka, part_ws);
+#endif
     if (moe_status_t st = check_launch("grouped_gemm_bf16_256"))
         return st;
     if (!part_ws)
         return MOE_OK;
     grouped_gemm_reduce<G, GELU, BIAS, F32OUT><<<(unsigned)(grid / 2 * G::NW), 64 * G::FA, 0, stream>>>(
-        seg, S, max_rows, (const uint16_t *)bias, out, N, K, kLargeBK, grid, part_ws);
+        seg, S, max_rows, (const uint16_t *)bias, out, N, K, kLargeBK, min_len, grid, part_ws);
     return check_launch("grouped_gemm_reduce");
 }
 
@@ -935,7 +1822,7 @@ moe_status_t launch_grouped_gemm(const void *a, const int32_t *seg_offsets, int 
         return MOE_OK;
     const int S = seg_offsets ? num_segments : 1;
     if (dt == MOE_BF16) {
-        if (K % kLargeBK == 0) {
+        if (K % 64 == 0 && K / kLargeBK >= (MOE_GEMM_PIPE == 2 ? 2 : kLargeStages - 1)) {
             float *part = (ws && ws_bytes >= gemm_ws_bytes()) ? (float *)ws : nullptr;
             return run_bf16_256(a, seg_offsets, S, max_rows, N, K, w, bias, activation, out, part, stream);
         }
