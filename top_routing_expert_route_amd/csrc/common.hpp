@@ -95,8 +95,9 @@ moe_status_t launch_grouped_gemm(const void *a, const int32_t *seg_offsets, int 
                                  const void *bias, int activation, void *out, void *ws, size_t ws_bytes,
                                  hipStream_t stream);
 
-// Router logits as a bf16 GEMM: x [T, d] against w3 [E, 3d] = (hi | mid | lo)
-// bf16 pieces of the fp32 router weight; fp32 logits [T, E].  Needs d % 64 == 0.
+// Router logits as a bf16 GEMM: x [T, d] against w3 [3E, d] = the hi, mid
+// and lo bf16 pieces of the fp32 router weight stacked along the rows; fp32
+// output [T, 3E] whose three column blocks sum to the logits.  Needs d % 64 == 0.
 moe_status_t launch_router_gemm(const void *x, const void *w3, int64_t T, int d, int E, float *logits, void *ws,
                                 size_t ws_bytes, hipStream_t stream);
 

@@ -1211,8 +1211,8 @@ template <bool WREG, bool AREG> __device__ __forceinline__ constexpr bool in_reg
 #ifndef MOE_PIPE_FA1
 #define MOE_PIPE_FA1 0 // 1: single-buffered A fragments (fewer registers, exposed LDS latency)
 #endif
-#ifndef MOE_PIPE_WCH
-#define MOE_PIPE_WCH 1 // the staged registers go to LDS after this many chunks (before any copy)
+#ifndef MOE_PIPE_WSP
+#define MOE_PIPE_WSP 8 // the staged registers go to LDS over the first WSP chunks of a K step
 #endif
 
 template <int BK, class G, int NBV, bool WREG, bool AREG>
@@ -1233,6 +1233,7 @@ __device__ __forceinline__ void k_step_pipe2(const uint16_t *cur, uint16_t *nxt,
     constexpr int RCH = MOE_PIPE_RCH < CPS ? MOE_PIPE_RCH : CPS;
     constexpr int RPC = (RDS + RCH - 1) / RCH;
     constexpr int NPRE = (KS - 1) * CPS;
+    constexpr int WSP = MOE_PIPE_WSP < NPRE ? MOE_PIPE_WSP : NPRE; // chunks the register writes spread over
     static_assert(KS >= 2 && (FA * FB) % CPS == 0, "chunking");
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -1288,11 +1289,13 @@ __device__ __forceinline__ void k_step_pipe2(const uint16_t *cur, uint16_t *nxt,
             if (ks + 1 < KS) {
                 const int g = ks * CPS + c;
                 __builtin_amdgcn_sched_barrier(0);
-                if (NREG > 0 && g + 1 == MOE_PIPE_WCH) {
-                    // staged registers (K step kt+1) -> the next stage
+                if (NREG > 0) {
+                    // staged registers (K step kt+1) -> the next stage, spread
+                    // over the first WSP chunks; register j is reloaded only in
+                    // this chunk or a later one (after its write)
 #pragma unroll
                     for (int j = 0; j < DPW; ++j)
-                        if (in_reg<WREG, AREG>(j))
+                        if (in_reg<WREG, AREG>(j) && (j * WSP) / DPW == g)
                             *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(nxt) + copy_ldsoff<BK, G>(wave, lane, j)) =
                                 stg.v[j];
                 }
@@ -1732,13 +1735,16 @@ int device_cus()
 constexpr int kLargeBK = MOE_GEMM_BK, kLargeStages = MOE_GEMM_STAGES;
 typedef Grid<2, MOE_GEMM_WGM> LargeGrid;
 
-int large_grid(int64_t max_rows, int S, int N)
+// One block per CU (a multiple of the XCD count).  With a split-K workspace
+// a problem of few tiles still fills the chip (the tail plan cuts their K);
+// without one, blocks beyond the tile count would only idle.
+int large_grid(int64_t max_rows, int S, int N, bool split)
 {
     const int64_t tiles_bound = ((max_rows + kL - 1) / kL + S) * (int64_t)((N + kL - 1) / kL);
     int64_t grid = (int64_t)device_cus();
     grid = (grid + kXcds - 1) / kXcds * kXcds;
     const int64_t need = (tiles_bound + kXcds - 1) / kXcds * kXcds;
-    if (need < grid)
+    if (!split && need < grid)
         grid = need;
     if (grid < kXcds)
         grid = kXcds;
@@ -1750,7 +1756,7 @@ moe_status_t run_large(const void *a, const int32_t *seg, int S, int64_t max_row
                        const void *w, const void *bias, void *out, float *part_ws, hipStream_t stream)
 {
     typedef LargeGrid G;
-    const int grid = large_grid(max_rows, S, N);
+    const int grid = large_grid(max_rows, S, N, part_ws != nullptr);
 #if MOE_GEMM_PIPE == 2
     const int min_len = 2;
     grouped_gemm_pipe2<kLargeBK, G, MOE_PIPE_WREG, MOE_PIPE_AREG, GELU, BIAS, F32OUT>
@@ -1841,9 +1847,9 @@ moe_status_t launch_grouped_gemm(const void *a, const int32_t *seg_offsets, int 
 moe_status_t launch_router_gemm(const void *x, const void *w3, int64_t T, int d, int E, float *logits, void *ws,
                                 size_t ws_bytes, hipStream_t stream)
 {
-    // logits[T, E] = sum over the three bf16 pieces p of x . w3[:, p*d:(p+1)*d]^T
+    // logits3[T, 3E]: column p*E + e = x . (bf16 piece p of router row e)
     float *part = (ws && ws_bytes >= gemm_ws_bytes()) ? (float *)ws : nullptr;
-    return run_large<false, false, true>(x, nullptr, 1, T, E, 3 * d, d, w3, nullptr, logits, part, stream);
+    return run_large<false, false, true>(x, nullptr, 1, T, 3 * E, d, d, w3, nullptr, logits, part, stream);
 }
 
 } // namespace moe

@@ -7,19 +7,25 @@
 // sum f_i P_i).
 //
 // Kernels
-//  route_logits_mfma  bf16 activations.  The fp32 router weight is split
-//                     exactly into three bf16 pieces (hi + mid + lo = w); each
-//                     piece times a bf16 activation is exact in fp32, so three
-//                     bf16 MFMAs accumulating in fp32 give fp32-class logits at
-//                     matrix-core rate.  The four waves of a block split K and
-//                     their partial tiles are summed in LDS in a fixed order.
+//  route_fused_small  bf16 activations, E <= 64: logits (split-bf16 MFMAs, see
+//                     below), softmax, top-k and block partials in one pass.
+//  route_split_weight + grouped GEMM
+//                     bf16 activations, E > 64: the fp32 router weight is split
+//                     exactly into three bf16 pieces (hi + mid + lo = w), stacked
+//                     as 3E rows; each piece times a bf16 activation is exact in
+//                     fp32, so the bf16 GEMM (fp32 accumulate, fp32 output) gives
+//                     three partial logits per expert, summed by route_select.
+//  route_logits_mfma  the same split for d % 64 != 0, 64x64 blocks, the four
+//                     waves of a block split K and sum in LDS in a fixed order.
 //  route_logits_f32   fp32 activations: one thread per (token, expert) fp32
 //                     dot product (the small fp32 workloads).
 //  route_select       one wave per token: softmax, top-k by (logit desc, id
 //                     asc), routing weights, and per-block partial sums of the
 //                     probabilities and selection counts.
-//  route_finalize     one block: fixed-order sums of the partials -> counts,
-//                     f, P and L_aux (bitwise reproducible).
+//  route_reduce_partials / route_finalize
+//                     fixed-order sums of the partials (chunks of rows, then
+//                     the chunk sums in one block) -> counts, f, P and L_aux
+//                     (bitwise reproducible).
 #include "common.hpp"
 
 #include <math.h>
@@ -312,24 +318,23 @@ __global__ __launch_bounds__(64 * NW) void route_fused_small(const uint16_t *__r
     }
 }
 
-// w3[e, p*d + i] = bf16 piece p of w_router[e, i]: hi = w truncated to bf16,
-// mid = (w - hi) truncated, lo = w - hi - mid (exact); hi + mid + lo = w.
-__global__ __launch_bounds__(256) void route_split_weight(const float *__restrict__ wr, int64_t n, int d,
+// w3[p*E + e, i] = bf16 piece p of w_router[e, i]: hi = w truncated to bf16,
+// mid = (w - hi) truncated, lo = w - hi - mid (exact: at most 8 significant
+// bits remain); hi + mid + lo = w.  n = E * d.
+__global__ __launch_bounds__(256) void route_split_weight(const float *__restrict__ wr, int64_t n,
                                                           uint16_t *__restrict__ w3)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= n)
         return;
-    const int64_t e = i / d, c = i % d;
     const float w = wr[i];
     const float h = trunc_bf16(w);
     const float r1 = w - h;
     const float m = trunc_bf16(r1);
     const float l = r1 - m;
-    uint16_t *row = w3 + e * 3 * (int64_t)d;
-    row[c] = (uint16_t)(__float_as_uint(h) >> 16);
-    row[d + c] = (uint16_t)(__float_as_uint(m) >> 16);
-    row[2 * d + c] = (uint16_t)(__float_as_uint(l) >> 16);
+    w3[i] = (uint16_t)(__float_as_uint(h) >> 16);
+    w3[n + i] = (uint16_t)(__float_as_uint(m) >> 16);
+    w3[2 * n + i] = (uint16_t)(__float_as_uint(l) >> 16);
 }
 
 __global__ __launch_bounds__(256) void route_logits_f32(const float *__restrict__ x, const float *__restrict__ wr,
@@ -369,9 +374,11 @@ __device__ __forceinline__ float wave_sum(float v)
     return v;
 }
 
-// EPL = experts held per lane (ceil(E / 64)).
+// EPL = experts held per lane (ceil(E / 64)).  pieces = 3: row t of
+// `logits` holds three column blocks of E (hi, mid, lo router pieces) whose
+// sum (mid + lo) + hi is the logit; pieces = 1: plain [T, E] logits.
 template <int EPL>
-__global__ __launch_bounds__(256) void route_select(const float *__restrict__ logits,
+__global__ __launch_bounds__(256) void route_select(const float *__restrict__ logits, int pieces,
                                                     const float *__restrict__ bias, int64_t T, int E, int k,
                                                     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
                                                     float *__restrict__ part_p, int32_t *__restrict__ part_c)
@@ -398,8 +405,11 @@ __global__ __launch_bounds__(256) void route_select(const float *__restrict__ lo
         for (int i = 0; i < EPL; ++i) {
             const int e = lane + 64 * i;
             l[i] = -INFINITY;
-            if (e < E)
-                l[i] = logits[t * E + e] + (bias ? bias[e] : 0.f);
+            if (e < E) {
+                const float *row = logits + t * (int64_t)(pieces * E);
+                const float v = pieces == 3 ? row[e] + (row[E + e] + row[2 * E + e]) : row[e];
+                l[i] = v + (bias ? bias[e] : 0.f);
+            }
         }
         float m = -INFINITY;
 #pragma unroll
@@ -467,10 +477,32 @@ __global__ __launch_bounds__(256) void route_select(const float *__restrict__ lo
     }
 }
 
-// One block of 1024 threads; G threads per expert sum the block partials in a
+// First level of the partial-sum reduction: chunk c (one block) sums rows
+// [c R, (c+1) R) of the per-block partials, in row order, for every expert.
+constexpr int kFinRows = 32;
+
+__global__ __launch_bounds__(256) void route_reduce_partials(const float *__restrict__ part_p,
+                                                             const int32_t *__restrict__ part_c, int nblk, int E,
+                                                             double *__restrict__ fin_p, long long *__restrict__ fin_c)
+{
+    const int c = blockIdx.x;
+    const int r0 = c * kFinRows, r1 = min(nblk, r0 + kFinRows);
+    for (int e = threadIdx.x; e < E; e += 256) {
+        double ps = 0.0;
+        long long cs = 0;
+        for (int r = r0; r < r1; ++r) {
+            ps += (double)part_p[(int64_t)r * E + e];
+            cs += part_c[(int64_t)r * E + e];
+        }
+        fin_p[(int64_t)c * E + e] = ps;
+        fin_c[(int64_t)c * E + e] = cs;
+    }
+}
+
+// One block of 1024 threads; G threads per expert sum the chunk sums in a
 // fixed strided order, then the G partial sums are added in order.
-__global__ __launch_bounds__(1024) void route_finalize(const float *__restrict__ part_p,
-                                                       const int32_t *__restrict__ part_c, int nblk, int64_t T,
+__global__ __launch_bounds__(1024) void route_finalize(const double *__restrict__ fin_p,
+                                                       const long long *__restrict__ fin_c, int nrows, int64_t T,
                                                        int E, float alpha, int32_t *__restrict__ expert_count,
                                                        float *__restrict__ f, float *__restrict__ P,
                                                        float *__restrict__ l_aux)
@@ -486,9 +518,9 @@ __global__ __launch_bounds__(1024) void route_finalize(const float *__restrict__
     double ps = 0.0;
     long long cs = 0;
     if (e < E) {
-        for (int b = g; b < nblk; b += G) {
-            ps += (double)part_p[(int64_t)b * E + e];
-            cs += part_c[(int64_t)b * E + e];
+        for (int b = g; b < nrows; b += G) {
+            ps += fin_p[(int64_t)b * E + e];
+            cs += fin_c[(int64_t)b * E + e];
         }
     }
     rp[tid] = ps;
@@ -522,6 +554,8 @@ __global__ __launch_bounds__(1024) void route_finalize(const float *__restrict__
 
 } // namespace
 
+static int fin_chunks(int nblk) { return (nblk + kFinRows - 1) / kFinRows; }
+
 static int select_blocks(int64_t T) { return (int)((T + kSelTokensPerBlock - 1) / kSelTokensPerBlock); }
 
 // Tokens per block of the fused small-E path.
@@ -541,8 +575,10 @@ size_t route_ws_bytes(int64_t T, int d, int E)
     // logits (two-kernel paths) + partials of the larger block count, plus the
     // split router weight and the grouped GEMM's tail partials for large E
     const int nblk = (int)((T + 15) / 16);
-    size_t b = align_up((size_t)T * E * sizeof(float)) + 2 * align_up((size_t)nblk * E * sizeof(float));
-    if (E > 64 && d % 64 == 0)
+    const bool split = E > 64 && d % 64 == 0;
+    size_t b = align_up((size_t)T * E * (split ? 3 : 1) * sizeof(float)) +
+               2 * align_up((size_t)nblk * E * sizeof(float)) + 2 * align_up((size_t)fin_chunks(nblk) * E * 8);
+    if (split)
         b += align_up((size_t)E * 3 * d * sizeof(uint16_t)) + align_up(gemm_ws_bytes());
     return b;
 }
@@ -555,10 +591,13 @@ moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, 
     const int nblk = route_blocks(T, E, dt);
     const int nblk_max = (int)((T + 15) / 16);
     Carver cv{(char *)ws, 0};
-    float *logits = cv.take<float>((size_t)T * E);
+    const bool on_gemm = router_on_gemm(dt, d, E);
+    const int pieces = on_gemm ? 3 : 1;
+    float *logits = cv.take<float>((size_t)T * E * pieces);
     float *part_p = cv.take<float>((size_t)nblk_max * E);
     int32_t *part_c = cv.take<int32_t>((size_t)nblk_max * E);
-    const bool on_gemm = router_on_gemm(dt, d, E);
+    double *fin_p = cv.take<double>((size_t)fin_chunks(nblk_max) * E);
+    long long *fin_c = cv.take<long long>((size_t)fin_chunks(nblk_max) * E);
     uint16_t *w3 = on_gemm ? cv.take<uint16_t>((size_t)E * 3 * d) : nullptr;
     void *gws = on_gemm ? cv.take<char>(gemm_ws_bytes()) : nullptr;
 
@@ -580,7 +619,7 @@ moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, 
         } else {
             if (on_gemm) {
                 const int64_t n = (int64_t)E * d;
-                route_split_weight<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(w_router, n, d, w3);
+                route_split_weight<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(w_router, n, w3);
                 if (moe_status_t s = check_launch("route_split_weight"))
                     return s;
                 if (moe_status_t s = launch_router_gemm(x, w3, T, d, E, logits, gws, gemm_ws_bytes(), stream))
@@ -598,20 +637,26 @@ moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, 
             const int epl = (E + 63) / 64;
             const dim3 g((unsigned)nblk);
             switch (epl) {
-            case 1: route_select<1><<<g, 256, 0, stream>>>(logits, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
-            case 2: route_select<2><<<g, 256, 0, stream>>>(logits, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+            case 1: route_select<1><<<g, 256, 0, stream>>>(logits, pieces, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+            case 2: route_select<2><<<g, 256, 0, stream>>>(logits, pieces, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
             case 3:
-            case 4: route_select<4><<<g, 256, 0, stream>>>(logits, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+            case 4: route_select<4><<<g, 256, 0, stream>>>(logits, pieces, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
             case 5: case 6: case 7: case 8:
-                route_select<8><<<g, 256, 0, stream>>>(logits, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+                route_select<8><<<g, 256, 0, stream>>>(logits, pieces, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
             default:
-                route_select<16><<<g, 256, 0, stream>>>(logits, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+                route_select<16><<<g, 256, 0, stream>>>(logits, pieces, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
             }
             if (moe_status_t s = check_launch("route_select"))
                 return s;
         }
     }
-    route_finalize<<<1, 1024, 0, stream>>>(part_p, part_c, T > 0 ? nblk : 0, T, E, alpha, expert_count, f, P,
+    const int nfin = T > 0 ? fin_chunks(nblk) : 0;
+    if (nfin > 0) {
+        route_reduce_partials<<<(unsigned)nfin, 256, 0, stream>>>(part_p, part_c, nblk, E, fin_p, fin_c);
+        if (moe_status_t s = check_launch("route_reduce_partials"))
+            return s;
+    }
+    route_finalize<<<1, 1024, 0, stream>>>(fin_p, fin_c, nfin, T, E, alpha, expert_count, f, P,
                                            l_aux);
     return check_launch("route_finalize");
 }
