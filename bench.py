@@ -253,7 +253,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(g1_tf, 2), "peak": acc.PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(g1_tf / acc.PEAK_BF16_TFLOPS, 4),
                      "traffic": _traffic(w.name, "gemm1_gelu"),
-                     "kernel": "grouped_gemm_bf16 (first Linear + GELU)",
+                     "kernel": "grouped_gemm_256 (first Linear + GELU)",
                      "flops_per_launch": g1_flops, "avg_us": round(avg_us["gemm1_gelu"], 2)},
         "stages": stages,
         "staged_step_us": round(staged_total, 1),

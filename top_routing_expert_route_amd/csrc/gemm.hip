@@ -7,16 +7,12 @@
 // Parallelism (EP)", section "Key math / How it works" (the expert GEMMs run
 // locally on the rows dispatched to this GPU).
 //
-// bf16 kernel (gfx950 matrix cores)
+// bf16 kernels (gfx950 matrix cores)
 //  - out[r, n] = act(sum_k a[r, k] w[s, n, k] + b[s, n]) is computed as
 //    out^T = W . A^T: the weight rows are the MFMA "A" operand and the token
 //    rows the "B" operand, so each lane's accumulators hold 4 consecutive
-//    output features of one row (8-byte bf16 stores).
-//  - Block tile BN (features) x BM (rows), BK = 64; four waves in a 2 x 2
-//    grid, each owning (BN/2) x (BM/2) as 32x32x16 bf16 MFMAs with fp32
-//    accumulation.  Tiles of A and W are staged through LDS with an XOR
-//    swizzle of the 16-byte chunks (row & 7) and double-buffered: the global
-//    loads of step k+1 are in flight while step k computes.
+//    output features of one row (8-byte bf16 stores).  32x32x16 bf16 MFMAs,
+//    fp32 accumulation.
 //  - Persistent grid.  The tile list is derived on the device from the
 //    segment offsets (no host round trip): segment s contributes
 //    ceil(rows_s / BM) * (N / BN) tiles, ordered (segment, feature tile,
@@ -24,8 +20,13 @@
 //    dealt to the 8 XCDs round-robin by the hardware, so each XCD is given one
 //    contiguous range of the tile list: the tiles that share weights run on
 //    the same L2.
-//  - Ragged tails: rows past the segment end are clamped on load and masked
-//    on store; K tails are zero-filled in whole 8-element chunks.
+//  - grouped_gemm_256 (K % 64 == 0, the main path): 256 x 256 tiles, eight
+//    waves, register-staged three-deep operand pipeline, split-K for a short
+//    last round (described at the kernel).
+//  - grouped_gemm_bf16 (any K % 8 == 0): 128 x 128 tiles, four waves in a
+//    2 x 2 grid; A and W staged through LDS with an XOR swizzle of the
+//    16-byte chunks, double-buffered.  Rows past the segment end are clamped
+//    on load and masked on store; K tails are zero-filled in 8-element chunks.
 // fp32 kernel: straightforward LDS-tiled VALU GEMM for the fp32 workloads.
 #include "common.hpp"
 
@@ -260,79 +261,47 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_bf16(const uint16_t *__re
 }
 
 // ---------------------------------------------------------------------------
-// Large-tile bf16 kernel: 256 (features) x 256 (rows) per block, four waves
-// of 128 x 128 (4 x 4 MFMA 32x32x16 tiles, 256 fp32 accumulators per lane,
-// held in AGPRs).
+// Large-tile bf16 kernel: 256 (features) x 256 (rows) per block, eight waves
+// in a 2 x 4 grid, each owning 128 x 64 as 4 x 2 MFMA 32x32x16 tiles (128
+// fp32 accumulators per lane; two waves per SIMD, so that one wave's MFMAs
+// cover the other's waits).
 //
-// Global -> LDS copies are buffer_load_dwordx4 ... lds (LDS DMA): each lane's
-// 16 bytes land at M0 + 16 * lane, so a wave fills 1 KB of contiguous LDS per
-// instruction and the XOR swizzle of the 16-byte chunks is applied on the
-// global side.  The copies are issued as inline assembly so that the
-// compiler's conservative wait-for-all-DMA before every LDS read does not
-// serialise them; the kernel keeps its own vmcnt accounting: STAGES-1 K
-// steps are in flight while one computes.  They have no output registers.
+// Operand path, per K step of 64: both operand tiles (256 rows x 128 bytes
+// each) go global -> VGPR (buffer loads, 16 bytes per lane) two steps ahead
+// and VGPR -> LDS (ds_write_b128) one step ahead, into the LDS stage that is
+// not being read.  The two LDS stages plus the staged registers keep three
+// K steps in flight.  (On this access pattern plain vector loads stream into
+// the CU markedly faster than LDS-DMA copies.)
+//
+// The block synchronises once per K step, before the last 16-wide sub-step:
+// the next stage is then complete, and the last sub-step's MFMAs cover the
+// LDS reads of the next stage's first sub-step, so the matrix pipe does not
+// drain at step boundaries.  The last two steps of a tile already load the
+// first two steps of the block's next tile: a new tile starts without a load
+// bubble, and its loads overlap this tile's epilogue.
 //
 // LDS on gfx950 serves a ds_read_b128 16 lanes at a time over 64 banks
-// (256 bytes): rows of BK bf16 are swizzled so that the 16 rows read by one
-// group of lanes at the same logical chunk hit 16 distinct bank groups.
-// Requires K % BK == 0; rows past the weight matrix or the segment end read
-// as zeros (buffer range checking); row sub-tiles past the segment end skip
-// their MFMAs; stores are masked.
+// (256 bytes): 16-byte chunk c of row r is stored at c ^ ((r >> 1) & 7), so
+// the 16 rows read by one group of lanes at the same logical chunk hit 16
+// distinct bank groups.
+// Requires K % 64 == 0 and K >= 128; rows past the weight matrix or the
+// segment end read as zeros (buffer range checking); row sub-tiles past the
+// segment end skip their MFMAs; stores are masked.
 // ---------------------------------------------------------------------------
 constexpr int kL = 256; // tile edge
-
-typedef __attribute__((address_space(3))) void lds_void;
 // Word 3 of a raw (unformatted, stride 0) buffer resource on gfx9-family GPUs.
 constexpr int kRsrcWord3 = 0x00020000;
-// A scalar offset past every tile's buffer range: such a copy reads zeros.
-constexpr uint32_t kOutOfRange = 0x40000000u;
 
-template <int N> __device__ __forceinline__ void wait_vmcnt()
+// This wave's loads except the newest N have completed, every wave got that
+// far, and every wave's LDS accesses issued so far have completed.
+template <int N> __device__ __forceinline__ void stage_barrier()
 {
     static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
-// Logical 16-byte chunk stored at physical chunk p of a row: p ^ f(row).
-template <int BK> __device__ __forceinline__ int swz(int row)
-{
-    return BK == 64 ? ((row >> 1) & 7) : ((row >> 2) & 3);
-}
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// LDS-DMA copy: 16 bytes per lane from buffer `rsrc` at voff + soff into LDS
-// at m0 + 16 * lane.  Written as inline assembly so that the compiler's
-// wait-count pass does not track it (it would wait for every copy before
-// any LDS read); the kernel keeps the vmcnt accounting itself.  The
-// instruction writes no registers.  The compiler's hazard recognizer does
-// not look inside inline assembly, so the block carries its own wait states:
-// the M0 write just before it needs one, and a scalar offset that a VALU op
-// wrote (readfirstlane, or a reload of a spilled SGPR with v_readlane) needs
-// five before a vector memory instruction may read it.
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t m0)
-{
-    i32x4 r;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-        r[k] = __builtin_amdgcn_readfirstlane(rsrc[k]);
-    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
-                 :
-                 : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(soff)),
-                   "{m0}"(__builtin_amdgcn_readfirstlane(m0))
-                 : "memory");
-}
-
-__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes)
-{
-    const uint64_t a = (uint64_t)base;
-    i32x4 r;
-    r[0] = (int)(uint32_t)a;
-    r[1] = (int)((uint32_t)(a >> 32) & 0xFFFFu);
-    r[2] = (int)bytes;
-    r[3] = kRsrcWord3;
-    return r;
-}
+// Logical 16-byte chunk stored at physical chunk p of a 64-element row.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 // Values the whole wave shares, held in scalar registers (the compiler
 // cannot prove that values read from LDS are uniform).
@@ -344,113 +313,17 @@ __device__ __forceinline__ int64_t uni64(int64_t v)
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const void *p)
-{
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
-}
-
 // Wave grid of a 256x256 tile: WGN waves along the features and WGM along
 // the rows; each wave owns (256/WGN) x (256/WGM) as FA x FB MFMA tiles of
-// 32x32.  Four waves (2x2, 128x128 each, one wave per SIMD) or eight (2x4,
-// 128x64 each, two waves per SIMD so that one wave's MFMAs cover the
-// other's waits).
+// 32x32.
 template <int WGN, int WGM> struct Grid {
     static constexpr int WGN_ = WGN, WGM_ = WGM;
     static constexpr int NW = WGN * WGM;
     static constexpr int WTN = kL / WGN, WTM = kL / WGM;
     static constexpr int FA = WTN / 32, FB = WTM / 32;
 };
-
-// One K step of a 256x256 tile: MFMAs on stage `cur` (already in LDS) while
-// the LDS-DMA copies of a later K step fill the stage at LDS byte address
-// `nxt`.  Each 16-wide K sub-step is cut into chunks of MFMAs plus a share of
-// the LDS reads of the next sub-step; one copy is issued after each chunk, so
-// the copies trickle out at the rate the address unit drains them instead of
-// stalling the wave in a burst.
-#ifndef MOE_GEMM_CPS
-#define MOE_GEMM_CPS 0 // chunks per 16-wide sub-step; 0: one per copy
-#endif
-#ifndef MOE_GEMM_LEAD
-#define MOE_GEMM_LEAD 8 // copies are spread over LEAD/8 of the K step
-#endif
-template <int BK, class G, int NBV>
-__device__ __forceinline__ void k_step(const uint16_t *cur, uint32_t nxt, f32x16 (&acc)[G::FA][G::FB], i32x4 rw,
-                                       i32x4 ra, uint32_t vbase, uint32_t vbase_a, uint32_t so_w, uint32_t so_a,
-                                       uint32_t row_w, uint32_t row_a, int wave, int wn, int wm, int r32, int khalf,
-                                       int sw)
-{
-    constexpr int FA = G::FA, FB = G::FB, NW = G::NW;
-    constexpr int CPR = BK / 8, RPI = 64 / CPR, NQ = kL / (NW * RPI), KS = BK / 16;
-    constexpr int DPW = 2 * NQ;                                  // copies per wave per stage
-    constexpr int CPS = MOE_GEMM_CPS > 0 ? MOE_GEMM_CPS : DPW / KS; // chunks per sub-step
-    constexpr int NCH = KS * CPS;                                // chunks per K step
-    constexpr int MPC = FA * FB / CPS;                           // MFMAs per chunk
-    constexpr int RDS = FA + FB;                                 // fragment reads per sub-step
-    constexpr int RPC = (RDS + CPS - 1) / CPS;
-    static_assert(DPW % KS == 0 && (FA * FB) % CPS == 0, "chunking");
-    const uint16_t *sW = cur;
-    const uint16_t *sA = cur + kL * BK;
-    bf16x8 fa[2][FA], fb[2][FB];
-    auto read = [&](int ks, int buf, int r) {
-        const int ch = ((ks * 2 + khalf) ^ sw) * 8;
-        if (r < FA) {
-            fa[buf][r] = *reinterpret_cast<const bf16x8 *>(sW + (wn * G::WTN + r * 32 + r32) * BK + ch);
-        } else if (r - FA < NBV) {
-            const int b = r - FA;
-            fb[buf][b] = *reinterpret_cast<const bf16x8 *>(sA + (wm * G::WTM + b * 32 + r32) * BK + ch);
-        }
-    };
-    auto dma = [&](int i) { // copy i of DPW: W rows for even i, A rows for odd i
-        const int q = i >> 1;
-        const uint32_t R = (uint32_t)((NW * q + wave) * RPI);
-        const uint32_t so = (i & 1) ? (uint32_t)q * (uint32_t)(NW * RPI) * row_a + so_a
-                                    : (uint32_t)q * (uint32_t)(NW * RPI) * row_w + so_w;
-        dma16((i & 1) ? ra : rw, (i & 1) ? vbase_a : vbase, so, nxt + (uint32_t)((i & 1) * (kL * BK) + R * BK) * 2u);
-    };
-    if (NBV > 0) {
-#pragma unroll
-        for (int r = 0; r < RDS; ++r)
-            read(0, 0, r);
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int c = 0; c < CPS; ++c) {
-            if (NBV > 0) {
-#pragma unroll
-                for (int i = c * MPC; i < (c + 1) * MPC; ++i) {
-                    const int a = i / FB, b = i % FB;
-                    if (b < NBV)
-                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks & 1][a], fb[ks & 1][b], acc[a][b],
-                                                                            0, 0, 0);
-                }
-                if (ks + 1 < KS) {
-#pragma unroll
-                    for (int r = c * RPC; r < (c + 1) * RPC && r < RDS; ++r)
-                        read(ks + 1, (ks + 1) & 1, r);
-                }
-                if (NBV == FB) {
-#pragma unroll
-                    for (int m = 0; m < MPC; ++m) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        if (ks + 1 < KS && m < RPC && c * RPC + m < RDS)
-                            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    }
-                }
-            }
-            // Copy j goes out after chunk (j * NCH * LEAD) / (8 * DPW).
-            const int g = ks * CPS + c;
-#pragma unroll
-            for (int j = 0; j < DPW; ++j) {
-                if ((j * NCH * MOE_GEMM_LEAD) / (8 * DPW) == g) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    dma(j);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-        }
-    }
-}
+typedef Grid<2, 4> LargeGrid;
+constexpr int kLargeBK = 64;
 
 // Epilogue of a 256x256 tile: bias, activation and store of the rows inside
 // [row0, row_end) and features < N, as bf16 (rounded to nearest even) or,
@@ -509,119 +382,19 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[G::FA][G::FB], vo
     }
 }
 
-// One 256x256 tile over K steps [kt_lo, kt_hi).  With PART the raw fp32
-// accumulators go to `part` (one 256 KB slab: per wave, per register, lane
-// fastest) for a later fixed-order reduction; otherwise the epilogue stores
-// bf16.
-template <int BK, int STAGES, class G, int NBV, bool GELU, bool BIAS, bool F32OUT, bool PART>
-__device__ __forceinline__ void tile_256(const uint16_t *__restrict__ A, const uint16_t *__restrict__ wseg,
-                                         const uint16_t *__restrict__ bseg, void *__restrict__ C,
-                                         float *__restrict__ part, uint16_t *smem, int64_t row0, int64_t row_end,
-                                         int n0, int N, int K, int Ka, int kt_lo, int kt_hi)
-{
-    constexpr int NW = G::NW, FA = G::FA, FB = G::FB;
-    constexpr int CPR = BK / 8;            // 16-byte chunks per row
-    constexpr int RPI = 64 / CPR;          // rows filled per DMA instruction (1 KB)
-    constexpr int NQ = kL / (NW * RPI);    // DMA instructions per operand per wave
-    constexpr int STAGE = 2 * kL * BK;     // bf16 elements per stage (W then A)
-    constexpr int PER_STAGE = 2 * NQ;      // DMA instructions per thread per stage
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wn = wave % G::WGN_, wm = wave / G::WGN_;
-    const int r32 = lane & 31, khalf = lane >> 5;
-
-    // Instruction q of this wave fills LDS rows R = (NW q + wave) * RPI ..
-    // R + RPI - 1; lane -> row R + lane / CPR, physical chunk lane % CPR,
-    // which holds logical chunk (lane % CPR) ^ swizzle(row).  The byte offset
-    // of that row is vbase + q * NW * RPI * K * 2 (the q part is scalar).  The
-    // buffer resources cover exactly the tile's valid rows: rows past the
-    // weight matrix or the segment end read as zeros.
-    // A's rows have Ka elements: its K offset wraps every Ka (Ka = K for a
-    // plain GEMM; the router's split weight repeats the activations thrice).
-    const uint32_t row_bytes = (uint32_t)K * 2u, row_a = (uint32_t)Ka * 2u;
-    const int KTa = Ka / BK;
-    const int lrow = lane / CPR;
-    const int prow = wave * RPI + lrow;
-    const int lchunk = (lane % CPR) ^ swz<BK>(prow);
-    const uint32_t vbase = (uint32_t)prow * row_bytes + (uint32_t)lchunk * 16u;
-    const uint32_t vbase_a = (uint32_t)prow * row_a + (uint32_t)lchunk * 16u;
-    const int wrows = min(kL, N - n0);
-    const int arows = (int)(row_end - row0);
-    const i32x4 rw = make_rsrc(wseg + (int64_t)n0 * K, (uint32_t)wrows * row_bytes);
-    const i32x4 ra = make_rsrc(A + row0 * Ka, (uint32_t)arows * row_a);
-    const uint32_t lds0 = lds_addr(smem);
-
-    f32x16 acc[FA][FB];
-#pragma unroll
-    for (int a = 0; a < FA; ++a)
-#pragma unroll
-        for (int b = 0; b < FB; ++b)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                acc[a][b][v] = 0.f;
-
-    const int sw = swz<BK>(r32);
-    // Prologue: stages 0 .. STAGES-2 hold K steps kt_lo .. kt_lo+STAGES-2 (a
-    // copy past kt_hi reads out of range: zeros).
-    for (int p = 0; p < STAGES - 1; ++p) {
-        const uint32_t dst = lds0 + (uint32_t)(p * STAGE) * 2u;
-        const bool live = kt_lo + p < kt_hi;
-        const uint32_t so_w = live ? (uint32_t)(kt_lo + p) * (BK * 2) : kOutOfRange;
-        const uint32_t so_a = live ? (uint32_t)((kt_lo + p) % KTa) * (BK * 2) : kOutOfRange;
-#pragma unroll
-        for (int i = 0; i < 2 * NQ; ++i) {
-            const int q = i >> 1;
-            const uint32_t R = (uint32_t)((NW * q + wave) * RPI);
-            const uint32_t so = (i & 1) ? (uint32_t)q * (uint32_t)(NW * RPI) * row_a + so_a
-                                        : (uint32_t)q * (uint32_t)(NW * RPI) * row_bytes + so_w;
-            dma16((i & 1) ? ra : rw, (i & 1) ? vbase_a : vbase, so,
-                  dst + (uint32_t)((i & 1) * (kL * BK) + R * BK) * 2u);
-        }
-    }
-    wait_vmcnt<(STAGES - 2) * PER_STAGE>();
-    __syncthreads();
-
-    for (int kt = kt_lo; kt < kt_hi; ++kt) {
-        const int fill = kt + STAGES - 1;
-        const bool live = fill < kt_hi;
-        const uint32_t so_w = live ? (uint32_t)fill * (BK * 2) : kOutOfRange;
-        const uint32_t so_a = live ? (uint32_t)(fill % KTa) * (BK * 2) : kOutOfRange;
-        k_step<BK, G, NBV>(smem + ((kt - kt_lo) % STAGES) * STAGE,
-                           lds0 + (uint32_t)(((fill - kt_lo) % STAGES) * STAGE) * 2u, acc, rw, ra, vbase, vbase_a,
-                           so_w, so_a, row_bytes, row_a, wave, wn, wm, r32, khalf, sw);
-        // Stage kt+1 must have landed; the STAGES-2 stages issued after it
-        // may stay in flight.
-        wait_vmcnt<(STAGES - 2) * PER_STAGE>();
-        __syncthreads();
-    }
-    wait_vmcnt<0>(); // the zero-fill copies of the last steps must land before the next tile's copies
-
-    if (PART) {
-        float *dst = part + (size_t)wave * (FA * FB * 16 * 64) + lane;
-#pragma unroll
-        for (int a = 0; a < FA; ++a)
-#pragma unroll
-            for (int b = 0; b < FB; ++b)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    dst[((a * FB + b) * 16 + v) * 64] = acc[a][b][v];
-    } else {
-        store_tile<G, NBV, GELU, BIAS, F32OUT>(acc, C, bseg, row0, row_end, n0, N, wn, wm, r32, khalf);
-    }
-}
-
 // Split of the tile list over a persistent grid of G blocks.  F whole tiles
 // run in full rounds (each block gets the same number); when the rest
 // (`rem` tiles, at most half a round) would leave CUs idle, each of them is
-// cut into `sk` K ranges, one per block, written as fp32 partials and summed
-// by grouped_gemm_reduce.  Computed identically by both kernels.
+// cut into `sk` K ranges of at least min_len steps, one per block, written as
+// fp32 partials and summed by grouped_gemm_reduce.  Computed identically by
+// both kernels.
 struct TailPlan {
-    int64_t F;   // whole tiles
-    int rem;     // tail tiles split in K (0: none)
-    int sk;      // K ranges per tail tile
+    int64_t F;
+    int rem;
+    int sk;
 };
 
-__device__ __forceinline__ TailPlan plan_tail(int64_t total, int G, int KT, bool have_ws, int min_len = 1)
+__device__ __forceinline__ TailPlan plan_tail(int64_t total, int G, int KT, bool have_ws, int min_len)
 {
     TailPlan p{total, 0, 1};
     const int64_t R = total / G;
@@ -637,29 +410,6 @@ __device__ __forceinline__ TailPlan plan_tail(int64_t total, int G, int KT, bool
         }
     }
     return p;
-}
-
-template <int BK, int STAGES, class G, bool GELU, bool BIAS, bool F32OUT, bool PART>
-__device__ __forceinline__ void tile_any(int nbv, const uint16_t *A, const uint16_t *wseg, const uint16_t *bseg,
-                                         void *C, float *part, uint16_t *smem, int64_t row0, int64_t row_end, int n0,
-                                         int N, int K, int Ka, int kt_lo, int kt_hi)
-{
-#define MOE_TILE(V) tile_256<BK, STAGES, G, V, GELU, BIAS, F32OUT, PART>(A, wseg, bseg, C, part, smem, row0, row_end, \
-                                                                     n0, N, K, Ka, kt_lo, kt_hi)
-    if (G::FB == 4) {
-        switch (nbv) {
-        case 4: MOE_TILE(G::FB >= 4 ? 4 : G::FB); return;
-        case 3: MOE_TILE(G::FB >= 3 ? 3 : G::FB); return;
-        default: break;
-        }
-    }
-    switch (nbv) {
-    case 2: MOE_TILE(G::FB >= 2 ? 2 : G::FB); break;
-    case 1: MOE_TILE(1); break;
-    case 0: MOE_TILE(0); break;
-    default: break;
-    }
-#undef MOE_TILE
 }
 
 // Location of tile L of the list: segment, rows and first feature.
@@ -686,119 +436,88 @@ __device__ __forceinline__ TileLoc locate(const int *tb, const int32_t *seg, int
     return t;
 }
 
+// Row sub-tiles of wave row wm that hold rows of the tile.
 template <class G> __device__ __forceinline__ int valid_b(const TileLoc &t, int wm)
 {
     const int64_t left = t.row_end - (t.row0 + (int64_t)wm * G::WTM);
     return left <= 0 ? 0 : (left >= G::WTM ? G::FB : (int)((left + 31) / 32));
 }
 
-template <int BK, int STAGES, class G, bool GELU, bool BIAS, bool F32OUT>
-__global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_bf16_256(const uint16_t *__restrict__ A,
-                                                                       const int32_t *__restrict__ seg, int S,
-                                                                       int64_t max_rows,
-                                                                       const uint16_t *__restrict__ W,
-                                                                       const uint16_t *__restrict__ bias,
-                                                                       void *__restrict__ C, int N, int K, int Ka,
-                                                                       float *__restrict__ part_ws)
-{
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * 2 * kL * BK];
-    __shared__ int tb[kMaxSeg + 1];
-    build_tile_prefix<kL>(seg, S, max_rows, tb);
+// A block's work item: a whole tile, or one K range of a tail tile.
+struct Work {
+    TileLoc t;
+    int kt_lo, kt_hi;
+    int unit; // tail unit, or -1 for a whole tile
+};
 
-    const int wm = (threadIdx.x >> 6) / G::WGN_;
-    const int NT = (N + kL - 1) / kL;
-    const int KT = K / BK;
-    const int64_t total = (int64_t)tb[S] * NT;
-    const TailPlan plan = plan_tail(total, (int)gridDim.x, KT, part_ws != nullptr);
-
-    // Whole tiles: an XCD-contiguous share of tiles [0, F).
-    const int xcd = blockIdx.x % kXcds;
-    const int per = gridDim.x / kXcds;
-    const int j = blockIdx.x / kXcds;
-    const int64_t rlo = plan.F * xcd / kXcds, rhi = plan.F * (xcd + 1) / kXcds;
-    for (int64_t L = rlo + j; L < rhi; L += per) {
-        const TileLoc t = locate(tb, seg, S, max_rows, NT, L);
-        tile_any<BK, STAGES, G, GELU, BIAS, F32OUT, false>(valid_b<G>(t, wm), A, W + (int64_t)t.s * N * K,
-                                                           bias ? bias + (int64_t)t.s * N : nullptr, C, nullptr, smem,
-                                                           t.row0, t.row_end, t.n0, N, K, Ka, 0, KT);
-        __syncthreads(); // the next tile's copies overwrite stages still read here
-    }
-    // Tail: one K range of one tail tile per block.
-    const int u = blockIdx.x;
-    if (plan.rem > 0 && u < plan.rem * plan.sk) {
-        const int64_t L = plan.F + u / plan.sk;
-        const int c = u % plan.sk;
-        const TileLoc t = locate(tb, seg, S, max_rows, NT, L);
-        const int klo = (int)((int64_t)KT * c / plan.sk), khi = (int)((int64_t)KT * (c + 1) / plan.sk);
-        tile_any<BK, STAGES, G, GELU, BIAS, F32OUT, true>(valid_b<G>(t, wm), A, W + (int64_t)t.s * N * K, nullptr,
-                                                          C, part_ws + (size_t)u * (kL * kL), smem, t.row0, t.row_end,
-                                                          t.n0, N, K, Ka, klo, khi);
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Software-pipelined form of the same tiling.  Two LDS stages; within a K
-// step the copies of the next stage go out during the first KS-1 sub-steps,
-// the block synchronises once, before the last sub-step, and the last
-// sub-step's MFMAs cover the LDS reads of the next stage's first sub-step, so
-// the matrix pipe does not drain at K-step boundaries.  The last K step of a
-// tile already copies the first stage of the block's next tile, so that tile
-// starts without a load bubble and its copies overlap this tile's epilogue.
-// ---------------------------------------------------------------------------
-
-// Per-launch copy geometry: per-lane byte offsets (row and swizzled chunk)
+// Per-launch load geometry: per-lane byte offsets (row and swizzled chunk)
 // into a W and an A row, bytes per row, and K steps per A row.
 struct CopyGeo {
     uint32_t vbase, vbase_a, row_w, row_a;
     int KTa;
 };
 
-// One stage's source: the tile's buffer resources and the K step's scalar
-// offsets.  A fill with nothing to load uses resources of zero bytes: every
-// copy is then out of range and writes zeros to LDS without touching memory
-// (no branch in the K loop, and the wait counts stay uniform).
+// One wave's staged registers: copy i of a K step (W rows for even i, A
+// rows for odd i).
+template <int BK, class G> struct Staged {
+    static constexpr int DPW = 2 * (kL / (G::NW * (64 / (BK / 8))));
+    u32x4 v[DPW];
+};
+
+// A K step's source: base addresses and byte sizes of the tile's W and A
+// rows, and the step's byte offset into them.  Sizes of zero make every load
+// out of range (zeros, no memory access).
 struct Fill {
-    i32x4 rw, ra;
+    uint64_t wbase, abase;
+    uint32_t wbytes, abytes;
     uint32_t so_w, so_a;
 };
 
-template <int BK> __device__ __forceinline__ Fill fill_at(i32x4 rw, i32x4 ra, int kt, int KTa)
+template <int BK>
+__device__ __forceinline__ Fill fill_k(uint64_t wb, uint64_t ab, uint32_t ws, uint32_t as, int k, int KTa)
 {
     Fill f;
-    f.rw = rw;
-    f.ra = ra;
-    f.so_w = (uint32_t)kt * (BK * 2);
-    f.so_a = (uint32_t)(kt % KTa) * (BK * 2);
+    f.wbase = wb;
+    f.abase = ab;
+    f.wbytes = ws;
+    f.abytes = as;
+    f.so_w = (uint32_t)k * (BK * 2);
+    f.so_a = (uint32_t)(k % KTa) * (BK * 2);
     return f;
 }
 
-template <int BK, class G>
-__device__ __forceinline__ void copy_one(const CopyGeo &cg, const Fill &f, uint32_t dst, int wave, int i)
+__device__ __forceinline__ u32x4 buf_load16(uint64_t base, uint32_t bytes, uint32_t voff, uint32_t soff)
+{
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)base, (short)0, (int)bytes, kRsrcWord3);
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Copy i of a K step: its rows' scalar byte offset.  Instruction q of a wave
+// covers rows (NW q + wave) * RPI .. + RPI - 1 (RPI = 8 rows of 128 bytes).
+template <int BK, class G> __device__ __forceinline__ uint32_t copy_soff(const CopyGeo &cg, const Fill &f, int i)
+{
+    constexpr int CPR = BK / 8, RPI = 64 / CPR, NW = G::NW;
+    const int q = i >> 1;
+    return (i & 1) ? (uint32_t)q * (uint32_t)(NW * RPI) * cg.row_a + f.so_a
+                   : (uint32_t)q * (uint32_t)(NW * RPI) * cg.row_w + f.so_w;
+}
+
+template <int BK, class G> __device__ __forceinline__ u32x4 copy_load(const CopyGeo &cg, const Fill &f, int i)
+{
+    const uint32_t so = copy_soff<BK, G>(cg, f, i);
+    return (i & 1) ? buf_load16(f.abase, f.abytes, cg.vbase_a, so) : buf_load16(f.wbase, f.wbytes, cg.vbase, so);
+}
+
+// LDS byte offset (within a stage) of copy i's 16 bytes for this lane: the
+// stage holds W's 256 rows, then A's.
+template <int BK, class G> __device__ __forceinline__ uint32_t copy_ldsoff(int wave, int lane, int i)
 {
     constexpr int CPR = BK / 8, RPI = 64 / CPR, NW = G::NW;
     const int q = i >> 1;
     const uint32_t R = (uint32_t)((NW * q + wave) * RPI);
-    const uint32_t so = (i & 1) ? (uint32_t)q * (uint32_t)(NW * RPI) * cg.row_a + f.so_a
-                                : (uint32_t)q * (uint32_t)(NW * RPI) * cg.row_w + f.so_w;
-    dma16((i & 1) ? f.ra : f.rw, (i & 1) ? cg.vbase_a : cg.vbase, so,
-          dst + (uint32_t)((i & 1) * (kL * BK) + R * BK) * 2u);
+    return (uint32_t)((i & 1) * (kL * BK) + R * BK) * 2u + (uint32_t)lane * 16u;
 }
-
-// This wave's copies except the newest N have landed, every wave got that
-// far, and every wave's LDS reads issued so far have completed.  (Copies
-// complete in issue order.)
-template <int N> __device__ __forceinline__ void stage_barrier()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
-}
-
-#ifndef MOE_PIPE_CPS
-#define MOE_PIPE_CPS 8 // chunks per 16-wide sub-step
-#endif
-#ifndef MOE_PIPE_RCH
-#define MOE_PIPE_RCH 2 // the next sub-step's fragment reads go out in the first RCH chunks
-#endif
 
 // Fragment reads in the order the next sub-step's MFMAs first use them: the
 // MFMA sequence is (a, b) = (i / FB, i % FB), so read r is A fragment a or B
@@ -836,28 +555,38 @@ __device__ __forceinline__ void read_frag(const uint16_t *stage, int ks, bf16x8 
     }
 }
 
-// One K step: MFMAs on stage `cur`; the copies of a later stage (`f`, to
-// LDS byte address `fill_lds`) go out during the first KS-1 sub-steps; then
-// one barrier, after which the next stage `nxt` has landed and the last
-// sub-step's MFMAs cover the reads of its first sub-step.
-template <int BK, int STAGES, class G, int NBV>
-__device__ __forceinline__ void k_step_pipe(const uint16_t *cur, const uint16_t *nxt, uint32_t fill_lds,
-                                            const Fill &f, const CopyGeo &cg, f32x16 (&acc)[G::FA][G::FB],
-                                            bf16x8 (&fa)[2][G::FA], bf16x8 (&fb)[2][G::FB], int wave, int wn, int wm,
-                                            int r32, int khalf, int sw)
+// Scheduling of a K step: each 16-wide sub-step is cut into kChunks chunks
+// of MFMAs; the next sub-step's fragment reads go out in the first
+// kReadChunks chunks, the staged registers are written to LDS over the first
+// kWriteChunks chunks of the step, and the loads of the step after next are
+// spread over the chunks before the barrier.
+constexpr int kChunks = 8, kReadChunks = 2, kWriteChunks = 8;
+
+// One K step: MFMAs on stage `cur`; the staged registers (K step kt+1) go to
+// stage `nxt`, and register loads of step kt+2 (`f`) refill them; then one
+// barrier, after which `nxt` is complete and the last sub-step's MFMAs cover
+// the reads of its first sub-step.
+template <int BK, class G, int NBV>
+__device__ __forceinline__ void k_step(const uint16_t *cur, uint16_t *nxt, const Fill &f, Staged<BK, G> &stg,
+                                       const CopyGeo &cg, f32x16 (&acc)[G::FA][G::FB], bf16x8 (&fa)[2][G::FA],
+                                       bf16x8 (&fb)[2][G::FB], int wave, int lane, int wn, int wm, int r32, int khalf,
+                                       int sw)
 {
     constexpr int FA = G::FA, FB = G::FB;
-    constexpr int CPR = BK / 8, RPI = 64 / CPR, NQ = kL / (G::NW * RPI), KS = BK / 16;
-    constexpr int DPW = 2 * NQ;            // copies per wave per stage
-    constexpr int CPS = MOE_PIPE_CPS < FA * FB ? MOE_PIPE_CPS : FA * FB; // chunks per sub-step
-    constexpr int MPC = FA * FB / CPS;     // MFMAs per chunk
-    constexpr int RDS = FA + FB;           // fragment reads per sub-step
-    constexpr int RCH = MOE_PIPE_RCH < CPS ? MOE_PIPE_RCH : CPS;
-    constexpr int RPC = (RDS + RCH - 1) / RCH; // reads per chunk in the first RCH chunks
-    constexpr int NPRE = (KS - 1) * CPS;   // chunks before the barrier
+    constexpr int KS = BK / 16;
+    constexpr int DPW = Staged<BK, G>::DPW;
+    constexpr int CPS = kChunks < FA * FB ? kChunks : FA * FB;
+    constexpr int MPC = FA * FB / CPS;
+    constexpr int RDS = FA + FB;
+    constexpr int RCH = kReadChunks < CPS ? kReadChunks : CPS;
+    constexpr int RPC = (RDS + RCH - 1) / RCH;
+    constexpr int NPRE = (KS - 1) * CPS;
+    constexpr int WSP = kWriteChunks < NPRE ? kWriteChunks : NPRE;
     static_assert(KS >= 2 && (FA * FB) % CPS == 0, "chunking");
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
+        // Sub-step ks+1 comes from this stage, except after the last one:
+        // then sub-step 0 of the next stage (complete: the barrier is behind).
         const uint16_t *src = ks + 1 < KS ? cur : nxt;
         const int kn = ks + 1 < KS ? ks + 1 : 0;
 #pragma unroll
@@ -892,562 +621,54 @@ __device__ __forceinline__ void k_step_pipe(const uint16_t *cur, const uint16_t 
             if (ks + 1 < KS) {
                 const int g = ks * CPS + c;
                 __builtin_amdgcn_sched_barrier(0);
+                // staged register j -> nxt, then its reload (step kt+2)
+#pragma unroll
+                for (int j = 0; j < DPW; ++j)
+                    if ((j * WSP) / DPW == g)
+                        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(nxt) + copy_ldsoff<BK, G>(wave, lane, j)) =
+                            stg.v[j];
 #pragma unroll
                 for (int j = 0; j < DPW; ++j)
                     if ((j * NPRE) / DPW == g)
-                        copy_one<BK, G>(cg, f, fill_lds, wave, j);
+                        stg.v[j] = copy_load<BK, G>(cg, f, j);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
         if (ks == KS - 2) {
-            // the next stage has landed; the STAGES-2 newer ones may be in flight
+            // nxt complete; the register loads of step kt+2 stay in flight
             __builtin_amdgcn_sched_barrier(0);
-            stage_barrier<(STAGES - 2) * DPW>();
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-}
-
-// Source of the next work item's first stages, for the last K steps of a
-// tile: its resources and K range (len >= STAGES-1), or none.
-struct NextSrc {
-    i32x4 rw, ra;
-    int kt_lo;
-    bool any;
-};
-
-// One tile (or one K range of a tail tile).  On entry ring slot b holds its
-// first K step (landed, behind a barrier) and the next STAGES-2 steps are in
-// flight; on exit the same holds for `next` at the returned slot.
-template <int BK, int STAGES, class G, int NBV, bool GELU, bool BIAS, bool F32OUT, bool PART>
-__device__ __forceinline__ int tile_pipe(const uint16_t *smem, uint32_t lds0, int b, const CopyGeo &cg, i32x4 rw,
-                                         i32x4 ra, int kt_lo, int kt_hi, const NextSrc &next, i32x4 null_w,
-                                         i32x4 null_a, void *C, const uint16_t *bseg, float *part, int64_t row0,
-                                         int64_t row_end, int n0, int N)
-{
-    constexpr int FA = G::FA, FB = G::FB, STAGE = 2 * kL * BK;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wn = wave % G::WGN_, wm = wave / G::WGN_;
-    const int r32 = lane & 31, khalf = lane >> 5;
-    const int sw = swz<BK>(r32);
-
-    f32x16 acc[FA][FB];
-#pragma unroll
-    for (int a = 0; a < FA; ++a)
-#pragma unroll
-        for (int q = 0; q < FB; ++q)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                acc[a][q][v] = 0.f;
-    bf16x8 fa[2][FA], fb[2][FB];
-    if (NBV > 0) {
-#pragma unroll
-        for (int r = 0; r < FA + FB; ++r)
-            read_frag<BK, G, NBV>(smem + b * STAGE, 0, fa[0], fb[0], r, wn, wm, r32, khalf, sw);
-    }
-    for (int kt = kt_lo; kt < kt_hi; ++kt) {
-        const int fs = kt + STAGES - 1; // K step to fill
-        Fill f;
-        if (fs < kt_hi)
-            f = fill_at<BK>(rw, ra, fs, cg.KTa);
-        else if (next.any)
-            f = fill_at<BK>(next.rw, next.ra, next.kt_lo + (fs - kt_hi), cg.KTa);
-        else
-            f = fill_at<BK>(null_w, null_a, 0, cg.KTa);
-        const int bn = b + 1 == STAGES ? 0 : b + 1;
-        const int bf = b == 0 ? STAGES - 1 : b - 1;
-        k_step_pipe<BK, STAGES, G, NBV>(smem + b * STAGE, smem + bn * STAGE, lds0 + (uint32_t)(bf * STAGE) * 2u, f,
-                                        cg, acc, fa, fb, wave, wn, wm, r32, khalf, sw);
-        b = bn;
-    }
-    if (PART) {
-        float *dst = part + (size_t)wave * (FA * FB * 16 * 64) + lane;
-#pragma unroll
-        for (int a = 0; a < FA; ++a)
-#pragma unroll
-            for (int q = 0; q < FB; ++q)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    dst[((a * FB + q) * 16 + v) * 64] = acc[a][q][v];
-    } else {
-        store_tile<G, NBV, GELU, BIAS, F32OUT>(acc, C, bseg, row0, row_end, n0, N, wn, wm, r32, khalf);
-    }
-    return b;
-}
-
-template <int BK, int STAGES, class G, bool GELU, bool BIAS, bool F32OUT, bool PART>
-__device__ __forceinline__ int tile_pipe_any(int nbv, const uint16_t *smem, uint32_t lds0, int b, const CopyGeo &cg,
-                                             i32x4 rw, i32x4 ra, int kt_lo, int kt_hi, const NextSrc &next,
-                                             i32x4 null_w, i32x4 null_a, void *C, const uint16_t *bseg, float *part,
-                                             int64_t row0, int64_t row_end, int n0, int N)
-{
-#define MOE_TP(V)                                                                                                   \
-    tile_pipe<BK, STAGES, G, V, GELU, BIAS, F32OUT, PART>(smem, lds0, b, cg, rw, ra, kt_lo, kt_hi, next, null_w,    \
-                                                          null_a, C, bseg, part, row0, row_end, n0, N)
-    if (G::FB == 4) {
-        switch (nbv) {
-        case 4: return MOE_TP(G::FB >= 4 ? 4 : G::FB);
-        case 3: return MOE_TP(G::FB >= 3 ? 3 : G::FB);
-        default: break;
-        }
-    }
-    switch (nbv) {
-    case 2: return MOE_TP(G::FB >= 2 ? 2 : G::FB);
-    case 1: return MOE_TP(1);
-    default: return MOE_TP(0);
-    }
-#undef MOE_TP
-}
-
-// Work item i of a block: its whole tiles (an XCD-contiguous share of
-// [0, F), as in grouped_gemm_bf16_256), then its tail unit if it has one.
-struct Work {
-    TileLoc t;
-    int kt_lo, kt_hi;
-    int unit; // tail unit, or -1 for a whole tile
-};
-
-// Needs K / BK >= STAGES - 1 (the tail plan keeps every K range that long).
-template <int BK, int STAGES, class G, bool GELU, bool BIAS, bool F32OUT>
-__global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_pipe(const uint16_t *__restrict__ A,
-                                                                   const int32_t *__restrict__ seg, int S,
-                                                                   int64_t max_rows, const uint16_t *__restrict__ W,
-                                                                   const uint16_t *__restrict__ bias,
-                                                                   void *__restrict__ C, int N, int K, int Ka,
-                                                                   float *__restrict__ part_ws)
-{
-    constexpr int CPR = BK / 8, RPI = 64 / CPR, NQ = kL / (G::NW * RPI);
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * 2 * kL * BK];
-    __shared__ int tb[kMaxSeg + 1];
-    build_tile_prefix<kL>(seg, S, max_rows, tb);
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / G::WGN_;
-    const int NT = (N + kL - 1) / kL;
-    const int KT = K / BK;
-    const int64_t total = (int64_t)tb[S] * NT;
-    const TailPlan plan = plan_tail(total, (int)gridDim.x, KT, part_ws != nullptr, STAGES - 1);
-
-    const int xcd = blockIdx.x % kXcds;
-    const int per = gridDim.x / kXcds;
-    const int j = blockIdx.x / kXcds;
-    const int64_t rlo = plan.F * xcd / kXcds, rhi = plan.F * (xcd + 1) / kXcds;
-    const int64_t first = rlo + j;
-    const int nw = first < rhi ? (int)((rhi - first + per - 1) / per) : 0;
-    const int unit = blockIdx.x;
-    const bool has_tail = plan.rem > 0 && unit < plan.rem * plan.sk;
-    const int n_work = nw + (has_tail ? 1 : 0);
-    if (n_work == 0)
-        return;
-
-    CopyGeo cg;
-    {
-        const int lrow = lane / CPR;
-        const int prow = wave * RPI + lrow;
-        const int lchunk = (lane % CPR) ^ swz<BK>(prow);
-        cg.row_w = (uint32_t)K * 2u;
-        cg.row_a = (uint32_t)Ka * 2u;
-        cg.vbase = (uint32_t)prow * cg.row_w + (uint32_t)lchunk * 16u;
-        cg.vbase_a = (uint32_t)prow * cg.row_a + (uint32_t)lchunk * 16u;
-        cg.KTa = Ka / BK;
-    }
-    auto work = [&](int i) {
-        Work w;
-        if (i < nw) {
-            w.t = locate(tb, seg, S, max_rows, NT, first + (int64_t)i * per);
-            w.kt_lo = 0;
-            w.kt_hi = KT;
-            w.unit = -1;
-        } else {
-            const int c = unit % plan.sk;
-            w.t = locate(tb, seg, S, max_rows, NT, plan.F + unit / plan.sk);
-            w.kt_lo = (int)((int64_t)KT * c / plan.sk);
-            w.kt_hi = (int)((int64_t)KT * (c + 1) / plan.sk);
-            w.unit = unit;
-        }
-        return w;
-    };
-    auto src_of = [&](const Work &w, i32x4 &rw, i32x4 &ra) {
-        const int wrows = min(kL, N - w.t.n0);
-        const int arows = (int)(w.t.row_end - w.t.row0);
-        rw = make_rsrc(W + (int64_t)w.t.s * N * K + (int64_t)w.t.n0 * K, (uint32_t)wrows * cg.row_w);
-        ra = make_rsrc(A + w.t.row0 * Ka, (uint32_t)arows * cg.row_a);
-    };
-    const i32x4 null_w = make_rsrc(W, 0), null_a = make_rsrc(A, 0);
-
-    const uint32_t lds0 = lds_addr(smem);
-    Work w = work(0);
-    i32x4 rw, ra;
-    src_of(w, rw, ra);
-    // Prologue: the first STAGES-1 K steps of the first work item.
-#pragma unroll
-    for (int p = 0; p < STAGES - 1; ++p) {
-        const Fill f = fill_at<BK>(rw, ra, w.kt_lo + p, cg.KTa);
-#pragma unroll
-        for (int i = 0; i < 2 * NQ; ++i)
-            copy_one<BK, G>(cg, f, lds0 + (uint32_t)(p * 2 * kL * BK) * 2u, wave, i);
-    }
-    stage_barrier<(STAGES - 2) * 2 * NQ>();
-    int b = 0;
-    for (int i = 0; i < n_work; ++i) {
-        Work wn = w;
-        NextSrc next;
-        next.any = i + 1 < n_work;
-        next.rw = null_w;
-        next.ra = null_a;
-        next.kt_lo = 0;
-        if (next.any) {
-            wn = work(i + 1);
-            src_of(wn, next.rw, next.ra);
-            next.kt_lo = wn.kt_lo;
-        }
-        const int nbv = valid_b<G>(w.t, wm);
-        if (w.unit < 0)
-            b = tile_pipe_any<BK, STAGES, G, GELU, BIAS, F32OUT, false>(
-                nbv, smem, lds0, b, cg, rw, ra, w.kt_lo, w.kt_hi, next, null_w, null_a, C,
-                bias ? bias + (int64_t)w.t.s * N : nullptr, nullptr, w.t.row0, w.t.row_end, w.t.n0, N);
-        else
-            b = tile_pipe_any<BK, STAGES, G, GELU, BIAS, F32OUT, true>(
-                nbv, smem, lds0, b, cg, rw, ra, w.kt_lo, w.kt_hi, next, null_w, null_a, C, nullptr,
-                part_ws + (size_t)w.unit * (kL * kL), w.t.row0, w.t.row_end, w.t.n0, N);
-        w = wn;
-        rw = next.rw;
-        ra = next.ra;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Register-staged form: operands marked REG go global -> VGPR two K steps
-// ahead and VGPR -> LDS (ds_write) one step ahead; the others go by LDS-DMA
-// one step ahead.  Two LDS stages plus the staged registers give three
-// stages in flight.  Plain vector loads stream faster into the CU than LDS-DMA
-// copies do, at the cost of the staging registers.
-// ---------------------------------------------------------------------------
-
-template <int BK, class G> struct Staged {
-    static constexpr int DPW = 2 * (kL / (G::NW * (64 / (BK / 8))));
-    u32x4 v[DPW];
-};
-
-// A stage source as plain scalars (base addresses and byte sizes of the
-// tile's W and A rows); the buffer resources are formed where a copy is
-// issued.  Sizes of zero make every copy out of range (zeros, no access).
-struct Src2 {
-    uint64_t wbase, abase;
-    uint32_t wbytes, abytes;
-};
-
-struct Fill2 {
-    Src2 s;
-    uint32_t so_w, so_a;
-};
-
-template <int BK> __device__ __forceinline__ Fill2 fill2_at(const Src2 &s, int kt, int KTa)
-{
-    Fill2 f;
-    f.s = s;
-    f.so_w = (uint32_t)kt * (BK * 2);
-    f.so_a = (uint32_t)(kt % KTa) * (BK * 2);
-    return f;
-}
-
-__device__ __forceinline__ Src2 src2_of(const uint16_t *w, uint32_t wbytes, const uint16_t *a, uint32_t abytes)
-{
-    Src2 s;
-    s.wbase = (uint64_t)uni64((int64_t)(uintptr_t)w);
-    s.abase = (uint64_t)uni64((int64_t)(uintptr_t)a);
-    s.wbytes = (uint32_t)uni((int)wbytes);
-    s.abytes = (uint32_t)uni((int)abytes);
-    return s;
-}
-
-__device__ __forceinline__ i32x4 raw_rsrc(uint64_t base, uint32_t bytes)
-{
-    return make_rsrc((const void *)(uintptr_t)base, bytes);
-}
-
-__device__ __forceinline__ u32x4 buf_load16(uint64_t base, uint32_t bytes, uint32_t voff, uint32_t soff)
-{
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)base, (short)0, (int)bytes, kRsrcWord3);
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-
-// Order in which a K step issues its copies: LDS-DMA ones first, then the
-// register loads (so a wait that leaves the register loads in flight has
-// the LDS-DMA copies landed).
-template <bool WREG, bool AREG, int DPW> __device__ __forceinline__ constexpr int copy_order(int n)
-{
-    return (WREG == AREG) ? n : (!WREG ? (n < DPW / 2 ? 2 * n : 2 * (n - DPW / 2) + 1)
-                                       : (n < DPW / 2 ? 2 * n + 1 : 2 * (n - DPW / 2)));
-}
-
-// Copy i of a stage: scalar offset of its rows.
-template <int BK, class G>
-__device__ __forceinline__ uint32_t copy_soff(const CopyGeo &cg, const Fill2 &f, int i)
-{
-    constexpr int CPR = BK / 8, RPI = 64 / CPR, NW = G::NW;
-    const int q = i >> 1;
-    return (i & 1) ? (uint32_t)q * (uint32_t)(NW * RPI) * cg.row_a + f.so_a
-                   : (uint32_t)q * (uint32_t)(NW * RPI) * cg.row_w + f.so_w;
-}
-
-// LDS byte offset (within a stage) of copy i's 16 bytes for this lane.
-template <int BK, class G> __device__ __forceinline__ uint32_t copy_ldsoff(int wave, int lane, int i)
-{
-    constexpr int CPR = BK / 8, RPI = 64 / CPR, NW = G::NW;
-    const int q = i >> 1;
-    const uint32_t R = (uint32_t)((NW * q + wave) * RPI);
-    return (uint32_t)((i & 1) * (kL * BK) + R * BK) * 2u + (uint32_t)lane * 16u;
-}
-
-template <bool WREG, bool AREG> __device__ __forceinline__ constexpr bool in_reg(int i)
-{
-    return (i & 1) ? AREG : WREG;
-}
-
-#ifndef MOE_PIPE_FA1
-#define MOE_PIPE_FA1 0 // 1: single-buffered A fragments (fewer registers, exposed LDS latency)
-#endif
-#ifndef MOE_PIPE_WSP
-#define MOE_PIPE_WSP 8 // the staged registers go to LDS over the first WSP chunks of a K step
-#endif
-
-template <int BK, class G, int NBV, bool WREG, bool AREG>
-__device__ __forceinline__ void k_step_pipe2(const uint16_t *cur, uint16_t *nxt, uint32_t nxt_lds, const Fill2 &f1,
-                                             const Fill2 &f2, Staged<BK, G> &stg, const CopyGeo &cg,
-                                             f32x16 (&acc)[G::FA][G::FB], bf16x8 (&fa)[2][G::FA],
-                                             bf16x8 (&fb)[2][G::FB], int wave, int lane, int wn, int wm, int r32,
-                                             int khalf, int sw)
-{
-    constexpr int FA = G::FA, FB = G::FB;
-    constexpr int KS = BK / 16;
-    constexpr int DPW = Staged<BK, G>::DPW;
-    constexpr int NDMA = (WREG ? 0 : DPW / 2) + (AREG ? 0 : DPW / 2);
-    constexpr int NREG = DPW - NDMA;
-    constexpr int CPS = MOE_PIPE_CPS < FA * FB ? MOE_PIPE_CPS : FA * FB;
-    constexpr int MPC = FA * FB / CPS;
-    constexpr int RDS = FA + FB;
-    constexpr int RCH = MOE_PIPE_RCH < CPS ? MOE_PIPE_RCH : CPS;
-    constexpr int RPC = (RDS + RCH - 1) / RCH;
-    constexpr int NPRE = (KS - 1) * CPS;
-    constexpr int WSP = MOE_PIPE_WSP < NPRE ? MOE_PIPE_WSP : NPRE; // chunks the register writes spread over
-    static_assert(KS >= 2 && (FA * FB) % CPS == 0, "chunking");
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const uint16_t *src = ks + 1 < KS ? cur : nxt;
-        const int kn = ks + 1 < KS ? ks + 1 : 0;
-#pragma unroll
-        for (int c = 0; c < CPS; ++c) {
-            if (NBV > 0) {
-#pragma unroll
-                for (int m = 0; m < MPC; ++m) {
-                    const int i = c * MPC + m;
-                    const int a = i / FB, b = i % FB;
-                    if (b < NBV)
-                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[MOE_PIPE_FA1 ? 0 : ks & 1][a],
-                                                                            fb[ks & 1][b], acc[a][b], 0, 0, 0);
-                    if (MOE_PIPE_FA1) {
-                        // A fragment a is single-buffered: its next sub-step's
-                        // value is read once its last MFMA (a, FB-1) has issued;
-                        // B fragments are double-buffered and read first.
-                        if (i < FB)
-                            read_frag<BK, G, NBV>(src, kn, fa[0], fb[(ks + 1) & 1], FA + i, wn, wm, r32, khalf, sw);
-                        if (b == FB - 1)
-                            read_frag<BK, G, NBV>(src, kn, fa[0], fb[(ks + 1) & 1], a, wn, wm, r32, khalf, sw);
-                    } else {
-#pragma unroll
-                        for (int q = 0; q < RPC; ++q) {
-                            const int r = c * RPC + q;
-                            if (c < RCH && r < RDS && (q * MPC) / RPC == m)
-                                read_frag<BK, G, NBV>(src, kn, fa[(ks + 1) & 1], fb[(ks + 1) & 1], read_slot<G>(r),
-                                                      wn, wm, r32, khalf, sw);
-                        }
-                    }
-                }
-                if (NBV == FB) {
-#pragma unroll
-                    for (int m = 0; m < MPC; ++m) {
-                        const int i = c * MPC + m;
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        if (MOE_PIPE_FA1) {
-                            if (i < FB)
-                                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                            if (i % FB == FB - 1)
-                                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                        } else {
-#pragma unroll
-                            for (int q = 0; q < RPC; ++q)
-                                if (c < RCH && c * RPC + q < RDS && (q * MPC) / RPC == m)
-                                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                        }
-                    }
-                }
-            }
-            if (ks + 1 < KS) {
-                const int g = ks * CPS + c;
-                __builtin_amdgcn_sched_barrier(0);
-                if (NREG > 0) {
-                    // staged registers (K step kt+1) -> the next stage, spread
-                    // over the first WSP chunks; register j is reloaded only in
-                    // this chunk or a later one (after its write)
-#pragma unroll
-                    for (int j = 0; j < DPW; ++j)
-                        if (in_reg<WREG, AREG>(j) && (j * WSP) / DPW == g)
-                            *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(nxt) + copy_ldsoff<BK, G>(wave, lane, j)) =
-                                stg.v[j];
-                }
-                // copies in order: LDS-DMA ones (step kt+1) first, then the
-                // register loads (step kt+2); copy n goes after chunk n*NPRE/DPW
-#pragma unroll
-                for (int n = 0; n < DPW; ++n) {
-                    if ((n * NPRE) / DPW != g)
-                        continue;
-                    const int j = copy_order<WREG, AREG, DPW>(n);
-                    if (!in_reg<WREG, AREG>(j)) {
-                        const uint32_t so = copy_soff<BK, G>(cg, f1, j);
-                        dma16((j & 1) ? raw_rsrc(f1.s.abase, f1.s.abytes) : raw_rsrc(f1.s.wbase, f1.s.wbytes),
-                              (j & 1) ? cg.vbase_a : cg.vbase, so, nxt_lds + copy_ldsoff<BK, G>(wave, 0, j));
-                    } else {
-                        const uint32_t so = copy_soff<BK, G>(cg, f2, j);
-                        stg.v[j] = (j & 1) ? buf_load16(f2.s.abase, f2.s.abytes, cg.vbase_a, so)
-                                           : buf_load16(f2.s.wbase, f2.s.wbytes, cg.vbase, so);
-                    }
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        if (ks == KS - 2) {
-            // the next stage is complete (its copies and register writes);
-            // the register loads of the stage after it may be in flight
-            __builtin_amdgcn_sched_barrier(0);
-            stage_barrier<NREG>();
+            stage_barrier<DPW>();
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
 
-// One tile (or one K range of a tail tile) of the register-staged kernel.
-// On entry LDS stage b holds its first K step (landed, behind a barrier) and
-// the staged registers hold its second; on exit the same holds for the next
-// work item (sw*/sa*: own rows; nw*/na*: the next item's, sizes 0 if none).
-template <int BK, class G, int NBV, bool WREG, bool AREG, bool GELU, bool BIAS, bool F32OUT, bool PART>
-__device__ __forceinline__ int tile_pipe2(uint16_t *smem, uint32_t lds0, int b, const CopyGeo &cg, uint64_t swb,
-                                          uint64_t sab, uint32_t sws, uint32_t sas, int kt_lo, int kt_hi,
-                                          uint64_t nwb, uint64_t nab, uint32_t nws, uint32_t nas, int n_kt_lo,
-                                          Staged<BK, G> &stg, void *C, const uint16_t *bseg, float *part,
-                                          int64_t row0, int64_t row_end, int n0, int N)
-{
-    constexpr int FA = G::FA, FB = G::FB, STAGE = 2 * kL * BK;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wn = wave % G::WGN_, wm = wave / G::WGN_;
-    const int r32 = lane & 31, khalf = lane >> 5;
-    const int sw = swz<BK>(r32);
+// What a block needs to find its work items: item i < nw is whole tile
+// first + i * per (an XCD-contiguous share of [0, F)); item nw, if any, is
+// its tail unit (one K range of a tail tile).
+struct WorkCtx {
+    const int *tb;
+    const int32_t *seg;
+    const uint16_t *A, *W;
+    int64_t max_rows, first, F;
+    int S, N, K, Ka, NT, KT, per, nw, unit, sk, n_work;
+};
 
-    f32x16 acc[FA][FB];
-#pragma unroll
-    for (int a = 0; a < FA; ++a)
-#pragma unroll
-        for (int q = 0; q < FB; ++q)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                acc[a][q][v] = 0.f;
-    bf16x8 fa[2][FA], fb[2][FB];
-    if (NBV > 0) {
-#pragma unroll
-        for (int r = 0; r < FA + FB; ++r)
-            read_frag<BK, G, NBV>(smem + b * STAGE, 0, fa[0], fb[0], r, wn, wm, r32, khalf, sw);
-    }
-    for (int kt = kt_lo; kt < kt_hi; ++kt) {
-        // K steps kt+1 (LDS-DMA operands) and kt+2 (register operands): own
-        // rows while inside [kt_lo, kt_hi), else the next item's first steps.
-        Fill2 f1, f2;
-        {
-            const bool own = kt + 1 < kt_hi;
-            f1.s.wbase = own ? swb : nwb;
-            f1.s.abase = own ? sab : nab;
-            f1.s.wbytes = own ? sws : nws;
-            f1.s.abytes = own ? sas : nas;
-            const int k1 = own ? kt + 1 : n_kt_lo + (kt + 1 - kt_hi);
-            f1.so_w = (uint32_t)k1 * (BK * 2);
-            f1.so_a = (uint32_t)(k1 % cg.KTa) * (BK * 2);
-        }
-        {
-            const bool own = kt + 2 < kt_hi;
-            f2.s.wbase = own ? swb : nwb;
-            f2.s.abase = own ? sab : nab;
-            f2.s.wbytes = own ? sws : nws;
-            f2.s.abytes = own ? sas : nas;
-            const int k2 = own ? kt + 2 : n_kt_lo + (kt + 2 - kt_hi);
-            f2.so_w = (uint32_t)k2 * (BK * 2);
-            f2.so_a = (uint32_t)(k2 % cg.KTa) * (BK * 2);
-        }
-        const int bn = b ^ 1;
-        k_step_pipe2<BK, G, NBV, WREG, AREG>(smem + b * STAGE, smem + bn * STAGE, lds0 + (uint32_t)(bn * STAGE) * 2u,
-                                             f1, f2, stg, cg, acc, fa, fb, wave, lane, wn, wm, r32, khalf, sw);
-        b = bn;
-    }
-    if (PART) {
-        float *dst = part + (size_t)wave * (FA * FB * 16 * 64) + lane;
-#pragma unroll
-        for (int a = 0; a < FA; ++a)
-#pragma unroll
-            for (int q = 0; q < FB; ++q)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    dst[((a * FB + q) * 16 + v) * 64] = acc[a][q][v];
-    } else {
-        store_tile<G, NBV, GELU, BIAS, F32OUT>(acc, C, bseg, row0, row_end, n0, N, wn, wm, r32, khalf);
-    }
-    return b;
-}
-
-template <int BK, class G, bool WREG, bool AREG, bool GELU, bool BIAS, bool F32OUT, bool PART>
-__device__ __forceinline__ int tile_pipe2_any(int nbv, uint16_t *smem, uint32_t lds0, int b, const CopyGeo &cg,
-                                              uint64_t swb, uint64_t sab, uint32_t sws, uint32_t sas, int kt_lo,
-                                              int kt_hi, uint64_t nwb, uint64_t nab, uint32_t nws, uint32_t nas,
-                                              int n_kt_lo, Staged<BK, G> &stg, void *C, const uint16_t *bseg,
-                                              float *part, int64_t row0, int64_t row_end, int n0, int N)
-{
-#define MOE_TP2(V)                                                                                                  \
-    tile_pipe2<BK, G, V, WREG, AREG, GELU, BIAS, F32OUT, PART>(smem, lds0, b, cg, swb, sab, sws, sas, kt_lo, kt_hi, \
-                                                               nwb, nab, nws, nas, n_kt_lo, stg, C, bseg, part,     \
-                                                               row0, row_end, n0, N)
-    if (G::FB == 4) {
-        switch (nbv) {
-        case 4: return MOE_TP2(G::FB >= 4 ? 4 : G::FB);
-        case 3: return MOE_TP2(G::FB >= 3 ? 3 : G::FB);
-        default: break;
-        }
-    }
-    switch (nbv) {
-    case 2: return MOE_TP2(G::FB >= 2 ? 2 : G::FB);
-    case 1: return MOE_TP2(1);
-    default: return MOE_TP2(0);
-    }
-#undef MOE_TP2
-}
-
-// Work item i of a block: its whole tiles (an XCD-contiguous share of
-// [0, F)), then its tail unit if it has one; all fields wave-uniform.
-__device__ __forceinline__ Work get_work(int i, int nw, int64_t first, int per, int unit, const TailPlan &plan,
-                                         const int *tb, const int32_t *seg, int S, int64_t max_rows, int NT, int KT)
+// Work item i, all fields wave-uniform.
+__device__ __forceinline__ Work get_work(const WorkCtx &x, int i)
 {
     Work w;
-    if (i < nw) {
-        w.t = locate(tb, seg, S, max_rows, NT, first + (int64_t)i * per);
+    if (i < x.nw) {
+        w.t = locate(x.tb, x.seg, x.S, x.max_rows, x.NT, x.first + (int64_t)i * x.per);
         w.kt_lo = 0;
-        w.kt_hi = KT;
+        w.kt_hi = x.KT;
         w.unit = -1;
     } else {
-        const int c = unit % plan.sk;
-        w.t = locate(tb, seg, S, max_rows, NT, plan.F + unit / plan.sk);
-        w.kt_lo = (int)((int64_t)KT * c / plan.sk);
-        w.kt_hi = (int)((int64_t)KT * (c + 1) / plan.sk);
-        w.unit = unit;
+        const int c = x.unit % x.sk;
+        w.t = locate(x.tb, x.seg, x.S, x.max_rows, x.NT, x.F + x.unit / x.sk);
+        w.kt_lo = (int)((int64_t)x.KT * c / x.sk);
+        w.kt_hi = (int)((int64_t)x.KT * (c + 1) / x.sk);
+        w.unit = x.unit;
     }
     w.t.s = uni(w.t.s);
     w.t.row0 = uni64(w.t.row0);
@@ -1458,19 +679,128 @@ __device__ __forceinline__ Work get_work(int i, int nw, int64_t first, int per, 
     return w;
 }
 
-// Needs K / BK >= 2 (the tail plan keeps every K range that long).
-template <int BK, class G, bool WREG, bool AREG, bool GELU, bool BIAS, bool F32OUT>
-__global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_pipe2(const uint16_t *__restrict__ A,
-                                                                    const int32_t *__restrict__ seg, int S,
-                                                                    int64_t max_rows, const uint16_t *__restrict__ W,
-                                                                    const uint16_t *__restrict__ bias,
-                                                                    void *__restrict__ C, int N, int K, int Ka,
-                                                                    float *__restrict__ part_ws)
+// Load source (W and A rows) of work item w.
+struct Src {
+    uint64_t wbase, abase;
+    uint32_t wbytes, abytes;
+};
+
+__device__ __forceinline__ Src src_of(const WorkCtx &x, const CopyGeo &cg, const Work &w)
+{
+    Src s;
+    s.wbase = (uint64_t)(uintptr_t)(x.W + (int64_t)w.t.s * x.N * x.K + (int64_t)w.t.n0 * x.K);
+    s.abase = (uint64_t)(uintptr_t)(x.A + w.t.row0 * x.Ka);
+    s.wbytes = (uint32_t)min(kL, x.N - w.t.n0) * cg.row_w;
+    s.abytes = (uint32_t)(w.t.row_end - w.t.row0) * cg.row_a;
+    return s;
+}
+
+// One tile (or one K range of a tail tile): work item i.  On entry LDS
+// stage b holds its first K step (complete, behind a barrier) and the staged
+// registers hold its second; on exit the same holds for item i+1 (nothing
+// is loaded if there is none).  The loads switch to item i+1's rows for the
+// last two K steps; its source is looked up only then, so that it does not
+// occupy registers during the loop.
+template <int BK, class G, int NBV, bool GELU, bool BIAS, bool F32OUT, bool PART>
+__device__ __forceinline__ int tile(uint16_t *smem, int b, const CopyGeo &cg, const WorkCtx &x, int i, Src src,
+                                    int kt_lo, int kt_hi, Staged<BK, G> &stg, void *C, const uint16_t *bseg,
+                                    float *part, int64_t row0, int64_t row_end, int n0, int N)
+{
+    constexpr int FA = G::FA, FB = G::FB, STAGE = 2 * kL * BK;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wn = wave % G::WGN_, wm = wave / G::WGN_;
+    const int r32 = lane & 31, khalf = lane >> 5;
+    const int sw = swz(r32);
+
+    f32x16 acc[FA][FB];
+#pragma unroll
+    for (int a = 0; a < FA; ++a)
+#pragma unroll
+        for (int q = 0; q < FB; ++q)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[a][q][v] = 0.f;
+    bf16x8 fa[2][FA], fb[2][FB];
+    if (NBV > 0) {
+#pragma unroll
+        for (int r = 0; r < FA + FB; ++r)
+            read_frag<BK, G, NBV>(smem + b * STAGE, 0, fa[0], fb[0], r, wn, wm, r32, khalf, sw);
+    }
+    int koff = 0; // K step of `src` loaded at step kt: kt + 2 + koff
+    for (int kt = kt_lo; kt < kt_hi; ++kt) {
+        if (kt + 2 == kt_hi) {
+            // from here on, load the next item's first steps
+            if (i + 1 < x.n_work) {
+                const Work wn = get_work(x, i + 1);
+                src = src_of(x, cg, wn);
+                koff = wn.kt_lo - kt_hi;
+            } else {
+                src.wbytes = 0;
+                src.abytes = 0;
+                koff = -kt_hi;
+            }
+        }
+        const Fill f = fill_k<BK>(src.wbase, src.abase, src.wbytes, src.abytes, kt + 2 + koff, cg.KTa);
+        const int bn = b ^ 1;
+        k_step<BK, G, NBV>(smem + b * STAGE, smem + bn * STAGE, f, stg, cg, acc, fa, fb, wave, lane, wn, wm, r32,
+                           khalf, sw);
+        b = bn;
+    }
+    if (PART) {
+        float *dst = part + (size_t)wave * (FA * FB * 16 * 64) + lane;
+#pragma unroll
+        for (int a = 0; a < FA; ++a)
+#pragma unroll
+            for (int q = 0; q < FB; ++q)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    dst[((a * FB + q) * 16 + v) * 64] = acc[a][q][v];
+    } else {
+        store_tile<G, NBV, GELU, BIAS, F32OUT>(acc, C, bseg, row0, row_end, n0, N, wn, wm, r32, khalf);
+    }
+    return b;
+}
+
+template <int BK, class G, bool GELU, bool BIAS, bool F32OUT, bool PART>
+__device__ __forceinline__ int tile_any(int nbv, uint16_t *smem, int b, const CopyGeo &cg, const WorkCtx &x, int i,
+                                        Src src, int kt_lo, int kt_hi, Staged<BK, G> &stg, void *C,
+                                        const uint16_t *bseg, float *part, int64_t row0, int64_t row_end, int n0,
+                                        int N)
+{
+#define MOE_TILE(V)                                                                                                 \
+    tile<BK, G, V, GELU, BIAS, F32OUT, PART>(smem, b, cg, x, i, src, kt_lo, kt_hi, stg, C, bseg, part, row0,       \
+                                             row_end, n0, N)
+    if (G::FB == 4) {
+        switch (nbv) {
+        case 4: return MOE_TILE(G::FB >= 4 ? 4 : G::FB);
+        case 3: return MOE_TILE(G::FB >= 3 ? 3 : G::FB);
+        default: break;
+        }
+    }
+    switch (nbv) {
+    case 2: return MOE_TILE(G::FB >= 2 ? 2 : G::FB);
+    case 1: return MOE_TILE(1);
+    default: return MOE_TILE(0);
+    }
+#undef MOE_TILE
+}
+
+// Persistent grouped GEMM over 256x256 tiles.  The tile list is derived on
+// the device from the segment offsets; whole tiles are dealt to the XCDs as
+// contiguous ranges, and a short last round is split along K (tail units).
+// A's rows have Ka elements: its K offset wraps every Ka (Ka = K for a plain
+// GEMM).  Every K range is at least two steps long.
+template <int BK, class G, bool GELU, bool BIAS, bool F32OUT>
+__global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_256(const uint16_t *__restrict__ A,
+                                                                  const int32_t *__restrict__ seg, int S,
+                                                                  int64_t max_rows, const uint16_t *__restrict__ W,
+                                                                  const uint16_t *__restrict__ bias,
+                                                                  void *__restrict__ C, int N, int K, int Ka,
+                                                                  float *__restrict__ part_ws)
 {
     constexpr int CPR = BK / 8, RPI = 64 / CPR;
     constexpr int DPW = Staged<BK, G>::DPW;
-    constexpr int NDMA = (WREG ? 0 : DPW / 2) + (AREG ? 0 : DPW / 2);
-    constexpr int NREG = DPW - NDMA;
     __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * kL * BK];
     __shared__ int tb[kMaxSeg + 1];
     build_tile_prefix<kL>(seg, S, max_rows, tb);
@@ -1483,96 +813,75 @@ __global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_pipe2(const uint16
     const int64_t total = (int64_t)tb[S] * NT;
     const TailPlan plan = plan_tail(total, (int)gridDim.x, KT, part_ws != nullptr, 2);
 
+    WorkCtx x;
+    x.tb = tb;
+    x.seg = seg;
+    x.A = A;
+    x.W = W;
+    x.max_rows = max_rows;
+    x.S = S;
+    x.N = N;
+    x.K = K;
+    x.Ka = Ka;
+    x.NT = NT;
+    x.KT = KT;
+    x.F = plan.F;
+    x.sk = plan.sk;
     const int xcd = blockIdx.x % kXcds;
-    const int per = gridDim.x / kXcds;
-    const int jb = blockIdx.x / kXcds;
+    x.per = gridDim.x / kXcds;
     const int64_t rlo = plan.F * xcd / kXcds, rhi = plan.F * (xcd + 1) / kXcds;
-    const int64_t first = rlo + jb;
-    const int nw = first < rhi ? (int)((rhi - first + per - 1) / per) : 0;
-    const int unit = blockIdx.x;
-    const bool has_tail = plan.rem > 0 && unit < plan.rem * plan.sk;
-    const int n_work = nw + (has_tail ? 1 : 0);
-    if (n_work == 0)
+    x.first = rlo + blockIdx.x / kXcds;
+    x.nw = x.first < rhi ? (int)((rhi - x.first + x.per - 1) / x.per) : 0;
+    x.unit = blockIdx.x;
+    const bool has_tail = plan.rem > 0 && x.unit < plan.rem * plan.sk;
+    x.n_work = x.nw + (has_tail ? 1 : 0);
+    if (x.n_work == 0)
         return;
 
     CopyGeo cg;
     {
         const int lrow = lane / CPR;
         const int prow = wave * RPI + lrow;
-        const int lchunk = (lane % CPR) ^ swz<BK>(prow);
+        const int lchunk = (lane % CPR) ^ swz(prow);
         cg.row_w = (uint32_t)K * 2u;
         cg.row_a = (uint32_t)Ka * 2u;
         cg.vbase = (uint32_t)prow * cg.row_w + (uint32_t)lchunk * 16u;
         cg.vbase_a = (uint32_t)prow * cg.row_a + (uint32_t)lchunk * 16u;
         cg.KTa = Ka / BK;
     }
-    const uint32_t lds0 = lds_addr(smem);
 
-    Work w = get_work(0, nw, first, per, unit, plan, tb, seg, S, max_rows, NT, KT);
-    uint64_t swb = (uint64_t)(uintptr_t)(W + (int64_t)w.t.s * N * K + (int64_t)w.t.n0 * K);
-    uint64_t sab = (uint64_t)(uintptr_t)(A + w.t.row0 * Ka);
-    uint32_t sws = (uint32_t)min(kL, N - w.t.n0) * cg.row_w;
-    uint32_t sas = (uint32_t)(w.t.row_end - w.t.row0) * cg.row_a;
     Staged<BK, G> stg;
-    // Prologue: K step kt_lo into LDS stage 0, kt_lo+1 into the staged registers.
+    // Prologue: K step kt_lo of item 0 into LDS stage 0, kt_lo+1 into the
+    // staged registers.
     {
-        Fill2 f0;
-        f0.s.wbase = swb;
-        f0.s.abase = sab;
-        f0.s.wbytes = sws;
-        f0.s.abytes = sas;
-        f0.so_w = (uint32_t)w.kt_lo * (BK * 2);
-        f0.so_a = (uint32_t)(w.kt_lo % cg.KTa) * (BK * 2);
-#pragma unroll
-        for (int i = 0; i < DPW; ++i) {
-            const uint32_t so = copy_soff<BK, G>(cg, f0, i);
-            if (in_reg<WREG, AREG>(i))
-                stg.v[i] = (i & 1) ? buf_load16(sab, sas, cg.vbase_a, so) : buf_load16(swb, sws, cg.vbase, so);
-            else
-                dma16((i & 1) ? raw_rsrc(sab, sas) : raw_rsrc(swb, sws), (i & 1) ? cg.vbase_a : cg.vbase, so,
-                      lds0 + copy_ldsoff<BK, G>(wave, 0, i));
-        }
+        const Work w = get_work(x, 0);
+        const Src o = src_of(x, cg, w);
+        const Fill f0 = fill_k<BK>(o.wbase, o.abase, o.wbytes, o.abytes, w.kt_lo, cg.KTa);
 #pragma unroll
         for (int i = 0; i < DPW; ++i)
-            if (in_reg<WREG, AREG>(i))
-                *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(smem) + copy_ldsoff<BK, G>(wave, lane, i)) =
-                    stg.v[i];
-        wait_vmcnt<0>();
-        f0.so_w = (uint32_t)(w.kt_lo + 1) * (BK * 2);
-        f0.so_a = (uint32_t)((w.kt_lo + 1) % cg.KTa) * (BK * 2);
+            stg.v[i] = copy_load<BK, G>(cg, f0, i);
 #pragma unroll
         for (int i = 0; i < DPW; ++i)
-            if (in_reg<WREG, AREG>(i))
-                stg.v[i] = (i & 1) ? buf_load16(sab, sas, cg.vbase_a, copy_soff<BK, G>(cg, f0, i))
-                                   : buf_load16(swb, sws, cg.vbase, copy_soff<BK, G>(cg, f0, i));
-        stage_barrier<NREG>();
+            *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(smem) + copy_ldsoff<BK, G>(wave, lane, i)) = stg.v[i];
+        const Fill f1 = fill_k<BK>(o.wbase, o.abase, o.wbytes, o.abytes, w.kt_lo + 1, cg.KTa);
+#pragma unroll
+        for (int i = 0; i < DPW; ++i)
+            stg.v[i] = copy_load<BK, G>(cg, f1, i);
+        stage_barrier<DPW>();
     }
     int b = 0;
-    for (int i = 0; i < n_work; ++i) {
-        Work wn = w;
-        uint64_t nwb = swb, nab = sab;
-        uint32_t nws = 0, nas = 0;
-        if (i + 1 < n_work) {
-            wn = get_work(i + 1, nw, first, per, unit, plan, tb, seg, S, max_rows, NT, KT);
-            nwb = (uint64_t)(uintptr_t)(W + (int64_t)wn.t.s * N * K + (int64_t)wn.t.n0 * K);
-            nab = (uint64_t)(uintptr_t)(A + wn.t.row0 * Ka);
-            nws = (uint32_t)min(kL, N - wn.t.n0) * cg.row_w;
-            nas = (uint32_t)(wn.t.row_end - wn.t.row0) * cg.row_a;
-        }
+    for (int i = 0; i < x.n_work; ++i) {
+        const Work w = get_work(x, i);
+        const Src o = src_of(x, cg, w);
         const int nbv = valid_b<G>(w.t, wm);
         if (w.unit < 0)
-            b = tile_pipe2_any<BK, G, WREG, AREG, GELU, BIAS, F32OUT, false>(
-                nbv, smem, lds0, b, cg, swb, sab, sws, sas, w.kt_lo, w.kt_hi, nwb, nab, nws, nas, wn.kt_lo, stg, C,
-                bias ? bias + (int64_t)w.t.s * N : nullptr, nullptr, w.t.row0, w.t.row_end, w.t.n0, N);
+            b = tile_any<BK, G, GELU, BIAS, F32OUT, false>(nbv, smem, b, cg, x, i, o, w.kt_lo, w.kt_hi, stg, C,
+                                                           bias ? bias + (int64_t)w.t.s * N : nullptr, nullptr,
+                                                           w.t.row0, w.t.row_end, w.t.n0, N);
         else
-            b = tile_pipe2_any<BK, G, WREG, AREG, GELU, BIAS, F32OUT, true>(
-                nbv, smem, lds0, b, cg, swb, sab, sws, sas, w.kt_lo, w.kt_hi, nwb, nab, nws, nas, wn.kt_lo, stg, C,
-                nullptr, part_ws + (size_t)w.unit * (kL * kL), w.t.row0, w.t.row_end, w.t.n0, N);
-        w = wn;
-        swb = nwb;
-        sab = nab;
-        sws = nws;
-        sas = nas;
+            b = tile_any<BK, G, GELU, BIAS, F32OUT, true>(nbv, smem, b, cg, x, i, o, w.kt_lo, w.kt_hi, stg, C,
+                                                          nullptr, part_ws + (size_t)w.unit * (kL * kL), w.t.row0,
+                                                          w.t.row_end, w.t.n0, N);
     }
 }
 
@@ -1714,27 +1023,6 @@ int device_cus()
     return cached_cus;
 }
 
-#ifndef MOE_GEMM_BK
-#define MOE_GEMM_BK 64
-#endif
-#ifndef MOE_GEMM_STAGES
-#define MOE_GEMM_STAGES 2
-#endif
-#ifndef MOE_GEMM_WGM
-#define MOE_GEMM_WGM 4
-#endif
-#ifndef MOE_GEMM_PIPE
-#define MOE_GEMM_PIPE 2
-#endif
-#ifndef MOE_PIPE_WREG
-#define MOE_PIPE_WREG 1
-#endif
-#ifndef MOE_PIPE_AREG
-#define MOE_PIPE_AREG 1
-#endif
-constexpr int kLargeBK = MOE_GEMM_BK, kLargeStages = MOE_GEMM_STAGES;
-typedef Grid<2, MOE_GEMM_WGM> LargeGrid;
-
 // One block per CU (a multiple of the XCD count).  With a split-K workspace
 // a problem of few tiles still fills the chip (the tail plan cuts their K);
 // without one, blocks beyond the tile count would only idle.
@@ -1757,26 +1045,14 @@ moe_status_t run_large(const void *a, const int32_t *seg, int S, int64_t max_row
 {
     typedef LargeGrid G;
     const int grid = large_grid(max_rows, S, N, part_ws != nullptr);
-#if MOE_GEMM_PIPE == 2
-    const int min_len = 2;
-    grouped_gemm_pipe2<kLargeBK, G, MOE_PIPE_WREG, MOE_PIPE_AREG, GELU, BIAS, F32OUT>
-        <<<(unsigned)grid, 64 * G::NW, 0, stream>>>((const uint16_t *)a, seg, S, max_rows, (const uint16_t *)w,
-                                                     (const uint16_t *)bias, out, N, K, Ka, part_ws);
-#elif MOE_GEMM_PIPE
-    const int min_len = kLargeStages - 1;
-    grouped_gemm_pipe<kLargeBK, kLargeStages, G, GELU, BIAS, F32OUT><<<(unsigned)grid, 64 * G::NW, 0, stream>>>(
+    grouped_gemm_256<kLargeBK, G, GELU, BIAS, F32OUT><<<(unsigned)grid, 64 * G::NW, 0, stream>>>(
         (const uint16_t *)a, seg, S, max_rows, (const uint16_t *)w, (const uint16_t *)bias, out, N, K, Ka, part_ws);
-#else
-    const int min_len = 1;
-    grouped_gemm_bf16_256<kLargeBK, kLargeStages, G, GELU, BIAS, F32OUT><<<(unsigned)grid, 64 * G::NW, 0, stream>>>(
-        (const uint16_t *)a, seg, S, max_rows, (const uint16_t *)w, (const uint16_t *)bias, out, N, K, Ka, part_ws);
-#endif
-    if (moe_status_t st = check_launch("grouped_gemm_bf16_256"))
+    if (moe_status_t st = check_launch("grouped_gemm_256"))
         return st;
     if (!part_ws)
         return MOE_OK;
     grouped_gemm_reduce<G, GELU, BIAS, F32OUT><<<(unsigned)(grid / 2 * G::NW), 64 * G::FA, 0, stream>>>(
-        seg, S, max_rows, (const uint16_t *)bias, out, N, K, kLargeBK, min_len, grid, part_ws);
+        seg, S, max_rows, (const uint16_t *)bias, out, N, K, kLargeBK, 2, grid, part_ws);
     return check_launch("grouped_gemm_reduce");
 }
 
@@ -1828,7 +1104,7 @@ moe_status_t launch_grouped_gemm(const void *a, const int32_t *seg_offsets, int 
         return MOE_OK;
     const int S = seg_offsets ? num_segments : 1;
     if (dt == MOE_BF16) {
-        if (K % 64 == 0 && K / kLargeBK >= (MOE_GEMM_PIPE == 2 ? 2 : kLargeStages - 1)) {
+        if (K % kLargeBK == 0 && K / kLargeBK >= 2) {
             float *part = (ws && ws_bytes >= gemm_ws_bytes()) ? (float *)ws : nullptr;
             return run_bf16_256(a, seg_offsets, S, max_rows, N, K, w, bias, activation, out, part, stream);
         }
