@@ -148,6 +148,24 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = w.T * args.steps / elapsed
 
+    # ---- with a shared expert: the same step with it on a second stream ----
+    overlap = None
+    if w.shared_expert:
+        side = torch.cuda.Stream(device=dev)
+        y_ov = torch.empty_like(y)
+        for _ in range(args.warmup):
+            layer.forward(x, y_ov, side_stream=side)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            layer.forward(x, y_ov, side_stream=side)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t1
+        overlap = {"entry_point": "moe_forward_overlap", "ms_per_step": round(el * 1e3 / args.steps, 4),
+                   "value": round(w.T * args.steps / el, 1), "speedup": round(elapsed / el, 4),
+                   "same_bits": bool(torch.equal(y_ov.view(torch.int16), y.view(torch.int16)))
+                   if y.dtype == torch.bfloat16 else bool(torch.equal(y_ov, y))}
+
     # counts of the actual run
     seg = outs["seg_offsets"].cpu().numpy()
     rows = int(seg[-1])
@@ -258,6 +276,8 @@ def main():
         "stages": stages,
         "staged_step_us": round(staged_total, 1),
     }
+    if overlap is not None:
+        result["shared_overlap"] = overlap
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(result))

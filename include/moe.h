@@ -263,6 +263,28 @@ size_t moe_forward_workspace_size(const moe_problem_t *p);
 moe_status_t moe_forward(const moe_problem_t *p, const moe_weights_t *w, const void *x, void *y,
                          const moe_outputs_t *out, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------ *
+ * moe_forward_overlap - moe_forward with the shared expert on a second stream
+ * ("Expert Parallelism (EP)", "Key math / How it works": the shared expert's
+ * work does not depend on the routing, so it can run while the routed path
+ * routes and dispatches).
+ *
+ * side: a second stream of the same device (default priority).  The shared
+ * expert's two GEMMs are enqueued on it, ordered after the work already on
+ * `stream` at the call; the combine on `stream` waits for them.  Everything
+ * else is enqueued on `stream` exactly as in moe_forward, and the results
+ * are bitwise identical to moe_forward's.  Without a shared expert (or with
+ * side == NULL or side == stream) this is moe_forward.
+ * ws: moe_forward_overlap_workspace_size(p) bytes (the shared expert gets its
+ * own intermediate and split-K buffers).  The call creates two HIP events and
+ * releases them before returning (they are freed once the GPU passes them).
+ * Errors: as moe_forward, plus MOE_ERR_HIP if an event cannot be created.
+ * ------------------------------------------------------------------------ */
+size_t moe_forward_overlap_workspace_size(const moe_problem_t *p);
+moe_status_t moe_forward_overlap(const moe_problem_t *p, const moe_weights_t *w, const void *x, void *y,
+                                 const moe_outputs_t *out, void *ws, size_t ws_bytes, hipStream_t stream,
+                                 hipStream_t side);
+
 #ifdef __cplusplus
 }
 #endif

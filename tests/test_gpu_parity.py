@@ -223,6 +223,34 @@ def test_forward_is_deterministic_small():
         assert torch.equal(o1[k], layer.outputs[k]), k
 
 
+@pytest.mark.parametrize("name", ["dsv3-small", "mixtral-small", "deepseekv3-share-32of256"])
+def test_forward_overlap_matches_forward(name):
+    """moe_forward_overlap (shared expert on a second stream) gives the same
+    bits as moe_forward, on two calls in a row (workspace reuse)."""
+    w = SMALL[name] if name in SMALL else FULL[name]
+    inp, t = _inputs(w)
+    ref_layer = _layer(w, t)
+    ref_layer.alloc_outputs()
+    y_ref = ref_layer.forward(t["x"]).clone()
+    layer = _layer(w, t)
+    layer.alloc_outputs()
+    side = torch.cuda.Stream(device=DEV)
+    for _ in range(2):
+        y = layer.forward(t["x"], side_stream=side)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32),
+                           y_ref.view(torch.int16) if y_ref.dtype == torch.bfloat16 else y_ref.view(torch.int32))
+        rows = int(ref_layer.outputs["seg_offsets"][-1].item())
+        for k in ref_layer.outputs:
+            a, b = layer.outputs[k], ref_layer.outputs[k]
+            if k == "row_src":  # defined for the first `rows` entries only
+                a, b = a[:rows], b[:rows]
+            assert torch.equal(a, b), k
+    if w.shared_expert and name in SMALL:
+        ref = oracle.forward(inp, topk_idx=ref_layer.outputs["topk_idx"].cpu().numpy())
+        assert rel_err(_host(y), ref.y) <= _ytol(w)
+
+
 # ------------------------------------------------------------ edge cases --
 
 def test_zero_tokens():

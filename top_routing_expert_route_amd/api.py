@@ -49,7 +49,8 @@ class Outputs(ctypes.Structure):
 
 EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_error", "moe_max_rows", "moe_route_workspace_size",
            "moe_route", "moe_dispatch_workspace_size", "moe_dispatch", "moe_grouped_gemm_workspace_size",
-           "moe_grouped_gemm", "moe_expert_ffn", "moe_combine", "moe_forward_workspace_size", "moe_forward"]
+           "moe_grouped_gemm", "moe_expert_ffn", "moe_combine", "moe_forward_workspace_size", "moe_forward",
+           "moe_forward_overlap_workspace_size", "moe_forward_overlap"]
 
 _lib = None
 
@@ -86,6 +87,11 @@ def lib():
     L.moe_forward.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Weights), P, P, ctypes.POINTER(Outputs), P,
                               SZ, P]
     L.moe_forward.restype = I
+    L.moe_forward_overlap_workspace_size.argtypes = [ctypes.POINTER(Problem)]
+    L.moe_forward_overlap_workspace_size.restype = SZ
+    L.moe_forward_overlap.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Weights), P, P,
+                                      ctypes.POINTER(Outputs), P, SZ, P, P]
+    L.moe_forward_overlap.restype = I
     _lib = L
     return L
 
@@ -263,14 +269,26 @@ class Layer:
         self.ws = None
         return self.outputs
 
-    def workspace_bytes(self) -> int:
-        return int(lib().moe_forward_workspace_size(ctypes.byref(self.problem)))
+    def workspace_bytes(self, overlap: bool = False) -> int:
+        fn = lib().moe_forward_overlap_workspace_size if overlap else lib().moe_forward_workspace_size
+        return int(fn(ctypes.byref(self.problem)))
 
-    def forward(self, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
-        if self.ws is None:
-            self.ws = _ws(self.workspace_bytes(), self.device)
+    def forward(self, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                side_stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+        """moe_forward on the current stream; with side_stream, moe_forward_overlap
+        (the shared expert runs on side_stream)."""
+        overlap = side_stream is not None
+        if self.ws is None or getattr(self, "_ws_overlap", None) != overlap:
+            self.ws = _ws(self.workspace_bytes(overlap), self.device)
+            self._ws_overlap = overlap
         if y is None:
             y = torch.empty((self.problem.T, self.problem.d), dtype=x.dtype, device=x.device)
-        check(lib().moe_forward(ctypes.byref(self.problem), ctypes.byref(self.weights), _p(x), _p(y),
-                                ctypes.byref(self.out_struct), _p(self.ws), self.ws.numel(), _stream(x.device)))
+        if overlap:
+            check(lib().moe_forward_overlap(ctypes.byref(self.problem), ctypes.byref(self.weights), _p(x), _p(y),
+                                            ctypes.byref(self.out_struct), _p(self.ws), self.ws.numel(),
+                                            _stream(x.device), ctypes.c_void_p(side_stream.cuda_stream)))
+        else:
+            check(lib().moe_forward(ctypes.byref(self.problem), ctypes.byref(self.weights), _p(x), _p(y),
+                                    ctypes.byref(self.out_struct), _p(self.ws), self.ws.numel(),
+                                    _stream(x.device)))
         return y

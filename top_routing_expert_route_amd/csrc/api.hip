@@ -142,11 +142,12 @@ struct ForwardWs {
     int32_t *topk_idx, *expert_count, *seg_offsets, *kept_count, *slot_row, *row_src, *n_dropped;
     float *topk_w, *f, *P, *l_aux;
     void *route_ws, *dispatch_ws, *gemm_ws, *x_perm, *h, *y_perm, *y_sh;
+    void *h_sh, *gemm_ws_sh; // the shared expert's own buffers when it runs on a second stream
     size_t gemm_ws_bytes;
     size_t bytes;
 };
 
-ForwardWs carve_forward(const moe_problem_t *p, const moe_outputs_t *out, void *base)
+ForwardWs carve_forward(const moe_problem_t *p, const moe_outputs_t *out, void *base, bool overlap = false)
 {
     static const moe_outputs_t none = {};
     if (!out)
@@ -177,6 +178,9 @@ ForwardWs carve_forward(const moe_problem_t *p, const moe_outputs_t *out, void *
     w.h = cv.take<char>((size_t)h_rows * p->ffn * es);
     w.y_perm = cv.take<char>((size_t)max_rows * p->d * es);
     w.y_sh = p->has_shared ? cv.take<char>((size_t)p->T * p->d * es) : nullptr;
+    const bool sep = overlap && p->has_shared;
+    w.h_sh = sep ? cv.take<char>((size_t)p->T * p->ffn * es) : w.h;
+    w.gemm_ws_sh = sep ? cv.take<char>(w.gemm_ws_bytes) : w.gemm_ws;
     w.bytes = cv.off;
     return w;
 }
@@ -311,8 +315,10 @@ size_t moe_forward_workspace_size(const moe_problem_t *p)
 
 } // extern "C"
 
-extern "C" moe_status_t moe_forward(const moe_problem_t *p, const moe_weights_t *w, const void *x, void *y,
-                                    const moe_outputs_t *out, void *ws, size_t ws_bytes, hipStream_t stream)
+namespace {
+
+moe_status_t forward_impl(const moe_problem_t *p, const moe_weights_t *w, const void *x, void *y,
+                          const moe_outputs_t *out, void *ws, size_t ws_bytes, hipStream_t stream, hipStream_t side)
 {
     clear_error();
     if (!p || !w)
@@ -344,33 +350,90 @@ extern "C" moe_status_t moe_forward(const moe_problem_t *p, const moe_weights_t 
         return fail(MOE_ERR_INVALID_ARG, "forward: shared expert buffers must be 16-byte aligned");
     if (!aligned16(y))
         return fail(MOE_ERR_INVALID_ARG, "forward: y must be 16-byte aligned");
-    const ForwardWs need = carve_forward(p, out, nullptr);
+    const bool overlap = side != nullptr && side != stream && p->has_shared && p->T > 0;
+    const ForwardWs need = carve_forward(p, out, nullptr, side != nullptr);
     if (moe_status_t s = check_ws(ws, ws_bytes, need.bytes, "forward"))
         return s;
-    const ForwardWs b = carve_forward(p, out, ws);
+    const ForwardWs b = carve_forward(p, out, ws, side != nullptr);
 
-    if (moe_status_t s = launch_route(x, p->dtype, w->w_router, w->b_router, p->T, p->d, p->E, p->k, p->alpha,
-                                      b.topk_idx, b.topk_w, b.expert_count, b.f, b.P, b.l_aux, b.route_ws, stream))
-        return s;
-    if (moe_status_t s = launch_dispatch(x, p->dtype, b.topk_idx, p->T, p->d, p->E, p->k, p->capacity_factor,
-                                         p->expert_begin, E_loc, b.seg_offsets, b.kept_count, b.slot_row, b.row_src,
-                                         b.x_perm, max_rows, b.n_dropped, b.dispatch_ws, stream))
-        return s;
-    if (p->T == 0)
-        return MOE_OK;
-    if (moe_status_t s = launch_grouped_gemm(b.x_perm, b.seg_offsets, E_loc, max_rows, p->ffn, p->d, p->dtype, w->w1,
-                                             w->b1, 1, b.h, b.gemm_ws, b.gemm_ws_bytes, stream))
-        return s;
-    if (moe_status_t s = launch_grouped_gemm(b.h, b.seg_offsets, E_loc, max_rows, p->d, p->ffn, p->dtype, w->w2,
-                                             w->b2, 0, b.y_perm, b.gemm_ws, b.gemm_ws_bytes, stream))
-        return s;
-    if (p->has_shared) {
-        if (moe_status_t s = launch_grouped_gemm(x, nullptr, 1, p->T, p->ffn, p->d, p->dtype, w->ws1, w->bs1, 1, b.h,
-                                                 b.gemm_ws, b.gemm_ws_bytes, stream))
+    // The shared expert needs only x: on the side stream it runs while the
+    // routed path routes, dispatches and runs its own GEMMs.
+    hipEvent_t ev_start = nullptr, ev_done = nullptr;
+    auto release = [&]() {
+        if (ev_start)
+            (void)hipEventDestroy(ev_start);
+        if (ev_done)
+            (void)hipEventDestroy(ev_done);
+    };
+    if (overlap) {
+        if (hipEventCreateWithFlags(&ev_start, hipEventDisableTiming) != hipSuccess ||
+            hipEventCreateWithFlags(&ev_done, hipEventDisableTiming) != hipSuccess) {
+            release();
+            return fail(MOE_ERR_HIP, "forward: cannot create events for the side stream");
+        }
+        if (hipEventRecord(ev_start, stream) != hipSuccess || hipStreamWaitEvent(side, ev_start, 0) != hipSuccess) {
+            release();
+            return fail(MOE_ERR_HIP, "forward: cannot order the side stream after the main stream");
+        }
+        moe_status_t s = launch_grouped_gemm(x, nullptr, 1, p->T, p->ffn, p->d, p->dtype, w->ws1, w->bs1, 1,
+                                             b.h_sh, b.gemm_ws_sh, b.gemm_ws_bytes, side);
+        if (!s)
+            s = launch_grouped_gemm(b.h_sh, nullptr, 1, p->T, p->d, p->ffn, p->dtype, w->ws2, w->bs2, 0, b.y_sh,
+                                    b.gemm_ws_sh, b.gemm_ws_bytes, side);
+        if (!s && hipEventRecord(ev_done, side) != hipSuccess)
+            s = fail(MOE_ERR_HIP, "forward: cannot record the side stream's completion");
+        if (s) {
+            release();
             return s;
-        if (moe_status_t s = launch_grouped_gemm(b.h, nullptr, 1, p->T, p->d, p->ffn, p->dtype, w->ws2, w->bs2, 0,
-                                                 b.y_sh, b.gemm_ws, b.gemm_ws_bytes, stream))
-            return s;
+        }
     }
-    return launch_combine(b.y_perm, max_rows, b.slot_row, b.topk_w, b.y_sh, p->T, p->d, p->k, p->dtype, y, stream);
+    moe_status_t s = launch_route(x, p->dtype, w->w_router, w->b_router, p->T, p->d, p->E, p->k, p->alpha,
+                                  b.topk_idx, b.topk_w, b.expert_count, b.f, b.P, b.l_aux, b.route_ws, stream);
+    if (!s)
+        s = launch_dispatch(x, p->dtype, b.topk_idx, p->T, p->d, p->E, p->k, p->capacity_factor, p->expert_begin,
+                            E_loc, b.seg_offsets, b.kept_count, b.slot_row, b.row_src, b.x_perm, max_rows,
+                            b.n_dropped, b.dispatch_ws, stream);
+    if (!s && p->T > 0) {
+        s = launch_grouped_gemm(b.x_perm, b.seg_offsets, E_loc, max_rows, p->ffn, p->d, p->dtype, w->w1, w->b1, 1,
+                                b.h, b.gemm_ws, b.gemm_ws_bytes, stream);
+        if (!s)
+            s = launch_grouped_gemm(b.h, b.seg_offsets, E_loc, max_rows, p->d, p->ffn, p->dtype, w->w2, w->b2, 0,
+                                    b.y_perm, b.gemm_ws, b.gemm_ws_bytes, stream);
+        if (!s && p->has_shared && !overlap) {
+            s = launch_grouped_gemm(x, nullptr, 1, p->T, p->ffn, p->d, p->dtype, w->ws1, w->bs1, 1, b.h, b.gemm_ws,
+                                    b.gemm_ws_bytes, stream);
+            if (!s)
+                s = launch_grouped_gemm(b.h, nullptr, 1, p->T, p->d, p->ffn, p->dtype, w->ws2, w->bs2, 0, b.y_sh,
+                                        b.gemm_ws, b.gemm_ws_bytes, stream);
+        }
+        if (!s && overlap && hipStreamWaitEvent(stream, ev_done, 0) != hipSuccess)
+            s = fail(MOE_ERR_HIP, "forward: cannot order the combine after the side stream");
+        if (!s)
+            s = launch_combine(b.y_perm, max_rows, b.slot_row, b.topk_w, b.y_sh, p->T, p->d, p->k, p->dtype, y,
+                               stream);
+    }
+    release();
+    return s;
+}
+
+} // namespace
+
+extern "C" moe_status_t moe_forward(const moe_problem_t *p, const moe_weights_t *w, const void *x, void *y,
+                                    const moe_outputs_t *out, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return forward_impl(p, w, x, y, out, ws, ws_bytes, stream, nullptr);
+}
+
+extern "C" size_t moe_forward_overlap_workspace_size(const moe_problem_t *p)
+{
+    if (!p || p->T < 0 || p->E < 1 || p->k < 1 || p->d < 1 || p->ffn < 1 || p->num_local_experts < 0)
+        return 0;
+    return carve_forward(p, nullptr, nullptr, true).bytes;
+}
+
+extern "C" moe_status_t moe_forward_overlap(const moe_problem_t *p, const moe_weights_t *w, const void *x,
+                                            void *y, const moe_outputs_t *out, void *ws, size_t ws_bytes,
+                                            hipStream_t stream, hipStream_t side)
+{
+    return forward_impl(p, w, x, y, out, ws, ws_bytes, stream, side ? side : stream);
 }
