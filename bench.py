@@ -131,7 +131,7 @@ def main():
     dt = torch.bfloat16 if w.dtype == wl.BF16 else torch.float32
     layer = api.Layer(w.T, w.d, w.E, w.k, w.ffn, dt, w.capacity_factor, w.expert_begin, w.num_local_experts,
                       w.alpha, t["w_router"], t["b_router"], t["w1"], t["b1"], t["w2"], t["b2"], t["ws1"],
-                      t["bs1"], t["ws2"], t["bs2"], device=dev)
+                      t["bs1"], t["ws2"], t["bs2"], device=dev, sel_bias=t["sel_bias"])
     outs = layer.alloc_outputs()
     x = t["x"]
     y = torch.empty((w.T, w.d), dtype=dt, device=dev)
@@ -187,7 +187,7 @@ def main():
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] if record else None
         if record:
             ev[0].record(stream)
-        r = api.moe_route(x, t["w_router"], t["b_router"], w.k, w.alpha)
+        r = api.moe_route(x, t["w_router"], t["b_router"], w.k, w.alpha, sel_bias=t["sel_bias"])
         if record:
             ev[1].record(stream)
         dp = api.moe_dispatch(x, r["topk_idx"], w.E, w.capacity_factor, w.expert_begin, w.num_local_experts)

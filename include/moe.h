@@ -85,9 +85,15 @@ int64_t moe_max_rows(int64_t T, int E, int k, float capacity_factor, int num_loc
  * weight of an expert multiplies its output in Y.  Computed here:
  *   logits[t,e] = sum_i x[t,i] * w_router[e,i] + b_router[e]  (fp32 accumulate)
  *   p[t,:]      = softmax(logits[t,:]) over all E experts
- *   topk_idx[t,j], j = 0..k-1: experts by logit descending, ties to the lower id
+ *   topk_idx[t,j], j = 0..k-1: experts by score descending, ties to the lower
+ *                 id; score[t,e] = logits[t,e] (+ sel_bias[e] when given)
  *   topk_w[t,j] = p[t, topk_idx[t,j]]  (full-softmax probability, not
  *                 renormalised over the selected experts)
+ * sel_bias ("Expert Parallelism (EP)", "Key math / How it works", load
+ * balancing: DeepSeek-V3 balances with a bias adjustment instead of the
+ * auxiliary loss) is a per-expert bias on the selection only: the weights,
+ * P and L_aux come from the unbiased softmax.  How the bias is updated
+ * between steps is not part of this call.
  * "Load Balancing: The Auxiliary Loss":
  *   expert_count[e] = number of (t, j) with topk_idx[t,j] = e (before any cap)
  *   f[e] = expert_count[e] / T,  P[e] = (1/T) sum_t p[t,e]
@@ -95,7 +101,8 @@ int64_t moe_max_rows(int64_t T, int E, int k, float capacity_factor, int num_loc
  * The reductions over tokens run in a fixed order: results are bitwise
  * reproducible run to run.
  *
- * x [T,d] (dtype), w_router [E,d] f32, b_router [E] f32 or NULL (zero bias).
+ * x [T,d] (dtype), w_router [E,d] f32, b_router [E] f32 or NULL (zero bias),
+ * sel_bias [E] f32 or NULL (plain top-k).
  * topk_idx [T,k] i32 and topk_w [T,k] f32 are required; expert_count [E],
  * f [E], P [E], l_aux [1] may each be NULL (not written).
  * ws: moe_route_workspace_size(T, d, E) bytes.
@@ -105,7 +112,8 @@ int64_t moe_max_rows(int64_t T, int E, int k, float capacity_factor, int num_loc
  * ------------------------------------------------------------------------ */
 size_t moe_route_workspace_size(int64_t T, int d, int E);
 moe_status_t moe_route(const void *x, moe_dtype_t dtype, const float *w_router,
-                       const float *b_router, int64_t T, int d, int E, int k, float alpha,
+                       const float *b_router, const float *sel_bias, int64_t T, int d, int E, int k,
+                       float alpha,
                        int32_t *topk_idx, float *topk_w, int32_t *expert_count, float *f,
                        float *P, float *l_aux, void *ws, size_t ws_bytes, hipStream_t stream);
 
@@ -244,6 +252,8 @@ typedef struct {
                                            [E_loc,d,ffn], [E_loc,d]|NULL        */
     const void *ws1, *bs1, *ws2, *bs2;  /* shared expert: [ffn,d], [ffn]|NULL,
                                            [d,ffn], [d]|NULL                    */
+    const float *sel_bias;              /* [E] or NULL: selection-only router bias
+                                           (see moe_route)                      */
 } moe_weights_t;
 
 /* Optional outputs; every field may be NULL (then kept in the workspace). */

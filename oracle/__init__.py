@@ -50,7 +50,7 @@ def _load():
         i64 = ctypes.c_int64
         I = ctypes.c_int
         D = ctypes.c_double
-        lib.oracle_route.argtypes = [P, I, P, P, i64, I, I, I, P, P, P, P, I]
+        lib.oracle_route.argtypes = [P, I, P, P, P, i64, I, I, I, P, P, P, P, I]
         lib.oracle_route.restype = I
         lib.oracle_load_stats.argtypes = [P, P, i64, I, I, D, P, P, P, P]
         lib.oracle_load_stats.restype = I
@@ -95,25 +95,34 @@ class Route:
     probs: np.ndarray     # [T, E] float64
     topk_idx: np.ndarray  # [T, k] int32
     topk_w: np.ndarray    # [T, k] float64
+    scores: Optional[np.ndarray] = None  # [T, E] float64: what top-k ranks (logits + sel_bias)
 
 
 def route(x: np.ndarray, w_router: np.ndarray, b_router: Optional[np.ndarray], k: int,
-          threads: Optional[int] = None, want_logits: bool = True) -> Route:
+          threads: Optional[int] = None, want_logits: bool = True,
+          sel_bias: Optional[np.ndarray] = None) -> Route:
+    """Router Linear, softmax, top-k.  ``sel_bias`` (optional, [E] float32)
+    is added to the logits for the top-k choice only."""
     T, d = x.shape
     E = w_router.shape[0]
     x = np.ascontiguousarray(x)
     w_router = np.ascontiguousarray(w_router, dtype=np.float32)
     if b_router is not None:
         b_router = np.ascontiguousarray(b_router, dtype=np.float32)
+    if sel_bias is not None:
+        sel_bias = np.ascontiguousarray(sel_bias, dtype=np.float32)
     logits = np.empty((T, E), np.float64) if want_logits else None
     probs = np.empty((T, E), np.float64)
     idx = np.empty((T, k), np.int32)
     w = np.empty((T, k), np.float64)
-    rc = _load().oracle_route(_ptr(x), _dtype_of(x), _ptr(w_router), _ptr(b_router), T, d, E, k,
-                              _ptr(logits), _ptr(probs), _ptr(idx), _ptr(w), _threads(threads))
+    rc = _load().oracle_route(_ptr(x), _dtype_of(x), _ptr(w_router), _ptr(b_router), _ptr(sel_bias), T, d,
+                              E, k, _ptr(logits), _ptr(probs), _ptr(idx), _ptr(w), _threads(threads))
     if rc != 0:
         raise ValueError("oracle_route: invalid sizes")
-    return Route(logits, probs, idx, w)
+    scores = None
+    if logits is not None:
+        scores = logits if sel_bias is None else logits + sel_bias.astype(np.float64)[None, :]
+    return Route(logits, probs, idx, w, scores)
 
 
 @dataclass
@@ -220,7 +229,7 @@ def forward(inp, tokens: Optional[np.ndarray] = None, threads: Optional[int] = N
     own probabilities at those indices as routing weights.
     """
     w = inp.w
-    r = route(inp.x, inp.w_router, inp.b_router, w.k, threads=threads)
+    r = route(inp.x, inp.w_router, inp.b_router, w.k, threads=threads, sel_bias=getattr(inp, "sel_bias", None))
     idx = r.topk_idx if topk_idx is None else np.ascontiguousarray(topk_idx, dtype=np.int32)
     wts = np.take_along_axis(r.probs, idx.astype(np.int64).clip(0, w.E - 1), axis=1)
     st = load_stats(idx, r.probs, w.alpha)

@@ -110,7 +110,7 @@ static void parallel_for(int64_t n, int nthreads, range_fn fn, void *ctx)
 struct route_ctx {
     const void *x;
     int x_dtype;
-    const float *w_router, *b_router;
+    const float *w_router, *b_router, *sel_bias;
     int d, E, k;
     double *logits, *probs, *topk_w;
     int32_t *topk_idx;
@@ -121,6 +121,7 @@ static void route_range(void *p, int64_t t0, int64_t t1)
     struct route_ctx *c = (struct route_ctx *)p;
     const int d = c->d, E = c->E, k = c->k;
     double *lg = (double *)malloc(sizeof(double) * (size_t)E);
+    double *sc = (double *)malloc(sizeof(double) * (size_t)E);
     char *taken = (char *)malloc((size_t)E);
     for (int64_t t = t0; t < t1; ++t) {
         /* Router Linear d -> E ("MoE Layer Structure"). */
@@ -145,7 +146,14 @@ static void route_range(void *p, int64_t t0, int64_t t1)
             pr[e] = exp(lg[e] - mx) / z;
         if (c->logits)
             memcpy(c->logits + t * E, lg, sizeof(double) * (size_t)E);
-        /* Top-k: repeatedly take the largest remaining logit; scanning ids
+        /* Selection score: the logit, plus the per-expert selection-only
+         * bias when one is given ("Expert Parallelism (EP)", load balancing:
+         * DeepSeek-V3's bias adjustment instead of the auxiliary loss).  The
+         * bias steers which experts are chosen; the weights below stay the
+         * unbiased softmax probabilities. */
+        for (int e = 0; e < E; ++e)
+            sc[e] = c->sel_bias ? lg[e] + (double)c->sel_bias[e] : lg[e];
+        /* Top-k: repeatedly take the largest remaining score; scanning ids
          * upward with a strict comparison keeps the lower id on a tie. */
         memset(taken, 0, (size_t)E);
         for (int j = 0; j < k; ++j) {
@@ -153,7 +161,7 @@ static void route_range(void *p, int64_t t0, int64_t t1)
             for (int e = 0; e < E; ++e) {
                 if (taken[e])
                     continue;
-                if (best < 0 || lg[e] > lg[best])
+                if (best < 0 || sc[e] > sc[best])
                     best = e;
             }
             taken[best] = 1;
@@ -162,20 +170,21 @@ static void route_range(void *p, int64_t t0, int64_t t1)
         }
     }
     free(lg);
+    free(sc);
     free(taken);
 }
 
 /* Route T tokens.  x is [T, d] (float32 or bfloat16 bits per x_dtype),
- * w_router [E, d] float32, b_router [E] float32 or NULL.  Outputs: logits
- * [T, E] (may be NULL), probs [T, E], topk_idx [T, k], topk_w [T, k].
- * Returns 0, or -1 on invalid sizes. */
+ * w_router [E, d] float32, b_router [E] float32 or NULL, sel_bias [E] float32
+ * or NULL (selection-only bias).  Outputs: logits [T, E] (may be NULL), probs
+ * [T, E], topk_idx [T, k], topk_w [T, k].  Returns 0, or -1 on invalid sizes. */
 int oracle_route(const void *x, int x_dtype, const float *w_router, const float *b_router,
-                 int64_t T, int d, int E, int k, double *logits, double *probs,
+                 const float *sel_bias, int64_t T, int d, int E, int k, double *logits, double *probs,
                  int32_t *topk_idx, double *topk_w, int nthreads)
 {
     if (T < 0 || d < 1 || E < 1 || k < 1 || k > E)
         return -1;
-    struct route_ctx c = {x, x_dtype, w_router, b_router, d, E, k, logits, probs, topk_w, topk_idx};
+    struct route_ctx c = {x, x_dtype, w_router, b_router, sel_bias, d, E, k, logits, probs, topk_w, topk_idx};
     parallel_for(T, nthreads, route_range, &c);
     return 0;
 }

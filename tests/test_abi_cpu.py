@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strings(lib):
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     assert lib.moe_status_string(0) == b"ok"
     assert lib.moe_status_string(3) == b"workspace too small"
 
@@ -71,7 +71,7 @@ FAKE = 1 << 20  # a 16-byte aligned non-NULL address that is never dereferenced
 def test_route_rejects_bad_arguments(lib):
     from top_routing_expert_route_amd import api
     P = FAKE
-    call = lambda **kw: lib.moe_route(kw.get("x", P), kw.get("dt", 1), P, None, kw.get("T", 16), kw.get("d", 64),
+    call = lambda **kw: lib.moe_route(kw.get("x", P), kw.get("dt", 1), P, None, None, kw.get("T", 16), kw.get("d", 64),
                                       kw.get("E", 8), kw.get("k", 2), 0.01, P, P, None, None, None, None,
                                       kw.get("ws", P), kw.get("wsb", 1 << 30), None)
     assert call(k=9) == api.MOE_ERR_INVALID_ARG

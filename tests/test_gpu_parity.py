@@ -27,6 +27,11 @@ SMALL = {
                             expert_bias="gauss"),
     "bias-f32": wl.scaled(wl.get(0), name="bias-f32", T=301, d=72, ffn=136, router_bias="gauss",
                           expert_bias="gauss", capacity_factor=1.1),
+    # selection-only router bias: the fused small-E router and the E > 64 path
+    "selbias-e32": wl.scaled(wl.get(1), name="selbias-e32", T=400, d=192, E=32, k=4, ffn=128,
+                             sel_bias="gauss", router_bias="gauss"),
+    "selbias-e128": wl.scaled(wl.get(3), name="selbias-e128", T=300, d=128, ffn=96, sel_bias="gauss",
+                              capacity_factor=1.5),
 }
 
 FULL = {w.name: w for w in wl.WORKLOADS[1:]}
@@ -66,7 +71,7 @@ def _x_f64(inp):
 
 def _run_stages(w, inp, t):
     """Route, dispatch, expert FFN and combine called one by one."""
-    r = api.moe_route(t["x"], t["w_router"], t["b_router"], w.k, w.alpha)
+    r = api.moe_route(t["x"], t["w_router"], t["b_router"], w.k, w.alpha, sel_bias=t["sel_bias"])
     dp = api.moe_dispatch(t["x"], r["topk_idx"], w.E, w.capacity_factor, w.expert_begin, w.num_local_experts)
     h, y_perm = api.moe_expert_ffn(dp["x_perm"], dp["seg_offsets"], t["w1"], t["b1"], t["w2"], t["b2"])
     y_sh = None
@@ -80,7 +85,7 @@ def _run_stages(w, inp, t):
 
 def _check_route(w, inp, r, ref_route):
     gidx = r["topk_idx"].cpu().numpy()
-    nt = check_topk(gidx, ref_route.logits, ref_route.topk_idx, w.k)
+    nt = check_topk(gidx, ref_route.scores, ref_route.topk_idx, w.k)
     # routing weight = oracle probability at the GPU's selection
     ref_w = np.take_along_axis(ref_route.probs, gidx.astype(np.int64), 1)
     assert rel_err(r["topk_w"].cpu().numpy(), ref_w) <= TOL_ROUTER
@@ -136,7 +141,7 @@ def test_stages_small(name):
     w = SMALL[name]
     inp, t = _inputs(w)
     r, dp, y_perm, y_sh, y = _run_stages(w, inp, t)
-    ref_route = oracle.route(inp.x, inp.w_router, inp.b_router, w.k)
+    ref_route = oracle.route(inp.x, inp.w_router, inp.b_router, w.k, sel_bias=inp.sel_bias)
     gidx, nt = _check_route(w, inp, r, ref_route)
     ref_dp = _check_dispatch(w, inp, gidx, dp)
     rows = int(ref_dp.seg_offsets[-1])
@@ -162,7 +167,7 @@ def test_stages_small(name):
 def _layer(w, t, **kw):
     return api.Layer(w.T, w.d, w.E, w.k, w.ffn, _torch_dtype(w), w.capacity_factor, w.expert_begin,
                      w.num_local_experts, w.alpha, t["w_router"], t["b_router"], t["w1"], t["b1"], t["w2"],
-                     t["b2"], t["ws1"], t["bs1"], t["ws2"], t["bs2"], device=DEV, **kw)
+                     t["b2"], t["ws1"], t["bs1"], t["ws2"], t["bs2"], device=DEV, sel_bias=t["sel_bias"], **kw)
 
 
 def _check_forward(w, inp, t, tokens=None):
@@ -170,7 +175,7 @@ def _check_forward(w, inp, t, tokens=None):
     outs = layer.alloc_outputs()
     y = layer.forward(t["x"])
     torch.cuda.synchronize()
-    ref_route = oracle.route(inp.x, inp.w_router, inp.b_router, w.k)
+    ref_route = oracle.route(inp.x, inp.w_router, inp.b_router, w.k, sel_bias=inp.sel_bias)
     gidx, nt = _check_route(w, inp, outs, ref_route)
     ref_dp = oracle.capacity(gidx, w.E, np.float32(w.capacity_factor), w.expert_begin, w.num_local_experts)
     np.testing.assert_array_equal(outs["slot_row"].cpu().numpy(), ref_dp.slot_row)
@@ -179,7 +184,7 @@ def _check_forward(w, inp, t, tokens=None):
     np.testing.assert_array_equal(outs["row_src"].cpu().numpy()[:rows], ref_dp.row_src)
     assert int(outs["n_dropped"].item()) == ref_dp.n_dropped
     if tokens is not None:
-        b, o = near_ties(ref_route.logits, w.k)
+        b, o = near_ties(ref_route.scores, w.k)
         ties = np.flatnonzero(b | o)[:32]
         tokens = wl.token_sample(w.T, tokens, must_include=ties)
     ref = oracle.forward(inp, tokens=tokens, topk_idx=gidx)
@@ -386,6 +391,27 @@ def test_route_bitwise_reproducible_and_stats_fixed_order():
     torch.cuda.synchronize()
     for k in r1:
         assert torch.equal(r1[k], r2[k]), k
+
+
+def test_route_sel_bias_full_size():
+    """The DeepSeek-shaped router (T=32768, d=7168, E=256, top-8, the E > 64
+    path) with a selection-only bias, against the oracle on every token."""
+    w = wl.scaled(wl.get(4), sel_bias="gauss")
+    inp = wl.make_layer(w, seed=0, with_experts=False)
+    x = wl.to_torch(inp.x, DEV)
+    wr = wl.to_torch(inp.w_router, DEV)
+    sb = wl.to_torch(inp.sel_bias, DEV)
+    r = api.moe_route(x, wr, None, w.k, w.alpha, sel_bias=sb)
+    torch.cuda.synchronize()
+    ref = oracle.route(inp.x, inp.w_router, None, w.k, sel_bias=inp.sel_bias)
+    _gidx, nt = _check_route(w, inp, r, ref)
+    plain = api.moe_route(x, wr, None, w.k, w.alpha)
+    torch.cuda.synchronize()
+    changed = (plain["topk_idx"] != r["topk_idx"]).any(dim=1).float().mean().item()
+    assert changed > 0.1, changed  # the bias moved a real share of the selections
+    assert torch.equal(plain["P"], r["P"])  # P is the unbiased mean probability
+    print("sel_bias: near ties boundary %d order %d; %.1f%% of tokens re-routed" %
+          (nt["boundary"], nt["order"], 100 * changed))
 
 
 def test_gelu_epilogue_matches_fp64_erf():

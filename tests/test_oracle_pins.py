@@ -79,6 +79,62 @@ def test_topk_exact_ties_go_to_lower_id():
     assert n_ties > 0
 
 
+# ---- selection-only bias ("Expert Parallelism (EP)", load balancing:
+# DeepSeek-V3's bias adjustment): the bias moves which experts are chosen,
+# the weights stay the unbiased softmax probabilities.
+
+@pytest.mark.parametrize("E,k", [(4, 2), (5, 3), (7, 2)])
+def test_sel_bias_topk_matches_brute_force(E, k):
+    T, d = 40, 6
+    x = _rand((T, d), 30 + E)
+    w = _rand((E, d), 40 + k, 1 / math.sqrt(d))
+    sb = _rand((E,), 50 + E, 0.7)
+    r = oracle.route(x, w, None, k, threads=2, sel_bias=sb)
+    plain = oracle.route(x, w, None, k, threads=2)
+    # logits and probabilities do not see the bias
+    np.testing.assert_array_equal(r.logits, plain.logits)
+    np.testing.assert_array_equal(r.probs, plain.probs)
+    for t in range(T):
+        score = [float(r.logits[t, e]) + float(sb[e]) for e in range(E)]
+        assert list(r.topk_idx[t]) == _brute_topk(score, k)
+    np.testing.assert_array_equal(r.topk_w, np.take_along_axis(plain.probs, r.topk_idx.astype(np.int64), 1))
+    # the bias changed some selections (else this pin pins nothing)
+    assert (r.topk_idx != plain.topk_idx).any()
+
+
+def test_sel_bias_zero_or_constant_changes_nothing():
+    T, d, E, k = 64, 8, 12, 3
+    x = _rand((T, d), 61)
+    w = _rand((E, d), 62, 1 / math.sqrt(d))
+    plain = oracle.route(x, w, None, k)
+    for sb in (np.zeros(E, np.float32), np.full(E, 0.25, np.float32)):
+        r = oracle.route(x, w, None, k, sel_bias=sb)
+        np.testing.assert_array_equal(r.topk_idx, plain.topk_idx)
+        np.testing.assert_array_equal(r.topk_w, plain.topk_w)
+
+
+def test_sel_bias_forces_an_expert_with_its_unbiased_weight():
+    """A bias far above every logit gap puts expert e* first for every token;
+    its weight is still p[t, e*], however small."""
+    T, d, E, k, es = 50, 8, 10, 2, 7
+    x = _rand((T, d), 71)
+    w = _rand((E, d), 72, 1 / math.sqrt(d))
+    sb = np.zeros(E, np.float32)
+    sb[es] = 1000.0
+    r = oracle.route(x, w, None, k, sel_bias=sb)
+    assert (r.topk_idx[:, 0] == es).all()
+    np.testing.assert_array_equal(r.topk_w[:, 0], r.probs[:, es])
+    # the other slot is the token's best remaining expert by logit
+    for t in range(T):
+        l = r.logits[t].copy()
+        l[es] = -np.inf
+        assert r.topk_idx[t, 1] == int(np.argmax(l))
+    st = oracle.load_stats(r.topk_idx, r.probs)
+    assert st.f[es] == 1.0 and abs(st.f.sum() - k) < 1e-12
+    # P is the mean unbiased probability, whatever the selection
+    np.testing.assert_allclose(st.P, r.probs.mean(0), rtol=1e-12)
+
+
 def test_uniform_router_closed_form():
     """W_r = 0, b_r = 0: every logit is 0, so idx = [0..k-1], p = 1/E,
     f_e = 1 for e < k, P_e = 1/E and L_aux = alpha * k / E."""

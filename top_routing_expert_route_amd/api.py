@@ -38,7 +38,7 @@ class Problem(ctypes.Structure):
 
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("w_router", "b_router", "w1", "b1", "w2", "b2", "ws1", "bs1", "ws2", "bs2")]
+                ("w_router", "b_router", "w1", "b1", "w2", "b2", "ws1", "bs1", "ws2", "bs2", "sel_bias")]
 
 
 class Outputs(ctypes.Structure):
@@ -70,7 +70,7 @@ def lib():
     L.moe_last_error.argtypes, L.moe_last_error.restype = [], ctypes.c_char_p
     L.moe_max_rows.argtypes, L.moe_max_rows.restype = [I64, I, I, F, I], I64
     L.moe_route_workspace_size.argtypes, L.moe_route_workspace_size.restype = [I64, I, I], SZ
-    L.moe_route.argtypes = [P, I, P, P, I64, I, I, I, F, P, P, P, P, P, P, P, SZ, P]
+    L.moe_route.argtypes = [P, I, P, P, P, I64, I, I, I, F, P, P, P, P, P, P, P, SZ, P]
     L.moe_route.restype = I
     L.moe_dispatch_workspace_size.argtypes, L.moe_dispatch_workspace_size.restype = [I64, I, I], SZ
     L.moe_dispatch.argtypes = [P, I, P, I64, I, I, I, F, I, I, P, P, P, P, P, I64, P, P, SZ, P]
@@ -134,7 +134,7 @@ def max_rows(T: int, E: int, k: int, capacity_factor: float = 0.0, num_local_exp
 # ----------------------------------------------------------------- steps --
 
 def moe_route(x: torch.Tensor, w_router: torch.Tensor, b_router: Optional[torch.Tensor], k: int,
-              alpha: float = 0.01) -> dict:
+              alpha: float = 0.01, sel_bias: Optional[torch.Tensor] = None) -> dict:
     T, d = x.shape
     E = w_router.shape[0]
     dev = x.device
@@ -146,7 +146,7 @@ def moe_route(x: torch.Tensor, w_router: torch.Tensor, b_router: Optional[torch.
                l_aux=torch.empty(1, dtype=torch.float32, device=dev))
     nb = lib().moe_route_workspace_size(T, d, E)
     ws = _ws(nb, dev)
-    check(lib().moe_route(_p(x), _dt(x), _p(w_router), _p(b_router), T, d, E, k, alpha,
+    check(lib().moe_route(_p(x), _dt(x), _p(w_router), _p(b_router), _p(sel_bias), T, d, E, k, alpha,
                           _p(out["topk_idx"]), _p(out["topk_w"]), _p(out["expert_count"]), _p(out["f"]),
                           _p(out["P"]), _p(out["l_aux"]), _p(ws), nb, _stream(dev)))
     return out
@@ -237,11 +237,11 @@ class Layer:
 
     def __init__(self, T, d, E, k, ffn, dtype, capacity_factor=0.0, expert_begin=0, num_local_experts=0,
                  alpha=0.01, w_router=None, b_router=None, w1=None, b1=None, w2=None, b2=None,
-                 ws1=None, bs1=None, ws2=None, bs2=None, device="cuda"):
+                 ws1=None, bs1=None, ws2=None, bs2=None, device="cuda", sel_bias=None):
         self.problem = Problem(T, d, E, k, ffn, capacity_factor, expert_begin, num_local_experts,
                                1 if ws1 is not None else 0, alpha, MOE_BF16 if dtype == torch.bfloat16 else MOE_F32)
         self.tensors = dict(w_router=w_router, b_router=b_router, w1=w1, b1=b1, w2=w2, b2=b2,
-                            ws1=ws1, bs1=bs1, ws2=ws2, bs2=bs2)
+                            ws1=ws1, bs1=bs1, ws2=ws2, bs2=bs2, sel_bias=sel_bias)
         self.weights = Weights(*[_p(self.tensors[n]) for n, _ in Weights._fields_])
         self.E_loc = num_local_experts if num_local_experts > 0 else E
         self.max_rows = max_rows(T, E, k, capacity_factor, num_local_experts)

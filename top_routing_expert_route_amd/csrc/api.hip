@@ -224,17 +224,18 @@ size_t moe_route_workspace_size(int64_t T, int d, int E)
     return route_ws_bytes(T, d, E);
 }
 
-moe_status_t moe_route(const void *x, moe_dtype_t dtype, const float *w_router, const float *b_router, int64_t T,
-                       int d, int E, int k, float alpha, int32_t *topk_idx, float *topk_w, int32_t *expert_count,
-                       float *f, float *P, float *l_aux, void *ws, size_t ws_bytes, hipStream_t stream)
+moe_status_t moe_route(const void *x, moe_dtype_t dtype, const float *w_router, const float *b_router,
+                       const float *sel_bias, int64_t T, int d, int E, int k, float alpha, int32_t *topk_idx,
+                       float *topk_w, int32_t *expert_count, float *f, float *P, float *l_aux, void *ws,
+                       size_t ws_bytes, hipStream_t stream)
 {
     clear_error();
     if (moe_status_t s = check_route_args(x, dtype, w_router, T, d, E, k, topk_idx, topk_w))
         return s;
     if (moe_status_t s = check_ws(ws, ws_bytes, route_ws_bytes(T, d, E), "route"))
         return s;
-    return launch_route(x, dtype, w_router, b_router, T, d, E, k, alpha, topk_idx, topk_w, expert_count, f, P,
-                        l_aux, ws, stream);
+    return launch_route(x, dtype, w_router, b_router, sel_bias, T, d, E, k, alpha, topk_idx, topk_w, expert_count,
+                        f, P, l_aux, ws, stream);
 }
 
 size_t moe_dispatch_workspace_size(int64_t T, int k, int num_local_experts)
@@ -387,7 +388,8 @@ moe_status_t forward_impl(const moe_problem_t *p, const moe_weights_t *w, const 
             return s;
         }
     }
-    moe_status_t s = launch_route(x, p->dtype, w->w_router, w->b_router, p->T, p->d, p->E, p->k, p->alpha,
+    moe_status_t s = launch_route(x, p->dtype, w->w_router, w->b_router, w->sel_bias, p->T, p->d, p->E, p->k,
+                                  p->alpha,
                                   b.topk_idx, b.topk_w, b.expert_count, b.f, b.P, b.l_aux, b.route_ws, stream);
     if (!s)
         s = launch_dispatch(x, p->dtype, b.topk_idx, p->T, p->d, p->E, p->k, p->capacity_factor, p->expert_begin,

@@ -8,7 +8,7 @@
 
 #include "moe.h"
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 namespace moe {
 
@@ -79,7 +79,8 @@ struct Carver {
 size_t route_ws_bytes(int64_t T, int d, int E);
 size_t gemm_ws_bytes();
 moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, const float *b_router,
-                          int64_t T, int d, int E, int k, float alpha, int32_t *topk_idx, float *topk_w,
+                          const float *sel_bias, int64_t T, int d, int E, int k, float alpha, int32_t *topk_idx,
+                          float *topk_w,
                           int32_t *expert_count, float *f, float *P, float *l_aux, void *ws,
                           hipStream_t stream);
 

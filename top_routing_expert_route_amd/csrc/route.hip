@@ -4,7 +4,10 @@
 // Pages: "Expert Parallelism (MoE)", section "MoE Layer Structure" (router
 // Linear d -> N_experts, top-K experts per token, routing weight in Y) and
 // section "Load Balancing: The Auxiliary Loss" (f_i, P_i, L_aux = alpha *
-// sum f_i P_i).
+// sum f_i P_i).  Optional selection-only bias ("Expert Parallelism (EP)",
+// "Key math / How it works", load balancing: DeepSeek-V3's auxiliary-loss-
+// free bias adjustment): a per-expert bias added to the logits for the top-k
+// choice only; routing weights, P and L_aux use the unbiased softmax.
 //
 // Kernels
 //  route_fused_small  bf16 activations, E <= 64: logits (split-bf16 MFMAs, see
@@ -159,7 +162,8 @@ __global__ __launch_bounds__(256) void route_logits_mfma(const uint16_t *__restr
 template <int ET, int TT, int U, int NW>
 __global__ __launch_bounds__(64 * NW) void route_fused_small(const uint16_t *__restrict__ x,
                                                          const float *__restrict__ wr,
-                                                         const float *__restrict__ bias, int64_t T, int d, int E,
+                                                         const float *__restrict__ bias,
+                                                         const float *__restrict__ sel, int64_t T, int d, int E,
                                                          int k, int32_t *__restrict__ topk_idx,
                                                          float *__restrict__ topk_w, float *__restrict__ part_p,
                                                          int32_t *__restrict__ part_c)
@@ -282,6 +286,7 @@ __global__ __launch_bounds__(64 * NW) void route_fused_small(const uint16_t *__r
         for (int e = 0; e < E; ++e)
             sum += expf(row[e] - m);
         const float inv = 1.0f / sum;
+        // selection score: the logit, plus the selection-only bias if given
         uint64_t taken = 0;
         for (int j = 0; j < k; ++j) {
             int best = -1;
@@ -289,14 +294,15 @@ __global__ __launch_bounds__(64 * NW) void route_fused_small(const uint16_t *__r
             for (int e = 0; e < E; ++e) {
                 if ((taken >> e) & 1ull)
                     continue;
-                if (best < 0 || row[e] > bv) {
+                const float sc = sel ? row[e] + sel[e] : row[e];
+                if (best < 0 || sc > bv) {
                     best = e;
-                    bv = row[e];
+                    bv = sc;
                 }
             }
             taken |= 1ull << best;
             topk_idx[t * k + j] = best;
-            topk_w[t * k + j] = expf(bv - m) * inv;
+            topk_w[t * k + j] = expf(row[best] - m) * inv;
             atomicAdd(&cnt[best], 1);
         }
         for (int e = 0; e < E; ++e)
@@ -379,7 +385,8 @@ __device__ __forceinline__ float wave_sum(float v)
 // sum (mid + lo) + hi is the logit; pieces = 1: plain [T, E] logits.
 template <int EPL>
 __global__ __launch_bounds__(256) void route_select(const float *__restrict__ logits, int pieces,
-                                                    const float *__restrict__ bias, int64_t T, int E, int k,
+                                                    const float *__restrict__ bias, const float *__restrict__ sel,
+                                                    int64_t T, int E, int k,
                                                     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
                                                     float *__restrict__ part_p, int32_t *__restrict__ part_c)
 {
@@ -429,7 +436,14 @@ __global__ __launch_bounds__(256) void route_select(const float *__restrict__ lo
         for (int i = 0; i < EPL; ++i)
             pacc[i] += ex[i] * inv_s;
 
-        // top-k: k rounds of a wave arg-max on (logit desc, id asc)
+        // top-k: k rounds of a wave arg-max on (score desc, id asc); the
+        // score is the logit, plus the selection-only bias if given
+        float sv[EPL];
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            const int e = lane + 64 * i;
+            sv[i] = (sel && e < E) ? l[i] + sel[e] : l[i];
+        }
         uint32_t taken = 0;
         for (int j = 0; j < k; ++j) {
             float bv = -INFINITY;
@@ -437,8 +451,8 @@ __global__ __launch_bounds__(256) void route_select(const float *__restrict__ lo
 #pragma unroll
             for (int i = 0; i < EPL; ++i) {
                 const int e = lane + 64 * i;
-                if (e < E && !((taken >> i) & 1u) && (l[i] > bv || bi == 0x7FFFFFFF))
-                    bv = l[i], bi = e;
+                if (e < E && !((taken >> i) & 1u) && (sv[i] > bv || bi == 0x7FFFFFFF))
+                    bv = sv[i], bi = e;
             }
 #pragma unroll
             for (int o = 32; o > 0; o >>= 1) {
@@ -584,7 +598,8 @@ size_t route_ws_bytes(int64_t T, int d, int E)
 }
 
 moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, const float *b_router,
-                          int64_t T, int d, int E, int k, float alpha, int32_t *topk_idx, float *topk_w,
+                          const float *sel_bias, int64_t T, int d, int E, int k, float alpha, int32_t *topk_idx,
+                          float *topk_w,
                           int32_t *expert_count, float *f, float *P, float *l_aux, void *ws,
                           hipStream_t stream)
 {
@@ -606,13 +621,13 @@ moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, 
             const uint16_t *xb = (const uint16_t *)x;
             const dim3 g((unsigned)nblk);
             if (E <= 16)
-                route_fused_small<1, 1, 8, 8><<<g, 512, 0, stream>>>(xb, w_router, b_router, T, d, E, k, topk_idx,
+                route_fused_small<1, 1, 8, 8><<<g, 512, 0, stream>>>(xb, w_router, b_router, sel_bias, T, d, E, k, topk_idx,
                                                                   topk_w, part_p, part_c);
             else if (E <= 32)
-                route_fused_small<2, 2, 4, 8><<<g, 512, 0, stream>>>(xb, w_router, b_router, T, d, E, k, topk_idx,
+                route_fused_small<2, 2, 4, 8><<<g, 512, 0, stream>>>(xb, w_router, b_router, sel_bias, T, d, E, k, topk_idx,
                                                                   topk_w, part_p, part_c);
             else
-                route_fused_small<4, 2, 2, 8><<<g, 512, 0, stream>>>(xb, w_router, b_router, T, d, E, k, topk_idx,
+                route_fused_small<4, 2, 2, 8><<<g, 512, 0, stream>>>(xb, w_router, b_router, sel_bias, T, d, E, k, topk_idx,
                                                                   topk_w, part_p, part_c);
             if (moe_status_t s = check_launch("route_fused_small"))
                 return s;
@@ -637,14 +652,14 @@ moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, 
             const int epl = (E + 63) / 64;
             const dim3 g((unsigned)nblk);
             switch (epl) {
-            case 1: route_select<1><<<g, 256, 0, stream>>>(logits, pieces, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
-            case 2: route_select<2><<<g, 256, 0, stream>>>(logits, pieces, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+            case 1: route_select<1><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+            case 2: route_select<2><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c); break;
             case 3:
-            case 4: route_select<4><<<g, 256, 0, stream>>>(logits, pieces, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+            case 4: route_select<4><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c); break;
             case 5: case 6: case 7: case 8:
-                route_select<8><<<g, 256, 0, stream>>>(logits, pieces, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+                route_select<8><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c); break;
             default:
-                route_select<16><<<g, 256, 0, stream>>>(logits, pieces, b_router, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+                route_select<16><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c); break;
             }
             if (moe_status_t s = check_launch("route_select"))
                 return s;

@@ -48,6 +48,7 @@ class Workload:
     shared_expert: bool = False    # one non-routed expert run on every token
     router_bias: str = "zero"      # "zero" | "zipf" (b_i = 2 ln(1/(i+1))) | "gauss"
     expert_bias: str = "zero"      # "zero" | "gauss"
+    sel_bias: str = "none"         # "none" | "gauss": selection-only router bias, N(0, 0.3^2)
     alpha: float = 0.01
 
     @property
@@ -148,6 +149,7 @@ class LayerInputs:
     bs1: Optional[np.ndarray] = None
     ws2: Optional[np.ndarray] = None  # [d, ffn]
     bs2: Optional[np.ndarray] = None
+    sel_bias: Optional[np.ndarray] = None  # [E] float32: selection-only router bias
     extra: dict = field(default_factory=dict)
 
 
@@ -162,8 +164,9 @@ def make_layer(w: Workload, seed: int = 0, threads: Optional[int] = None,
     E, E_loc, e0 = w.E, w.E_loc, w.expert_begin
     root = np.random.SeedSequence(seed)
     # slots: 0 x, 1 router W, 2..2+E W1[e], 2+E..2+2E W2[e], 2+2E shared W1,
-    # 3+2E shared W2, 4+2E router bias, 5+2E b1, 6+2E b2, 7+2E shared biases
-    slots = root.spawn(8 + 2 * E)
+    # 3+2E shared W2, 4+2E router bias, 5+2E b1, 6+2E b2, 7+2E shared biases,
+    # 8+2E selection bias
+    slots = root.spawn(9 + 2 * E)
     jobs: list = []
 
     x = np.empty((w.T, w.d), dtype=act_dt)
@@ -223,7 +226,15 @@ def make_layer(w: Workload, seed: int = 0, threads: Optional[int] = None,
             bs1 = f32_to_bf16_bits(s1) if bf else s1
             bs2 = f32_to_bf16_bits(s2) if bf else s2
 
-    return LayerInputs(w, x, w_router, b_router, w1, b1, w2, b2, ws1, bs1, ws2, bs2)
+    if w.sel_bias == "none":
+        sel_bias = None
+    elif w.sel_bias == "gauss":
+        g = np.random.Generator(np.random.PCG64(slots[8 + 2 * E]))
+        sel_bias = g.standard_normal(E, dtype=np.float32) * np.float32(0.3)
+    else:
+        raise ValueError(w.sel_bias)
+
+    return LayerInputs(w, x, w_router, b_router, w1, b1, w2, b2, ws1, bs1, ws2, bs2, sel_bias)
 
 
 def token_sample(T: int, n: int, seed: int = 1234, must_include=()) -> np.ndarray:
@@ -249,5 +260,5 @@ def to_torch(a: Optional[np.ndarray], device=None):
 
 def device_layer(inp: LayerInputs, device="cuda") -> dict:
     """Every tensor of a layer copied to ``device`` (names as in LayerInputs)."""
-    names = ("x", "w_router", "b_router", "w1", "b1", "w2", "b2", "ws1", "bs1", "ws2", "bs2")
+    names = ("x", "w_router", "b_router", "w1", "b1", "w2", "b2", "ws1", "bs1", "ws2", "bs2", "sel_bias")
     return {n: to_torch(getattr(inp, n), device) for n in names}
