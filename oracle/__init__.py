@@ -61,6 +61,12 @@ def _load():
         lib.oracle_combine.restype = I
         lib.oracle_gelu.argtypes = [D]
         lib.oracle_gelu.restype = D
+        lib.oracle_gelu_grad.argtypes = [D]
+        lib.oracle_gelu_grad.restype = D
+        lib.oracle_backward.argtypes = [P, I, i64, I, I, I, I, P, P, P, P, P, P, D, D, I, I,
+                                        P, P, P, P, P, P, P, P, P,
+                                        P, P, P, P, P, P, P, P, P, P, P, P, I]
+        lib.oracle_backward.restype = I
         _lib = lib
     return _lib
 
@@ -240,3 +246,61 @@ def forward(inp, tokens: Optional[np.ndarray] = None, threads: Optional[int] = N
     y = combine(inp.x, tokens, idx, wts, dp.slot_row, inp.w1, inp.b1, inp.w2, inp.b2,
                 w.expert_begin, inp.ws1, inp.bs1, inp.ws2, inp.bs2, threads=threads)
     return Forward(r, st, dp, np.asarray(tokens), y)
+
+
+def gelu_grad(u: float) -> float:
+    return float(_load().oracle_gelu_grad(float(u)))
+
+
+@dataclass
+class Grads:
+    dx: np.ndarray        # [T, d]
+    dW_r: np.ndarray      # [E, d]
+    db_r: np.ndarray      # [E]
+    dW1: np.ndarray       # [E_loc, ffn, d]
+    db1: np.ndarray       # [E_loc, ffn]
+    dW2: np.ndarray       # [E_loc, d, ffn]
+    db2: np.ndarray       # [E_loc, d]
+    dWs1: Optional[np.ndarray]
+    dbs1: Optional[np.ndarray]
+    dWs2: Optional[np.ndarray]
+    dbs2: Optional[np.ndarray]
+    dlogits: np.ndarray   # [T, E]
+
+
+def backward(inp, dY: np.ndarray, g_aux: float = 0.0, threads: Optional[int] = None,
+             topk_idx: Optional[np.ndarray] = None) -> Grads:
+    """Gradients of a scalar loss L through the whole layer, in float64.
+
+    dY = dL/dY [T, d]; g_aux = dL/dL_aux.  The forward is recomputed here
+    (route, statistics, capacity); ``topk_idx`` conditions it on another
+    implementation's selection, as in ``forward``.
+    """
+    w = inp.w
+    T, d, E, k, ffn = w.T, w.d, w.E, w.k, w.ffn
+    r = route(inp.x, inp.w_router, inp.b_router, k, threads=threads, sel_bias=getattr(inp, "sel_bias", None))
+    idx = r.topk_idx if topk_idx is None else np.ascontiguousarray(topk_idx, dtype=np.int32)
+    wts = np.ascontiguousarray(np.take_along_axis(r.probs, idx.astype(np.int64).clip(0, E - 1), axis=1))
+    st = load_stats(idx, r.probs, w.alpha)
+    dp = capacity(idx, E, float(np.float32(w.capacity_factor)), w.expert_begin, w.num_local_experts)
+    E_loc = w.E_loc
+    sh = inp.ws1 is not None
+    g = Grads(dx=np.empty((T, d)), dW_r=np.empty((E, d)), db_r=np.empty(E), dW1=np.empty((E_loc, ffn, d)),
+              db1=np.empty((E_loc, ffn)), dW2=np.empty((E_loc, d, ffn)), db2=np.empty((E_loc, d)),
+              dWs1=np.empty((ffn, d)) if sh else None, dbs1=np.empty(ffn) if sh else None,
+              dWs2=np.empty((d, ffn)) if sh else None, dbs2=np.empty(d) if sh else None,
+              dlogits=np.empty((T, E)))
+    c = lambda a: None if a is None else np.ascontiguousarray(a)
+    dY = np.ascontiguousarray(dY, dtype=np.float64)
+    f = np.ascontiguousarray(st.f, dtype=np.float64)
+    rc = _load().oracle_backward(
+        _ptr(np.ascontiguousarray(inp.x)), _dtype_of(inp.x), T, d, E, k, ffn,
+        _ptr(np.ascontiguousarray(inp.w_router, dtype=np.float32)), _ptr(r.probs), _ptr(idx), _ptr(wts),
+        _ptr(dp.slot_row), _ptr(f), float(w.alpha), float(g_aux), w.expert_begin, E_loc,
+        _ptr(c(inp.w1)), _ptr(c(inp.b1)), _ptr(c(inp.w2)), _ptr(c(inp.b2)),
+        _ptr(c(inp.ws1)), _ptr(c(inp.bs1)), _ptr(c(inp.ws2)), _ptr(c(inp.bs2)), _ptr(dY),
+        _ptr(g.dx), _ptr(g.dW_r), _ptr(g.db_r), _ptr(g.dW1), _ptr(g.db1), _ptr(g.dW2), _ptr(g.db2),
+        _ptr(g.dWs1), _ptr(g.dbs1), _ptr(g.dWs2), _ptr(g.dbs2), _ptr(g.dlogits), _threads(threads))
+    if rc != 0:
+        raise ValueError("oracle_backward: invalid sizes (%d)" % rc)
+    return g

@@ -399,3 +399,236 @@ int oracle_combine(const void *x, int dtype, int64_t T, int d, int k, int ffn,
     parallel_for(n_tokens, nthreads, combine_range, &c);
     return 0;
 }
+
+/* ---------------------------------------------------------------------- */
+/* Backward: gradients of a scalar loss through the layer                   */
+/* ---------------------------------------------------------------------- */
+
+/* d/du GELU(u) = Phi(u) + u * phi(u), with Phi the standard normal CDF and
+ * phi its density. */
+double oracle_gelu_grad(double u)
+{
+    const double pi = 3.14159265358979323846;
+    return 0.5 * (1.0 + erf(u / sqrt(2.0))) + u * exp(-0.5 * u * u) / sqrt(2.0 * pi);
+}
+
+struct bwd_ctx {
+    const void *x;
+    int dtype;
+    int64_t T;
+    int d, E, k, ffn, e0, E_loc;
+    const float *w_router;
+    const double *probs, *topk_w, *f, *dY;
+    const int32_t *topk_idx, *slot_row;
+    const void *w1, *b1, *w2, *b2, *ws1, *bs1, *ws2, *bs2;
+    double g_aux, alpha;
+    double *dx, *dlogits;
+    /* per-part private accumulators, summed in part order afterwards */
+    int nparts;
+    double **acc;
+};
+
+/* sizes of the accumulator block of one part */
+static int64_t bwd_acc_size(const struct bwd_ctx *c, int64_t *off)
+{
+    const int64_t d = c->d, E = c->E, F = c->ffn, L = c->E_loc;
+    int64_t o = 0;
+    off[0] = o; o += E * d;        /* dW_r */
+    off[1] = o; o += E;            /* db_r */
+    off[2] = o; o += L * F * d;    /* dW1  */
+    off[3] = o; o += L * F;        /* db1  */
+    off[4] = o; o += L * d * F;    /* dW2  */
+    off[5] = o; o += L * d;        /* db2  */
+    off[6] = o; o += c->ws1 ? F * d : 0; /* dWs1 */
+    off[7] = o; o += c->ws1 ? F : 0;     /* dbs1 */
+    off[8] = o; o += c->ws1 ? d * F : 0; /* dWs2 */
+    off[9] = o; o += c->ws1 ? d : 0;     /* dbs2 */
+    return o;
+}
+
+/* One FFN (W1 [ffn,d], W2 [d,ffn], nn.Linear layout) seen from the output
+ * side: Y gets weight * v with v = W2 GELU(W1 x + b1) + b2.  Given dv (the
+ * loss gradient at v, already multiplied by the weight), adds dW1, db1, dW2,
+ * db2 and dx; returns v . dYt when dYt is given (the gradient of the weight). */
+static double ffn_backward(const double *xt, int d, int ffn, int dtype, const void *w1, const void *b1,
+                           const void *w2, const void *b2, const double *dv, const double *dYt, double *u,
+                           double *g, double *dg, double *dW1, double *db1, double *dW2, double *db2,
+                           double *dxt)
+{
+    for (int q = 0; q < ffn; ++q) {
+        double s = 0.0;
+        for (int i = 0; i < d; ++i)
+            s += elem(w1, dtype, (int64_t)q * d + i) * xt[i];
+        if (b1)
+            s += elem(b1, dtype, q);
+        u[q] = s;
+        g[q] = oracle_gelu(s);
+    }
+    double dw = 0.0;
+    if (dYt) {
+        for (int o = 0; o < d; ++o) {
+            double v = 0.0;
+            for (int q = 0; q < ffn; ++q)
+                v += elem(w2, dtype, (int64_t)o * ffn + q) * g[q];
+            if (b2)
+                v += elem(b2, dtype, o);
+            dw += dYt[o] * v;
+        }
+    }
+    /* second Linear: dW2 += dv g^T, db2 += dv, dg = W2^T dv */
+    for (int q = 0; q < ffn; ++q)
+        dg[q] = 0.0;
+    for (int o = 0; o < d; ++o) {
+        for (int q = 0; q < ffn; ++q) {
+            dW2[(int64_t)o * ffn + q] += dv[o] * g[q];
+            dg[q] += elem(w2, dtype, (int64_t)o * ffn + q) * dv[o];
+        }
+        db2[o] += dv[o];
+    }
+    /* GELU, then the first Linear: du = dg GELU'(u); dW1 += du x^T, db1 += du,
+     * dx += W1^T du */
+    for (int q = 0; q < ffn; ++q) {
+        const double du = dg[q] * oracle_gelu_grad(u[q]);
+        for (int i = 0; i < d; ++i) {
+            dW1[(int64_t)q * d + i] += du * xt[i];
+            dxt[i] += elem(w1, dtype, (int64_t)q * d + i) * du;
+        }
+        db1[q] += du;
+    }
+    return dw;
+}
+
+static void bwd_range(void *p, int64_t t0, int64_t t1)
+{
+    struct bwd_ctx *c = (struct bwd_ctx *)p;
+    const int d = c->d, E = c->E, k = c->k, ffn = c->ffn;
+    int64_t off[10];
+    bwd_acc_size(c, off);
+    /* the part this range belongs to (parallel_for hands out [T p / n,
+     * T (p+1) / n) to part p) */
+    int part = 0;
+    for (int q = 0; q < c->nparts; ++q)
+        if (c->T * q / c->nparts == t0)
+            part = q;
+    double *A = c->acc[part];
+    double *xt = (double *)malloc(sizeof(double) * (size_t)d);
+    double *dxt = (double *)malloc(sizeof(double) * (size_t)d);
+    double *dv = (double *)malloc(sizeof(double) * (size_t)d);
+    double *u = (double *)malloc(sizeof(double) * (size_t)ffn);
+    double *g = (double *)malloc(sizeof(double) * (size_t)ffn);
+    double *dg = (double *)malloc(sizeof(double) * (size_t)ffn);
+    double *dp = (double *)malloc(sizeof(double) * (size_t)E);
+    const size_t es = c->dtype == ORACLE_DT_BF16 ? 2 : 4;
+    for (int64_t t = t0; t < t1; ++t) {
+        const double *dYt = c->dY + t * d;
+        const double *pt = c->probs + t * E;
+        for (int i = 0; i < d; ++i) {
+            xt[i] = elem(c->x, c->dtype, t * d + i);
+            dxt[i] = 0.0;
+        }
+        /* L_aux = alpha sum_e f_e P_e with P_e = mean_t p[t,e]; f counts the
+         * selections and has no gradient ("Load Balancing: The Auxiliary
+         * Loss"), so dL/dp[t,e] = g_aux alpha f_e / T. */
+        for (int e = 0; e < E; ++e)
+            dp[e] = c->g_aux * c->alpha * c->f[e] / (double)c->T;
+        /* Kept selections: Y_t += w v with w = p[t, e] ("MoE Layer
+         * Structure"); dropped and remote selections are not in Y. */
+        for (int j = 0; j < k; ++j) {
+            const int64_t s = t * k + j;
+            if (c->slot_row[s] < 0)
+                continue;
+            const int e = c->topk_idx[s], le = e - c->e0;
+            const double w = c->topk_w[s];
+            for (int o = 0; o < d; ++o)
+                dv[o] = w * dYt[o];
+            const int64_t w1o = (int64_t)le * ffn * d, b1o = (int64_t)le * ffn;
+            const int64_t w2o = (int64_t)le * d * ffn, b2o = (int64_t)le * d;
+            const double dw = ffn_backward(
+                xt, d, ffn, c->dtype, (const char *)c->w1 + w1o * es, c->b1 ? (const char *)c->b1 + b1o * es : NULL,
+                (const char *)c->w2 + w2o * es, c->b2 ? (const char *)c->b2 + b2o * es : NULL, dv, dYt, u, g, dg,
+                A + off[2] + w1o, A + off[3] + b1o, A + off[4] + w2o, A + off[5] + b2o, dxt);
+            dp[e] += dw;
+        }
+        /* Router: w = softmax(logits)[e]; dl_i = p_i (dp_i - sum_e p_e dp_e). */
+        double sdot = 0.0;
+        for (int e = 0; e < E; ++e)
+            sdot += pt[e] * dp[e];
+        for (int e = 0; e < E; ++e) {
+            const double dl = pt[e] * (dp[e] - sdot);
+            if (c->dlogits)
+                c->dlogits[t * E + e] = dl;
+            A[off[1] + e] += dl;
+            for (int i = 0; i < d; ++i) {
+                A[off[0] + (int64_t)e * d + i] += dl * xt[i];
+                dxt[i] += (double)c->w_router[(int64_t)e * d + i] * dl;
+            }
+        }
+        /* Shared expert: weight 1 on every token. */
+        if (c->ws1)
+            ffn_backward(xt, d, ffn, c->dtype, c->ws1, c->bs1, c->ws2, c->bs2, dYt, NULL, u, g, dg, A + off[6],
+                         A + off[7], A + off[8], A + off[9], dxt);
+        for (int i = 0; i < d; ++i)
+            c->dx[t * d + i] = dxt[i];
+    }
+    free(xt);
+    free(dxt);
+    free(dv);
+    free(u);
+    free(g);
+    free(dg);
+    free(dp);
+}
+
+/* Gradients of a scalar loss with dL/dY = dY [T, d] (float64) and
+ * dL/dL_aux = g_aux, through the layer whose forward made topk_idx,
+ * topk_w (= probs at the selection), slot_row (oracle_capacity) and f.
+ * probs [T, E] are the router's softmax probabilities.  Selection (top-k,
+ * capacity) is piecewise constant and has no gradient.  Outputs (float64,
+ * all required except the shared-expert ones when ws1 is NULL and dlogits):
+ * dx [T,d], dW_r [E,d], db_r [E], dW1 [E_loc,ffn,d], db1 [E_loc,ffn],
+ * dW2 [E_loc,d,ffn], db2 [E_loc,d], dWs1 [ffn,d], dbs1 [ffn], dWs2 [d,ffn],
+ * dbs2 [d], dlogits [T,E]. */
+int oracle_backward(const void *x, int dtype, int64_t T, int d, int E, int k, int ffn, const float *w_router,
+                    const double *probs, const int32_t *topk_idx, const double *topk_w, const int32_t *slot_row,
+                    const double *f, double alpha, double g_aux, int e0, int E_loc, const void *w1, const void *b1,
+                    const void *w2, const void *b2, const void *ws1, const void *bs1, const void *ws2,
+                    const void *bs2, const double *dY, double *dx, double *dW_r, double *db_r, double *dW1,
+                    double *db1, double *dW2, double *db2, double *dWs1, double *dbs1, double *dWs2, double *dbs2,
+                    double *dlogits, int nthreads)
+{
+    if (T < 1 || d < 1 || E < 1 || k < 1 || ffn < 1 || e0 < 0 || E_loc < 1 || e0 + E_loc > E)
+        return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > T)
+        nthreads = (int)T;
+    struct bwd_ctx c = {x, dtype, T, d, E, k, ffn, e0, E_loc, w_router, probs, topk_w, f, dY, topk_idx, slot_row,
+                        w1, b1, w2, b2, ws1, bs1, ws2, bs2, g_aux, alpha, dx, dlogits, nthreads, NULL};
+    int64_t off[10];
+    const int64_t n = bwd_acc_size(&c, off);
+    c.acc = (double **)malloc(sizeof(double *) * (size_t)nthreads);
+    for (int p = 0; p < nthreads; ++p) {
+        c.acc[p] = (double *)calloc((size_t)n, sizeof(double));
+        if (!c.acc[p])
+            return -2;
+    }
+    /* one contiguous token range per part, so each accumulator is private */
+    parallel_for(T, nthreads, bwd_range, &c);
+    /* fixed-order sum of the parts */
+    double *outs[10] = {dW_r, db_r, dW1, db1, dW2, db2, dWs1, dbs1, dWs2, dbs2};
+    for (int q = 0; q < 10; ++q) {
+        const int64_t len = (q < 9 ? off[q + 1] : n) - off[q];
+        if (!outs[q] || len == 0)
+            continue;
+        for (int64_t i = 0; i < len; ++i) {
+            double s = 0.0;
+            for (int p = 0; p < nthreads; ++p)
+                s += c.acc[p][off[q] + i];
+            outs[q][i] = s;
+        }
+    }
+    for (int p = 0; p < nthreads; ++p)
+        free(c.acc[p]);
+    free(c.acc);
+    return 0;
+}

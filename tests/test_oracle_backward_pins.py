@@ -1,0 +1,96 @@
+"""Pins of the oracle's backward pass.
+
+The analytic gradients (``oracle.backward``) are checked against central
+finite differences of the oracle's own forward pass (route, statistics,
+capacity and combine), on tiny float32 layers where every parameter element
+can be perturbed, plus the closed form of the auxiliary-loss-only gradient.
+Selection (top-k, capacity) is piecewise constant: an element whose
+perturbation changes a selection is skipped and counted.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from top_routing_expert_route_amd import workloads as wl
+
+
+def _loss(inp, R, g_aux):
+    fw = oracle.forward(inp, threads=1)
+    return float((R * fw.y).sum() + g_aux * fw.stats.l_aux), fw.route.topk_idx, fw.dispatch.slot_row
+
+
+PARAMS = ["x", "w_router", "b_router", "w1", "b1", "w2", "b2", "ws1", "bs1", "ws2", "bs2"]
+GRAD = {"x": "dx", "w_router": "dW_r", "b_router": "db_r", "w1": "dW1", "b1": "db1", "w2": "dW2",
+        "b2": "db2", "ws1": "dWs1", "bs1": "dbs1", "ws2": "dWs2", "bs2": "dbs2"}
+
+
+@pytest.mark.parametrize("case", ["plain", "shared-capacity", "selbias"])
+def test_backward_matches_finite_differences(case):
+    kw = dict(T=6, d=5, E=4, k=2, ffn=7, expert_bias="gauss", router_bias="gauss")
+    if case == "shared-capacity":
+        kw.update(shared_expert=True, capacity_factor=1.0, E=5, T=8)
+    if case == "selbias":
+        kw.update(sel_bias="gauss", E=6, k=3)
+    w = wl.scaled(wl.get(0), name="fd-" + case, **kw)
+    inp = wl.make_layer(w, seed=11)
+    rng = np.random.default_rng(5)
+    R = rng.standard_normal((w.T, w.d))
+    g_aux = 0.75
+    g = oracle.backward(inp, R, g_aux, threads=1)
+    L0, idx0, sr0 = _loss(inp, R, g_aux)
+    if case == "shared-capacity":
+        assert (sr0 == -1).any(), "the capacity case should drop some selections"
+    checked = skipped = 0
+    for name in PARAMS:
+        arr = getattr(inp, name)
+        if arr is None:
+            continue
+        ga = getattr(g, GRAD[name])
+        flat = arr.reshape(-1)
+        for i in range(flat.size):
+            v = float(flat[i])
+            h = 1e-3 * max(1.0, abs(v))
+            vp, vm = np.float32(v + h), np.float32(v - h)
+            flat[i] = vp
+            Lp, ip, sp = _loss(inp, R, g_aux)
+            flat[i] = vm
+            Lm, im, sm = _loss(inp, R, g_aux)
+            flat[i] = np.float32(v)
+            if not (np.array_equal(ip, idx0) and np.array_equal(im, idx0) and np.array_equal(sp, sr0)
+                    and np.array_equal(sm, sr0)):
+                skipped += 1
+                continue
+            fd = (Lp - Lm) / (float(vp) - float(vm))
+            an = float(ga.reshape(-1)[i])
+            assert abs(fd - an) <= 1e-5 + 1e-4 * abs(an), (name, i, fd, an)
+            checked += 1
+    assert checked > 10 * skipped, (checked, skipped)
+
+
+def test_aux_only_gradient_closed_form():
+    """dY = 0: only L_aux = alpha sum f_e P_e carries gradient, through P:
+    dlogits[t] = p_t * (a - p_t . a) with a_e = g_aux alpha f_e / T, and
+    dW_r = dlogits^T x, db_r = column sums, dx = dlogits W_r; the experts get
+    nothing."""
+    w = wl.scaled(wl.get(0), name="aux-only", T=40, d=12, E=6, k=2, ffn=9, router_bias="gauss")
+    inp = wl.make_layer(w, seed=4)
+    g_aux = 2.5
+    g = oracle.backward(inp, np.zeros((w.T, w.d)), g_aux)
+    r = oracle.route(inp.x, inp.w_router, inp.b_router, w.k)
+    st = oracle.load_stats(r.topk_idx, r.probs, w.alpha)
+    a = g_aux * w.alpha * st.f / w.T
+    dl = r.probs * (a[None, :] - (r.probs * a[None, :]).sum(1, keepdims=True))
+    np.testing.assert_allclose(g.dlogits, dl, rtol=1e-12, atol=1e-18)
+    x = inp.x.astype(np.float64)
+    np.testing.assert_allclose(g.dW_r, dl.T @ x, rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(g.db_r, dl.sum(0), rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(g.dx, dl @ inp.w_router.astype(np.float64), rtol=1e-10, atol=1e-15)
+    for a_ in (g.dW1, g.db1, g.dW2, g.db2):
+        assert not a_.any()
+
+
+def test_gelu_grad_matches_difference_quotient():
+    for u in (-6.0, -2.5, -0.7, 0.0, 0.3, 1.0, 2.2, 7.5):
+        h = 1e-5
+        fd = (oracle.gelu(u + h) - oracle.gelu(u - h)) / (2 * h)
+        assert abs(fd - oracle.gelu_grad(u)) < 1e-9
