@@ -295,6 +295,51 @@ moe_status_t moe_forward_overlap(const moe_problem_t *p, const moe_weights_t *w,
                                  const moe_outputs_t *out, void *ws, size_t ws_bytes, hipStream_t stream,
                                  hipStream_t side);
 
+/* ------------------------------------------------------------------------ *
+ * moe_backward - gradients of a scalar loss L through the layer of moe_forward.
+ *
+ * "Load Balancing: The Auxiliary Loss": L_aux = alpha * sum_i f_i * P_i is
+ * added to the task loss and backpropagated; f_i counts selections and has no
+ * gradient, P_i is the mean router probability of expert i.  "MoE Layer
+ * Structure": Y is the routing-weighted sum of the expert outputs, the
+ * routing weight being the softmax probability of the selected expert.  Top-k
+ * selection (with or without sel_bias) and capacity dropping are piecewise
+ * constant: no gradient flows through them.
+ *
+ * Inputs: the layer (p, w, x) exactly as given to moe_forward, dy = dL/dY
+ * [T,d] in the layer's dtype, g_aux = dL/dL_aux.  Routing, dispatch and the
+ * first Linear are recomputed on the device with the forward's kernels, so the
+ * selections and drops are those of moe_forward.
+ * Outputs (float32, caller-owned, overwritten; grads->... NULL where allowed):
+ *   dx [T,d] (may be NULL when T = 0), dw_router [E,d], dw1 [E_loc,ffn,d],
+ *   dw2 [E_loc,d,ffn] required;
+ *   dws1 [ffn,d], dws2 [d,ffn] required with a shared expert;
+ *   db_router [E], db1 [E_loc,ffn], db2 [E_loc,d], dbs1 [ffn], dbs2 [d] and
+ *   dlogits [T,E] (dL/d router logits) optional.
+ * With a local share (num_local_experts < E) the routed terms cover this
+ * GPU's experts only: dL/dp takes the dw of the local kept selections, plus
+ * the auxiliary-loss term g_aux * alpha * f_e / T for every e.
+ * Arithmetic: expert GEMMs on the layer's dtype with fp32 accumulation (bf16
+ * operands for MOE_BF16: the GELU-backward output and the hidden activation
+ * are rounded to bf16 before their GEMMs); router, softmax and every
+ * reduction in fp32.  Results are bitwise reproducible run to run.
+ * Sizes: as moe_forward; MOE_BF16 also needs d and ffn multiples of 64 and at
+ * least 128 (else MOE_ERR_UNSUPPORTED).
+ * ws: moe_backward_workspace_size(p) bytes.
+ * Errors: as moe_forward.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    float *dx;                       /* [T,d]                                  */
+    float *dw_router, *db_router;    /* [E,d], [E]                             */
+    float *dw1, *db1, *dw2, *db2;    /* [E_loc,ffn,d], [E_loc,ffn], [E_loc,d,ffn], [E_loc,d] */
+    float *dws1, *dbs1, *dws2, *dbs2; /* [ffn,d], [ffn], [d,ffn], [d]          */
+    float *dlogits;                  /* [T,E]                                  */
+} moe_grads_t;
+
+size_t moe_backward_workspace_size(const moe_problem_t *p);
+moe_status_t moe_backward(const moe_problem_t *p, const moe_weights_t *w, const void *x, const void *dy,
+                          float g_aux, const moe_grads_t *grads, void *ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

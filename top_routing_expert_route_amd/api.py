@@ -41,6 +41,12 @@ class Weights(ctypes.Structure):
                 ("w_router", "b_router", "w1", "b1", "w2", "b2", "ws1", "bs1", "ws2", "bs2", "sel_bias")]
 
 
+class Grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("dx", "dw_router", "db_router", "dw1", "db1", "dw2", "db2", "dws1", "dbs1", "dws2", "dbs2",
+                 "dlogits")]
+
+
 class Outputs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("topk_idx", "topk_w", "expert_count", "f", "P", "l_aux", "seg_offsets", "kept_count",
@@ -50,7 +56,8 @@ class Outputs(ctypes.Structure):
 EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_error", "moe_max_rows", "moe_route_workspace_size",
            "moe_route", "moe_dispatch_workspace_size", "moe_dispatch", "moe_grouped_gemm_workspace_size",
            "moe_grouped_gemm", "moe_expert_ffn", "moe_combine", "moe_forward_workspace_size", "moe_forward",
-           "moe_forward_overlap_workspace_size", "moe_forward_overlap"]
+           "moe_forward_overlap_workspace_size", "moe_forward_overlap", "moe_backward_workspace_size",
+           "moe_backward"]
 
 _lib = None
 
@@ -92,6 +99,11 @@ def lib():
     L.moe_forward_overlap.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Weights), P, P,
                                       ctypes.POINTER(Outputs), P, SZ, P, P]
     L.moe_forward_overlap.restype = I
+    L.moe_backward_workspace_size.argtypes = [ctypes.POINTER(Problem)]
+    L.moe_backward_workspace_size.restype = SZ
+    L.moe_backward.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Weights), P, P, F, ctypes.POINTER(Grads), P,
+                               SZ, P]
+    L.moe_backward.restype = I
     _lib = L
     return L
 
@@ -292,3 +304,35 @@ class Layer:
                                     ctypes.byref(self.out_struct), _p(self.ws), self.ws.numel(),
                                     _stream(x.device)))
         return y
+
+    def backward_workspace_bytes(self) -> int:
+        return int(lib().moe_backward_workspace_size(ctypes.byref(self.problem)))
+
+    def backward(self, x: torch.Tensor, dy: torch.Tensor, g_aux: float = 0.0, bias_grads: bool = True,
+                 dlogits: bool = False, grads: Optional[dict] = None) -> dict:
+        """moe_backward on the current stream: float32 gradients of a loss with
+        dL/dY = dy and dL/dL_aux = g_aux.  Returns (or fills) a dict with dx,
+        dw_router, dw1, dw2 (dws1, dws2 with a shared expert), the bias
+        gradients when bias_grads, and dlogits when asked for."""
+        p, dev = self.problem, self.device
+        if grads is None:
+            f32 = dict(dtype=torch.float32, device=dev)
+            E_loc, T, d, E, F = self.E_loc, p.T, p.d, p.E, p.ffn
+            grads = dict(dx=torch.empty((T, d), **f32), dw_router=torch.empty((E, d), **f32),
+                         dw1=torch.empty((E_loc, F, d), **f32), dw2=torch.empty((E_loc, d, F), **f32))
+            if bias_grads:
+                grads.update(db_router=torch.empty(E, **f32), db1=torch.empty((E_loc, F), **f32),
+                             db2=torch.empty((E_loc, d), **f32))
+            if p.has_shared:
+                grads.update(dws1=torch.empty((F, d), **f32), dws2=torch.empty((d, F), **f32))
+                if bias_grads:
+                    grads.update(dbs1=torch.empty(F, **f32), dbs2=torch.empty(d, **f32))
+            if dlogits:
+                grads["dlogits"] = torch.empty((T, E), **f32)
+        gs = Grads(*[_p(grads.get(n)) for n, _ in Grads._fields_])
+        nb = self.backward_workspace_bytes()
+        if getattr(self, "_bws", None) is None or self._bws.numel() < nb:
+            self._bws = _ws(nb, dev)
+        check(lib().moe_backward(ctypes.byref(self.problem), ctypes.byref(self.weights), _p(x), _p(dy),
+                                 float(g_aux), ctypes.byref(gs), _p(self._bws), self._bws.numel(), _stream(x.device)))
+        return grads

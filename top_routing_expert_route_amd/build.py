@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_hip.so")
-SOURCES = ["api.hip", "route.hip", "dispatch.hip", "gemm.hip", "combine.hip"]
+SOURCES = ["api.hip", "route.hip", "dispatch.hip", "gemm.hip", "combine.hip", "backward.hip"]
 ARCH = "gfx950"
 
 

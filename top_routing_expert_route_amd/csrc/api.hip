@@ -235,7 +235,7 @@ moe_status_t moe_route(const void *x, moe_dtype_t dtype, const float *w_router, 
     if (moe_status_t s = check_ws(ws, ws_bytes, route_ws_bytes(T, d, E), "route"))
         return s;
     return launch_route(x, dtype, w_router, b_router, sel_bias, T, d, E, k, alpha, topk_idx, topk_w, expert_count,
-                        f, P, l_aux, ws, stream);
+                        f, P, l_aux, nullptr, ws, stream);
 }
 
 size_t moe_dispatch_workspace_size(int64_t T, int k, int num_local_experts)
@@ -390,7 +390,8 @@ moe_status_t forward_impl(const moe_problem_t *p, const moe_weights_t *w, const 
     }
     moe_status_t s = launch_route(x, p->dtype, w->w_router, w->b_router, w->sel_bias, p->T, p->d, p->E, p->k,
                                   p->alpha,
-                                  b.topk_idx, b.topk_w, b.expert_count, b.f, b.P, b.l_aux, b.route_ws, stream);
+                                  b.topk_idx, b.topk_w, b.expert_count, b.f, b.P, b.l_aux, nullptr, b.route_ws,
+                                  stream);
     if (!s)
         s = launch_dispatch(x, p->dtype, b.topk_idx, p->T, p->d, p->E, p->k, p->capacity_factor, p->expert_begin,
                             E_loc, b.seg_offsets, b.kept_count, b.slot_row, b.row_src, b.x_perm, max_rows,
@@ -438,4 +439,243 @@ extern "C" moe_status_t moe_forward_overlap(const moe_problem_t *p, const moe_we
                                             hipStream_t stream, hipStream_t side)
 {
     return forward_impl(p, w, x, y, out, ws, ws_bytes, stream, side ? side : stream);
+}
+
+// ------------------------------------------------------------------ backward
+namespace {
+
+// Workspace of moe_backward.  The shared expert runs first and leaves only
+// dx_sh; the routed experts then reuse its buffers (rows = max(routed rows,
+// T), transposed weights for max(E_loc, 1) experts).
+struct BackwardWs {
+    int32_t *topk_idx, *expert_count, *seg_offsets, *kept_count, *slot_row, *row_src, *kcol;
+    float *topk_w, *f, *P, *l_aux, *probs, *dl;
+    void *route_ws, *dispatch_ws, *gemm_ws, *router_ws;
+    size_t gemm_ws_bytes;
+    void *x_perm, *dyp, *du, *w1t, *w2t, *xT, *dyT, *duT, *gwT;
+    float *u, *dh, *dx_rows, *dx_sh, *dwpart, *colpart;
+    int64_t Kp;
+    size_t bytes;
+};
+
+BackwardWs carve_backward(const moe_problem_t *p, const moe_grads_t *g, void *base)
+{
+    const int E_loc = local_count(p->E, p->num_local_experts);
+    const int64_t max_rows = moe_max_rows(p->T, p->E, p->k, p->capacity_factor, p->num_local_experts);
+    const int64_t rows = p->has_shared && p->T > max_rows ? p->T : max_rows;
+    const size_t es = elem_size(p->dtype);
+    const int64_t Tk = p->T * p->k;
+    const int64_t kp_r = kseg_cols_bound(max_rows, E_loc), kp_s = p->has_shared ? kseg_cols_bound(p->T, 1) : 0;
+    Carver cv{(char *)base, 0};
+    BackwardWs w;
+    w.Kp = kp_r > kp_s ? kp_r : kp_s;
+    w.topk_idx = cv.take<int32_t>((size_t)Tk);
+    w.topk_w = cv.take<float>((size_t)Tk);
+    w.expert_count = cv.take<int32_t>((size_t)p->E);
+    w.f = cv.take<float>((size_t)p->E);
+    w.P = cv.take<float>((size_t)p->E);
+    w.l_aux = cv.take<float>(1);
+    w.probs = cv.take<float>((size_t)p->T * p->E);
+    w.dl = (g && g->dlogits) ? g->dlogits : cv.take<float>((size_t)p->T * p->E);
+    w.route_ws = cv.take<char>(route_ws_bytes(p->T, p->d, p->E));
+    w.seg_offsets = cv.take<int32_t>((size_t)E_loc + 1);
+    w.kept_count = cv.take<int32_t>((size_t)E_loc);
+    w.slot_row = cv.take<int32_t>((size_t)Tk);
+    w.row_src = cv.take<int32_t>((size_t)max_rows);
+    w.kcol = cv.take<int32_t>((size_t)E_loc + 1);
+    w.dispatch_ws = cv.take<char>(dispatch_ws_bytes(p->T, p->k, E_loc));
+    w.gemm_ws_bytes = p->dtype == MOE_BF16 ? gemm_ws_bytes() : 0;
+    w.gemm_ws = cv.take<char>(w.gemm_ws_bytes);
+    w.router_ws = cv.take<char>(router_wgrad_ws_bytes(p->T, p->d, p->E));
+    w.x_perm = cv.take<char>((size_t)max_rows * p->d * es);
+    w.dyp = cv.take<char>((size_t)max_rows * p->d * es);
+    w.du = cv.take<char>((size_t)rows * p->ffn * es);
+    w.w1t = cv.take<char>((size_t)E_loc * p->ffn * p->d * es);
+    w.w2t = cv.take<char>((size_t)E_loc * p->ffn * p->d * es);
+    w.xT = cv.take<char>((size_t)p->d * w.Kp * es);
+    w.dyT = cv.take<char>((size_t)p->d * w.Kp * es);
+    w.duT = cv.take<char>((size_t)p->ffn * w.Kp * es);
+    w.gwT = cv.take<char>((size_t)p->ffn * w.Kp * es);
+    w.u = cv.take<float>((size_t)rows * p->ffn);
+    w.dh = cv.take<float>((size_t)rows * p->ffn);
+    w.dx_rows = cv.take<float>((size_t)rows * p->d);
+    w.dx_sh = p->has_shared ? cv.take<float>((size_t)p->T * p->d) : nullptr;
+    w.dwpart = cv.take<float>((size_t)max_rows * ((p->ffn + 63) / 64));
+    const int64_t maxdim = p->d > p->ffn ? p->d : p->ffn;
+    w.colpart = cv.take<float>((size_t)(w.Kp / 64) * maxdim);
+    w.bytes = cv.off;
+    return w;
+}
+
+// One FFN's backward (the routed experts over their dispatched rows, or the
+// shared expert over all tokens with seg = row_src = wgt = NULL).
+struct FfnBwd {
+    const void *a_rows;            // rows of the first Linear's input: x_perm, or x
+    const void *dy_rows;           // NULL: gather dy rows into b.dyp
+    const int32_t *seg, *row_src;
+    int S;
+    int64_t rows;
+    const float *wgt;              // routing weights by slot, or NULL (= 1)
+    const void *w1, *b1, *w2;
+    float *dw1, *db1, *dw2, *db2, *dx_rows, *dwpart;
+};
+
+moe_status_t ffn_backward(const moe_problem_t *p, const void *x, const void *dy, const FfnBwd &a,
+                          const BackwardWs &b, hipStream_t st)
+{
+    const moe_dtype_t dt = p->dtype;
+    const int d = p->d, F = p->ffn;
+    moe_status_t s = launch_kseg_layout(a.seg, a.S, a.rows, b.kcol, st);
+    if (!s) // W1^T [S, d, F], W2^T [S, F, d]
+        s = launch_transpose_batched(a.w1, a.S, F, d, dt, b.w1t, st);
+    if (!s)
+        s = launch_transpose_batched(a.w2, a.S, d, F, dt, b.w2t, st);
+    if (!s) // u = W1 x + b1 (fp32)
+        s = launch_grouped_gemm_f32out(a.a_rows, a.seg, a.S, a.rows, F, d, dt, a.w1, a.b1, b.u, b.gemm_ws,
+                                       b.gemm_ws_bytes, st);
+    if (!s) // dY rows (row-major for dh', transposed for dW2) and db2
+        s = launch_gather_t(dy, d, a.row_src, p->k, a.wgt, a.seg, a.S, a.rows, b.kcol, b.Kp, dt, b.dyT,
+                            a.dy_rows ? nullptr : b.dyp, a.db2 ? b.colpart : nullptr, st);
+    if (!s)
+        s = launch_seg_colsum(b.colpart, b.kcol, a.S, d, a.db2, st);
+    const void *dyr = a.dy_rows ? a.dy_rows : b.dyp;
+    if (!s) // dh' = W2^T dY
+        s = launch_grouped_gemm_f32out(dyr, a.seg, a.S, a.rows, F, d, dt, b.w2t, nullptr, b.dh, b.gemm_ws,
+                                       b.gemm_ws_bytes, st);
+    if (!s)
+        s = launch_act_bwd(b.u, b.dh, F, a.row_src, a.wgt, a.seg, a.S, a.rows, b.kcol, b.Kp, dt, b.du, b.duT, b.gwT,
+                           a.dwpart, a.db1 ? b.colpart : nullptr, st);
+    if (!s)
+        s = launch_seg_colsum(b.colpart, b.kcol, a.S, F, a.db1, st);
+    if (!s) // dx rows = W1^T du
+        s = launch_grouped_gemm_f32out(b.du, a.seg, a.S, a.rows, d, F, dt, b.w1t, nullptr, a.dx_rows, b.gemm_ws,
+                                       b.gemm_ws_bytes, st);
+    if (!s) // x rows, transposed, for dW1
+        s = launch_gather_t(x, d, a.row_src, p->k, nullptr, a.seg, a.S, a.rows, b.kcol, b.Kp, dt, b.xT, nullptr,
+                            nullptr, st);
+    if (!s) // dW2_s = sum_r dY (w g)^T : [d, F]
+        s = launch_kseg_gemm(b.dyT, b.gwT, b.kcol, a.S, d, F, b.Kp, dt, a.dw2, st);
+    if (!s) // dW1_s = sum_r du x^T : [F, d]
+        s = launch_kseg_gemm(b.duT, b.xT, b.kcol, a.S, F, d, b.Kp, dt, a.dw1, st);
+    return s;
+}
+
+} // namespace
+
+extern "C" size_t moe_backward_workspace_size(const moe_problem_t *p)
+{
+    if (!p || p->T < 0 || p->E < 1 || p->k < 1 || p->d < 1 || p->ffn < 1 || p->num_local_experts < 0)
+        return 0;
+    return carve_backward(p, nullptr, nullptr).bytes;
+}
+
+extern "C" moe_status_t moe_backward(const moe_problem_t *p, const moe_weights_t *w, const void *x, const void *dy,
+                                     float g_aux, const moe_grads_t *g, void *ws, size_t ws_bytes,
+                                     hipStream_t stream)
+{
+    clear_error();
+    if (!p || !w || !g)
+        return fail(MOE_ERR_INVALID_ARG, "backward: problem, weights and grads are required");
+    if (p->T < 0 || p->d < 1 || p->ffn < 1 || p->E < 1 || p->k < 1)
+        return fail(MOE_ERR_INVALID_ARG, "backward: invalid sizes");
+    if (!(g_aux == g_aux))
+        return fail(MOE_ERR_INVALID_ARG, "backward: g_aux is NaN");
+    if (moe_status_t s = check_route_args(x, p->dtype, w->w_router, p->T, p->d, p->E, p->k, (const int32_t *)1,
+                                          (const float *)1))
+        return s;
+    const int E_loc = local_count(p->E, p->num_local_experts);
+    const int64_t max_rows = moe_max_rows(p->T, p->E, p->k, p->capacity_factor, p->num_local_experts);
+    if (moe_status_t s = check_dispatch_args(x, p->dtype, (const int32_t *)1, p->T, p->d, p->E, p->k,
+                                             p->capacity_factor, p->expert_begin, p->num_local_experts,
+                                             (const int32_t *)1, (const int32_t *)1, (const int32_t *)1,
+                                             (const int32_t *)1, nullptr, max_rows))
+        return s;
+    if (!w->w1 || !w->w2 || (p->has_shared && (!w->ws1 || !w->ws2)))
+        return fail(MOE_ERR_INVALID_ARG, "backward: expert weights are required");
+    if ((p->T > 0 && !g->dx) || !g->dw_router || !g->dw1 || !g->dw2 || (p->has_shared && (!g->dws1 || !g->dws2)))
+        return fail(MOE_ERR_INVALID_ARG, "backward: dx, dw_router, dw1, dw2 (and dws1, dws2) are required");
+    if (p->T > 0 && !dy)
+        return fail(MOE_ERR_INVALID_ARG, "backward: dy is required");
+    if (moe_status_t s = check_gemm_args(x, nullptr, 1, max_rows, p->ffn, p->d, p->dtype, w->w1, w->b1, 1, g->dx,
+                                         "backward (first Linear)"))
+        return s;
+    if (moe_status_t s = check_gemm_args(x, nullptr, 1, max_rows, p->d, p->ffn, p->dtype, w->w2, w->b2, 0, g->dx,
+                                         "backward (second Linear)"))
+        return s;
+    if (!aligned16(dy) || (p->has_shared && (!aligned16(w->ws1) || !aligned16(w->ws2) || !aligned16(w->bs1))))
+        return fail(MOE_ERR_INVALID_ARG, "backward: dy and the shared expert buffers must be 16-byte aligned");
+    if (p->dtype == MOE_BF16 && (p->d % 64 != 0 || p->ffn % 64 != 0 || p->d < 128 || p->ffn < 128))
+        return fail(MOE_ERR_UNSUPPORTED, "backward: bf16 needs d and ffn multiples of 64, at least 128 (d=%d ffn=%d)",
+                    p->d, p->ffn);
+    const BackwardWs need = carve_backward(p, g, nullptr);
+    if (moe_status_t s = check_ws(ws, ws_bytes, need.bytes, "backward"))
+        return s;
+    const BackwardWs b = carve_backward(p, g, ws);
+    const int64_t T = p->T;
+    const int d = p->d, F = p->ffn, E = p->E;
+
+    moe_status_t s = launch_route(x, p->dtype, w->w_router, w->b_router, w->sel_bias, T, d, E, p->k, p->alpha,
+                                  b.topk_idx, b.topk_w, b.expert_count, b.f, b.P, b.l_aux, b.probs, b.route_ws,
+                                  stream);
+    if (!s)
+        s = launch_dispatch(x, p->dtype, b.topk_idx, T, d, E, p->k, p->capacity_factor, p->expert_begin, E_loc,
+                            b.seg_offsets, b.kept_count, b.slot_row, b.row_src, b.x_perm, max_rows, nullptr,
+                            b.dispatch_ws, stream);
+    if (s)
+        return s;
+    if (T == 0) {
+        // no tokens: every weight gradient is zero
+        float *z[] = {g->dw_router, g->db_router, g->dw1, g->db1, g->dw2, g->db2, g->dws1, g->dbs1, g->dws2, g->dbs2};
+        const int64_t n[] = {(int64_t)E * d, E, (int64_t)E_loc * F * d, (int64_t)E_loc * F, (int64_t)E_loc * d * F,
+                             (int64_t)E_loc * d, p->has_shared ? (int64_t)F * d : 0, p->has_shared ? F : 0,
+                             p->has_shared ? (int64_t)d * F : 0, p->has_shared ? d : 0};
+        for (int i = 0; i < 10 && !s; ++i)
+            s = launch_fill_zero(z[i], n[i], stream);
+        return s;
+    }
+    if (p->has_shared) {
+        FfnBwd a = {};
+        a.a_rows = x;
+        a.dy_rows = dy;
+        a.S = 1;
+        a.rows = T;
+        a.w1 = w->ws1;
+        a.b1 = w->bs1;
+        a.w2 = w->ws2;
+        a.dw1 = g->dws1;
+        a.db1 = g->dbs1;
+        a.dw2 = g->dws2;
+        a.db2 = g->dbs2;
+        a.dx_rows = b.dx_sh;
+        s = ffn_backward(p, x, dy, a, b, stream);
+    }
+    if (!s) {
+        FfnBwd a = {};
+        a.a_rows = b.x_perm;
+        a.seg = b.seg_offsets;
+        a.row_src = b.row_src;
+        a.S = E_loc;
+        a.rows = max_rows;
+        a.wgt = b.topk_w;
+        a.w1 = w->w1;
+        a.b1 = w->b1;
+        a.w2 = w->w2;
+        a.dw1 = g->dw1;
+        a.db1 = g->db1;
+        a.dw2 = g->dw2;
+        a.db2 = g->db2;
+        a.dx_rows = b.dx_rows;
+        a.dwpart = b.dwpart;
+        s = ffn_backward(p, x, dy, a, b, stream);
+    }
+    if (!s) {
+        const float c_aux = (float)((double)g_aux * (double)p->alpha / (double)T);
+        s = launch_router_bwd(b.probs, b.topk_idx, b.slot_row, b.dwpart, (F + 63) / 64, w->b2, dy, p->dtype, d,
+                              p->expert_begin, b.f, c_aux, T, E, p->k, b.dl, stream);
+    }
+    if (!s)
+        s = launch_router_wgrad(x, p->dtype, b.dl, T, d, E, g->dw_router, g->db_router, b.router_ws, stream);
+    if (!s)
+        s = launch_dx_combine(b.dx_rows, b.slot_row, p->k, b.dx_sh, b.dl, w->w_router, T, d, E, g->dx, stream);
+    return s;
 }

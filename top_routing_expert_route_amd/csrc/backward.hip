@@ -1,0 +1,593 @@
+// Backward pass of the MoE layer: the element-wise, permutation and router
+// kernels around the grouped GEMMs (which live in gemm.hip).
+//
+// Pages: "Load Balancing: The Auxiliary Loss" (L_aux is added to the task
+// loss and backpropagated; f counts selections and carries no gradient) and
+// "MoE Layer Structure" (Y = sum of routing weight times expert output, the
+// weight being the router's softmax probability).
+//
+// Notation, per kept selection placed in dispatched row r (token t, local
+// expert s, routing weight w_r = p[t, e]):
+//   u_r = W1_s x_t + b1_s,  g_r = GELU(u_r),  v_r = W2_s g_r + b2_s,
+//   Y_t += w_r v_r.
+// With dY = dL/dY:
+//   dh'_r = W2_s^T dY_t                     (the gradient at g_r, before w_r)
+//   dw_r  = dY_t . v_r = dh'_r . g_r + dY_t . b2_s
+//   du_r  = w_r dh'_r * GELU'(u_r)
+//   dW2_s = sum_r dY_t (w_r g_r)^T,  db2_s = sum_r w_r dY_t
+//   dW1_s = sum_r du_r x_t^T,        db1_s = sum_r du_r
+//   dx_t += W1_s^T du_r
+// Router, softmax over E: dp[t, e] = g_aux alpha f_e / T + sum of dw_r over
+// t's kept selections of e; dl[t, e] = p[t, e] (dp[t, e] - sum_e' p dp);
+//   dW_r = sum_t dl_t x_t^T, db_r = sum_t dl_t, dx_t += W_r^T dl_t.
+// The shared expert is the same FFN with w_r = 1 on every token.
+//
+// The weight-gradient GEMMs contract over dispatched rows, so their operands
+// are stored transposed in the K-segmented layout (kcol): row block s of
+// 64-aligned columns per segment, zero-padded.  The kernels here write those
+// operands straight from the row-major data through LDS tile transposes.
+#include "common.hpp"
+
+namespace moe {
+
+namespace {
+
+template <class T> struct Elt;
+template <> struct Elt<float> {
+    static __device__ __forceinline__ float ld(const float *p, int64_t i) { return p[i]; }
+    static __device__ __forceinline__ void st(float *p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elt<uint16_t> {
+    static __device__ __forceinline__ float ld(const uint16_t *p, int64_t i) { return bf16_bits_to_f32(p[i]); }
+    static __device__ __forceinline__ void st(uint16_t *p, int64_t i, float v) { p[i] = f32_to_bf16_bits(v); }
+};
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Rows of segment s: seg == NULL is one segment of `rows` rows.
+__device__ __forceinline__ void seg_rows(const int32_t *seg, int s, int64_t rows, int64_t &lo, int64_t &hi)
+{
+    if (!seg) {
+        lo = 0;
+        hi = rows;
+        return;
+    }
+    lo = seg[s];
+    hi = seg[s + 1];
+    lo = lo < 0 ? 0 : (lo > rows ? rows : lo);
+    hi = hi < lo ? lo : (hi > rows ? rows : hi);
+}
+
+// Segment owning column tile ct < kcol[S]: the largest s with kcol[s] <= ct
+// (empty segments share their kcol with the next one).
+__device__ __forceinline__ int seg_of_tile(const int32_t *kcol, int S, int ct)
+{
+    int lo = 0, hi = S - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (kcol[mid] <= ct)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// dst[b, c, r] = src[b, r, c] for B matrices of R x C (64 x 64 LDS tiles).
+template <class T>
+__global__ __launch_bounds__(256) void transpose_batched(const T *__restrict__ src, int R, int C, T *__restrict__ dst)
+{
+    __shared__ float tile[64][65];
+    const int64_t b = blockIdx.z;
+    const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+    const T *s = src + b * R * C;
+    T *o = dst + b * R * C;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int i = ty; i < 64; i += 4)
+        if (r0 + i < R && c0 + tx < C)
+            tile[i][tx] = Elt<T>::ld(s, (int64_t)(r0 + i) * C + c0 + tx);
+    __syncthreads();
+    for (int i = ty; i < 64; i += 4)
+        if (c0 + i < C && r0 + tx < R)
+            Elt<T>::st(o, (int64_t)(c0 + i) * R + r0 + tx, tile[tx][i]);
+}
+
+// Gather of token rows into the K-segmented layout.  Column 64 kcol[s] + i
+// holds row r = lo_s + i of segment s (token t = row_src[r] / k, or r when
+// row_src is NULL); columns past the segment's rows are zero.
+//   dstT[f, col]     = src[t, f]
+//   dst[r, f]        = src[t, f]                      (if dst)
+//   colpart[ct, f]   = sum over the tile's rows of wgt[row_src[r]] src[t, f]
+//                      (wgt NULL: weight 1)           (if colpart)
+// Grid (feature tiles of 64, strided over the column tiles).
+template <class T>
+__global__ __launch_bounds__(256) void gather_t(const T *__restrict__ src, int D, const int32_t *__restrict__ row_src,
+                                                int k, const float *__restrict__ wgt, const int32_t *__restrict__ seg,
+                                                int S, int64_t rows, const int32_t *__restrict__ kcol, int64_t Kp,
+                                                T *__restrict__ dstT, T *__restrict__ dst, float *__restrict__ colpart)
+{
+    __shared__ float tile[64][65];
+    __shared__ int64_t s_tok[64];
+    __shared__ float s_w[64];
+    const int f0 = blockIdx.x * 64;
+    const int total = kcol[S];
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    for (int ct = blockIdx.y; ct < total; ct += gridDim.y) {
+        const int s = seg_of_tile(kcol, S, ct);
+        int64_t lo, hi;
+        seg_rows(seg, s, rows, lo, hi);
+        const int64_t rbase = lo + (int64_t)(ct - kcol[s]) * 64;
+        if (threadIdx.x < 64) {
+            const int64_t r = rbase + threadIdx.x;
+            int64_t tok = -1;
+            float w = 0.f;
+            if (r < hi) {
+                const int64_t slot = row_src ? (int64_t)row_src[r] : r;
+                tok = row_src ? slot / k : slot;
+                w = wgt ? wgt[slot] : 1.f;
+            }
+            s_tok[threadIdx.x] = tok;
+            s_w[threadIdx.x] = w;
+        }
+        __syncthreads();
+        const int f = f0 + tx;
+        for (int i = ty; i < 64; i += 4) {
+            const int64_t tok = s_tok[i];
+            float v = 0.f;
+            if (tok >= 0 && f < D) {
+                v = Elt<T>::ld(src, tok * D + f);
+                if (dst)
+                    Elt<T>::st(dst, (rbase + i) * D + f, v);
+            }
+            tile[i][tx] = v;
+        }
+        __syncthreads();
+        if (colpart && ty == 0 && f < D) {
+            float a = 0.f;
+            for (int i = 0; i < 64; ++i)
+                a = fmaf(s_w[i], tile[i][tx], a);
+            colpart[(int64_t)ct * D + f] = a;
+        }
+        const int64_t col = (int64_t)ct * 64 + tx;
+        for (int i = ty; i < 64; i += 4)
+            if (f0 + i < D)
+                Elt<T>::st(dstT, (int64_t)(f0 + i) * Kp + col, tile[tx][i]);
+        __syncthreads();
+    }
+}
+
+// GELU backward over the K-segmented rows (same row/column map as gather_t),
+// from u = W1 x + b1 and dh' (both fp32 [rows, F]):
+//   du[r, q]  = w_r dh'[r, q] GELU'(u[r, q])        (row-major, T)
+//   duT[q, col] = du[r, q],  gwT[q, col] = w_r GELU(u[r, q])   (zero padding)
+//   dwpart[r, qt] = sum_{q in feature tile qt} dh'[r, q] GELU(u[r, q])   (if dwpart)
+//   colpart[ct, q] = sum over the tile's rows of du[r, q]
+// w_r = wgt[row_src[r]] (1 when wgt is NULL).  Grid (ceil(F / 64), column tiles).
+template <class T>
+__global__ __launch_bounds__(256) void act_bwd(const float *__restrict__ u, const float *__restrict__ dh, int F,
+                                               const int32_t *__restrict__ row_src, const float *__restrict__ wgt,
+                                               const int32_t *__restrict__ seg, int S, int64_t rows,
+                                               const int32_t *__restrict__ kcol, int64_t Kp, T *__restrict__ du,
+                                               T *__restrict__ duT, T *__restrict__ gwT, float *__restrict__ dwpart,
+                                               float *__restrict__ colpart)
+{
+    __shared__ float t_du[64][65], t_gw[64][65];
+    __shared__ float s_w[64];
+    __shared__ int s_ok[64];
+    __shared__ float s_cs[4][64];
+    const int q0 = blockIdx.x * 64;
+    const int FT = gridDim.x;
+    const int total = kcol[S];
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+    const int q = q0 + tx;
+    for (int ct = blockIdx.y; ct < total; ct += gridDim.y) {
+        const int s = seg_of_tile(kcol, S, ct);
+        int64_t lo, hi;
+        seg_rows(seg, s, rows, lo, hi);
+        const int64_t rbase = lo + (int64_t)(ct - kcol[s]) * 64;
+        if (threadIdx.x < 64) {
+            const int64_t r = rbase + threadIdx.x;
+            const bool ok = r < hi;
+            s_ok[threadIdx.x] = ok ? 1 : 0;
+            s_w[threadIdx.x] = ok ? (wgt ? wgt[row_src ? row_src[r] : r] : 1.f) : 0.f;
+        }
+        __syncthreads();
+        float cs = 0.f;
+        for (int i = ty; i < 64; i += 4) {
+            const int64_t r = rbase + i;
+            const bool ok = s_ok[i] != 0;
+            float vdu = 0.f, vgw = 0.f, dwp = 0.f;
+            if (ok && q < F) {
+                const float uu = u[r * F + q], hh = dh[r * F + q];
+                float g, gp;
+                gelu_and_grad(uu, g, gp);
+                const float w = s_w[i];
+                vdu = w * hh * gp;
+                vgw = w * g;
+                dwp = hh * g;
+                Elt<T>::st(du, r * F + q, vdu);
+            }
+            cs += vdu;
+            t_du[i][tx] = vdu;
+            t_gw[i][tx] = vgw;
+            if (dwpart) {
+                dwp = wave_sum(dwp);
+                if (tx == 0 && ok)
+                    dwpart[r * FT + blockIdx.x] = dwp;
+            }
+        }
+        s_cs[ty][tx] = cs;
+        __syncthreads();
+        if (colpart && ty == 0 && q < F)
+            colpart[(int64_t)ct * F + q] = ((s_cs[0][tx] + s_cs[1][tx]) + s_cs[2][tx]) + s_cs[3][tx];
+        const int64_t col = (int64_t)ct * 64 + tx;
+        for (int i = ty; i < 64; i += 4) {
+            if (q0 + i < F) {
+                Elt<T>::st(duT, (int64_t)(q0 + i) * Kp + col, t_du[tx][i]);
+                Elt<T>::st(gwT, (int64_t)(q0 + i) * Kp + col, t_gw[tx][i]);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// out[s, f] = sum of colpart[ct, f] over segment s's column tiles, in tile
+// order (0 for an empty segment).  Grid (ceil(D / 256), S).
+__global__ __launch_bounds__(256) void seg_colsum(const float *__restrict__ colpart, const int32_t *__restrict__ kcol,
+                                                  int D, float *__restrict__ out)
+{
+    const int s = blockIdx.y;
+    const int f = blockIdx.x * 256 + threadIdx.x;
+    if (f >= D)
+        return;
+    float a = 0.f;
+    for (int ct = kcol[s]; ct < kcol[s + 1]; ++ct)
+        a += colpart[(int64_t)ct * D + f];
+    out[(int64_t)s * D + f] = a;
+}
+
+// Router backward, one wave per token: dw of every kept selection, then
+//   dp[e] = c_aux f[e] + sum_{kept j with topk_idx = e} dw_j   (c_aux = g_aux alpha / T)
+//   dl[t, e] = p[t, e] (dp[e] - sum_e' p[t, e'] dp[e']).
+// dw_j = sum_qt dwpart[r, qt] (+ dY_t . b2[e - e0]).
+template <class T>
+__global__ __launch_bounds__(256) void router_bwd(const float *__restrict__ probs, const int32_t *__restrict__ topk_idx,
+                                                  const int32_t *__restrict__ slot_row,
+                                                  const float *__restrict__ dwpart, int FT, const T *__restrict__ b2,
+                                                  const T *__restrict__ dY, int d, int e0,
+                                                  const float *__restrict__ f, float c_aux, int64_t Ttok, int E, int k,
+                                                  float *__restrict__ dl)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= Ttok)
+        return; // wave-uniform; the block has no barrier
+    // lane j keeps selection j: its expert (-1 unless kept) and dw
+    int my_e = -1;
+    float my_dw = 0.f;
+    for (int j = 0; j < k; ++j) {
+        const int64_t slot = t * k + j;
+        const int r = slot_row[slot];
+        const int e = topk_idx[slot];
+        float a = 0.f;
+        if (r >= 0) {
+            for (int qt = lane; qt < FT; qt += 64)
+                a += dwpart[(int64_t)r * FT + qt];
+            if (b2) {
+                const T *brow = b2 + (int64_t)(e - e0) * d;
+                for (int o = lane; o < d; o += 64)
+                    a = fmaf(Elt<T>::ld(dY, t * d + o), Elt<T>::ld(brow, o), a);
+            }
+        }
+        a = wave_sum(a);
+        if (lane == j) {
+            my_e = r >= 0 ? e : -1;
+            my_dw = a;
+        }
+    }
+    const float *pt = probs + t * E;
+    float sd = 0.f;
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int b = 0; b < E; b += 64) {
+            const int e = b + lane;
+            float dp = e < E ? c_aux * f[e] : 0.f;
+            for (int j = 0; j < k; ++j) {
+                const int ej = __shfl(my_e, j, 64);
+                const float dj = __shfl(my_dw, j, 64);
+                if (ej == e)
+                    dp += dj;
+            }
+            if (e < E) {
+                if (pass == 0)
+                    sd = fmaf(pt[e], dp, sd);
+                else
+                    dl[t * E + e] = pt[e] * (dp - sd);
+            }
+        }
+        if (pass == 0)
+            sd = wave_sum(sd);
+    }
+}
+
+// Router weight gradient, first level: part[c, e, i] = sum over token chunk
+// c of dl[t, e] x[t, i], for EG experts of group blockIdx.z.
+// Grid (ceil(d / 256), chunks, ceil(E / EG)).
+template <class T, int EG>
+__global__ __launch_bounds__(256) void router_wgrad_part(const T *__restrict__ x, const float *__restrict__ dl,
+                                                         int64_t Ttok, int d, int E, int64_t tc,
+                                                         float *__restrict__ part)
+{
+    __shared__ float s_dl[64][EG];
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    const int c = blockIdx.y;
+    const int eg0 = blockIdx.z * EG;
+    float acc[EG];
+#pragma unroll
+    for (int e = 0; e < EG; ++e)
+        acc[e] = 0.f;
+    const int64_t t0 = (int64_t)c * tc, t1 = t0 + tc < Ttok ? t0 + tc : Ttok;
+    for (int64_t tb = t0; tb < t1; tb += 64) {
+        __syncthreads();
+        for (int q = threadIdx.x; q < 64 * EG; q += 256) {
+            const int tt = q / EG, e = q % EG;
+            const int64_t t = tb + tt;
+            s_dl[tt][e] = (t < t1 && eg0 + e < E) ? dl[t * E + eg0 + e] : 0.f;
+        }
+        __syncthreads();
+        const int n = (int)(t1 - tb < 64 ? t1 - tb : 64);
+        if (i < d) {
+            for (int tt = 0; tt < n; ++tt) {
+                const float xv = Elt<T>::ld(x, (tb + tt) * d + i);
+#pragma unroll
+                for (int e = 0; e < EG; ++e)
+                    acc[e] = fmaf(s_dl[tt][e], xv, acc[e]);
+            }
+        }
+    }
+    if (i < d) {
+#pragma unroll
+        for (int e = 0; e < EG; ++e)
+            if (eg0 + e < E)
+                part[((int64_t)c * E + eg0 + e) * d + i] = acc[e];
+    }
+}
+
+// dW_r[e, i] = sum_c part[c, e, i] in chunk order.
+__global__ __launch_bounds__(256) void router_wgrad_reduce(const float *__restrict__ part, int nchunk, int64_t n,
+                                                           float *__restrict__ out)
+{
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= n)
+        return;
+    float a = 0.f;
+    for (int c = 0; c < nchunk; ++c)
+        a += part[(int64_t)c * n + q];
+    out[q] = a;
+}
+
+// db_r[e] = sum_t dl[t, e]: one block per expert, strided partial sums and a
+// fixed-shape tree.
+__global__ __launch_bounds__(256) void router_bias_grad(const float *__restrict__ dl, int64_t Ttok, int E,
+                                                        float *__restrict__ db)
+{
+    __shared__ float red[256];
+    const int e = blockIdx.x;
+    float a = 0.f;
+    for (int64_t t = threadIdx.x; t < Ttok; t += 256)
+        a += dl[t * E + e];
+    red[threadIdx.x] = a;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w)
+            red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0)
+        db[e] = red[0];
+}
+
+// dx[t, i] = sum_e dl[t, e] W_r[e, i] + sum over t's kept selections of
+// dx_rows[slot_row, i] + dx_sh[t, i].  Block = TB tokens x 256 columns.
+template <int TB>
+__global__ __launch_bounds__(256) void dx_combine(const float *__restrict__ dx_rows,
+                                                  const int32_t *__restrict__ slot_row, int k,
+                                                  const float *__restrict__ dx_sh, const float *__restrict__ dl,
+                                                  const float *__restrict__ w_r, int64_t Ttok, int d, int E,
+                                                  float *__restrict__ dx)
+{
+    __shared__ float s_dl[TB][256];
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    const int64_t t0 = (int64_t)blockIdx.y * TB;
+    float acc[TB];
+#pragma unroll
+    for (int q = 0; q < TB; ++q)
+        acc[q] = 0.f;
+    for (int eb = 0; eb < E; eb += 256) {
+        const int ne = E - eb < 256 ? E - eb : 256;
+        __syncthreads();
+        for (int q = threadIdx.x; q < TB * 256; q += 256) {
+            const int tq = q / 256, e = q % 256;
+            s_dl[tq][e] = (t0 + tq < Ttok && e < ne) ? dl[(t0 + tq) * E + eb + e] : 0.f;
+        }
+        __syncthreads();
+        if (i < d) {
+            for (int e = 0; e < ne; ++e) {
+                const float wv = w_r[(int64_t)(eb + e) * d + i];
+#pragma unroll
+                for (int q = 0; q < TB; ++q)
+                    acc[q] = fmaf(s_dl[q][e], wv, acc[q]);
+            }
+        }
+    }
+    if (i >= d)
+        return;
+#pragma unroll
+    for (int q = 0; q < TB; ++q) {
+        const int64_t t = t0 + q;
+        if (t >= Ttok)
+            break;
+        float v = acc[q];
+        for (int j = 0; j < k; ++j) {
+            const int r = slot_row[t * k + j];
+            if (r >= 0)
+                v += dx_rows[(int64_t)r * d + i];
+        }
+        if (dx_sh)
+            v += dx_sh[t * d + i];
+        dx[t * d + i] = v;
+    }
+}
+
+__global__ __launch_bounds__(256) void fill_zero(float *__restrict__ p, int64_t n)
+{
+    for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < n; q += (int64_t)gridDim.x * 256)
+        p[q] = 0.f;
+}
+
+unsigned strided_grid(int64_t n, int64_t cap) { return (unsigned)(n < 1 ? 1 : (n < cap ? n : cap)); }
+
+} // namespace
+
+moe_status_t launch_fill_zero(float *p, int64_t n, hipStream_t stream)
+{
+    if (!p || n <= 0)
+        return MOE_OK;
+    fill_zero<<<strided_grid((n + 255) / 256, 4096), 256, 0, stream>>>(p, n);
+    return check_launch("fill_zero");
+}
+
+moe_status_t launch_transpose_batched(const void *src, int B, int R, int C, moe_dtype_t dt, void *dst,
+                                      hipStream_t stream)
+{
+    const dim3 g((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64), (unsigned)B);
+    if (dt == MOE_BF16)
+        transpose_batched<uint16_t><<<g, 256, 0, stream>>>((const uint16_t *)src, R, C, (uint16_t *)dst);
+    else
+        transpose_batched<float><<<g, 256, 0, stream>>>((const float *)src, R, C, (float *)dst);
+    return check_launch("transpose_batched");
+}
+
+moe_status_t launch_gather_t(const void *src, int D, const int32_t *row_src, int k, const float *wgt,
+                             const int32_t *seg, int S, int64_t rows, const int32_t *kcol, int64_t Kp, moe_dtype_t dt,
+                             void *dstT, void *dst, float *colpart, hipStream_t stream)
+{
+    const int64_t ctiles = Kp / 64;
+    const int fx = (D + 63) / 64;
+    const dim3 g((unsigned)fx, strided_grid(ctiles, (8192 + fx - 1) / fx));
+    if (dt == MOE_BF16)
+        gather_t<uint16_t><<<g, 256, 0, stream>>>((const uint16_t *)src, D, row_src, k, wgt, seg, S, rows, kcol, Kp,
+                                                  (uint16_t *)dstT, (uint16_t *)dst, colpart);
+    else
+        gather_t<float><<<g, 256, 0, stream>>>((const float *)src, D, row_src, k, wgt, seg, S, rows, kcol, Kp,
+                                               (float *)dstT, (float *)dst, colpart);
+    return check_launch("gather_t");
+}
+
+moe_status_t launch_act_bwd(const float *u, const float *dh, int F, const int32_t *row_src, const float *wgt,
+                            const int32_t *seg, int S, int64_t rows, const int32_t *kcol, int64_t Kp, moe_dtype_t dt,
+                            void *du, void *duT, void *gwT, float *dwpart, float *colpart, hipStream_t stream)
+{
+    const int64_t ctiles = Kp / 64;
+    const int fx = (F + 63) / 64;
+    const dim3 g((unsigned)fx, strided_grid(ctiles, (8192 + fx - 1) / fx));
+    if (dt == MOE_BF16)
+        act_bwd<uint16_t><<<g, 256, 0, stream>>>(u, dh, F, row_src, wgt, seg, S, rows, kcol, Kp, (uint16_t *)du,
+                                                 (uint16_t *)duT, (uint16_t *)gwT, dwpart, colpart);
+    else
+        act_bwd<float><<<g, 256, 0, stream>>>(u, dh, F, row_src, wgt, seg, S, rows, kcol, Kp, (float *)du,
+                                              (float *)duT, (float *)gwT, dwpart, colpart);
+    return check_launch("act_bwd");
+}
+
+moe_status_t launch_seg_colsum(const float *colpart, const int32_t *kcol, int S, int D, float *out,
+                               hipStream_t stream)
+{
+    if (!out)
+        return MOE_OK;
+    seg_colsum<<<dim3((unsigned)((D + 255) / 256), (unsigned)S), 256, 0, stream>>>(colpart, kcol, D, out);
+    return check_launch("seg_colsum");
+}
+
+moe_status_t launch_router_bwd(const float *probs, const int32_t *topk_idx, const int32_t *slot_row,
+                               const float *dwpart, int FT, const void *b2, const void *dY, moe_dtype_t dt, int d,
+                               int e0, const float *f, float c_aux, int64_t T, int E, int k, float *dl,
+                               hipStream_t stream)
+{
+    const unsigned g = (unsigned)((T + 3) / 4);
+    if (dt == MOE_BF16)
+        router_bwd<uint16_t><<<g, 256, 0, stream>>>(probs, topk_idx, slot_row, dwpart, FT, (const uint16_t *)b2,
+                                                    (const uint16_t *)dY, d, e0, f, c_aux, T, E, k, dl);
+    else
+        router_bwd<float><<<g, 256, 0, stream>>>(probs, topk_idx, slot_row, dwpart, FT, (const float *)b2,
+                                                 (const float *)dY, d, e0, f, c_aux, T, E, k, dl);
+    return check_launch("router_bwd");
+}
+
+// Chunks of the router weight-gradient partials: about 2048 blocks in all,
+// at least 64 tokens per chunk.
+static int router_chunks(int64_t T, int d, int E)
+{
+    const int64_t cx = (d + 255) / 256, cz = E <= 8 ? 1 : (E <= 16 ? 1 : (E + 31) / 32);
+    int64_t n = 2048 / (cx * cz);
+    const int64_t most = (T + 63) / 64;
+    n = n < 1 ? 1 : (n > most ? most : n);
+    return (int)n;
+}
+
+size_t router_wgrad_ws_bytes(int64_t T, int d, int E)
+{
+    return align_up((size_t)router_chunks(T, d, E) * E * d * sizeof(float));
+}
+
+moe_status_t launch_router_wgrad(const void *x, moe_dtype_t dt, const float *dl, int64_t T, int d, int E,
+                                 float *dw_r, float *db_r, void *ws, hipStream_t stream)
+{
+    const int nch = router_chunks(T, d, E);
+    const int64_t tc = (T + nch - 1) / nch;
+    float *part = (float *)ws;
+    const unsigned cx = (unsigned)((d + 255) / 256);
+#define MOE_WGRAD(EG)                                                                                               \
+    do {                                                                                                            \
+        const dim3 g(cx, (unsigned)nch, (unsigned)((E + EG - 1) / EG));                                             \
+        if (dt == MOE_BF16)                                                                                         \
+            router_wgrad_part<uint16_t, EG><<<g, 256, 0, stream>>>((const uint16_t *)x, dl, T, d, E, tc, part);     \
+        else                                                                                                        \
+            router_wgrad_part<float, EG><<<g, 256, 0, stream>>>((const float *)x, dl, T, d, E, tc, part);           \
+    } while (0)
+    if (E <= 8)
+        MOE_WGRAD(8);
+    else if (E <= 16)
+        MOE_WGRAD(16);
+    else
+        MOE_WGRAD(32);
+#undef MOE_WGRAD
+    if (moe_status_t s = check_launch("router_wgrad_part"))
+        return s;
+    const int64_t n = (int64_t)E * d;
+    router_wgrad_reduce<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(part, nch, n, dw_r);
+    if (moe_status_t s = check_launch("router_wgrad_reduce"))
+        return s;
+    if (db_r) {
+        router_bias_grad<<<(unsigned)E, 256, 0, stream>>>(dl, T, E, db_r);
+        return check_launch("router_bias_grad");
+    }
+    return MOE_OK;
+}
+
+moe_status_t launch_dx_combine(const float *dx_rows, const int32_t *slot_row, int k, const float *dx_sh,
+                               const float *dl, const float *w_r, int64_t T, int d, int E, float *dx,
+                               hipStream_t stream)
+{
+    constexpr int TB = 16;
+    const dim3 g((unsigned)((d + 255) / 256), (unsigned)((T + TB - 1) / TB));
+    dx_combine<TB><<<g, 256, 0, stream>>>(dx_rows, slot_row, k, dx_sh, dl, w_r, T, d, E, dx);
+    return check_launch("dx_combine");
+}
+
+} // namespace moe

@@ -58,6 +58,26 @@ __device__ __forceinline__ float gelu_erf(float u)
     return u >= 0.f ? u - u * q : u * q;
 }
 
+// GELU and its derivative together: with Phi the standard normal CDF and phi
+// its density, GELU(u) = u Phi(u) and GELU'(u) = Phi(u) + u phi(u).  Phi
+// comes from the same erf approximation as gelu_erf (bitwise the same
+// GELU), phi(u) = exp(-u^2 / 2) / sqrt(2 pi) shares its exponential.
+__device__ __forceinline__ void gelu_and_grad(float u, float &g, float &gp)
+{
+    const float x = fabsf(u) * 0.70710678118654752f;
+    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+    float poly = fmaf(1.061405429f, t, -1.453152027f);
+    poly = fmaf(poly, t, 1.421413741f);
+    poly = fmaf(poly, t, -0.284496736f);
+    poly = fmaf(poly, t, 0.254829592f);
+    poly *= t;
+    const float e = __expf(-x * x);
+    const float q = 0.5f * poly * e; // Phi(-|u|)
+    g = u >= 0.f ? u - u * q : u * q;
+    const float Phi = u >= 0.f ? 1.0f - q : q;
+    gp = fmaf(u, e * 0.39894228040143268f, Phi);
+}
+
 // ------------------------------------------------------------ workspaces --
 constexpr size_t kAlign = 256;
 __host__ __device__ constexpr size_t align_up(size_t n, size_t a = kAlign) { return (n + a - 1) / a * a; }
@@ -81,8 +101,8 @@ size_t gemm_ws_bytes();
 moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, const float *b_router,
                           const float *sel_bias, int64_t T, int d, int E, int k, float alpha, int32_t *topk_idx,
                           float *topk_w,
-                          int32_t *expert_count, float *f, float *P, float *l_aux, void *ws,
-                          hipStream_t stream);
+                          int32_t *expert_count, float *f, float *P, float *l_aux, float *probs, void *ws,
+                          hipStream_t stream); // probs [T, E] fp32 softmax output, or NULL
 
 size_t dispatch_ws_bytes(int64_t T, int k, int E_loc);
 int64_t capacity_of(int64_t T, int E, float capacity_factor); // -1: no cap
@@ -102,8 +122,49 @@ moe_status_t launch_grouped_gemm(const void *a, const int32_t *seg_offsets, int 
 moe_status_t launch_router_gemm(const void *x, const void *w3, int64_t T, int d, int E, float *logits, void *ws,
                                 size_t ws_bytes, hipStream_t stream);
 
+// Forward-form grouped GEMM with an fp32 output and no activation:
+// out[r, n] = sum_k a[r, k] w[s, n, k] (+ bias[s, n]).  bf16 needs K % 64 == 0.
+moe_status_t launch_grouped_gemm_f32out(const void *a, const int32_t *seg_offsets, int num_segments,
+                                        int64_t max_rows, int N, int K, moe_dtype_t dt, const void *w,
+                                        const void *bias, float *out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+// K-segmented layout of the weight-gradient GEMMs: segment s of seg (NULL =
+// one segment of max_rows rows) takes max(2, ceil(rows_s / 64)) steps of 64
+// columns (none if empty); kcol [S+1] = first step of each segment, kcol[S]
+// the total.  kseg_cols_bound bounds 64 * kcol[S].
+int64_t kseg_cols_bound(int64_t max_rows, int S);
+moe_status_t launch_kseg_layout(const int32_t *seg, int S, int64_t max_rows, int32_t *kcol, hipStream_t stream);
+// C [S, M, N] fp32: C_s[m, n] = sum over segment s's columns k of A[m, k] W[n, k],
+// A [M, Kp], W [N, Kp] (dt; padding columns zero).  Empty segments give zeros.
+moe_status_t launch_kseg_gemm(const void *A, const void *W, const int32_t *kcol, int S, int M, int N, int64_t Kp,
+                              moe_dtype_t dt, float *C, hipStream_t stream);
+
 moe_status_t launch_combine(const void *y_perm, int64_t max_rows, const int32_t *slot_row,
                             const float *topk_w, const void *y_shared, int64_t T, int d, int k,
                             moe_dtype_t dt, void *y, hipStream_t stream);
+
+// Backward-pass kernels (backward.hip); the K-segmented layout and column
+// map are those of launch_kseg_layout.
+moe_status_t launch_fill_zero(float *p, int64_t n, hipStream_t stream);
+moe_status_t launch_transpose_batched(const void *src, int B, int R, int C, moe_dtype_t dt, void *dst,
+                                      hipStream_t stream);
+moe_status_t launch_gather_t(const void *src, int D, const int32_t *row_src, int k, const float *wgt,
+                             const int32_t *seg, int S, int64_t rows, const int32_t *kcol, int64_t Kp, moe_dtype_t dt,
+                             void *dstT, void *dst, float *colpart, hipStream_t stream);
+moe_status_t launch_act_bwd(const float *u, const float *dh, int F, const int32_t *row_src, const float *wgt,
+                            const int32_t *seg, int S, int64_t rows, const int32_t *kcol, int64_t Kp, moe_dtype_t dt,
+                            void *du, void *duT, void *gwT, float *dwpart, float *colpart, hipStream_t stream);
+moe_status_t launch_seg_colsum(const float *colpart, const int32_t *kcol, int S, int D, float *out,
+                               hipStream_t stream);
+moe_status_t launch_router_bwd(const float *probs, const int32_t *topk_idx, const int32_t *slot_row,
+                               const float *dwpart, int FT, const void *b2, const void *dY, moe_dtype_t dt, int d,
+                               int e0, const float *f, float c_aux, int64_t T, int E, int k, float *dl,
+                               hipStream_t stream);
+size_t router_wgrad_ws_bytes(int64_t T, int d, int E);
+moe_status_t launch_router_wgrad(const void *x, moe_dtype_t dt, const float *dl, int64_t T, int d, int E,
+                                 float *dw_r, float *db_r, void *ws, hipStream_t stream);
+moe_status_t launch_dx_combine(const float *dx_rows, const int32_t *slot_row, int k, const float *dx_sh,
+                               const float *dl, const float *w_r, int64_t T, int d, int E, float *dx,
+                               hipStream_t stream);
 
 } // namespace moe

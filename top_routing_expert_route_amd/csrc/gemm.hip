@@ -701,8 +701,8 @@ __device__ __forceinline__ Src src_of(const WorkCtx &x, const CopyGeo &cg, const
 // is loaded if there is none).  The loads switch to item i+1's rows for the
 // last two K steps; its source is looked up only then, so that it does not
 // occupy registers during the loop.
-template <int BK, class G, int NBV, bool GELU, bool BIAS, bool F32OUT, bool PART>
-__device__ __forceinline__ int tile(uint16_t *smem, int b, const CopyGeo &cg, const WorkCtx &x, int i, Src src,
+template <int BK, class G, int NBV, bool GELU, bool BIAS, bool F32OUT, bool PART, class X>
+__device__ __forceinline__ int tile(uint16_t *smem, int b, const CopyGeo &cg, const X &x, int i, Src src,
                                     int kt_lo, int kt_hi, Staged<BK, G> &stg, void *C, const uint16_t *bseg,
                                     float *part, int64_t row0, int64_t row_end, int n0, int N)
 {
@@ -762,14 +762,14 @@ __device__ __forceinline__ int tile(uint16_t *smem, int b, const CopyGeo &cg, co
     return b;
 }
 
-template <int BK, class G, bool GELU, bool BIAS, bool F32OUT, bool PART>
-__device__ __forceinline__ int tile_any(int nbv, uint16_t *smem, int b, const CopyGeo &cg, const WorkCtx &x, int i,
+template <int BK, class G, bool GELU, bool BIAS, bool F32OUT, bool PART, class X>
+__device__ __forceinline__ int tile_any(int nbv, uint16_t *smem, int b, const CopyGeo &cg, const X &x, int i,
                                         Src src, int kt_lo, int kt_hi, Staged<BK, G> &stg, void *C,
                                         const uint16_t *bseg, float *part, int64_t row0, int64_t row_end, int n0,
                                         int N)
 {
 #define MOE_TILE(V)                                                                                                 \
-    tile<BK, G, V, GELU, BIAS, F32OUT, PART>(smem, b, cg, x, i, src, kt_lo, kt_hi, stg, C, bseg, part, row0,       \
+    tile<BK, G, V, GELU, BIAS, F32OUT, PART, X>(smem, b, cg, x, i, src, kt_lo, kt_hi, stg, C, bseg, part, row0,    \
                                              row_end, n0, N)
     if (G::FB == 4) {
         switch (nbv) {
@@ -883,6 +883,266 @@ __global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_256(const uint16_t
                                                           nullptr, part_ws + (size_t)w.unit * (kL * kL), w.t.row0,
                                                           w.t.row_end, w.t.n0, N);
     }
+}
+
+// ---------------------------------------------------------------------------
+// K-segmented grouped GEMM (weight gradients): for every segment s,
+//   out_s[m, n] = sum_{k in segment s} A[m, k] W[n, k]      (fp32, [M, N])
+// with A [M, Kp] and W [N, Kp] holding the segments' columns at 64-aligned
+// offsets, zero-padded: segment s (rows_s rows of the forward) occupies
+// max(2, ceil(rows_s / 64)) K steps of 64 columns, none if it is empty; kcol
+// [S+1] holds the first step of each segment (kseg_layout).  Empty segments
+// get no tiles (their outputs are zeroed separately).  Same tile machinery
+// as grouped_gemm_256; no split-K tail.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int kseg_steps(int64_t rows) { return rows <= 0 ? 0 : (int)max<int64_t>(2, (rows + 63) / 64); }
+
+// kcol[s] = first K step of segment s, kcol[S] = total steps.  One wave.
+__global__ __launch_bounds__(64) void kseg_layout(const int32_t *__restrict__ seg, int S, int64_t max_rows,
+                                                  int32_t *__restrict__ kcol)
+{
+    const int lane = threadIdx.x;
+    int carry = 0;
+    for (int s0 = 0; s0 < S; s0 += 64) {
+        const int s = s0 + lane;
+        int v = 0;
+        if (s < S) {
+            int64_t lo, hi;
+            seg_bounds(seg, s, max_rows, lo, hi);
+            v = kseg_steps(hi - lo);
+        }
+        int inc = v;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(inc, o, 64);
+            if (lane >= o)
+                inc += u;
+        }
+        if (s < S)
+            kcol[s] = carry + inc - v;
+        carry += __shfl(inc, 63, 64);
+    }
+    if (lane == 0)
+        kcol[S] = carry;
+}
+
+// LDS copy of kcol and ne[s] = non-empty segments before s (ne[S] = total).
+__device__ void load_kseg_prefix(const int32_t *kcol, int S, int *kb, int *ne)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (wave == 0) {
+        int cn = 0;
+        for (int s0 = 0; s0 < S; s0 += 64) {
+            const int s = s0 + lane;
+            int vn = 0;
+            if (s < S) {
+                const int a = kcol[s], b = kcol[s + 1];
+                kb[s] = a;
+                vn = b > a ? 1 : 0;
+            }
+            int in = vn;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int un = __shfl_up(in, o, 64);
+                if (lane >= o)
+                    in += un;
+            }
+            if (s < S)
+                ne[s] = cn + in - vn;
+            cn += __shfl(in, 63, 64);
+        }
+        if (lane == 0) {
+            kb[S] = kcol[S];
+            ne[S] = cn;
+        }
+    }
+    __syncthreads();
+}
+
+struct KsegCtx {
+    const int *kb, *ne;
+    const uint16_t *A, *W;
+    int64_t first;
+    int S, M, N, Kp, MT, NT, per, nw, n_work;
+};
+
+// Work item i of the block: tile L = first + i * per of the list (non-empty
+// segments ascending, then feature tile, then row tile).
+__device__ __forceinline__ Work get_work(const KsegCtx &x, int i)
+{
+    const int64_t L = x.first + (int64_t)i * x.per;
+    const int per_seg = x.MT * x.NT;
+    const int q = (int)(L / per_seg); // index among the non-empty segments
+    // The last segment with ne[s] <= q is the q-th non-empty one: an empty
+    // segment is followed by one with the same ne, and the segments after
+    // the q-th non-empty one have ne > q.
+    int lo = 0, hi = x.S - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (x.ne[mid] <= q)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    const int local = (int)(L - (int64_t)q * per_seg);
+    Work w;
+    w.t.s = uni(lo);
+    w.t.n0 = uni((local / x.MT) * kL);
+    w.t.row0 = uni((local % x.MT) * kL);
+    w.t.row_end = uni((int)min<int64_t>(w.t.row0 + kL, x.M));
+    w.kt_lo = uni(x.kb[lo]);
+    w.kt_hi = uni(x.kb[lo + 1]);
+    w.unit = -1;
+    return w;
+}
+
+__device__ __forceinline__ Src src_of(const KsegCtx &x, const CopyGeo &cg, const Work &w)
+{
+    Src s;
+    s.wbase = (uint64_t)(uintptr_t)(x.W + (int64_t)w.t.n0 * x.Kp);
+    s.abase = (uint64_t)(uintptr_t)(x.A + w.t.row0 * x.Kp);
+    s.wbytes = (uint32_t)min(kL, x.N - w.t.n0) * cg.row_w;
+    s.abytes = (uint32_t)(w.t.row_end - w.t.row0) * cg.row_a;
+    return s;
+}
+
+template <int BK, class G>
+__global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_kseg(const uint16_t *__restrict__ A,
+                                                                   const uint16_t *__restrict__ W,
+                                                                   const int32_t *__restrict__ kcol, int S, int M,
+                                                                   int N, int Kp, float *__restrict__ C)
+{
+    constexpr int CPR = BK / 8, RPI = 64 / CPR;
+    constexpr int DPW = Staged<BK, G>::DPW;
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * kL * BK];
+    __shared__ int kb[kMaxSeg + 1], ne[kMaxSeg + 1];
+    load_kseg_prefix(kcol, S, kb, ne);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / G::WGN_;
+    KsegCtx x;
+    x.kb = kb;
+    x.ne = ne;
+    x.A = A;
+    x.W = W;
+    x.S = S;
+    x.M = M;
+    x.N = N;
+    x.Kp = Kp;
+    x.MT = (M + kL - 1) / kL;
+    x.NT = (N + kL - 1) / kL;
+    const int64_t total = (int64_t)ne[S] * x.MT * x.NT;
+    const int xcd = blockIdx.x % kXcds;
+    x.per = gridDim.x / kXcds;
+    const int64_t rlo = total * xcd / kXcds, rhi = total * (xcd + 1) / kXcds;
+    x.first = rlo + blockIdx.x / kXcds;
+    x.nw = x.first < rhi ? (int)((rhi - x.first + x.per - 1) / x.per) : 0;
+    x.n_work = x.nw;
+    if (x.n_work == 0)
+        return;
+
+    CopyGeo cg;
+    {
+        const int lrow = lane / CPR;
+        const int prow = wave * RPI + lrow;
+        const int lchunk = (lane % CPR) ^ swz(prow);
+        cg.row_w = (uint32_t)Kp * 2u;
+        cg.row_a = (uint32_t)Kp * 2u;
+        cg.vbase = (uint32_t)prow * cg.row_w + (uint32_t)lchunk * 16u;
+        cg.vbase_a = cg.vbase;
+        cg.KTa = Kp / BK;
+    }
+    Staged<BK, G> stg;
+    {
+        const Work w = get_work(x, 0);
+        const Src o = src_of(x, cg, w);
+        const Fill f0 = fill_k<BK>(o.wbase, o.abase, o.wbytes, o.abytes, w.kt_lo, cg.KTa);
+#pragma unroll
+        for (int i = 0; i < DPW; ++i)
+            stg.v[i] = copy_load<BK, G>(cg, f0, i);
+#pragma unroll
+        for (int i = 0; i < DPW; ++i)
+            *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(smem) + copy_ldsoff<BK, G>(wave, lane, i)) = stg.v[i];
+        const Fill f1 = fill_k<BK>(o.wbase, o.abase, o.wbytes, o.abytes, w.kt_lo + 1, cg.KTa);
+#pragma unroll
+        for (int i = 0; i < DPW; ++i)
+            stg.v[i] = copy_load<BK, G>(cg, f1, i);
+        stage_barrier<DPW>();
+    }
+    int b = 0;
+    for (int i = 0; i < x.n_work; ++i) {
+        const Work w = get_work(x, i);
+        const Src o = src_of(x, cg, w);
+        const int nbv = valid_b<G>(w.t, wm);
+        b = tile_any<BK, G, false, false, true, false>(nbv, smem, b, cg, x, i, o, w.kt_lo, w.kt_hi, stg,
+                                                       C + (int64_t)w.t.s * M * N, nullptr, nullptr, w.t.row0,
+                                                       w.t.row_end, w.t.n0, N);
+    }
+}
+
+// fp32 K-segmented GEMM: 64 x 64 output tiles of segment blockIdx.z, K
+// slices of 16 through LDS; an empty segment's tile is written as zeros.
+__global__ __launch_bounds__(256) void grouped_gemm_kseg_f32(const float *__restrict__ A,
+                                                             const float *__restrict__ W,
+                                                             const int32_t *__restrict__ kcol, int M, int N,
+                                                             int64_t Kp, float *__restrict__ C)
+{
+    constexpr int TM = 64, TN = 64, TK = 16;
+    __shared__ float sa[TK][TM + 4];
+    __shared__ float sw[TK][TN + 4];
+    const int s = blockIdx.z;
+    const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
+    const int64_t k_lo = (int64_t)kcol[s] * 64, k_hi = (int64_t)kcol[s + 1] * 64;
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    float acc[4][4] = {};
+    for (int64_t k0 = k_lo; k0 < k_hi; k0 += TK) {
+        for (int q = tid; q < TM * TK; q += 256) {
+            const int r = q / TK, kk = q % TK;
+            const int m = min(m0 + r, M - 1), n = min(n0 + r, N - 1);
+            sa[kk][r] = A[(int64_t)m * Kp + k0 + kk];
+            sw[kk][r] = W[(int64_t)n * Kp + k0 + kk];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < TK; ++kk) {
+            float av[4], wv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                av[i] = sa[kk][ty * 4 + i];
+                wv[i] = sw[kk][tx * 4 + i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc[i][q] = fmaf(av[i], wv[q], acc[i][q]);
+        }
+        __syncthreads();
+    }
+    float *out = C + (int64_t)s * M * N;
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + ty * 4 + i;
+        if (m >= M)
+            continue;
+        for (int q = 0; q < 4; ++q) {
+            const int n = n0 + tx * 4 + q;
+            if (n < N)
+                out[(int64_t)m * N + n] = acc[i][q];
+        }
+    }
+}
+
+// Zeroes out_s [MN] of every empty segment (the bf16 path gives them no tiles).
+__global__ __launch_bounds__(256) void kseg_zero_empty(const int32_t *__restrict__ kcol, int64_t MN,
+                                                       float *__restrict__ C)
+{
+    const int s = blockIdx.y;
+    if (kcol[s + 1] != kcol[s])
+        return;
+    float *out = C + (int64_t)s * MN;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < MN; i += (int64_t)gridDim.x * 256)
+        out[i] = 0.f;
 }
 
 // Sums the K-range partials of each tail tile in range order and applies the
@@ -1126,6 +1386,60 @@ moe_status_t launch_router_gemm(const void *x, const void *w3, int64_t T, int d,
     // logits3[T, 3E]: column p*E + e = x . (bf16 piece p of router row e)
     float *part = (ws && ws_bytes >= gemm_ws_bytes()) ? (float *)ws : nullptr;
     return run_large<false, false, true>(x, nullptr, 1, T, 3 * E, d, d, w3, nullptr, logits, part, stream);
+}
+
+int64_t kseg_cols_bound(int64_t max_rows, int S)
+{
+    // a non-empty segment of r rows takes max(2, ceil(r / 64)) <= ceil(r / 64) + 1
+    // steps, and sum_s ceil(r_s / 64) * 64 <= max_rows + 63 S
+    return (max_rows + 63) / 64 * 64 + 128 * (int64_t)S;
+}
+
+moe_status_t launch_kseg_layout(const int32_t *seg, int S, int64_t max_rows, int32_t *kcol, hipStream_t stream)
+{
+    kseg_layout<<<1, 64, 0, stream>>>(seg, S, max_rows, kcol);
+    return check_launch("kseg_layout");
+}
+
+moe_status_t launch_kseg_gemm(const void *A, const void *W, const int32_t *kcol, int S, int M, int N, int64_t Kp,
+                              moe_dtype_t dt, float *C, hipStream_t stream)
+{
+    if (S < 1 || M < 1 || N < 1)
+        return MOE_OK;
+    if (dt == MOE_F32) {
+        const dim3 g((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64), (unsigned)S);
+        grouped_gemm_kseg_f32<<<g, 256, 0, stream>>>((const float *)A, (const float *)W, kcol, M, N, Kp, C);
+        return check_launch("grouped_gemm_kseg_f32");
+    }
+    typedef LargeGrid G;
+    int64_t grid = (int64_t)device_cus();
+    grid = (grid + kXcds - 1) / kXcds * kXcds;
+    grouped_gemm_kseg<kLargeBK, G><<<(unsigned)grid, 64 * G::NW, 0, stream>>>(
+        (const uint16_t *)A, (const uint16_t *)W, kcol, S, M, N, (int)Kp, C);
+    if (moe_status_t st = check_launch("grouped_gemm_kseg"))
+        return st;
+    const int64_t MN = (int64_t)M * N;
+    const int64_t bx0 = (MN + 1023) / 1024, bx = bx0 < 64 ? bx0 : 64;
+    kseg_zero_empty<<<dim3((unsigned)bx, (unsigned)S), 256, 0, stream>>>(kcol, MN, C);
+    return check_launch("kseg_zero_empty");
+}
+
+moe_status_t launch_grouped_gemm_f32out(const void *a, const int32_t *seg_offsets, int num_segments,
+                                        int64_t max_rows, int N, int K, moe_dtype_t dt, const void *w,
+                                        const void *bias, float *out, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (max_rows == 0)
+        return MOE_OK;
+    const int S = seg_offsets ? num_segments : 1;
+    if (dt == MOE_BF16) {
+        float *part = (ws && ws_bytes >= gemm_ws_bytes()) ? (float *)ws : nullptr;
+        return bias ? run_large<false, true, true>(a, seg_offsets, S, max_rows, N, K, K, w, bias, out, part, stream)
+                    : run_large<false, false, true>(a, seg_offsets, S, max_rows, N, K, K, w, bias, out, part, stream);
+    }
+    const dim3 g((unsigned)((N + 63) / 64), (unsigned)((max_rows + 63) / 64 + S));
+    grouped_gemm_f32<false><<<g, 256, 0, stream>>>((const float *)a, seg_offsets, S, max_rows, (const float *)w,
+                                                    (const float *)bias, out, N, K);
+    return check_launch("grouped_gemm_f32");
 }
 
 } // namespace moe

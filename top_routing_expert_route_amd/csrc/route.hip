@@ -166,7 +166,7 @@ __global__ __launch_bounds__(64 * NW) void route_fused_small(const uint16_t *__r
                                                          const float *__restrict__ sel, int64_t T, int d, int E,
                                                          int k, int32_t *__restrict__ topk_idx,
                                                          float *__restrict__ topk_w, float *__restrict__ part_p,
-                                                         int32_t *__restrict__ part_c)
+                                                         int32_t *__restrict__ part_c, float *__restrict__ probs)
 {
     constexpr int EB = 16 * ET, TB = 16 * TT;
     constexpr int LS = EB + 1; // padded LDS row of one token's logits
@@ -313,6 +313,13 @@ __global__ __launch_bounds__(64 * NW) void route_fused_small(const uint16_t *__r
             row[e] = 0.f;
     }
     __syncthreads();
+    if (probs) {
+        for (int q = threadIdx.x; q < TB * E; q += 64 * NW) {
+            const int tq = q / E, e = q - tq * E;
+            if (t0 + tq < T)
+                probs[(t0 + tq) * E + e] = lg[tq * LS + e];
+        }
+    }
     // Block partials: probabilities summed in token order.
     if (threadIdx.x < E) {
         const int e = threadIdx.x;
@@ -388,7 +395,8 @@ __global__ __launch_bounds__(256) void route_select(const float *__restrict__ lo
                                                     const float *__restrict__ bias, const float *__restrict__ sel,
                                                     int64_t T, int E, int k,
                                                     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
-                                                    float *__restrict__ part_p, int32_t *__restrict__ part_c)
+                                                    float *__restrict__ part_p, int32_t *__restrict__ part_c,
+                                                    float *__restrict__ probs)
 {
     __shared__ float sp[4][EPL * 64];
     __shared__ int sc[4][EPL * 64];
@@ -435,6 +443,12 @@ __global__ __launch_bounds__(256) void route_select(const float *__restrict__ lo
 #pragma unroll
         for (int i = 0; i < EPL; ++i)
             pacc[i] += ex[i] * inv_s;
+        if (probs) {
+#pragma unroll
+            for (int i = 0; i < EPL; ++i)
+                if (lane + 64 * i < E)
+                    probs[t * E + lane + 64 * i] = ex[i] * inv_s;
+        }
 
         // top-k: k rounds of a wave arg-max on (score desc, id asc); the
         // score is the logit, plus the selection-only bias if given
@@ -600,7 +614,7 @@ size_t route_ws_bytes(int64_t T, int d, int E)
 moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, const float *b_router,
                           const float *sel_bias, int64_t T, int d, int E, int k, float alpha, int32_t *topk_idx,
                           float *topk_w,
-                          int32_t *expert_count, float *f, float *P, float *l_aux, void *ws,
+                          int32_t *expert_count, float *f, float *P, float *l_aux, float *probs, void *ws,
                           hipStream_t stream)
 {
     const int nblk = route_blocks(T, E, dt);
@@ -622,13 +636,13 @@ moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, 
             const dim3 g((unsigned)nblk);
             if (E <= 16)
                 route_fused_small<1, 1, 8, 8><<<g, 512, 0, stream>>>(xb, w_router, b_router, sel_bias, T, d, E, k, topk_idx,
-                                                                  topk_w, part_p, part_c);
+                                                                  topk_w, part_p, part_c, probs);
             else if (E <= 32)
                 route_fused_small<2, 2, 4, 8><<<g, 512, 0, stream>>>(xb, w_router, b_router, sel_bias, T, d, E, k, topk_idx,
-                                                                  topk_w, part_p, part_c);
+                                                                  topk_w, part_p, part_c, probs);
             else
                 route_fused_small<4, 2, 2, 8><<<g, 512, 0, stream>>>(xb, w_router, b_router, sel_bias, T, d, E, k, topk_idx,
-                                                                  topk_w, part_p, part_c);
+                                                                  topk_w, part_p, part_c, probs);
             if (moe_status_t s = check_launch("route_fused_small"))
                 return s;
         } else {
@@ -652,14 +666,14 @@ moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, 
             const int epl = (E + 63) / 64;
             const dim3 g((unsigned)nblk);
             switch (epl) {
-            case 1: route_select<1><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c); break;
-            case 2: route_select<2><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+            case 1: route_select<1><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs); break;
+            case 2: route_select<2><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs); break;
             case 3:
-            case 4: route_select<4><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+            case 4: route_select<4><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs); break;
             case 5: case 6: case 7: case 8:
-                route_select<8><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+                route_select<8><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs); break;
             default:
-                route_select<16><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c); break;
+                route_select<16><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs); break;
             }
             if (moe_status_t s = check_launch("route_select"))
                 return s;

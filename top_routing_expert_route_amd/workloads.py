@@ -237,6 +237,24 @@ def make_layer(w: Workload, seed: int = 0, threads: Optional[int] = None,
     return LayerInputs(w, x, w_router, b_router, w1, b1, w2, b2, ws1, bs1, ws2, bs2, sel_bias)
 
 
+def make_grad_output(w: Workload, seed: int = 0, threads: Optional[int] = None) -> np.ndarray:
+    """Seeded dL/dY [T, d] ~ N(0, 1) for the backward pass, in the layer's
+    storage dtype (uint16 bf16 bits or float32); drawn from its own seed
+    stream, so the layer's inputs do not depend on it."""
+    bf = w.dtype == BF16
+    dy = np.empty((w.T, w.d), dtype=np.uint16 if bf else np.float32)
+    jobs: list = []
+    _fill_gaussian(dy, np.random.SeedSequence([seed, 0x6772]), 1.0, bf, jobs)
+    n = threads or _threads()
+    if n > 1 and len(jobs) > 1:
+        with ThreadPoolExecutor(max_workers=n) as ex:
+            list(ex.map(lambda j: j(), jobs))
+    else:
+        for j in jobs:
+            j()
+    return dy
+
+
 def token_sample(T: int, n: int, seed: int = 1234, must_include=()) -> np.ndarray:
     """Sorted seeded sample of ``n`` distinct token ids (plus ``must_include``)."""
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, T, n])))
