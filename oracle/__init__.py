@@ -67,6 +67,11 @@ def _load():
                                         P, P, P, P, P, P, P, P, P,
                                         P, P, P, P, P, P, P, P, P, P, P, P, I]
         lib.oracle_backward.restype = I
+        lib.oracle_backward_tokens.argtypes = [P, I, i64, I, I, I, I, P, P, P, P, P, P, D, D, I, I,
+                                               P, P, P, P, P, P, P, P, P, P, i64, P, P, I]
+        lib.oracle_backward_tokens.restype = I
+        lib.oracle_ffn_grad_columns.argtypes = [P, I, i64, I, I, P, P, P, P, P, i64, P, P, I, P, P, P, P, I]
+        lib.oracle_ffn_grad_columns.restype = I
         _lib = lib
     return _lib
 
@@ -304,3 +309,61 @@ def backward(inp, dY: np.ndarray, g_aux: float = 0.0, threads: Optional[int] = N
     if rc != 0:
         raise ValueError("oracle_backward: invalid sizes (%d)" % rc)
     return g
+
+
+def backward_tokens(inp, dY: np.ndarray, tokens, g_aux: float = 0.0, threads: Optional[int] = None,
+                    topk_idx: Optional[np.ndarray] = None):
+    """dx [n, d] and dlogits [n, E] of the tokens ``tokens`` only, with the
+    arithmetic of ``backward`` (no weight gradients).  dY is the full [T, d]
+    gradient (only the listed rows are read)."""
+    w = inp.w
+    T, d, E, k, ffn = w.T, w.d, w.E, w.k, w.ffn
+    r = route(inp.x, inp.w_router, inp.b_router, k, threads=threads, sel_bias=getattr(inp, "sel_bias", None))
+    idx = r.topk_idx if topk_idx is None else np.ascontiguousarray(topk_idx, dtype=np.int32)
+    wts = np.ascontiguousarray(np.take_along_axis(r.probs, idx.astype(np.int64).clip(0, E - 1), axis=1))
+    st = load_stats(idx, r.probs, w.alpha)
+    dp = capacity(idx, E, float(np.float32(w.capacity_factor)), w.expert_begin, w.num_local_experts)
+    tok = np.ascontiguousarray(tokens, dtype=np.int64)
+    dx = np.empty((tok.size, d))
+    dl = np.empty((tok.size, E))
+    c = lambda a: None if a is None else np.ascontiguousarray(a)
+    rc = _load().oracle_backward_tokens(
+        _ptr(np.ascontiguousarray(inp.x)), _dtype_of(inp.x), T, d, E, k, ffn,
+        _ptr(np.ascontiguousarray(inp.w_router, dtype=np.float32)), _ptr(r.probs), _ptr(idx), _ptr(wts),
+        _ptr(dp.slot_row), _ptr(np.ascontiguousarray(st.f, dtype=np.float64)), float(w.alpha), float(g_aux),
+        w.expert_begin, w.E_loc, _ptr(c(inp.w1)), _ptr(c(inp.b1)), _ptr(c(inp.w2)), _ptr(c(inp.b2)),
+        _ptr(c(inp.ws1)), _ptr(c(inp.bs1)), _ptr(c(inp.ws2)), _ptr(c(inp.bs2)),
+        _ptr(np.ascontiguousarray(dY, dtype=np.float64)), _ptr(tok), tok.size, _ptr(dx), _ptr(dl),
+        _threads(threads))
+    if rc != 0:
+        raise ValueError("oracle_backward_tokens: invalid arguments (%d)" % rc)
+    return dx, dl
+
+
+@dataclass
+class FfnColumns:
+    dW1_rows: np.ndarray   # [nq, d]: rows qs of dW1
+    db1: np.ndarray        # [nq]
+    dW2_cols: np.ndarray   # [nq, d]: columns qs of dW2
+    db2: np.ndarray        # [d]
+
+
+def ffn_grad_columns(x: np.ndarray, w1: np.ndarray, b1, w2: np.ndarray, tokens, weights, dY: np.ndarray, qs,
+                     threads: Optional[int] = None) -> FfnColumns:
+    """Hidden features ``qs`` of one FFN's weight gradients (w1 [ffn, d],
+    w2 [d, ffn]) over the rows (tokens[r], output weight weights[r]); see
+    oracle_ffn_grad_columns."""
+    T, d = x.shape
+    ffn = w1.shape[0]
+    tok = np.ascontiguousarray(tokens, dtype=np.int64)
+    wt = np.ascontiguousarray(weights, dtype=np.float64)
+    q = np.ascontiguousarray(qs, dtype=np.int32)
+    out = FfnColumns(np.empty((q.size, d)), np.empty(q.size), np.empty((q.size, d)), np.empty(d))
+    c = lambda a: None if a is None else np.ascontiguousarray(a)
+    rc = _load().oracle_ffn_grad_columns(
+        _ptr(np.ascontiguousarray(x)), _dtype_of(x), T, d, ffn, _ptr(c(w1)), _ptr(c(b1)), _ptr(c(w2)), _ptr(tok),
+        _ptr(wt), tok.size, _ptr(np.ascontiguousarray(dY, dtype=np.float64)), _ptr(q), q.size, _ptr(out.dW1_rows),
+        _ptr(out.db1), _ptr(out.dW2_cols), _ptr(out.db2), _threads(threads))
+    if rc != 0:
+        raise ValueError("oracle_ffn_grad_columns: invalid arguments (%d)" % rc)
+    return out

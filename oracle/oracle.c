@@ -423,9 +423,12 @@ struct bwd_ctx {
     const void *w1, *b1, *w2, *b2, *ws1, *bs1, *ws2, *bs2;
     double g_aux, alpha;
     double *dx, *dlogits;
-    /* per-part private accumulators, summed in part order afterwards */
+    /* per-part private accumulators, summed in part order afterwards; NULL
+     * when only dx and dlogits of a token subset are wanted */
     int nparts;
     double **acc;
+    const int64_t *tokens; /* item i is token tokens[i] (NULL: token i) */
+    int64_t n_items;
 };
 
 /* sizes of the accumulator block of one part */
@@ -475,25 +478,30 @@ static double ffn_backward(const double *xt, int d, int ffn, int dtype, const vo
             dw += dYt[o] * v;
         }
     }
-    /* second Linear: dW2 += dv g^T, db2 += dv, dg = W2^T dv */
+    /* second Linear: dW2 += dv g^T, db2 += dv, dg = W2^T dv (the weight
+     * gradients are skipped when dW1 is NULL) */
     for (int q = 0; q < ffn; ++q)
         dg[q] = 0.0;
     for (int o = 0; o < d; ++o) {
         for (int q = 0; q < ffn; ++q) {
-            dW2[(int64_t)o * ffn + q] += dv[o] * g[q];
+            if (dW1)
+                dW2[(int64_t)o * ffn + q] += dv[o] * g[q];
             dg[q] += elem(w2, dtype, (int64_t)o * ffn + q) * dv[o];
         }
-        db2[o] += dv[o];
+        if (dW1)
+            db2[o] += dv[o];
     }
     /* GELU, then the first Linear: du = dg GELU'(u); dW1 += du x^T, db1 += du,
      * dx += W1^T du */
     for (int q = 0; q < ffn; ++q) {
         const double du = dg[q] * oracle_gelu_grad(u[q]);
         for (int i = 0; i < d; ++i) {
-            dW1[(int64_t)q * d + i] += du * xt[i];
+            if (dW1)
+                dW1[(int64_t)q * d + i] += du * xt[i];
             dxt[i] += elem(w1, dtype, (int64_t)q * d + i) * du;
         }
-        db1[q] += du;
+        if (dW1)
+            db1[q] += du;
     }
     return dw;
 }
@@ -508,9 +516,9 @@ static void bwd_range(void *p, int64_t t0, int64_t t1)
      * T (p+1) / n) to part p) */
     int part = 0;
     for (int q = 0; q < c->nparts; ++q)
-        if (c->T * q / c->nparts == t0)
+        if (c->n_items * q / c->nparts == t0)
             part = q;
-    double *A = c->acc[part];
+    double *A = c->acc ? c->acc[part] : NULL;
     double *xt = (double *)malloc(sizeof(double) * (size_t)d);
     double *dxt = (double *)malloc(sizeof(double) * (size_t)d);
     double *dv = (double *)malloc(sizeof(double) * (size_t)d);
@@ -519,7 +527,8 @@ static void bwd_range(void *p, int64_t t0, int64_t t1)
     double *dg = (double *)malloc(sizeof(double) * (size_t)ffn);
     double *dp = (double *)malloc(sizeof(double) * (size_t)E);
     const size_t es = c->dtype == ORACLE_DT_BF16 ? 2 : 4;
-    for (int64_t t = t0; t < t1; ++t) {
+    for (int64_t it = t0; it < t1; ++it) {
+        const int64_t t = c->tokens ? c->tokens[it] : it;
         const double *dYt = c->dY + t * d;
         const double *pt = c->probs + t * E;
         for (int i = 0; i < d; ++i) {
@@ -546,7 +555,8 @@ static void bwd_range(void *p, int64_t t0, int64_t t1)
             const double dw = ffn_backward(
                 xt, d, ffn, c->dtype, (const char *)c->w1 + w1o * es, c->b1 ? (const char *)c->b1 + b1o * es : NULL,
                 (const char *)c->w2 + w2o * es, c->b2 ? (const char *)c->b2 + b2o * es : NULL, dv, dYt, u, g, dg,
-                A + off[2] + w1o, A + off[3] + b1o, A + off[4] + w2o, A + off[5] + b2o, dxt);
+                A ? A + off[2] + w1o : NULL, A ? A + off[3] + b1o : NULL, A ? A + off[4] + w2o : NULL,
+                A ? A + off[5] + b2o : NULL, dxt);
             dp[e] += dw;
         }
         /* Router: w = softmax(logits)[e]; dl_i = p_i (dp_i - sum_e p_e dp_e). */
@@ -556,19 +566,22 @@ static void bwd_range(void *p, int64_t t0, int64_t t1)
         for (int e = 0; e < E; ++e) {
             const double dl = pt[e] * (dp[e] - sdot);
             if (c->dlogits)
-                c->dlogits[t * E + e] = dl;
-            A[off[1] + e] += dl;
+                c->dlogits[it * E + e] = dl;
+            if (A)
+                A[off[1] + e] += dl;
             for (int i = 0; i < d; ++i) {
-                A[off[0] + (int64_t)e * d + i] += dl * xt[i];
+                if (A)
+                    A[off[0] + (int64_t)e * d + i] += dl * xt[i];
                 dxt[i] += (double)c->w_router[(int64_t)e * d + i] * dl;
             }
         }
         /* Shared expert: weight 1 on every token. */
         if (c->ws1)
-            ffn_backward(xt, d, ffn, c->dtype, c->ws1, c->bs1, c->ws2, c->bs2, dYt, NULL, u, g, dg, A + off[6],
-                         A + off[7], A + off[8], A + off[9], dxt);
+            ffn_backward(xt, d, ffn, c->dtype, c->ws1, c->bs1, c->ws2, c->bs2, dYt, NULL, u, g, dg,
+                         A ? A + off[6] : NULL, A ? A + off[7] : NULL, A ? A + off[8] : NULL, A ? A + off[9] : NULL,
+                         dxt);
         for (int i = 0; i < d; ++i)
-            c->dx[t * d + i] = dxt[i];
+            c->dx[it * d + i] = dxt[i];
     }
     free(xt);
     free(dxt);
@@ -603,7 +616,7 @@ int oracle_backward(const void *x, int dtype, int64_t T, int d, int E, int k, in
     if (nthreads > T)
         nthreads = (int)T;
     struct bwd_ctx c = {x, dtype, T, d, E, k, ffn, e0, E_loc, w_router, probs, topk_w, f, dY, topk_idx, slot_row,
-                        w1, b1, w2, b2, ws1, bs1, ws2, bs2, g_aux, alpha, dx, dlogits, nthreads, NULL};
+                        w1, b1, w2, b2, ws1, bs1, ws2, bs2, g_aux, alpha, dx, dlogits, nthreads, NULL, NULL, T};
     int64_t off[10];
     const int64_t n = bwd_acc_size(&c, off);
     c.acc = (double **)malloc(sizeof(double *) * (size_t)nthreads);
@@ -630,5 +643,114 @@ int oracle_backward(const void *x, int dtype, int64_t T, int d, int E, int k, in
     for (int p = 0; p < nthreads; ++p)
         free(c.acc[p]);
     free(c.acc);
+    return 0;
+}
+
+/* dx and dlogits of the tokens tokens[0..n_tokens) only (rows i of dx
+ * [n_tokens, d] and dlogits [n_tokens, E]), with the same arithmetic as
+ * oracle_backward; no weight gradients.  Arguments otherwise as there. */
+int oracle_backward_tokens(const void *x, int dtype, int64_t T, int d, int E, int k, int ffn, const float *w_router,
+                           const double *probs, const int32_t *topk_idx, const double *topk_w,
+                           const int32_t *slot_row, const double *f, double alpha, double g_aux, int e0, int E_loc,
+                           const void *w1, const void *b1, const void *w2, const void *b2, const void *ws1,
+                           const void *bs1, const void *ws2, const void *bs2, const double *dY,
+                           const int64_t *tokens, int64_t n_tokens, double *dx, double *dlogits, int nthreads)
+{
+    if (T < 1 || d < 1 || E < 1 || k < 1 || ffn < 1 || e0 < 0 || E_loc < 1 || e0 + E_loc > E || n_tokens < 0)
+        return -1;
+    for (int64_t i = 0; i < n_tokens; ++i)
+        if (tokens[i] < 0 || tokens[i] >= T)
+            return -1;
+    if (n_tokens == 0)
+        return 0;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > n_tokens)
+        nthreads = (int)n_tokens;
+    struct bwd_ctx c = {x, dtype, T, d, E, k, ffn, e0, E_loc, w_router, probs, topk_w, f, dY, topk_idx, slot_row,
+                        w1, b1, w2, b2, ws1, bs1, ws2, bs2, g_aux, alpha, dx, dlogits, nthreads, NULL, tokens,
+                        n_tokens};
+    parallel_for(n_tokens, nthreads, bwd_range, &c);
+    return 0;
+}
+
+/* Columns of one FFN's weight gradients, from the definition restricted to
+ * feature q of the hidden layer.  The FFN (w1 [ffn,d], b1 [ffn] or NULL,
+ * w2 [d,ffn], nn.Linear layout, dtype of x) sees rows r = 0..n_rows-1:
+ * token tok[r] with output weight wt[r] (Y_t += wt v).  For each q = qs[j]:
+ *   u = w1[q,:] . x_t + b1[q],  dg = sum_o w2[o,q] dY[t,o],
+ *   du = wt dg GELU'(u)
+ *   dW1_row[j, :] = sum_r du x_t,   db1[j] = sum_r du,
+ *   dW2_col[j, o] = sum_r dY[t,o] wt GELU(u)    (column q of dW2)
+ * and db2 [d] = sum_r wt dY[t, :] (if not NULL).  Sums run in row order. */
+struct col_ctx {
+    const void *x, *w1, *b1, *w2;
+    int dtype, d, ffn;
+    const int64_t *tok;
+    const double *wt, *dY;
+    int64_t n_rows;
+    const int32_t *qs;
+    double *dW1_row, *db1, *dW2_col;
+};
+
+static void col_range(void *p, int64_t j0, int64_t j1)
+{
+    struct col_ctx *c = (struct col_ctx *)p;
+    const int d = c->d, F = c->ffn;
+    for (int64_t j = j0; j < j1; ++j) {
+        const int q = c->qs[j];
+        double *rw = c->dW1_row + j * d, *cw = c->dW2_col + j * d;
+        double sb = 0.0;
+        for (int i = 0; i < d; ++i)
+            rw[i] = cw[i] = 0.0;
+        for (int64_t r = 0; r < c->n_rows; ++r) {
+            const int64_t t = c->tok[r];
+            double u = c->b1 ? elem(c->b1, c->dtype, q) : 0.0;
+            for (int i = 0; i < d; ++i)
+                u += elem(c->w1, c->dtype, (int64_t)q * d + i) * elem(c->x, c->dtype, t * d + i);
+            double dg = 0.0;
+            for (int o = 0; o < d; ++o)
+                dg += elem(c->w2, c->dtype, (int64_t)o * F + q) * c->dY[t * d + o];
+            const double du = c->wt[r] * dg * oracle_gelu_grad(u);
+            const double gw = c->wt[r] * oracle_gelu(u);
+            for (int i = 0; i < d; ++i) {
+                rw[i] += du * elem(c->x, c->dtype, t * d + i);
+                cw[i] += c->dY[t * d + i] * gw;
+            }
+            sb += du;
+        }
+        c->db1[j] = sb;
+    }
+}
+
+int oracle_ffn_grad_columns(const void *x, int dtype, int64_t T, int d, int ffn, const void *w1, const void *b1,
+                            const void *w2, const int64_t *tok, const double *wt, int64_t n_rows, const double *dY,
+                            const int32_t *qs, int nq, double *dW1_row, double *db1, double *dW2_col, double *db2,
+                            int nthreads)
+{
+    if (T < 0 || d < 1 || ffn < 1 || n_rows < 0 || nq < 0)
+        return -1;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (tok[r] < 0 || tok[r] >= T)
+            return -1;
+    for (int j = 0; j < nq; ++j)
+        if (qs[j] < 0 || qs[j] >= ffn)
+            return -1;
+    if (db2) {
+        for (int o = 0; o < d; ++o) {
+            double s = 0.0;
+            for (int64_t r = 0; r < n_rows; ++r)
+                s += wt[r] * dY[tok[r] * d + o];
+            db2[o] = s;
+        }
+    }
+    if (nq == 0)
+        return 0;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > nq)
+        nthreads = nq;
+    struct col_ctx c = {x, w1, b1, w2, dtype, d, ffn, tok, wt, dY, n_rows, qs, dW1_row, db1, dW2_col};
+    parallel_for(nq, nthreads, col_range, &c);
     return 0;
 }

@@ -144,3 +144,62 @@ def test_backward_rejects_unsupported_bf16_shape():
     with pytest.raises(api.MoeError) as e:
         layer.backward(t["x"], dy, 0.0)
     assert e.value.status == api.MOE_ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------- full size --
+# The pages' workload shapes at full size, in the launch configuration of the
+# benchmark.  The oracle cannot produce every gradient at these sizes in
+# seconds, so it is sampled: dx and dlogits on a token sample, and hidden
+# features of two experts' (and the shared expert's) weight gradients.  The
+# router weight gradient is checked against its definition dW_r = dl^T x
+# on the GPU's own dlogits (which the token sample pins to the oracle).
+
+FULL = {w.name: w for w in wl.WORKLOADS[1:]}
+FULL_TOKENS = {"mixtral8x7b-layer": 24, "capacity-drop-zipf": 48, "fine-grained-e128-k8": 48,
+               "deepseekv3-share-32of256": 24}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_backward_full_size_sampled(name):
+    w = FULL[name]
+    g_aux = 0.7
+    inp, t, dy, dy_host, layer, outs, grads = _run(w, g_aux=g_aux)
+    gidx = outs["topk_idx"].cpu().numpy()
+    dY64 = _dy64(w, dy_host)
+    tol = TOL_Y_BF16 if w.dtype == wl.BF16 else TOL_Y_F32
+    slot_row = outs["slot_row"].cpu().numpy()
+    dropped = np.flatnonzero((slot_row == -1).any(1))
+    toks = wl.token_sample(w.T, FULL_TOKENS[name], seed=5, must_include=dropped[:2])
+    dx_ref, dl_ref = oracle.backward_tokens(inp, dY64, toks, g_aux, topk_idx=gidx)
+    dx = grads["dx"][torch.from_numpy(toks).to(DEV)].cpu().numpy()
+    dl_all = grads["dlogits"].cpu().numpy()
+    assert rel_err(dx, dx_ref) <= tol
+    assert rel_err(dl_all[toks], dl_ref) <= TOL_ROUTER
+    # router weight and bias gradients: the contraction of the GPU's dlogits
+    x64 = (wl.bf16_bits_to_f32(inp.x) if inp.x.dtype == np.uint16 else inp.x).astype(np.float64)
+    dl64 = dl_all.astype(np.float64)
+    assert rel_err(grads["dw_router"].cpu().numpy(), dl64.T @ x64) <= TOL_ROUTER
+    assert rel_err(grads["db_router"].cpu().numpy(), dl64.sum(0)) <= TOL_ROUTER
+    del x64, dl64
+    # sampled hidden features of the first and last non-empty local expert
+    r = oracle.route(inp.x, inp.w_router, inp.b_router, w.k, sel_bias=inp.sel_bias)
+    cap = oracle.capacity(gidx, w.E, float(np.float32(w.capacity_factor)), w.expert_begin, w.num_local_experts)
+    seg = cap.seg_offsets
+    nonempty = [le for le in range(w.E_loc) if seg[le + 1] > seg[le]]
+    qs = np.array([0, w.ffn // 2 + 3, w.ffn - 1])
+    for le in sorted({nonempty[0], nonempty[-1]}):
+        slots = cap.row_src[seg[le]:seg[le + 1]].astype(np.int64)
+        tk = slots // w.k
+        wts = r.probs[tk, gidx.reshape(-1)[slots]]
+        c = oracle.ffn_grad_columns(inp.x, inp.w1[le], None if inp.b1 is None else inp.b1[le], inp.w2[le], tk, wts,
+                                    dY64, qs)
+        assert rel_err(grads["dw1"][le][qs].cpu().numpy(), c.dW1_rows) <= tol, le
+        assert rel_err(grads["db1"][le][qs].cpu().numpy(), c.db1) <= tol, le
+        assert rel_err(grads["dw2"][le][:, qs].T.cpu().numpy(), c.dW2_cols) <= tol, le
+        assert rel_err(grads["db2"][le].cpu().numpy(), c.db2) <= tol, le
+    if w.shared_expert:
+        c = oracle.ffn_grad_columns(inp.x, inp.ws1, inp.bs1, inp.ws2, np.arange(w.T), np.ones(w.T), dY64, qs)
+        assert rel_err(grads["dws1"][qs].cpu().numpy(), c.dW1_rows) <= tol
+        assert rel_err(grads["dbs1"][qs].cpu().numpy(), c.db1) <= tol
+        assert rel_err(grads["dws2"][:, qs].T.cpu().numpy(), c.dW2_cols) <= tol
+        assert rel_err(grads["dbs2"].cpu().numpy(), c.db2) <= tol

@@ -94,3 +94,65 @@ def test_gelu_grad_matches_difference_quotient():
         h = 1e-5
         fd = (oracle.gelu(u + h) - oracle.gelu(u - h)) / (2 * h)
         assert abs(fd - oracle.gelu_grad(u)) < 1e-9
+
+
+SUBSET_CASES = {
+    "plain-bf16": dict(base=1, T=50, d=16, E=8, k=2, ffn=24, expert_bias="gauss"),
+    "share-shared": dict(base=4, T=60, d=16, E=16, k=4, ffn=20, num_local_experts=4, expert_begin=4,
+                         expert_bias="gauss", capacity_factor=1.5),
+}
+
+
+def _subset_case(name):
+    kw = dict(SUBSET_CASES[name])
+    base = kw.pop("base")
+    w = wl.scaled(wl.get(base), name="subset-" + name, **kw)
+    inp = wl.make_layer(w, seed=7)
+    rng = np.random.default_rng(9)
+    dY = rng.standard_normal((w.T, w.d))
+    return w, inp, dY
+
+
+@pytest.mark.parametrize("name", list(SUBSET_CASES))
+def test_backward_tokens_matches_full(name):
+    """The token-subset variant gives the full backward's dx and dlogits rows."""
+    w, inp, dY = _subset_case(name)
+    full = oracle.backward(inp, dY, 0.6)
+    toks = np.array([w.T - 1, 0, 17, 3, 17])
+    dx, dl = oracle.backward_tokens(inp, dY, toks, 0.6)
+    np.testing.assert_array_equal(dx, full.dx[toks])
+    np.testing.assert_array_equal(dl, full.dlogits[toks])
+
+
+@pytest.mark.parametrize("name", list(SUBSET_CASES))
+def test_ffn_grad_columns_match_full(name):
+    """Feature columns of the expert weight gradients, written from the
+    per-feature definition, agree with the full backward (a second, separately
+    written accumulation of the same sums)."""
+    w, inp, dY = _subset_case(name)
+    full = oracle.backward(inp, dY, 0.0)
+    r = oracle.route(inp.x, inp.w_router, inp.b_router, w.k)
+    cap = oracle.capacity(r.topk_idx, w.E, float(np.float32(w.capacity_factor)), w.expert_begin,
+                          w.num_local_experts)
+    qs = np.array([0, w.ffn - 1, 5, 11])
+    checked = 0
+    for le in range(w.E_loc):
+        lo, hi = int(cap.seg_offsets[le]), int(cap.seg_offsets[le + 1])
+        slots = cap.row_src[lo:hi].astype(np.int64)
+        toks = slots // w.k
+        wts = r.probs[toks, r.topk_idx.reshape(-1)[slots]]
+        c = oracle.ffn_grad_columns(inp.x, inp.w1[le], None if inp.b1 is None else inp.b1[le], inp.w2[le], toks,
+                                    wts, dY, qs)
+        np.testing.assert_allclose(c.dW1_rows, full.dW1[le][qs], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(c.db1, full.db1[le][qs], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(c.dW2_cols, full.dW2[le][:, qs].T, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(c.db2, full.db2[le], rtol=1e-12, atol=1e-12)
+        checked += hi > lo
+    assert checked >= 2
+    if inp.ws1 is not None:
+        toks = np.arange(w.T)
+        c = oracle.ffn_grad_columns(inp.x, inp.ws1, inp.bs1, inp.ws2, toks, np.ones(w.T), dY, qs)
+        np.testing.assert_allclose(c.dW1_rows, full.dWs1[qs], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(c.db1, full.dbs1[qs], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(c.dW2_cols, full.dWs2[:, qs].T, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(c.db2, full.dbs2, rtol=1e-12, atol=1e-12)
