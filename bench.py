@@ -96,6 +96,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip the moe_backward timing")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -251,6 +252,29 @@ def main():
                                                acc.PEAK_BF16_TFLOPS, 4)}
     staged_total = sum(avg_us.values())
 
+    # ---- backward: K steps of moe_backward on the same layer (dL/dY seeded
+    # Gaussian, dL/dL_aux = 1); reported beside the forward, not in `value` ----
+    backward = None
+    if not args.no_backward and not (w.dtype == wl.BF16 and (w.d % 64 or w.ffn % 64)):
+        dy = wl.to_torch(wl.make_grad_output(w, seed=0), dev)
+        grads = layer.backward(x, dy, 1.0)
+        for _ in range(args.warmup):
+            layer.backward(x, dy, 1.0, grads=grads)
+        torch.cuda.synchronize()
+        tb = time.perf_counter()
+        for _ in range(args.steps):
+            layer.backward(x, dy, 1.0, grads=grads)
+        torch.cuda.synchronize()
+        elb = time.perf_counter() - tb
+        bflops = acc.backward_gemm_flops(counts)
+        btf = bflops * args.steps / elb / 1e12
+        backward = {"entry_point": "moe_backward", "ms_per_step": round(elb * 1e3 / args.steps, 4),
+                    "value": round(w.T * args.steps / elb, 1), "unit": "tokens/s",
+                    "gemm_flops": bflops, "router_flops": acc.backward_router_flops(counts),
+                    "gemm_tflops_over_step": round(btf, 2),
+                    "mfma_frac_over_step": round(btf / acc.PEAK_BF16_TFLOPS, 4)}
+        del grads, dy
+
     result = {
         "metric": "MoE layer tokens/sec (1 GPU)",
         "value": round(tokens_per_s, 1),
@@ -278,6 +302,8 @@ def main():
     }
     if overlap is not None:
         result["shared_overlap"] = overlap
+    if backward is not None:
+        result["backward"] = backward
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(result))

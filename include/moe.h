@@ -323,6 +323,7 @@ moe_status_t moe_forward_overlap(const moe_problem_t *p, const moe_weights_t *w,
  * operands for MOE_BF16: the GELU-backward output and the hidden activation
  * are rounded to bf16 before their GEMMs); router, softmax and every
  * reduction in fp32.  Results are bitwise reproducible run to run.
+ * Every buffer is 16-byte aligned.
  * Sizes: as moe_forward; MOE_BF16 also needs d and ffn multiples of 64 and at
  * least 128 (else MOE_ERR_UNSUPPORTED).
  * ws: moe_backward_workspace_size(p) bytes.

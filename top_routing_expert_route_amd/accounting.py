@@ -98,3 +98,19 @@ def combine_bytes(c: RunCounts) -> int:
     if c.shared:
         b += c.T * c.d * s
     return b
+
+
+def backward_gemm_flops(c: RunCounts) -> int:
+    """Matrix-core work of one moe_backward: per FFN (routed rows, and the
+    shared expert over all tokens) five GEMMs of 2 * rows * d * ffn: the
+    recomputed first Linear, dh' = W2^T dY, dx = W1^T du, dW2 and dW1."""
+    f = 5 * 2 * c.rows * c.d * c.ffn
+    if c.shared:
+        f += 5 * 2 * c.T * c.d * c.ffn
+    return f
+
+
+def backward_router_flops(c: RunCounts) -> int:
+    """fp32 vector work of the router backward: dW_r = dl^T x and the dx term
+    dl W_r, 2 * T * E * d each (the router forward recompute is route_flops)."""
+    return 2 * 2 * c.T * c.E * c.d

@@ -527,9 +527,9 @@ moe_status_t ffn_backward(const moe_problem_t *p, const void *x, const void *dy,
     const int d = p->d, F = p->ffn;
     moe_status_t s = launch_kseg_layout(a.seg, a.S, a.rows, b.kcol, st);
     if (!s) // W1^T [S, d, F], W2^T [S, F, d]
-        s = launch_transpose_batched(a.w1, a.S, F, d, dt, b.w1t, st);
+        s = launch_transpose_batched(a.w1, a.S, F, d, a.seg, dt, b.w1t, st);
     if (!s)
-        s = launch_transpose_batched(a.w2, a.S, d, F, dt, b.w2t, st);
+        s = launch_transpose_batched(a.w2, a.S, d, F, a.seg, dt, b.w2t, st);
     if (!s) // u = W1 x + b1 (fp32)
         s = launch_grouped_gemm_f32out(a.a_rows, a.seg, a.S, a.rows, F, d, dt, a.w1, a.b1, b.u, b.gemm_ws,
                                        b.gemm_ws_bytes, st);
@@ -596,6 +596,13 @@ extern "C" moe_status_t moe_backward(const moe_problem_t *p, const moe_weights_t
         return fail(MOE_ERR_INVALID_ARG, "backward: dx, dw_router, dw1, dw2 (and dws1, dws2) are required");
     if (p->T > 0 && !dy)
         return fail(MOE_ERR_INVALID_ARG, "backward: dy is required");
+    {
+        const void *gp[] = {g->dx, g->dw_router, g->db_router, g->dw1, g->db1, g->dw2, g->db2,
+                            g->dws1, g->dbs1, g->dws2, g->dbs2, g->dlogits};
+        for (const void *q : gp)
+            if (!aligned16(q))
+                return fail(MOE_ERR_INVALID_ARG, "backward: gradient buffers must be 16-byte aligned");
+    }
     if (moe_status_t s = check_gemm_args(x, nullptr, 1, max_rows, p->ffn, p->d, p->dtype, w->w1, w->b1, 1, g->dx,
                                          "backward (first Linear)"))
         return s;

@@ -25,7 +25,8 @@
 // The weight-gradient GEMMs contract over dispatched rows, so their operands
 // are stored transposed in the K-segmented layout (kcol): row block s of
 // 64-aligned columns per segment, zero-padded.  The kernels here write those
-// operands straight from the row-major data through LDS tile transposes.
+// operands straight from the row-major data, transposing through LDS tiles
+// (gather_t) or in registers (act_bwd, the weight transposes).
 #include "common.hpp"
 
 namespace moe {
@@ -79,23 +80,72 @@ __device__ __forceinline__ int seg_of_tile(const int32_t *kcol, int S, int ct)
     return lo;
 }
 
-// dst[b, c, r] = src[b, r, c] for B matrices of R x C (64 x 64 LDS tiles).
-template <class T>
-__global__ __launch_bounds__(256) void transpose_batched(const T *__restrict__ src, int R, int C, T *__restrict__ dst)
+// 8 x 8 blocks of 16-bit values held as 8 rows of 16 bytes: out[j] element i
+// = in[i] element j.
+__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8])
 {
-    __shared__ float tile[64][65];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            // out[j] dword h = (in[2h] elem j, in[2h+1] elem j)
+            const uint32_t lo = in[2 * h][j >> 1], hi = in[2 * h + 1][j >> 1];
+            out[j][h] = (j & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+        }
+    }
+}
+
+// 4 x 4 blocks of 32-bit values.
+__device__ __forceinline__ void transpose4x4(const u32x4 (&in)[4], u32x4 (&out)[4])
+{
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            out[j][i] = in[i][j];
+}
+
+// dst[b, c, r] = src[b, r, c] for B matrices of R x C (R, C multiples of 8),
+// skipping matrix b when seg says segment b has no rows.  Each lane moves a
+// V x V block (V = 16 bytes / element size) with V 16-byte loads, an
+// in-register transpose and V 16-byte stores; a wave covers 8V x 8V with
+// 128-byte row segments on both sides.
+template <int ES>
+__global__ __launch_bounds__(256) void transpose_batched(const uint16_t *__restrict__ src, int R, int C,
+                                                         const int32_t *__restrict__ seg,
+                                                         uint16_t *__restrict__ dst)
+{
+    constexpr int V = 16 / ES, W = 8 * V; // wave tile edge in elements
     const int64_t b = blockIdx.z;
-    const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-    const T *s = src + b * R * C;
-    T *o = dst + b * R * C;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    for (int i = ty; i < 64; i += 4)
-        if (r0 + i < R && c0 + tx < C)
-            tile[i][tx] = Elt<T>::ld(s, (int64_t)(r0 + i) * C + c0 + tx);
-    __syncthreads();
-    for (int i = ty; i < 64; i += 4)
-        if (c0 + i < C && r0 + tx < R)
-            Elt<T>::st(o, (int64_t)(c0 + i) * R + r0 + tx, tile[tx][i]);
+    if (seg && seg[b + 1] <= seg[b])
+        return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int cg = lane & 7, rg = lane >> 3;
+    const int r0 = (blockIdx.y * 2 + (wave >> 1)) * W + rg * V;
+    const int c0 = (blockIdx.x * 2 + (wave & 1)) * W + cg * V;
+    if (r0 >= R || c0 >= C)
+        return;
+    const char *s = reinterpret_cast<const char *>(src) + (b * R * C) * ES;
+    char *o = reinterpret_cast<char *>(dst) + (b * R * C) * ES;
+    if (V == 8) {
+        u32x4 in[8], out[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            in[i] = *reinterpret_cast<const u32x4 *>(s + ((int64_t)(r0 + i) * C + c0) * ES);
+        transpose8x8(in, out);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            *reinterpret_cast<u32x4 *>(o + ((int64_t)(c0 + j) * R + r0) * ES) = out[j];
+    } else {
+        u32x4 in[4], out[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            in[i] = *reinterpret_cast<const u32x4 *>(s + ((int64_t)(r0 + i) * C + c0) * ES);
+        transpose4x4(in, out);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<u32x4 *>(o + ((int64_t)(c0 + j) * R + r0) * ES) = out[j];
+    }
 }
 
 // Gather of token rows into the K-segmented layout.  Column 64 kcol[s] + i
@@ -163,77 +213,127 @@ __global__ __launch_bounds__(256) void gather_t(const T *__restrict__ src, int D
 }
 
 // GELU backward over the K-segmented rows (same row/column map as gather_t),
-// from u = W1 x + b1 and dh' (both fp32 [rows, F]):
+// from u = W1 x + b1 and dh' (both fp32 [rows, F], F % 8 == 0):
 //   du[r, q]  = w_r dh'[r, q] GELU'(u[r, q])        (row-major, T)
 //   duT[q, col] = du[r, q],  gwT[q, col] = w_r GELU(u[r, q])   (zero padding)
 //   dwpart[r, qt] = sum_{q in feature tile qt} dh'[r, q] GELU(u[r, q])   (if dwpart)
-//   colpart[ct, q] = sum over the tile's rows of du[r, q]
-// w_r = wgt[row_src[r]] (1 when wgt is NULL).  Grid (ceil(F / 64), column tiles).
+//   colpart[ct, q] = sum over the tile's rows of du[r, q]               (if colpart)
+// w_r = wgt[row_src[r]] (1 when wgt is NULL).  A wave takes a 64-row column
+// tile x 64 features; each lane an 8 x 8 block (rows 8 rg.., features 8 cg..),
+// so row-major and transposed accesses are all 16-byte vectors.  Sums over a
+// tile's features / rows are fixed shuffle trees.  Grid (ceil(F / 256),
+// strided over the column tiles); FT = ceil(F / 64).
+template <class T> __device__ __forceinline__ void store8(T *p, const float (&v)[8]);
+template <> __device__ __forceinline__ void store8<uint16_t>(uint16_t *p, const float (&v)[8])
+{
+    u32x4 o;
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+        o[h] = pack_bf16x2(v[2 * h], v[2 * h + 1]);
+    *reinterpret_cast<u32x4 *>(p) = o;
+}
+template <> __device__ __forceinline__ void store8<float>(float *p, const float (&v)[8])
+{
+    *reinterpret_cast<f32x4 *>(p) = f32x4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4 *>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+}
+
 template <class T>
 __global__ __launch_bounds__(256) void act_bwd(const float *__restrict__ u, const float *__restrict__ dh, int F,
-                                               const int32_t *__restrict__ row_src, const float *__restrict__ wgt,
-                                               const int32_t *__restrict__ seg, int S, int64_t rows,
-                                               const int32_t *__restrict__ kcol, int64_t Kp, T *__restrict__ du,
-                                               T *__restrict__ duT, T *__restrict__ gwT, float *__restrict__ dwpart,
-                                               float *__restrict__ colpart)
+                                               int FT, const int32_t *__restrict__ row_src,
+                                               const float *__restrict__ wgt, const int32_t *__restrict__ seg, int S,
+                                               int64_t rows, const int32_t *__restrict__ kcol, int64_t Kp,
+                                               T *__restrict__ du, T *__restrict__ duT, T *__restrict__ gwT,
+                                               float *__restrict__ dwpart, float *__restrict__ colpart)
 {
-    __shared__ float t_du[64][65], t_gw[64][65];
-    __shared__ float s_w[64];
-    __shared__ int s_ok[64];
-    __shared__ float s_cs[4][64];
-    const int q0 = blockIdx.x * 64;
-    const int FT = gridDim.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int cg = lane & 7, rg = lane >> 3;
+    const int qt = blockIdx.x * 4 + wave;
+    const int q0 = qt * 64 + cg * 8;
+    if (qt * 64 >= F)
+        return; // whole wave; there is no barrier below
+    // lanes past F (F % 64 != 0) take part in the shuffles with zeros
+    const bool qv = q0 < F;
     const int total = kcol[S];
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    const int q = q0 + tx;
     for (int ct = blockIdx.y; ct < total; ct += gridDim.y) {
         const int s = seg_of_tile(kcol, S, ct);
         int64_t lo, hi;
         seg_rows(seg, s, rows, lo, hi);
-        const int64_t rbase = lo + (int64_t)(ct - kcol[s]) * 64;
-        if (threadIdx.x < 64) {
-            const int64_t r = rbase + threadIdx.x;
-            const bool ok = r < hi;
-            s_ok[threadIdx.x] = ok ? 1 : 0;
-            s_w[threadIdx.x] = ok ? (wgt ? wgt[row_src ? row_src[r] : r] : 1.f) : 0.f;
-        }
-        __syncthreads();
-        float cs = 0.f;
-        for (int i = ty; i < 64; i += 4) {
-            const int64_t r = rbase + i;
-            const bool ok = s_ok[i] != 0;
-            float vdu = 0.f, vgw = 0.f, dwp = 0.f;
-            if (ok && q < F) {
-                const float uu = u[r * F + q], hh = dh[r * F + q];
+        const int64_t r0 = lo + (int64_t)(ct - kcol[s]) * 64 + rg * 8;
+        float vdu[8][8], vgw[8][8], rs[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t r = r0 + i;
+            const bool ok = r < hi && qv;
+            const float w = ok ? (wgt ? wgt[row_src ? row_src[r] : r] : 1.f) : 0.f;
+            f32x4 ua = {0.f, 0.f, 0.f, 0.f}, ub = ua, ha = ua, hb = ua;
+            if (ok) {
+                const f32x4 *pu = reinterpret_cast<const f32x4 *>(u + r * F + q0);
+                const f32x4 *ph = reinterpret_cast<const f32x4 *>(dh + r * F + q0);
+                ua = pu[0];
+                ub = pu[1];
+                ha = ph[0];
+                hb = ph[1];
+            }
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float uu = j < 4 ? ua[j] : ub[j - 4], hh = j < 4 ? ha[j] : hb[j - 4];
                 float g, gp;
                 gelu_and_grad(uu, g, gp);
-                const float w = s_w[i];
-                vdu = w * hh * gp;
-                vgw = w * g;
-                dwp = hh * g;
-                Elt<T>::st(du, r * F + q, vdu);
+                vdu[i][j] = ok ? w * hh * gp : 0.f;
+                vgw[i][j] = ok ? w * g : 0.f;
+                acc = fmaf(hh, g, acc);
             }
-            cs += vdu;
-            t_du[i][tx] = vdu;
-            t_gw[i][tx] = vgw;
-            if (dwpart) {
-                dwp = wave_sum(dwp);
-                if (tx == 0 && ok)
-                    dwpart[r * FT + blockIdx.x] = dwp;
+            rs[i] = ok ? acc : 0.f;
+            if (ok)
+                store8<T>(du + r * F + q0, vdu[i]);
+        }
+        if (dwpart) {
+            // row sums over the tile's 64 features: the 8 lanes of a row group
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float v = rs[i];
+                v += __shfl_xor(v, 1, 64);
+                v += __shfl_xor(v, 2, 64);
+                v += __shfl_xor(v, 4, 64);
+                rs[i] = v;
+            }
+            if (cg == 0) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (r0 + i < hi)
+                        dwpart[(r0 + i) * FT + qt] = rs[i];
             }
         }
-        s_cs[ty][tx] = cs;
-        __syncthreads();
-        if (colpart && ty == 0 && q < F)
-            colpart[(int64_t)ct * F + q] = ((s_cs[0][tx] + s_cs[1][tx]) + s_cs[2][tx]) + s_cs[3][tx];
-        const int64_t col = (int64_t)ct * 64 + tx;
-        for (int i = ty; i < 64; i += 4) {
-            if (q0 + i < F) {
-                Elt<T>::st(duT, (int64_t)(q0 + i) * Kp + col, t_du[tx][i]);
-                Elt<T>::st(gwT, (int64_t)(q0 + i) * Kp + col, t_gw[tx][i]);
+        if (colpart) {
+            // column sums over the tile's 64 rows: the 8 lanes of a feature group
+            float cs[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float v = ((vdu[0][j] + vdu[1][j]) + (vdu[2][j] + vdu[3][j])) +
+                          ((vdu[4][j] + vdu[5][j]) + (vdu[6][j] + vdu[7][j]));
+                v += __shfl_xor(v, 8, 64);
+                v += __shfl_xor(v, 16, 64);
+                v += __shfl_xor(v, 32, 64);
+                cs[j] = v;
             }
+            if (rg == 0 && qv)
+                store8<float>(colpart + (int64_t)ct * F + q0, cs);
         }
-        __syncthreads();
+        // transposed: feature row q0 + j, columns 64 ct + 8 rg .. + 8
+        const int64_t col = (int64_t)ct * 64 + rg * 8;
+#pragma unroll
+        for (int j = 0; j < 8 && qv; ++j) {
+            float a[8], g8[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                a[i] = vdu[i][j];
+                g8[i] = vgw[i][j];
+            }
+            store8<T>(duT + (int64_t)(q0 + j) * Kp + col, a);
+            store8<T>(gwT + (int64_t)(q0 + j) * Kp + col, g8);
+        }
     }
 }
 
@@ -462,14 +562,15 @@ moe_status_t launch_fill_zero(float *p, int64_t n, hipStream_t stream)
     return check_launch("fill_zero");
 }
 
-moe_status_t launch_transpose_batched(const void *src, int B, int R, int C, moe_dtype_t dt, void *dst,
-                                      hipStream_t stream)
+moe_status_t launch_transpose_batched(const void *src, int B, int R, int C, const int32_t *seg, moe_dtype_t dt,
+                                      void *dst, hipStream_t stream)
 {
-    const dim3 g((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64), (unsigned)B);
+    const int W = dt == MOE_BF16 ? 64 : 32; // wave tile; a block is 2 x 2 waves
+    const dim3 g((unsigned)((C + 2 * W - 1) / (2 * W)), (unsigned)((R + 2 * W - 1) / (2 * W)), (unsigned)B);
     if (dt == MOE_BF16)
-        transpose_batched<uint16_t><<<g, 256, 0, stream>>>((const uint16_t *)src, R, C, (uint16_t *)dst);
+        transpose_batched<2><<<g, 256, 0, stream>>>((const uint16_t *)src, R, C, seg, (uint16_t *)dst);
     else
-        transpose_batched<float><<<g, 256, 0, stream>>>((const float *)src, R, C, (float *)dst);
+        transpose_batched<4><<<g, 256, 0, stream>>>((const uint16_t *)src, R, C, seg, (uint16_t *)dst);
     return check_launch("transpose_batched");
 }
 
@@ -494,13 +595,14 @@ moe_status_t launch_act_bwd(const float *u, const float *dh, int F, const int32_
                             void *du, void *duT, void *gwT, float *dwpart, float *colpart, hipStream_t stream)
 {
     const int64_t ctiles = Kp / 64;
-    const int fx = (F + 63) / 64;
-    const dim3 g((unsigned)fx, strided_grid(ctiles, (8192 + fx - 1) / fx));
+    const int fx = (F + 255) / 256;
+    const int FT = (F + 63) / 64;
+    const dim3 g((unsigned)fx, strided_grid(ctiles, (4096 + fx - 1) / fx));
     if (dt == MOE_BF16)
-        act_bwd<uint16_t><<<g, 256, 0, stream>>>(u, dh, F, row_src, wgt, seg, S, rows, kcol, Kp, (uint16_t *)du,
+        act_bwd<uint16_t><<<g, 256, 0, stream>>>(u, dh, F, FT, row_src, wgt, seg, S, rows, kcol, Kp, (uint16_t *)du,
                                                  (uint16_t *)duT, (uint16_t *)gwT, dwpart, colpart);
     else
-        act_bwd<float><<<g, 256, 0, stream>>>(u, dh, F, row_src, wgt, seg, S, rows, kcol, Kp, (float *)du,
+        act_bwd<float><<<g, 256, 0, stream>>>(u, dh, F, FT, row_src, wgt, seg, S, rows, kcol, Kp, (float *)du,
                                               (float *)duT, (float *)gwT, dwpart, colpart);
     return check_launch("act_bwd");
 }

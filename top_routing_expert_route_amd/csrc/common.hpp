@@ -146,8 +146,10 @@ moe_status_t launch_combine(const void *y_perm, int64_t max_rows, const int32_t 
 // Backward-pass kernels (backward.hip); the K-segmented layout and column
 // map are those of launch_kseg_layout.
 moe_status_t launch_fill_zero(float *p, int64_t n, hipStream_t stream);
-moe_status_t launch_transpose_batched(const void *src, int B, int R, int C, moe_dtype_t dt, void *dst,
-                                      hipStream_t stream);
+// dst[b] = src[b]^T for B matrices of R x C (multiples of 8); matrix b is
+// skipped when seg (may be NULL) gives segment b no rows.
+moe_status_t launch_transpose_batched(const void *src, int B, int R, int C, const int32_t *seg, moe_dtype_t dt,
+                                      void *dst, hipStream_t stream);
 moe_status_t launch_gather_t(const void *src, int D, const int32_t *row_src, int k, const float *wgt,
                              const int32_t *seg, int S, int64_t rows, const int32_t *kcol, int64_t Kp, moe_dtype_t dt,
                              void *dstT, void *dst, float *colpart, hipStream_t stream);

@@ -292,12 +292,14 @@ constexpr int kL = 256; // tile edge
 // Word 3 of a raw (unformatted, stride 0) buffer resource on gfx9-family GPUs.
 constexpr int kRsrcWord3 = 0x00020000;
 
-// This wave's loads except the newest N have completed, every wave got that
-// far, and every wave's LDS accesses issued so far have completed.
-template <int N> __device__ __forceinline__ void stage_barrier()
+// Every wave got this far and every wave's LDS accesses issued so far have
+// completed.  Global loads are not waited for here: the staged registers
+// reach LDS through ds_writes, before which the compiler waits for the loads
+// that filled them, so outstanding epilogue stores of the previous tile do
+// not hold up the pipeline.
+__device__ __forceinline__ void lds_barrier()
 {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 }
 
 // Logical 16-byte chunk stored at physical chunk p of a 64-element row.
@@ -637,7 +639,7 @@ __device__ __forceinline__ void k_step(const uint16_t *cur, uint16_t *nxt, const
         if (ks == KS - 2) {
             // nxt complete; the register loads of step kt+2 stay in flight
             __builtin_amdgcn_sched_barrier(0);
-            stage_barrier<DPW>();
+            lds_barrier();
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -867,7 +869,7 @@ __global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_256(const uint16_t
 #pragma unroll
         for (int i = 0; i < DPW; ++i)
             stg.v[i] = copy_load<BK, G>(cg, f1, i);
-        stage_barrier<DPW>();
+        lds_barrier();
     }
     int b = 0;
     for (int i = 0; i < x.n_work; ++i) {
@@ -964,10 +966,13 @@ struct KsegCtx {
     const uint16_t *A, *W;
     int64_t first;
     int S, M, N, Kp, MT, NT, per, nw, n_work;
+    bool n_inner; // consecutive tiles walk the feature tiles (M > N)
 };
 
 // Work item i of the block: tile L = first + i * per of the list (non-empty
-// segments ascending, then feature tile, then row tile).
+// segments ascending, then the tiles of the larger operand, then those of the
+// smaller one, so that consecutive tiles share a tile of the larger operand
+// and only the smaller one is re-read).
 __device__ __forceinline__ Work get_work(const KsegCtx &x, int i)
 {
     const int64_t L = x.first + (int64_t)i * x.per;
@@ -985,24 +990,30 @@ __device__ __forceinline__ Work get_work(const KsegCtx &x, int i)
             hi = mid - 1;
     }
     const int local = (int)(L - (int64_t)q * per_seg);
+    const int row0 = (x.n_inner ? local / x.NT : local % x.MT) * kL;
+    const int n0 = (x.n_inner ? local % x.NT : local / x.MT) * kL;
+    const int row_end = row0 + kL < x.M ? row0 + kL : x.M;
     Work w;
     w.t.s = uni(lo);
-    w.t.n0 = uni((local / x.MT) * kL);
-    w.t.row0 = uni((local % x.MT) * kL);
-    w.t.row_end = uni((int)min<int64_t>(w.t.row0 + kL, x.M));
+    w.t.n0 = uni(n0);
+    w.t.row0 = uni(row0);
+    w.t.row_end = uni(row_end);
     w.kt_lo = uni(x.kb[lo]);
     w.kt_hi = uni(x.kb[lo + 1]);
     w.unit = -1;
     return w;
 }
 
+// All fields wave-uniform (the buffer descriptors must be scalar).
 __device__ __forceinline__ Src src_of(const KsegCtx &x, const CopyGeo &cg, const Work &w)
 {
     Src s;
-    s.wbase = (uint64_t)(uintptr_t)(x.W + (int64_t)w.t.n0 * x.Kp);
-    s.abase = (uint64_t)(uintptr_t)(x.A + w.t.row0 * x.Kp);
-    s.wbytes = (uint32_t)min(kL, x.N - w.t.n0) * cg.row_w;
-    s.abytes = (uint32_t)(w.t.row_end - w.t.row0) * cg.row_a;
+    const int n0 = (int)w.t.n0, row0 = (int)w.t.row0, rows = (int)(w.t.row_end - w.t.row0);
+    const int nw = x.N - n0 < kL ? x.N - n0 : kL;
+    s.wbase = (uint64_t)uni64((int64_t)(uintptr_t)(x.W + (int64_t)n0 * x.Kp));
+    s.abase = (uint64_t)uni64((int64_t)(uintptr_t)(x.A + (int64_t)row0 * x.Kp));
+    s.wbytes = (uint32_t)uni(nw * (int)cg.row_w);
+    s.abytes = (uint32_t)uni(rows * (int)cg.row_a);
     return s;
 }
 
@@ -1032,6 +1043,7 @@ __global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_kseg(const uint16_
     x.Kp = Kp;
     x.MT = (M + kL - 1) / kL;
     x.NT = (N + kL - 1) / kL;
+    x.n_inner = M > N;
     const int64_t total = (int64_t)ne[S] * x.MT * x.NT;
     const int xcd = blockIdx.x % kXcds;
     x.per = gridDim.x / kXcds;
@@ -1068,15 +1080,14 @@ __global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_kseg(const uint16_
 #pragma unroll
         for (int i = 0; i < DPW; ++i)
             stg.v[i] = copy_load<BK, G>(cg, f1, i);
-        stage_barrier<DPW>();
+        lds_barrier();
     }
     int b = 0;
     for (int i = 0; i < x.n_work; ++i) {
         const Work w = get_work(x, i);
         const Src o = src_of(x, cg, w);
-        const int nbv = valid_b<G>(w.t, wm);
-        b = tile_any<BK, G, false, false, true, false>(nbv, smem, b, cg, x, i, o, w.kt_lo, w.kt_hi, stg,
-                                                       C + (int64_t)w.t.s * M * N, nullptr, nullptr, w.t.row0,
+        b = tile_any<BK, G, false, false, true, false>(valid_b<G>(w.t, wm), smem, b, cg, x, i, o, w.kt_lo, w.kt_hi,
+                                                       stg, C + (int64_t)w.t.s * M * N, nullptr, nullptr, w.t.row0,
                                                        w.t.row_end, w.t.n0, N);
     }
 }
@@ -1133,16 +1144,18 @@ __global__ __launch_bounds__(256) void grouped_gemm_kseg_f32(const float *__rest
     }
 }
 
-// Zeroes out_s [MN] of every empty segment (the bf16 path gives them no tiles).
+// Zeroes out_s [MN] (MN % 4 == 0) of every empty segment (the bf16 path gives
+// them no tiles), 16 bytes per store.
 __global__ __launch_bounds__(256) void kseg_zero_empty(const int32_t *__restrict__ kcol, int64_t MN,
                                                        float *__restrict__ C)
 {
     const int s = blockIdx.y;
     if (kcol[s + 1] != kcol[s])
         return;
-    float *out = C + (int64_t)s * MN;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < MN; i += (int64_t)gridDim.x * 256)
-        out[i] = 0.f;
+    f32x4 *out = reinterpret_cast<f32x4 *>(C + (int64_t)s * MN);
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < MN / 4; i += (int64_t)gridDim.x * 256)
+        out[i] = z;
 }
 
 // Sums the K-range partials of each tail tile in range order and applies the
@@ -1419,7 +1432,7 @@ moe_status_t launch_kseg_gemm(const void *A, const void *W, const int32_t *kcol,
     if (moe_status_t st = check_launch("grouped_gemm_kseg"))
         return st;
     const int64_t MN = (int64_t)M * N;
-    const int64_t bx0 = (MN + 1023) / 1024, bx = bx0 < 64 ? bx0 : 64;
+    const int64_t bx0 = (MN / 4 + 255) / 256, bx = bx0 < 256 ? bx0 : 256;
     kseg_zero_empty<<<dim3((unsigned)bx, (unsigned)S), 256, 0, stream>>>(kcol, MN, C);
     return check_launch("kseg_zero_empty");
 }
