@@ -444,8 +444,8 @@ extern "C" moe_status_t moe_forward_overlap(const moe_problem_t *p, const moe_we
 // ------------------------------------------------------------------ backward
 namespace {
 
-// Workspace of moe_backward.  The shared expert runs first and leaves only
-// dx_sh; the routed experts then reuse its buffers (rows = max(routed rows,
+// Workspace of moe_backward.  The shared expert runs first and writes its dx
+// straight into the caller's dx; the routed experts then reuse its buffers (rows = max(routed rows,
 // T), transposed weights for max(E_loc, 1) experts).
 struct BackwardWs {
     int32_t *topk_idx, *expert_count, *seg_offsets, *kept_count, *slot_row, *row_src, *kcol;
@@ -453,10 +453,17 @@ struct BackwardWs {
     void *route_ws, *dispatch_ws, *gemm_ws, *router_ws;
     size_t gemm_ws_bytes;
     void *x_perm, *dyp, *du, *w1t, *w2t, *xT, *dyT, *duT, *gwT;
-    float *u, *dh, *dx_rows, *dx_sh, *dwpart, *colpart;
+    float *u, *dh, *dx_rows, *dwpart, *colpart;
     int64_t Kp;
     size_t bytes;
 };
+
+// The router backward runs on the matrix cores for bf16 layers with many
+// experts (its fp32 vector form costs 2 T E d FMAs twice).
+bool router_on_mfma(const moe_problem_t *p)
+{
+    return p->dtype == MOE_BF16 && p->E >= 32 && p->E % 8 == 0 && p->d % 64 == 0;
+}
 
 BackwardWs carve_backward(const moe_problem_t *p, const moe_grads_t *g, void *base)
 {
@@ -486,7 +493,11 @@ BackwardWs carve_backward(const moe_problem_t *p, const moe_grads_t *g, void *ba
     w.dispatch_ws = cv.take<char>(dispatch_ws_bytes(p->T, p->k, E_loc));
     w.gemm_ws_bytes = p->dtype == MOE_BF16 ? gemm_ws_bytes() : 0;
     w.gemm_ws = cv.take<char>(w.gemm_ws_bytes);
-    w.router_ws = cv.take<char>(router_wgrad_ws_bytes(p->T, p->d, p->E));
+    {
+        const size_t a = router_wgrad_ws_bytes(p->T, p->d, p->E);
+        const size_t m = router_on_mfma(p) ? router_mfma_ws_bytes(p->T, p->d, p->E) : 0;
+        w.router_ws = cv.take<char>(a > m ? a : m);
+    }
     w.x_perm = cv.take<char>((size_t)max_rows * p->d * es);
     w.dyp = cv.take<char>((size_t)max_rows * p->d * es);
     w.du = cv.take<char>((size_t)rows * p->ffn * es);
@@ -499,7 +510,6 @@ BackwardWs carve_backward(const moe_problem_t *p, const moe_grads_t *g, void *ba
     w.u = cv.take<float>((size_t)rows * p->ffn);
     w.dh = cv.take<float>((size_t)rows * p->ffn);
     w.dx_rows = cv.take<float>((size_t)rows * p->d);
-    w.dx_sh = p->has_shared ? cv.take<float>((size_t)p->T * p->d) : nullptr;
     w.dwpart = cv.take<float>((size_t)max_rows * ((p->ffn + 63) / 64));
     const int64_t maxdim = p->d > p->ffn ? p->d : p->ffn;
     w.colpart = cv.take<float>((size_t)(w.Kp / 64) * maxdim);
@@ -653,7 +663,7 @@ extern "C" moe_status_t moe_backward(const moe_problem_t *p, const moe_weights_t
         a.db1 = g->dbs1;
         a.dw2 = g->dws2;
         a.db2 = g->dbs2;
-        a.dx_rows = b.dx_sh;
+        a.dx_rows = g->dx; // the routed rows and the router term are added in place
         s = ffn_backward(p, x, dy, a, b, stream);
     }
     if (!s) {
@@ -675,14 +685,20 @@ extern "C" moe_status_t moe_backward(const moe_problem_t *p, const moe_weights_t
         a.dwpart = b.dwpart;
         s = ffn_backward(p, x, dy, a, b, stream);
     }
-    if (!s) {
-        const float c_aux = (float)((double)g_aux * (double)p->alpha / (double)T);
+    const float c_aux = (float)((double)g_aux * (double)p->alpha / (double)T);
+    float *dx_r = nullptr;
+    if (!s && router_on_mfma(p)) {
+        s = launch_router_bwd_mfma(b.probs, b.topk_idx, b.slot_row, b.dwpart, (F + 63) / 64, w->b2, dy, d,
+                                   p->expert_begin, b.f, c_aux, T, E, p->k, x, w->w_router, b.dl, g->dw_router,
+                                   g->db_router, &dx_r, b.router_ws, b.gemm_ws, b.gemm_ws_bytes, stream);
+    } else if (!s) {
         s = launch_router_bwd(b.probs, b.topk_idx, b.slot_row, b.dwpart, (F + 63) / 64, w->b2, dy, p->dtype, d,
                               p->expert_begin, b.f, c_aux, T, E, p->k, b.dl, stream);
+        if (!s)
+            s = launch_router_wgrad(x, p->dtype, b.dl, T, d, E, g->dw_router, g->db_router, b.router_ws, stream);
     }
     if (!s)
-        s = launch_router_wgrad(x, p->dtype, b.dl, T, d, E, g->dw_router, g->db_router, b.router_ws, stream);
-    if (!s)
-        s = launch_dx_combine(b.dx_rows, b.slot_row, p->k, b.dx_sh, b.dl, w->w_router, T, d, E, g->dx, stream);
+        s = launch_dx_combine(b.dx_rows, b.slot_row, p->k, p->has_shared ? g->dx : nullptr, dx_r, b.dl,
+                              w->w_router, T, d, E, g->dx, stream);
     return s;
 }

@@ -150,79 +150,35 @@ __global__ __launch_bounds__(256) void transpose_batched(const uint16_t *__restr
 
 // Gather of token rows into the K-segmented layout.  Column 64 kcol[s] + i
 // holds row r = lo_s + i of segment s (token t = row_src[r] / k, or r when
-// row_src is NULL); columns past the segment's rows are zero.
+// row_src is NULL); columns past the segment's rows are zero.  D % 8 == 0.
 //   dstT[f, col]     = src[t, f]
 //   dst[r, f]        = src[t, f]                      (if dst)
 //   colpart[ct, f]   = sum over the tile's rows of wgt[row_src[r]] src[t, f]
 //                      (wgt NULL: weight 1)           (if colpart)
-// Grid (feature tiles of 64, strided over the column tiles).
-template <class T>
-__global__ __launch_bounds__(256) void gather_t(const T *__restrict__ src, int D, const int32_t *__restrict__ row_src,
-                                                int k, const float *__restrict__ wgt, const int32_t *__restrict__ seg,
-                                                int S, int64_t rows, const int32_t *__restrict__ kcol, int64_t Kp,
-                                                T *__restrict__ dstT, T *__restrict__ dst, float *__restrict__ colpart)
+// A wave takes a 64-row column tile x 64 features, each lane an 8 x 8 block
+// (rows 8 rg.., features 8 cg..): 16-byte loads and stores on both sides,
+// the column sums a fixed shuffle tree.  Grid (ceil(D / 256), strided over
+// the column tiles).
+template <class T> __device__ __forceinline__ void load8(const T *p, float (&v)[8]);
+template <> __device__ __forceinline__ void load8<uint16_t>(const uint16_t *p, float (&v)[8])
 {
-    __shared__ float tile[64][65];
-    __shared__ int64_t s_tok[64];
-    __shared__ float s_w[64];
-    const int f0 = blockIdx.x * 64;
-    const int total = kcol[S];
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-    for (int ct = blockIdx.y; ct < total; ct += gridDim.y) {
-        const int s = seg_of_tile(kcol, S, ct);
-        int64_t lo, hi;
-        seg_rows(seg, s, rows, lo, hi);
-        const int64_t rbase = lo + (int64_t)(ct - kcol[s]) * 64;
-        if (threadIdx.x < 64) {
-            const int64_t r = rbase + threadIdx.x;
-            int64_t tok = -1;
-            float w = 0.f;
-            if (r < hi) {
-                const int64_t slot = row_src ? (int64_t)row_src[r] : r;
-                tok = row_src ? slot / k : slot;
-                w = wgt ? wgt[slot] : 1.f;
-            }
-            s_tok[threadIdx.x] = tok;
-            s_w[threadIdx.x] = w;
-        }
-        __syncthreads();
-        const int f = f0 + tx;
-        for (int i = ty; i < 64; i += 4) {
-            const int64_t tok = s_tok[i];
-            float v = 0.f;
-            if (tok >= 0 && f < D) {
-                v = Elt<T>::ld(src, tok * D + f);
-                if (dst)
-                    Elt<T>::st(dst, (rbase + i) * D + f, v);
-            }
-            tile[i][tx] = v;
-        }
-        __syncthreads();
-        if (colpart && ty == 0 && f < D) {
-            float a = 0.f;
-            for (int i = 0; i < 64; ++i)
-                a = fmaf(s_w[i], tile[i][tx], a);
-            colpart[(int64_t)ct * D + f] = a;
-        }
-        const int64_t col = (int64_t)ct * 64 + tx;
-        for (int i = ty; i < 64; i += 4)
-            if (f0 + i < D)
-                Elt<T>::st(dstT, (int64_t)(f0 + i) * Kp + col, tile[tx][i]);
-        __syncthreads();
+    const u32x4 q = *reinterpret_cast<const u32x4 *>(p);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        v[2 * h] = bf16_bits_to_f32(q[h] & 0xFFFFu);
+        v[2 * h + 1] = bf16_bits_to_f32(q[h] >> 16);
+    }
+}
+template <> __device__ __forceinline__ void load8<float>(const float *p, float (&v)[8])
+{
+    const f32x4 a = reinterpret_cast<const f32x4 *>(p)[0], b = reinterpret_cast<const f32x4 *>(p)[1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v[j] = a[j];
+        v[j + 4] = b[j];
     }
 }
 
-// GELU backward over the K-segmented rows (same row/column map as gather_t),
-// from u = W1 x + b1 and dh' (both fp32 [rows, F], F % 8 == 0):
-//   du[r, q]  = w_r dh'[r, q] GELU'(u[r, q])        (row-major, T)
-//   duT[q, col] = du[r, q],  gwT[q, col] = w_r GELU(u[r, q])   (zero padding)
-//   dwpart[r, qt] = sum_{q in feature tile qt} dh'[r, q] GELU(u[r, q])   (if dwpart)
-//   colpart[ct, q] = sum over the tile's rows of du[r, q]               (if colpart)
-// w_r = wgt[row_src[r]] (1 when wgt is NULL).  A wave takes a 64-row column
-// tile x 64 features; each lane an 8 x 8 block (rows 8 rg.., features 8 cg..),
-// so row-major and transposed accesses are all 16-byte vectors.  Sums over a
-// tile's features / rows are fixed shuffle trees.  Grid (ceil(F / 256),
-// strided over the column tiles); FT = ceil(F / 64).
 template <class T> __device__ __forceinline__ void store8(T *p, const float (&v)[8]);
 template <> __device__ __forceinline__ void store8<uint16_t>(uint16_t *p, const float (&v)[8])
 {
@@ -238,6 +194,99 @@ template <> __device__ __forceinline__ void store8<float>(float *p, const float 
     *reinterpret_cast<f32x4 *>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
 }
 
+template <class T> __device__ __forceinline__ void store4v(T *p, const float (&v)[4]);
+template <> __device__ __forceinline__ void store4v<uint16_t>(uint16_t *p, const float (&v)[4])
+{
+    uint2 o;
+    o.x = pack_bf16x2(v[0], v[1]);
+    o.y = pack_bf16x2(v[2], v[3]);
+    *reinterpret_cast<uint2 *>(p) = o;
+}
+template <> __device__ __forceinline__ void store4v<float>(float *p, const float (&v)[4])
+{
+    *reinterpret_cast<f32x4 *>(p) = f32x4{v[0], v[1], v[2], v[3]};
+}
+
+template <class T>
+__global__ __launch_bounds__(256) void gather_t(const T *__restrict__ src, int D, const int32_t *__restrict__ row_src,
+                                                int k, const float *__restrict__ wgt, const int32_t *__restrict__ seg,
+                                                int S, int64_t rows, const int32_t *__restrict__ kcol, int64_t Kp,
+                                                T *__restrict__ dstT, T *__restrict__ dst, float *__restrict__ colpart)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int cg = lane & 7, rg = lane >> 3;
+    const int ft = blockIdx.x * 4 + wave;
+    if (ft * 64 >= D)
+        return; // whole wave; there is no barrier below
+    const int f0 = ft * 64 + cg * 8;
+    const bool fv = f0 < D; // lanes past D take part in the shuffles with zeros
+    const int total = kcol[S];
+    for (int ct = blockIdx.y; ct < total; ct += gridDim.y) {
+        const int s = seg_of_tile(kcol, S, ct);
+        int64_t lo, hi;
+        seg_rows(seg, s, rows, lo, hi);
+        const int64_t r0 = lo + (int64_t)(ct - kcol[s]) * 64 + rg * 8;
+        float v[8][8], w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t r = r0 + i;
+            const bool ok = r < hi;
+            int64_t tok = 0;
+            w[i] = 0.f;
+            if (ok) {
+                const int64_t slot = row_src ? (int64_t)row_src[r] : r;
+                tok = row_src ? slot / k : slot;
+                w[i] = wgt ? wgt[slot] : 1.f;
+            }
+            if (ok && fv) {
+                load8<T>(src + tok * D + f0, v[i]);
+                if (dst)
+                    store8<T>(dst + r * D + f0, v[i]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    v[i][j] = 0.f;
+            }
+        }
+        if (colpart) {
+            float cs[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                float a = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    a = fmaf(w[i], v[i][j], a);
+                a += __shfl_xor(a, 8, 64);
+                a += __shfl_xor(a, 16, 64);
+                a += __shfl_xor(a, 32, 64);
+                cs[j] = a;
+            }
+            if (rg == 0 && fv)
+                store8<float>(colpart + (int64_t)ct * D + f0, cs);
+        }
+        const int64_t col = (int64_t)ct * 64 + rg * 8;
+#pragma unroll
+        for (int j = 0; j < 8 && fv; ++j) {
+            float c[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                c[i] = v[i][j];
+            store8<T>(dstT + (int64_t)(f0 + j) * Kp + col, c);
+        }
+    }
+}
+
+// GELU backward over the K-segmented rows (same row/column map as gather_t),
+// from u = W1 x + b1 and dh' (both fp32 [rows, F], F % 8 == 0):
+//   du[r, q]  = w_r dh'[r, q] GELU'(u[r, q])        (row-major, T)
+//   duT[q, col] = du[r, q],  gwT[q, col] = w_r GELU(u[r, q])   (zero padding)
+//   dwpart[r, qt] = sum_{q in feature tile qt} dh'[r, q] GELU(u[r, q])   (if dwpart)
+//   colpart[ct, q] = sum over the tile's rows of du[r, q]               (if colpart)
+// w_r = wgt[row_src[r]] (1 when wgt is NULL).  A wave takes a 64-row column
+// tile x 64 features; each lane an 8 x 8 block (rows 8 rg.., features 8 cg..),
+// so row-major and transposed accesses are all 16-byte vectors.  Sums over a
+// tile's features / rows are fixed shuffle trees.  Grid (ceil(F / 256),
+// strided over the column tiles); FT = ceil(F / 64).
 template <class T>
 __global__ __launch_bounds__(256) void act_bwd(const float *__restrict__ u, const float *__restrict__ dh, int F,
                                                int FT, const int32_t *__restrict__ row_src,
@@ -260,34 +309,70 @@ __global__ __launch_bounds__(256) void act_bwd(const float *__restrict__ u, cons
         int64_t lo, hi;
         seg_rows(seg, s, rows, lo, hi);
         const int64_t r0 = lo + (int64_t)(ct - kcol[s]) * 64 + rg * 8;
-        float vdu[8][8], vgw[8][8], rs[8];
+        float rs[8], w[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int64_t r = r0 + i;
-            const bool ok = r < hi && qv;
-            const float w = ok ? (wgt ? wgt[row_src ? row_src[r] : r] : 1.f) : 0.f;
-            f32x4 ua = {0.f, 0.f, 0.f, 0.f}, ub = ua, ha = ua, hb = ua;
-            if (ok) {
-                const f32x4 *pu = reinterpret_cast<const f32x4 *>(u + r * F + q0);
-                const f32x4 *ph = reinterpret_cast<const f32x4 *>(dh + r * F + q0);
-                ua = pu[0];
-                ub = pu[1];
-                ha = ph[0];
-                hb = ph[1];
-            }
-            float acc = 0.f;
+            w[i] = (r < hi && qv) ? (wgt ? wgt[row_src ? row_src[r] : r] : 1.f) : 0.f;
+            rs[i] = 0.f;
+        }
+        const int64_t col = (int64_t)ct * 64 + rg * 8;
+        // two halves of 4 features keep the live state small
+#pragma unroll 1
+        for (int hf = 0; hf < 2; ++hf) {
+            const int q = q0 + 4 * hf;
+            float vdu[8][4], vgw[8][4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float uu = j < 4 ? ua[j] : ub[j - 4], hh = j < 4 ? ha[j] : hb[j - 4];
-                float g, gp;
-                gelu_and_grad(uu, g, gp);
-                vdu[i][j] = ok ? w * hh * gp : 0.f;
-                vgw[i][j] = ok ? w * g : 0.f;
-                acc = fmaf(hh, g, acc);
+            for (int i = 0; i < 8; ++i) {
+                const int64_t r = r0 + i;
+                const bool ok = r < hi && qv;
+                f32x4 uu = {0.f, 0.f, 0.f, 0.f}, hh = uu;
+                if (ok) {
+                    uu = *reinterpret_cast<const f32x4 *>(u + r * F + q);
+                    hh = *reinterpret_cast<const f32x4 *>(dh + r * F + q);
+                }
+                float acc = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float g, gp;
+                    gelu_and_grad(uu[j], g, gp);
+                    vdu[i][j] = ok ? w[i] * hh[j] * gp : 0.f;
+                    vgw[i][j] = ok ? w[i] * g : 0.f;
+                    acc = fmaf(hh[j], g, acc);
+                }
+                rs[i] += ok ? acc : 0.f;
+                if (ok)
+                    store4v<T>(du + r * F + q, vdu[i]);
             }
-            rs[i] = ok ? acc : 0.f;
-            if (ok)
-                store8<T>(du + r * F + q0, vdu[i]);
+            if (colpart) {
+                // column sums over the tile's 64 rows: the 8 lanes of a feature group
+                f32x4 cs;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float v = ((vdu[0][j] + vdu[1][j]) + (vdu[2][j] + vdu[3][j])) +
+                              ((vdu[4][j] + vdu[5][j]) + (vdu[6][j] + vdu[7][j]));
+                    v += __shfl_xor(v, 8, 64);
+                    v += __shfl_xor(v, 16, 64);
+                    v += __shfl_xor(v, 32, 64);
+                    cs[j] = v;
+                }
+                if (rg == 0 && qv)
+                    *reinterpret_cast<f32x4 *>(colpart + (int64_t)ct * F + q) = cs;
+            }
+            // transposed: feature row q + j, columns 64 ct + 8 rg .. + 8
+            if (qv) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    float a8[8], g8[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        a8[i] = vdu[i][j];
+                        g8[i] = vgw[i][j];
+                    }
+                    store8<T>(duT + (int64_t)(q + j) * Kp + col, a8);
+                    store8<T>(gwT + (int64_t)(q + j) * Kp + col, g8);
+                }
+            }
         }
         if (dwpart) {
             // row sums over the tile's 64 features: the 8 lanes of a row group
@@ -305,34 +390,6 @@ __global__ __launch_bounds__(256) void act_bwd(const float *__restrict__ u, cons
                     if (r0 + i < hi)
                         dwpart[(r0 + i) * FT + qt] = rs[i];
             }
-        }
-        if (colpart) {
-            // column sums over the tile's 64 rows: the 8 lanes of a feature group
-            float cs[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                float v = ((vdu[0][j] + vdu[1][j]) + (vdu[2][j] + vdu[3][j])) +
-                          ((vdu[4][j] + vdu[5][j]) + (vdu[6][j] + vdu[7][j]));
-                v += __shfl_xor(v, 8, 64);
-                v += __shfl_xor(v, 16, 64);
-                v += __shfl_xor(v, 32, 64);
-                cs[j] = v;
-            }
-            if (rg == 0 && qv)
-                store8<float>(colpart + (int64_t)ct * F + q0, cs);
-        }
-        // transposed: feature row q0 + j, columns 64 ct + 8 rg .. + 8
-        const int64_t col = (int64_t)ct * 64 + rg * 8;
-#pragma unroll
-        for (int j = 0; j < 8 && qv; ++j) {
-            float a[8], g8[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                a[i] = vdu[i][j];
-                g8[i] = vgw[i][j];
-            }
-            store8<T>(duT + (int64_t)(q0 + j) * Kp + col, a);
-            store8<T>(gwT + (int64_t)(q0 + j) * Kp + col, g8);
         }
     }
 }
@@ -362,7 +419,7 @@ __global__ __launch_bounds__(256) void router_bwd(const float *__restrict__ prob
                                                   const float *__restrict__ dwpart, int FT, const T *__restrict__ b2,
                                                   const T *__restrict__ dY, int d, int e0,
                                                   const float *__restrict__ f, float c_aux, int64_t Ttok, int E, int k,
-                                                  float *__restrict__ dl)
+                                                  float *__restrict__ dl, uint16_t *__restrict__ dl2, int E64)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t t = (int64_t)blockIdx.x * 4 + wave;
@@ -394,7 +451,8 @@ __global__ __launch_bounds__(256) void router_bwd(const float *__restrict__ prob
     const float *pt = probs + t * E;
     float sd = 0.f;
     for (int pass = 0; pass < 2; ++pass) {
-        for (int b = 0; b < E; b += 64) {
+        const int eb = pass == 1 && dl2 ? E64 : E;
+        for (int b = 0; b < eb; b += 64) {
             const int e = b + lane;
             float dp = e < E ? c_aux * f[e] : 0.f;
             for (int j = 0; j < k; ++j) {
@@ -403,16 +461,123 @@ __global__ __launch_bounds__(256) void router_bwd(const float *__restrict__ prob
                 if (ej == e)
                     dp += dj;
             }
-            if (e < E) {
-                if (pass == 0)
+            if (pass == 0) {
+                if (e < E)
                     sd = fmaf(pt[e], dp, sd);
-                else
-                    dl[t * E + e] = pt[e] * (dp - sd);
+            } else {
+                const float v = e < E ? pt[e] * (dp - sd) : 0.f;
+                if (e < E)
+                    dl[t * E + e] = v;
+                if (dl2 && e < E64) {
+                    // two bf16 pieces, laid out (hi, hi, lo) for the dl . W_r GEMM
+                    const uint16_t hi = f32_to_bf16_bits(v);
+                    const uint16_t lo = f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
+                    uint16_t *row = dl2 + t * (3 * (int64_t)E64);
+                    row[e] = hi;
+                    row[E64 + e] = hi;
+                    row[2 * E64 + e] = lo;
+                }
             }
         }
         if (pass == 0)
             sd = wave_sum(sd);
     }
+}
+
+// w2p[i, p E64 + e] = piece p of W_r[e, i] in the order (hi, lo, hi), the
+// counterpart of router_bwd's (hi, hi, lo) rows: the GEMM sums
+// dl_hi w_hi + dl_hi w_lo + dl_lo w_hi.  Zero for e >= E.
+__global__ __launch_bounds__(256) void router_weight_pieces_t(const float *__restrict__ wr, int E, int d, int E64,
+                                                              uint16_t *__restrict__ w2p)
+{
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= (int64_t)d * E64)
+        return;
+    const int i = (int)(q / E64), e = (int)(q % E64);
+    const float v = e < E ? wr[(int64_t)e * d + i] : 0.f;
+    const uint16_t hi = f32_to_bf16_bits(v);
+    const uint16_t lo = f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
+    uint16_t *row = w2p + (int64_t)i * 3 * E64;
+    row[e] = hi;
+    row[E64 + e] = lo;
+    row[2 * E64 + e] = hi;
+}
+
+// T equal token ranges: seg[s] = T s / S.
+__global__ __launch_bounds__(64) void linear_segments(int32_t *__restrict__ seg, int S, int64_t T)
+{
+    for (int s = threadIdx.x; s <= S; s += 64)
+        seg[s] = (int32_t)(T * s / S);
+}
+
+// Exact three-piece split of dl in the K-segmented layout of tokens:
+// dlT3[p E + e, col] = piece p of dl[t, e] (hi, mid, lo: hi and mid are
+// truncations, hi + mid + lo == dl), t the column's token; zero padding.
+// E % 8 == 0.  A wave takes 64 tokens x 64 experts, a lane 8 x 8.
+__device__ __forceinline__ float trunc_to_bf16(float v) { return __uint_as_float(__float_as_uint(v) & 0xFFFF0000u); }
+
+__global__ __launch_bounds__(256) void dl_pieces_t(const float *__restrict__ dl, int E, const int32_t *__restrict__ seg,
+                                                   int S, int64_t T, const int32_t *__restrict__ kcol, int64_t Kp,
+                                                   uint16_t *__restrict__ dlT3)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int cg = lane & 7, rg = lane >> 3;
+    const int et = blockIdx.x * 4 + wave;
+    if (et * 64 >= E)
+        return;
+    const int e0 = et * 64 + cg * 8;
+    if (e0 >= E)
+        return; // no shuffles below
+    const int total = kcol[S];
+    for (int ct = blockIdx.y; ct < total; ct += gridDim.y) {
+        const int s = seg_of_tile(kcol, S, ct);
+        int64_t lo, hi;
+        seg_rows(seg, s, T, lo, hi);
+        const int64_t r0 = lo + (int64_t)(ct - kcol[s]) * 64 + rg * 8;
+        float v[8][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (r0 + i < hi) {
+                load8<float>(dl + (r0 + i) * E + e0, v[i]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    v[i][j] = 0.f;
+            }
+        }
+        const int64_t col = (int64_t)ct * 64 + rg * 8;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float ph[8], pm[8], pl[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float x = v[i][j];
+                ph[i] = trunc_to_bf16(x);
+                const float r1 = x - ph[i];
+                pm[i] = trunc_to_bf16(r1);
+                pl[i] = r1 - pm[i];
+            }
+            store8<uint16_t>(dlT3 + (int64_t)(e0 + j) * Kp + col, ph);
+            store8<uint16_t>(dlT3 + (int64_t)(E + e0 + j) * Kp + col, pm);
+            store8<uint16_t>(dlT3 + (int64_t)(2 * E + e0 + j) * Kp + col, pl);
+        }
+    }
+}
+
+// dW_r[e, i] = sum over token ranges c of (hi + (mid + lo)) partials.
+__global__ __launch_bounds__(256) void router_wgrad_pieces_reduce(const float *__restrict__ part, int nc, int E, int d,
+                                                                  float *__restrict__ out)
+{
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t n = (int64_t)E * d;
+    if (q >= n)
+        return;
+    float a = 0.f;
+    for (int c = 0; c < nc; ++c) {
+        const float *pc = part + (int64_t)c * 3 * n;
+        a += pc[q] + (pc[n + q] + pc[2 * n + q]);
+    }
+    out[q] = a;
 }
 
 // Router weight gradient, first level: part[c, e, i] = sum over token chunk
@@ -492,36 +657,44 @@ __global__ __launch_bounds__(256) void router_bias_grad(const float *__restrict_
         db[e] = red[0];
 }
 
-// dx[t, i] = sum_e dl[t, e] W_r[e, i] + sum over t's kept selections of
-// dx_rows[slot_row, i] + dx_sh[t, i].  Block = TB tokens x 256 columns.
+// dx[t, i] = sum_e dl[t, e] W_r[e, i] (skipped when E = 0) + sum over t's
+// kept selections of dx_rows[slot_row, i] + dx_sh[t, i] + dx_r[t, i] (each
+// optional).  dx_sh may be dx itself (accumulation in place: each element is
+// read and written by the same thread).  Block = TB tokens x 1024 columns,
+// 4 columns per thread (d % 4 == 0).
 template <int TB>
 __global__ __launch_bounds__(256) void dx_combine(const float *__restrict__ dx_rows,
-                                                  const int32_t *__restrict__ slot_row, int k,
-                                                  const float *__restrict__ dx_sh, const float *__restrict__ dl,
+                                                  const int32_t *__restrict__ slot_row, int k, const float *dx_sh,
+                                                  const float *__restrict__ dx_r, const float *__restrict__ dl,
                                                   const float *__restrict__ w_r, int64_t Ttok, int d, int E,
-                                                  float *__restrict__ dx)
+                                                  float *dx)
 {
-    __shared__ float s_dl[TB][256];
-    const int i = blockIdx.x * 256 + threadIdx.x;
+    __shared__ float s_dl[TB][64];
+    const int i = (blockIdx.x * 256 + threadIdx.x) * 4;
     const int64_t t0 = (int64_t)blockIdx.y * TB;
-    float acc[TB];
+    f32x4 acc[TB];
 #pragma unroll
     for (int q = 0; q < TB; ++q)
-        acc[q] = 0.f;
-    for (int eb = 0; eb < E; eb += 256) {
-        const int ne = E - eb < 256 ? E - eb : 256;
+        acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int eb = 0; eb < E; eb += 64) {
+        const int ne = E - eb < 64 ? E - eb : 64;
         __syncthreads();
-        for (int q = threadIdx.x; q < TB * 256; q += 256) {
-            const int tq = q / 256, e = q % 256;
+        for (int q = threadIdx.x; q < TB * 64; q += 256) {
+            const int tq = q / 64, e = q % 64;
             s_dl[tq][e] = (t0 + tq < Ttok && e < ne) ? dl[(t0 + tq) * E + eb + e] : 0.f;
         }
         __syncthreads();
         if (i < d) {
             for (int e = 0; e < ne; ++e) {
-                const float wv = w_r[(int64_t)(eb + e) * d + i];
+                const f32x4 wv = *reinterpret_cast<const f32x4 *>(w_r + (int64_t)(eb + e) * d + i);
 #pragma unroll
-                for (int q = 0; q < TB; ++q)
-                    acc[q] = fmaf(s_dl[q][e], wv, acc[q]);
+                for (int q = 0; q < TB; ++q) {
+                    const float c = s_dl[q][e];
+                    acc[q][0] = fmaf(c, wv[0], acc[q][0]);
+                    acc[q][1] = fmaf(c, wv[1], acc[q][1]);
+                    acc[q][2] = fmaf(c, wv[2], acc[q][2]);
+                    acc[q][3] = fmaf(c, wv[3], acc[q][3]);
+                }
             }
         }
     }
@@ -532,15 +705,17 @@ __global__ __launch_bounds__(256) void dx_combine(const float *__restrict__ dx_r
         const int64_t t = t0 + q;
         if (t >= Ttok)
             break;
-        float v = acc[q];
+        f32x4 v = acc[q];
         for (int j = 0; j < k; ++j) {
             const int r = slot_row[t * k + j];
             if (r >= 0)
-                v += dx_rows[(int64_t)r * d + i];
+                v += *reinterpret_cast<const f32x4 *>(dx_rows + (int64_t)r * d + i);
         }
         if (dx_sh)
-            v += dx_sh[t * d + i];
-        dx[t * d + i] = v;
+            v += *reinterpret_cast<const f32x4 *>(dx_sh + t * d + i);
+        if (dx_r)
+            v += *reinterpret_cast<const f32x4 *>(dx_r + t * d + i);
+        *reinterpret_cast<f32x4 *>(dx + t * d + i) = v;
     }
 }
 
@@ -579,8 +754,8 @@ moe_status_t launch_gather_t(const void *src, int D, const int32_t *row_src, int
                              void *dstT, void *dst, float *colpart, hipStream_t stream)
 {
     const int64_t ctiles = Kp / 64;
-    const int fx = (D + 63) / 64;
-    const dim3 g((unsigned)fx, strided_grid(ctiles, (8192 + fx - 1) / fx));
+    const int fx = (D + 255) / 256;
+    const dim3 g((unsigned)fx, strided_grid(ctiles, (4096 + fx - 1) / fx));
     if (dt == MOE_BF16)
         gather_t<uint16_t><<<g, 256, 0, stream>>>((const uint16_t *)src, D, row_src, k, wgt, seg, S, rows, kcol, Kp,
                                                   (uint16_t *)dstT, (uint16_t *)dst, colpart);
@@ -624,10 +799,12 @@ moe_status_t launch_router_bwd(const float *probs, const int32_t *topk_idx, cons
     const unsigned g = (unsigned)((T + 3) / 4);
     if (dt == MOE_BF16)
         router_bwd<uint16_t><<<g, 256, 0, stream>>>(probs, topk_idx, slot_row, dwpart, FT, (const uint16_t *)b2,
-                                                    (const uint16_t *)dY, d, e0, f, c_aux, T, E, k, dl);
+                                                    (const uint16_t *)dY, d, e0, f, c_aux, T, E, k, dl,
+                                                    nullptr, 0);
     else
         router_bwd<float><<<g, 256, 0, stream>>>(probs, topk_idx, slot_row, dwpart, FT, (const float *)b2,
-                                                 (const float *)dY, d, e0, f, c_aux, T, E, k, dl);
+                                                 (const float *)dY, d, e0, f, c_aux, T, E, k, dl,
+                                                 nullptr, 0);
     return check_launch("router_bwd");
 }
 
@@ -683,13 +860,96 @@ moe_status_t launch_router_wgrad(const void *x, moe_dtype_t dt, const float *dl,
 }
 
 moe_status_t launch_dx_combine(const float *dx_rows, const int32_t *slot_row, int k, const float *dx_sh,
-                               const float *dl, const float *w_r, int64_t T, int d, int E, float *dx,
+                               const float *dx_r, const float *dl, const float *w_r, int64_t T, int d, int E, float *dx,
                                hipStream_t stream)
 {
     constexpr int TB = 16;
-    const dim3 g((unsigned)((d + 255) / 256), (unsigned)((T + TB - 1) / TB));
-    dx_combine<TB><<<g, 256, 0, stream>>>(dx_rows, slot_row, k, dx_sh, dl, w_r, T, d, E, dx);
+    const dim3 g((unsigned)((d + 1023) / 1024), (unsigned)((T + TB - 1) / TB));
+    // with the router term precomputed (dx_r), the dl . W_r loop is skipped
+    dx_combine<TB><<<g, 256, 0, stream>>>(dx_rows, slot_row, k, dx_sh, dx_r, dl, w_r, T, d, dx_r ? 0 : E, dx);
     return check_launch("dx_combine");
+}
+
+int router_mfma_chunks(int64_t T, int d, int E)
+{
+    const int64_t tiles = ((3 * (int64_t)E + 255) / 256) * ((d + 255) / 256);
+    int64_t n = (384 + tiles - 1) / tiles;
+    const int64_t most = T / 512 > 1 ? T / 512 : 1;
+    n = n < 1 ? 1 : (n > most ? most : n);
+    return (int)n;
+}
+
+size_t router_mfma_ws_bytes(int64_t T, int d, int E)
+{
+    const int E64 = (E + 63) / 64 * 64;
+    const int nc = router_mfma_chunks(T, d, E);
+    const int64_t Kp = kseg_cols_bound(T, nc);
+    return align_up((size_t)T * 3 * E64 * 2) + align_up((size_t)d * 3 * E64 * 2) + align_up((size_t)T * d * 4) +
+           2 * align_up((size_t)(nc + 1) * 4) + align_up((size_t)d * Kp * 2) + align_up((size_t)3 * E * Kp * 2) +
+           align_up((size_t)nc * 3 * E * d * 4);
+}
+
+moe_status_t launch_router_bwd_mfma(const float *probs, const int32_t *topk_idx, const int32_t *slot_row,
+                                    const float *dwpart, int FT, const void *b2, const void *dY, int d, int e0,
+                                    const float *f, float c_aux, int64_t T, int E, int k, const void *x,
+                                    const float *w_r, float *dl, float *dw_r, float *db_r, float **dx_r, void *ws,
+                                    void *gemm_ws, size_t gemm_ws_bytes, hipStream_t stream)
+{
+    const int E64 = (E + 63) / 64 * 64;
+    const int nc = router_mfma_chunks(T, d, E);
+    const int64_t Kp = kseg_cols_bound(T, nc);
+    Carver cv{(char *)ws, 0};
+    uint16_t *dl2 = cv.take<uint16_t>((size_t)T * 3 * E64);
+    uint16_t *w2p = cv.take<uint16_t>((size_t)d * 3 * E64);
+    float *dxr = cv.take<float>((size_t)T * d);
+    int32_t *seg = cv.take<int32_t>((size_t)nc + 1);
+    int32_t *kcol = cv.take<int32_t>((size_t)nc + 1);
+    uint16_t *xT = cv.take<uint16_t>((size_t)d * Kp);
+    uint16_t *dlT3 = cv.take<uint16_t>((size_t)3 * E * Kp);
+    float *part = cv.take<float>((size_t)nc * 3 * E * d);
+
+    router_bwd<uint16_t><<<(unsigned)((T + 3) / 4), 256, 0, stream>>>(
+        probs, topk_idx, slot_row, dwpart, FT, (const uint16_t *)b2, (const uint16_t *)dY, d, e0, f, c_aux, T, E, k,
+        dl, dl2, E64);
+    if (moe_status_t s = check_launch("router_bwd"))
+        return s;
+    // dx router term: [dl_hi | dl_hi | dl_lo] . [w_hi | w_lo | w_hi]^T
+    const int64_t nw = (int64_t)d * E64;
+    router_weight_pieces_t<<<(unsigned)((nw + 255) / 256), 256, 0, stream>>>(w_r, E, d, E64, w2p);
+    if (moe_status_t s = check_launch("router_weight_pieces_t"))
+        return s;
+    if (moe_status_t s = launch_grouped_gemm_f32out(dl2, nullptr, 1, T, d, 3 * E64, MOE_BF16, w2p, nullptr, dxr,
+                                                    gemm_ws, gemm_ws_bytes, stream))
+        return s;
+    // dW_r = sum over token ranges of dlT3 . x^T (exact pieces of dl)
+    linear_segments<<<1, 64, 0, stream>>>(seg, nc, T);
+    if (moe_status_t s = check_launch("linear_segments"))
+        return s;
+    if (moe_status_t s = launch_kseg_layout(seg, nc, T, kcol, stream))
+        return s;
+    if (moe_status_t s = launch_gather_t(x, d, nullptr, 1, nullptr, seg, nc, T, kcol, Kp, MOE_BF16, xT, nullptr,
+                                         nullptr, stream))
+        return s;
+    {
+        const int ex = (E + 255) / 256;
+        const dim3 g((unsigned)ex, strided_grid(Kp / 64, (4096 + ex - 1) / ex));
+        dl_pieces_t<<<g, 256, 0, stream>>>(dl, E, seg, nc, T, kcol, Kp, dlT3);
+        if (moe_status_t s = check_launch("dl_pieces_t"))
+            return s;
+    }
+    if (moe_status_t s = launch_kseg_gemm(dlT3, xT, kcol, nc, 3 * E, d, Kp, MOE_BF16, part, stream))
+        return s;
+    const int64_t n = (int64_t)E * d;
+    router_wgrad_pieces_reduce<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(part, nc, E, d, dw_r);
+    if (moe_status_t s = check_launch("router_wgrad_pieces_reduce"))
+        return s;
+    if (db_r) {
+        router_bias_grad<<<(unsigned)E, 256, 0, stream>>>(dl, T, E, db_r);
+        if (moe_status_t s = check_launch("router_bias_grad"))
+            return s;
+    }
+    *dx_r = dxr;
+    return MOE_OK;
 }
 
 } // namespace moe

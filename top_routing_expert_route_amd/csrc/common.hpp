@@ -165,8 +165,20 @@ moe_status_t launch_router_bwd(const float *probs, const int32_t *topk_idx, cons
 size_t router_wgrad_ws_bytes(int64_t T, int d, int E);
 moe_status_t launch_router_wgrad(const void *x, moe_dtype_t dt, const float *dl, int64_t T, int d, int E,
                                  float *dw_r, float *db_r, void *ws, hipStream_t stream);
+// dx = kept dx rows + dx_sh (may be NULL) + the router term: dx_r if given,
+// else dl . W_r on the vector units.
 moe_status_t launch_dx_combine(const float *dx_rows, const int32_t *slot_row, int k, const float *dx_sh,
-                               const float *dl, const float *w_r, int64_t T, int d, int E, float *dx,
+                               const float *dx_r, const float *dl, const float *w_r, int64_t T, int d, int E, float *dx,
                                hipStream_t stream);
+// Router backward on the matrix cores (bf16 layers, E % 8 == 0, d % 64 == 0):
+// dl as launch_router_bwd; dW_r = dl^T x from an exact three-piece bf16 split
+// of dl (fp32-accurate), db_r (if not NULL); *dx_r = a workspace buffer
+// [T, d] holding dl . W_r from two-piece splits of both operands.
+size_t router_mfma_ws_bytes(int64_t T, int d, int E);
+moe_status_t launch_router_bwd_mfma(const float *probs, const int32_t *topk_idx, const int32_t *slot_row,
+                                    const float *dwpart, int FT, const void *b2, const void *dY, int d, int e0,
+                                    const float *f, float c_aux, int64_t T, int E, int k, const void *x,
+                                    const float *w_r, float *dl, float *dw_r, float *db_r, float **dx_r, void *ws,
+                                    void *gemm_ws, size_t gemm_ws_bytes, hipStream_t stream);
 
 } // namespace moe

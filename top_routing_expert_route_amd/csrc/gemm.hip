@@ -961,18 +961,18 @@ __device__ void load_kseg_prefix(const int32_t *kcol, int S, int *kb, int *ne)
     __syncthreads();
 }
 
+constexpr int kKsegPanel = 4;
+
 struct KsegCtx {
     const int *kb, *ne;
     const uint16_t *A, *W;
     int64_t first;
     int S, M, N, Kp, MT, NT, per, nw, n_work;
-    bool n_inner; // consecutive tiles walk the feature tiles (M > N)
+    bool n_inner; // the feature tiles (W) are the smaller operand's (M > N)
 };
 
 // Work item i of the block: tile L = first + i * per of the list (non-empty
-// segments ascending, then the tiles of the larger operand, then those of the
-// smaller one, so that consecutive tiles share a tile of the larger operand
-// and only the smaller one is re-read).
+// segments ascending, then panels of the smaller operand's tiles).
 __device__ __forceinline__ Work get_work(const KsegCtx &x, int i)
 {
     const int64_t L = x.first + (int64_t)i * x.per;
@@ -990,8 +990,17 @@ __device__ __forceinline__ Work get_work(const KsegCtx &x, int i)
             hi = mid - 1;
     }
     const int local = (int)(L - (int64_t)q * per_seg);
-    const int row0 = (x.n_inner ? local / x.NT : local % x.MT) * kL;
-    const int n0 = (x.n_inner ? local % x.NT : local / x.MT) * kL;
+    // Panels of kKsegPanel tiles of the smaller operand: within a panel the
+    // larger operand's tiles are walked, the panel's tiles fastest, so the
+    // panel (about 2 MB) stays in the XCD's L2 while the 32 CUs sweep the
+    // larger operand, which is read once per panel.
+    const int SI = x.n_inner ? x.NT : x.MT, LO = x.n_inner ? x.MT : x.NT;
+    const int panel = local / (kKsegPanel * LO);
+    const int rem = local - panel * (kKsegPanel * LO);
+    const int pw = SI - panel * kKsegPanel < kKsegPanel ? SI - panel * kKsegPanel : kKsegPanel;
+    const int big = rem / pw, small = panel * kKsegPanel + rem % pw;
+    const int row0 = (x.n_inner ? big : small) * kL;
+    const int n0 = (x.n_inner ? small : big) * kL;
     const int row_end = row0 + kL < x.M ? row0 + kL : x.M;
     Work w;
     w.t.s = uni(lo);
