@@ -22,6 +22,8 @@
 //                    ballots over the bits of the expert id, so the rank is
 //                    stable (token order) without atomics.  Writes slot_row
 //                    and row_src.
+//  dispatch_plan_small  the three steps above in one block of 16 waves when
+//                    T*k <= 32768 and E_loc <= 256 (counts and bases in LDS).
 //  dispatch_scatter  one wave per token: the token's row of x is read once
 //                    and written to each of its kept rows (16-byte accesses).
 #include "common.hpp"
@@ -176,6 +178,114 @@ __global__ __launch_bounds__(256) void dispatch_rank(const int32_t *__restrict__
     }
 }
 
+// count + scan + rank in one block of 16 waves for small problems (at most
+// 16 chunks, E_loc <= kSmallExperts): the per-chunk counts and bases stay in
+// LDS.  Same ranks, rows and counts as dispatch_count / _scan / _rank.
+constexpr int kSmallExperts = 256;
+
+__global__ __launch_bounds__(1024) void dispatch_plan_small(const int32_t *__restrict__ topk_idx, int64_t items,
+                                                            int chunk, int nchunks, int e0, int E_loc, int nbits,
+                                                            int64_t cap, int32_t *__restrict__ seg_offsets,
+                                                            int32_t *__restrict__ kept_count,
+                                                            int32_t *__restrict__ n_dropped, int64_t max_rows,
+                                                            int32_t *__restrict__ slot_row,
+                                                            int32_t *__restrict__ row_src)
+{
+    __shared__ int cb[16][kSmallExperts]; // counts, then running bases per chunk
+    __shared__ int tot[kSmallExperts], seg[kSmallExperts + 1];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int q = threadIdx.x; q < 16 * kSmallExperts; q += 1024)
+        cb[q / kSmallExperts][q % kSmallExperts] = 0;
+    __syncthreads();
+    const int c = wave;
+    const int64_t beg = (int64_t)c * chunk;
+    const int64_t end = min(items, beg + chunk);
+    if (c < nchunks) {
+        for (int64_t i = beg + lane; i < end; i += 64) {
+            const int l = local_of(topk_idx[i], e0, E_loc);
+            if (l >= 0)
+                atomicAdd(&cb[c][l], 1);
+        }
+    }
+    __syncthreads();
+    // exclusive scan over the chunks, per expert
+    for (int l = threadIdx.x; l < E_loc; l += 1024) {
+        int run = 0;
+        for (int q = 0; q < nchunks; ++q) {
+            const int v = cb[q][l];
+            cb[q][l] = run;
+            run += v;
+        }
+        tot[l] = run;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        int carry = 0, drop = 0;
+        for (int l0 = 0; l0 < E_loc; l0 += 64) {
+            const int l = l0 + lane;
+            int t = 0, kept = 0;
+            if (l < E_loc) {
+                t = tot[l];
+                kept = (cap >= 0 && (int64_t)t > cap) ? (int)cap : t;
+            }
+            const int inc = wave_incl_scan(kept, lane);
+            int dr = t - kept;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1)
+                dr += __shfl_xor(dr, o, 64);
+            if (l < E_loc) {
+                seg[l] = carry + inc - kept;
+                seg_offsets[l] = carry + inc - kept;
+                kept_count[l] = kept;
+            }
+            carry += __shfl(inc, 63, 64);
+            drop += dr;
+        }
+        if (lane == 0) {
+            seg[E_loc] = carry;
+            seg_offsets[E_loc] = carry;
+            if (n_dropped)
+                n_dropped[0] = drop;
+        }
+    }
+    __syncthreads();
+    if (c >= nchunks)
+        return; // no barrier below
+    int *run = cb[c];
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int64_t i0 = beg; i0 < end; i0 += 64) {
+        const int64_t i = i0 + lane;
+        const bool valid = i < end;
+        const int l = valid ? local_of(topk_idx[i], e0, E_loc) : -1;
+        const bool local = l >= 0;
+        uint64_t m = __ballot(local);
+        for (int b = 0; b < nbits; ++b) {
+            const bool bit = local && ((l >> b) & 1);
+            const uint64_t bb = __ballot(bit);
+            m &= bit ? bb : ~bb;
+        }
+        if (local) {
+            const int lrank = __popcll(m & below);
+            const int base = run[l];
+            const int64_t r = (int64_t)base + lrank;
+            const bool last = (m >> lane) == 1ull;
+            if (last)
+                run[l] = base + __popcll(m);
+            int32_t out = -1;
+            if (cap < 0 || r < cap) {
+                const int64_t row = (int64_t)seg[l] + r;
+                if (row < max_rows) {
+                    out = (int32_t)row;
+                    row_src[row] = (int32_t)i;
+                }
+            }
+            slot_row[i] = out;
+        } else if (valid) {
+            slot_row[i] = -2;
+        }
+    }
+}
+
 template <int U>
 __global__ __launch_bounds__(256) void dispatch_scatter(const u32x4 *__restrict__ x, const int32_t *__restrict__ slot_row,
                                                         int64_t T, int k, int64_t units, u32x4 *__restrict__ x_perm)
@@ -252,29 +362,39 @@ moe_status_t launch_dispatch(const void *x, moe_dtype_t dt, const int32_t *topk_
                              int64_t max_rows, int32_t *n_dropped, void *ws, hipStream_t stream)
 {
     const int64_t items = T * k;
-    const ChunkPlan p = plan_chunks(items, E_loc);
     const int64_t cap = capacity_of(T, E, capacity_factor);
-    int32_t *chunk_cb = (int32_t *)ws;
-    const size_t lds = (size_t)4 * E_loc * sizeof(int);
-    const unsigned blocks = (unsigned)((p.nchunks + 3) / 4);
-    if (items > 0) {
-        dispatch_count<<<blocks, 256, lds, stream>>>(topk_idx, items, p.chunk, p.nchunks, e0, E_loc, chunk_cb);
-        if (moe_status_t s = check_launch("dispatch_count"))
-            return s;
-    }
-    dispatch_scan<<<1, 1024, 0, stream>>>(chunk_cb, items > 0 ? p.nchunks : 0, E_loc, cap, seg_offsets, kept_count,
-                                          n_dropped);
-    if (moe_status_t s = check_launch("dispatch_scan"))
-        return s;
-    if (items == 0)
-        return MOE_OK;
     int nbits = 0;
     while ((1 << nbits) < E_loc)
         ++nbits;
-    dispatch_rank<<<blocks, 256, lds, stream>>>(topk_idx, items, p.chunk, p.nchunks, e0, E_loc, nbits, cap,
-                                                chunk_cb, seg_offsets, max_rows, slot_row, row_src);
-    if (moe_status_t s = check_launch("dispatch_rank"))
-        return s;
+    if (items > 0 && items <= 16 * 2048 && E_loc <= kSmallExperts) {
+        // one block plans the whole dispatch: 16 chunks of a multiple of 64
+        const int chunk = (int)((items + 16 * 64 - 1) / (16 * 64) * 64);
+        const int nch = (int)((items + chunk - 1) / chunk);
+        dispatch_plan_small<<<1, 1024, 0, stream>>>(topk_idx, items, chunk, nch, e0, E_loc, nbits, cap, seg_offsets,
+                                                    kept_count, n_dropped, max_rows, slot_row, row_src);
+        if (moe_status_t s = check_launch("dispatch_plan_small"))
+            return s;
+    } else {
+        const ChunkPlan p = plan_chunks(items, E_loc);
+        int32_t *chunk_cb = (int32_t *)ws;
+        const size_t lds = (size_t)4 * E_loc * sizeof(int);
+        const unsigned blocks = (unsigned)((p.nchunks + 3) / 4);
+        if (items > 0) {
+            dispatch_count<<<blocks, 256, lds, stream>>>(topk_idx, items, p.chunk, p.nchunks, e0, E_loc, chunk_cb);
+            if (moe_status_t s = check_launch("dispatch_count"))
+                return s;
+        }
+        dispatch_scan<<<1, 1024, 0, stream>>>(chunk_cb, items > 0 ? p.nchunks : 0, E_loc, cap, seg_offsets,
+                                              kept_count, n_dropped);
+        if (moe_status_t s = check_launch("dispatch_scan"))
+            return s;
+        if (items == 0)
+            return MOE_OK;
+        dispatch_rank<<<blocks, 256, lds, stream>>>(topk_idx, items, p.chunk, p.nchunks, e0, E_loc, nbits, cap,
+                                                    chunk_cb, seg_offsets, max_rows, slot_row, row_src);
+        if (moe_status_t s = check_launch("dispatch_rank"))
+            return s;
+    }
     if (x_perm) {
         const int64_t units = (int64_t)d * (dt == MOE_BF16 ? 2 : 4) / 16;
         dispatch_scatter<8><<<(unsigned)((T + 3) / 4), 256, 0, stream>>>((const u32x4 *)x, slot_row, T, k, units,
