@@ -35,6 +35,11 @@ BWD_SMALL = {
                           expert_bias="gauss"),
     "selbias-bwd": wl.scaled(wl.get(1), name="selbias-bwd", T=400, d=192, E=32, k=4, ffn=128,
                              sel_bias="gauss", router_bias="gauss"),
+    # fp32 layer with a local share and a shared expert (fp32 K-segmented path, dx accumulated in place)
+    "f32-shared": wl.scaled(wl.get(0), name="f32-shared", T=200, d=64, E=8, k=2, ffn=128, shared_expert=True,
+                            expert_begin=2, num_local_experts=4, expert_bias="gauss", router_bias="gauss"),
+    # E >= 32 but not a multiple of 8: the router backward stays on the vector units
+    "e36-bwd": wl.scaled(wl.get(1), name="e36-bwd", T=300, d=128, E=36, k=3, ffn=128, capacity_factor=1.3),
 }
 
 EXPERT_GRADS = (("dx", "dx"), ("dw1", "dW1"), ("db1", "db1"), ("dw2", "dW2"), ("db2", "db2"))
@@ -118,6 +123,33 @@ def test_backward_aux_only():
     p = r.probs
     ref = 2.5 * w.alpha / w.T * p * (f[None, :] - (p * f[None, :]).sum(1, keepdims=True))
     assert rel_err(g["dlogits"].cpu().numpy(), ref) <= TOL_ROUTER
+
+
+def test_backward_all_remote():
+    """A selection bias keeps every token off the local experts: every routed
+    weight gradient comes from empty segments (zero), dx is the router and
+    shared-expert terms only."""
+    w = wl.scaled(wl.get(1), name="all-remote", T=300, d=128, E=16, k=2, ffn=128, expert_begin=4,
+                  num_local_experts=4, shared_expert=True)
+    inp = wl.make_layer(w, seed=2)
+    sb = np.zeros(w.E, np.float32)
+    sb[4:8] = -100.0
+    inp.sel_bias = sb
+    t = wl.device_layer(inp, DEV)
+    dy_host = wl.make_grad_output(w, seed=2)
+    layer = _layer(w, t)
+    outs = layer.alloc_outputs()
+    layer.forward(t["x"])
+    g = layer.backward(t["x"], wl.to_torch(dy_host, DEV), 0.7, dlogits=True)
+    torch.cuda.synchronize()
+    assert int(outs["seg_offsets"][-1].item()) == 0
+    for n in ("dw1", "db1", "dw2", "db2"):
+        assert torch.count_nonzero(g[n]).item() == 0, n
+    ref = oracle.backward(inp, _dy64(w, dy_host), g_aux=0.7, topk_idx=outs["topk_idx"].cpu().numpy())
+    for gname, rname in EXPERT_GRADS + SHARED_GRADS:
+        assert rel_err(g[gname].cpu().numpy(), getattr(ref, rname)) <= TOL_Y_BF16, gname
+    for gname, rname in ROUTER_GRADS:
+        assert rel_err(g[gname].cpu().numpy(), getattr(ref, rname)) <= TOL_ROUTER, gname
 
 
 def test_backward_zero_tokens():
