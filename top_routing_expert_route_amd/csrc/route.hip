@@ -371,20 +371,36 @@ __global__ __launch_bounds__(256) void route_logits_f32(const float *__restrict_
     logits[i] = s;
 }
 
+// Wave reductions without the LDS crossbar: DPP moves within rows of 16
+// lanes (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror: after the four steps every lane holds its row's result), then
+// the four row results are read into scalars and combined in a fixed order.
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
 __device__ __forceinline__ float wave_max(float v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = fmaxf(v, dpp_mov<0xB1>(v));
+    v = fmaxf(v, dpp_mov<0x4E>(v));
+    v = fmaxf(v, dpp_mov<0x141>(v));
+    v = fmaxf(v, dpp_mov<0x140>(v));
+    return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
 }
 
 __device__ __forceinline__ float wave_sum(float v)
 {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_mov<0xB1>(v);
+    v += dpp_mov<0x4E>(v);
+    v += dpp_mov<0x141>(v);
+    v += dpp_mov<0x140>(v);
+    return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
 // EPL = experts held per lane (ceil(E / 64)).  pieces = 3: row t of
@@ -458,23 +474,32 @@ __global__ __launch_bounds__(256) void route_select(const float *__restrict__ lo
             const int e = lane + 64 * i;
             sv[i] = (sel && e < E) ? l[i] + sel[e] : l[i];
         }
+        // each round: the largest untaken score (wave max), then the lowest
+        // expert id holding it (ballots; expert lane + 64 i, so slot order
+        // is id order)
         uint32_t taken = 0;
         for (int j = 0; j < k; ++j) {
             float bv = -INFINITY;
-            int bi = 0x7FFFFFFF;
 #pragma unroll
             for (int i = 0; i < EPL; ++i) {
                 const int e = lane + 64 * i;
-                if (e < E && !((taken >> i) & 1u) && (sv[i] > bv || bi == 0x7FFFFFFF))
-                    bv = sv[i], bi = e;
+                if (e < E && !((taken >> i) & 1u))
+                    bv = fmaxf(bv, sv[i]);
             }
+            const float m = wave_max(bv);
+            int bi = -1, first = -1;
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                const float ov = __shfl_xor(bv, o, 64);
-                const int oi = __shfl_xor(bi, o, 64);
-                if (ov > bv || (ov == bv && oi < bi))
-                    bv = ov, bi = oi;
+            for (int i = 0; i < EPL; ++i) {
+                const bool free_e = lane + 64 * i < E && !((taken >> i) & 1u);
+                const uint64_t hit = __ballot(free_e && sv[i] == m);
+                const uint64_t any = __ballot(free_e);
+                if (bi < 0 && hit != 0ull)
+                    bi = (int)__builtin_ctzll(hit) + 64 * i;
+                if (first < 0 && any != 0ull)
+                    first = (int)__builtin_ctzll(any) + 64 * i;
             }
+            if (bi < 0)
+                bi = first; // only NaN scores left: the lowest untaken id
             if ((bi & 63) == lane) {
                 const int slot = bi >> 6;
 #pragma unroll
