@@ -136,3 +136,33 @@ def test_forward_rejects_bad_arguments(lib):
     p.has_shared = 1
     assert lib.moe_forward(ctypes.byref(p), ctypes.byref(w), FAKE, FAKE, None, FAKE, 1 << 40, None) \
         == api.MOE_ERR_INVALID_ARG
+
+
+def test_backward_workspace_and_rejections(lib):
+    """moe_backward validates everything before enqueuing (no GPU touched)."""
+    from top_routing_expert_route_amd import api
+    p = api.Problem(4096, 4096, 8, 2, 16384, 0.0, 0, 0, 0, 0.01, api.MOE_BF16)
+    nb = lib.moe_backward_workspace_size(ctypes.byref(p))
+    # u, dh' (fp32) and dx rows (fp32) for 8192 rows, at least
+    assert nb >= 8192 * (16384 * 2 + 4096) * 4
+    assert nb > lib.moe_forward_workspace_size(ctypes.byref(p))
+    assert lib.moe_backward(None, None, None, None, 0.0, None, None, 0, None) == api.MOE_ERR_INVALID_ARG
+
+    p = api.Problem(64, 128, 8, 2, 128, 0.0, 0, 0, 0, 0.01, api.MOE_BF16)
+    w = api.Weights(FAKE, None, FAKE, None, FAKE, None, None, None, None, None)
+    full = dict(dx=FAKE, dw_router=FAKE, dw1=FAKE, dw2=FAKE)
+
+    def call(prob, grads, ws_bytes=1 << 40, g_aux=0.0):
+        g = api.Grads(**{n: grads.get(n) for n, _ in api.Grads._fields_})
+        return lib.moe_backward(ctypes.byref(prob), ctypes.byref(w), FAKE, FAKE, g_aux, ctypes.byref(g), FAKE,
+                                ws_bytes, None)
+
+    assert call(p, full, ws_bytes=16) == api.MOE_ERR_WORKSPACE
+    assert call(p, dict(full, dw1=None)) == api.MOE_ERR_INVALID_ARG
+    assert call(p, dict(full, db1=FAKE + 4)) == api.MOE_ERR_INVALID_ARG      # misaligned
+    assert call(p, full, g_aux=float("nan")) == api.MOE_ERR_INVALID_ARG
+    p.has_shared = 1                                                            # no shared weights/grads
+    assert call(p, full) == api.MOE_ERR_INVALID_ARG
+    p = api.Problem(64, 136, 8, 2, 128, 0.0, 0, 0, 0, 0.01, api.MOE_BF16)     # d % 64 != 0 in bf16
+    assert call(p, full) == api.MOE_ERR_UNSUPPORTED
+    assert b"multiples of 64" in lib.moe_last_error()
