@@ -453,7 +453,7 @@ struct BackwardWs {
     void *route_ws, *dispatch_ws, *gemm_ws, *router_ws;
     size_t gemm_ws_bytes;
     void *x_perm, *dyp, *du, *w1t, *w2t, *xT, *dyT, *duT, *gwT;
-    float *u, *dh, *dx_rows, *dwpart, *colpart;
+    float *u, *dh, *dx_rows, *dwpart, *colpart, *bias_part;
     int64_t Kp;
     size_t bytes;
 };
@@ -513,6 +513,7 @@ BackwardWs carve_backward(const moe_problem_t *p, const moe_grads_t *g, void *ba
     w.dwpart = cv.take<float>((size_t)max_rows * ((p->ffn + 63) / 64));
     const int64_t maxdim = p->d > p->ffn ? p->d : p->ffn;
     w.colpart = cv.take<float>((size_t)(w.Kp / 64) * maxdim);
+    w.bias_part = cv.take<float>(router_bias_ws_bytes(p->E) / sizeof(float));
     w.bytes = cv.off;
     return w;
 }
@@ -690,12 +691,14 @@ extern "C" moe_status_t moe_backward(const moe_problem_t *p, const moe_weights_t
     if (!s && router_on_mfma(p)) {
         s = launch_router_bwd_mfma(b.probs, b.topk_idx, b.slot_row, b.dwpart, (F + 63) / 64, w->b2, dy, d,
                                    p->expert_begin, b.f, c_aux, T, E, p->k, x, w->w_router, b.dl, g->dw_router,
-                                   g->db_router, &dx_r, b.router_ws, b.gemm_ws, b.gemm_ws_bytes, stream);
+                                   g->db_router, b.bias_part, &dx_r, b.router_ws, b.gemm_ws, b.gemm_ws_bytes,
+                                   stream);
     } else if (!s) {
         s = launch_router_bwd(b.probs, b.topk_idx, b.slot_row, b.dwpart, (F + 63) / 64, w->b2, dy, p->dtype, d,
                               p->expert_begin, b.f, c_aux, T, E, p->k, b.dl, stream);
         if (!s)
-            s = launch_router_wgrad(x, p->dtype, b.dl, T, d, E, g->dw_router, g->db_router, b.router_ws, stream);
+            s = launch_router_wgrad(x, p->dtype, b.dl, T, d, E, g->dw_router, g->db_router, b.bias_part,
+                                    b.router_ws, stream);
     }
     if (!s)
         s = launch_dx_combine(b.dx_rows, b.slot_row, p->k, p->has_shared ? g->dx : nullptr, dx_r, b.dl,

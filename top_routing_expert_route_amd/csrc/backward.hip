@@ -43,14 +43,6 @@ template <> struct Elt<uint16_t> {
     static __device__ __forceinline__ void st(uint16_t *p, int64_t i, float v) { p[i] = f32_to_bf16_bits(v); }
 };
 
-__device__ __forceinline__ float wave_sum(float v)
-{
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        v += __shfl_xor(v, o, 64);
-    return v;
-}
-
 // Rows of segment s: seg == NULL is one segment of `rows` rows.
 __device__ __forceinline__ void seg_rows(const int32_t *seg, int s, int64_t rows, int64_t &lo, int64_t &hi)
 {
@@ -394,19 +386,74 @@ __global__ __launch_bounds__(256) void act_bwd(const float *__restrict__ u, cons
     }
 }
 
-// out[s, f] = sum of colpart[ct, f] over segment s's column tiles, in tile
-// order (0 for an empty segment).  Grid (ceil(D / 256), S).
-__global__ __launch_bounds__(256) void seg_colsum(const float *__restrict__ colpart, const int32_t *__restrict__ kcol,
-                                                  int D, float *__restrict__ out)
+// out[s, f] = sum of colpart[ct, f] over segment s's column tiles (0 for an
+// empty segment).  Block = 64 features x 16 waves: wave w sums the tiles
+// c = kcol[s] + w + 16 i in order (256-byte rows), then the 16 partials are
+// added in wave order.  Grid (ceil(D / 64), S).
+__global__ __launch_bounds__(1024) void seg_colsum(const float *__restrict__ colpart, const int32_t *__restrict__ kcol,
+                                                   int D, float *__restrict__ out)
 {
+    __shared__ float red[16][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int s = blockIdx.y;
-    const int f = blockIdx.x * 256 + threadIdx.x;
-    if (f >= D)
-        return;
+    const int f = blockIdx.x * 64 + lane;
     float a = 0.f;
-    for (int ct = kcol[s]; ct < kcol[s + 1]; ++ct)
-        a += colpart[(int64_t)ct * D + f];
-    out[(int64_t)s * D + f] = a;
+    if (f < D)
+        for (int c = kcol[s] + wave; c < kcol[s + 1]; c += 16)
+            a += colpart[(int64_t)c * D + f];
+    red[wave][lane] = a;
+    __syncthreads();
+    if (wave == 0 && f < D) {
+        float t = 0.f;
+        for (int w = 0; w < 16; ++w)
+            t += red[w][lane];
+        out[(int64_t)s * D + f] = t;
+    }
+}
+
+constexpr int kMaxFastK = 8;
+
+// dl as two bf16 pieces, laid out (hi, hi, lo) for the dl . W_r GEMM.
+__device__ __forceinline__ void store_dl2(uint16_t *row, int e, int E64, float v)
+{
+    const uint16_t hi = f32_to_bf16_bits(v);
+    const uint16_t lo = f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
+    row[e] = hi;
+    row[E64 + e] = hi;
+    row[2 * E64 + e] = lo;
+}
+
+// dp and the softmax backward of one token when lane j holds selection j
+// (general k): the pairs are broadcast with shuffles.
+__device__ void slow_router_tail(const float *pt, const float *f, float c_aux, int E, int k, int my_e, float my_dw,
+                                 int lane, float *dlt, uint16_t *dl2t, int E64)
+{
+    float sd = 0.f;
+    for (int pass = 0; pass < 2; ++pass) {
+        const int eb = pass == 1 && dl2t ? E64 : E;
+        for (int b = 0; b < eb; b += 64) {
+            const int e = b + lane;
+            float dp = e < E ? c_aux * f[e] : 0.f;
+            for (int j = 0; j < k; ++j) {
+                const int ej = __shfl(my_e, j, 64);
+                const float dj = __shfl(my_dw, j, 64);
+                if (ej == e)
+                    dp += dj;
+            }
+            if (pass == 0) {
+                if (e < E)
+                    sd = fmaf(pt[e], dp, sd);
+            } else {
+                const float v = e < E ? pt[e] * (dp - sd) : 0.f;
+                if (e < E)
+                    dlt[e] = v;
+                if (dl2t && e < E64)
+                    store_dl2(dl2t, e, E64, v);
+            }
+        }
+        if (pass == 0)
+            sd = wave_sum(sd);
+    }
 }
 
 // Router backward, one wave per token: dw of every kept selection, then
@@ -425,28 +472,55 @@ __global__ __launch_bounds__(256) void router_bwd(const float *__restrict__ prob
     const int64_t t = (int64_t)blockIdx.x * 4 + wave;
     if (t >= Ttok)
         return; // wave-uniform; the block has no barrier
-    // lane j keeps selection j: its expert (-1 unless kept) and dw
-    int my_e = -1;
-    float my_dw = 0.f;
-    for (int j = 0; j < k; ++j) {
-        const int64_t slot = t * k + j;
-        const int r = slot_row[slot];
-        const int e = topk_idx[slot];
+    // (expert or -1 unless kept, dw) of selection j, held uniformly
+    int se[kMaxFastK];
+    float sw[kMaxFastK];
+    const bool fast = !b2 && k <= kMaxFastK && FT <= 8 * kMaxFastK;
+    if (fast) {
+        // 8 lanes per selection sum its row of partials; one DPP tree per group
+        const int j = lane >> 3, sub = lane & 7;
+        int e = -1;
         float a = 0.f;
-        if (r >= 0) {
-            for (int qt = lane; qt < FT; qt += 64)
-                a += dwpart[(int64_t)r * FT + qt];
-            if (b2) {
-                const T *brow = b2 + (int64_t)(e - e0) * d;
-                for (int o = lane; o < d; o += 64)
-                    a = fmaf(Elt<T>::ld(dY, t * d + o), Elt<T>::ld(brow, o), a);
+        if (j < k) {
+            const int r = slot_row[t * k + j];
+            if (r >= 0) {
+                e = topk_idx[t * k + j];
+                for (int qt = sub; qt < FT; qt += 8)
+                    a += dwpart[(int64_t)r * FT + qt];
             }
         }
-        a = wave_sum(a);
-        if (lane == j) {
-            my_e = r >= 0 ? e : -1;
-            my_dw = a;
+        a = group8_sum(a);
+#pragma unroll
+        for (int jj = 0; jj < kMaxFastK; ++jj) {
+            se[jj] = jj < k ? __builtin_amdgcn_readlane(e, 8 * jj) : -1;
+            sw[jj] = jj < k ? lane_value(a, 8 * jj) : 0.f;
         }
+    } else {
+        // lane j keeps selection j: its expert (-1 unless kept) and dw
+        int my_e = -1;
+        float my_dw = 0.f;
+        for (int j = 0; j < k; ++j) {
+            const int64_t slot = t * k + j;
+            const int r = slot_row[slot];
+            const int e = topk_idx[slot];
+            float a = 0.f;
+            if (r >= 0) {
+                for (int qt = lane; qt < FT; qt += 64)
+                    a += dwpart[(int64_t)r * FT + qt];
+                if (b2) {
+                    const T *brow = b2 + (int64_t)(e - e0) * d;
+                    for (int o = lane; o < d; o += 64)
+                        a = fmaf(Elt<T>::ld(dY, t * d + o), Elt<T>::ld(brow, o), a);
+                }
+            }
+            a = wave_sum(a);
+            if (lane == j) {
+                my_e = r >= 0 ? e : -1;
+                my_dw = a;
+            }
+        }
+        slow_router_tail(probs + t * E, f, c_aux, E, k, my_e, my_dw, lane, dl + t * E, dl2 ? dl2 + t * 3 * (int64_t)E64 : nullptr, E64);
+        return;
     }
     const float *pt = probs + t * E;
     float sd = 0.f;
@@ -455,12 +529,10 @@ __global__ __launch_bounds__(256) void router_bwd(const float *__restrict__ prob
         for (int b = 0; b < eb; b += 64) {
             const int e = b + lane;
             float dp = e < E ? c_aux * f[e] : 0.f;
-            for (int j = 0; j < k; ++j) {
-                const int ej = __shfl(my_e, j, 64);
-                const float dj = __shfl(my_dw, j, 64);
-                if (ej == e)
-                    dp += dj;
-            }
+#pragma unroll
+            for (int jj = 0; jj < kMaxFastK; ++jj)
+                if (se[jj] == e)
+                    dp += sw[jj];
             if (pass == 0) {
                 if (e < E)
                     sd = fmaf(pt[e], dp, sd);
@@ -468,15 +540,8 @@ __global__ __launch_bounds__(256) void router_bwd(const float *__restrict__ prob
                 const float v = e < E ? pt[e] * (dp - sd) : 0.f;
                 if (e < E)
                     dl[t * E + e] = v;
-                if (dl2 && e < E64) {
-                    // two bf16 pieces, laid out (hi, hi, lo) for the dl . W_r GEMM
-                    const uint16_t hi = f32_to_bf16_bits(v);
-                    const uint16_t lo = f32_to_bf16_bits(v - bf16_bits_to_f32(hi));
-                    uint16_t *row = dl2 + t * (3 * (int64_t)E64);
-                    row[e] = hi;
-                    row[E64 + e] = hi;
-                    row[2 * E64 + e] = lo;
-                }
+                if (dl2 && e < E64)
+                    store_dl2(dl2 + t * (3 * (int64_t)E64), e, E64, v);
             }
         }
         if (pass == 0)
@@ -636,25 +701,42 @@ __global__ __launch_bounds__(256) void router_wgrad_reduce(const float *__restri
     out[q] = a;
 }
 
-// db_r[e] = sum_t dl[t, e]: one block per expert, strided partial sums and a
-// fixed-shape tree.
-__global__ __launch_bounds__(256) void router_bias_grad(const float *__restrict__ dl, int64_t Ttok, int E,
-                                                        float *__restrict__ db)
+// db_r = column sums of dl [T, E].  First level: part[c, e] = sum of dl[t, e]
+// over token chunk c; a block takes 64 experts (a wave reads 256 contiguous
+// bytes per token) and 4 token lanes (t = t0 + j, t0 + j + 4, ...) whose
+// sums are added in lane order.  Second level: the same shape over the
+// chunk partials.  Grids (chunks, ceil(E / 64)) and ceil(E / 64).
+__global__ __launch_bounds__(256) void router_bias_part(const float *__restrict__ dl, int64_t Ttok, int E, int64_t tc,
+                                                        float *__restrict__ part)
 {
-    __shared__ float red[256];
-    const int e = blockIdx.x;
+    __shared__ float red[4][64];
+    const int el = threadIdx.x & 63, j = threadIdx.x >> 6;
+    const int e = blockIdx.y * 64 + el;
+    const int64_t t0 = (int64_t)blockIdx.x * tc, t1 = t0 + tc < Ttok ? t0 + tc : Ttok;
     float a = 0.f;
-    for (int64_t t = threadIdx.x; t < Ttok; t += 256)
-        a += dl[t * E + e];
-    red[threadIdx.x] = a;
+    if (e < E)
+        for (int64_t t = t0 + j; t < t1; t += 4)
+            a += dl[t * E + e];
+    red[j][el] = a;
     __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if ((int)threadIdx.x < w)
-            red[threadIdx.x] += red[threadIdx.x + w];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0)
-        db[e] = red[0];
+    if (j == 0 && e < E)
+        part[(int64_t)blockIdx.x * E + e] = ((red[0][el] + red[1][el]) + red[2][el]) + red[3][el];
+}
+
+__global__ __launch_bounds__(256) void router_bias_reduce(const float *__restrict__ part, int nch, int E,
+                                                          float *__restrict__ db)
+{
+    __shared__ float red[4][64];
+    const int el = threadIdx.x & 63, j = threadIdx.x >> 6;
+    const int e = blockIdx.x * 64 + el;
+    float a = 0.f;
+    if (e < E)
+        for (int c = j; c < nch; c += 4)
+            a += part[(int64_t)c * E + e];
+    red[j][el] = a;
+    __syncthreads();
+    if (j == 0 && e < E)
+        db[e] = ((red[0][el] + red[1][el]) + red[2][el]) + red[3][el];
 }
 
 // dx[t, i] = sum_e dl[t, e] W_r[e, i] (skipped when E = 0) + sum over t's
@@ -727,6 +809,8 @@ __global__ __launch_bounds__(256) void fill_zero(float *__restrict__ p, int64_t 
 
 unsigned strided_grid(int64_t n, int64_t cap) { return (unsigned)(n < 1 ? 1 : (n < cap ? n : cap)); }
 
+constexpr int kBiasChunks = 256; // token chunks of the router bias gradient
+
 } // namespace
 
 moe_status_t launch_fill_zero(float *p, int64_t n, hipStream_t stream)
@@ -787,8 +871,24 @@ moe_status_t launch_seg_colsum(const float *colpart, const int32_t *kcol, int S,
 {
     if (!out)
         return MOE_OK;
-    seg_colsum<<<dim3((unsigned)((D + 255) / 256), (unsigned)S), 256, 0, stream>>>(colpart, kcol, D, out);
+    seg_colsum<<<dim3((unsigned)((D + 63) / 64), (unsigned)S), 1024, 0, stream>>>(colpart, kcol, D, out);
     return check_launch("seg_colsum");
+}
+
+size_t router_bias_ws_bytes(int E) { return align_up((size_t)kBiasChunks * E * sizeof(float)); }
+
+// db_r[e] = sum_t dl[t, e]: chunk partials, then their sum in chunk order.
+static moe_status_t launch_router_bias_grad(const float *dl, int64_t T, int E, float *part, float *db_r,
+                                            hipStream_t stream)
+{
+    const int64_t most = (T + 63) / 64;
+    const int nch = (int)(most < kBiasChunks ? (most < 1 ? 1 : most) : kBiasChunks);
+    const int64_t tc = (T + nch - 1) / nch;
+    router_bias_part<<<dim3((unsigned)nch, (unsigned)((E + 63) / 64)), 256, 0, stream>>>(dl, T, E, tc, part);
+    if (moe_status_t s = check_launch("router_bias_part"))
+        return s;
+    router_bias_reduce<<<(unsigned)((E + 63) / 64), 256, 0, stream>>>(part, nch, E, db_r);
+    return check_launch("router_bias_reduce");
 }
 
 moe_status_t launch_router_bwd(const float *probs, const int32_t *topk_idx, const int32_t *slot_row,
@@ -825,7 +925,7 @@ size_t router_wgrad_ws_bytes(int64_t T, int d, int E)
 }
 
 moe_status_t launch_router_wgrad(const void *x, moe_dtype_t dt, const float *dl, int64_t T, int d, int E,
-                                 float *dw_r, float *db_r, void *ws, hipStream_t stream)
+                                 float *dw_r, float *db_r, float *bias_part, void *ws, hipStream_t stream)
 {
     const int nch = router_chunks(T, d, E);
     const int64_t tc = (T + nch - 1) / nch;
@@ -852,10 +952,8 @@ moe_status_t launch_router_wgrad(const void *x, moe_dtype_t dt, const float *dl,
     router_wgrad_reduce<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(part, nch, n, dw_r);
     if (moe_status_t s = check_launch("router_wgrad_reduce"))
         return s;
-    if (db_r) {
-        router_bias_grad<<<(unsigned)E, 256, 0, stream>>>(dl, T, E, db_r);
-        return check_launch("router_bias_grad");
-    }
+    if (db_r)
+        return launch_router_bias_grad(dl, T, E, bias_part, db_r, stream);
     return MOE_OK;
 }
 
@@ -892,8 +990,8 @@ size_t router_mfma_ws_bytes(int64_t T, int d, int E)
 moe_status_t launch_router_bwd_mfma(const float *probs, const int32_t *topk_idx, const int32_t *slot_row,
                                     const float *dwpart, int FT, const void *b2, const void *dY, int d, int e0,
                                     const float *f, float c_aux, int64_t T, int E, int k, const void *x,
-                                    const float *w_r, float *dl, float *dw_r, float *db_r, float **dx_r, void *ws,
-                                    void *gemm_ws, size_t gemm_ws_bytes, hipStream_t stream)
+                                    const float *w_r, float *dl, float *dw_r, float *db_r, float *bias_part,
+                                    float **dx_r, void *ws, void *gemm_ws, size_t gemm_ws_bytes, hipStream_t stream)
 {
     const int E64 = (E + 63) / 64 * 64;
     const int nc = router_mfma_chunks(T, d, E);
@@ -943,11 +1041,9 @@ moe_status_t launch_router_bwd_mfma(const float *probs, const int32_t *topk_idx,
     router_wgrad_pieces_reduce<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(part, nc, E, d, dw_r);
     if (moe_status_t s = check_launch("router_wgrad_pieces_reduce"))
         return s;
-    if (db_r) {
-        router_bias_grad<<<(unsigned)E, 256, 0, stream>>>(dl, T, E, db_r);
-        if (moe_status_t s = check_launch("router_bias_grad"))
+    if (db_r)
+        if (moe_status_t s = launch_router_bias_grad(dl, T, E, bias_part, db_r, stream))
             return s;
-    }
     *dx_r = dxr;
     return MOE_OK;
 }

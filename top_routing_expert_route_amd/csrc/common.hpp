@@ -78,6 +78,46 @@ __device__ __forceinline__ void gelu_and_grad(float u, float &g, float &gp)
     gp = fmaf(u, e * 0.39894228040143268f, Phi);
 }
 
+// Wave reductions without the LDS crossbar: DPP moves within rows of 16
+// lanes (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror: after the first three steps every lane holds its group of 8
+// lanes' result, after the fourth its row of 16), then the four row results
+// are read into scalars and combined in a fixed order.  Every lane must be
+// active.
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float lane_value(float v, int lane)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+__device__ __forceinline__ float group8_sum(float v)
+{
+    v += dpp_mov<0xB1>(v);
+    v += dpp_mov<0x4E>(v);
+    v += dpp_mov<0x141>(v);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+    v = fmaxf(v, dpp_mov<0xB1>(v));
+    v = fmaxf(v, dpp_mov<0x4E>(v));
+    v = fmaxf(v, dpp_mov<0x141>(v));
+    v = fmaxf(v, dpp_mov<0x140>(v));
+    return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+    v = group8_sum(v);
+    v += dpp_mov<0x140>(v);
+    return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
+}
+
 // ------------------------------------------------------------ workspaces --
 constexpr size_t kAlign = 256;
 __host__ __device__ constexpr size_t align_up(size_t n, size_t a = kAlign) { return (n + a - 1) / a * a; }
@@ -163,8 +203,9 @@ moe_status_t launch_router_bwd(const float *probs, const int32_t *topk_idx, cons
                                int e0, const float *f, float c_aux, int64_t T, int E, int k, float *dl,
                                hipStream_t stream);
 size_t router_wgrad_ws_bytes(int64_t T, int d, int E);
+size_t router_bias_ws_bytes(int E); // bias_part of the router launchers
 moe_status_t launch_router_wgrad(const void *x, moe_dtype_t dt, const float *dl, int64_t T, int d, int E,
-                                 float *dw_r, float *db_r, void *ws, hipStream_t stream);
+                                 float *dw_r, float *db_r, float *bias_part, void *ws, hipStream_t stream);
 // dx = kept dx rows + dx_sh (may be NULL) + the router term: dx_r if given,
 // else dl . W_r on the vector units.
 moe_status_t launch_dx_combine(const float *dx_rows, const int32_t *slot_row, int k, const float *dx_sh,
@@ -178,7 +219,7 @@ size_t router_mfma_ws_bytes(int64_t T, int d, int E);
 moe_status_t launch_router_bwd_mfma(const float *probs, const int32_t *topk_idx, const int32_t *slot_row,
                                     const float *dwpart, int FT, const void *b2, const void *dY, int d, int e0,
                                     const float *f, float c_aux, int64_t T, int E, int k, const void *x,
-                                    const float *w_r, float *dl, float *dw_r, float *db_r, float **dx_r, void *ws,
-                                    void *gemm_ws, size_t gemm_ws_bytes, hipStream_t stream);
+                                    const float *w_r, float *dl, float *dw_r, float *db_r, float *bias_part,
+                                    float **dx_r, void *ws, void *gemm_ws, size_t gemm_ws_bytes, hipStream_t stream);
 
 } // namespace moe

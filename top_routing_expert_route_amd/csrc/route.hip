@@ -371,38 +371,6 @@ __global__ __launch_bounds__(256) void route_logits_f32(const float *__restrict_
     logits[i] = s;
 }
 
-// Wave reductions without the LDS crossbar: DPP moves within rows of 16
-// lanes (quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
-// row_mirror: after the four steps every lane holds its row's result), then
-// the four row results are read into scalars and combined in a fixed order.
-template <int CTRL> __device__ __forceinline__ float dpp_mov(float v)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-
-__device__ __forceinline__ float lane_value(float v, int lane)
-{
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
-}
-
-__device__ __forceinline__ float wave_max(float v)
-{
-    v = fmaxf(v, dpp_mov<0xB1>(v));
-    v = fmaxf(v, dpp_mov<0x4E>(v));
-    v = fmaxf(v, dpp_mov<0x141>(v));
-    v = fmaxf(v, dpp_mov<0x140>(v));
-    return fmaxf(fmaxf(lane_value(v, 0), lane_value(v, 16)), fmaxf(lane_value(v, 32), lane_value(v, 48)));
-}
-
-__device__ __forceinline__ float wave_sum(float v)
-{
-    v += dpp_mov<0xB1>(v);
-    v += dpp_mov<0x4E>(v);
-    v += dpp_mov<0x141>(v);
-    v += dpp_mov<0x140>(v);
-    return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
-}
-
 // EPL = experts held per lane (ceil(E / 64)).  pieces = 3: row t of
 // `logits` holds three column blocks of E (hi, mid, lo router pieces) whose
 // sum (mid + lo) + hi is the logit; pieces = 1: plain [T, E] logits.
