@@ -7,6 +7,12 @@ synthetic layers already resident in HBM.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
+Beside the mean step time the line carries the median and minimum of the
+same steps timed one by one; the HBM-bound stages (route, dispatch, combine)
+timed warm and cold (a 1 GiB copy before each evicts L2 and the MALL); a
+plain 1 GiB device copy as the practical HBM ceiling; and the oracle on all
+cores (cpu_baseline) and on one thread.
+
 The roofline entry covers the dominant kernel (the first grouped GEMM with
 the fused GELU): algorithmic flops of one launch (2 * rows * d * ffn, rows =
 the kept (token, expert) pairs of the run) over its average duration, timed
@@ -53,6 +59,45 @@ def _traffic(workload: str, kernel: str):
         return None
 
 
+_ROUTED = {}  # the oracle's routing and capacity plan of a layer, from cpu_baseline
+
+
+def cpu_baseline_single_thread(inp, budget_s: float = 5.0) -> dict:
+    """The oracle on one thread: routing of the first min(T, 512) tokens and
+    the expert FFN + combine of a seeded token sample sized to about budget_s
+    seconds, each scaled per token (routing and the FFN are per-token work;
+    the statistics and capacity passes are integer bookkeeping)."""
+    import numpy as np
+    import oracle
+    from top_routing_expert_route_amd import workloads as wl
+    w = inp.w
+    n_r = min(w.T, 512)
+    t0 = time.perf_counter()
+    oracle.route(inp.x[:n_r], inp.w_router, inp.b_router, w.k, threads=1, want_logits=False)
+    t_route = (time.perf_counter() - t0) / n_r
+    if id(inp) in _ROUTED:
+        r, dp = _ROUTED[id(inp)]
+    else:
+        r = oracle.route(inp.x, inp.w_router, inp.b_router, w.k, threads=len(os.sched_getaffinity(0)),
+                         want_logits=False)
+        dp = oracle.capacity(r.topk_idx, w.E, float(np.float32(w.capacity_factor)), w.expert_begin,
+                             w.num_local_experts)
+
+    def ffn(tokens):
+        s = time.perf_counter()
+        oracle.combine(inp.x, tokens, r.topk_idx, r.topk_w, dp.slot_row, inp.w1, inp.b1, inp.w2, inp.b2,
+                       w.expert_begin, inp.ws1, inp.bs1, inp.ws2, inp.bs2, threads=1)
+        return time.perf_counter() - s
+
+    probe = ffn(wl.token_sample(w.T, 1, seed=98))
+    n = int(min(w.T, max(1, (budget_s - probe) / max(probe, 1e-9))))
+    tok = wl.token_sample(w.T, n, seed=101)
+    t_ffn = ffn(tok) / len(tok)
+    return {"value": round(1.0 / (t_route + t_ffn), 3), "unit": "tokens/s", "cores": 1,
+            "sample": "fp64 oracle on 1 thread: routing of %d tokens (%.3f ms/token), expert FFN+combine of a "
+                      "seeded sample of %d tokens (%.1f ms/token)" % (n_r, t_route * 1e3, len(tok), t_ffn * 1e3)}
+
+
 def cpu_baseline(inp, budget_s: float = 15.0) -> dict:
     """The oracle, as it stands, on a bounded sample of the same workload:
     routing, statistics and capacity over all T tokens, the expert FFN and
@@ -68,6 +113,7 @@ def cpu_baseline(inp, budget_s: float = 15.0) -> dict:
     dp = oracle.capacity(r.topk_idx, w.E, float(np.float32(w.capacity_factor)), w.expert_begin,
                          w.num_local_experts)
     t_route = time.perf_counter() - t0
+    _ROUTED[id(inp)] = (r, dp)
 
     def ffn(tokens):
         s = time.perf_counter()
@@ -87,6 +133,34 @@ def cpu_baseline(inp, budget_s: float = 15.0) -> dict:
             "sample": "fp64 oracle: route+stats+capacity over all %d tokens (%.2f s), expert FFN+combine on a "
                       "seeded sample of %d tokens (%.2f s); tokens/s = 1/(t_route/T + t_ffn/n)"
                       % (w.T, t_route, len(tok), t_ffn)}
+
+
+def _median(v):
+    v = sorted(v)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+
+
+def hbm_copy_ceiling(torch, dev, reps: int = 5) -> dict:
+    """A plain 1 GiB device-to-device copy timed with HIP events: the
+    practical HBM ceiling beside the nominal 8 TB/s (2 GiB moved a copy)."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    stream = torch.cuda.current_stream(dev)
+    us = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        b.copy_(a)
+        e1.record(stream)
+        e1.synchronize()
+        us.append(e0.elapsed_time(e1) * 1e3)
+    del a, b
+    best = min(us)
+    return {"bytes_moved": 2 * n, "us_median": round(_median(us), 1), "us_min": round(best, 1),
+            "gbps_best": round(2 * n / (best * 1e-6) / 1e9, 1)}
 
 
 def main():
@@ -149,6 +223,17 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = w.T * args.steps / elapsed
 
+    # ---- per-step spread: the same steps, each between two HIP events ----
+    stream = torch.cuda.current_stream(dev)
+    step_ms = []
+    for _ in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        layer.forward(x, y)
+        e1.record(stream)
+        e1.synchronize()
+        step_ms.append(e0.elapsed_time(e1))
+
     # ---- with a shared expert: the same step with it on a second stream ----
     overlap = None
     if w.shared_expert:
@@ -177,8 +262,13 @@ def main():
                            tokens_with_rows=int((slot_row >= 0).any(axis=1).sum()), shared=w.shared_expert,
                            has_router_bias=inp.b_router is not None)
 
+    def tflops(flops, us):
+        return flops / (us * 1e-6) / 1e12 if us > 0 else 0.0
+
+    def gbps(b, us):
+        return b / (us * 1e-6) / 1e9 if us > 0 else 0.0
+
     # ---- per-stage timing with HIP events on the launch stream ----
-    stream = torch.cuda.current_stream(dev)
     names = ["route", "dispatch", "gemm1_gelu", "gemm2", "shared", "combine"]
     acc_ms = {n: 0.0 for n in names}
     r_buf = {}
@@ -225,12 +315,6 @@ def main():
             acc_ms[n] += ev[i].elapsed_time(ev[i + 1])
     avg_us = {n: acc_ms[n] * 1e3 / args.steps for n in names}
 
-    def tflops(flops, us):
-        return flops / (us * 1e-6) / 1e12 if us > 0 else 0.0
-
-    def gbps(b, us):
-        return b / (us * 1e-6) / 1e9 if us > 0 else 0.0
-
     g1_flops = acc.gemm1_flops(counts)
     g1_tf = tflops(g1_flops, avg_us["gemm1_gelu"])
     stages = {
@@ -251,6 +335,45 @@ def main():
                             "mfma_frac": round(tflops(acc.shared_flops(counts), avg_us["shared"]) /
                                                acc.PEAK_BF16_TFLOPS, 4)}
     staged_total = sum(avg_us.values())
+
+    # ---- cold HBM-bound stages: a 1 GiB copy (512 MiB read, 512 MiB written)
+    # before each timed stage evicts L2 and the 256 MB MALL ----
+    sa = torch.empty(1 << 29, dtype=torch.uint8, device=dev).fill_(3)
+    sb = torch.empty_like(sa)
+    cold = {"route": [], "dispatch": [], "combine": []}
+
+    def timed(fn):
+        sb.copy_(sa)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        out = fn()
+        e1.record(stream)
+        return out, (e0, e1)
+
+    cold_reps = max(5, min(args.steps, 10))
+    for _ in range(cold_reps + 1):
+        r, ev_r = timed(lambda: api.moe_route(x, t["w_router"], t["b_router"], w.k, w.alpha, sel_bias=t["sel_bias"]))
+        dp, ev_d = timed(lambda: api.moe_dispatch(x, r["topk_idx"], w.E, w.capacity_factor, w.expert_begin,
+                                                  w.num_local_experts))
+        h = api.moe_grouped_gemm(dp["x_perm"], dp["seg_offsets"], t["w1"], t["b1"], 1, out=dp_ws["h"])
+        yp = api.moe_grouped_gemm(h, dp["seg_offsets"], t["w2"], t["b2"], 0, out=dp_ws["yp"])
+        ysh = None
+        if w.shared_expert:
+            hs = api.moe_grouped_gemm(x, None, t["ws1"].unsqueeze(0), None, 1)
+            ysh = api.moe_grouped_gemm(hs, None, t["ws2"].unsqueeze(0), None, 0)
+        _, ev_c = timed(lambda: api.moe_combine(yp, dp["slot_row"], r["topk_w"], ysh, y=y))
+        torch.cuda.synchronize()
+        for n, (e0, e1) in (("route", ev_r), ("dispatch", ev_d), ("combine", ev_c)):
+            cold[n].append(e0.elapsed_time(e1) * 1e3)
+    del sa, sb
+    cold_bytes = {"route": acc.route_bytes(counts), "dispatch": acc.dispatch_bytes(counts),
+                  "combine": acc.combine_bytes(counts)}
+    stages_cold = {}
+    for n, v in cold.items():
+        v = v[1:]  # the first round warms up the allocator
+        med = _median(v)
+        stages_cold[n] = {"us_median": round(med, 2), "us_min": round(min(v), 2), "bytes": cold_bytes[n],
+                          "hbm_frac_median": round(gbps(cold_bytes[n], med) / acc.PEAK_HBM_GBPS, 4)}
 
     # ---- backward: K steps of moe_backward on the same layer (dL/dY seeded
     # Gaussian, dL/dL_aux = 1); reported beside the forward, not in `value` ----
@@ -297,8 +420,12 @@ def main():
                      "traffic": _traffic(w.name, "gemm1_gelu"),
                      "kernel": "grouped_gemm_256 (first Linear + GELU)",
                      "flops_per_launch": g1_flops, "avg_us": round(avg_us["gemm1_gelu"], 2)},
+        "step_ms": {"mean": round(ms_per_step, 4), "median": round(_median(step_ms), 4),
+                    "min": round(min(step_ms), 4)},
         "stages": stages,
+        "stages_cold": stages_cold,
         "staged_step_us": round(staged_total, 1),
+        "hbm_copy": hbm_copy_ceiling(torch, dev),
     }
     if overlap is not None:
         result["shared_overlap"] = overlap
@@ -306,6 +433,7 @@ def main():
         result["backward"] = backward
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp)
+        result["cpu_baseline"]["single_thread"] = cpu_baseline_single_thread(inp)
     print(json.dumps(result))
 
 
