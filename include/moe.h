@@ -181,7 +181,7 @@ moe_status_t moe_dispatch(const void *x, moe_dtype_t dtype, const int32_t *topk_
  * reproducible); without it every tile runs whole.
  * Errors: INVALID_ARG for sizes < 1 (max_rows = 0 is a no-op), NULL a, w or
  * out, misaligned buffers; UNSUPPORTED for N or K not a multiple of 8,
- * activation not 0 or 1, more than 1024 segments.
+ * K above 2^21, activation not 0 or 1, more than 1024 segments.
  * ------------------------------------------------------------------------ */
 size_t moe_grouped_gemm_workspace_size(void);
 moe_status_t moe_grouped_gemm(const void *a, const int32_t *seg_offsets, int num_segments,
@@ -325,7 +325,8 @@ moe_status_t moe_forward_overlap(const moe_problem_t *p, const moe_weights_t *w,
  * reduction in fp32.  Results are bitwise reproducible run to run.
  * Every buffer is 16-byte aligned.
  * Sizes: as moe_forward; MOE_BF16 also needs d and ffn multiples of 64 and at
- * least 128 (else MOE_ERR_UNSUPPORTED).
+ * least 128, and the weight-gradient GEMMs at most 2^21 columns (about the
+ * layer's kept rows plus 128 per local expert) (else MOE_ERR_UNSUPPORTED).
  * ws: moe_backward_workspace_size(p) bytes.
  * Errors: as moe_forward.
  * ------------------------------------------------------------------------ */

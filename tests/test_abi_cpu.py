@@ -114,6 +114,9 @@ def test_gemm_and_combine_reject_bad_arguments(lib):
     assert g(P, P, 0, 100, 64, 64, 1, P, None, 0, P) == api.MOE_ERR_INVALID_ARG
     assert g(P, P, 2000, 100, 64, 64, 1, P, None, 0, P) == api.MOE_ERR_UNSUPPORTED
     assert g(None, P, 4, 100, 64, 64, 1, P, None, 0, P) == api.MOE_ERR_INVALID_ARG
+    # K past 2^21: a 256-row operand tile would not fit one 32-bit buffer record
+    assert g(P, P, 4, 100, 64, (1 << 21) + 64, 1, P, None, 0, P) == api.MOE_ERR_UNSUPPORTED
+    assert b"buffer" in lib.moe_last_error()
     assert lib.moe_grouped_gemm(P, P, 4, 100, 64, 64, 1, P, None, 0, P, P + 4, 1 << 30, None) \
         == api.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(P, 10, P, P, None, 4, 64, 33, 1, P, None) == api.MOE_ERR_UNSUPPORTED
@@ -166,3 +169,7 @@ def test_backward_workspace_and_rejections(lib):
     p = api.Problem(64, 136, 8, 2, 128, 0.0, 0, 0, 0, 0.01, api.MOE_BF16)     # d % 64 != 0 in bf16
     assert call(p, full) == api.MOE_ERR_UNSUPPORTED
     assert b"multiples of 64" in lib.moe_last_error()
+    # 2^20 tokens x k = 2 rows: the weight-gradient GEMMs would need > 2^21 columns
+    p = api.Problem(1 << 20, 128, 8, 2, 128, 0.0, 0, 0, 0, 0.01, api.MOE_BF16)
+    assert call(p, full) == api.MOE_ERR_UNSUPPORTED
+    assert b"columns" in lib.moe_last_error()

@@ -38,6 +38,10 @@ namespace {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Largest reduction length of a GEMM: the kernels address a 256-row operand
+// tile through one buffer record of at most 2^31 bytes (256 x K x 4).
+constexpr int kMaxK = 1 << 21;
+
 int local_count(int E, int num_local_experts) { return num_local_experts > 0 ? num_local_experts : E; }
 
 moe_status_t check_ws(void *ws, size_t ws_bytes, size_t need, const char *who)
@@ -114,6 +118,9 @@ moe_status_t check_gemm_args(const void *a, const int32_t *seg, int S, int64_t m
         return fail(MOE_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", who);
     if (N % 8 != 0 || K % 8 != 0 || act < 0 || act > 1 || (seg && S > 1024))
         return fail(MOE_ERR_UNSUPPORTED, "%s: needs N, K multiples of 8, activation 0/1, <= 1024 segments", who);
+    if (K > kMaxK)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: K = %d above %d (a 256-row operand tile must fit a 32-bit buffer "
+                    "record)", who, K, kMaxK);
     if (max_rows > (int64_t)INT32_MAX)
         return fail(MOE_ERR_UNSUPPORTED, "%s: rows must fit int32", who);
     return MOE_OK;
@@ -626,6 +633,9 @@ extern "C" moe_status_t moe_backward(const moe_problem_t *p, const moe_weights_t
         return fail(MOE_ERR_UNSUPPORTED, "backward: bf16 needs d and ffn multiples of 64, at least 128 (d=%d ffn=%d)",
                     p->d, p->ffn);
     const BackwardWs need = carve_backward(p, g, nullptr);
+    if (need.Kp > kMaxK)
+        return fail(MOE_ERR_UNSUPPORTED, "backward: %lld columns in the weight-gradient GEMMs, above %d",
+                    (long long)need.Kp, kMaxK);
     if (moe_status_t s = check_ws(ws, ws_bytes, need.bytes, "backward"))
         return s;
     const BackwardWs b = carve_backward(p, g, ws);
