@@ -269,16 +269,20 @@ __global__ __launch_bounds__(256) void gather_t(const T *__restrict__ src, int D
 }
 
 // GELU backward over the K-segmented rows (same row/column map as gather_t),
-// from u = W1 x + b1 and dh' (both fp32 [rows, F], F % 8 == 0):
+// from u = W1 x + b1 and dh' (both fp32 [rows, F], F % 4 == 0):
 //   du[r, q]  = w_r dh'[r, q] GELU'(u[r, q])        (row-major, T)
 //   duT[q, col] = du[r, q],  gwT[q, col] = w_r GELU(u[r, q])   (zero padding)
 //   dwpart[r, qt] = sum_{q in feature tile qt} dh'[r, q] GELU(u[r, q])   (if dwpart)
 //   colpart[ct, q] = sum over the tile's rows of du[r, q]               (if colpart)
-// w_r = wgt[row_src[r]] (1 when wgt is NULL).  A wave takes a 64-row column
-// tile x 64 features; each lane an 8 x 8 block (rows 8 rg.., features 8 cg..),
-// so row-major and transposed accesses are all 16-byte vectors.  Sums over a
-// tile's features / rows are fixed shuffle trees.  Grid (ceil(F / 256),
-// strided over the column tiles); FT = ceil(F / 64).
+// w_r = wgt[row_src[r]] (1 when wgt is NULL).  A block takes one 64-row
+// column tile x 64 features.  Thread (wave w, lane l) holds a 4 x 4 block:
+// features 4 (l % 16).., rows 16 (l / 16) + 4 w..; one load instruction of a
+// wave reads 4 rows of 256 contiguous bytes.  du goes out row-major from
+// registers; duT and gwT go through LDS ([feature][row], rows padded to a
+// 16-byte multiple) and out as 16-byte row pieces of the transposed arrays.
+// Row sums over the 16 lanes of a row are DPP trees, column sums add the
+// thread's rows, the wave's four row groups and then the waves in order.
+// Grid (FT = ceil(F / 64), strided over the column tiles).
 template <class T>
 __global__ __launch_bounds__(256) void act_bwd(const float *__restrict__ u, const float *__restrict__ dh, int F,
                                                int FT, const int32_t *__restrict__ row_src,
@@ -287,100 +291,107 @@ __global__ __launch_bounds__(256) void act_bwd(const float *__restrict__ u, cons
                                                T *__restrict__ du, T *__restrict__ duT, T *__restrict__ gwT,
                                                float *__restrict__ dwpart, float *__restrict__ colpart)
 {
+    constexpr int ES = (int)sizeof(T);
+    constexpr int LS = 64 + 16 / ES;            // LDS row (one feature) of 64 rows, padded
+    constexpr int VPC = 16 / ES;                // elements per 16-byte piece
+    constexpr int LPR = 64 / VPC;               // lanes per transposed row (feature)
+    constexpr int FPP = 256 / LPR;              // features per pass of the block
+    __shared__ __attribute__((aligned(16))) T sdu[64 * LS];
+    __shared__ __attribute__((aligned(16))) T sgw[64 * LS];
+    __shared__ float red[4][64];
+
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int cg = lane & 7, rg = lane >> 3;
-    const int qt = blockIdx.x * 4 + wave;
-    const int q0 = qt * 64 + cg * 8;
-    if (qt * 64 >= F)
-        return; // whole wave; there is no barrier below
-    // lanes past F (F % 64 != 0) take part in the shuffles with zeros
-    const bool qv = q0 < F;
+    const int c = lane & 15, rq = lane >> 4;
+    const int qt = blockIdx.x;
+    const int fl = 4 * c;                       // first feature of the thread within the tile
+    const int q = qt * 64 + fl;
+    const bool qv = q < F;                      // F % 4 == 0: all four features or none
+    const int rl = 16 * rq + 4 * wave;          // first row of the thread within the tile
     const int total = kcol[S];
     for (int ct = blockIdx.y; ct < total; ct += gridDim.y) {
         const int s = seg_of_tile(kcol, S, ct);
         int64_t lo, hi;
         seg_rows(seg, s, rows, lo, hi);
-        const int64_t r0 = lo + (int64_t)(ct - kcol[s]) * 64 + rg * 8;
-        float rs[8], w[8];
+        const int64_t rt = lo + (int64_t)(ct - kcol[s]) * 64; // tile's first row
+        f32x4 uu[4], hh[4];
+        float w[4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int64_t r = r0 + i;
-            w[i] = (r < hi && qv) ? (wgt ? wgt[row_src ? row_src[r] : r] : 1.f) : 0.f;
-            rs[i] = 0.f;
+        for (int i = 0; i < 4; ++i) {
+            const int64_t r = rt + rl + i;
+            const bool ok = r < hi && qv;
+            uu[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            hh[i] = uu[i];
+            if (ok) {
+                uu[i] = *reinterpret_cast<const f32x4 *>(u + r * F + q);
+                hh[i] = *reinterpret_cast<const f32x4 *>(dh + r * F + q);
+            }
+            w[i] = ok ? (wgt ? wgt[row_src ? row_src[r] : r] : 1.f) : 0.f;
         }
-        const int64_t col = (int64_t)ct * 64 + rg * 8;
-        // two halves of 4 features keep the live state small
-#pragma unroll 1
-        for (int hf = 0; hf < 2; ++hf) {
-            const int q = q0 + 4 * hf;
-            float vdu[8][4], vgw[8][4];
+        float vdu[4][4], vgw[4][4], rs[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int64_t r = r0 + i;
-                const bool ok = r < hi && qv;
-                f32x4 uu = {0.f, 0.f, 0.f, 0.f}, hh = uu;
-                if (ok) {
-                    uu = *reinterpret_cast<const f32x4 *>(u + r * F + q);
-                    hh = *reinterpret_cast<const f32x4 *>(dh + r * F + q);
-                }
-                float acc = 0.f;
+        for (int i = 0; i < 4; ++i) {
+            const int64_t r = rt + rl + i;
+            float acc = 0.f;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float g, gp;
-                    gelu_and_grad(uu[j], g, gp);
-                    vdu[i][j] = ok ? w[i] * hh[j] * gp : 0.f;
-                    vgw[i][j] = ok ? w[i] * g : 0.f;
-                    acc = fmaf(hh[j], g, acc);
-                }
-                rs[i] += ok ? acc : 0.f;
-                if (ok)
-                    store4v<T>(du + r * F + q, vdu[i]);
+            for (int j = 0; j < 4; ++j) {
+                float g, gp;
+                gelu_and_grad(uu[i][j], g, gp);
+                vdu[i][j] = w[i] * hh[i][j] * gp; // zero outside the segment (w = 0)
+                vgw[i][j] = w[i] * g;
+                acc = fmaf(hh[i][j], g, acc);
             }
-            if (colpart) {
-                // column sums over the tile's 64 rows: the 8 lanes of a feature group
-                f32x4 cs;
+            rs[i] = acc;
+            if (r < hi && qv)
+                store4v<T>(du + r * F + q, vdu[i]);
+        }
+        // transposed through LDS: feature fl + j, rows rl .. rl + 3
+        __syncthreads(); // the previous tile's LDS reads are done
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float v = ((vdu[0][j] + vdu[1][j]) + (vdu[2][j] + vdu[3][j])) +
-                              ((vdu[4][j] + vdu[5][j]) + (vdu[6][j] + vdu[7][j]));
-                    v += __shfl_xor(v, 8, 64);
-                    v += __shfl_xor(v, 16, 64);
-                    v += __shfl_xor(v, 32, 64);
-                    cs[j] = v;
-                }
-                if (rg == 0 && qv)
-                    *reinterpret_cast<f32x4 *>(colpart + (int64_t)ct * F + q) = cs;
-            }
-            // transposed: feature row q + j, columns 64 ct + 8 rg .. + 8
-            if (qv) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float a8[8], g8[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        a8[i] = vdu[i][j];
-                        g8[i] = vgw[i][j];
-                    }
-                    store8<T>(duT + (int64_t)(q + j) * Kp + col, a8);
-                    store8<T>(gwT + (int64_t)(q + j) * Kp + col, g8);
-                }
-            }
+        for (int j = 0; j < 4; ++j) {
+            const float a4[4] = {vdu[0][j], vdu[1][j], vdu[2][j], vdu[3][j]};
+            const float g4[4] = {vgw[0][j], vgw[1][j], vgw[2][j], vgw[3][j]};
+            store4v<T>(sdu + (fl + j) * LS + rl, a4);
+            store4v<T>(sgw + (fl + j) * LS + rl, g4);
         }
         if (dwpart) {
-            // row sums over the tile's 64 features: the 8 lanes of a row group
+            // row sums over the tile's 64 features: the row's 16 lanes
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float v = rs[i];
-                v += __shfl_xor(v, 1, 64);
-                v += __shfl_xor(v, 2, 64);
-                v += __shfl_xor(v, 4, 64);
-                rs[i] = v;
+            for (int i = 0; i < 4; ++i) {
+                const float v = row16_sum(rs[i]);
+                const int64_t r = rt + rl + i;
+                if (c == 0 && r < hi)
+                    dwpart[r * FT + qt] = v;
             }
-            if (cg == 0) {
+        }
+        if (colpart) {
+            // column sums over the tile's 64 rows
+            f32x4 cs;
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    if (r0 + i < hi)
-                        dwpart[(r0 + i) * FT + qt] = rs[i];
+            for (int j = 0; j < 4; ++j) {
+                float v = (vdu[0][j] + vdu[1][j]) + (vdu[2][j] + vdu[3][j]);
+                v += __shfl_xor(v, 16, 64);
+                v += __shfl_xor(v, 32, 64);
+                cs[j] = v;
+            }
+            if (rq == 0)
+                *reinterpret_cast<f32x4 *>(&red[wave][fl]) = cs;
+        }
+        __syncthreads();
+        if (colpart && threadIdx.x < 64) {
+            const int f = threadIdx.x;
+            const float v = (red[0][f] + red[1][f]) + (red[2][f] + red[3][f]);
+            if (qt * 64 + f < F)
+                colpart[(int64_t)ct * F + qt * 64 + f] = v;
+        }
+        // transposed rows: feature fq, a 16-byte piece of the tile's 64 columns
+#pragma unroll
+        for (int p = 0; p < 64 / FPP; ++p) {
+            const int fq = p * FPP + threadIdx.x / LPR;
+            const int piece = threadIdx.x % LPR;
+            if (qt * 64 + fq < F) {
+                const int64_t at = (int64_t)(qt * 64 + fq) * Kp + (int64_t)ct * 64 + piece * VPC;
+                *reinterpret_cast<u32x4 *>(duT + at) = *reinterpret_cast<const u32x4 *>(sdu + fq * LS + piece * VPC);
+                *reinterpret_cast<u32x4 *>(gwT + at) = *reinterpret_cast<const u32x4 *>(sgw + fq * LS + piece * VPC);
             }
         }
     }
@@ -854,9 +865,8 @@ moe_status_t launch_act_bwd(const float *u, const float *dh, int F, const int32_
                             void *du, void *duT, void *gwT, float *dwpart, float *colpart, hipStream_t stream)
 {
     const int64_t ctiles = Kp / 64;
-    const int fx = (F + 255) / 256;
     const int FT = (F + 63) / 64;
-    const dim3 g((unsigned)fx, strided_grid(ctiles, (4096 + fx - 1) / fx));
+    const dim3 g((unsigned)FT, strided_grid(ctiles, (32768 + FT - 1) / FT));
     if (dt == MOE_BF16)
         act_bwd<uint16_t><<<g, 256, 0, stream>>>(u, dh, F, FT, row_src, wgt, seg, S, rows, kcol, Kp, (uint16_t *)du,
                                                  (uint16_t *)duT, (uint16_t *)gwT, dwpart, colpart);

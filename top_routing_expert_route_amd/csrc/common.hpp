@@ -102,6 +102,13 @@ __device__ __forceinline__ float group8_sum(float v)
     return v;
 }
 
+__device__ __forceinline__ float row16_sum(float v)
+{
+    v = group8_sum(v);
+    v += dpp_mov<0x140>(v);
+    return v;
+}
+
 __device__ __forceinline__ float wave_max(float v)
 {
     v = fmaxf(v, dpp_mov<0xB1>(v));
