@@ -396,7 +396,29 @@ def main():
                     "gemm_flops": bflops, "router_flops": acc.backward_router_flops(counts),
                     "gemm_tflops_over_step": round(btf, 2),
                     "mfma_frac_over_step": round(btf / acc.PEAK_BF16_TFLOPS, 4)}
-        del grads, dy
+        # the same with the first Linear's pre-activations kept from the
+        # forward (moe_forward_save + moe_backward_saved): no GEMM recompute
+        y_s = torch.empty_like(y)
+        for _ in range(args.warmup):
+            layer.forward_save(x, y_s)
+            layer.backward(x, dy, 1.0, grads=grads, saved=True)
+        torch.cuda.synchronize()
+        tf = time.perf_counter()
+        for _ in range(args.steps):
+            layer.forward_save(x, y_s)
+        torch.cuda.synchronize()
+        tb2 = time.perf_counter()
+        for _ in range(args.steps):
+            layer.backward(x, dy, 1.0, grads=grads, saved=True)
+        torch.cuda.synchronize()
+        te = time.perf_counter()
+        backward["saved"] = {"entry_points": "moe_forward_save + moe_backward_saved",
+                             "forward_save_ms": round((tb2 - tf) * 1e3 / args.steps, 4),
+                             "backward_saved_ms": round((te - tb2) * 1e3 / args.steps, 4),
+                             "same_bits_y": bool(torch.equal(y_s.view(torch.int16), y.view(torch.int16)))
+                             if y.dtype == torch.bfloat16 else bool(torch.equal(y_s, y))}
+        layer.u_saved = layer.u_shared_saved = None
+        del grads, dy, y_s
 
     result = {
         "metric": "MoE layer tokens/sec (1 GPU)",

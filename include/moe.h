@@ -342,6 +342,36 @@ size_t moe_backward_workspace_size(const moe_problem_t *p);
 moe_status_t moe_backward(const moe_problem_t *p, const moe_weights_t *w, const void *x, const void *dy,
                           float g_aux, const moe_grads_t *grads, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------------------ *
+ * moe_forward_save / moe_backward_saved - the same forward and backward with
+ * the first Linear's pre-activations kept in between, so that the backward
+ * does not recompute that GEMM ("MoE Layer Structure": each expert is
+ * Linear -> GELU -> Linear; the backward of GELU needs its input).
+ *
+ * moe_forward_save writes, besides everything moe_forward writes,
+ *   u_saved        [moe_max_rows(...), ffn] fp32: u = W1 x + b1 of every
+ *                  dispatched row, in the dispatch's row order (rows past
+ *                  the kept ones are left untouched);
+ *   u_shared_saved [T, ffn] fp32: the shared expert's u (NULL without one),
+ * and then applies GELU to them in a separate pass; y and the outputs are
+ * bitwise those of moe_forward.  ws: moe_forward_workspace_size(p) bytes.
+ * moe_backward_saved takes the same arguments as moe_backward plus those two
+ * buffers, which must come from moe_forward_save on the same p, w and x
+ * (the routing is recomputed and is the forward's: same inputs, same
+ * selections); its gradients are bitwise those of moe_backward.
+ * ws: moe_backward_workspace_size(p) bytes.
+ * Both buffers are caller-owned, 16-byte aligned, required when T > 0
+ * (u_shared_saved only with a shared expert).
+ * Errors: as moe_forward / moe_backward, plus MOE_ERR_INVALID_ARG for a
+ * missing or misaligned u buffer.
+ * ------------------------------------------------------------------------ */
+moe_status_t moe_forward_save(const moe_problem_t *p, const moe_weights_t *w, const void *x, void *y,
+                              const moe_outputs_t *out, float *u_saved, float *u_shared_saved, void *ws,
+                              size_t ws_bytes, hipStream_t stream);
+moe_status_t moe_backward_saved(const moe_problem_t *p, const moe_weights_t *w, const void *x, const void *dy,
+                                float g_aux, const float *u_saved, const float *u_shared_saved,
+                                const moe_grads_t *grads, void *ws, size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

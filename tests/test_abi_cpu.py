@@ -169,6 +169,15 @@ def test_backward_workspace_and_rejections(lib):
     p = api.Problem(64, 136, 8, 2, 128, 0.0, 0, 0, 0, 0.01, api.MOE_BF16)     # d % 64 != 0 in bf16
     assert call(p, full) == api.MOE_ERR_UNSUPPORTED
     assert b"multiples of 64" in lib.moe_last_error()
+    # the saved-activation entry points need their u buffers
+    g = api.Grads(**{n: full.get(n) for n, _ in api.Grads._fields_})
+    assert lib.moe_backward_saved(ctypes.byref(p), ctypes.byref(w), FAKE, FAKE, 0.0, None, None, ctypes.byref(g),
+                                  FAKE, 1 << 40, None) == api.MOE_ERR_INVALID_ARG
+    assert b"u_saved" in lib.moe_last_error()
+    assert lib.moe_backward_saved(ctypes.byref(p), ctypes.byref(w), FAKE, FAKE, 0.0, FAKE + 8, None,
+                                  ctypes.byref(g), FAKE, 1 << 40, None) == api.MOE_ERR_INVALID_ARG
+    assert lib.moe_forward_save(ctypes.byref(p), ctypes.byref(w), FAKE, FAKE, None, None, None, FAKE, 1 << 40,
+                                None) == api.MOE_ERR_INVALID_ARG
     # 2^20 tokens x k = 2 rows: the weight-gradient GEMMs would need > 2^21 columns
     p = api.Problem(1 << 20, 128, 8, 2, 128, 0.0, 0, 0, 0, 0.01, api.MOE_BF16)
     assert call(p, full) == api.MOE_ERR_UNSUPPORTED

@@ -178,6 +178,72 @@ def test_backward_rejects_unsupported_bf16_shape():
     assert e.value.status == api.MOE_ERR_UNSUPPORTED
 
 
+def _f64(w, a):
+    if a is None:
+        return None
+    return (wl.bf16_bits_to_f32(a) if w.dtype == wl.BF16 else a).astype(np.float64)
+
+
+def _bits(a):
+    return a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32)
+
+
+@pytest.mark.parametrize("name", ["mixtral-small", "drop-small", "dsv3-bwd", "f32-shared", "tiny-fp32"])
+def test_forward_save_and_backward_saved(name):
+    """moe_forward_save writes moe_forward's bits and keeps u = W1 x + b1 of
+    the kept rows (checked in fp64 on a row sample: row r of segment e holds
+    token row_src[r] // k); moe_backward_saved on it gives moe_backward's
+    bits, twice in a row."""
+    w = BWD_SMALL[name]
+    inp = wl.make_layer(w, seed=4)
+    t = wl.device_layer(inp, DEV)
+    dy = wl.to_torch(wl.make_grad_output(w, seed=4), DEV)
+    layer = _layer(w, t)
+    outs = layer.alloc_outputs()
+    y_ref = layer.forward(t["x"]).clone()
+    o_ref = {k: v.clone() for k, v in outs.items()}
+    g_ref = {k: v.clone() for k, v in layer.backward(t["x"], dy, 0.7, dlogits=True).items()}
+    y = layer.forward_save(t["x"])
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(y), _bits(y_ref))
+    for k in ("topk_idx", "topk_w", "seg_offsets", "kept_count", "slot_row"):
+        assert torch.equal(outs[k], o_ref[k]), k
+
+    seg = outs["seg_offsets"].cpu().numpy()
+    row_src = outs["row_src"].cpu().numpy()
+    u = layer.u_saved.cpu().numpy()
+    x64, w1, b1 = _f64(w, inp.x), _f64(w, inp.w1), _f64(w, inp.b1)
+    kept = int(seg[-1])
+    assert kept > 0
+    rows = np.random.default_rng(1).choice(kept, size=min(48, kept), replace=False)
+    ref = np.empty((len(rows), w.ffn))
+    for i, r in enumerate(rows):
+        e = int(np.searchsorted(seg, r, side="right")) - 1
+        ref[i] = w1[e] @ x64[row_src[r] // w.k] + (b1[e] if b1 is not None else 0.0)
+    assert rel_err(u[rows].astype(np.float64), ref) <= 1e-5
+    if w.shared_expert:
+        us = layer.u_shared_saved.cpu().numpy().astype(np.float64)
+        tok = np.random.default_rng(2).choice(w.T, size=min(32, w.T), replace=False)
+        ref_s = x64[tok] @ _f64(w, inp.ws1).T + (_f64(w, inp.bs1) if inp.bs1 is not None else 0.0)
+        assert rel_err(us[tok], ref_s) <= 1e-5
+
+    for _ in range(2):
+        g = layer.backward(t["x"], dy, 0.7, dlogits=True, saved=True)
+        torch.cuda.synchronize()
+        for k in g_ref:
+            assert torch.equal(g[k].view(torch.int32), g_ref[k].view(torch.int32)), k
+
+
+def test_backward_saved_needs_forward_save():
+    w = BWD_SMALL["mixtral-small"]
+    inp = wl.make_layer(w, seed=1)
+    t = wl.device_layer(inp, DEV)
+    layer = _layer(w, t)
+    dy = torch.zeros((w.T, w.d), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(RuntimeError):
+        layer.backward(t["x"], dy, 0.0, saved=True)
+
+
 # ------------------------------------------------------------- full size --
 # The pages' workload shapes at full size, in the launch configuration of the
 # benchmark.  The oracle cannot produce every gradient at these sizes in

@@ -57,7 +57,7 @@ EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_error", "moe_max_ro
            "moe_route", "moe_dispatch_workspace_size", "moe_dispatch", "moe_grouped_gemm_workspace_size",
            "moe_grouped_gemm", "moe_expert_ffn", "moe_combine", "moe_forward_workspace_size", "moe_forward",
            "moe_forward_overlap_workspace_size", "moe_forward_overlap", "moe_backward_workspace_size",
-           "moe_backward"]
+           "moe_backward", "moe_forward_save", "moe_backward_saved"]
 
 _lib = None
 
@@ -104,6 +104,12 @@ def lib():
     L.moe_backward.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Weights), P, P, F, ctypes.POINTER(Grads), P,
                                SZ, P]
     L.moe_backward.restype = I
+    L.moe_forward_save.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Weights), P, P, ctypes.POINTER(Outputs),
+                                   P, P, P, SZ, P]
+    L.moe_forward_save.restype = I
+    L.moe_backward_saved.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Weights), P, P, F, P, P,
+                                     ctypes.POINTER(Grads), P, SZ, P]
+    L.moe_backward_saved.restype = I
     _lib = L
     return L
 
@@ -305,15 +311,35 @@ class Layer:
                                     _stream(x.device)))
         return y
 
+    def forward_save(self, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """moe_forward_save on the current stream: moe_forward that also keeps
+        the first Linear's fp32 pre-activations (self.u_saved, and
+        self.u_shared_saved with a shared expert) for backward(saved=True)."""
+        p, dev = self.problem, self.device
+        if self.ws is None or getattr(self, "_ws_overlap", None):
+            self.ws = _ws(self.workspace_bytes(False), dev)
+            self._ws_overlap = False
+        if getattr(self, "u_saved", None) is None:
+            self.u_saved = torch.empty((max(1, self.max_rows), p.ffn), dtype=torch.float32, device=dev)
+            self.u_shared_saved = (torch.empty((max(1, p.T), p.ffn), dtype=torch.float32, device=dev)
+                                   if p.has_shared else None)
+        if y is None:
+            y = torch.empty((p.T, p.d), dtype=x.dtype, device=x.device)
+        check(lib().moe_forward_save(ctypes.byref(p), ctypes.byref(self.weights), _p(x), _p(y),
+                                     ctypes.byref(self.out_struct), _p(self.u_saved), _p(self.u_shared_saved),
+                                     _p(self.ws), self.ws.numel(), _stream(x.device)))
+        return y
+
     def backward_workspace_bytes(self) -> int:
         return int(lib().moe_backward_workspace_size(ctypes.byref(self.problem)))
 
     def backward(self, x: torch.Tensor, dy: torch.Tensor, g_aux: float = 0.0, bias_grads: bool = True,
-                 dlogits: bool = False, grads: Optional[dict] = None) -> dict:
+                 dlogits: bool = False, grads: Optional[dict] = None, saved: bool = False) -> dict:
         """moe_backward on the current stream: float32 gradients of a loss with
         dL/dY = dy and dL/dL_aux = g_aux.  Returns (or fills) a dict with dx,
         dw_router, dw1, dw2 (dws1, dws2 with a shared expert), the bias
-        gradients when bias_grads, and dlogits when asked for."""
+        gradients when bias_grads, and dlogits when asked for.  With saved,
+        moe_backward_saved on the pre-activations of the last forward_save."""
         p, dev = self.problem, self.device
         if grads is None:
             f32 = dict(dtype=torch.float32, device=dev)
@@ -333,6 +359,14 @@ class Layer:
         nb = self.backward_workspace_bytes()
         if getattr(self, "_bws", None) is None or self._bws.numel() < nb:
             self._bws = _ws(nb, dev)
-        check(lib().moe_backward(ctypes.byref(self.problem), ctypes.byref(self.weights), _p(x), _p(dy),
-                                 float(g_aux), ctypes.byref(gs), _p(self._bws), self._bws.numel(), _stream(x.device)))
+        if saved:
+            if getattr(self, "u_saved", None) is None:
+                raise RuntimeError("backward(saved=True) needs a forward_save first")
+            check(lib().moe_backward_saved(ctypes.byref(self.problem), ctypes.byref(self.weights), _p(x), _p(dy),
+                                           float(g_aux), _p(self.u_saved), _p(self.u_shared_saved), ctypes.byref(gs),
+                                           _p(self._bws), self._bws.numel(), _stream(x.device)))
+        else:
+            check(lib().moe_backward(ctypes.byref(self.problem), ctypes.byref(self.weights), _p(x), _p(dy),
+                                     float(g_aux), ctypes.byref(gs), _p(self._bws), self._bws.numel(),
+                                     _stream(x.device)))
         return grads

@@ -325,8 +325,12 @@ size_t moe_forward_workspace_size(const moe_problem_t *p)
 
 namespace {
 
+// u_save / u_sh_save (moe_forward_save): the first Linear's fp32
+// pre-activations of the routed rows and of the shared expert are written
+// there, and GELU runs as its own pass from them.
 moe_status_t forward_impl(const moe_problem_t *p, const moe_weights_t *w, const void *x, void *y,
-                          const moe_outputs_t *out, void *ws, size_t ws_bytes, hipStream_t stream, hipStream_t side)
+                          const moe_outputs_t *out, void *ws, size_t ws_bytes, hipStream_t stream, hipStream_t side,
+                          float *u_save = nullptr, float *u_sh_save = nullptr)
 {
     clear_error();
     if (!p || !w)
@@ -404,14 +408,28 @@ moe_status_t forward_impl(const moe_problem_t *p, const moe_weights_t *w, const 
                             E_loc, b.seg_offsets, b.kept_count, b.slot_row, b.row_src, b.x_perm, max_rows,
                             b.n_dropped, b.dispatch_ws, stream);
     if (!s && p->T > 0) {
-        s = launch_grouped_gemm(b.x_perm, b.seg_offsets, E_loc, max_rows, p->ffn, p->d, p->dtype, w->w1, w->b1, 1,
-                                b.h, b.gemm_ws, b.gemm_ws_bytes, stream);
+        if (u_save) {
+            s = launch_grouped_gemm_f32out(b.x_perm, b.seg_offsets, E_loc, max_rows, p->ffn, p->d, p->dtype, w->w1,
+                                           w->b1, u_save, b.gemm_ws, b.gemm_ws_bytes, stream);
+            if (!s)
+                s = launch_gelu_rows(u_save, b.seg_offsets, E_loc, max_rows, p->ffn, p->dtype, b.h, stream);
+        } else {
+            s = launch_grouped_gemm(b.x_perm, b.seg_offsets, E_loc, max_rows, p->ffn, p->d, p->dtype, w->w1, w->b1,
+                                    1, b.h, b.gemm_ws, b.gemm_ws_bytes, stream);
+        }
         if (!s)
             s = launch_grouped_gemm(b.h, b.seg_offsets, E_loc, max_rows, p->d, p->ffn, p->dtype, w->w2, w->b2, 0,
                                     b.y_perm, b.gemm_ws, b.gemm_ws_bytes, stream);
         if (!s && p->has_shared && !overlap) {
-            s = launch_grouped_gemm(x, nullptr, 1, p->T, p->ffn, p->d, p->dtype, w->ws1, w->bs1, 1, b.h, b.gemm_ws,
-                                    b.gemm_ws_bytes, stream);
+            if (u_sh_save) {
+                s = launch_grouped_gemm_f32out(x, nullptr, 1, p->T, p->ffn, p->d, p->dtype, w->ws1, w->bs1, u_sh_save,
+                                               b.gemm_ws, b.gemm_ws_bytes, stream);
+                if (!s)
+                    s = launch_gelu_rows(u_sh_save, nullptr, 1, p->T, p->ffn, p->dtype, b.h, stream);
+            } else {
+                s = launch_grouped_gemm(x, nullptr, 1, p->T, p->ffn, p->d, p->dtype, w->ws1, w->bs1, 1, b.h,
+                                        b.gemm_ws, b.gemm_ws_bytes, stream);
+            }
             if (!s)
                 s = launch_grouped_gemm(b.h, nullptr, 1, p->T, p->d, p->ffn, p->dtype, w->ws2, w->bs2, 0, b.y_sh,
                                         b.gemm_ws, b.gemm_ws_bytes, stream);
@@ -432,6 +450,20 @@ extern "C" moe_status_t moe_forward(const moe_problem_t *p, const moe_weights_t 
                                     const moe_outputs_t *out, void *ws, size_t ws_bytes, hipStream_t stream)
 {
     return forward_impl(p, w, x, y, out, ws, ws_bytes, stream, nullptr);
+}
+
+extern "C" moe_status_t moe_forward_save(const moe_problem_t *p, const moe_weights_t *w, const void *x, void *y,
+                                         const moe_outputs_t *out, float *u_saved, float *u_shared_saved, void *ws,
+                                         size_t ws_bytes, hipStream_t stream)
+{
+    clear_error();
+    if (!p)
+        return fail(MOE_ERR_INVALID_ARG, "forward_save: problem is required");
+    if (p->T > 0 && (!u_saved || (p->has_shared && !u_shared_saved)))
+        return fail(MOE_ERR_INVALID_ARG, "forward_save: u_saved (and u_shared_saved with a shared expert) required");
+    if (!aligned16(u_saved) || !aligned16(u_shared_saved))
+        return fail(MOE_ERR_INVALID_ARG, "forward_save: u_saved and u_shared_saved must be 16-byte aligned");
+    return forward_impl(p, w, x, y, out, ws, ws_bytes, stream, nullptr, u_saved, p->has_shared ? u_shared_saved : nullptr);
 }
 
 extern "C" size_t moe_forward_overlap_workspace_size(const moe_problem_t *p)
@@ -536,6 +568,7 @@ struct FfnBwd {
     const float *wgt;              // routing weights by slot, or NULL (= 1)
     const void *w1, *b1, *w2;
     float *dw1, *db1, *dw2, *db2, *dx_rows, *dwpart;
+    const float *u_saved;          // the forward's pre-activations, or NULL (recomputed)
 };
 
 moe_status_t ffn_backward(const moe_problem_t *p, const void *x, const void *dy, const FfnBwd &a,
@@ -548,7 +581,8 @@ moe_status_t ffn_backward(const moe_problem_t *p, const void *x, const void *dy,
         s = launch_transpose_batched(a.w1, a.S, F, d, a.seg, dt, b.w1t, st);
     if (!s)
         s = launch_transpose_batched(a.w2, a.S, d, F, a.seg, dt, b.w2t, st);
-    if (!s) // u = W1 x + b1 (fp32)
+    const float *u = a.u_saved ? a.u_saved : b.u;
+    if (!s && !a.u_saved) // u = W1 x + b1 (fp32)
         s = launch_grouped_gemm_f32out(a.a_rows, a.seg, a.S, a.rows, F, d, dt, a.w1, a.b1, b.u, b.gemm_ws,
                                        b.gemm_ws_bytes, st);
     if (!s) // dY rows (row-major for dh', transposed for dW2) and db2
@@ -561,7 +595,7 @@ moe_status_t ffn_backward(const moe_problem_t *p, const void *x, const void *dy,
         s = launch_grouped_gemm_f32out(dyr, a.seg, a.S, a.rows, F, d, dt, b.w2t, nullptr, b.dh, b.gemm_ws,
                                        b.gemm_ws_bytes, st);
     if (!s)
-        s = launch_act_bwd(b.u, b.dh, F, a.row_src, a.wgt, a.seg, a.S, a.rows, b.kcol, b.Kp, dt, b.du, b.duT, b.gwT,
+        s = launch_act_bwd(u, b.dh, F, a.row_src, a.wgt, a.seg, a.S, a.rows, b.kcol, b.Kp, dt, b.du, b.duT, b.gwT,
                            a.dwpart, a.db1 ? b.colpart : nullptr, st);
     if (!s)
         s = launch_seg_colsum(b.colpart, b.kcol, a.S, F, a.db1, st);
@@ -587,9 +621,13 @@ extern "C" size_t moe_backward_workspace_size(const moe_problem_t *p)
     return carve_backward(p, nullptr, nullptr).bytes;
 }
 
-extern "C" moe_status_t moe_backward(const moe_problem_t *p, const moe_weights_t *w, const void *x, const void *dy,
-                                     float g_aux, const moe_grads_t *g, void *ws, size_t ws_bytes,
-                                     hipStream_t stream)
+namespace {
+
+// moe_backward; with u_saved (and u_sh_saved) the first Linear's
+// pre-activations come from moe_forward_save instead of being recomputed.
+moe_status_t backward_impl(const moe_problem_t *p, const moe_weights_t *w, const void *x, const void *dy,
+                           float g_aux, const moe_grads_t *g, void *ws, size_t ws_bytes, hipStream_t stream,
+                           const float *u_saved, const float *u_sh_saved)
 {
     clear_error();
     if (!p || !w || !g)
@@ -675,6 +713,7 @@ extern "C" moe_status_t moe_backward(const moe_problem_t *p, const moe_weights_t
         a.dw2 = g->dws2;
         a.db2 = g->dbs2;
         a.dx_rows = g->dx; // the routed rows and the router term are added in place
+        a.u_saved = u_sh_saved;
         s = ffn_backward(p, x, dy, a, b, stream);
     }
     if (!s) {
@@ -694,6 +733,7 @@ extern "C" moe_status_t moe_backward(const moe_problem_t *p, const moe_weights_t
         a.db2 = g->db2;
         a.dx_rows = b.dx_rows;
         a.dwpart = b.dwpart;
+        a.u_saved = u_saved;
         s = ffn_backward(p, x, dy, a, b, stream);
     }
     const float c_aux = (float)((double)g_aux * (double)p->alpha / (double)T);
@@ -714,4 +754,29 @@ extern "C" moe_status_t moe_backward(const moe_problem_t *p, const moe_weights_t
         s = launch_dx_combine(b.dx_rows, b.slot_row, p->k, p->has_shared ? g->dx : nullptr, dx_r, b.dl,
                               w->w_router, T, d, E, g->dx, stream);
     return s;
+}
+
+} // namespace
+
+extern "C" moe_status_t moe_backward(const moe_problem_t *p, const moe_weights_t *w, const void *x, const void *dy,
+                                     float g_aux, const moe_grads_t *g, void *ws, size_t ws_bytes,
+                                     hipStream_t stream)
+{
+    return backward_impl(p, w, x, dy, g_aux, g, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+extern "C" moe_status_t moe_backward_saved(const moe_problem_t *p, const moe_weights_t *w, const void *x,
+                                           const void *dy, float g_aux, const float *u_saved,
+                                           const float *u_shared_saved, const moe_grads_t *g, void *ws,
+                                           size_t ws_bytes, hipStream_t stream)
+{
+    clear_error();
+    if (!p)
+        return fail(MOE_ERR_INVALID_ARG, "backward_saved: problem is required");
+    if (p->T > 0 && (!u_saved || (p->has_shared && !u_shared_saved)))
+        return fail(MOE_ERR_INVALID_ARG, "backward_saved: u_saved (and u_shared_saved with a shared expert) required");
+    if (!aligned16(u_saved) || !aligned16(u_shared_saved))
+        return fail(MOE_ERR_INVALID_ARG, "backward_saved: u_saved and u_shared_saved must be 16-byte aligned");
+    return backward_impl(p, w, x, dy, g_aux, g, ws, ws_bytes, stream, p->T > 0 ? u_saved : nullptr,
+                         p->T > 0 && p->has_shared ? u_shared_saved : nullptr);
 }

@@ -134,7 +134,45 @@ __global__ __launch_bounds__(256) void combine_f32(const f32x4 *__restrict__ y_p
     }
 }
 
+// h = GELU(u) in the layer's dtype for the rows in use (the first seg[S]
+// rows; all `rows` when seg is NULL), from the fp32 pre-activations u
+// [rows, F] (F % 4 == 0).  The same GELU and the same rounding as the first
+// GEMM's fused epilogue, so h is bitwise what that epilogue writes.
+template <class T>
+__global__ __launch_bounds__(256) void gelu_rows(const float *__restrict__ u, const int32_t *__restrict__ seg, int S,
+                                                 int64_t rows, int F, T *__restrict__ h)
+{
+    const int64_t used = seg ? (int64_t)seg[S] : rows;
+    const int64_t n4 = (used < rows ? used : rows) * (F / 4);
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+        const f32x4 v = reinterpret_cast<const f32x4 *>(u)[i];
+        const float g0 = gelu_erf(v[0]), g1 = gelu_erf(v[1]), g2 = gelu_erf(v[2]), g3 = gelu_erf(v[3]);
+        if constexpr (sizeof(T) == 2) {
+            uint2 o;
+            o.x = pack_bf16x2(g0, g1);
+            o.y = pack_bf16x2(g2, g3);
+            reinterpret_cast<uint2 *>(h)[i] = o;
+        } else {
+            reinterpret_cast<f32x4 *>(h)[i] = f32x4{g0, g1, g2, g3};
+        }
+    }
+}
+
 } // namespace
+
+moe_status_t launch_gelu_rows(const float *u, const int32_t *seg, int S, int64_t rows, int F, moe_dtype_t dt,
+                              void *h, hipStream_t stream)
+{
+    const int64_t n4 = rows * (F / 4);
+    if (n4 == 0)
+        return MOE_OK;
+    const unsigned blocks = (unsigned)((n4 + 255) / 256 < 8192 ? (n4 + 255) / 256 : 8192);
+    if (dt == MOE_BF16)
+        gelu_rows<uint16_t><<<blocks, 256, 0, stream>>>(u, seg, S, rows, F, (uint16_t *)h);
+    else
+        gelu_rows<float><<<blocks, 256, 0, stream>>>(u, seg, S, rows, F, (float *)h);
+    return check_launch("gelu_rows");
+}
 
 moe_status_t launch_combine(const void *y_perm, int64_t max_rows, const int32_t *slot_row, const float *topk_w,
                             const void *y_shared, int64_t T, int d, int k, moe_dtype_t dt, void *y,

@@ -186,6 +186,11 @@ moe_status_t launch_kseg_layout(const int32_t *seg, int S, int64_t max_rows, int
 moe_status_t launch_kseg_gemm(const void *A, const void *W, const int32_t *kcol, int S, int M, int N, int64_t Kp,
                               moe_dtype_t dt, float *C, hipStream_t stream);
 
+// h = GELU(u) (dtype dt) over the rows in use of u [rows, F] fp32 (seg[S]
+// of them, or all rows when seg is NULL); F % 4 == 0.
+moe_status_t launch_gelu_rows(const float *u, const int32_t *seg, int S, int64_t rows, int F, moe_dtype_t dt,
+                              void *h, hipStream_t stream);
+
 moe_status_t launch_combine(const void *y_perm, int64_t max_rows, const int32_t *slot_row,
                             const float *topk_w, const void *y_shared, int64_t T, int d, int k,
                             moe_dtype_t dt, void *y, hipStream_t stream);
