@@ -181,7 +181,7 @@ moe_status_t moe_dispatch(const void *x, moe_dtype_t dtype, const int32_t *topk_
  * reproducible); without it every tile runs whole.
  * Errors: INVALID_ARG for sizes < 1 (max_rows = 0 is a no-op), NULL a, w or
  * out, misaligned buffers; UNSUPPORTED for N or K not a multiple of 8,
- * K above 2^21, activation not 0 or 1, more than 1024 segments.
+ * N or K above 2^21, activation not 0 or 1, more than 1024 segments.
  * ------------------------------------------------------------------------ */
 size_t moe_grouped_gemm_workspace_size(void);
 moe_status_t moe_grouped_gemm(const void *a, const int32_t *seg_offsets, int num_segments,

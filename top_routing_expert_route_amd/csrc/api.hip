@@ -38,8 +38,9 @@ namespace {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Largest reduction length of a GEMM: the kernels address a 256-row operand
-// tile through one buffer record of at most 2^31 bytes (256 x K x 4).
+// Largest reduction length and output width of a GEMM: the kernels address
+// a 256-row operand or output tile through one buffer record of at most 2^31
+// bytes (256 x K x 4, 256 x N x 4).
 constexpr int kMaxK = 1 << 21;
 
 int local_count(int E, int num_local_experts) { return num_local_experts > 0 ? num_local_experts : E; }
@@ -118,9 +119,9 @@ moe_status_t check_gemm_args(const void *a, const int32_t *seg, int S, int64_t m
         return fail(MOE_ERR_INVALID_ARG, "%s: buffers must be 16-byte aligned", who);
     if (N % 8 != 0 || K % 8 != 0 || act < 0 || act > 1 || (seg && S > 1024))
         return fail(MOE_ERR_UNSUPPORTED, "%s: needs N, K multiples of 8, activation 0/1, <= 1024 segments", who);
-    if (K > kMaxK)
-        return fail(MOE_ERR_UNSUPPORTED, "%s: K = %d above %d (a 256-row operand tile must fit a 32-bit buffer "
-                    "record)", who, K, kMaxK);
+    if (K > kMaxK || N > kMaxK)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: N = %d, K = %d, at most %d (a 256-row tile must fit a 32-bit buffer "
+                    "record)", who, N, K, kMaxK);
     if (max_rows > (int64_t)INT32_MAX)
         return fail(MOE_ERR_UNSUPPORTED, "%s: rows must fit int32", who);
     return MOE_OK;

@@ -329,11 +329,34 @@ constexpr int kLargeBK = 64;
 
 // Epilogue of a 256x256 tile: bias, activation and store of the rows inside
 // [row0, row_end) and features < N, as bf16 (rounded to nearest even) or,
-// with F32OUT, as fp32.  Accumulators are read unconditionally and only the
-// stores are predicated, so no accumulator has to live outside its register.
+// with F32OUT, as fp32.  Accumulators are read unconditionally and the
+// stores go through a buffer record of the tile's rows: a masked lane gets
+// an offset past the record and its store is dropped by the range check.
+// With no branches, and the stores of every row sub-tile issued (empty ones
+// are all dropped), each variant issues the same stores, so the compiler
+// counts them exactly and does not drain them before the next tile's work.
+// (Offsets are 32-bit: 256 x N x 4 bytes must fit, N <= 2^21.)
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Output rows of one tile as a buffer record: rows [row0, row_end) of C.
+struct TileOut {
+    __amdgpu_buffer_rsrc_t r;
+    int64_t row0;
+};
+
+template <bool F32OUT> __device__ __forceinline__ TileOut tile_out(void *C, int64_t row0, int64_t row_end, int N)
+{
+    constexpr uint32_t es = F32OUT ? 4u : 2u;
+    TileOut rt;
+    rt.row0 = row0;
+    rt.r = __builtin_amdgcn_make_buffer_rsrc((char *)C + (size_t)row0 * N * es, (short)0,
+                                             (int)((uint32_t)(row_end - row0) * (uint32_t)N * es), kRsrcWord3);
+    return rt;
+}
+
 template <bool GELU, bool BIAS, bool F32OUT>
-__device__ __forceinline__ void store4(void *C, const uint16_t *__restrict__ bseg, int64_t row, bool row_ok, int n,
-                                       int N, float v0, float v1, float v2, float v3)
+__device__ __forceinline__ void store4(const TileOut &rt, const uint16_t *__restrict__ bseg, int64_t row, bool row_ok,
+                                       int n, int N, float v0, float v1, float v2, float v3)
 {
     if (BIAS) {
         const uint2 bb = *reinterpret_cast<const uint2 *>(bseg + (n < N ? n : 0));
@@ -349,17 +372,15 @@ __device__ __forceinline__ void store4(void *C, const uint16_t *__restrict__ bse
         v3 = gelu_erf(v3);
     }
     const bool ok = row_ok && n < N;
-    const int64_t at = (ok ? row : 0) * N + (ok ? n : 0);
+    const uint32_t off = ok ? (uint32_t)((row - rt.row0) * N + n) * (F32OUT ? 4u : 2u) : 0x80000000u;
     if (F32OUT) {
         const f32x4 o = {v0, v1, v2, v3};
-        if (ok)
-            *reinterpret_cast<f32x4 *>((float *)C + at) = o;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rt.r, off, 0, 0);
     } else {
         uint2 o;
         o.x = pack_bf16x2(v0, v1);
         o.y = pack_bf16x2(v2, v3);
-        if (ok)
-            *reinterpret_cast<uint2 *>((uint16_t *)C + at) = o;
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, o), rt.r, off, 0, 0);
     }
 }
 
@@ -368,8 +389,9 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[G::FA][G::FB], vo
                                            const uint16_t *__restrict__ bseg, int64_t row0, int64_t row_end, int n0,
                                            int N, int wn, int wm, int r32, int khalf)
 {
+    const TileOut rt = tile_out<F32OUT>(C, row0, row_end, N);
 #pragma unroll
-    for (int b = 0; b < NBV; ++b) {
+    for (int b = 0; b < G::FB; ++b) {
         const int64_t row = row0 + wm * G::WTM + b * 32 + r32;
         const bool row_ok = row < row_end;
 #pragma unroll
@@ -377,7 +399,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[G::FA][G::FB], vo
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int n = n0 + wn * G::WTN + a * 32 + 8 * g + 4 * khalf;
-                store4<GELU, BIAS, F32OUT>(C, bseg, row, row_ok, n, N, acc[a][b][4 * g + 0], acc[a][b][4 * g + 1],
+                store4<GELU, BIAS, F32OUT>(rt, bseg, row, row_ok, n, N, acc[a][b][4 * g + 0], acc[a][b][4 * g + 1],
                                            acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]);
             }
         }
@@ -709,7 +731,8 @@ __device__ __forceinline__ int tile(uint16_t *smem, int b, const CopyGeo &cg, co
                                     float *part, int64_t row0, int64_t row_end, int n0, int N)
 {
     constexpr int FA = G::FA, FB = G::FB, STAGE = 2 * kL * BK;
-    const int tid = threadIdx.x;
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid)); // lane values are rederived per tile, not kept (spilled) across tiles
     const int lane = tid & 63, wave = tid >> 6;
     const int wn = wave % G::WGN_, wm = wave / G::WGN_;
     const int r32 = lane & 31, khalf = lane >> 5;
@@ -976,7 +999,8 @@ struct KsegCtx {
 __device__ __forceinline__ Work get_work(const KsegCtx &x, int i)
 {
     const int64_t L = x.first + (int64_t)i * x.per;
-    const int per_seg = x.MT * x.NT;
+    int per_seg = x.MT * x.NT;
+    asm volatile("" : "+s"(per_seg)); // keeps the divisions' reciprocals out of the loop (no spill)
     const int q = (int)(L / per_seg); // index among the non-empty segments
     // The last segment with ne[s] <= q is the q-th non-empty one: an empty
     // segment is followed by one with the same ne, and the segments after
@@ -994,7 +1018,8 @@ __device__ __forceinline__ Work get_work(const KsegCtx &x, int i)
     // larger operand's tiles are walked, the panel's tiles fastest, so the
     // panel (about 2 MB) stays in the XCD's L2 while the 32 CUs sweep the
     // larger operand, which is read once per panel.
-    const int SI = x.n_inner ? x.NT : x.MT, LO = x.n_inner ? x.MT : x.NT;
+    int SI = x.n_inner ? x.NT : x.MT, LO = x.n_inner ? x.MT : x.NT;
+    asm volatile("" : "+s"(SI), "+s"(LO));
     const int panel = local / (kKsegPanel * LO);
     const int rem = local - panel * (kKsegPanel * LO);
     const int pw = SI - panel * kKsegPanel < kKsegPanel ? SI - panel * kKsegPanel : kKsegPanel;
@@ -1192,6 +1217,7 @@ __global__ __launch_bounds__(64 * G::FA) void grouped_gemm_reduce(const int32_t 
     const int r32 = lane & 31, khalf = lane >> 5;
     const TileLoc t = locate(tb, seg, S, max_rows, NT, plan.F + tile);
     const uint16_t *bseg = bias ? bias + (int64_t)t.s * N : nullptr;
+    const TileOut rt = tile_out<F32OUT>(C, t.row0, t.row_end, N);
     for (int b = 0; b < G::FB; ++b) {
         const float *src = part_ws + (size_t)tile * plan.sk * (kL * kL) +
                            (size_t)wave * (G::FA * G::FB * 16 * 64) + (size_t)((a * G::FB + b) * 16) * 64 + lane;
@@ -1216,7 +1242,7 @@ __global__ __launch_bounds__(64 * G::FA) void grouped_gemm_reduce(const int32_t 
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int n = t.n0 + wn * G::WTN + a * 32 + 8 * g + 4 * khalf;
-            store4<GELU, BIAS, F32OUT>(C, bseg, row, row_ok, n, N, v[4 * g], v[4 * g + 1], v[4 * g + 2],
+            store4<GELU, BIAS, F32OUT>(rt, bseg, row, row_ok, n, N, v[4 * g], v[4 * g + 1], v[4 * g + 2],
                                        v[4 * g + 3]);
         }
     }
