@@ -10,8 +10,9 @@ synthetic layers already resident in HBM.  Prints one JSON line.
 Beside the mean step time the line carries the median and minimum of the
 same steps timed one by one; the HBM-bound stages (route, dispatch, combine)
 timed warm and cold (a 1 GiB copy before each evicts L2 and the MALL); a
-plain 1 GiB device copy as the practical HBM ceiling; and the oracle on all
-cores (cpu_baseline) and on one thread.
+plain 1 GiB device copy as the practical HBM ceiling; the step replayed from
+a HIP graph captured once (graph_replay); and the oracle on all cores
+(cpu_baseline) and on one thread.
 
 The roofline entry covers the dominant kernel (the first grouped GEMM with
 the fused GELU): algorithmic flops of one launch (2 * rows * d * ffn, rows =
@@ -234,6 +235,31 @@ def main():
         e1.synchronize()
         step_ms.append(e0.elapsed_time(e1))
 
+    # ---- the same step replayed from a HIP graph (captured once) ----
+    graph = None
+    try:
+        side_g = torch.cuda.Stream(device=dev)
+        side_g.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side_g):
+            layer.forward(x, y)
+        torch.cuda.current_stream(dev).wait_stream(side_g)
+        torch.cuda.synchronize()
+        cg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cg):
+            layer.forward(x, y)
+        for _ in range(args.warmup):
+            cg.replay()
+        torch.cuda.synchronize()
+        tg = time.perf_counter()
+        for _ in range(args.steps):
+            cg.replay()
+        torch.cuda.synchronize()
+        elg = time.perf_counter() - tg
+        graph = {"ms_per_step": round(elg * 1e3 / args.steps, 4), "value": round(w.T * args.steps / elg, 1)}
+        del cg
+    except RuntimeError as e:  # reported, not fatal: the eager line above is the headline
+        graph = {"error": str(e)[:200]}
+
     # ---- with a shared expert: the same step with it on a second stream ----
     overlap = None
     if w.shared_expert:
@@ -449,6 +475,8 @@ def main():
         "staged_step_us": round(staged_total, 1),
         "hbm_copy": hbm_copy_ceiling(torch, dev),
     }
+    if graph is not None:
+        result["graph_replay"] = graph
     if overlap is not None:
         result["shared_overlap"] = overlap
     if backward is not None:

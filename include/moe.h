@@ -25,7 +25,10 @@
  *    asynchronous: a call returns before the GPU has finished and never
  *    synchronises.  Counts that the GPU computes (rows per expert, drops) never
  *    come back to the host inside a call: grids are sized from bounds and read
- *    the actual counts on the device.
+ *    the actual counts on the device.  A call enqueues kernel launches only
+ *    (no memset or copy nodes), so it may be captured into a HIP graph and
+ *    replayed, with the same buffers (moe_forward_overlap also records and
+ *    waits on events between its two streams).
  *  - Errors: arguments are validated before anything is enqueued; an invalid
  *    call returns a non-zero status, enqueues nothing and leaves every output
  *    untouched.  MOE_ERR_HIP reports a launch failure (moe_last_error() has the
