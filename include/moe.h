@@ -364,7 +364,8 @@ moe_status_t moe_backward(const moe_problem_t *p, const moe_weights_t *w, const 
  * selections); its gradients are bitwise those of moe_backward.
  * ws: moe_backward_workspace_size(p) bytes.
  * Both buffers are caller-owned, 16-byte aligned, required when T > 0
- * (u_shared_saved only with a shared expert).
+ * (u_shared_saved only with a shared expert).  MOE_BF16 needs d a multiple
+ * of 64 and at least 128 (else MOE_ERR_UNSUPPORTED), as moe_backward does.
  * Errors: as moe_forward / moe_backward, plus MOE_ERR_INVALID_ARG for a
  * missing or misaligned u buffer.
  * ------------------------------------------------------------------------ */

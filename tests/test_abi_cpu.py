@@ -178,6 +178,9 @@ def test_backward_workspace_and_rejections(lib):
                                   ctypes.byref(g), FAKE, 1 << 40, None) == api.MOE_ERR_INVALID_ARG
     assert lib.moe_forward_save(ctypes.byref(p), ctypes.byref(w), FAKE, FAKE, None, None, None, FAKE, 1 << 40,
                                 None) == api.MOE_ERR_INVALID_ARG
+    # bf16 with d % 64 != 0 (here d = 136): the fp32-output first Linear needs the 256x256 kernel
+    assert lib.moe_forward_save(ctypes.byref(p), ctypes.byref(w), FAKE, FAKE, None, FAKE, None, FAKE, 1 << 40,
+                                None) == api.MOE_ERR_UNSUPPORTED
     # 2^20 tokens x k = 2 rows: the weight-gradient GEMMs would need > 2^21 columns
     p = api.Problem(1 << 20, 128, 8, 2, 128, 0.0, 0, 0, 0, 0.01, api.MOE_BF16)
     assert call(p, full) == api.MOE_ERR_UNSUPPORTED

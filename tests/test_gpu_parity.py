@@ -32,6 +32,8 @@ SMALL = {
                              sel_bias="gauss", router_bias="gauss"),
     "selbias-e128": wl.scaled(wl.get(3), name="selbias-e128", T=300, d=128, ffn=96, sel_bias="gauss",
                               capacity_factor=1.5),
+    # E > 64 with d = 64: too short a reduction for the router's grouped-GEMM path
+    "e128-d64": wl.scaled(wl.get(3), name="e128-d64", T=300, d=64, ffn=96),
 }
 
 FULL = {w.name: w for w in wl.WORKLOADS[1:]}

@@ -464,6 +464,9 @@ extern "C" moe_status_t moe_forward_save(const moe_problem_t *p, const moe_weigh
         return fail(MOE_ERR_INVALID_ARG, "forward_save: u_saved (and u_shared_saved with a shared expert) required");
     if (!aligned16(u_saved) || !aligned16(u_shared_saved))
         return fail(MOE_ERR_INVALID_ARG, "forward_save: u_saved and u_shared_saved must be 16-byte aligned");
+    // the fp32-output first Linear runs on the 256x256 kernel only
+    if (p->dtype == MOE_BF16 && (p->d % 64 != 0 || p->d < 128))
+        return fail(MOE_ERR_UNSUPPORTED, "forward_save: bf16 needs d a multiple of 64, at least 128 (d=%d)", p->d);
     return forward_impl(p, w, x, y, out, ws, ws_bytes, stream, nullptr, u_saved, p->has_shared ? u_shared_saved : nullptr);
 }
 

@@ -589,7 +589,11 @@ static int route_blocks(int64_t T, int E, moe_dtype_t dt)
     return select_blocks(T);
 }
 
-static bool router_on_gemm(moe_dtype_t dt, int d, int E) { return dt == MOE_BF16 && E > 64 && d % 64 == 0; }
+// The grouped GEMM needs K % 64 == 0 and at least two K steps (d >= 128).
+static bool router_on_gemm(moe_dtype_t dt, int d, int E)
+{
+    return dt == MOE_BF16 && E > 64 && d % 64 == 0 && d >= 128;
+}
 
 size_t route_ws_bytes(int64_t T, int d, int E)
 {
