@@ -34,6 +34,8 @@ SMALL = {
                               capacity_factor=1.5),
     # E > 64 with d = 64: too short a reduction for the router's grouped-GEMM path
     "e128-d64": wl.scaled(wl.get(3), name="e128-d64", T=300, d=64, ffn=96),
+    # E > 64 not a multiple of 8 (3E logits per row not in whole 16-byte groups), k = 16
+    "e65-k16": wl.scaled(wl.get(3), name="e65-k16", T=325, d=192, E=65, k=16, ffn=128, router_bias="gauss"),
 }
 
 FULL = {w.name: w for w in wl.WORKLOADS[1:]}

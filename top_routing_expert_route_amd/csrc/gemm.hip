@@ -1352,6 +1352,10 @@ moe_status_t run_large(const void *a, const int32_t *seg, int S, int64_t max_row
                        const void *w, const void *bias, void *out, float *part_ws, hipStream_t stream)
 {
     typedef LargeGrid G;
+    // the epilogue writes 4 features per lane; rows of the output must not split such a group
+    if (N % 4 != 0 || K % kLargeBK != 0 || K / kLargeBK < 2 || Ka % kLargeBK != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "grouped_gemm_256: needs N %% 4 == 0, K %% 64 == 0, K >= 128 (N=%d K=%d)",
+                    N, K);
     const int grid = large_grid(max_rows, S, N, part_ws != nullptr);
     grouped_gemm_256<kLargeBK, G, GELU, BIAS, F32OUT><<<(unsigned)grid, 64 * G::NW, 0, stream>>>(
         (const uint16_t *)a, seg, S, max_rows, (const uint16_t *)w, (const uint16_t *)bias, out, N, K, Ka, part_ws);
@@ -1460,6 +1464,8 @@ moe_status_t launch_kseg_gemm(const void *A, const void *W, const int32_t *kcol,
         return check_launch("grouped_gemm_kseg_f32");
     }
     typedef LargeGrid G;
+    if (N % 4 != 0)
+        return fail(MOE_ERR_UNSUPPORTED, "grouped_gemm_kseg: needs N %% 4 == 0 (N=%d)", N);
     int64_t grid = (int64_t)device_cus();
     grid = (grid + kXcds - 1) / kXcds * kXcds;
     grouped_gemm_kseg<kLargeBK, G><<<(unsigned)grid, 64 * G::NW, 0, stream>>>(

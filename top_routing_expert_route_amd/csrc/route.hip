@@ -589,10 +589,12 @@ static int route_blocks(int64_t T, int E, moe_dtype_t dt)
     return select_blocks(T);
 }
 
-// The grouped GEMM needs K % 64 == 0 and at least two K steps (d >= 128).
+// The grouped GEMM needs K % 64 == 0 and at least two K steps (d >= 128),
+// and rows of whole 16-byte groups in its output (3E % 4 == 0; E % 8 == 0
+// keeps the three column blocks 32-byte aligned).
 static bool router_on_gemm(moe_dtype_t dt, int d, int E)
 {
-    return dt == MOE_BF16 && E > 64 && d % 64 == 0 && d >= 128;
+    return dt == MOE_BF16 && E > 64 && E % 8 == 0 && d % 64 == 0 && d >= 128;
 }
 
 size_t route_ws_bytes(int64_t T, int d, int E)
