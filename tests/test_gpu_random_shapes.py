@@ -75,3 +75,43 @@ def test_random_shape(name):
     for gname, rname in ROUTER_GRADS:
         err = rel_err(grads[gname].cpu().numpy(), getattr(ref, rname))
         assert err <= TOL_ROUTER, (gname, err)
+
+
+def _draw_large(n=8, seed=1001):
+    """Larger layers (multi-round GEMMs, split-K tails, the large dispatch
+    planner, many route blocks), checked on a token sample."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = wl.BF16 if rng.random() < 0.85 else wl.F32
+        E = int(rng.choice([8, 16, 60, 64, 72, 128, 256, 512]))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        mult = 64 if rng.random() < 0.7 else 8
+        d = mult * int(rng.integers(max(1, 256 // mult), 2048 // mult + 1))
+        ffn = mult * int(rng.integers(max(1, 128 // mult), 4096 // mult + 1))
+        T = int(rng.integers(2000, 40000))
+        if dtype == wl.F32:
+            d, ffn, T = min(d, 512), min(ffn, 512), min(T, 4000)
+        cap = float(rng.choice([0.0, 0.0, 1.0, 1.25]))
+        nle = 0
+        e0 = 0
+        if rng.random() < 0.3:
+            nle = int(rng.integers(1, E + 1))
+            e0 = int(rng.integers(0, E - nle + 1))
+        cases.append(wl.Workload(
+            "large%02d" % i, T=T, d=d, E=E, k=k, ffn=ffn, dtype=dtype, capacity_factor=cap, expert_begin=e0,
+            num_local_experts=nle, shared_expert=bool(rng.random() < 0.2),
+            router_bias=str(rng.choice(["zero", "gauss", "zipf"])), expert_bias=str(rng.choice(["zero", "gauss"])),
+            sel_bias=str(rng.choice(["none", "gauss"]))))
+    return cases
+
+
+LARGE = {w.name: w for w in _draw_large()}
+
+
+@pytest.mark.parametrize("name", list(LARGE))
+def test_random_large_shape(name):
+    w = LARGE[name]
+    print("random large case", w, flush=True)
+    inp, t = _inputs(w, seed=3)
+    _check_forward(w, inp, t, tokens=64)
