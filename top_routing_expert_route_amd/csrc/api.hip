@@ -544,8 +544,10 @@ BackwardWs carve_backward(const moe_problem_t *p, const moe_grads_t *g, void *ba
     w.x_perm = cv.take<char>((size_t)max_rows * p->d * es);
     w.dyp = cv.take<char>((size_t)max_rows * p->d * es);
     w.du = cv.take<char>((size_t)rows * p->ffn * es);
-    w.w1t = cv.take<char>((size_t)E_loc * p->ffn * p->d * es);
-    w.w2t = cv.take<char>((size_t)E_loc * p->ffn * p->d * es);
+    // transposed weights only for fp32 (bf16 GEMMs read W1, W2 K-major as stored)
+    const size_t wt_bytes = p->dtype == MOE_BF16 ? 0 : (size_t)E_loc * p->ffn * p->d * es;
+    w.w1t = cv.take<char>(wt_bytes);
+    w.w2t = cv.take<char>(wt_bytes);
     w.xT = cv.take<char>((size_t)p->d * w.Kp * es);
     w.dyT = cv.take<char>((size_t)p->d * w.Kp * es);
     w.duT = cv.take<char>((size_t)p->ffn * w.Kp * es);
@@ -580,10 +582,13 @@ moe_status_t ffn_backward(const moe_problem_t *p, const void *x, const void *dy,
 {
     const moe_dtype_t dt = p->dtype;
     const int d = p->d, F = p->ffn;
+    // bf16: the GEMMs against W2 and W1 read them K-major as stored; fp32:
+    // explicit transposes W1^T [S, d, F], W2^T [S, F, d]
+    const bool kmajor = dt == MOE_BF16;
     moe_status_t s = launch_kseg_layout(a.seg, a.S, a.rows, b.kcol, st);
-    if (!s) // W1^T [S, d, F], W2^T [S, F, d]
+    if (!s && !kmajor)
         s = launch_transpose_batched(a.w1, a.S, F, d, a.seg, dt, b.w1t, st);
-    if (!s)
+    if (!s && !kmajor)
         s = launch_transpose_batched(a.w2, a.S, d, F, a.seg, dt, b.w2t, st);
     const float *u = a.u_saved ? a.u_saved : b.u;
     if (!s && !a.u_saved) // u = W1 x + b1 (fp32)
@@ -596,16 +601,20 @@ moe_status_t ffn_backward(const moe_problem_t *p, const void *x, const void *dy,
         s = launch_seg_colsum(b.colpart, b.kcol, a.S, d, a.db2, st);
     const void *dyr = a.dy_rows ? a.dy_rows : b.dyp;
     if (!s) // dh' = W2^T dY
-        s = launch_grouped_gemm_f32out(dyr, a.seg, a.S, a.rows, F, d, dt, b.w2t, nullptr, b.dh, b.gemm_ws,
-                                       b.gemm_ws_bytes, st);
+        s = kmajor ? launch_grouped_gemm_kmajor_f32out(dyr, a.seg, a.S, a.rows, F, d, a.w2, b.dh, b.gemm_ws,
+                                                       b.gemm_ws_bytes, st)
+                   : launch_grouped_gemm_f32out(dyr, a.seg, a.S, a.rows, F, d, dt, b.w2t, nullptr, b.dh, b.gemm_ws,
+                                                b.gemm_ws_bytes, st);
     if (!s)
         s = launch_act_bwd(u, b.dh, F, a.row_src, a.wgt, a.seg, a.S, a.rows, b.kcol, b.Kp, dt, b.du, b.duT, b.gwT,
                            a.dwpart, a.db1 ? b.colpart : nullptr, st);
     if (!s)
         s = launch_seg_colsum(b.colpart, b.kcol, a.S, F, a.db1, st);
     if (!s) // dx rows = W1^T du
-        s = launch_grouped_gemm_f32out(b.du, a.seg, a.S, a.rows, d, F, dt, b.w1t, nullptr, a.dx_rows, b.gemm_ws,
-                                       b.gemm_ws_bytes, st);
+        s = kmajor ? launch_grouped_gemm_kmajor_f32out(b.du, a.seg, a.S, a.rows, d, F, a.w1, a.dx_rows, b.gemm_ws,
+                                                       b.gemm_ws_bytes, st)
+                   : launch_grouped_gemm_f32out(b.du, a.seg, a.S, a.rows, d, F, dt, b.w1t, nullptr, a.dx_rows,
+                                                b.gemm_ws, b.gemm_ws_bytes, st);
     if (!s) // x rows, transposed, for dW1
         s = launch_gather_t(x, d, a.row_src, p->k, nullptr, a.seg, a.S, a.rows, b.kcol, b.Kp, dt, b.xT, nullptr,
                             nullptr, st);

@@ -175,6 +175,13 @@ moe_status_t launch_grouped_gemm_f32out(const void *a, const int32_t *seg_offset
                                         int64_t max_rows, int N, int K, moe_dtype_t dt, const void *w,
                                         const void *bias, float *out, void *ws, size_t ws_bytes, hipStream_t stream);
 
+// The same with a K-major weight, w_kn [S, K, N] (N contiguous): out[r, n] =
+// sum_k a[r, k] w_kn[s, k, n], no bias; bf16 only, K % 64 == 0, K >= 128,
+// N % 4 == 0, K * N < 2^31.
+moe_status_t launch_grouped_gemm_kmajor_f32out(const void *a, const int32_t *seg_offsets, int num_segments,
+                                               int64_t max_rows, int N, int K, const void *w_kn, float *out,
+                                               void *ws, size_t ws_bytes, hipStream_t stream);
+
 // K-segmented layout of the weight-gradient GEMMs: segment s of seg (NULL =
 // one segment of max_rows rows) takes max(2, ceil(rows_s / 64)) steps of 64
 // columns (none if empty); kcol [S+1] = first step of each segment, kcol[S]

@@ -318,13 +318,16 @@ __device__ __forceinline__ int64_t uni64(int64_t v)
 // Wave grid of a 256x256 tile: WGN waves along the features and WGM along
 // the rows; each wave owns (256/WGN) x (256/WGM) as FA x FB MFMA tiles of
 // 32x32.
-template <int WGN, int WGM> struct Grid {
+template <int WGN, int WGM, bool WT_ = false> struct Grid {
     static constexpr int WGN_ = WGN, WGM_ = WGM;
+    // WT: the weight operand is K-major ([K][N] per segment, N contiguous)
+    static constexpr bool WT = WT_;
     static constexpr int NW = WGN * WGM;
     static constexpr int WTN = kL / WGN, WTM = kL / WGM;
     static constexpr int FA = WTN / 32, FB = WTM / 32;
 };
 typedef Grid<2, 4> LargeGrid;
+typedef Grid<2, 4, true> LargeGridWT;
 constexpr int kLargeBK = 64;
 
 // Epilogue of a 256x256 tile: bias, activation and store of the rows inside
@@ -497,15 +500,16 @@ struct Fill {
     uint32_t so_w, so_a;
 };
 
-template <int BK>
-__device__ __forceinline__ Fill fill_k(uint64_t wb, uint64_t ab, uint32_t ws, uint32_t as, int k, int KTa)
+template <int BK, bool WT = false>
+__device__ __forceinline__ Fill fill_k(uint64_t wb, uint64_t ab, uint32_t ws, uint32_t as, int k, int KTa,
+                                       uint32_t row_w = 0)
 {
     Fill f;
     f.wbase = wb;
     f.abase = ab;
     f.wbytes = ws;
     f.abytes = as;
-    f.so_w = (uint32_t)k * (BK * 2);
+    f.so_w = WT ? (uint32_t)k * (uint32_t)BK * row_w : (uint32_t)k * (BK * 2);
     f.so_a = (uint32_t)(k % KTa) * (BK * 2);
     return f;
 }
@@ -523,6 +527,8 @@ template <int BK, class G> __device__ __forceinline__ uint32_t copy_soff(const C
 {
     constexpr int CPR = BK / 8, RPI = 64 / CPR, NW = G::NW;
     const int q = i >> 1;
+    if (G::WT && !(i & 1))
+        return (uint32_t)q * (uint32_t)(2 * NW) * cg.row_w + f.so_w;
     return (i & 1) ? (uint32_t)q * (uint32_t)(NW * RPI) * cg.row_a + f.so_a
                    : (uint32_t)q * (uint32_t)(NW * RPI) * cg.row_w + f.so_w;
 }
@@ -539,6 +545,13 @@ template <int BK, class G> __device__ __forceinline__ uint32_t copy_ldsoff(int w
 {
     constexpr int CPR = BK / 8, RPI = 64 / CPR, NW = G::NW;
     const int q = i >> 1;
+    if (G::WT && !(i & 1)) {
+        // K-row kr of the stage's [k][n] weight tile: 512-byte rows, 32-byte
+        // chunk c stored at c ^ (2 (kr & 3))
+        const int kr = 2 * (NW * q + wave) + (lane >> 5);
+        const int c = (lane & 31) >> 1;
+        return (uint32_t)(kr * (kL * 2) + ((c ^ (2 * (kr & 3))) * 32) + (lane & 1) * 16);
+    }
     const uint32_t R = (uint32_t)((NW * q + wave) * RPI);
     return (uint32_t)((i & 1) * (kL * BK) + R * BK) * 2u + (uint32_t)lane * 16u;
 }
@@ -571,7 +584,20 @@ __device__ __forceinline__ void read_frag(const uint16_t *stage, int ks, bf16x8 
                                           int r, int wn, int wm, int r32, int khalf, int sw)
 {
     const int ch = ((ks * 2 + khalf) ^ sw) * 8;
-    if (r < G::FA) {
+    if (r < G::FA && G::WT) {
+        // lanes 16 g + i of a half-wave take n = base + 16 g + i, k0 .. k0 + 7
+        // (k0 = 16 ks + 8 khalf) from two transposed reads of 4 K-rows each
+        const int g = r32 >> 4, i = r32 & 15;
+        const int kr = ks * 16 + khalf * 8 + (i >> 2);
+        const int c = (wn * G::WTN + r * 32) / 16 + g;
+        typedef short v4i16 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+        const char *st = reinterpret_cast<const char *>(stage);
+        const int off0 = kr * (kL * 2) + ((c ^ (2 * (kr & 3))) * 32) + (i & 3) * 8;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(st + off0));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(st + off0 + 4 * (kL * 2)));
+        fa[r] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else if (r < G::FA) {
         fa[r] = *reinterpret_cast<const bf16x8 *>(stage + (wn * G::WTN + r * 32 + r32) * BK + ch);
     } else if (r - G::FA < NBV) {
         const int b = r - G::FA;
@@ -638,7 +664,12 @@ __device__ __forceinline__ void k_step(const uint16_t *cur, uint16_t *nxt, const
 #pragma unroll
                         for (int q = 0; q < RPC; ++q)
                             if (c < RCH && c * RPC + q < RDS && (q * MPC) / RPC == m)
-                                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                            {
+                                if (G::WT && read_slot<G>(c * RPC + q) < FA)
+                                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                                else
+                                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                            }
                     }
                 }
             }
@@ -676,6 +707,7 @@ struct WorkCtx {
     const uint16_t *A, *W;
     int64_t max_rows, first, F;
     int S, N, K, Ka, NT, KT, per, nw, unit, sk, n_work;
+    bool wt; // weight operand K-major
 };
 
 // Work item i, all fields wave-uniform.
@@ -712,9 +744,15 @@ struct Src {
 __device__ __forceinline__ Src src_of(const WorkCtx &x, const CopyGeo &cg, const Work &w)
 {
     Src s;
-    s.wbase = (uint64_t)(uintptr_t)(x.W + (int64_t)w.t.s * x.N * x.K + (int64_t)w.t.n0 * x.K);
     s.abase = (uint64_t)(uintptr_t)(x.A + w.t.row0 * x.Ka);
-    s.wbytes = (uint32_t)min(kL, x.N - w.t.n0) * cg.row_w;
+    if (x.wt) {
+        // K-major: from (k = 0, n = n0) to the end of the segment's [K][N] matrix
+        s.wbase = (uint64_t)(uintptr_t)(x.W + (int64_t)w.t.s * x.N * x.K + w.t.n0);
+        s.wbytes = (uint32_t)((int64_t)x.K * x.N - w.t.n0) * 2u;
+    } else {
+        s.wbase = (uint64_t)(uintptr_t)(x.W + (int64_t)w.t.s * x.N * x.K + (int64_t)w.t.n0 * x.K);
+        s.wbytes = (uint32_t)min(kL, x.N - w.t.n0) * cg.row_w;
+    }
     s.abytes = (uint32_t)(w.t.row_end - w.t.row0) * cg.row_a;
     return s;
 }
@@ -766,7 +804,7 @@ __device__ __forceinline__ int tile(uint16_t *smem, int b, const CopyGeo &cg, co
                 koff = -kt_hi;
             }
         }
-        const Fill f = fill_k<BK>(src.wbase, src.abase, src.wbytes, src.abytes, kt + 2 + koff, cg.KTa);
+        const Fill f = fill_k<BK, G::WT>(src.wbase, src.abase, src.wbytes, src.abytes, kt + 2 + koff, cg.KTa, cg.row_w);
         const int bn = b ^ 1;
         k_step<BK, G, NBV>(smem + b * STAGE, smem + bn * STAGE, f, stg, cg, acc, fa, fb, wave, lane, wn, wm, r32,
                            khalf, sw);
@@ -848,6 +886,7 @@ __global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_256(const uint16_t
     x.N = N;
     x.K = K;
     x.Ka = Ka;
+    x.wt = G::WT;
     x.NT = NT;
     x.KT = KT;
     x.F = plan.F;
@@ -868,9 +907,11 @@ __global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_256(const uint16_t
         const int lrow = lane / CPR;
         const int prow = wave * RPI + lrow;
         const int lchunk = (lane % CPR) ^ swz(prow);
-        cg.row_w = (uint32_t)K * 2u;
+        cg.row_w = (uint32_t)(G::WT ? N : K) * 2u;
         cg.row_a = (uint32_t)Ka * 2u;
-        cg.vbase = (uint32_t)prow * cg.row_w + (uint32_t)lchunk * 16u;
+        // K-major weight: a copy instruction moves two 512-byte K-rows
+        cg.vbase = G::WT ? (uint32_t)(2 * wave + (lane >> 5)) * cg.row_w + (uint32_t)(lane & 31) * 16u
+                         : (uint32_t)prow * cg.row_w + (uint32_t)lchunk * 16u;
         cg.vbase_a = (uint32_t)prow * cg.row_a + (uint32_t)lchunk * 16u;
         cg.KTa = Ka / BK;
     }
@@ -881,14 +922,14 @@ __global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_256(const uint16_t
     {
         const Work w = get_work(x, 0);
         const Src o = src_of(x, cg, w);
-        const Fill f0 = fill_k<BK>(o.wbase, o.abase, o.wbytes, o.abytes, w.kt_lo, cg.KTa);
+        const Fill f0 = fill_k<BK, G::WT>(o.wbase, o.abase, o.wbytes, o.abytes, w.kt_lo, cg.KTa, cg.row_w);
 #pragma unroll
         for (int i = 0; i < DPW; ++i)
             stg.v[i] = copy_load<BK, G>(cg, f0, i);
 #pragma unroll
         for (int i = 0; i < DPW; ++i)
             *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(smem) + copy_ldsoff<BK, G>(wave, lane, i)) = stg.v[i];
-        const Fill f1 = fill_k<BK>(o.wbase, o.abase, o.wbytes, o.abytes, w.kt_lo + 1, cg.KTa);
+        const Fill f1 = fill_k<BK, G::WT>(o.wbase, o.abase, o.wbytes, o.abytes, w.kt_lo + 1, cg.KTa, cg.row_w);
 #pragma unroll
         for (int i = 0; i < DPW; ++i)
             stg.v[i] = copy_load<BK, G>(cg, f1, i);
@@ -1103,14 +1144,14 @@ __global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_kseg(const uint16_
     {
         const Work w = get_work(x, 0);
         const Src o = src_of(x, cg, w);
-        const Fill f0 = fill_k<BK>(o.wbase, o.abase, o.wbytes, o.abytes, w.kt_lo, cg.KTa);
+        const Fill f0 = fill_k<BK, G::WT>(o.wbase, o.abase, o.wbytes, o.abytes, w.kt_lo, cg.KTa, cg.row_w);
 #pragma unroll
         for (int i = 0; i < DPW; ++i)
             stg.v[i] = copy_load<BK, G>(cg, f0, i);
 #pragma unroll
         for (int i = 0; i < DPW; ++i)
             *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(smem) + copy_ldsoff<BK, G>(wave, lane, i)) = stg.v[i];
-        const Fill f1 = fill_k<BK>(o.wbase, o.abase, o.wbytes, o.abytes, w.kt_lo + 1, cg.KTa);
+        const Fill f1 = fill_k<BK, G::WT>(o.wbase, o.abase, o.wbytes, o.abytes, w.kt_lo + 1, cg.KTa, cg.row_w);
 #pragma unroll
         for (int i = 0; i < DPW; ++i)
             stg.v[i] = copy_load<BK, G>(cg, f1, i);
@@ -1347,11 +1388,10 @@ int large_grid(int64_t max_rows, int S, int N, bool split)
     return (int)grid;
 }
 
-template <bool GELU, bool BIAS, bool F32OUT>
+template <bool GELU, bool BIAS, bool F32OUT, class G = LargeGrid>
 moe_status_t run_large(const void *a, const int32_t *seg, int S, int64_t max_rows, int N, int K, int Ka,
                        const void *w, const void *bias, void *out, float *part_ws, hipStream_t stream)
 {
-    typedef LargeGrid G;
     // the epilogue writes 4 features per lane; rows of the output must not split such a group
     if (N % 4 != 0 || K % kLargeBK != 0 || K / kLargeBK < 2 || Ka % kLargeBK != 0)
         return fail(MOE_ERR_UNSUPPORTED, "grouped_gemm_256: needs N %% 4 == 0, K %% 64 == 0, K >= 128 (N=%d K=%d)",
@@ -1476,6 +1516,21 @@ moe_status_t launch_kseg_gemm(const void *A, const void *W, const int32_t *kcol,
     const int64_t bx0 = (MN / 4 + 255) / 256, bx = bx0 < 256 ? bx0 : 256;
     kseg_zero_empty<<<dim3((unsigned)bx, (unsigned)S), 256, 0, stream>>>(kcol, MN, C);
     return check_launch("kseg_zero_empty");
+}
+
+moe_status_t launch_grouped_gemm_kmajor_f32out(const void *a, const int32_t *seg_offsets, int num_segments,
+                                               int64_t max_rows, int N, int K, const void *w_kn, float *out,
+                                               void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (max_rows == 0)
+        return MOE_OK;
+    if ((int64_t)K * N > ((int64_t)1 << 31) - 1)
+        return fail(MOE_ERR_UNSUPPORTED, "grouped_gemm (K-major weight): K x N = %lld above 2^31",
+                    (long long)K * N);
+    const int S = seg_offsets ? num_segments : 1;
+    float *part = (ws && ws_bytes >= gemm_ws_bytes()) ? (float *)ws : nullptr;
+    return run_large<false, false, true, LargeGridWT>(a, seg_offsets, S, max_rows, N, K, K, w_kn, nullptr, out,
+                                                      part, stream);
 }
 
 moe_status_t launch_grouped_gemm_f32out(const void *a, const int32_t *seg_offsets, int num_segments,
