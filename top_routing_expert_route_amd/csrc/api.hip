@@ -488,8 +488,9 @@ extern "C" moe_status_t moe_forward_overlap(const moe_problem_t *p, const moe_we
 namespace {
 
 // Workspace of moe_backward.  The shared expert runs first and writes its dx
-// straight into the caller's dx; the routed experts then reuse its buffers (rows = max(routed rows,
-// T), transposed weights for max(E_loc, 1) experts).
+// straight into the caller's dx; the routed experts then reuse its buffers
+// (rows = max(routed rows, T); transposed weights, fp32 layers only, for
+// max(E_loc, 1) experts).
 struct BackwardWs {
     int32_t *topk_idx, *expert_count, *seg_offsets, *kept_count, *slot_row, *row_src, *kcol;
     float *topk_w, *f, *P, *l_aux, *probs, *dl;

@@ -26,7 +26,9 @@
 // are stored transposed in the K-segmented layout (kcol): row block s of
 // 64-aligned columns per segment, zero-padded.  The kernels here write those
 // operands straight from the row-major data, transposing through LDS tiles
-// (gather_t) or in registers (act_bwd, the weight transposes).
+// (gather_t, act_bwd).  The weights need no transpose for bf16 layers (the
+// GEMMs read them K-major); fp32 layers transpose them in registers
+// (transpose_batched).
 #include "common.hpp"
 
 namespace moe {
