@@ -496,7 +496,7 @@ struct BackwardWs {
     float *topk_w, *f, *P, *l_aux, *probs, *dl;
     void *route_ws, *dispatch_ws, *gemm_ws, *router_ws;
     size_t gemm_ws_bytes;
-    void *x_perm, *dyp, *du, *w1t, *w2t, *xT, *dyT, *duT, *gwT;
+    void *x_perm, *dyp, *du, *w1t, *w2t, *xT, *dyT, *duT, *gwT, *gw;
     float *u, *dh, *dx_rows, *dwpart, *colpart, *bias_part;
     int64_t Kp;
     size_t bytes;
@@ -507,6 +507,14 @@ struct BackwardWs {
 bool router_on_mfma(const moe_problem_t *p)
 {
     return p->dtype == MOE_BF16 && p->E >= 32 && p->E % 8 == 0 && p->d % 64 == 0;
+}
+
+// bf16 weight-gradient GEMMs on the row-major dispatched rows (no
+// transposed copies), when their sizes allow.  A segment holds at most T
+// rows: an expert takes each token at most once, the shared expert all T.
+bool wgrad_on_rows(const moe_problem_t *p)
+{
+    return p->dtype == MOE_BF16 && kseg_kmajor_ok(p->T, p->d, p->ffn);
 }
 
 BackwardWs carve_backward(const moe_problem_t *p, const moe_grads_t *g, void *base)
@@ -549,10 +557,13 @@ BackwardWs carve_backward(const moe_problem_t *p, const moe_grads_t *g, void *ba
     const size_t wt_bytes = p->dtype == MOE_BF16 ? 0 : (size_t)E_loc * p->ffn * p->d * es;
     w.w1t = cv.take<char>(wt_bytes);
     w.w2t = cv.take<char>(wt_bytes);
-    w.xT = cv.take<char>((size_t)p->d * w.Kp * es);
-    w.dyT = cv.take<char>((size_t)p->d * w.Kp * es);
-    w.duT = cv.take<char>((size_t)p->ffn * w.Kp * es);
-    w.gwT = cv.take<char>((size_t)p->ffn * w.Kp * es);
+    // transposed operands of the weight-gradient GEMMs, or (on rows) gw rows
+    const bool on_rows = wgrad_on_rows(p);
+    w.xT = cv.take<char>(on_rows ? 0 : (size_t)p->d * w.Kp * es);
+    w.dyT = cv.take<char>(on_rows ? 0 : (size_t)p->d * w.Kp * es);
+    w.duT = cv.take<char>(on_rows ? 0 : (size_t)p->ffn * w.Kp * es);
+    w.gwT = cv.take<char>(on_rows ? 0 : (size_t)p->ffn * w.Kp * es);
+    w.gw = cv.take<char>(on_rows ? (size_t)rows * p->ffn * es : 0);
     w.u = cv.take<float>((size_t)rows * p->ffn);
     w.dh = cv.take<float>((size_t)rows * p->ffn);
     w.dx_rows = cv.take<float>((size_t)rows * p->d);
@@ -586,6 +597,9 @@ moe_status_t ffn_backward(const moe_problem_t *p, const void *x, const void *dy,
     // bf16: the GEMMs against W2 and W1 read them K-major as stored; fp32:
     // explicit transposes W1^T [S, d, F], W2^T [S, F, d]
     const bool kmajor = dt == MOE_BF16;
+    // bf16 (sizes allowing): dW1 and dW2 from the row-major rows of x, dY, du
+    // and gw; otherwise from transposed copies [D, Kp]
+    const bool on_rows = wgrad_on_rows(p);
     moe_status_t s = launch_kseg_layout(a.seg, a.S, a.rows, b.kcol, st);
     if (!s && !kmajor)
         s = launch_transpose_batched(a.w1, a.S, F, d, a.seg, dt, b.w1t, st);
@@ -595,9 +609,9 @@ moe_status_t ffn_backward(const moe_problem_t *p, const void *x, const void *dy,
     if (!s && !a.u_saved) // u = W1 x + b1 (fp32)
         s = launch_grouped_gemm_f32out(a.a_rows, a.seg, a.S, a.rows, F, d, dt, a.w1, a.b1, b.u, b.gemm_ws,
                                        b.gemm_ws_bytes, st);
-    if (!s) // dY rows (row-major for dh', transposed for dW2) and db2
-        s = launch_gather_t(dy, d, a.row_src, p->k, a.wgt, a.seg, a.S, a.rows, b.kcol, b.Kp, dt, b.dyT,
-                            a.dy_rows ? nullptr : b.dyp, a.db2 ? b.colpart : nullptr, st);
+    if (!s && !(on_rows && a.dy_rows && !a.db2)) // dY rows (row-major for dh', transposed for dW2) and db2
+        s = launch_gather_t(dy, d, a.row_src, p->k, a.wgt, a.seg, a.S, a.rows, b.kcol, b.Kp, dt,
+                            on_rows ? nullptr : b.dyT, a.dy_rows ? nullptr : b.dyp, a.db2 ? b.colpart : nullptr, st);
     if (!s)
         s = launch_seg_colsum(b.colpart, b.kcol, a.S, d, a.db2, st);
     const void *dyr = a.dy_rows ? a.dy_rows : b.dyp;
@@ -607,8 +621,9 @@ moe_status_t ffn_backward(const moe_problem_t *p, const void *x, const void *dy,
                    : launch_grouped_gemm_f32out(dyr, a.seg, a.S, a.rows, F, d, dt, b.w2t, nullptr, b.dh, b.gemm_ws,
                                                 b.gemm_ws_bytes, st);
     if (!s)
-        s = launch_act_bwd(u, b.dh, F, a.row_src, a.wgt, a.seg, a.S, a.rows, b.kcol, b.Kp, dt, b.du, b.duT, b.gwT,
-                           a.dwpart, a.db1 ? b.colpart : nullptr, st);
+        s = launch_act_bwd(u, b.dh, F, a.row_src, a.wgt, a.seg, a.S, a.rows, b.kcol, b.Kp, dt, b.du,
+                           on_rows ? nullptr : b.duT, on_rows ? nullptr : b.gwT, on_rows ? b.gw : nullptr, a.dwpart,
+                           a.db1 ? b.colpart : nullptr, st);
     if (!s)
         s = launch_seg_colsum(b.colpart, b.kcol, a.S, F, a.db1, st);
     if (!s) // dx rows = W1^T du
@@ -616,6 +631,13 @@ moe_status_t ffn_backward(const moe_problem_t *p, const void *x, const void *dy,
                                                        b.gemm_ws_bytes, st)
                    : launch_grouped_gemm_f32out(b.du, a.seg, a.S, a.rows, d, F, dt, b.w1t, nullptr, a.dx_rows,
                                                 b.gemm_ws, b.gemm_ws_bytes, st);
+    if (on_rows) {
+        if (!s) // dW2_s = sum_r dY (w g)^T : [d, F]
+            s = launch_kseg_gemm_kmajor(dyr, b.gw, a.seg, a.rows, p->T, b.kcol, a.S, d, F, a.dw2, st);
+        if (!s) // dW1_s = sum_r du x^T : [F, d]
+            s = launch_kseg_gemm_kmajor(b.du, a.a_rows, a.seg, a.rows, p->T, b.kcol, a.S, F, d, a.dw1, st);
+        return s;
+    }
     if (!s) // x rows, transposed, for dW1
         s = launch_gather_t(x, d, a.row_src, p->k, nullptr, a.seg, a.S, a.rows, b.kcol, b.Kp, dt, b.xT, nullptr,
                             nullptr, st);

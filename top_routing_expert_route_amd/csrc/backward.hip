@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void transpose_batched(const uint16_t *__restr
 // Gather of token rows into the K-segmented layout.  Column 64 kcol[s] + i
 // holds row r = lo_s + i of segment s (token t = row_src[r] / k, or r when
 // row_src is NULL); columns past the segment's rows are zero.  D % 8 == 0.
-//   dstT[f, col]     = src[t, f]
+//   dstT[f, col]     = src[t, f]                      (if dstT)
 //   dst[r, f]        = src[t, f]                      (if dst)
 //   colpart[ct, f]   = sum over the tile's rows of wgt[row_src[r]] src[t, f]
 //                      (wgt NULL: weight 1)           (if colpart)
@@ -258,6 +258,8 @@ __global__ __launch_bounds__(256) void gather_t(const T *__restrict__ src, int D
             if (rg == 0 && fv)
                 store8<float>(colpart + (int64_t)ct * D + f0, cs);
         }
+        if (!dstT)
+            continue;
         const int64_t col = (int64_t)ct * 64 + rg * 8;
 #pragma unroll
         for (int j = 0; j < 8 && fv; ++j) {
@@ -273,7 +275,8 @@ __global__ __launch_bounds__(256) void gather_t(const T *__restrict__ src, int D
 // GELU backward over the K-segmented rows (same row/column map as gather_t),
 // from u = W1 x + b1 and dh' (both fp32 [rows, F], F % 4 == 0):
 //   du[r, q]  = w_r dh'[r, q] GELU'(u[r, q])        (row-major, T)
-//   duT[q, col] = du[r, q],  gwT[q, col] = w_r GELU(u[r, q])   (zero padding)
+//   gw[r, q]  = w_r GELU(u[r, q])                    (row-major, if gw)
+//   duT[q, col] = du[r, q],  gwT[q, col] = gw[r, q]  (zero padding; if duT)
 //   dwpart[r, qt] = sum_{q in feature tile qt} dh'[r, q] GELU(u[r, q])   (if dwpart)
 //   colpart[ct, q] = sum over the tile's rows of du[r, q]               (if colpart)
 // w_r = wgt[row_src[r]] (1 when wgt is NULL).  A block takes one 64-row
@@ -291,7 +294,8 @@ __global__ __launch_bounds__(256) void act_bwd(const float *__restrict__ u, cons
                                                const float *__restrict__ wgt, const int32_t *__restrict__ seg, int S,
                                                int64_t rows, const int32_t *__restrict__ kcol, int64_t Kp,
                                                T *__restrict__ du, T *__restrict__ duT, T *__restrict__ gwT,
-                                               float *__restrict__ dwpart, float *__restrict__ colpart)
+                                               T *__restrict__ gw, float *__restrict__ dwpart,
+                                               float *__restrict__ colpart)
 {
     constexpr int ES = (int)sizeof(T);
     constexpr int LS = 64 + 16 / ES;            // LDS row (one feature) of 64 rows, padded
@@ -343,13 +347,16 @@ __global__ __launch_bounds__(256) void act_bwd(const float *__restrict__ u, cons
                 acc = fmaf(hh[i][j], g, acc);
             }
             rs[i] = acc;
-            if (r < hi && qv)
+            if (r < hi && qv) {
                 store4v<T>(du + r * F + q, vdu[i]);
+                if (gw)
+                    store4v<T>(gw + r * F + q, vgw[i]);
+            }
         }
         // transposed through LDS: feature fl + j, rows rl .. rl + 3
         __syncthreads(); // the previous tile's LDS reads are done
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 4 && duT; ++j) {
             const float a4[4] = {vdu[0][j], vdu[1][j], vdu[2][j], vdu[3][j]};
             const float g4[4] = {vgw[0][j], vgw[1][j], vgw[2][j], vgw[3][j]};
             store4v<T>(sdu + (fl + j) * LS + rl, a4);
@@ -390,7 +397,7 @@ __global__ __launch_bounds__(256) void act_bwd(const float *__restrict__ u, cons
         for (int p = 0; p < 64 / FPP; ++p) {
             const int fq = p * FPP + threadIdx.x / LPR;
             const int piece = threadIdx.x % LPR;
-            if (qt * 64 + fq < F) {
+            if (duT && qt * 64 + fq < F) {
                 const int64_t at = (int64_t)(qt * 64 + fq) * Kp + (int64_t)ct * 64 + piece * VPC;
                 *reinterpret_cast<u32x4 *>(duT + at) = *reinterpret_cast<const u32x4 *>(sdu + fq * LS + piece * VPC);
                 *reinterpret_cast<u32x4 *>(gwT + at) = *reinterpret_cast<const u32x4 *>(sgw + fq * LS + piece * VPC);
@@ -864,17 +871,18 @@ moe_status_t launch_gather_t(const void *src, int D, const int32_t *row_src, int
 
 moe_status_t launch_act_bwd(const float *u, const float *dh, int F, const int32_t *row_src, const float *wgt,
                             const int32_t *seg, int S, int64_t rows, const int32_t *kcol, int64_t Kp, moe_dtype_t dt,
-                            void *du, void *duT, void *gwT, float *dwpart, float *colpart, hipStream_t stream)
+                            void *du, void *duT, void *gwT, void *gw, float *dwpart, float *colpart,
+                            hipStream_t stream)
 {
     const int64_t ctiles = Kp / 64;
     const int FT = (F + 63) / 64;
     const dim3 g((unsigned)FT, strided_grid(ctiles, (32768 + FT - 1) / FT));
     if (dt == MOE_BF16)
         act_bwd<uint16_t><<<g, 256, 0, stream>>>(u, dh, F, FT, row_src, wgt, seg, S, rows, kcol, Kp, (uint16_t *)du,
-                                                 (uint16_t *)duT, (uint16_t *)gwT, dwpart, colpart);
+                                                 (uint16_t *)duT, (uint16_t *)gwT, (uint16_t *)gw, dwpart, colpart);
     else
         act_bwd<float><<<g, 256, 0, stream>>>(u, dh, F, FT, row_src, wgt, seg, S, rows, kcol, Kp, (float *)du,
-                                              (float *)duT, (float *)gwT, dwpart, colpart);
+                                              (float *)duT, (float *)gwT, (float *)gw, dwpart, colpart);
     return check_launch("act_bwd");
 }
 

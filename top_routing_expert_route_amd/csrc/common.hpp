@@ -192,6 +192,15 @@ moe_status_t launch_kseg_layout(const int32_t *seg, int S, int64_t max_rows, int
 // A [M, Kp], W [N, Kp] (dt; padding columns zero).  Empty segments give zeros.
 moe_status_t launch_kseg_gemm(const void *A, const void *W, const int32_t *kcol, int S, int M, int N, int64_t Kp,
                               moe_dtype_t dt, float *C, hipStream_t stream);
+// The same sums over the row-major rows themselves (bf16): A_rows [rows, M],
+// W_rows [rows, N], segment s = rows seg[s] .. seg[s+1] (seg NULL: all rows),
+// kcol from launch_kseg_layout over the same seg; no segment may hold more
+// than seg_max rows.  kseg_kmajor_ok: M and N multiples of 8 and
+// seg_max x max(M, N) below 2^30.
+bool kseg_kmajor_ok(int64_t seg_max, int M, int N);
+moe_status_t launch_kseg_gemm_kmajor(const void *A_rows, const void *W_rows, const int32_t *seg, int64_t rows,
+                                     int64_t seg_max, const int32_t *kcol, int S, int M, int N, float *C,
+                                     hipStream_t stream);
 
 // h = GELU(u) (dtype dt) over the rows in use of u [rows, F] fp32 (seg[S]
 // of them, or all rows when seg is NULL); F % 4 == 0.
@@ -214,7 +223,8 @@ moe_status_t launch_gather_t(const void *src, int D, const int32_t *row_src, int
                              void *dstT, void *dst, float *colpart, hipStream_t stream);
 moe_status_t launch_act_bwd(const float *u, const float *dh, int F, const int32_t *row_src, const float *wgt,
                             const int32_t *seg, int S, int64_t rows, const int32_t *kcol, int64_t Kp, moe_dtype_t dt,
-                            void *du, void *duT, void *gwT, float *dwpart, float *colpart, hipStream_t stream);
+                            void *du, void *duT, void *gwT, void *gw, float *dwpart, float *colpart,
+                            hipStream_t stream);
 moe_status_t launch_seg_colsum(const float *colpart, const int32_t *kcol, int S, int D, float *out,
                                hipStream_t stream);
 moe_status_t launch_router_bwd(const float *probs, const int32_t *topk_idx, const int32_t *slot_row,

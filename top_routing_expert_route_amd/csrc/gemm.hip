@@ -318,16 +318,27 @@ __device__ __forceinline__ int64_t uni64(int64_t v)
 // Wave grid of a 256x256 tile: WGN waves along the features and WGM along
 // the rows; each wave owns (256/WGN) x (256/WGM) as FA x FB MFMA tiles of
 // 32x32.
-template <int WGN, int WGM, bool WT_ = false> struct Grid {
+// A K-major LDS tile holds 64 K-rows of 256 values; rows are padded to 576
+// bytes so that the transposing reads of four consecutive K-rows fall on
+// disjoint banks.
+constexpr int kKmPitch = kL * 2 + 64;
+
+template <int WGN, int WGM, bool WT_ = false, bool AT_ = false> struct Grid {
     static constexpr int WGN_ = WGN, WGM_ = WGM;
-    // WT: the weight operand is K-major ([K][N] per segment, N contiguous)
-    static constexpr bool WT = WT_;
+    // WT / AT: the weight / row operand is K-major ([K][N] or [K][M], the
+    // K-segmented GEMM's dispatched rows as they are stored)
+    static constexpr bool WT = WT_, AT = AT_;
     static constexpr int NW = WGN * WGM;
     static constexpr int WTN = kL / WGN, WTM = kL / WGM;
     static constexpr int FA = WTN / 32, FB = WTM / 32;
+    // one LDS stage (K step of 64): the weight tile, then the row tile
+    static constexpr int W_BYTES = WT ? 64 * kKmPitch : kL * 64 * 2;
+    static constexpr int A_BYTES = AT ? 64 * kKmPitch : kL * 64 * 2;
+    static constexpr int STAGE_ELEMS = (W_BYTES + A_BYTES) / 2;
 };
 typedef Grid<2, 4> LargeGrid;
 typedef Grid<2, 4, true> LargeGridWT;
+typedef Grid<2, 4, true, true> LargeGridKK;
 constexpr int kLargeBK = 64;
 
 // Epilogue of a 256x256 tile: bias, activation and store of the rows inside
@@ -500,9 +511,9 @@ struct Fill {
     uint32_t so_w, so_a;
 };
 
-template <int BK, bool WT = false>
+template <int BK, bool WT = false, bool AT = false>
 __device__ __forceinline__ Fill fill_k(uint64_t wb, uint64_t ab, uint32_t ws, uint32_t as, int k, int KTa,
-                                       uint32_t row_w = 0)
+                                       uint32_t row_w = 0, uint32_t row_a = 0)
 {
     Fill f;
     f.wbase = wb;
@@ -510,7 +521,7 @@ __device__ __forceinline__ Fill fill_k(uint64_t wb, uint64_t ab, uint32_t ws, ui
     f.wbytes = ws;
     f.abytes = as;
     f.so_w = WT ? (uint32_t)k * (uint32_t)BK * row_w : (uint32_t)k * (BK * 2);
-    f.so_a = (uint32_t)(k % KTa) * (BK * 2);
+    f.so_a = AT ? (uint32_t)k * (uint32_t)BK * row_a : (uint32_t)(k % KTa) * (BK * 2);
     return f;
 }
 
@@ -529,6 +540,8 @@ template <int BK, class G> __device__ __forceinline__ uint32_t copy_soff(const C
     const int q = i >> 1;
     if (G::WT && !(i & 1))
         return (uint32_t)q * (uint32_t)(2 * NW) * cg.row_w + f.so_w;
+    if (G::AT && (i & 1))
+        return (uint32_t)q * (uint32_t)(2 * NW) * cg.row_a + f.so_a;
     return (i & 1) ? (uint32_t)q * (uint32_t)(NW * RPI) * cg.row_a + f.so_a
                    : (uint32_t)q * (uint32_t)(NW * RPI) * cg.row_w + f.so_w;
 }
@@ -545,15 +558,15 @@ template <int BK, class G> __device__ __forceinline__ uint32_t copy_ldsoff(int w
 {
     constexpr int CPR = BK / 8, RPI = 64 / CPR, NW = G::NW;
     const int q = i >> 1;
-    if (G::WT && !(i & 1)) {
-        // K-row kr of the stage's [k][n] weight tile: 512-byte rows, 32-byte
-        // chunk c stored at c ^ (2 (kr & 3))
+    if ((G::WT && !(i & 1)) || (G::AT && (i & 1))) {
+        // K-row kr of the stage's [k][n] (or [k][m]) tile (kKmPitch-byte rows),
+        // 16 bytes of its 32-byte chunk c
         const int kr = 2 * (NW * q + wave) + (lane >> 5);
         const int c = (lane & 31) >> 1;
-        return (uint32_t)(kr * (kL * 2) + ((c ^ (2 * (kr & 3))) * 32) + (lane & 1) * 16);
+        return (uint32_t)((i & 1) * G::W_BYTES + kr * kKmPitch + c * 32 + (lane & 1) * 16);
     }
     const uint32_t R = (uint32_t)((NW * q + wave) * RPI);
-    return (uint32_t)((i & 1) * (kL * BK) + R * BK) * 2u + (uint32_t)lane * 16u;
+    return (uint32_t)((i & 1) * G::W_BYTES) + (uint32_t)(R * BK) * 2u + (uint32_t)lane * 16u;
 }
 
 // Fragment reads in the order the next sub-step's MFMAs first use them: the
@@ -593,15 +606,27 @@ __device__ __forceinline__ void read_frag(const uint16_t *stage, int ks, bf16x8 
         typedef short v4i16 __attribute__((ext_vector_type(4)));
         typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
         const char *st = reinterpret_cast<const char *>(stage);
-        const int off0 = kr * (kL * 2) + ((c ^ (2 * (kr & 3))) * 32) + (i & 3) * 8;
+        const int off0 = kr * kKmPitch + c * 32 + (i & 3) * 8;
         const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(st + off0));
-        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(st + off0 + 4 * (kL * 2)));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(st + off0 + 4 * kKmPitch));
         fa[r] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     } else if (r < G::FA) {
         fa[r] = *reinterpret_cast<const bf16x8 *>(stage + (wn * G::WTN + r * 32 + r32) * BK + ch);
+    } else if (r - G::FA < NBV && G::AT) {
+        const int b = r - G::FA;
+        const int g = r32 >> 4, i = r32 & 15;
+        const int kr = ks * 16 + khalf * 8 + (i >> 2);
+        const int c = (wm * G::WTM + b * 32) / 16 + g;
+        typedef short v4i16 __attribute__((ext_vector_type(4)));
+        typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+        const char *st = reinterpret_cast<const char *>(stage) + G::W_BYTES;
+        const int off0 = kr * kKmPitch + c * 32 + (i & 3) * 8;
+        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(st + off0));
+        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(st + off0 + 4 * kKmPitch));
+        fb[b] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     } else if (r - G::FA < NBV) {
         const int b = r - G::FA;
-        fb[b] = *reinterpret_cast<const bf16x8 *>(stage + kL * BK + (wm * G::WTM + b * 32 + r32) * BK + ch);
+        fb[b] = *reinterpret_cast<const bf16x8 *>(stage + G::W_BYTES / 2 + (wm * G::WTM + b * 32 + r32) * BK + ch);
     }
 }
 
@@ -665,7 +690,8 @@ __device__ __forceinline__ void k_step(const uint16_t *cur, uint16_t *nxt, const
                         for (int q = 0; q < RPC; ++q)
                             if (c < RCH && c * RPC + q < RDS && (q * MPC) / RPC == m)
                             {
-                                if (G::WT && read_slot<G>(c * RPC + q) < FA)
+                                if ((G::WT && read_slot<G>(c * RPC + q) < FA) ||
+                                    (G::AT && read_slot<G>(c * RPC + q) >= FA))
                                     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
                                 else
                                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
@@ -768,7 +794,7 @@ __device__ __forceinline__ int tile(uint16_t *smem, int b, const CopyGeo &cg, co
                                     int kt_lo, int kt_hi, Staged<BK, G> &stg, void *C, const uint16_t *bseg,
                                     float *part, int64_t row0, int64_t row_end, int n0, int N)
 {
-    constexpr int FA = G::FA, FB = G::FB, STAGE = 2 * kL * BK;
+    constexpr int FA = G::FA, FB = G::FB, STAGE = G::STAGE_ELEMS;
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid)); // lane values are rederived per tile, not kept (spilled) across tiles
     const int lane = tid & 63, wave = tid >> 6;
@@ -791,6 +817,7 @@ __device__ __forceinline__ int tile(uint16_t *smem, int b, const CopyGeo &cg, co
             read_frag<BK, G, NBV>(smem + b * STAGE, 0, fa[0], fb[0], r, wn, wm, r32, khalf, sw);
     }
     int koff = 0; // K step of `src` loaded at step kt: kt + 2 + koff
+    int kbase = G::AT ? kt_lo : 0; // K step at src's base address
     for (int kt = kt_lo; kt < kt_hi; ++kt) {
         if (kt + 2 == kt_hi) {
             // from here on, load the next item's first steps
@@ -798,13 +825,15 @@ __device__ __forceinline__ int tile(uint16_t *smem, int b, const CopyGeo &cg, co
                 const Work wn = get_work(x, i + 1);
                 src = src_of(x, cg, wn);
                 koff = wn.kt_lo - kt_hi;
+                kbase = G::AT ? wn.kt_lo : 0;
             } else {
                 src.wbytes = 0;
                 src.abytes = 0;
                 koff = -kt_hi;
             }
         }
-        const Fill f = fill_k<BK, G::WT>(src.wbase, src.abase, src.wbytes, src.abytes, kt + 2 + koff, cg.KTa, cg.row_w);
+        const Fill f = fill_k<BK, G::WT, G::AT>(src.wbase, src.abase, src.wbytes, src.abytes, kt + 2 + koff - kbase, cg.KTa, cg.row_w,
+                                                    cg.row_a);
         const int bn = b ^ 1;
         k_step<BK, G, NBV>(smem + b * STAGE, smem + bn * STAGE, f, stg, cg, acc, fa, fb, wave, lane, wn, wm, r32,
                            khalf, sw);
@@ -864,7 +893,7 @@ __global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_256(const uint16_t
 {
     constexpr int CPR = BK / 8, RPI = 64 / CPR;
     constexpr int DPW = Staged<BK, G>::DPW;
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * kL * BK];
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * G::STAGE_ELEMS];
     __shared__ int tb[kMaxSeg + 1];
     build_tile_prefix<kL>(seg, S, max_rows, tb);
 
@@ -922,14 +951,15 @@ __global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_256(const uint16_t
     {
         const Work w = get_work(x, 0);
         const Src o = src_of(x, cg, w);
-        const Fill f0 = fill_k<BK, G::WT>(o.wbase, o.abase, o.wbytes, o.abytes, w.kt_lo, cg.KTa, cg.row_w);
+        const int k0 = G::AT ? 0 : w.kt_lo; // K-major sources start at the item's first step
+        const Fill f0 = fill_k<BK, G::WT, G::AT>(o.wbase, o.abase, o.wbytes, o.abytes, k0, cg.KTa, cg.row_w, cg.row_a);
 #pragma unroll
         for (int i = 0; i < DPW; ++i)
             stg.v[i] = copy_load<BK, G>(cg, f0, i);
 #pragma unroll
         for (int i = 0; i < DPW; ++i)
             *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(smem) + copy_ldsoff<BK, G>(wave, lane, i)) = stg.v[i];
-        const Fill f1 = fill_k<BK, G::WT>(o.wbase, o.abase, o.wbytes, o.abytes, w.kt_lo + 1, cg.KTa, cg.row_w);
+        const Fill f1 = fill_k<BK, G::WT, G::AT>(o.wbase, o.abase, o.wbytes, o.abytes, k0 + 1, cg.KTa, cg.row_w, cg.row_a);
 #pragma unroll
         for (int i = 0; i < DPW; ++i)
             stg.v[i] = copy_load<BK, G>(cg, f1, i);
@@ -959,7 +989,13 @@ __global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_256(const uint16_t
 // max(2, ceil(rows_s / 64)) K steps of 64 columns, none if it is empty; kcol
 // [S+1] holds the first step of each segment (kseg_layout).  Empty segments
 // get no tiles (their outputs are zeroed separately).  Same tile machinery
-// as grouped_gemm_256; no split-K tail.
+// as grouped_gemm_256; no split-K tail.  The K-major form (Grid with WT and
+// AT, bf16) reads the same sums from the row-major rows A [rows, M] and
+// W [rows, N] themselves: each K step copies 64 rows of a segment into
+// [k][m] and [k][n] LDS tiles, the fragments come from transposing reads,
+// and rows past the segment's end read as zeros (range-checked loads), so
+// the products meet the accumulators in the same order as with the
+// zero-padded transposed copies.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int kseg_steps(int64_t rows) { return rows <= 0 ? 0 : (int)max<int64_t>(2, (rows + 63) / 64); }
 
@@ -1030,6 +1066,9 @@ constexpr int kKsegPanel = 4;
 struct KsegCtx {
     const int *kb, *ne;
     const uint16_t *A, *W;
+    const int32_t *seg; // K-major operands: dispatched rows of the segments (NULL: one of `rows`)
+    int64_t rows;
+    bool kmajor;        // A [rows, M] and W [rows, N] row-major instead of A [M, Kp], W [N, Kp]
     int64_t first;
     int S, M, N, Kp, MT, NT, per, nw, n_work;
     bool n_inner; // the feature tiles (W) are the smaller operand's (M > N)
@@ -1085,6 +1124,18 @@ __device__ __forceinline__ Src src_of(const KsegCtx &x, const CopyGeo &cg, const
     Src s;
     const int n0 = (int)w.t.n0, row0 = (int)w.t.row0, rows = (int)(w.t.row_end - w.t.row0);
     const int nw = x.N - n0 < kL ? x.N - n0 : kL;
+    if (x.kmajor) {
+        // K-major: both operands start at the segment's first dispatched row;
+        // rows past its end read as zeros
+        int64_t lo, hi;
+        seg_bounds(x.seg, w.t.s, x.rows, lo, hi);
+        const int64_t n = hi - lo;
+        s.wbase = (uint64_t)uni64((int64_t)(uintptr_t)(x.W + lo * x.N + n0));
+        s.abase = (uint64_t)uni64((int64_t)(uintptr_t)(x.A + lo * x.M + row0));
+        s.wbytes = (uint32_t)uni((int)((n * x.N - n0) * 2));
+        s.abytes = (uint32_t)uni((int)((n * x.M - row0) * 2));
+        return s;
+    }
     s.wbase = (uint64_t)uni64((int64_t)(uintptr_t)(x.W + (int64_t)n0 * x.Kp));
     s.abase = (uint64_t)uni64((int64_t)(uintptr_t)(x.A + (int64_t)row0 * x.Kp));
     s.wbytes = (uint32_t)uni(nw * (int)cg.row_w);
@@ -1096,11 +1147,12 @@ template <int BK, class G>
 __global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_kseg(const uint16_t *__restrict__ A,
                                                                    const uint16_t *__restrict__ W,
                                                                    const int32_t *__restrict__ kcol, int S, int M,
-                                                                   int N, int Kp, float *__restrict__ C)
+                                                                   int N, int Kp, float *__restrict__ C,
+                                                                   const int32_t *__restrict__ seg, int64_t rows)
 {
     constexpr int CPR = BK / 8, RPI = 64 / CPR;
     constexpr int DPW = Staged<BK, G>::DPW;
-    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * kL * BK];
+    __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * G::STAGE_ELEMS];
     __shared__ int kb[kMaxSeg + 1], ne[kMaxSeg + 1];
     load_kseg_prefix(kcol, S, kb, ne);
 
@@ -1116,6 +1168,9 @@ __global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_kseg(const uint16_
     x.M = M;
     x.N = N;
     x.Kp = Kp;
+    x.seg = seg;
+    x.rows = rows;
+    x.kmajor = G::AT;
     x.MT = (M + kL - 1) / kL;
     x.NT = (N + kL - 1) / kL;
     x.n_inner = M > N;
@@ -1134,24 +1189,34 @@ __global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_kseg(const uint16_
         const int lrow = lane / CPR;
         const int prow = wave * RPI + lrow;
         const int lchunk = (lane % CPR) ^ swz(prow);
-        cg.row_w = (uint32_t)Kp * 2u;
-        cg.row_a = (uint32_t)Kp * 2u;
-        cg.vbase = (uint32_t)prow * cg.row_w + (uint32_t)lchunk * 16u;
-        cg.vbase_a = cg.vbase;
+        if (G::AT) {
+            // K-major: each wave instruction copies two 512-byte K-rows
+            cg.row_w = (uint32_t)N * 2u;
+            cg.row_a = (uint32_t)M * 2u;
+            const uint32_t kr = (uint32_t)(2 * wave + (lane >> 5)), col = (uint32_t)(lane & 31) * 16u;
+            cg.vbase = kr * cg.row_w + col;
+            cg.vbase_a = kr * cg.row_a + col;
+        } else {
+            cg.row_w = (uint32_t)Kp * 2u;
+            cg.row_a = (uint32_t)Kp * 2u;
+            cg.vbase = (uint32_t)prow * cg.row_w + (uint32_t)lchunk * 16u;
+            cg.vbase_a = cg.vbase;
+        }
         cg.KTa = Kp / BK;
     }
     Staged<BK, G> stg;
     {
         const Work w = get_work(x, 0);
         const Src o = src_of(x, cg, w);
-        const Fill f0 = fill_k<BK, G::WT>(o.wbase, o.abase, o.wbytes, o.abytes, w.kt_lo, cg.KTa, cg.row_w);
+        const int k0 = G::AT ? 0 : w.kt_lo; // K-major sources start at the item's first step
+        const Fill f0 = fill_k<BK, G::WT, G::AT>(o.wbase, o.abase, o.wbytes, o.abytes, k0, cg.KTa, cg.row_w, cg.row_a);
 #pragma unroll
         for (int i = 0; i < DPW; ++i)
             stg.v[i] = copy_load<BK, G>(cg, f0, i);
 #pragma unroll
         for (int i = 0; i < DPW; ++i)
             *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(smem) + copy_ldsoff<BK, G>(wave, lane, i)) = stg.v[i];
-        const Fill f1 = fill_k<BK, G::WT>(o.wbase, o.abase, o.wbytes, o.abytes, w.kt_lo + 1, cg.KTa, cg.row_w);
+        const Fill f1 = fill_k<BK, G::WT, G::AT>(o.wbase, o.abase, o.wbytes, o.abytes, k0 + 1, cg.KTa, cg.row_w, cg.row_a);
 #pragma unroll
         for (int i = 0; i < DPW; ++i)
             stg.v[i] = copy_load<BK, G>(cg, f1, i);
@@ -1509,7 +1574,37 @@ moe_status_t launch_kseg_gemm(const void *A, const void *W, const int32_t *kcol,
     int64_t grid = (int64_t)device_cus();
     grid = (grid + kXcds - 1) / kXcds * kXcds;
     grouped_gemm_kseg<kLargeBK, G><<<(unsigned)grid, 64 * G::NW, 0, stream>>>(
-        (const uint16_t *)A, (const uint16_t *)W, kcol, S, M, N, (int)Kp, C);
+        (const uint16_t *)A, (const uint16_t *)W, kcol, S, M, N, (int)Kp, C, nullptr, 0);
+    if (moe_status_t st = check_launch("grouped_gemm_kseg"))
+        return st;
+    const int64_t MN = (int64_t)M * N;
+    const int64_t bx0 = (MN / 4 + 255) / 256, bx = bx0 < 256 ? bx0 : 256;
+    kseg_zero_empty<<<dim3((unsigned)bx, (unsigned)S), 256, 0, stream>>>(kcol, MN, C);
+    return check_launch("kseg_zero_empty");
+}
+
+bool kseg_kmajor_ok(int64_t seg_max, int M, int N)
+{
+    const int64_t w = M > N ? M : N;
+    return M % 8 == 0 && N % 8 == 0 && seg_max * w * 2 < ((int64_t)1 << 31);
+}
+
+moe_status_t launch_kseg_gemm_kmajor(const void *A_rows, const void *W_rows, const int32_t *seg, int64_t rows,
+                                     int64_t seg_max, const int32_t *kcol, int S, int M, int N, float *C,
+                                     hipStream_t stream)
+{
+    if (S < 1 || M < 1 || N < 1)
+        return MOE_OK;
+    // each segment's operands are addressed with 32-bit byte offsets
+    if (!kseg_kmajor_ok(seg_max < rows ? seg_max : rows, M, N))
+        return fail(MOE_ERR_UNSUPPORTED, "grouped_gemm_kseg (K-major): needs M, N multiples of 8 and rows per "
+                                         "segment x max(M, N) below 2^30 (rows=%lld M=%d N=%d)",
+                    (long long)(seg_max < rows ? seg_max : rows), M, N);
+    typedef LargeGridKK G;
+    int64_t grid = (int64_t)device_cus();
+    grid = (grid + kXcds - 1) / kXcds * kXcds;
+    grouped_gemm_kseg<kLargeBK, G><<<(unsigned)grid, 64 * G::NW, 0, stream>>>(
+        (const uint16_t *)A_rows, (const uint16_t *)W_rows, kcol, S, M, N, 0, C, seg, rows);
     if (moe_status_t st = check_launch("grouped_gemm_kseg"))
         return st;
     const int64_t MN = (int64_t)M * N;
