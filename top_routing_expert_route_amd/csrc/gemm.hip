@@ -398,6 +398,116 @@ __device__ __forceinline__ void store4(const TileOut &rt, const uint16_t *__rest
     }
 }
 
+// fp32 tile without bias or activation, through LDS: the accumulator layout
+// gives each wave store 32 rows x 32 bytes, which a CU issues at a fraction
+// of the rate of row-contiguous stores.  Four rounds per wave, each 32 rows x
+// 64 features (8 KB of the wave's slice of the free LDS stage, 256-byte rows,
+// 16-byte chunk c of row r at c ^ (r & 15)): the lanes write their
+// accumulators, then read back and store 4 rows x 256 contiguous bytes per
+// instruction.  The caller puts a barrier between this and the next writes
+// to the stage.
+template <class G, bool BIAS>
+__device__ __forceinline__ void store_tile_f32_lds(const f32x16 (&acc)[G::FA][G::FB], float *C,
+                                                   const uint16_t *__restrict__ bseg, char *lds, int64_t row0,
+                                                   int64_t row_end, int n0, int N, int wave, int lane, int wn, int wm,
+                                                   int r32, int khalf)
+{
+    static_assert(G::FA == 4 && G::FB == 2, "one 8 KB round per pair of A fragments and B fragment");
+    const TileOut rt = tile_out<true>(C, row0, row_end, N);
+    char *mine = lds + wave * 8192;
+#pragma unroll
+    for (int b = 0; b < G::FB; ++b) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+#pragma unroll
+            for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int c = a2 * 8 + 2 * g + khalf;
+                    const f32x16 &v = acc[2 * p + a2][b];
+                    f32x4 o = {v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
+                    if (BIAS) {
+                        const int n = n0 + wn * G::WTN + (2 * p + a2) * 32 + 8 * g + 4 * khalf;
+                        const uint2 bb = *reinterpret_cast<const uint2 *>(bseg + (n < N ? n : 0));
+                        o[0] += bf16_bits_to_f32(bb.x & 0xFFFFu);
+                        o[1] += bf16_bits_to_f32(bb.x >> 16);
+                        o[2] += bf16_bits_to_f32(bb.y & 0xFFFFu);
+                        o[3] += bf16_bits_to_f32(bb.y >> 16);
+                    }
+                    *reinterpret_cast<f32x4 *>(mine + r32 * 256 + ((c ^ (r32 & 15)) * 16)) = o;
+                }
+            asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int lr = 4 * q + (lane >> 4), c = lane & 15;
+                const f32x4 o = *reinterpret_cast<const f32x4 *>(mine + lr * 256 + ((c ^ (lr & 15)) * 16));
+                const int64_t row = row0 + wm * G::WTM + b * 32 + lr;
+                const int n = n0 + wn * G::WTN + p * 64 + 4 * c;
+                const bool ok = row < row_end && n < N;
+                const uint32_t off = ok ? (uint32_t)((row - rt.row0) * N + n) * 4u : 0x80000000u;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o), rt.r, off, 0, 0);
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); // reads done before the next round's writes
+        }
+    }
+}
+
+// bf16 tile (bias, GELU applied first) through LDS, as store_tile_f32_lds:
+// two rounds per wave of 32 rows x 128 features (8-byte pieces written at
+// piece c ^ 2 (r & 15) of 256-byte rows), read back and stored as 4 rows x
+// 256 contiguous bytes per instruction.  N % 8 == 0.
+template <class G, bool GELU, bool BIAS>
+__device__ __forceinline__ void store_tile_bf16_lds(const f32x16 (&acc)[G::FA][G::FB], uint16_t *C,
+                                                    const uint16_t *__restrict__ bseg, char *lds, int64_t row0,
+                                                    int64_t row_end, int n0, int N, int wave, int lane, int wn,
+                                                    int wm, int r32, int khalf)
+{
+    static_assert(G::FA == 4 && G::FB == 2, "one 8 KB round per B fragment");
+    const TileOut rt = tile_out<false>(C, row0, row_end, N);
+    char *mine = lds + wave * 8192;
+#pragma unroll
+    for (int b = 0; b < G::FB; ++b) {
+#pragma unroll
+        for (int a = 0; a < G::FA; ++a)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int n = n0 + wn * G::WTN + a * 32 + 8 * g + 4 * khalf;
+                float v0 = acc[a][b][4 * g], v1 = acc[a][b][4 * g + 1], v2 = acc[a][b][4 * g + 2],
+                      v3 = acc[a][b][4 * g + 3];
+                if (BIAS) {
+                    const uint2 bb = *reinterpret_cast<const uint2 *>(bseg + (n < N ? n : 0));
+                    v0 += bf16_bits_to_f32(bb.x & 0xFFFFu);
+                    v1 += bf16_bits_to_f32(bb.x >> 16);
+                    v2 += bf16_bits_to_f32(bb.y & 0xFFFFu);
+                    v3 += bf16_bits_to_f32(bb.y >> 16);
+                }
+                if (GELU) {
+                    v0 = gelu_erf(v0);
+                    v1 = gelu_erf(v1);
+                    v2 = gelu_erf(v2);
+                    v3 = gelu_erf(v3);
+                }
+                uint2 o;
+                o.x = pack_bf16x2(v0, v1);
+                o.y = pack_bf16x2(v2, v3);
+                const int c8 = a * 8 + 2 * g + khalf;
+                *reinterpret_cast<uint2 *>(mine + r32 * 256 + ((c8 ^ ((r32 & 15) << 1)) * 8)) = o;
+            }
+        asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory");
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int lr = 4 * q + (lane >> 4), c = lane & 15;
+            const u32x4 o = *reinterpret_cast<const u32x4 *>(mine + lr * 256 + ((c ^ (lr & 15)) * 16));
+            const int64_t row = row0 + wm * G::WTM + b * 32 + lr;
+            const int n = n0 + wn * G::WTN + 8 * c;
+            const bool ok = row < row_end && n < N;
+            const uint32_t off = ok ? (uint32_t)((row - rt.row0) * N + n) * 2u : 0x80000000u;
+            __builtin_amdgcn_raw_buffer_store_b128(o, rt.r, off, 0, 0);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); // reads done before the next round's writes
+    }
+}
+
 template <class G, int NBV, bool GELU, bool BIAS, bool F32OUT>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[G::FA][G::FB], void *C,
                                            const uint16_t *__restrict__ bseg, int64_t row0, int64_t row_end, int n0,
@@ -849,7 +959,18 @@ __device__ __forceinline__ int tile(uint16_t *smem, int b, const CopyGeo &cg, co
                 for (int v = 0; v < 16; ++v)
                     dst[((a * FB + q) * 16 + v) * 64] = acc[a][q][v];
     } else {
-        store_tile<G, NBV, GELU, BIAS, F32OUT>(acc, C, bseg, row0, row_end, n0, N, wn, wm, r32, khalf);
+        // the stage other than b (the next item's first K step) is free after
+        // the loop's last barrier
+        char *free_stage = reinterpret_cast<char *>(smem + (b ^ 1) * STAGE);
+        if (F32OUT && !GELU)
+            store_tile_f32_lds<G, BIAS>(acc, (float *)C, bseg, free_stage, row0, row_end, n0, N, wave, lane, wn, wm,
+                                        r32, khalf);
+        else if (!F32OUT)
+            store_tile_bf16_lds<G, GELU, BIAS>(acc, (uint16_t *)C, bseg, free_stage, row0, row_end, n0, N, wave,
+                                               lane, wn, wm, r32, khalf);
+        else
+            store_tile<G, NBV, GELU, BIAS, F32OUT>(acc, C, bseg, row0, row_end, n0, N, wn, wm, r32, khalf);
+        lds_barrier();
     }
     return b;
 }
@@ -1457,10 +1578,11 @@ template <bool GELU, bool BIAS, bool F32OUT, class G = LargeGrid>
 moe_status_t run_large(const void *a, const int32_t *seg, int S, int64_t max_rows, int N, int K, int Ka,
                        const void *w, const void *bias, void *out, float *part_ws, hipStream_t stream)
 {
-    // the epilogue writes 4 features per lane; rows of the output must not split such a group
-    if (N % 4 != 0 || K % kLargeBK != 0 || K / kLargeBK < 2 || Ka % kLargeBK != 0)
-        return fail(MOE_ERR_UNSUPPORTED, "grouped_gemm_256: needs N %% 4 == 0, K %% 64 == 0, K >= 128 (N=%d K=%d)",
-                    N, K);
+    // the epilogue stores 16 bytes per lane (4 fp32 or 8 bf16 features); rows
+    // of the output must not split such a group
+    if (N % (F32OUT ? 4 : 8) != 0 || K % kLargeBK != 0 || K / kLargeBK < 2 || Ka % kLargeBK != 0)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "grouped_gemm_256: needs N %% %d == 0, K %% 64 == 0, K >= 128 (N=%d K=%d)", F32OUT ? 4 : 8, N, K);
     const int grid = large_grid(max_rows, S, N, part_ws != nullptr);
     grouped_gemm_256<kLargeBK, G, GELU, BIAS, F32OUT><<<(unsigned)grid, 64 * G::NW, 0, stream>>>(
         (const uint16_t *)a, seg, S, max_rows, (const uint16_t *)w, (const uint16_t *)bias, out, N, K, Ka, part_ws);
