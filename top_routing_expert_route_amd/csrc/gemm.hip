@@ -508,28 +508,6 @@ __device__ __forceinline__ void store_tile_bf16_lds(const f32x16 (&acc)[G::FA][G
     }
 }
 
-template <class G, int NBV, bool GELU, bool BIAS, bool F32OUT>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[G::FA][G::FB], void *C,
-                                           const uint16_t *__restrict__ bseg, int64_t row0, int64_t row_end, int n0,
-                                           int N, int wn, int wm, int r32, int khalf)
-{
-    const TileOut rt = tile_out<F32OUT>(C, row0, row_end, N);
-#pragma unroll
-    for (int b = 0; b < G::FB; ++b) {
-        const int64_t row = row0 + wm * G::WTM + b * 32 + r32;
-        const bool row_ok = row < row_end;
-#pragma unroll
-        for (int a = 0; a < G::FA; ++a) {
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * G::WTN + a * 32 + 8 * g + 4 * khalf;
-                store4<GELU, BIAS, F32OUT>(rt, bseg, row, row_ok, n, N, acc[a][b][4 * g + 0], acc[a][b][4 * g + 1],
-                                           acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]);
-            }
-        }
-    }
-}
-
 // Split of the tile list over a persistent grid of G blocks.  F whole tiles
 // run in full rounds (each block gets the same number); when the rest
 // (`rem` tiles, at most half a round) would leave CUs idle, each of them is
@@ -962,14 +940,14 @@ __device__ __forceinline__ int tile(uint16_t *smem, int b, const CopyGeo &cg, co
         // the stage other than b (the next item's first K step) is free after
         // the loop's last barrier
         char *free_stage = reinterpret_cast<char *>(smem + (b ^ 1) * STAGE);
-        if (F32OUT && !GELU)
+        if constexpr (F32OUT) {
+            static_assert(!GELU, "fp32 outputs are pre-activation");
             store_tile_f32_lds<G, BIAS>(acc, (float *)C, bseg, free_stage, row0, row_end, n0, N, wave, lane, wn, wm,
                                         r32, khalf);
-        else if (!F32OUT)
+        } else {
             store_tile_bf16_lds<G, GELU, BIAS>(acc, (uint16_t *)C, bseg, free_stage, row0, row_end, n0, N, wave,
                                                lane, wn, wm, r32, khalf);
-        else
-            store_tile<G, NBV, GELU, BIAS, F32OUT>(acc, C, bseg, row0, row_end, n0, N, wn, wm, r32, khalf);
+        }
         lds_barrier();
     }
     return b;
