@@ -521,27 +521,35 @@ __global__ __launch_bounds__(256) void route_reduce_partials(const float *__rest
 }
 
 // One block of 1024 threads; G threads per expert sum the chunk sums in a
-// fixed strided order, then the G partial sums are added in order.
-__global__ __launch_bounds__(1024) void route_finalize(const double *__restrict__ fin_p,
-                                                       const long long *__restrict__ fin_c, int nrows, int64_t T,
-                                                       int E, float alpha, int32_t *__restrict__ expert_count,
-                                                       float *__restrict__ f, float *__restrict__ P,
-                                                       float *__restrict__ l_aux)
+// fixed strided order, then the G partial sums are added in order.  DIRECT:
+// the rows are the per-block partials themselves (few blocks: one launch
+// instead of two).
+__host__ __device__ constexpr int finalize_threads_per_expert(int E)
+{
+    int G = 1;
+    while (G * 2 * E <= 1024)
+        G *= 2;
+    return G;
+}
+
+template <bool DIRECT, class TP, class TC>
+__global__ __launch_bounds__(1024) void route_finalize(const TP *__restrict__ fin_p, const TC *__restrict__ fin_c,
+                                                       int nrows, int64_t T, int E, float alpha,
+                                                       int32_t *__restrict__ expert_count, float *__restrict__ f,
+                                                       float *__restrict__ P, float *__restrict__ l_aux)
 {
     __shared__ double rp[1024];
     __shared__ long long rc[1024];
     __shared__ double terms[1024];
-    int G = 1;
-    while (G * 2 * E <= 1024)
-        G *= 2;
+    const int G = finalize_threads_per_expert(E);
     const int tid = threadIdx.x;
     const int e = tid / G, g = tid % G;
     double ps = 0.0;
     long long cs = 0;
     if (e < E) {
         for (int b = g; b < nrows; b += G) {
-            ps += fin_p[(int64_t)b * E + e];
-            cs += fin_c[(int64_t)b * E + e];
+            ps += (double)fin_p[(int64_t)b * E + e];
+            cs += (long long)fin_c[(int64_t)b * E + e];
         }
     }
     rp[tid] = ps;
@@ -678,14 +686,17 @@ moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, 
                 return s;
         }
     }
-    const int nfin = T > 0 ? fin_chunks(nblk) : 0;
-    if (nfin > 0) {
-        route_reduce_partials<<<(unsigned)nfin, 256, 0, stream>>>(part_p, part_c, nblk, E, fin_p, fin_c);
-        if (moe_status_t s = check_launch("route_reduce_partials"))
-            return s;
+    const int rows = T > 0 ? nblk : 0;
+    if (rows <= 32 * finalize_threads_per_expert(E)) {
+        // at most 32 partial rows per thread: sum them directly
+        route_finalize<true><<<1, 1024, 0, stream>>>(part_p, part_c, rows, T, E, alpha, expert_count, f, P, l_aux);
+        return check_launch("route_finalize");
     }
-    route_finalize<<<1, 1024, 0, stream>>>(fin_p, fin_c, nfin, T, E, alpha, expert_count, f, P,
-                                           l_aux);
+    const int nfin = fin_chunks(nblk);
+    route_reduce_partials<<<(unsigned)nfin, 256, 0, stream>>>(part_p, part_c, nblk, E, fin_p, fin_c);
+    if (moe_status_t s = check_launch("route_reduce_partials"))
+        return s;
+    route_finalize<false><<<1, 1024, 0, stream>>>(fin_p, fin_c, nfin, T, E, alpha, expert_count, f, P, l_aux);
     return check_launch("route_finalize");
 }
 
