@@ -609,7 +609,9 @@ moe_status_t ffn_backward(const moe_problem_t *p, const void *x, const void *dy,
     if (!s && !a.u_saved) // u = W1 x + b1 (fp32)
         s = launch_grouped_gemm_f32out(a.a_rows, a.seg, a.S, a.rows, F, d, dt, a.w1, a.b1, b.u, b.gemm_ws,
                                        b.gemm_ws_bytes, st);
-    if (!s && !(on_rows && a.dy_rows && !a.db2)) // dY rows (row-major for dh', transposed for dW2) and db2
+    // dY rows (row-major for dh'; transposed for dW2 unless on rows) and db2;
+    // nothing to do for given dY rows on rows without db2
+    if (!s && !(on_rows && a.dy_rows && !a.db2))
         s = launch_gather_t(dy, d, a.row_src, p->k, a.wgt, a.seg, a.S, a.rows, b.kcol, b.Kp, dt,
                             on_rows ? nullptr : b.dyT, a.dy_rows ? nullptr : b.dyp, a.db2 ? b.colpart : nullptr, st);
     if (!s)
