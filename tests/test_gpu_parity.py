@@ -2,8 +2,12 @@
 through the C ABI, on seeded workloads shaped like the pages' layers.
 
 Small cases span several tiles and ragged tails and are compared on every
-element; the full-size workloads (in the launch configuration the benchmark
-times) compare all integers on every token and Y on a seeded token sample.
+element.  The full-size workloads run in the launch configuration the
+benchmark times; they compare every integer output on every token, and Y on
+every token of the Mixtral-shaped and capacity-drop layers, and on a seeded
+sample of at least 512 tokens of the fine-grained and DeepSeek-shaped layers
+that also holds every near-tie token and one token of every 256-row tile of
+every expert segment (and of the shared expert, which covers all tokens).
 """
 import numpy as np
 import pytest
@@ -39,8 +43,34 @@ SMALL = {
 }
 
 FULL = {w.name: w for w in wl.WORKLOADS[1:]}
-FULL_SAMPLE = {"mixtral8x7b-layer": 192, "capacity-drop-zipf": 384, "fine-grained-e128-k8": 256,
-               "deepseekv3-share-32of256": 128}
+# Y on every token (None) or on a seeded sample of this many tokens, plus
+# every near tie and one token per 256-row tile (see _sample_tokens)
+FULL_SAMPLE = {"mixtral8x7b-layer": None, "capacity-drop-zipf": None, "fine-grained-e128-k8": 768,
+               "deepseekv3-share-32of256": 640}
+TILE = 256  # row tile edge of the grouped GEMM
+
+
+def _sample_tokens(w, n, scores, seg_offsets, row_src, seed=17):
+    """At least n tokens: a seeded sample, every near-tie token, and for every
+    256-row tile of every local segment the token of one (seeded) row of it,
+    plus each segment's first and last row; with a shared expert (one segment
+    of all T tokens in order) one token of every 256-token tile as well."""
+    b, o = near_ties(scores, w.k)
+    must = [np.flatnonzero(b | o)]
+    g = np.random.default_rng([seed, w.T])
+    rows = []
+    for s in range(len(seg_offsets) - 1):
+        lo, hi = int(seg_offsets[s]), int(seg_offsets[s + 1])
+        if hi <= lo:
+            continue
+        rows += [lo, hi - 1]
+        for r0 in range(lo, hi, TILE):
+            rows.append(int(g.integers(r0, min(r0 + TILE, hi))))
+    if rows:
+        must.append(np.asarray(row_src)[np.asarray(rows)] // w.k)
+    if w.shared_expert:
+        must.append(np.array([int(g.integers(t0, min(t0 + TILE, w.T))) for t0 in range(0, w.T, TILE)]))
+    return wl.token_sample(w.T, n, must_include=np.concatenate(must).astype(np.int64))
 
 _cache = {}
 
@@ -189,15 +219,14 @@ def _check_forward(w, inp, t, tokens=None):
     np.testing.assert_array_equal(outs["row_src"].cpu().numpy()[:rows], ref_dp.row_src)
     assert int(outs["n_dropped"].item()) == ref_dp.n_dropped
     if tokens is not None:
-        b, o = near_ties(ref_route.scores, w.k)
-        ties = np.flatnonzero(b | o)[:32]
-        tokens = wl.token_sample(w.T, tokens, must_include=ties)
+        tokens = _sample_tokens(w, tokens, ref_route.scores, ref_dp.seg_offsets, ref_dp.row_src)
     ref = oracle.forward(inp, tokens=tokens, topk_idx=gidx)
     yh = _host(y)
     yg = yh if tokens is None else yh[tokens]
     err = rel_err(yg, ref.y)
     assert err <= _ytol(w), err
-    return layer, y, outs, nt, err
+    ntok = w.T if tokens is None else len(tokens)
+    return layer, y, outs, nt, err, ntok
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -207,12 +236,16 @@ def test_forward_small(name):
     _check_forward(w, inp, t)
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", list(FULL))
 def test_forward_full_size(name):
+    import time
     w = FULL[name]
+    t0 = time.perf_counter()
     inp, t = _inputs(w)
-    layer, y, outs, nt, err = _check_forward(w, inp, t, tokens=FULL_SAMPLE[name])
-    print("%s: near ties boundary %d order %d, Y rel err %.3e" % (name, nt["boundary"], nt["order"], err))
+    layer, y, outs, nt, err, ntok = _check_forward(w, inp, t, tokens=FULL_SAMPLE[name])
+    print("%s: near ties boundary %d order %d, Y rel err %.3e on %d of %d tokens (%.1f s)"
+          % (name, nt["boundary"], nt["order"], err, ntok, w.T, time.perf_counter() - t0), flush=True)
     # bitwise reproducible
     y2 = layer.forward(t["x"])
     torch.cuda.synchronize()
@@ -289,7 +322,7 @@ def test_few_tokens(T):
 def test_single_expert_is_dense_ffn():
     w = wl.scaled(wl.get(1), T=130, d=128, E=1, k=1, ffn=256, expert_bias="gauss")
     inp, t = _inputs(w)
-    layer, y, outs, nt, err = _check_forward(w, inp, t)
+    layer, y, outs, nt, err, _ = _check_forward(w, inp, t)
     assert (outs["topk_w"] == 1.0).all()
 
 
@@ -303,7 +336,7 @@ def test_capacity_zero_drops_everything():
     # C = floor(64 * 0.05 / 8) = 0
     w = wl.scaled(wl.get(1), T=64, d=64, ffn=128, capacity_factor=0.05)
     inp, t = _inputs(w)
-    layer, y, outs, nt, err = _check_forward(w, inp, t)
+    layer, y, outs, nt, err, _ = _check_forward(w, inp, t)
     assert (outs["slot_row"] == -1).all() and outs["n_dropped"].item() == 64 * 2
     assert (y.float() == 0).all()
 

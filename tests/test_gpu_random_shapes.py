@@ -79,7 +79,8 @@ def test_random_shape(name):
 
 def _draw_large(n=8, seed=1001):
     """Larger layers (multi-round GEMMs, split-K tails, the large dispatch
-    planner, many route blocks), checked on a token sample."""
+    planner, many route blocks), checked on a token sample of at least 512
+    tokens holding every near tie and one token of every 256-row tile."""
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
@@ -109,9 +110,10 @@ def _draw_large(n=8, seed=1001):
 LARGE = {w.name: w for w in _draw_large()}
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", list(LARGE))
 def test_random_large_shape(name):
     w = LARGE[name]
     print("random large case", w, flush=True)
     inp, t = _inputs(w, seed=3)
-    _check_forward(w, inp, t, tokens=64)
+    _check_forward(w, inp, t, tokens=512)
