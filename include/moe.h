@@ -28,16 +28,19 @@
  *    the actual counts on the device.  A call enqueues kernel launches only
  *    (no memset or copy nodes), so it may be captured into a HIP graph and
  *    replayed, with the same buffers (moe_forward_overlap also records and
- *    waits on events between its two streams).
+ *    waits on the caller's events between its two streams).
  *  - Errors: arguments are validated before anything is enqueued; an invalid
  *    call returns a non-zero status, enqueues nothing and leaves every output
  *    untouched.  MOE_ERR_HIP reports a launch failure (moe_last_error() has the
  *    HIP message); faults inside a kernel surface at the caller's next
  *    synchronisation, as with any asynchronous HIP work.
  *  - Workspaces (`ws`, `ws_bytes`) are caller-provided device scratch of at
- *    least the size the matching *_workspace_size function returns; their
- *    contents need no initialisation and are undefined afterwards.  Calls that
- *    share one workspace must be ordered on one stream.
+ *    least the size the matching *_workspace_size function returns.  Their
+ *    first 256 bytes hold arrival counters (the single-launch router's): they
+ *    must be zero before the first call on a workspace (allocate it zeroed or
+ *    clear it once), and every call leaves them zero when its work completes.
+ *    The rest needs no initialisation and is undefined afterwards.  Calls
+ *    that share one workspace must be ordered on one stream.
  *  - dtype: MOE_BF16 (bfloat16) or MOE_F32 for activations, expert weights and
  *    expert biases.  The router weight and bias, routing weights and load
  *    statistics are always float32.  Integer outputs are int32.
@@ -102,7 +105,9 @@ int64_t moe_max_rows(int64_t T, int E, int k, float capacity_factor, int num_loc
  *   f[e] = expert_count[e] / T,  P[e] = (1/T) sum_t p[t,e]
  *   l_aux[0] = alpha * sum_e f[e] * P[e]     (alpha: 0.01 is the usual value)
  * The reductions over tokens run in a fixed order: results are bitwise
- * reproducible run to run.
+ * reproducible run to run.  With bf16 activations and E <= 64 the whole call
+ * is one kernel launch: the last block to finish sums the per-block partial
+ * statistics (in a fixed order), using the workspace's arrival counter.
  *
  * x [T,d] (dtype), w_router [E,d] f32, b_router [E] f32 or NULL (zero bias),
  * sel_bias [E] f32 or NULL (plain top-k).
@@ -110,8 +115,8 @@ int64_t moe_max_rows(int64_t T, int E, int k, float capacity_factor, int num_loc
  * f [E], P [E], l_aux [1] may each be NULL (not written).
  * ws: moe_route_workspace_size(T, d, E) bytes.
  * Errors: INVALID_ARG for T < 0, d < 1, E < 1, k < 1, k > E, NULL x, w_router,
- * topk_idx or topk_w; UNSUPPORTED for E > 1024, k > 32, d % 8 != 0;
- * WORKSPACE for a small ws.
+ * topk_idx or topk_w; UNSUPPORTED for E > 1024, k > 32, d % 8 != 0,
+ * d > 2^21; WORKSPACE for a small ws.
  * ------------------------------------------------------------------------ */
 size_t moe_route_workspace_size(int64_t T, int d, int E);
 moe_status_t moe_route(const void *x, moe_dtype_t dtype, const float *w_router,
@@ -282,21 +287,30 @@ moe_status_t moe_forward(const moe_problem_t *p, const moe_weights_t *w, const v
  * work does not depend on the routing, so it can run while the routed path
  * routes and dispatches).
  *
- * side: a second stream of the same device (default priority).  The shared
- * expert's two GEMMs are enqueued on it, ordered after the work already on
- * `stream` at the call; the combine on `stream` waits for them.  Everything
- * else is enqueued on `stream` exactly as in moe_forward, and the results
- * are bitwise identical to moe_forward's.  Without a shared expert (or with
- * side == NULL or side == stream) this is moe_forward.
+ * side: a second stream of the same device (default priority); fork, join:
+ * two caller-owned events (hipEventDisableTiming is enough), reused by every
+ * call and recorded by it, so the call creates and frees nothing.  `fork` is
+ * recorded on `stream` and waited for by `side`; the shared expert's two
+ * GEMMs are enqueued on `side`; `join` is recorded on `side` and waited for
+ * by `stream` before the combine.  Everything else is enqueued on `stream`
+ * exactly as in moe_forward, and the results are bitwise identical to
+ * moe_forward's.  Without a shared expert (or with side == NULL or side ==
+ * stream) this is moe_forward and the events are not used.
+ * If an error stops the call after work was put on `side`, `side` is still
+ * joined back into `stream` before the call returns, so nothing the call
+ * enqueued runs outside `stream`'s order.  Events and streams may be captured
+ * into a HIP graph together with the call (fork/join edges).
  * ws: moe_forward_overlap_workspace_size(p) bytes (the shared expert gets its
- * own intermediate and split-K buffers).  The call creates two HIP events and
- * releases them before returning (they are freed once the GPU passes them).
- * Errors: as moe_forward, plus MOE_ERR_HIP if an event cannot be created.
+ * own intermediate and split-K buffers).
+ * Errors: as moe_forward, plus INVALID_ARG for a missing event when the
+ * shared expert goes to `side`, and MOE_ERR_HIP if an event record or wait
+ * fails.
  * ------------------------------------------------------------------------ */
+typedef struct ihipEvent_t *hipEvent_t;
 size_t moe_forward_overlap_workspace_size(const moe_problem_t *p);
 moe_status_t moe_forward_overlap(const moe_problem_t *p, const moe_weights_t *w, const void *x, void *y,
                                  const moe_outputs_t *out, void *ws, size_t ws_bytes, hipStream_t stream,
-                                 hipStream_t side);
+                                 hipStream_t side, hipEvent_t fork, hipEvent_t join);
 
 /* ------------------------------------------------------------------------ *
  * moe_backward - gradients of a scalar loss L through the layer of moe_forward.

@@ -77,3 +77,41 @@ def test_forward_and_backward_graph_replays(name):
             assert torch.equal(_bits(outs[k]), _bits(o_ref[k])), k
         for k in g_ref:
             assert torch.equal(_bits(grads[k]), _bits(g_ref[k])), k
+
+
+def test_overlap_forward_graph_replays():
+    """moe_forward_overlap captured with its side stream and fork/join events:
+    every replay reproduces the eager moe_forward bits."""
+    w = CASES["dsv3-small"]
+    inp = wl.make_layer(w, seed=6)
+    t = wl.device_layer(inp, DEV)
+    layer = api.Layer(w.T, w.d, w.E, w.k, w.ffn, torch.bfloat16, w.capacity_factor, w.expert_begin,
+                      w.num_local_experts, w.alpha, t["w_router"], t["b_router"], t["w1"], t["b1"], t["w2"],
+                      t["b2"], t["ws1"], t["bs1"], t["ws2"], t["bs2"], device=DEV, sel_bias=t["sel_bias"])
+    outs = layer.alloc_outputs()
+    x = t["x"]
+    y_ref = layer.forward(x).clone()
+    o_ref = {k: v.clone() for k, v in outs.items()}
+    torch.cuda.synchronize()
+    y = torch.empty_like(y_ref)
+    cap = torch.cuda.Stream()
+    side = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        layer.forward(x, y, side_stream=side)  # warm-up on the capture stream (events created here)
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(y), _bits(y_ref))
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        layer.forward(x, y, side_stream=side)
+    for _ in range(3):
+        y.fill_(3.0)
+        outs["topk_idx"].fill_(-1)
+        outs["slot_row"].fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(y), _bits(y_ref))
+        for k in ("topk_idx", "topk_w", "seg_offsets", "slot_row", "f", "P", "l_aux"):
+            assert torch.equal(_bits(outs[k]), _bits(o_ref[k])), k

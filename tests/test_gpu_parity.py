@@ -431,6 +431,22 @@ def test_route_bitwise_reproducible_and_stats_fixed_order():
         assert torch.equal(r1[k], r2[k]), k
 
 
+def test_route_leaves_workspace_counters_zero():
+    """The single-launch router's arrival counter (the workspace's first 256
+    bytes) is zero again after every call, whatever the grid size, so the
+    workspace is reusable as is (and in graph replays)."""
+    for name in ("mixtral-small", "fine-small", "drop-small", "selbias-e32"):
+        w = SMALL[name]
+        inp, t = _inputs(w)
+        for _ in range(2):
+            r = api.moe_route(t["x"], t["w_router"], t["b_router"], w.k, w.alpha, sel_bias=t["sel_bias"])
+            torch.cuda.synchronize()
+            ws = api.workspace(t["x"].device, 0)
+            assert int(ws[:256].count_nonzero().item()) == 0, name
+            ref_route = oracle.route(inp.x, inp.w_router, inp.b_router, w.k, sel_bias=inp.sel_bias)
+            _check_route(w, inp, r, ref_route)
+
+
 def test_route_sel_bias_full_size():
     """The DeepSeek-shaped router (T=32768, d=7168, E=256, top-8, the E > 64
     path) with a selection-only bias, against the oracle on every token."""

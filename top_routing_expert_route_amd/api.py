@@ -97,7 +97,7 @@ def lib():
     L.moe_forward_overlap_workspace_size.argtypes = [ctypes.POINTER(Problem)]
     L.moe_forward_overlap_workspace_size.restype = SZ
     L.moe_forward_overlap.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Weights), P, P,
-                                      ctypes.POINTER(Outputs), P, SZ, P, P]
+                                      ctypes.POINTER(Outputs), P, SZ, P, P, P, P]
     L.moe_forward_overlap.restype = I
     L.moe_backward_workspace_size.argtypes = [ctypes.POINTER(Problem)]
     L.moe_backward_workspace_size.restype = SZ
@@ -142,7 +142,24 @@ def _stream(dev: torch.device):
 
 
 def _ws(nbytes: int, dev) -> torch.Tensor:
-    return torch.empty(max(1, int(nbytes)), dtype=torch.uint8, device=dev)
+    """A workspace: zero-filled once at allocation (its leading counters must
+    start at zero; every call leaves them zero)."""
+    return torch.zeros(max(1, int(nbytes)), dtype=torch.uint8, device=dev)
+
+
+_ws_cache = {}
+
+
+def workspace(device, nbytes: int) -> torch.Tensor:
+    """A zero-initialised workspace of at least nbytes, cached per device and
+    reused by the step functions below (their calls are ordered on the
+    current stream; every call leaves the leading counters zero)."""
+    dev = torch.device(device)
+    buf = _ws_cache.get(dev)
+    if buf is None or buf.numel() < nbytes:
+        buf = _ws(nbytes, dev)
+        _ws_cache[dev] = buf
+    return buf
 
 
 def max_rows(T: int, E: int, k: int, capacity_factor: float = 0.0, num_local_experts: int = 0) -> int:
@@ -163,7 +180,7 @@ def moe_route(x: torch.Tensor, w_router: torch.Tensor, b_router: Optional[torch.
                P=torch.empty(E, dtype=torch.float32, device=dev),
                l_aux=torch.empty(1, dtype=torch.float32, device=dev))
     nb = lib().moe_route_workspace_size(T, d, E)
-    ws = _ws(nb, dev)
+    ws = workspace(dev, nb)
     check(lib().moe_route(_p(x), _dt(x), _p(w_router), _p(b_router), _p(sel_bias), T, d, E, k, alpha,
                           _p(out["topk_idx"]), _p(out["topk_w"]), _p(out["expert_count"]), _p(out["f"]),
                           _p(out["P"]), _p(out["l_aux"]), _p(ws), nb, _stream(dev)))
@@ -187,7 +204,7 @@ def moe_dispatch(x: Optional[torch.Tensor], topk_idx: torch.Tensor, E: int, capa
                x_perm=(torch.empty((max(1, mr), d), dtype=x.dtype, device=dev) if (with_x_perm and x is not None)
                        else None))
     nb = lib().moe_dispatch_workspace_size(T, k, E_loc)
-    ws = _ws(nb, dev)
+    ws = workspace(dev, nb)
     check(lib().moe_dispatch(_p(x), dt, _p(topk_idx), T, d, E, k, capacity_factor, expert_begin,
                              num_local_experts, _p(out["seg_offsets"]), _p(out["kept_count"]), _p(out["slot_row"]),
                              _p(out["row_src"]), _p(out["x_perm"]), mr, _p(out["n_dropped"]), _p(ws), nb,
@@ -302,9 +319,17 @@ class Layer:
         if y is None:
             y = torch.empty((self.problem.T, self.problem.d), dtype=x.dtype, device=x.device)
         if overlap:
+            if getattr(self, "_events", None) is None:
+                # caller-owned fork/join events, created once per layer (torch
+                # creates an event's handle at its first record)
+                self._events = (torch.cuda.Event(), torch.cuda.Event())
+                for e in self._events:
+                    e.record(torch.cuda.current_stream(self.device))
+            fork, join = self._events
             check(lib().moe_forward_overlap(ctypes.byref(self.problem), ctypes.byref(self.weights), _p(x), _p(y),
                                             ctypes.byref(self.out_struct), _p(self.ws), self.ws.numel(),
-                                            _stream(x.device), ctypes.c_void_p(side_stream.cuda_stream)))
+                                            _stream(x.device), ctypes.c_void_p(side_stream.cuda_stream),
+                                            ctypes.c_void_p(fork.cuda_event), ctypes.c_void_p(join.cuda_event)))
         else:
             check(lib().moe_forward(ctypes.byref(self.problem), ctypes.byref(self.weights), _p(x), _p(y),
                                     ctypes.byref(self.out_struct), _p(self.ws), self.ws.numel(),

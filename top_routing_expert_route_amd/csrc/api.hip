@@ -64,8 +64,9 @@ moe_status_t check_route_args(const void *x, moe_dtype_t dt, const float *w_rout
         return fail(MOE_ERR_INVALID_ARG, "route: a required pointer is NULL");
     if (!aligned16(x) || !aligned16(w_router))
         return fail(MOE_ERR_INVALID_ARG, "route: x and w_router must be 16-byte aligned");
-    if (E > 1024 || k > 32 || d % 8 != 0)
-        return fail(MOE_ERR_UNSUPPORTED, "route: needs E <= 1024, k <= 32, d %% 8 == 0 (E=%d k=%d d=%d)", E, k, d);
+    if (E > 1024 || k > 32 || d % 8 != 0 || d > kMaxK)
+        return fail(MOE_ERR_UNSUPPORTED, "route: needs E <= 1024, k <= 32, d %% 8 == 0, d <= %d (E=%d k=%d d=%d)",
+                    kMaxK, E, k, d);
     if (T > (int64_t)INT32_MAX / (k > 0 ? k : 1))
         return fail(MOE_ERR_UNSUPPORTED, "route: T*k must fit int32");
     return MOE_OK;
@@ -164,7 +165,7 @@ ForwardWs carve_forward(const moe_problem_t *p, const moe_outputs_t *out, void *
     const int64_t max_rows = moe_max_rows(p->T, p->E, p->k, p->capacity_factor, p->num_local_experts);
     const size_t es = elem_size(p->dtype);
     const int64_t Tk = p->T * p->k;
-    Carver cv{(char *)base, 0};
+    Carver cv{(char *)base, kCtrlBytes}; // [0, kCtrlBytes): the router's arrival counter
     ForwardWs w;
     w.topk_idx = out->topk_idx ? out->topk_idx : cv.take<int32_t>((size_t)Tk);
     w.topk_w = out->topk_w ? out->topk_w : cv.take<float>((size_t)Tk);
@@ -172,7 +173,7 @@ ForwardWs carve_forward(const moe_problem_t *p, const moe_outputs_t *out, void *
     w.f = out->f;
     w.P = out->P;
     w.l_aux = out->l_aux;
-    w.route_ws = cv.take<char>(route_ws_bytes(p->T, p->d, p->E));
+    w.route_ws = cv.take<char>(route_ws_bytes(p->T, p->d, p->E, p->dtype));
     w.seg_offsets = out->seg_offsets ? out->seg_offsets : cv.take<int32_t>((size_t)E_loc + 1);
     w.kept_count = out->kept_count ? out->kept_count : cv.take<int32_t>((size_t)E_loc);
     w.slot_row = out->slot_row ? out->slot_row : cv.take<int32_t>((size_t)Tk);
@@ -225,11 +226,20 @@ int64_t moe_max_rows(int64_t T, int E, int k, float capacity_factor, int num_loc
     return rows;
 }
 
+// Route workspaces: the arrival counter in the control bytes, then the
+// partial rows (and, off the single-launch path, logits and chunk sums).
+static size_t route_ws_total(int64_t T, int d, int E, moe_dtype_t dt)
+{
+    return T > 0 ? kCtrlBytes + route_ws_bytes(T, d, E, dt) : 0;
+}
+
 size_t moe_route_workspace_size(int64_t T, int d, int E)
 {
     if (T < 0 || E < 1 || d < 1)
         return 0;
-    return route_ws_bytes(T, d, E);
+    // the fp32-activation layout is the larger of the two
+    const size_t a = route_ws_total(T, d, E, MOE_F32), b = route_ws_total(T, d, E, MOE_BF16);
+    return a > b ? a : b;
 }
 
 moe_status_t moe_route(const void *x, moe_dtype_t dtype, const float *w_router, const float *b_router,
@@ -240,17 +250,17 @@ moe_status_t moe_route(const void *x, moe_dtype_t dtype, const float *w_router, 
     clear_error();
     if (moe_status_t s = check_route_args(x, dtype, w_router, T, d, E, k, topk_idx, topk_w))
         return s;
-    if (moe_status_t s = check_ws(ws, ws_bytes, route_ws_bytes(T, d, E), "route"))
+    if (moe_status_t s = check_ws(ws, ws_bytes, route_ws_total(T, d, E, dtype), "route"))
         return s;
     return launch_route(x, dtype, w_router, b_router, sel_bias, T, d, E, k, alpha, topk_idx, topk_w, expert_count,
-                        f, P, l_aux, nullptr, ws, stream);
+                        f, P, l_aux, nullptr, T > 0 ? (char *)ws + kCtrlBytes : nullptr, (unsigned *)ws, stream);
 }
 
 size_t moe_dispatch_workspace_size(int64_t T, int k, int num_local_experts)
 {
     if (T < 0 || k < 1 || num_local_experts < 1)
         return 0;
-    return dispatch_ws_bytes(T, k, num_local_experts);
+    return kCtrlBytes + dispatch_ws_bytes(T, k, num_local_experts);
 }
 
 moe_status_t moe_dispatch(const void *x, moe_dtype_t dtype, const int32_t *topk_idx, int64_t T, int d, int E, int k,
@@ -264,13 +274,25 @@ moe_status_t moe_dispatch(const void *x, moe_dtype_t dtype, const int32_t *topk_
                                              max_rows))
         return s;
     const int E_loc = local_count(E, num_local_experts);
-    if (moe_status_t s = check_ws(ws, ws_bytes, dispatch_ws_bytes(T, k, E_loc), "dispatch"))
+    if (moe_status_t s = check_ws(ws, ws_bytes, kCtrlBytes + dispatch_ws_bytes(T, k, E_loc), "dispatch"))
         return s;
     return launch_dispatch(x, dtype, topk_idx, T, d, E, k, capacity_factor, expert_begin, E_loc, seg_offsets,
-                           kept_count, slot_row, row_src, x_perm, max_rows, n_dropped, ws, stream);
+                           kept_count, slot_row, row_src, x_perm, max_rows, n_dropped, (char *)ws + kCtrlBytes,
+                           stream);
 }
 
-size_t moe_grouped_gemm_workspace_size(void) { return gemm_ws_bytes(); }
+size_t moe_grouped_gemm_workspace_size(void) { return kCtrlBytes + gemm_ws_bytes(); }
+
+// The split-K partials of an optional GEMM workspace (after its control bytes).
+static void *gemm_part(void *ws, size_t ws_bytes, size_t *part_bytes)
+{
+    if (!ws || ws_bytes < kCtrlBytes + gemm_ws_bytes()) {
+        *part_bytes = 0;
+        return nullptr;
+    }
+    *part_bytes = ws_bytes - kCtrlBytes;
+    return (char *)ws + kCtrlBytes;
+}
 
 moe_status_t moe_grouped_gemm(const void *a, const int32_t *seg_offsets, int num_segments, int64_t max_rows, int N,
                               int K, moe_dtype_t dtype, const void *w, const void *bias, int activation, void *out,
@@ -282,8 +304,10 @@ moe_status_t moe_grouped_gemm(const void *a, const int32_t *seg_offsets, int num
         return s;
     if (!aligned16(ws))
         return fail(MOE_ERR_INVALID_ARG, "grouped_gemm: ws must be 16-byte aligned");
-    return launch_grouped_gemm(a, seg_offsets, num_segments, max_rows, N, K, dtype, w, bias, activation, out, ws,
-                               ws_bytes, stream);
+    size_t pb = 0;
+    void *part = gemm_part(ws, ws_bytes, &pb);
+    return launch_grouped_gemm(a, seg_offsets, num_segments, max_rows, N, K, dtype, w, bias, activation, out, part, pb,
+                               stream);
 }
 
 moe_status_t moe_expert_ffn(const void *x_perm, const int32_t *seg_offsets, int num_segments, int64_t max_rows,
@@ -299,10 +323,12 @@ moe_status_t moe_expert_ffn(const void *x_perm, const int32_t *seg_offsets, int 
         return s;
     if (!aligned16(ws))
         return fail(MOE_ERR_INVALID_ARG, "expert_ffn: ws must be 16-byte aligned");
+    size_t pb = 0;
+    void *part = gemm_part(ws, ws_bytes, &pb);
     if (moe_status_t s = launch_grouped_gemm(x_perm, seg_offsets, num_segments, max_rows, ffn, d, dtype, w1, b1, 1,
-                                             h, ws, ws_bytes, stream))
+                                             h, part, pb, stream))
         return s;
-    return launch_grouped_gemm(h, seg_offsets, num_segments, max_rows, d, ffn, dtype, w2, b2, 0, y_perm, ws, ws_bytes,
+    return launch_grouped_gemm(h, seg_offsets, num_segments, max_rows, d, ffn, dtype, w2, b2, 0, y_perm, part, pb,
                                stream);
 }
 
@@ -331,7 +357,8 @@ namespace {
 // there, and GELU runs as its own pass from them.
 moe_status_t forward_impl(const moe_problem_t *p, const moe_weights_t *w, const void *x, void *y,
                           const moe_outputs_t *out, void *ws, size_t ws_bytes, hipStream_t stream, hipStream_t side,
-                          float *u_save = nullptr, float *u_sh_save = nullptr)
+                          float *u_save = nullptr, float *u_sh_save = nullptr, hipEvent_t ev_fork = nullptr,
+                          hipEvent_t ev_join = nullptr)
 {
     clear_error();
     if (!p || !w)
@@ -364,46 +391,44 @@ moe_status_t forward_impl(const moe_problem_t *p, const moe_weights_t *w, const 
     if (!aligned16(y))
         return fail(MOE_ERR_INVALID_ARG, "forward: y must be 16-byte aligned");
     const bool overlap = side != nullptr && side != stream && p->has_shared && p->T > 0;
+    if (overlap && (!ev_fork || !ev_join))
+        return fail(MOE_ERR_INVALID_ARG, "forward_overlap: the fork and join events are required");
     const ForwardWs need = carve_forward(p, out, nullptr, side != nullptr);
     if (moe_status_t s = check_ws(ws, ws_bytes, need.bytes, "forward"))
         return s;
     const ForwardWs b = carve_forward(p, out, ws, side != nullptr);
 
     // The shared expert needs only x: on the side stream it runs while the
-    // routed path routes, dispatches and runs its own GEMMs.
-    hipEvent_t ev_start = nullptr, ev_done = nullptr;
-    auto release = [&]() {
-        if (ev_start)
-            (void)hipEventDestroy(ev_start);
-        if (ev_done)
-            (void)hipEventDestroy(ev_done);
+    // routed path routes, dispatches and runs its own GEMMs.  Once anything
+    // is on the side stream, every return path joins it back into `stream`,
+    // so that no side work is left running past the call's stream order.
+    bool forked = false;
+    auto join = [&](moe_status_t s) -> moe_status_t {
+        if (!forked)
+            return s;
+        if (hipEventRecord(ev_join, side) != hipSuccess || hipStreamWaitEvent(stream, ev_join, 0) != hipSuccess) {
+            if (!s)
+                s = fail(MOE_ERR_HIP, "forward_overlap: cannot join the side stream");
+        }
+        forked = false;
+        return s;
     };
     if (overlap) {
-        if (hipEventCreateWithFlags(&ev_start, hipEventDisableTiming) != hipSuccess ||
-            hipEventCreateWithFlags(&ev_done, hipEventDisableTiming) != hipSuccess) {
-            release();
-            return fail(MOE_ERR_HIP, "forward: cannot create events for the side stream");
-        }
-        if (hipEventRecord(ev_start, stream) != hipSuccess || hipStreamWaitEvent(side, ev_start, 0) != hipSuccess) {
-            release();
-            return fail(MOE_ERR_HIP, "forward: cannot order the side stream after the main stream");
-        }
+        if (hipEventRecord(ev_fork, stream) != hipSuccess || hipStreamWaitEvent(side, ev_fork, 0) != hipSuccess)
+            return fail(MOE_ERR_HIP, "forward_overlap: cannot order the side stream after the main stream");
+        forked = true;
         moe_status_t s = launch_grouped_gemm(x, nullptr, 1, p->T, p->ffn, p->d, p->dtype, w->ws1, w->bs1, 1,
                                              b.h_sh, b.gemm_ws_sh, b.gemm_ws_bytes, side);
         if (!s)
             s = launch_grouped_gemm(b.h_sh, nullptr, 1, p->T, p->d, p->ffn, p->dtype, w->ws2, w->bs2, 0, b.y_sh,
                                     b.gemm_ws_sh, b.gemm_ws_bytes, side);
-        if (!s && hipEventRecord(ev_done, side) != hipSuccess)
-            s = fail(MOE_ERR_HIP, "forward: cannot record the side stream's completion");
-        if (s) {
-            release();
-            return s;
-        }
+        if (s)
+            return join(s);
     }
     moe_status_t s = launch_route(x, p->dtype, w->w_router, w->b_router, w->sel_bias, p->T, p->d, p->E, p->k,
                                   p->alpha,
                                   b.topk_idx, b.topk_w, b.expert_count, b.f, b.P, b.l_aux, nullptr, b.route_ws,
-                                  stream);
+                                  (unsigned *)ws, stream);
     if (!s)
         s = launch_dispatch(x, p->dtype, b.topk_idx, p->T, p->d, p->E, p->k, p->capacity_factor, p->expert_begin,
                             E_loc, b.seg_offsets, b.kept_count, b.slot_row, b.row_src, b.x_perm, max_rows,
@@ -435,14 +460,13 @@ moe_status_t forward_impl(const moe_problem_t *p, const moe_weights_t *w, const 
                 s = launch_grouped_gemm(b.h, nullptr, 1, p->T, p->d, p->ffn, p->dtype, w->ws2, w->bs2, 0, b.y_sh,
                                         b.gemm_ws, b.gemm_ws_bytes, stream);
         }
-        if (!s && overlap && hipStreamWaitEvent(stream, ev_done, 0) != hipSuccess)
-            s = fail(MOE_ERR_HIP, "forward: cannot order the combine after the side stream");
+        if (!s && overlap)
+            s = join(s); // the combine reads the shared expert's output
         if (!s)
             s = launch_combine(b.y_perm, max_rows, b.slot_row, b.topk_w, b.y_sh, p->T, p->d, p->k, p->dtype, y,
                                stream);
     }
-    release();
-    return s;
+    return join(s);
 }
 
 } // namespace
@@ -479,9 +503,9 @@ extern "C" size_t moe_forward_overlap_workspace_size(const moe_problem_t *p)
 
 extern "C" moe_status_t moe_forward_overlap(const moe_problem_t *p, const moe_weights_t *w, const void *x,
                                             void *y, const moe_outputs_t *out, void *ws, size_t ws_bytes,
-                                            hipStream_t stream, hipStream_t side)
+                                            hipStream_t stream, hipStream_t side, hipEvent_t fork, hipEvent_t join)
 {
-    return forward_impl(p, w, x, y, out, ws, ws_bytes, stream, side ? side : stream);
+    return forward_impl(p, w, x, y, out, ws, ws_bytes, stream, side ? side : stream, nullptr, nullptr, fork, join);
 }
 
 // ------------------------------------------------------------------ backward
@@ -525,7 +549,7 @@ BackwardWs carve_backward(const moe_problem_t *p, const moe_grads_t *g, void *ba
     const size_t es = elem_size(p->dtype);
     const int64_t Tk = p->T * p->k;
     const int64_t kp_r = kseg_cols_bound(max_rows, E_loc), kp_s = p->has_shared ? kseg_cols_bound(p->T, 1) : 0;
-    Carver cv{(char *)base, 0};
+    Carver cv{(char *)base, kCtrlBytes}; // [0, kCtrlBytes): the router's arrival counter
     BackwardWs w;
     w.Kp = kp_r > kp_s ? kp_r : kp_s;
     w.topk_idx = cv.take<int32_t>((size_t)Tk);
@@ -536,7 +560,7 @@ BackwardWs carve_backward(const moe_problem_t *p, const moe_grads_t *g, void *ba
     w.l_aux = cv.take<float>(1);
     w.probs = cv.take<float>((size_t)p->T * p->E);
     w.dl = (g && g->dlogits) ? g->dlogits : cv.take<float>((size_t)p->T * p->E);
-    w.route_ws = cv.take<char>(route_ws_bytes(p->T, p->d, p->E));
+    w.route_ws = cv.take<char>(route_ws_bytes(p->T, p->d, p->E, p->dtype));
     w.seg_offsets = cv.take<int32_t>((size_t)E_loc + 1);
     w.kept_count = cv.take<int32_t>((size_t)E_loc);
     w.slot_row = cv.take<int32_t>((size_t)Tk);
@@ -720,7 +744,7 @@ moe_status_t backward_impl(const moe_problem_t *p, const moe_weights_t *w, const
 
     moe_status_t s = launch_route(x, p->dtype, w->w_router, w->b_router, w->sel_bias, T, d, E, p->k, p->alpha,
                                   b.topk_idx, b.topk_w, b.expert_count, b.f, b.P, b.l_aux, b.probs, b.route_ws,
-                                  stream);
+                                  (unsigned *)ws, stream);
     if (!s)
         s = launch_dispatch(x, p->dtype, b.topk_idx, T, d, E, p->k, p->capacity_factor, p->expert_begin, E_loc,
                             b.seg_offsets, b.kept_count, b.slot_row, b.row_src, b.x_perm, max_rows, nullptr,

@@ -8,7 +8,7 @@
 
 #include "moe.h"
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 namespace moe {
 
@@ -143,13 +143,21 @@ struct Carver {
 // -------------------------------------------------- internal launchers ---
 // These assume validated arguments; the public entry points validate.
 
-size_t route_ws_bytes(int64_t T, int d, int E);
+// Every public workspace starts with kCtrlBytes of counters that must be zero
+// before the first call on it; each call leaves them zero when it completes.
+// The rest of the workspace is carved from kCtrlBytes on.
+constexpr size_t kCtrlBytes = 256;
+
+// Router workspace (after the control bytes) and launcher.  `ticket` is the
+// arrival counter of the single-launch router (zero on entry, zero again
+// when the launch completes); probs [T, E] fp32 softmax output, or NULL.
+size_t route_ws_bytes(int64_t T, int d, int E, moe_dtype_t dt);
 size_t gemm_ws_bytes();
 moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, const float *b_router,
                           const float *sel_bias, int64_t T, int d, int E, int k, float alpha, int32_t *topk_idx,
                           float *topk_w,
                           int32_t *expert_count, float *f, float *P, float *l_aux, float *probs, void *ws,
-                          hipStream_t stream); // probs [T, E] fp32 softmax output, or NULL
+                          unsigned *ticket, hipStream_t stream);
 
 size_t dispatch_ws_bytes(int64_t T, int k, int E_loc);
 int64_t capacity_of(int64_t T, int E, float capacity_factor); // -1: no cap

@@ -22,8 +22,12 @@
 //                    ballots over the bits of the expert id, so the rank is
 //                    stable (token order) without atomics.  Writes slot_row
 //                    and row_src.
-//  dispatch_plan_small  the three steps above in one block of 16 waves when
-//                    T*k <= 32768 and E_loc <= 256 (counts and bases in LDS).
+//  dispatch_fused    the whole dispatch in one launch when (blocks x
+//                    selections) is small: every block counts all selections
+//                    itself (see the kernel).
+//  dispatch_plan_small  count + scan + rank in one block of 16 waves when
+//                    T*k <= 32768 and E_loc <= 256 (counts and bases in LDS),
+//                    for sizes past the single-launch bound.
 //  dispatch_scatter  one wave per token: the token's row of x is read once
 //                    and written to each of its kept rows (16-byte accesses).
 #include "common.hpp"
@@ -33,6 +37,9 @@ namespace moe {
 namespace {
 
 constexpr int kScanCap = 16384; // chunks * local experts kept small for the scan
+// The single-launch dispatch reads all selections in every block: used while
+// blocks x selections stays within this many reads (32 MB of L2 traffic).
+constexpr int64_t kFusedReads = (int64_t)1 << 23;
 
 __device__ __forceinline__ int local_of(int32_t e, int e0, int E_loc)
 {
@@ -286,6 +293,191 @@ __global__ __launch_bounds__(1024) void dispatch_plan_small(const int32_t *__res
     }
 }
 
+// Lanes holding the same local expert id: 64-lane ballots over its bits.
+__device__ __forceinline__ uint64_t match_mask(int l, bool local, int nbits)
+{
+    uint64_t m = __ballot(local);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = local && ((l >> b) & 1);
+        const uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+    }
+    return m;
+}
+
+// Whole dispatch in one launch for small selection counts: each block of 16
+// waves owns kDispTB tokens.  Every block counts all selections per local
+// expert (ballot-matched groups of 64, one LDS add per expert and group) and
+// those before its own tokens, derives capacity, kept counts and segment
+// offsets itself (block 0 writes them), ranks its own selections in token
+// order (count before the block + earlier groups of the block + lanes below
+// in the group: the same rank as the multi-kernel path), writes slot_row and
+// row_src, and then each wave copies its token's row of x to the token's kept
+// rows.  With PREFETCH (no cap and the whole layer local: every selection is
+// kept) the first piece of the row is loaded before the planning, so the
+// row read overlaps it.
+constexpr int kDispTB = 16;
+
+template <bool PREFETCH, int U>
+__global__ __launch_bounds__(64 * kDispTB) void dispatch_fused(
+    const int32_t *__restrict__ topk_idx, int64_t T, int k, int e0, int E_loc, int nbits, int64_t cap,
+    const u32x4 *__restrict__ x, int64_t units, u32x4 *__restrict__ x_perm, int64_t max_rows,
+    int32_t *__restrict__ seg_offsets, int32_t *__restrict__ kept_count, int32_t *__restrict__ n_dropped,
+    int32_t *__restrict__ slot_row, int32_t *__restrict__ row_src)
+{
+    __shared__ int tot[kSmallExperts], pre[kSmallExperts], seg[kSmallExperts + 1];
+    __shared__ int gc[8][kSmallExperts]; // counts of the block's own items per group of 64 (k <= 32: <= 8 groups)
+    __shared__ int dst[kDispTB * 32];    // row of each own selection (-1 dropped, -2 remote)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t items = T * k;
+    const int64_t t0 = (int64_t)blockIdx.x * kDispTB;
+    const int64_t i0 = t0 * k, i1 = min(items, (t0 + kDispTB) * k);
+    const int64_t t = t0 + wave;
+    for (int q = tid; q < E_loc; q += 64 * kDispTB) {
+        tot[q] = 0;
+        pre[q] = 0;
+    }
+    u32x4 v[U];
+    if (PREFETCH && t < T) {
+#pragma unroll
+        for (int q = 0; q < U; ++q) {
+            const int64_t u = q * 64 + lane;
+            if (u < units)
+                v[q] = x[t * units + u];
+        }
+    }
+    __syncthreads();
+
+    // per-expert counts of all selections and of those before this block's;
+    // each wave takes groups of 64, eight groups' ids loaded at once
+    constexpr int kBatch = 8;
+    for (int64_t b0 = (int64_t)wave * 64; b0 < items; b0 += (int64_t)64 * kDispTB * kBatch) {
+        int id[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t i = b0 + (int64_t)u * 64 * kDispTB + lane;
+            id[u] = i < items ? topk_idx[i] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int64_t g0 = b0 + (int64_t)u * 64 * kDispTB;
+            if (g0 >= items)
+                break; // wave-uniform
+            const int l = g0 + lane < items ? local_of(id[u], e0, E_loc) : -1;
+            const bool loc = l >= 0;
+            const uint64_t m = match_mask(l, loc, nbits);
+            if (loc && (m >> lane) == 1ull) { // highest lane of its expert's group
+                atomicAdd(&tot[l], __popcll(m));
+                const int64_t below = i0 - g0;
+                const uint64_t pm = below >= 64 ? ~0ull : (below <= 0 ? 0ull : ((1ull << below) - 1ull));
+                const int c = __popcll(m & pm);
+                if (c)
+                    atomicAdd(&pre[l], c);
+            }
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        int carry = 0, drop = 0;
+        for (int l0 = 0; l0 < E_loc; l0 += 64) {
+            const int l = l0 + lane;
+            int tl = 0, kept = 0;
+            if (l < E_loc) {
+                tl = tot[l];
+                kept = (cap >= 0 && (int64_t)tl > cap) ? (int)cap : tl;
+            }
+            const int inc = wave_incl_scan(kept, lane);
+            int dr = tl - kept;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1)
+                dr += __shfl_xor(dr, o, 64);
+            if (l < E_loc) {
+                seg[l] = carry + inc - kept;
+                if (blockIdx.x == 0) {
+                    seg_offsets[l] = carry + inc - kept;
+                    kept_count[l] = kept;
+                }
+            }
+            carry += __shfl(inc, 63, 64);
+            drop += dr;
+        }
+        if (lane == 0) {
+            seg[E_loc] = carry;
+            if (blockIdx.x == 0) {
+                seg_offsets[E_loc] = carry;
+                if (n_dropped)
+                    n_dropped[0] = drop;
+            }
+        }
+    }
+
+    // this block's selections: group `wave` of 64
+    const int ngr = (int)((i1 - i0 + 63) / 64);
+    const int64_t i = i0 + (int64_t)wave * 64 + lane;
+    const bool valid = wave < ngr && i < i1;
+    const int l = valid ? local_of(topk_idx[i], e0, E_loc) : -1;
+    uint64_t m = 0;
+    if (wave < ngr) {
+        m = match_mask(l, l >= 0, nbits);
+        for (int q = lane; q < E_loc; q += 64)
+            gc[wave][q] = 0;
+        if (l >= 0 && (m >> lane) == 1ull)
+            gc[wave][l] = __popcll(m);
+    }
+    __syncthreads();
+    if (valid) {
+        int32_t out = -2;
+        if (l >= 0) {
+            int base = pre[l];
+            for (int w2 = 0; w2 < wave; ++w2)
+                base += gc[w2][l];
+            const int64_t r = (int64_t)base + __popcll(m & ((1ull << lane) - 1ull));
+            out = -1;
+            if (cap < 0 || r < cap) {
+                const int64_t row = (int64_t)seg[l] + r;
+                if (row < max_rows) {
+                    out = (int32_t)row;
+                    row_src[row] = (int32_t)i;
+                }
+            }
+        }
+        slot_row[i] = out;
+        dst[i - i0] = out;
+    }
+    __syncthreads();
+
+    // scatter: wave w copies token t0 + w to its kept rows
+    if (t >= T || !x_perm)
+        return;
+    bool any = false;
+    for (int j = 0; j < k; ++j)
+        any |= dst[wave * k + j] >= 0;
+    if (!any)
+        return;
+    for (int64_t u0 = 0; u0 < units; u0 += 64 * U) {
+        if (!PREFETCH || u0 > 0) {
+#pragma unroll
+            for (int q = 0; q < U; ++q) {
+                const int64_t u = u0 + q * 64 + lane;
+                if (u < units)
+                    v[q] = x[t * units + u];
+            }
+        }
+        for (int j = 0; j < k; ++j) {
+            const int r = dst[wave * k + j];
+            if (r < 0)
+                continue;
+            u32x4 *out = x_perm + (int64_t)r * units;
+#pragma unroll
+            for (int q = 0; q < U; ++q) {
+                const int64_t u = u0 + q * 64 + lane;
+                if (u < units)
+                    out[u] = v[q];
+            }
+        }
+    }
+}
+
 template <int U>
 __global__ __launch_bounds__(256) void dispatch_scatter(const u32x4 *__restrict__ x, const int32_t *__restrict__ slot_row,
                                                         int64_t T, int k, int64_t units, u32x4 *__restrict__ x_perm)
@@ -366,6 +558,21 @@ moe_status_t launch_dispatch(const void *x, moe_dtype_t dt, const int32_t *topk_
     int nbits = 0;
     while ((1 << nbits) < E_loc)
         ++nbits;
+    const int64_t fused_blocks = (T + kDispTB - 1) / kDispTB;
+    if (items > 0 && E_loc <= kSmallExperts && k <= 32 && fused_blocks * items <= kFusedReads) {
+        // one launch: every block counts all selections itself
+        const int64_t units = x ? (int64_t)d * (dt == MOE_BF16 ? 2 : 4) / 16 : 0;
+        const bool prefetch = x_perm && cap < 0 && E_loc == E;
+        if (prefetch)
+            dispatch_fused<true, 8><<<(unsigned)fused_blocks, 64 * kDispTB, 0, stream>>>(
+                topk_idx, T, k, e0, E_loc, nbits, cap, (const u32x4 *)x, units, (u32x4 *)x_perm, max_rows,
+                seg_offsets, kept_count, n_dropped, slot_row, row_src);
+        else
+            dispatch_fused<false, 8><<<(unsigned)fused_blocks, 64 * kDispTB, 0, stream>>>(
+                topk_idx, T, k, e0, E_loc, nbits, cap, (const u32x4 *)x, units, (u32x4 *)x_perm, max_rows,
+                seg_offsets, kept_count, n_dropped, slot_row, row_src);
+        return check_launch("dispatch_fused");
+    }
     if (items > 0 && items <= 16 * 2048 && E_loc <= kSmallExperts) {
         // one block plans the whole dispatch: 16 chunks of a multiple of 64
         const int chunk = (int)((items + 16 * 64 - 1) / (16 * 64) * 64);

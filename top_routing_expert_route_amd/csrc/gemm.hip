@@ -613,11 +613,29 @@ __device__ __forceinline__ Fill fill_k(uint64_t wb, uint64_t ab, uint32_t ws, ui
     return f;
 }
 
+// 16 bytes at byte offset voff + soff of a raw buffer record of `bytes`
+// bytes starting at `base`.  The wave-uniform part soff moves the record
+// itself (base + soff, bytes - soff, or an empty record once soff reaches
+// `bytes`), so the access has only the per-lane offset voff (scalar offset
+// and instruction offset zero).  The range check of a raw buffer access
+// compares that offset with the record size and returns zeros, without a
+// memory access, when it is not smaller: rows past a segment's end or past
+// the weight matrix read as zeros whatever part of the offset selects them.
+// All of the record arithmetic is scalar (no vector registers).
 __device__ __forceinline__ u32x4 buf_load16(uint64_t base, uint32_t bytes, uint32_t voff, uint32_t soff)
 {
+    // wave-uniform by construction; readfirstlane keeps the record in scalar
+    // registers (a record the compiler cannot prove uniform costs a loop)
+    soff = (uint32_t)__builtin_amdgcn_readfirstlane((int)soff);
+    bytes = (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes);
+    base = (uint64_t)uni64((int64_t)base);
+    // an empty record whenever soff >= bytes (also for a size-0 record with
+    // any soff: a block with no next work item passes an arbitrary offset);
+    // the saturating difference is read back into a scalar register
+    const uint32_t left = (uint32_t)__builtin_amdgcn_readfirstlane((int)(bytes > soff ? bytes - soff : 0u));
     const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)base, (short)0, (int)bytes, kRsrcWord3);
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+        __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)(base + soff), (short)0, (int)left, kRsrcWord3);
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
 // Copy i of a K step: its rows' scalar byte offset.  Instruction q of a wave

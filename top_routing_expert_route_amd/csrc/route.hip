@@ -10,8 +10,9 @@
 // choice only; routing weights, P and L_aux use the unbiased softmax.
 //
 // Kernels
-//  route_fused_small  bf16 activations, E <= 64: logits (split-bf16 MFMAs, see
-//                     below), softmax, top-k and block partials in one pass.
+//  route_fused        bf16 activations, E <= 64: logits (split-bf16 MFMAs, see
+//                     the kernel), softmax, top-k, block partials and, in the
+//                     last block to finish, the statistics: one launch.
 //  route_split_weight + grouped GEMM
 //                     bf16 activations, E > 64: the fp32 router weight is split
 //                     exactly into three bf16 pieces (hi + mid + lo = w), stacked
@@ -154,181 +155,347 @@ __global__ __launch_bounds__(256) void route_logits_mfma(const uint16_t *__restr
     }
 }
 
-// Fused router for E <= 64 with bf16 activations: one block scores TB = 16*TT
-// tokens against all experts (16*ET >= E) with the split-bf16 MFMAs (the four
-// waves split K, U K-steps of loads in flight per wave), parks the logits in
-// LDS, then one thread per token does softmax and top-k, and the block
-// writes its partial sums of the probabilities and selection counts.
-template <int ET, int TT, int U, int NW>
-__global__ __launch_bounds__(64 * NW) void route_fused_small(const uint16_t *__restrict__ x,
-                                                         const float *__restrict__ wr,
-                                                         const float *__restrict__ bias,
-                                                         const float *__restrict__ sel, int64_t T, int d, int E,
-                                                         int k, int32_t *__restrict__ topk_idx,
-                                                         float *__restrict__ topk_w, float *__restrict__ part_p,
-                                                         int32_t *__restrict__ part_c, float *__restrict__ probs)
-{
-    constexpr int EB = 16 * ET, TB = 16 * TT;
-    constexpr int LS = EB + 1; // padded LDS row of one token's logits
-    __shared__ float red[NW - 1][ET * TT * 256];
-    __shared__ float lg[TB * LS];
-    __shared__ int cnt[EB];
+// ----------------------------------------------------------------------------
+// Single-launch router for bf16 activations and E <= 64 experts.
+//
+// One block of eight waves scores kRouteTB = 16 tokens.  The eight waves split
+// the hidden dimension; per 32-wide K step a wave runs v_mfma_f32_16x16x32_bf16
+// with the weight rows as the A operand (16 experts per row tile, ET tiles) and
+// the 16 tokens as the B operand.  The fp32 router weight is split on the fly,
+// exactly, into three bf16 pieces (hi = w truncated to bf16, mid = (w - hi)
+// truncated, lo = w - hi - mid, at most 8 significant bits), each product with
+// a bf16 activation is exact in fp32, and the three MFMAs accumulate into the
+// same fp32 tile: fp32-class logits at matrix-core rate.  Loads are raw buffer
+// loads whose range check returns zeros for rows past T, experts past E and K
+// past the wave's range (no branches), two chunks of CH steps in flight per
+// wave, so a block keeps its whole share of x streaming while the weight
+// pieces are split.
+//
+// The waves' partial logits are summed in wave order through LDS; softmax and
+// top-k then run lane-parallel, G lanes per token (G = 8, 16, 32 or 64 >= E):
+// group max and sum with butterfly shuffles (every lane of a group ends with
+// the same bits), and each top-k round is a group maximum of a 64-bit key
+// (order-preserving score bits, then the complement of the expert id), so the
+// winner is the largest score and, on ties, the lowest id.  Each block writes
+// its selection counts and its probability sums (token order) as one partial
+// row (coherent agent-scope stores); the last block to arrive (an
+// agent-scope ticket, counted after the block's stores completed) sums the
+// partial rows in a fixed order and writes counts, f, P and L_aux, then
+// resets the ticket to zero for the next call.
+// ----------------------------------------------------------------------------
+constexpr int kRouteWaves = 8;
+constexpr int kRouteTB = 16;
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t t0 = (int64_t)blockIdx.x * TB;
-    const int kw = ((d + NW - 1) / NW + 31) / 32 * 32;
+template <int G> __device__ __forceinline__ float grp_max(float v)
+{
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+template <int G> __device__ __forceinline__ float grp_sum(float v)
+{
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1)
+        v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+template <int G> __device__ __forceinline__ uint64_t grp_max_u64(uint64_t v)
+{
+#pragma unroll
+    for (int o = G / 2; o > 0; o >>= 1) {
+        const uint64_t u = __shfl_xor(v, o, 64);
+        v = u > v ? u : v;
+    }
+    return v;
+}
+
+// Unsigned key with the order of the float scores: NaN below every number,
+// -0 equal to +0; 0 is left for "not a candidate".
+__device__ __forceinline__ uint32_t order_key(float s)
+{
+    if (s != s)
+        return 1u;
+    const uint32_t b = __float_as_uint(s + 0.0f);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// Cross-block publication without cache maintenance: the partial rows are
+// written and read with relaxed agent-scope atomic accesses (coherent across
+// the XCDs' L2s), and each writer waits for its stores to complete before
+// the block's arrival is counted, so the last block to arrive sees every
+// row.  (An agent-scope fence would write back and invalidate the whole L2
+// in every wave.)
+template <class V> __device__ __forceinline__ void publish(V *p, V v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <class V> __device__ __forceinline__ V collect(const V *p)
+{
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Fixed-order sum of the per-block partial rows by the last block (any
+// blockDim.x >= E): G2 threads per expert take rows g, g + G2, ... in double,
+// then thread e adds its G2 sums in order.
+__device__ void finalize_stats(const float *part_p, const int32_t *part_c, int nrows, int64_t T, int E, float alpha,
+                               int32_t *expert_count, float *f, float *P, float *l_aux, double *rp, long long *rc,
+                               double *terms)
+{
+    const int nt = blockDim.x, tid = threadIdx.x;
+    int G2 = 1;
+    while (G2 * 2 * E <= nt)
+        G2 *= 2;
+    const int e = tid / G2, g = tid % G2;
+    double ps = 0.0;
+    long long cs = 0;
+    if (e < E) {
+        for (int b = g; b < nrows; b += G2) {
+            ps += (double)collect(part_p + (int64_t)b * E + e);
+            cs += collect(part_c + (int64_t)b * E + e);
+        }
+    }
+    if (tid < G2 * E) {
+        rp[tid] = ps;
+        rc[tid] = cs;
+    }
+    __syncthreads();
+    for (int q = tid; q < E; q += nt) {
+        double p = 0.0;
+        long long c = 0;
+        for (int i = 0; i < G2; ++i) {
+            p += rp[q * G2 + i];
+            c += rc[q * G2 + i];
+        }
+        const float fe = T > 0 ? (float)c / (float)T : 0.f;
+        const float Pe = T > 0 ? (float)(p / (double)T) : 0.f;
+        if (expert_count)
+            expert_count[q] = (int32_t)c;
+        if (f)
+            f[q] = fe;
+        if (P)
+            P[q] = Pe;
+        terms[q] = (double)fe * (double)Pe;
+    }
+    __syncthreads();
+    if (tid == 0 && l_aux) {
+        double s = 0.0;
+        for (int q = 0; q < E; ++q)
+            s += terms[q];
+        l_aux[0] = (float)((double)alpha * s);
+    }
+}
+
+// True in every thread of the block that arrives last.  Call after the
+// block's partial row was published (every thread).
+__device__ __forceinline__ bool last_block_arrived(unsigned *ticket, int *s_flag)
+{
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); // this thread's published stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = old == gridDim.x - 1 ? 1 : 0;
+    }
+    __syncthreads();
+    return *s_flag != 0;
+}
+
+__device__ __forceinline__ void reset_ticket(unsigned *ticket)
+{
+    if (threadIdx.x == 0)
+        __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int ET, int CH, int G>
+__global__ __launch_bounds__(64 * kRouteWaves) void route_fused(
+    const uint16_t *__restrict__ x, const float *__restrict__ wr, const float *__restrict__ bias,
+    const float *__restrict__ sel, int64_t T, int d, int E, int k, float alpha, int32_t *__restrict__ topk_idx,
+    float *__restrict__ topk_w, float *__restrict__ probs, float *__restrict__ part_p, int32_t *__restrict__ part_c,
+    unsigned *__restrict__ ticket, int32_t *__restrict__ expert_count, float *__restrict__ f, float *__restrict__ P,
+    float *__restrict__ l_aux)
+{
+    constexpr int EB = 16 * ET;
+    constexpr int LS = EB + 1;
+    __shared__ float red[kRouteWaves][ET][4][64];
+    __shared__ float lg[kRouteTB][LS];
+    __shared__ int cnt[EB];
+    __shared__ int s_flag;
+    __shared__ double rp[64 * kRouteWaves];
+    __shared__ long long rc[64 * kRouteWaves];
+    __shared__ double terms[64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int64_t t0 = (int64_t)blockIdx.x * kRouteTB;
+    if (tid < EB)
+        cnt[tid] = 0;
+
+    // K range of this wave, in steps of 32
+    const int kw = ((d + kRouteWaves - 1) / kRouteWaves + 31) / 32 * 32;
     const int kbeg = wave * kw;
     const int kend = min(d, kbeg + kw);
-    const int r16 = lane & 15;
-    const int koff = (lane >> 4) * 8;
-    if (threadIdx.x < EB)
-        cnt[threadIdx.x] = 0;
+    const int nsteps = kend > kbeg ? (kend - kbeg + 31) / 32 : 0;
+    const int nch = (nsteps + CH - 1) / CH;
 
-    f32x4 acc[ET][TT];
+    // token rows of the block and the router weight as range-checked records
+    const int64_t trows = min((int64_t)kRouteTB, T - t0);
+    const __amdgpu_buffer_rsrc_t xr = raw_rsrc(x + t0 * d, (uint32_t)(trows * d * 2));
+    const __amdgpu_buffer_rsrc_t wrr = raw_rsrc(wr, (uint32_t)((int64_t)E * d * 4));
+    const uint32_t xoff0 = (uint32_t)(n * d * 2);
+    uint32_t woff0[ET];
+#pragma unroll
+    for (int a = 0; a < ET; ++a) {
+        const int e = 16 * a + n;
+        woff0[a] = e < E ? (uint32_t)(e * d * 4) : kOutOfRange;
+    }
+
+    f32x4 acc[ET];
 #pragma unroll
     for (int a = 0; a < ET; ++a)
-#pragma unroll
-        for (int b = 0; b < TT; ++b)
-            acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int k0 = kbeg; k0 < kend; k0 += 32 * U) {
-        u32x4 xv[U][TT];
-        f32x4 wv[U][ET][2];
+    // Offsets are made opaque before the loads (empty asm on the register):
+    // otherwise the compiler may turn the out-of-range select into divergent
+    // branches around duplicated loads and drain the load counter there.
+    auto load = [&](int c, u32x4 (&xv)[CH], f32x4 (&wv)[CH][ET][2]) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int kk = k0 + u * 32 + koff;
-            const bool kval = kk < kend;
-#pragma unroll
-            for (int b = 0; b < TT; ++b) {
-                const int64_t t = t0 + b * 16 + r16;
-                xv[u][b] = (kval && t < T) ? *reinterpret_cast<const u32x4 *>(x + t * d + kk) : u32x4{0u, 0u, 0u, 0u};
-            }
+        for (int s = 0; s < CH; ++s) {
+            const int kk = kbeg + (c * CH + s) * 32 + 8 * g;
+            const bool ok = kk < kend;
+            uint32_t xo = ok ? xoff0 + (uint32_t)kk * 2u : kOutOfRange;
+            asm volatile("" : "+v"(xo));
+            xv[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo, 0, 0));
 #pragma unroll
             for (int a = 0; a < ET; ++a) {
-                const int e = a * 16 + r16;
-                if (kval && e < E) {
-                    const f32x4 *p = reinterpret_cast<const f32x4 *>(wr + (int64_t)e * d + kk);
-                    wv[u][a][0] = p[0];
-                    wv[u][a][1] = p[1];
-                } else {
-                    wv[u][a][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    wv[u][a][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
+                uint32_t o0 = (ok && woff0[a] != kOutOfRange) ? woff0[a] + (uint32_t)kk * 4u : kOutOfRange;
+                uint32_t o1 = o0 == kOutOfRange ? o0 : o0 + 16u;
+                asm volatile("" : "+v"(o0), "+v"(o1));
+                wv[s][a][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(wrr, o0, 0, 0));
+                wv[s][a][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(wrr, o1, 0, 0));
             }
         }
+    };
+    auto compute = [&](const u32x4 (&xv)[CH], const f32x4 (&wv)[CH][ET][2]) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+        for (int s = 0; s < CH; ++s) {
+            const bf16x8 xb = __builtin_bit_cast(bf16x8, xv[s]);
 #pragma unroll
             for (int a = 0; a < ET; ++a) {
                 bf16x8 hi, mid, lo;
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
-                    const float w = wv[u][a][q >> 2][q & 3];
+                    const float w = wv[s][a][q >> 2][q & 3];
                     const float h = trunc_bf16(w);
-                    const float r1 = w - h;
+                    const float r1 = w - h;           // exact
                     const float m = trunc_bf16(r1);
                     hi[q] = bits_bf16(h);
                     mid[q] = bits_bf16(m);
-                    lo[q] = bits_bf16(r1 - m);
+                    lo[q] = bits_bf16(r1 - m);        // exact, <= 8 significant bits
                 }
-#pragma unroll
-                for (int b = 0; b < TT; ++b) {
-                    const bf16x8 xb = __builtin_bit_cast(bf16x8, xv[u][b]);
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, xb, acc[a][b], 0, 0, 0);
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, xb, acc[a][b], 0, 0, 0);
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, xb, acc[a][b], 0, 0, 0);
-                }
+                acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, xb, acc[a], 0, 0, 0);
+                acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, xb, acc[a], 0, 0, 0);
+                acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, xb, acc[a], 0, 0, 0);
             }
         }
-    }
+    };
 
-    if (wave > 0) {
-#pragma unroll
-        for (int a = 0; a < ET; ++a)
-#pragma unroll
-            for (int b = 0; b < TT; ++b)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    red[wave - 1][((a * TT + b) * 4 + v) * 64 + lane] = acc[a][b][v];
-    }
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-        for (int a = 0; a < ET; ++a)
-#pragma unroll
-            for (int b = 0; b < TT; ++b)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int slot = ((a * TT + b) * 4 + v) * 64 + lane;
-                    float sum = acc[a][b][v];
-#pragma unroll
-                    for (int q = 0; q < NW - 1; ++q)
-                        sum += red[q][slot];
-                    const int e = a * 16 + 4 * (lane >> 4) + v;
-                    const int tl = b * 16 + (lane & 15);
-                    lg[tl * LS + e] = sum;
-                }
-    }
-    __syncthreads();
-
-    // One thread per token: softmax over E, top-k by (logit desc, id asc).
-    const int tl = threadIdx.x;
-    const int64_t t = t0 + tl;
-    if (tl < TB && t < T) {
-        float *row = lg + tl * LS;
-        float m = -INFINITY;
-        for (int e = 0; e < E; ++e) {
-            const float l = row[e] + (bias ? bias[e] : 0.f);
-            row[e] = l;
-            m = fmaxf(m, l);
+    {
+        // two register chunks in flight; a chunk past the wave's range loads
+        // nothing (every offset out of range) and adds zeros
+        u32x4 xa[CH], xb2[CH];
+        f32x4 wa[CH][ET][2], wb[CH][ET][2];
+        load(0, xa, wa);
+        for (int c = 0; c < nch; c += 2) {
+            load(c + 1, xb2, wb);
+            __builtin_amdgcn_sched_barrier(0); // issue the next chunk's loads before this chunk's waits
+            compute(xa, wa);
+            __builtin_amdgcn_sched_barrier(0);
+            load(c + 2, xa, wa);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(xb2, wb);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        float sum = 0.f;
-        for (int e = 0; e < E; ++e)
-            sum += expf(row[e] - m);
-        const float inv = 1.0f / sum;
-        // selection score: the logit, plus the selection-only bias if given
-        uint64_t taken = 0;
+    }
+
+    // partial tiles: lane holds experts 16a + 4g + v of token n
+#pragma unroll
+    for (int a = 0; a < ET; ++a)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            red[wave][a][v][lane] = acc[a][v];
+    __syncthreads();
+    for (int q = tid; q < ET * 256; q += 64 * kRouteWaves) {
+        const int a = q >> 8, v = (q >> 6) & 3, l = q & 63;
+        float sum = red[0][a][v][l];
+#pragma unroll
+        for (int w = 1; w < kRouteWaves; ++w)
+            sum += red[w][a][v][l];
+        const int e = 16 * a + 4 * (l >> 4) + v;
+        if (e < E)
+            lg[l & 15][e] = sum + (bias ? bias[e] : 0.f);
+    }
+    __syncthreads();
+
+    // softmax and top-k: G lanes per token
+    for (int base = 0; base < kRouteTB * G; base += 64 * kRouteWaves) {
+        if ((base + wave * 64) / G >= kRouteTB)
+            break; // wave-uniform: no token left for this wave
+        const int idx = base + tid;
+        const int tl = idx / G, e = idx % G;
+        const bool ev = e < E;
+        const int64_t t = t0 + tl;
+        const bool tv = t < T;
+        const float l = ev ? lg[tl][e] : -INFINITY;
+        const float m = grp_max<G>(l);
+        const float ex = ev ? expf(l - m) : 0.f;
+        const float ssum = grp_sum<G>(ex);
+        const float p = ex * (1.0f / ssum);
+        const float sc = (ev && sel) ? l + sel[e] : l;
+        const uint64_t mine = ((uint64_t)(ev ? order_key(sc) : 0u) << 32) | (uint64_t)(uint32_t)~(uint32_t)e;
+        bool taken = false;
         for (int j = 0; j < k; ++j) {
-            int best = -1;
-            float bv = 0.f;
-            for (int e = 0; e < E; ++e) {
-                if ((taken >> e) & 1ull)
-                    continue;
-                const float sc = sel ? row[e] + sel[e] : row[e];
-                if (best < 0 || sc > bv) {
-                    best = e;
-                    bv = sc;
+            const uint64_t best = grp_max_u64<G>(taken || !ev ? 0ull : mine);
+            const int be = (int)~(uint32_t)best;
+            if (e == be) {
+                taken = true;
+                if (tv) {
+                    topk_idx[t * k + j] = e;
+                    topk_w[t * k + j] = p;
+                    atomicAdd(&cnt[e], 1);
                 }
             }
-            taken |= 1ull << best;
-            topk_idx[t * k + j] = best;
-            topk_w[t * k + j] = expf(row[best] - m) * inv;
-            atomicAdd(&cnt[best], 1);
         }
-        for (int e = 0; e < E; ++e)
-            row[e] = expf(row[e] - m) * inv;
-    } else if (tl < TB) {
-        float *row = lg + tl * LS;
-        for (int e = 0; e < E; ++e)
-            row[e] = 0.f;
+        if (ev) {
+            if (tv && probs)
+                probs[t * E + e] = p;
+            lg[tl][e] = tv ? p : 0.f;
+        }
     }
     __syncthreads();
-    if (probs) {
-        for (int q = threadIdx.x; q < TB * E; q += 64 * NW) {
-            const int tq = q / E, e = q - tq * E;
-            if (t0 + tq < T)
-                probs[(t0 + tq) * E + e] = lg[tq * LS + e];
-        }
-    }
-    // Block partials: probabilities summed in token order.
-    if (threadIdx.x < E) {
-        const int e = threadIdx.x;
+
+    // this block's partial row: counts, probabilities summed in token order
+    for (int e = tid; e < E; e += 64 * kRouteWaves) {
         float ps = 0.f;
-        for (int q = 0; q < TB; ++q)
-            ps += lg[q * LS + e];
-        part_p[(int64_t)blockIdx.x * E + e] = ps;
-        part_c[(int64_t)blockIdx.x * E + e] = cnt[e];
+        for (int q = 0; q < kRouteTB; ++q)
+            ps += lg[q][e];
+        publish(part_p + (int64_t)blockIdx.x * E + e, ps);
+        publish(part_c + (int64_t)blockIdx.x * E + e, (int32_t)cnt[e]);
     }
+    if (!last_block_arrived(ticket, &s_flag))
+        return;
+    finalize_stats(part_p, part_c, (int)gridDim.x, T, E, alpha, expert_count, f, P, l_aux, rp, rc, terms);
+    reset_ticket(ticket);
 }
 
 // w3[p*E + e, i] = bf16 piece p of w_router[e, i]: hi = w truncated to bf16,
@@ -588,12 +755,15 @@ static int fin_chunks(int nblk) { return (nblk + kFinRows - 1) / kFinRows; }
 static int select_blocks(int64_t T) { return (int)((T + kSelTokensPerBlock - 1) / kSelTokensPerBlock); }
 
 // Tokens per block of the fused small-E path.
-static int fused_tb(int E) { return E <= 16 ? 16 : 32; }
+// Path of the router: the single-launch kernel for bf16 activations with at
+// most 64 experts, otherwise logits (split-weight grouped GEMM, MFMA or fp32
+// kernel) + route_select + the partial-sum reduction.
+static bool route_is_fused(moe_dtype_t dt, int E) { return dt == MOE_BF16 && E <= 64; }
 
 static int route_blocks(int64_t T, int E, moe_dtype_t dt)
 {
-    if (dt == MOE_BF16 && E <= 64)
-        return (int)((T + fused_tb(E) - 1) / fused_tb(E));
+    if (route_is_fused(dt, E))
+        return (int)((T + kRouteTB - 1) / kRouteTB);
     return select_blocks(T);
 }
 
@@ -605,91 +775,113 @@ static bool router_on_gemm(moe_dtype_t dt, int d, int E)
     return dt == MOE_BF16 && E > 64 && E % 8 == 0 && d % 64 == 0 && d >= 128;
 }
 
-size_t route_ws_bytes(int64_t T, int d, int E)
+size_t route_ws_bytes(int64_t T, int d, int E, moe_dtype_t dt)
 {
-    // logits (two-kernel paths) + partials of the larger block count, plus the
-    // split router weight and the grouped GEMM's tail partials for large E
-    const int nblk = (int)((T + 15) / 16);
-    const bool split = E > 64 && d % 64 == 0;
-    size_t b = align_up((size_t)T * E * (split ? 3 : 1) * sizeof(float)) +
-               2 * align_up((size_t)nblk * E * sizeof(float)) + 2 * align_up((size_t)fin_chunks(nblk) * E * 8);
-    if (split)
+    if (T <= 0)
+        return 0;
+    const int nblk = route_blocks(T, E, dt);
+    const size_t parts = 2 * align_up((size_t)nblk * E * sizeof(float));
+    if (route_is_fused(dt, E))
+        return parts;
+    // logits, partials, chunk sums, plus the split router weight and the
+    // grouped GEMM's tail partials when the logits run on it
+    const bool on_gemm = router_on_gemm(dt, d, E);
+    size_t b = align_up((size_t)T * E * (on_gemm ? 3 : 1) * sizeof(float)) + parts +
+               2 * align_up((size_t)fin_chunks(nblk) * E * 8);
+    if (on_gemm)
         b += align_up((size_t)E * 3 * d * sizeof(uint16_t)) + align_up(gemm_ws_bytes());
     return b;
+}
+
+template <int ET, int CH, int G>
+static void launch_fused(const uint16_t *x, const float *w_router, const float *b_router, const float *sel_bias,
+                         int64_t T, int d, int E, int k, float alpha, int32_t *topk_idx, float *topk_w, float *probs,
+                         float *part_p, int32_t *part_c, unsigned *ticket, int32_t *expert_count, float *f, float *P,
+                         float *l_aux, int nblk, hipStream_t stream)
+{
+    route_fused<ET, CH, G><<<(unsigned)nblk, 64 * kRouteWaves, 0, stream>>>(
+        x, w_router, b_router, sel_bias, T, d, E, k, alpha, topk_idx, topk_w, probs, part_p, part_c, ticket,
+        expert_count, f, P, l_aux);
 }
 
 moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, const float *b_router,
                           const float *sel_bias, int64_t T, int d, int E, int k, float alpha, int32_t *topk_idx,
                           float *topk_w,
                           int32_t *expert_count, float *f, float *P, float *l_aux, float *probs, void *ws,
-                          hipStream_t stream)
+                          unsigned *ticket, hipStream_t stream)
 {
+    if (T == 0) {
+        // no tokens: zero counts and statistics
+        route_finalize<true><<<1, 1024, 0, stream>>>((const float *)nullptr, (const int *)nullptr, 0, T, E, alpha,
+                                                     expert_count, f, P, l_aux);
+        return check_launch("route_finalize");
+    }
     const int nblk = route_blocks(T, E, dt);
-    const int nblk_max = (int)((T + 15) / 16);
     Carver cv{(char *)ws, 0};
+    if (route_is_fused(dt, E)) {
+        float *part_p = cv.take<float>((size_t)nblk * E);
+        int32_t *part_c = cv.take<int32_t>((size_t)nblk * E);
+        const uint16_t *xb = (const uint16_t *)x;
+#define MOE_FUSED(ET, CH, G)                                                                                         \
+    launch_fused<ET, CH, G>(xb, w_router, b_router, sel_bias, T, d, E, k, alpha, topk_idx, topk_w, probs, part_p,   \
+                            part_c, ticket, expert_count, f, P, l_aux, nblk, stream)
+        if (E <= 8)
+            MOE_FUSED(1, 8, 8);
+        else if (E <= 16)
+            MOE_FUSED(1, 8, 16);
+        else if (E <= 32)
+            MOE_FUSED(2, 4, 32);
+        else if (E <= 48)
+            MOE_FUSED(3, 2, 64);
+        else
+            MOE_FUSED(4, 2, 64);
+#undef MOE_FUSED
+        return check_launch("route_fused");
+    }
     const bool on_gemm = router_on_gemm(dt, d, E);
     const int pieces = on_gemm ? 3 : 1;
     float *logits = cv.take<float>((size_t)T * E * pieces);
-    float *part_p = cv.take<float>((size_t)nblk_max * E);
-    int32_t *part_c = cv.take<int32_t>((size_t)nblk_max * E);
-    double *fin_p = cv.take<double>((size_t)fin_chunks(nblk_max) * E);
-    long long *fin_c = cv.take<long long>((size_t)fin_chunks(nblk_max) * E);
+    float *part_p = cv.take<float>((size_t)nblk * E);
+    int32_t *part_c = cv.take<int32_t>((size_t)nblk * E);
+    double *fin_p = cv.take<double>((size_t)fin_chunks(nblk) * E);
+    long long *fin_c = cv.take<long long>((size_t)fin_chunks(nblk) * E);
     uint16_t *w3 = on_gemm ? cv.take<uint16_t>((size_t)E * 3 * d) : nullptr;
     void *gws = on_gemm ? cv.take<char>(gemm_ws_bytes()) : nullptr;
 
-    if (T > 0) {
-        if (dt == MOE_BF16 && E <= 64) {
-            const uint16_t *xb = (const uint16_t *)x;
-            const dim3 g((unsigned)nblk);
-            if (E <= 16)
-                route_fused_small<1, 1, 8, 8><<<g, 512, 0, stream>>>(xb, w_router, b_router, sel_bias, T, d, E, k, topk_idx,
-                                                                  topk_w, part_p, part_c, probs);
-            else if (E <= 32)
-                route_fused_small<2, 2, 4, 8><<<g, 512, 0, stream>>>(xb, w_router, b_router, sel_bias, T, d, E, k, topk_idx,
-                                                                  topk_w, part_p, part_c, probs);
-            else
-                route_fused_small<4, 2, 2, 8><<<g, 512, 0, stream>>>(xb, w_router, b_router, sel_bias, T, d, E, k, topk_idx,
-                                                                  topk_w, part_p, part_c, probs);
-            if (moe_status_t s = check_launch("route_fused_small"))
-                return s;
-        } else {
-            if (on_gemm) {
-                const int64_t n = (int64_t)E * d;
-                route_split_weight<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(w_router, n, w3);
-                if (moe_status_t s = check_launch("route_split_weight"))
-                    return s;
-                if (moe_status_t s = launch_router_gemm(x, w3, T, d, E, logits, gws, gemm_ws_bytes(), stream))
-                    return s;
-            } else if (dt == MOE_BF16) {
-                dim3 g((unsigned)((T + 63) / 64), (unsigned)((E + 63) / 64));
-                route_logits_mfma<4, 4><<<g, 256, 0, stream>>>((const uint16_t *)x, w_router, T, d, E, logits);
-            } else {
-                const int64_t n = T * E;
-                route_logits_f32<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>((const float *)x, w_router, T, d,
-                                                                                 E, logits);
-            }
-            if (moe_status_t s = check_launch("route_logits"))
-                return s;
-            const int epl = (E + 63) / 64;
-            const dim3 g((unsigned)nblk);
-            switch (epl) {
-            case 1: route_select<1><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs); break;
-            case 2: route_select<2><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs); break;
-            case 3:
-            case 4: route_select<4><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs); break;
-            case 5: case 6: case 7: case 8:
-                route_select<8><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs); break;
-            default:
-                route_select<16><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs); break;
-            }
-            if (moe_status_t s = check_launch("route_select"))
-                return s;
-        }
+    if (on_gemm) {
+        const int64_t n = (int64_t)E * d;
+        route_split_weight<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(w_router, n, w3);
+        if (moe_status_t s = check_launch("route_split_weight"))
+            return s;
+        if (moe_status_t s = launch_router_gemm(x, w3, T, d, E, logits, gws, gemm_ws_bytes(), stream))
+            return s;
+    } else if (dt == MOE_BF16) {
+        dim3 g((unsigned)((T + 63) / 64), (unsigned)((E + 63) / 64));
+        route_logits_mfma<4, 4><<<g, 256, 0, stream>>>((const uint16_t *)x, w_router, T, d, E, logits);
+    } else {
+        const int64_t n = T * E;
+        route_logits_f32<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>((const float *)x, w_router, T, d, E,
+                                                                         logits);
     }
-    const int rows = T > 0 ? nblk : 0;
-    if (rows <= 32 * finalize_threads_per_expert(E)) {
+    if (moe_status_t s = check_launch("route_logits"))
+        return s;
+    const int epl = (E + 63) / 64;
+    const dim3 g((unsigned)nblk);
+    switch (epl) {
+    case 1: route_select<1><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs); break;
+    case 2: route_select<2><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs); break;
+    case 3:
+    case 4: route_select<4><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs); break;
+    case 5: case 6: case 7: case 8:
+        route_select<8><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs); break;
+    default:
+        route_select<16><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs); break;
+    }
+    if (moe_status_t s = check_launch("route_select"))
+        return s;
+    if (nblk <= 32 * finalize_threads_per_expert(E)) {
         // at most 32 partial rows per thread: sum them directly
-        route_finalize<true><<<1, 1024, 0, stream>>>(part_p, part_c, rows, T, E, alpha, expert_count, f, P, l_aux);
+        route_finalize<true><<<1, 1024, 0, stream>>>(part_p, part_c, nblk, T, E, alpha, expert_count, f, P, l_aux);
         return check_launch("route_finalize");
     }
     const int nfin = fin_chunks(nblk);
