@@ -19,8 +19,9 @@
  * Conventions for every entry point
  *  - Buffer pointers are DEVICE pointers on the current HIP device, allocated
  *    and owned by the caller, row-major and densely packed.  The library never
- *    allocates, frees or keeps device memory, and keeps no state between calls
- *    except a thread-local copy of the last error message.
+ *    allocates, frees or keeps device memory (except the fixed static scratch
+ *    of moe_dispatch_noalloc, part of the loaded library), and keeps no state
+ *    between calls except a thread-local copy of the last error message.
  *  - Work is enqueued on `stream` (NULL = the default stream) and is
  *    asynchronous: a call returns before the GPU has finished and never
  *    synchronises.  Counts that the GPU computes (rows per expert, drops) never
@@ -166,6 +167,28 @@ moe_status_t moe_dispatch(const void *x, moe_dtype_t dtype, const int32_t *topk_
                           int num_local_experts, int32_t *seg_offsets, int32_t *kept_count,
                           int32_t *slot_row, int32_t *row_src, void *x_perm, int64_t max_rows,
                           int32_t *n_dropped, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ *
+ * moe_dispatch_noalloc - moe_dispatch for callers that cannot allocate device
+ * memory or hand over a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).
+ *
+ * Same arguments, results and errors as moe_dispatch, without ws/ws_bytes:
+ * the planner's scratch lives in a static device buffer of the library
+ * (moe_dispatch_noalloc_scratch_bytes() bytes, 64 KiB, one per device, held
+ * until the process ends).  The call allocates nothing and calls no
+ * allocating routine.  Sizes whose scratch need (moe_dispatch_workspace_size)
+ * exceeds the buffer return MOE_ERR_UNSUPPORTED (the planner keeps it within
+ * 64 KiB for every supported size).  Every call on a device shares that
+ * device's buffer: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller.
+ * ------------------------------------------------------------------------ */
+size_t moe_dispatch_noalloc_scratch_bytes(void);
+moe_status_t moe_dispatch_noalloc(const void *x, moe_dtype_t dtype, const int32_t *topk_idx, int64_t T, int d,
+                                  int E, int k, float capacity_factor, int expert_begin, int num_local_experts,
+                                  int32_t *seg_offsets, int32_t *kept_count, int32_t *slot_row,
+                                  int32_t *row_src, void *x_perm, int64_t max_rows, int32_t *n_dropped,
+                                  hipStream_t stream);
 
 /* ------------------------------------------------------------------------ *
  * moe_grouped_gemm - one Linear layer of every expert over its row segment.

@@ -54,7 +54,8 @@ class Outputs(ctypes.Structure):
 
 
 EXPORTS = ["moe_abi_version", "moe_status_string", "moe_last_error", "moe_max_rows", "moe_route_workspace_size",
-           "moe_route", "moe_dispatch_workspace_size", "moe_dispatch", "moe_grouped_gemm_workspace_size",
+           "moe_route", "moe_dispatch_workspace_size", "moe_dispatch", "moe_dispatch_noalloc_scratch_bytes",
+           "moe_dispatch_noalloc", "moe_grouped_gemm_workspace_size",
            "moe_grouped_gemm", "moe_expert_ffn", "moe_combine", "moe_forward_workspace_size", "moe_forward",
            "moe_forward_overlap_workspace_size", "moe_forward_overlap", "moe_backward_workspace_size",
            "moe_backward", "moe_forward_save", "moe_backward_saved"]
@@ -82,6 +83,9 @@ def lib():
     L.moe_dispatch_workspace_size.argtypes, L.moe_dispatch_workspace_size.restype = [I64, I, I], SZ
     L.moe_dispatch.argtypes = [P, I, P, I64, I, I, I, F, I, I, P, P, P, P, P, I64, P, P, SZ, P]
     L.moe_dispatch.restype = I
+    L.moe_dispatch_noalloc_scratch_bytes.argtypes, L.moe_dispatch_noalloc_scratch_bytes.restype = [], SZ
+    L.moe_dispatch_noalloc.argtypes = [P, I, P, I64, I, I, I, F, I, I, P, P, P, P, P, I64, P, P]
+    L.moe_dispatch_noalloc.restype = I
     L.moe_grouped_gemm_workspace_size.argtypes, L.moe_grouped_gemm_workspace_size.restype = [], SZ
     L.moe_grouped_gemm.argtypes = [P, P, I, I64, I, I, I, P, P, I, P, P, SZ, P]
     L.moe_grouped_gemm.restype = I
@@ -189,7 +193,10 @@ def moe_route(x: torch.Tensor, w_router: torch.Tensor, b_router: Optional[torch.
 
 def moe_dispatch(x: Optional[torch.Tensor], topk_idx: torch.Tensor, E: int, capacity_factor: float = 0.0,
                  expert_begin: int = 0, num_local_experts: int = 0, with_x_perm: bool = True,
-                 rows: Optional[int] = None, dtype: Optional[torch.dtype] = None, d: Optional[int] = None) -> dict:
+                 rows: Optional[int] = None, dtype: Optional[torch.dtype] = None, d: Optional[int] = None,
+                 noalloc: bool = False) -> dict:
+    """moe_dispatch with a torch workspace; with noalloc, moe_dispatch_noalloc
+    (the library's static scratch, no workspace)."""
     T, k = topk_idx.shape
     dev = topk_idx.device
     E_loc = num_local_experts if num_local_experts > 0 else E
@@ -203,6 +210,13 @@ def moe_dispatch(x: Optional[torch.Tensor], topk_idx: torch.Tensor, E: int, capa
                n_dropped=torch.empty(1, dtype=torch.int32, device=dev),
                x_perm=(torch.empty((max(1, mr), d), dtype=x.dtype, device=dev) if (with_x_perm and x is not None)
                        else None))
+    if noalloc:
+        check(lib().moe_dispatch_noalloc(_p(x), dt, _p(topk_idx), T, d, E, k, capacity_factor, expert_begin,
+                                         num_local_experts, _p(out["seg_offsets"]), _p(out["kept_count"]),
+                                         _p(out["slot_row"]), _p(out["row_src"]), _p(out["x_perm"]), mr,
+                                         _p(out["n_dropped"]), _stream(dev)))
+        out["max_rows"] = mr
+        return out
     nb = lib().moe_dispatch_workspace_size(T, k, E_loc)
     ws = workspace(dev, nb)
     check(lib().moe_dispatch(_p(x), dt, _p(topk_idx), T, d, E, k, capacity_factor, expert_begin,

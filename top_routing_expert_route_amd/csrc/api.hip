@@ -3,6 +3,7 @@
 // Every entry point validates before anything is enqueued.
 #include "common.hpp"
 
+#include <mutex>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -279,6 +280,71 @@ moe_status_t moe_dispatch(const void *x, moe_dtype_t dtype, const int32_t *topk_
     return launch_dispatch(x, dtype, topk_idx, T, d, E, k, capacity_factor, expert_begin, E_loc, seg_offsets,
                            kept_count, slot_row, row_src, x_perm, max_rows, n_dropped, (char *)ws + kCtrlBytes,
                            stream);
+}
+
+} // extern "C"
+
+// ------------------------------------------------ dispatch without allocation
+// moe_dispatch_noalloc keeps its scratch (the per-chunk expert counts of the
+// dispatch planner) in this file-scope device array instead of a caller
+// workspace.  Each device holds its own copy for the life of the process; its
+// address on the current device is looked up once per device with
+// hipGetSymbolAddress and only that address is handed to kernels (the array's
+// name is a host-side stand-in in host code).
+namespace {
+
+constexpr size_t kStaticScratchBytes = 64 * 1024;
+constexpr int kMaxDevices = 64;
+
+__device__ __attribute__((used)) __align__(256) int32_t scratch[kStaticScratchBytes / sizeof(int32_t)];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+moe_status_t static_scratch(void **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return fail(MOE_ERR_HIP, "dispatch_noalloc: no usable current device (%d)", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(MOE_ERR_HIP, "dispatch_noalloc: hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+size_t moe_dispatch_noalloc_scratch_bytes(void) { return kStaticScratchBytes; }
+
+moe_status_t moe_dispatch_noalloc(const void *x, moe_dtype_t dtype, const int32_t *topk_idx, int64_t T, int d, int E,
+                                  int k, float capacity_factor, int expert_begin, int num_local_experts,
+                                  int32_t *seg_offsets, int32_t *kept_count, int32_t *slot_row, int32_t *row_src,
+                                  void *x_perm, int64_t max_rows, int32_t *n_dropped, hipStream_t stream)
+{
+    clear_error();
+    if (moe_status_t s = check_dispatch_args(x, dtype, topk_idx, T, d, E, k, capacity_factor, expert_begin,
+                                             num_local_experts, seg_offsets, kept_count, slot_row, row_src, x_perm,
+                                             max_rows))
+        return s;
+    const int E_loc = local_count(E, num_local_experts);
+    const size_t need = dispatch_ws_bytes(T, k, E_loc);
+    if (need > kStaticScratchBytes)
+        return fail(MOE_ERR_UNSUPPORTED, "dispatch_noalloc: needs %zu bytes of scratch, the static buffer holds %zu",
+                    need, kStaticScratchBytes);
+    void *ws = nullptr;
+    if (moe_status_t s = static_scratch(&ws))
+        return s;
+    return launch_dispatch(x, dtype, topk_idx, T, d, E, k, capacity_factor, expert_begin, E_loc, seg_offsets,
+                           kept_count, slot_row, row_src, x_perm, max_rows, n_dropped, ws, stream);
 }
 
 size_t moe_grouped_gemm_workspace_size(void) { return kCtrlBytes + gemm_ws_bytes(); }
