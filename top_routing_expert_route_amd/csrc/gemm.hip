@@ -613,49 +613,53 @@ __device__ __forceinline__ Fill fill_k(uint64_t wb, uint64_t ab, uint32_t ws, ui
     return f;
 }
 
-// 16 bytes at byte offset voff + soff of a raw buffer record of `bytes`
-// bytes starting at `base`.  The wave-uniform part soff moves the record
-// itself (base + soff, bytes - soff, or an empty record once soff reaches
-// `bytes`), so the access has only the per-lane offset voff (scalar offset
-// and instruction offset zero).  The range check of a raw buffer access
-// compares that offset with the record size and returns zeros, without a
-// memory access, when it is not smaller: rows past a segment's end or past
-// the weight matrix read as zeros whatever part of the offset selects them.
-// All of the record arithmetic is scalar (no vector registers).
-__device__ __forceinline__ u32x4 buf_load16(uint64_t base, uint32_t bytes, uint32_t voff, uint32_t soff)
+// max(a - b, 0) for wave-uniform a and b, on the scalar unit (the compiler
+// would turn the saturating difference into a vector instruction).
+__device__ __forceinline__ uint32_t sat_sub_scalar(uint32_t a, uint32_t b)
 {
-    // wave-uniform by construction; readfirstlane keeps the record in scalar
-    // registers (a record the compiler cannot prove uniform costs a loop)
-    soff = (uint32_t)__builtin_amdgcn_readfirstlane((int)soff);
+    uint32_t r;
+    asm("s_sub_u32 %0, %1, %2\n\ts_cselect_b32 %0, 0, %0" : "=&s"(r) : "s"(a), "s"(b) : "scc");
+    return r;
+}
+
+// 16 bytes of a raw buffer record of `bytes` bytes at `base`, at per-lane
+// byte offset voff within rows that start row_off bytes into the record,
+// plus a K offset k_off inside those rows.  The row part moves the record
+// itself (base + row_off, bytes - row_off, empty once row_off reaches
+// bytes), so which row is read is set by the per-lane offset alone; the K
+// part (smaller than one row) goes in the scalar offset.  The range check of
+// a raw buffer access compares its offset with the record size and returns
+// zeros without a memory access when it is not smaller, so rows past a
+// segment's end or past the weight matrix read as zeros and nothing past
+// the operand is touched, whether or not the scalar offset takes part in
+// the check.  All record arithmetic is scalar.
+__device__ __forceinline__ u32x4 buf_load16(uint64_t base, uint32_t bytes, uint32_t voff, uint32_t row_off,
+                                            uint32_t k_off)
+{
+    row_off = (uint32_t)__builtin_amdgcn_readfirstlane((int)row_off);
     bytes = (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes);
     base = (uint64_t)uni64((int64_t)base);
-    // an empty record whenever soff >= bytes (also for a size-0 record with
-    // any soff: a block with no next work item passes an arbitrary offset);
-    // the saturating difference is read back into a scalar register
-    const uint32_t left = (uint32_t)__builtin_amdgcn_readfirstlane((int)(bytes > soff ? bytes - soff : 0u));
-    const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)(base + soff), (short)0, (int)left, kRsrcWord3);
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(uintptr_t)(base + row_off), (short)0, (int)sat_sub_scalar(bytes, row_off), kRsrcWord3);
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, k_off, 0));
 }
 
-// Copy i of a K step: its rows' scalar byte offset.  Instruction q of a wave
-// covers rows (NW q + wave) * RPI .. + RPI - 1 (RPI = 8 rows of 128 bytes).
-template <int BK, class G> __device__ __forceinline__ uint32_t copy_soff(const CopyGeo &cg, const Fill &f, int i)
-{
-    constexpr int CPR = BK / 8, RPI = 64 / CPR, NW = G::NW;
-    const int q = i >> 1;
-    if (G::WT && !(i & 1))
-        return (uint32_t)q * (uint32_t)(2 * NW) * cg.row_w + f.so_w;
-    if (G::AT && (i & 1))
-        return (uint32_t)q * (uint32_t)(2 * NW) * cg.row_a + f.so_a;
-    return (i & 1) ? (uint32_t)q * (uint32_t)(NW * RPI) * cg.row_a + f.so_a
-                   : (uint32_t)q * (uint32_t)(NW * RPI) * cg.row_w + f.so_w;
-}
-
+// Copy i of a K step (W rows for even i, A rows for odd i).  Instruction q
+// of a wave covers rows (NW q + wave) * RPI .. + RPI - 1 (RPI = 8 rows of
+// 128 bytes); a K-major operand's copy moves two K-rows per instruction and
+// its K step is a row offset too.
 template <int BK, class G> __device__ __forceinline__ u32x4 copy_load(const CopyGeo &cg, const Fill &f, int i)
 {
-    const uint32_t so = copy_soff<BK, G>(cg, f, i);
-    return (i & 1) ? buf_load16(f.abase, f.abytes, cg.vbase_a, so) : buf_load16(f.wbase, f.wbytes, cg.vbase, so);
+    constexpr int CPR = BK / 8, RPI = 64 / CPR, NW = G::NW;
+    const uint32_t q = (uint32_t)(i >> 1);
+    if (i & 1) {
+        if (G::AT)
+            return buf_load16(f.abase, f.abytes, cg.vbase_a, q * (uint32_t)(2 * NW) * cg.row_a + f.so_a, 0u);
+        return buf_load16(f.abase, f.abytes, cg.vbase_a, q * (uint32_t)(NW * RPI) * cg.row_a, f.so_a);
+    }
+    if (G::WT)
+        return buf_load16(f.wbase, f.wbytes, cg.vbase, q * (uint32_t)(2 * NW) * cg.row_w + f.so_w, 0u);
+    return buf_load16(f.wbase, f.wbytes, cg.vbase, q * (uint32_t)(NW * RPI) * cg.row_w, f.so_w);
 }
 
 // LDS byte offset (within a stage) of copy i's 16 bytes for this lane: the
