@@ -337,6 +337,11 @@ __global__ __launch_bounds__(64 * kDispTB) void dispatch_fused(
         tot[q] = 0;
         pre[q] = 0;
     }
+    // this block's own selections (group `wave` of 64), loaded with the rest
+    const int ngr = (int)((i1 - i0 + 63) / 64);
+    const int64_t i = i0 + (int64_t)wave * 64 + lane;
+    const bool valid = wave < ngr && i < i1;
+    const int own_id = valid ? topk_idx[i] : -1;
     u32x4 v[U];
     if (PREFETCH && t < T) {
 #pragma unroll
@@ -411,11 +416,8 @@ __global__ __launch_bounds__(64 * kDispTB) void dispatch_fused(
         }
     }
 
-    // this block's selections: group `wave` of 64
-    const int ngr = (int)((i1 - i0 + 63) / 64);
-    const int64_t i = i0 + (int64_t)wave * 64 + lane;
-    const bool valid = wave < ngr && i < i1;
-    const int l = valid ? local_of(topk_idx[i], e0, E_loc) : -1;
+    // rank this block's selections: group `wave` of 64
+    const int l = valid ? local_of(own_id, e0, E_loc) : -1;
     uint64_t m = 0;
     if (wave < ngr) {
         m = match_mask(l, l >= 0, nbits);
