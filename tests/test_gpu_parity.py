@@ -411,6 +411,33 @@ def test_grouped_gemm_segments(dtype, act):
     assert (got[seg[-1]:] == 7.0).all()
 
 
+@pytest.mark.parametrize("use_ws", [False, True])
+def test_grouped_gemm_256_partial_row_tiles(use_ws):
+    """The 256x256 kernel on segments whose last row tile holds 1, 64, 65,
+    128, 129 or a whole tile's rows, empty segments included, with and
+    without the split-K tail (here every tile is split: 38 tiles on the
+    whole chip)."""
+    g = torch.Generator().manual_seed(8)
+    sizes = [0, 1, 64, 65, 128, 129, 0, 256, 257, 384, 385, 640, 700, 3]
+    rows, K, N = sum(sizes) + 5, 256, 512
+    S = len(sizes)
+    a = torch.randn(rows, K, generator=g).to(torch.bfloat16)
+    w = (torch.randn(S, N, K, generator=g) / K ** 0.5).to(torch.bfloat16)
+    b = (torch.randn(S, N, generator=g) * 0.1).to(torch.bfloat16)
+    seg = torch.tensor(np.concatenate([[0], np.cumsum(sizes)]), dtype=torch.int32)
+    out = torch.full((rows, N), 7.0, dtype=torch.bfloat16).to(DEV)
+    od = api.moe_grouped_gemm(a.to(DEV), seg.to(DEV), w.to(DEV), b.to(DEV), 1, out=out, use_ws=use_ws)
+    torch.cuda.synchronize()
+    got = od.float().cpu()
+    for s_ in range(S):
+        lo, hi = int(seg[s_]), int(seg[s_ + 1])
+        if hi > lo:
+            ref = torch.nn.functional.gelu(a[lo:hi].double() @ w[s_].double().T + b[s_].double(),
+                                           approximate="none")
+            assert rel_err(got[lo:hi].numpy(), ref.numpy()) <= 1e-2, s_
+    assert (got[int(seg[-1]):] == 7.0).all()
+
+
 def test_grouped_gemm_single_segment_null_offsets():
     g = torch.Generator().manual_seed(6)
     a = torch.randn(300, 128, generator=g).to(torch.bfloat16)

@@ -44,7 +44,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 //   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
 //   t = 1 / (1 + p x),
 // with erf(-x) = -erf(x).  With q = erfc(|u| / sqrt 2) / 2 this gives
-// GELU(u) = u - u q for u >= 0 and u q for u < 0.
+// GELU(u) = u - u q for u >= 0 and u q for u < 0, i.e. max(u, 0) - |u| q
+// (one fused multiply-add after the max: the same rounding as either branch,
+// without a compare and select).
 __device__ __forceinline__ float gelu_erf(float u)
 {
     const float x = fabsf(u) * 0.70710678118654752f;
@@ -55,7 +57,7 @@ __device__ __forceinline__ float gelu_erf(float u)
     poly = fmaf(poly, t, 0.254829592f);
     poly *= t;
     const float q = 0.5f * poly * __expf(-x * x);
-    return u >= 0.f ? u - u * q : u * q;
+    return fmaf(-fabsf(u), q, fmaxf(u, 0.f));
 }
 
 // GELU and its derivative together: with Phi the standard normal CDF and phi
@@ -73,7 +75,7 @@ __device__ __forceinline__ void gelu_and_grad(float u, float &g, float &gp)
     poly *= t;
     const float e = __expf(-x * x);
     const float q = 0.5f * poly * e; // Phi(-|u|)
-    g = u >= 0.f ? u - u * q : u * q;
+    g = fmaf(-fabsf(u), q, fmaxf(u, 0.f));
     const float Phi = u >= 0.f ? 1.0f - q : q;
     gp = fmaf(u, e * 0.39894228040143268f, Phi);
 }
