@@ -45,19 +45,43 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 //   t = 1 / (1 + p x),
 // with erf(-x) = -erf(x).  With q = erfc(|u| / sqrt 2) / 2 this gives
 // GELU(u) = u - u q for u >= 0 and u q for u < 0, i.e. max(u, 0) - |u| q
-// (one fused multiply-add after the max: the same rounding as either branch,
-// without a compare and select).
-__device__ __forceinline__ float gelu_erf(float u)
+// (one fused multiply-add after the max: the same rounding as either branch).
+// The factor 1/2 of q is folded into the coefficients: halving every
+// coefficient halves each step of the Horner chain exactly (a power-of-two
+// scale commutes with rounding), so q comes out bitwise as before with one
+// multiply less.
+constexpr float kGeluP = 0.3275911f;
+constexpr float kGeluA1 = 0.254829592f * 0.5f, kGeluA2 = -0.284496736f * 0.5f, kGeluA3 = 1.421413741f * 0.5f,
+                kGeluA4 = -1.453152027f * 0.5f, kGeluA5 = 1.061405429f * 0.5f;
+
+// max(u, 0) as one instruction (the generic maximum first quiets the input,
+// a second instruction the compiler cannot drop for a value of unknown origin).
+__device__ __forceinline__ float relu_f32(float u)
+{
+    float r;
+    asm("v_max_f32 %0, 0, %1" : "=v"(r) : "v"(u));
+    return r;
+}
+
+// q = erfc(|u| / sqrt 2) / 2 and e = exp(-u^2 / 2)
+__device__ __forceinline__ float gelu_q(float u, float &e)
 {
     const float x = fabsf(u) * 0.70710678118654752f;
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
-    float poly = fmaf(1.061405429f, t, -1.453152027f);
-    poly = fmaf(poly, t, 1.421413741f);
-    poly = fmaf(poly, t, -0.284496736f);
-    poly = fmaf(poly, t, 0.254829592f);
+    const float t = __builtin_amdgcn_rcpf(fmaf(kGeluP, x, 1.0f));
+    float poly = fmaf(kGeluA5, t, kGeluA4);
+    poly = fmaf(poly, t, kGeluA3);
+    poly = fmaf(poly, t, kGeluA2);
+    poly = fmaf(poly, t, kGeluA1);
     poly *= t;
-    const float q = 0.5f * poly * __expf(-x * x);
-    return fmaf(-fabsf(u), q, fmaxf(u, 0.f));
+    e = __expf(-x * x);
+    return poly * e;
+}
+
+__device__ __forceinline__ float gelu_erf(float u)
+{
+    float e;
+    const float q = gelu_q(u, e);
+    return fmaf(-fabsf(u), q, relu_f32(u));
 }
 
 // GELU and its derivative together: with Phi the standard normal CDF and phi
@@ -66,16 +90,9 @@ __device__ __forceinline__ float gelu_erf(float u)
 // GELU), phi(u) = exp(-u^2 / 2) / sqrt(2 pi) shares its exponential.
 __device__ __forceinline__ void gelu_and_grad(float u, float &g, float &gp)
 {
-    const float x = fabsf(u) * 0.70710678118654752f;
-    const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
-    float poly = fmaf(1.061405429f, t, -1.453152027f);
-    poly = fmaf(poly, t, 1.421413741f);
-    poly = fmaf(poly, t, -0.284496736f);
-    poly = fmaf(poly, t, 0.254829592f);
-    poly *= t;
-    const float e = __expf(-x * x);
-    const float q = 0.5f * poly * e; // Phi(-|u|)
-    g = fmaf(-fabsf(u), q, fmaxf(u, 0.f));
+    float e;
+    const float q = gelu_q(u, e); // Phi(-|u|)
+    g = fmaf(-fabsf(u), q, relu_f32(u));
     const float Phi = u >= 0.f ? 1.0f - q : q;
     gp = fmaf(u, e * 0.39894228040143268f, Phi);
 }
