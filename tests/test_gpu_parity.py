@@ -319,6 +319,19 @@ def test_few_tokens(T):
     _check_forward(w, inp, t)
 
 
+@pytest.mark.parametrize("d", [65536, 65544])
+def test_large_hidden_size(d):
+    """A hidden size far past the benchmark's: the router's per-wave K range
+    spans 256 steps and the first expert GEMM 1024 K steps (split along K
+    over the chip: eight row tiles); d = 65544 is a multiple of 8 but not of
+    64, so the first GEMM takes the 128x128 kernel and the router's last K
+    step is ragged."""
+    w = wl.scaled(wl.get(1), name="wide-d%d" % d, T=40, d=d, ffn=128, router_bias="gauss",
+                  expert_bias="gauss")
+    inp, t = _inputs(w)
+    _check_forward(w, inp, t)
+
+
 def test_single_expert_is_dense_ffn():
     w = wl.scaled(wl.get(1), T=130, d=128, E=1, k=1, ffn=256, expert_bias="gauss")
     inp, t = _inputs(w)
