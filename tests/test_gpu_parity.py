@@ -332,6 +332,17 @@ def test_large_hidden_size(d):
     _check_forward(w, inp, t)
 
 
+@pytest.mark.parametrize("cf", [0.0, 1.25])
+def test_many_tokens(cf):
+    """200 000 tokens of a narrow layer: 12 500 router blocks feeding the
+    last-block statistics, and a dispatch past the single-launch bound (the
+    histogram, scan, rank and scatter kernels), with and without a cap."""
+    w = wl.scaled(wl.get(1), name="many-t-cf%g" % cf, T=200000, d=64, ffn=64, capacity_factor=cf,
+                  router_bias="gauss", expert_bias="gauss")
+    inp, t = _inputs(w)
+    _check_forward(w, inp, t)
+
+
 def test_single_expert_is_dense_ffn():
     w = wl.scaled(wl.get(1), T=130, d=128, E=1, k=1, ffn=256, expert_bias="gauss")
     inp, t = _inputs(w)
