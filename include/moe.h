@@ -151,9 +151,10 @@ moe_status_t moe_route(const void *x, moe_dtype_t dtype, const float *w_router,
  * Rows are ordered by (local expert, token): the result is unique and
  * bitwise reproducible.
  *
- * x [T,d] (dtype; may be NULL when x_perm is NULL), topk_idx [T,k] i32,
- * seg_offsets [E_loc+1], kept_count [E_loc], slot_row [T,k], row_src
- * [max_rows], x_perm [max_rows, d] or NULL, n_dropped [1] or NULL.
+ * x [T,d] (dtype; may be NULL when x_perm is NULL or T = 0), topk_idx [T,k]
+ * i32, seg_offsets [E_loc+1], kept_count [E_loc], slot_row [T,k], row_src
+ * [max_rows], x_perm [max_rows, d] or NULL, n_dropped [1] or NULL (with
+ * T = 0 only seg_offsets, kept_count and n_dropped are written, all zero).
  * max_rows must be >= moe_max_rows(T, E, k, capacity_factor, num_local_experts).
  * num_local_experts = 0 means the whole layer (expert_begin must then be 0).
  * ws: moe_dispatch_workspace_size(T, k, E_loc) bytes.

@@ -314,6 +314,18 @@ def test_zero_tokens():
     assert outs["l_aux"].item() == 0.0 and outs["n_dropped"].item() == 0
 
 
+@pytest.mark.parametrize("noalloc", [False, True])
+def test_dispatch_zero_tokens(noalloc):
+    """moe_dispatch (and the allocation-free form) on zero tokens: an empty x
+    is allowed, the segment offsets, kept counts and drop count are zero."""
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    idx = torch.empty((0, 2), dtype=torch.int32, device=DEV)
+    out = api.moe_dispatch(x, idx, 8, 1.25, 0, 0, noalloc=noalloc)
+    torch.cuda.synchronize()
+    assert (out["seg_offsets"] == 0).all() and (out["kept_count"] == 0).all()
+    assert out["n_dropped"].item() == 0
+
+
 @pytest.mark.parametrize("T", [1, 17])
 def test_few_tokens(T):
     w = wl.scaled(wl.get(1), T=T, d=128, ffn=256, router_bias="gauss", expert_bias="gauss")

@@ -91,7 +91,7 @@ moe_status_t check_dispatch_args(const void *x, moe_dtype_t dt, const int32_t *t
         return fail(MOE_ERR_INVALID_ARG, "dispatch: capacity_factor is NaN");
     if (!seg_offsets || !kept_count || (T > 0 && (!topk_idx || !slot_row || !row_src)))
         return fail(MOE_ERR_INVALID_ARG, "dispatch: a required pointer is NULL");
-    if (x_perm && !x)
+    if (T > 0 && x_perm && !x)
         return fail(MOE_ERR_INVALID_ARG, "dispatch: x_perm needs x");
     if (!aligned16(x) || !aligned16(x_perm))
         return fail(MOE_ERR_INVALID_ARG, "dispatch: x and x_perm must be 16-byte aligned");
