@@ -512,6 +512,32 @@ def test_route_leaves_workspace_counters_zero():
             _check_route(w, inp, r, ref_route)
 
 
+@pytest.mark.parametrize("T,d,E,k,sel", [
+    (8205, 256, 64, 2, "none"),    # two token tiles per block, last block 13 tokens
+    (8223, 520, 16, 4, "gauss"),   # two tiles, ragged K range per wave, selection bias
+    (16421, 200, 33, 3, "none"),   # four tiles, three expert tiles, last block 37 tokens
+    (16384, 128, 8, 2, "none"),    # four tiles, whole blocks
+    (50000, 64, 64, 8, "gauss"),   # four tiles, 782 blocks feeding the statistics
+])
+def test_route_multi_tile_blocks(T, d, E, k, sel):
+    """The single-launch router's larger blocks (two or four 16-token tiles,
+    taken from 8192 and 16384 tokens on) against the oracle on every token,
+    with ragged last blocks, and bitwise equal on a second call."""
+    w = wl.scaled(wl.get(2), name="route-tt", T=T, d=d, E=E, k=k, router_bias="gauss", sel_bias=sel)
+    inp = wl.make_layer(w, seed=5, with_experts=False)
+    x = wl.to_torch(inp.x, DEV)
+    wr = wl.to_torch(inp.w_router, DEV)
+    br = wl.to_torch(inp.b_router, DEV)
+    sb = wl.to_torch(inp.sel_bias, DEV)
+    r = api.moe_route(x, wr, br, k, w.alpha, sel_bias=sb)
+    r2 = api.moe_route(x, wr, br, k, w.alpha, sel_bias=sb)
+    torch.cuda.synchronize()
+    ref = oracle.route(inp.x, inp.w_router, inp.b_router, k, sel_bias=inp.sel_bias)
+    _check_route(w, inp, r, ref)
+    for key in r:
+        assert torch.equal(r[key], r2[key]), key
+
+
 def test_route_sel_bias_full_size():
     """The DeepSeek-shaped router (T=32768, d=7168, E=256, top-8, the E > 64
     path) with a selection-only bias, against the oracle on every token."""

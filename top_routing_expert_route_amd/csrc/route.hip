@@ -158,10 +158,13 @@ __global__ __launch_bounds__(256) void route_logits_mfma(const uint16_t *__restr
 // ----------------------------------------------------------------------------
 // Single-launch router for bf16 activations and E <= 64 experts.
 //
-// One block of eight waves scores kRouteTB = 16 tokens.  The eight waves split
-// the hidden dimension; per 32-wide K step a wave runs v_mfma_f32_16x16x32_bf16
-// with the weight rows as the A operand (16 experts per row tile, ET tiles) and
-// the 16 tokens as the B operand.  The fp32 router weight is split on the fly,
+// One block of eight waves scores TT tiles of kRouteTB = 16 tokens (TT = 1, 2
+// or 4, chosen from T so that the grid still covers the chip: every block
+// reads and splits the whole router weight, so fewer, larger blocks do less of
+// that).  The eight waves split the hidden dimension; per 32-wide K step a
+// wave runs v_mfma_f32_16x16x32_bf16 with the weight rows as the A operand (16
+// experts per row tile, ET tiles) and each token tile as the B operand, the
+// weight split once for all TT tiles.  The fp32 router weight is split on the fly,
 // exactly, into three bf16 pieces (hi = w truncated to bf16, mid = (w - hi)
 // truncated, lo = w - hi - mid, at most 8 significant bits), each product with
 // a bf16 activation is exact in fp32, and the three MFMAs accumulate into the
@@ -316,7 +319,7 @@ __device__ __forceinline__ void reset_ticket(unsigned *ticket)
         __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int ET, int CH, int G>
+template <int ET, int TT, int CH, int G>
 __global__ __launch_bounds__(64 * kRouteWaves) void route_fused(
     const uint16_t *__restrict__ x, const float *__restrict__ wr, const float *__restrict__ bias,
     const float *__restrict__ sel, int64_t T, int d, int E, int k, float alpha, int32_t *__restrict__ topk_idx,
@@ -326,8 +329,9 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_fused(
 {
     constexpr int EB = 16 * ET;
     constexpr int LS = EB + 1;
+    constexpr int TB = kRouteTB * TT;
     __shared__ float red[kRouteWaves][ET][4][64];
-    __shared__ float lg[kRouteTB][LS];
+    __shared__ float lg[TB][LS];
     __shared__ int cnt[EB];
     __shared__ int s_flag;
     __shared__ double rp[64 * kRouteWaves];
@@ -337,7 +341,7 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_fused(
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, g = lane >> 4;
-    const int64_t t0 = (int64_t)blockIdx.x * kRouteTB;
+    const int64_t t0 = (int64_t)blockIdx.x * TB;
     if (tid < EB)
         cnt[tid] = 0;
 
@@ -349,7 +353,7 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_fused(
     const int nch = (nsteps + CH - 1) / CH;
 
     // token rows of the block and the router weight as range-checked records
-    const int64_t trows = min((int64_t)kRouteTB, T - t0);
+    const int64_t trows = min((int64_t)TB, T - t0);
     const __amdgpu_buffer_rsrc_t xr = raw_rsrc(x + t0 * d, (uint32_t)(trows * d * 2));
     const __amdgpu_buffer_rsrc_t wrr = raw_rsrc(wr, (uint32_t)((int64_t)E * d * 4));
     const uint32_t xoff0 = (uint32_t)(n * d * 2);
@@ -360,22 +364,27 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_fused(
         woff0[a] = e < E ? (uint32_t)(e * d * 4) : kOutOfRange;
     }
 
-    f32x4 acc[ET];
+    f32x4 acc[ET][TT];
 #pragma unroll
     for (int a = 0; a < ET; ++a)
-        acc[a] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < TT; ++u)
+            acc[a][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // Offsets are made opaque before the loads (empty asm on the register):
     // otherwise the compiler may turn the out-of-range select into divergent
     // branches around duplicated loads and drain the load counter there.
-    auto load = [&](int c, u32x4 (&xv)[CH], f32x4 (&wv)[CH][ET][2]) {
+    auto load = [&](int c, u32x4 (&xv)[CH][TT], f32x4 (&wv)[CH][ET][2]) {
 #pragma unroll
         for (int s = 0; s < CH; ++s) {
             const int kk = kbeg + (c * CH + s) * 32 + 8 * g;
             const bool ok = kk < kend;
-            uint32_t xo = ok ? xoff0 + (uint32_t)kk * 2u : kOutOfRange;
-            asm volatile("" : "+v"(xo));
-            xv[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo, 0, 0));
+#pragma unroll
+            for (int u = 0; u < TT; ++u) {
+                uint32_t xo = ok ? xoff0 + (uint32_t)(16 * u * d + kk) * 2u : kOutOfRange;
+                asm volatile("" : "+v"(xo));
+                xv[s][u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, xo, 0, 0));
+            }
 #pragma unroll
             for (int a = 0; a < ET; ++a) {
                 uint32_t o0 = (ok && woff0[a] != kOutOfRange) ? woff0[a] + (uint32_t)kk * 4u : kOutOfRange;
@@ -386,10 +395,9 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_fused(
             }
         }
     };
-    auto compute = [&](const u32x4 (&xv)[CH], const f32x4 (&wv)[CH][ET][2]) {
+    auto compute = [&](const u32x4 (&xv)[CH][TT], const f32x4 (&wv)[CH][ET][2]) {
 #pragma unroll
         for (int s = 0; s < CH; ++s) {
-            const bf16x8 xb = __builtin_bit_cast(bf16x8, xv[s]);
 #pragma unroll
             for (int a = 0; a < ET; ++a) {
                 bf16x8 hi, mid, lo;
@@ -403,9 +411,13 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_fused(
                     mid[q] = bits_bf16(m);
                     lo[q] = bits_bf16(r1 - m);        // exact, <= 8 significant bits
                 }
-                acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, xb, acc[a], 0, 0, 0);
-                acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, xb, acc[a], 0, 0, 0);
-                acc[a] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, xb, acc[a], 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < TT; ++u) {
+                    const bf16x8 xb = __builtin_bit_cast(bf16x8, xv[s][u]);
+                    acc[a][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, xb, acc[a][u], 0, 0, 0);
+                    acc[a][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, xb, acc[a][u], 0, 0, 0);
+                    acc[a][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, xb, acc[a][u], 0, 0, 0);
+                }
             }
         }
     };
@@ -413,7 +425,7 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_fused(
     {
         // two register chunks in flight; a chunk past the wave's range loads
         // nothing (every offset out of range) and adds zeros
-        u32x4 xa[CH], xb2[CH];
+        u32x4 xa[CH][TT], xb2[CH][TT];
         f32x4 wa[CH][ET][2], wb[CH][ET][2];
         load(0, xa, wa);
         for (int c = 0; c < nch; c += 2) {
@@ -428,28 +440,32 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_fused(
         }
     }
 
-    // partial tiles: lane holds experts 16a + 4g + v of token n
+    // partial tiles, one token tile at a time: lane holds experts 16a + 4g + v
+    // of token 16u + n
 #pragma unroll
-    for (int a = 0; a < ET; ++a)
+    for (int u = 0; u < TT; ++u) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-            red[wave][a][v][lane] = acc[a][v];
-    __syncthreads();
-    for (int q = tid; q < ET * 256; q += 64 * kRouteWaves) {
-        const int a = q >> 8, v = (q >> 6) & 3, l = q & 63;
-        float sum = red[0][a][v][l];
+        for (int a = 0; a < ET; ++a)
 #pragma unroll
-        for (int w = 1; w < kRouteWaves; ++w)
-            sum += red[w][a][v][l];
-        const int e = 16 * a + 4 * (l >> 4) + v;
-        if (e < E)
-            lg[l & 15][e] = sum + (bias ? bias[e] : 0.f);
+            for (int v = 0; v < 4; ++v)
+                red[wave][a][v][lane] = acc[a][u][v];
+        __syncthreads();
+        for (int q = tid; q < ET * 256; q += 64 * kRouteWaves) {
+            const int a = q >> 8, v = (q >> 6) & 3, l = q & 63;
+            float sum = red[0][a][v][l];
+#pragma unroll
+            for (int w = 1; w < kRouteWaves; ++w)
+                sum += red[w][a][v][l];
+            const int e = 16 * a + 4 * (l >> 4) + v;
+            if (e < E)
+                lg[16 * u + (l & 15)][e] = sum + (bias ? bias[e] : 0.f);
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
     // softmax and top-k: G lanes per token
-    for (int base = 0; base < kRouteTB * G; base += 64 * kRouteWaves) {
-        if ((base + wave * 64) / G >= kRouteTB)
+    for (int base = 0; base < TB * G; base += 64 * kRouteWaves) {
+        if ((base + wave * 64) / G >= TB)
             break; // wave-uniform: no token left for this wave
         const int idx = base + tid;
         const int tl = idx / G, e = idx % G;
@@ -487,7 +503,7 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_fused(
     // this block's partial row: counts, probabilities summed in token order
     for (int e = tid; e < E; e += 64 * kRouteWaves) {
         float ps = 0.f;
-        for (int q = 0; q < kRouteTB; ++q)
+        for (int q = 0; q < TB; ++q)
             ps += lg[q][e];
         publish(part_p + (int64_t)blockIdx.x * E + e, ps);
         publish(part_c + (int64_t)blockIdx.x * E + e, (int32_t)cnt[e]);
@@ -760,10 +776,18 @@ static int select_blocks(int64_t T) { return (int)((T + kSelTokensPerBlock - 1) 
 // kernel) + route_select + the partial-sum reduction.
 static bool route_is_fused(moe_dtype_t dt, int E) { return dt == MOE_BF16 && E <= 64; }
 
+// Token tiles of 16 per block of the single-launch router.  Every block reads
+// and splits the whole fp32 router weight, so a block scores as many tokens as
+// still leaves a block for each of the 256 compute units: 64 from 16384
+// tokens, 32 from 8192, else 16.
+static int route_tt(int64_t T) { return T >= 256 * 64 ? 4 : (T >= 256 * 32 ? 2 : 1); }
+
 static int route_blocks(int64_t T, int E, moe_dtype_t dt)
 {
-    if (route_is_fused(dt, E))
-        return (int)((T + kRouteTB - 1) / kRouteTB);
+    if (route_is_fused(dt, E)) {
+        const int tb = kRouteTB * route_tt(T);
+        return (int)((T + tb - 1) / tb);
+    }
     return select_blocks(T);
 }
 
@@ -793,15 +817,46 @@ size_t route_ws_bytes(int64_t T, int d, int E, moe_dtype_t dt)
     return b;
 }
 
-template <int ET, int CH, int G>
-static void launch_fused(const uint16_t *x, const float *w_router, const float *b_router, const float *sel_bias,
-                         int64_t T, int d, int E, int k, float alpha, int32_t *topk_idx, float *topk_w, float *probs,
-                         float *part_p, int32_t *part_c, unsigned *ticket, int32_t *expert_count, float *f, float *P,
-                         float *l_aux, int nblk, hipStream_t stream)
+template <int ET, int TT, int CH, int G>
+static void launch_fused1(const uint16_t *x, const float *w_router, const float *b_router, const float *sel_bias,
+                          int64_t T, int d, int E, int k, float alpha, int32_t *topk_idx, float *topk_w,
+                          float *probs, float *part_p, int32_t *part_c, unsigned *ticket, int32_t *expert_count,
+                          float *f, float *P, float *l_aux, int nblk, hipStream_t stream)
 {
-    route_fused<ET, CH, G><<<(unsigned)nblk, 64 * kRouteWaves, 0, stream>>>(
+    route_fused<ET, TT, CH, G><<<(unsigned)nblk, 64 * kRouteWaves, 0, stream>>>(
         x, w_router, b_router, sel_bias, T, d, E, k, alpha, topk_idx, topk_w, probs, part_p, part_c, ticket,
         expert_count, f, P, l_aux);
+}
+
+// K steps per register chunk: the largest power of two up to ch0 whose two
+// chunks in flight (x of TT token tiles, two fp32 vectors of each of the ET
+// weight tiles) and the accumulators fit the register file without spilling.
+constexpr int route_ch(int ch0, int ET, int TT)
+{
+    const int per = 4 * TT + 4 * ET * 2;
+    int ch = ch0;
+    while (ch > 1 && 2 * ch * per + 4 * ET * TT > 232)
+        ch /= 2;
+    return ch;
+}
+
+template <int ET, int CH, int G>
+static void launch_fused(int tt, const uint16_t *x, const float *w_router, const float *b_router,
+                         const float *sel_bias, int64_t T, int d, int E, int k, float alpha, int32_t *topk_idx,
+                         float *topk_w, float *probs, float *part_p, int32_t *part_c, unsigned *ticket,
+                         int32_t *expert_count, float *f, float *P, float *l_aux, int nblk, hipStream_t stream)
+{
+#define MOE_F1(TT)                                                                                                  \
+    launch_fused1<ET, TT, route_ch(CH, ET, TT), G>(x, w_router, b_router, sel_bias, T, d, E, k, alpha, topk_idx,    \
+                                                   topk_w, probs, part_p, part_c, ticket, expert_count, f, P, l_aux, \
+                                                   nblk, stream)
+    if (tt == 4)
+        MOE_F1(4);
+    else if (tt == 2)
+        MOE_F1(2);
+    else
+        MOE_F1(1);
+#undef MOE_F1
 }
 
 moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, const float *b_router,
@@ -823,8 +878,8 @@ moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, 
         int32_t *part_c = cv.take<int32_t>((size_t)nblk * E);
         const uint16_t *xb = (const uint16_t *)x;
 #define MOE_FUSED(ET, CH, G)                                                                                         \
-    launch_fused<ET, CH, G>(xb, w_router, b_router, sel_bias, T, d, E, k, alpha, topk_idx, topk_w, probs, part_p,   \
-                            part_c, ticket, expert_count, f, P, l_aux, nblk, stream)
+    launch_fused<ET, CH, G>(route_tt(T), xb, w_router, b_router, sel_bias, T, d, E, k, alpha, topk_idx, topk_w, probs,    \
+                            part_p, part_c, ticket, expert_count, f, P, l_aux, nblk, stream)
         if (E <= 8)
             MOE_FUSED(1, 8, 8);
         else if (E <= 16)
