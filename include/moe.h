@@ -107,8 +107,9 @@ int64_t moe_max_rows(int64_t T, int E, int k, float capacity_factor, int num_loc
  *   l_aux[0] = alpha * sum_e f[e] * P[e]     (alpha: 0.01 is the usual value)
  * The reductions over tokens run in a fixed order: results are bitwise
  * reproducible run to run.  With bf16 activations and E <= 64 the whole call
- * is one kernel launch: the last block to finish sums the per-block partial
- * statistics (in a fixed order), using the workspace's arrival counter.
+ * is one kernel launch: the blocks' partial statistics are summed in a fixed
+ * order, in groups of blocks and then over the groups, by the last blocks to
+ * finish, using the workspace's arrival counters.
  *
  * x [T,d] (dtype), w_router [E,d] f32, b_router [E] f32 or NULL (zero bias),
  * sel_bias [E] f32 or NULL (plain top-k).

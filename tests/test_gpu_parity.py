@@ -517,12 +517,15 @@ def test_route_leaves_workspace_counters_zero():
     (8223, 520, 16, 4, "gauss"),   # two tiles, ragged K range per wave, selection bias
     (16421, 200, 33, 3, "none"),   # four tiles, three expert tiles, last block 37 tokens
     (16384, 128, 8, 2, "none"),    # four tiles, whole blocks
-    (50000, 64, 64, 8, "gauss"),   # four tiles, 782 blocks feeding the statistics
+    (50000, 64, 64, 8, "gauss"),   # four tiles, 782 blocks: statistics in 28 groups of 28
+    (300007, 64, 64, 2, "none"),   # 4688 blocks: 63 groups (the counter limit), ragged last group
 ])
 def test_route_multi_tile_blocks(T, d, E, k, sel):
     """The single-launch router's larger blocks (two or four 16-token tiles,
-    taken from 8192 and 16384 tokens on) against the oracle on every token,
-    with ragged last blocks, and bitwise equal on a second call."""
+    taken from 8192 and 16384 tokens on) and its two-level statistics (block
+    groups, then the groups) against the oracle on every token, with ragged
+    last blocks and groups; bitwise equal on a second call, and the
+    workspace's arrival counters back at zero."""
     w = wl.scaled(wl.get(2), name="route-tt", T=T, d=d, E=E, k=k, router_bias="gauss", sel_bias=sel)
     inp = wl.make_layer(w, seed=5, with_experts=False)
     x = wl.to_torch(inp.x, DEV)
@@ -536,6 +539,8 @@ def test_route_multi_tile_blocks(T, d, E, k, sel):
     _check_route(w, inp, r, ref)
     for key in r:
         assert torch.equal(r[key], r2[key]), key
+    ws = api.workspace(x.device, 0)
+    assert int(ws[:256].count_nonzero().item()) == 0
 
 
 def test_route_sel_bias_full_size():

@@ -166,7 +166,7 @@ ForwardWs carve_forward(const moe_problem_t *p, const moe_outputs_t *out, void *
     const int64_t max_rows = moe_max_rows(p->T, p->E, p->k, p->capacity_factor, p->num_local_experts);
     const size_t es = elem_size(p->dtype);
     const int64_t Tk = p->T * p->k;
-    Carver cv{(char *)base, kCtrlBytes}; // [0, kCtrlBytes): the router's arrival counter
+    Carver cv{(char *)base, kCtrlBytes}; // [0, kCtrlBytes): the router's arrival counters
     ForwardWs w;
     w.topk_idx = out->topk_idx ? out->topk_idx : cv.take<int32_t>((size_t)Tk);
     w.topk_w = out->topk_w ? out->topk_w : cv.take<float>((size_t)Tk);
@@ -227,7 +227,7 @@ int64_t moe_max_rows(int64_t T, int E, int k, float capacity_factor, int num_loc
     return rows;
 }
 
-// Route workspaces: the arrival counter in the control bytes, then the
+// Route workspaces: the arrival counters in the control bytes, then the
 // partial rows (and, off the single-launch path, logits and chunk sums).
 static size_t route_ws_total(int64_t T, int d, int E, moe_dtype_t dt)
 {
@@ -615,7 +615,7 @@ BackwardWs carve_backward(const moe_problem_t *p, const moe_grads_t *g, void *ba
     const size_t es = elem_size(p->dtype);
     const int64_t Tk = p->T * p->k;
     const int64_t kp_r = kseg_cols_bound(max_rows, E_loc), kp_s = p->has_shared ? kseg_cols_bound(p->T, 1) : 0;
-    Carver cv{(char *)base, kCtrlBytes}; // [0, kCtrlBytes): the router's arrival counter
+    Carver cv{(char *)base, kCtrlBytes}; // [0, kCtrlBytes): the router's arrival counters
     BackwardWs w;
     w.Kp = kp_r > kp_s ? kp_r : kp_s;
     w.topk_idx = cv.take<int32_t>((size_t)Tk);

@@ -167,9 +167,10 @@ struct Carver {
 // The rest of the workspace is carved from kCtrlBytes on.
 constexpr size_t kCtrlBytes = 256;
 
-// Router workspace (after the control bytes) and launcher.  `ticket` is the
-// arrival counter of the single-launch router (zero on entry, zero again
-// when the launch completes); probs [T, E] fp32 softmax output, or NULL.
+// Router workspace (after the control bytes) and launcher.  `ticket` points at
+// the control bytes: the 64 arrival counters of the single-launch router
+// (zero on entry, zero again when the launch completes); probs [T, E] fp32
+// softmax output, or NULL.
 size_t route_ws_bytes(int64_t T, int d, int E, moe_dtype_t dt);
 size_t gemm_ws_bytes();
 moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, const float *b_router,

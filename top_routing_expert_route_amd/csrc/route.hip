@@ -248,12 +248,14 @@ template <class V> __device__ __forceinline__ V collect(const V *p)
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Fixed-order sum of the per-block partial rows by the last block (any
-// blockDim.x >= E): G2 threads per expert take rows g, g + G2, ... in double,
-// then thread e adds its G2 sums in order.
-__device__ void finalize_stats(const float *part_p, const int32_t *part_c, int nrows, int64_t T, int E, float alpha,
-                               int32_t *expert_count, float *f, float *P, float *l_aux, double *rp, long long *rc,
-                               double *terms)
+// Fixed-order sums of partial rows [r0, r1) (E values each; any blockDim.x >=
+// E): G2 threads per expert take rows r0 + g, r0 + g + G2, ... (four at a time,
+// so that their coherent loads are in flight together) in double and int64,
+// then thread e adds its G2 sums in order into sp[e], sc[e].  Every thread
+// sees sp and sc after the call.
+template <class TP, class TC>
+__device__ void sum_rows(const TP *pp, const TC *pc, int64_t r0, int64_t r1, int E, double *rp, long long *rc,
+                         double *sp, long long *sc)
 {
     const int nt = blockDim.x, tid = threadIdx.x;
     int G2 = 1;
@@ -263,9 +265,24 @@ __device__ void finalize_stats(const float *part_p, const int32_t *part_c, int n
     double ps = 0.0;
     long long cs = 0;
     if (e < E) {
-        for (int b = g; b < nrows; b += G2) {
-            ps += (double)collect(part_p + (int64_t)b * E + e);
-            cs += collect(part_c + (int64_t)b * E + e);
+        int64_t b = r0 + g;
+        for (; b + 3 * G2 < r1; b += 4 * G2) {
+            TP pv[4];
+            TC cv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                pv[u] = collect(pp + (b + u * G2) * E + e);
+                cv[u] = collect(pc + (b + u * G2) * E + e);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                ps += (double)pv[u];
+                cs += (long long)cv[u];
+            }
+        }
+        for (; b < r1; b += G2) {
+            ps += (double)collect(pp + b * E + e);
+            cs += (long long)collect(pc + b * E + e);
         }
     }
     if (tid < G2 * E) {
@@ -280,8 +297,68 @@ __device__ void finalize_stats(const float *part_p, const int32_t *part_c, int n
             p += rp[q * G2 + i];
             c += rc[q * G2 + i];
         }
+        sp[q] = p;
+        sc[q] = c;
+    }
+    __syncthreads();
+}
+
+// True in every thread of the block whose increment of `counter` is the n-th
+// (the last of n arrivals); that block also resets the counter to zero.  Call
+// after the block's published stores were issued (every thread): each thread
+// waits for its stores to complete before the block arrives.
+__device__ __forceinline__ bool arrived_last(unsigned *counter, unsigned n, int *s_flag)
+{
+    asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); // this thread's published stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const unsigned old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = old == n - 1;
+        if (last)
+            __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = last ? 1 : 0;
+    }
+    __syncthreads();
+    return *s_flag != 0;
+}
+
+// Statistics from the blocks' partial rows, in two fixed-order levels: the
+// blocks form groups of gsz consecutive blocks; the last block of a group to
+// arrive (counter 1 + group) sums the group's rows and publishes a group row
+// (double, int64); the last group to finish (counter 0) sums the group rows
+// in group order and writes counts, f, P and L_aux.  Each collecting block
+// reads gsz or ngroups rows instead of one block reading every row.  With one
+// group the last block sums the rows directly.  Every counter is back at zero
+// when the launch completes.
+__device__ void finish_stats(const float *part_p, const int32_t *part_c, int gsz, double *grp_p, long long *grp_c,
+                             unsigned *counters, int64_t T, int E, float alpha, int32_t *expert_count, float *f,
+                             float *P, float *l_aux, double *rp, long long *rc, double *sp, long long *sc,
+                             double *terms, int *s_flag)
+{
+    const int nb = (int)gridDim.x, tid = threadIdx.x, nt = blockDim.x;
+    const int ng = (nb + gsz - 1) / gsz;
+    if (ng > 1) {
+        const int g = (int)blockIdx.x / gsz;
+        const int r0 = g * gsz, r1 = min(nb, r0 + gsz);
+        if (!arrived_last(counters + 1 + g, (unsigned)(r1 - r0), s_flag))
+            return;
+        sum_rows(part_p, part_c, r0, r1, E, rp, rc, sp, sc);
+        for (int q = tid; q < E; q += nt) {
+            publish(grp_p + (int64_t)g * E + q, sp[q]);
+            publish(grp_c + (int64_t)g * E + q, sc[q]);
+        }
+        if (!arrived_last(counters, (unsigned)ng, s_flag))
+            return;
+        sum_rows(grp_p, grp_c, 0, ng, E, rp, rc, sp, sc);
+    } else {
+        if (!arrived_last(counters, (unsigned)nb, s_flag))
+            return;
+        sum_rows(part_p, part_c, 0, nb, E, rp, rc, sp, sc);
+    }
+    for (int q = tid; q < E; q += nt) {
+        const long long c = sc[q];
         const float fe = T > 0 ? (float)c / (float)T : 0.f;
-        const float Pe = T > 0 ? (float)(p / (double)T) : 0.f;
+        const float Pe = T > 0 ? (float)(sp[q] / (double)T) : 0.f;
         if (expert_count)
             expert_count[q] = (int32_t)c;
         if (f)
@@ -299,33 +376,13 @@ __device__ void finalize_stats(const float *part_p, const int32_t *part_c, int n
     }
 }
 
-// True in every thread of the block that arrives last.  Call after the
-// block's partial row was published (every thread).
-__device__ __forceinline__ bool last_block_arrived(unsigned *ticket, int *s_flag)
-{
-    asm volatile("s_waitcnt vmcnt(0)" : : : "memory"); // this thread's published stores are complete
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const unsigned old = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *s_flag = old == gridDim.x - 1 ? 1 : 0;
-    }
-    __syncthreads();
-    return *s_flag != 0;
-}
-
-__device__ __forceinline__ void reset_ticket(unsigned *ticket)
-{
-    if (threadIdx.x == 0)
-        __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 template <int ET, int TT, int CH, int G>
 __global__ __launch_bounds__(64 * kRouteWaves) void route_fused(
     const uint16_t *__restrict__ x, const float *__restrict__ wr, const float *__restrict__ bias,
     const float *__restrict__ sel, int64_t T, int d, int E, int k, float alpha, int32_t *__restrict__ topk_idx,
     float *__restrict__ topk_w, float *__restrict__ probs, float *__restrict__ part_p, int32_t *__restrict__ part_c,
-    unsigned *__restrict__ ticket, int32_t *__restrict__ expert_count, float *__restrict__ f, float *__restrict__ P,
-    float *__restrict__ l_aux)
+    int gsz, double *__restrict__ grp_p, long long *__restrict__ grp_c, unsigned *__restrict__ counters,
+    int32_t *__restrict__ expert_count, float *__restrict__ f, float *__restrict__ P, float *__restrict__ l_aux)
 {
     constexpr int EB = 16 * ET;
     constexpr int LS = EB + 1;
@@ -336,7 +393,8 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_fused(
     __shared__ int s_flag;
     __shared__ double rp[64 * kRouteWaves];
     __shared__ long long rc[64 * kRouteWaves];
-    __shared__ double terms[64];
+    __shared__ double sp[64], terms[64];
+    __shared__ long long sc[64];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -508,10 +566,8 @@ __global__ __launch_bounds__(64 * kRouteWaves) void route_fused(
         publish(part_p + (int64_t)blockIdx.x * E + e, ps);
         publish(part_c + (int64_t)blockIdx.x * E + e, (int32_t)cnt[e]);
     }
-    if (!last_block_arrived(ticket, &s_flag))
-        return;
-    finalize_stats(part_p, part_c, (int)gridDim.x, T, E, alpha, expert_count, f, P, l_aux, rp, rc, terms);
-    reset_ticket(ticket);
+    finish_stats(part_p, part_c, gsz, grp_p, grp_c, counters, T, E, alpha, expert_count, f, P, l_aux, rp, rc, sp, sc,
+                 terms, &s_flag);
 }
 
 // w3[p*E + e, i] = bf16 piece p of w_router[e, i]: hi = w truncated to bf16,
@@ -782,6 +838,21 @@ static bool route_is_fused(moe_dtype_t dt, int E) { return dt == MOE_BF16 && E <
 // tokens, 32 from 8192, else 16.
 static int route_tt(int64_t T) { return T >= 256 * 64 ? 4 : (T >= 256 * 32 ? 2 : 1); }
 
+// Blocks per group of the single-launch router's two-level statistics: about
+// sqrt(blocks), so that a group's collection and the final one are about as
+// long, with at most 63 groups (the workspace's counters 1..63).  Below 8192
+// partial values (blocks x E) one group: the last block's collection is short
+// enough that a second arrival round would cost more than it saves.
+static int route_group_size(int nblk, int E)
+{
+    if ((int64_t)nblk * E < 8192)
+        return nblk;
+    int g = (int)ceil(sqrt((double)nblk));
+    if ((nblk + g - 1) / g > 63)
+        g = (nblk + 62) / 63;
+    return g;
+}
+
 static int route_blocks(int64_t T, int E, moe_dtype_t dt)
 {
     if (route_is_fused(dt, E)) {
@@ -805,8 +876,10 @@ size_t route_ws_bytes(int64_t T, int d, int E, moe_dtype_t dt)
         return 0;
     const int nblk = route_blocks(T, E, dt);
     const size_t parts = 2 * align_up((size_t)nblk * E * sizeof(float));
-    if (route_is_fused(dt, E))
-        return parts;
+    if (route_is_fused(dt, E)) {
+        const int gsz = route_group_size(nblk, E);
+        return parts + 2 * align_up((size_t)((nblk + gsz - 1) / gsz) * E * 8);
+    }
     // logits, partials, chunk sums, plus the split router weight and the
     // grouped GEMM's tail partials when the logits run on it
     const bool on_gemm = router_on_gemm(dt, d, E);
@@ -820,12 +893,13 @@ size_t route_ws_bytes(int64_t T, int d, int E, moe_dtype_t dt)
 template <int ET, int TT, int CH, int G>
 static void launch_fused1(const uint16_t *x, const float *w_router, const float *b_router, const float *sel_bias,
                           int64_t T, int d, int E, int k, float alpha, int32_t *topk_idx, float *topk_w,
-                          float *probs, float *part_p, int32_t *part_c, unsigned *ticket, int32_t *expert_count,
-                          float *f, float *P, float *l_aux, int nblk, hipStream_t stream)
+                          float *probs, float *part_p, int32_t *part_c, int gsz, double *grp_p, long long *grp_c,
+                          unsigned *ticket, int32_t *expert_count, float *f, float *P, float *l_aux, int nblk,
+                          hipStream_t stream)
 {
     route_fused<ET, TT, CH, G><<<(unsigned)nblk, 64 * kRouteWaves, 0, stream>>>(
-        x, w_router, b_router, sel_bias, T, d, E, k, alpha, topk_idx, topk_w, probs, part_p, part_c, ticket,
-        expert_count, f, P, l_aux);
+        x, w_router, b_router, sel_bias, T, d, E, k, alpha, topk_idx, topk_w, probs, part_p, part_c, gsz, grp_p,
+        grp_c, ticket, expert_count, f, P, l_aux);
 }
 
 // K steps per register chunk: the largest power of two up to ch0 whose two
@@ -843,13 +917,14 @@ constexpr int route_ch(int ch0, int ET, int TT)
 template <int ET, int CH, int G>
 static void launch_fused(int tt, const uint16_t *x, const float *w_router, const float *b_router,
                          const float *sel_bias, int64_t T, int d, int E, int k, float alpha, int32_t *topk_idx,
-                         float *topk_w, float *probs, float *part_p, int32_t *part_c, unsigned *ticket,
-                         int32_t *expert_count, float *f, float *P, float *l_aux, int nblk, hipStream_t stream)
+                         float *topk_w, float *probs, float *part_p, int32_t *part_c, int gsz, double *grp_p,
+                         long long *grp_c, unsigned *ticket, int32_t *expert_count, float *f, float *P, float *l_aux,
+                         int nblk, hipStream_t stream)
 {
 #define MOE_F1(TT)                                                                                                  \
     launch_fused1<ET, TT, route_ch(CH, ET, TT), G>(x, w_router, b_router, sel_bias, T, d, E, k, alpha, topk_idx,    \
-                                                   topk_w, probs, part_p, part_c, ticket, expert_count, f, P, l_aux, \
-                                                   nblk, stream)
+                                                   topk_w, probs, part_p, part_c, gsz, grp_p, grp_c, ticket,         \
+                                                   expert_count, f, P, l_aux, nblk, stream)
     if (tt == 4)
         MOE_F1(4);
     else if (tt == 2)
@@ -876,10 +951,15 @@ moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, 
     if (route_is_fused(dt, E)) {
         float *part_p = cv.take<float>((size_t)nblk * E);
         int32_t *part_c = cv.take<int32_t>((size_t)nblk * E);
+        const int gsz = route_group_size(nblk, E);
+        const int ng = (nblk + gsz - 1) / gsz;
+        double *grp_p = cv.take<double>((size_t)ng * E);
+        long long *grp_c = cv.take<long long>((size_t)ng * E);
         const uint16_t *xb = (const uint16_t *)x;
 #define MOE_FUSED(ET, CH, G)                                                                                         \
-    launch_fused<ET, CH, G>(route_tt(T), xb, w_router, b_router, sel_bias, T, d, E, k, alpha, topk_idx, topk_w, probs,    \
-                            part_p, part_c, ticket, expert_count, f, P, l_aux, nblk, stream)
+    launch_fused<ET, CH, G>(route_tt(T), xb, w_router, b_router, sel_bias, T, d, E, k, alpha, topk_idx, topk_w,     \
+                            probs, part_p, part_c, gsz, grp_p, grp_c, ticket, expert_count, f, P, l_aux, nblk,       \
+                            stream)
         if (E <= 8)
             MOE_FUSED(1, 8, 8);
         else if (E <= 16)
