@@ -591,6 +591,39 @@ def test_gelu_epilogue_matches_fp64_erf():
     assert ((ob[:, 0].cpu().double() - refb).abs() <= 2.0 ** -8 * refb.abs() + 1e-6).all()
 
 
+@pytest.mark.parametrize("sizes,split", [
+    # 17 non-empty segments of at most one row tile x 8 feature tiles = 136
+    # tiles on a 256-block grid: more than half a round, so three K ranges per
+    # tile and two units per block (the capacity-drop layer's second GEMM)
+    ([160] * 6 + [92, 55, 12, 17, 7, 6, 0, 4, 4, 1, 1, 1], True),
+    # 200 tiles: more than two thirds of a round, not split
+    ([100] * 25, False),
+])
+def test_grouped_gemm_tail_two_units_per_block(sizes, split):
+    """The split-K tail with several units per block: against the fp64
+    product (bias, GELU) within bf16 rounding, bitwise reproducible, and, when
+    the plan does not split, bitwise equal to the call without a workspace."""
+    g = torch.Generator().manual_seed(11)
+    rows, K, N = sum(sizes), 1536, 2048
+    S = len(sizes)
+    a = torch.randn(rows, K, generator=g).to(torch.bfloat16).to(DEV)
+    w = (torch.randn(S, N, K, generator=g) / K ** 0.5).to(torch.bfloat16).to(DEV)
+    b = (torch.randn(S, N, generator=g) * 0.1).to(torch.bfloat16).to(DEV)
+    seg = torch.tensor(np.concatenate([[0], np.cumsum(sizes)]), dtype=torch.int32, device=DEV)
+    whole = api.moe_grouped_gemm(a, seg, w, b, 1, use_ws=False)
+    s1 = api.moe_grouped_gemm(a, seg, w, b, 1)
+    s2 = api.moe_grouped_gemm(a, seg, w, b, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(s1.view(torch.int16), s2.view(torch.int16))
+    if not split:
+        assert torch.equal(s1.view(torch.int16), whole.view(torch.int16))
+    ref = torch.cat([torch.nn.functional.gelu(a[lo:hi].double() @ w[s].double().T + b[s].double(),
+                                              approximate="none")
+                     for s, (lo, hi) in enumerate(zip(seg[:-1].tolist(), seg[1:].tolist()))])
+    assert rel_err(s1.float().cpu().numpy(), ref.cpu().numpy()) <= 1e-2
+    assert rel_err(whole.float().cpu().numpy(), ref.cpu().numpy()) <= 1e-2
+
+
 def test_grouped_gemm_split_tail_matches_whole_tiles():
     """With a workspace, tail tiles are split along K and reduced in a fixed
     order: equal to the unsplit result within bf16 rounding, and bitwise

@@ -509,31 +509,45 @@ __device__ __forceinline__ void store_tile_bf16_lds(const f32x16 (&acc)[G::FA][G
 }
 
 // Split of the tile list over a persistent grid of G blocks.  F whole tiles
-// run in full rounds (each block gets the same number); when the rest
-// (`rem` tiles, at most half a round) would leave CUs idle, each of them is
-// cut into `sk` K ranges of at least min_len steps, one per block, written as
-// fp32 partials and summed by grouped_gemm_reduce.  Computed identically by
-// both kernels.
+// run in full rounds (each block gets the same number); when the rest (`rem`
+// tiles) would leave CUs idle, each of them is cut into `sk` K ranges of at
+// least min_len steps (units u = sk * tile + range), written as fp32 partials
+// and summed by grouped_gemm_reduce.  Block b takes units b, b + G, ...: one
+// each when rem is at most half a round (sk up to 8); up to 2/3 of a round,
+// for tiles of at least kTailSplit3MinKT K steps, three ranges and at most two
+// units per block, so the last round takes two thirds of a tile's time
+// instead of a whole one (a fuller round is not split: two units of half a
+// tile gain nothing; with shorter tiles the third saved is less than the
+// partials' stores and the reduce cost).  The partial workspace holds 2G
+// tiles.  Computed identically by both kernels.
 struct TailPlan {
     int64_t F;
     int rem;
     int sk;
 };
 
+constexpr int kTailUnitsPerBlock = 2;
+constexpr int kTailSplit3MinKT = 64;
+
 __device__ __forceinline__ TailPlan plan_tail(int64_t total, int G, int KT, bool have_ws, int min_len)
 {
     TailPlan p{total, 0, 1};
     const int64_t R = total / G;
     const int64_t rem = total - R * G;
-    if (have_ws && rem > 0 && 2 * rem <= G) {
-        int sk = (int)(G / rem);
+    if (!have_ws || rem == 0)
+        return p;
+    int sk = 0;
+    if (2 * rem <= G) {
+        sk = (int)(G / rem);
         sk = sk > 8 ? 8 : sk;
-        sk = sk > KT / min_len ? KT / min_len : sk;
-        if (sk >= 2) {
-            p.F = R * G;
-            p.rem = (int)rem;
-            p.sk = sk;
-        }
+    } else if (3 * rem <= (int64_t)kTailUnitsPerBlock * G && KT >= kTailSplit3MinKT) {
+        sk = 3;
+    }
+    sk = sk > KT / min_len ? KT / min_len : sk;
+    if (sk >= 2) {
+        p.F = R * G;
+        p.rem = (int)rem;
+        p.sk = sk;
     }
     return p;
 }
@@ -846,7 +860,7 @@ struct WorkCtx {
     const int32_t *seg;
     const uint16_t *A, *W;
     int64_t max_rows, first, F;
-    int S, N, K, Ka, NT, KT, per, nw, unit, sk, n_work;
+    int S, N, K, Ka, NT, KT, per, nw, unit, ustride, sk, n_work;
     bool wt; // weight operand K-major
 };
 
@@ -860,11 +874,12 @@ __device__ __forceinline__ Work get_work(const WorkCtx &x, int i)
         w.kt_hi = x.KT;
         w.unit = -1;
     } else {
-        const int c = x.unit % x.sk;
-        w.t = locate(x.tb, x.seg, x.S, x.max_rows, x.NT, x.F + x.unit / x.sk);
+        const int u = x.unit + (i - x.nw) * x.ustride;
+        const int c = u % x.sk;
+        w.t = locate(x.tb, x.seg, x.S, x.max_rows, x.NT, x.F + u / x.sk);
         w.kt_lo = (int)((int64_t)x.KT * c / x.sk);
         w.kt_hi = (int)((int64_t)x.KT * (c + 1) / x.sk);
-        w.unit = x.unit;
+        w.unit = u;
     }
     w.t.s = uni(w.t.s);
     w.t.row0 = uni64(w.t.row0);
@@ -954,11 +969,12 @@ __device__ __forceinline__ int tile(uint16_t *smem, int b, const CopyGeo &cg, co
         b = bn;
     }
     if (PART) {
+        // only the row sub-tiles that hold rows (the reduce reads no others)
         float *dst = part + (size_t)wave * (FA * FB * 16 * 64) + lane;
 #pragma unroll
         for (int a = 0; a < FA; ++a)
 #pragma unroll
-            for (int q = 0; q < FB; ++q)
+            for (int q = 0; q < NBV; ++q)
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
                     dst[((a * FB + q) * 16 + v) * 64] = acc[a][q][v];
@@ -1051,8 +1067,10 @@ __global__ __launch_bounds__(64 * G::NW, 1) void grouped_gemm_256(const uint16_t
     x.first = rlo + blockIdx.x / kXcds;
     x.nw = x.first < rhi ? (int)((rhi - x.first + x.per - 1) / x.per) : 0;
     x.unit = blockIdx.x;
-    const bool has_tail = plan.rem > 0 && x.unit < plan.rem * plan.sk;
-    x.n_work = x.nw + (has_tail ? 1 : 0);
+    x.ustride = gridDim.x;
+    const int units = plan.rem * plan.sk;
+    const int ntail = x.unit < units ? (units - x.unit + x.ustride - 1) / x.ustride : 0;
+    x.n_work = x.nw + ntail;
     if (x.n_work == 0)
         return;
 
@@ -1425,9 +1443,11 @@ __global__ __launch_bounds__(256) void kseg_zero_empty(const int32_t *__restrict
 
 // Sums the K-range partials of each tail tile in range order and applies the
 // bias, activation and bf16 store; a no-op when the GEMM had no split tail.
-// Block = (tail tile, GEMM wave w); its FA waves take the feature sub-tiles
-// a and loop over the row sub-tiles b.  Each lane loads its 16 accumulators
-// of every K range up front (independent loads), then sums in range order.
+// Block = (tail tile, GEMM wave w), looping over the tail tiles with the
+// grid's stride; its FA waves take the feature sub-tiles a and loop over the
+// row sub-tiles b that hold rows (the only ones stored).  Each lane loads its
+// 16 accumulators of every K range up front (independent loads), then sums in
+// range order.
 template <class G, bool GELU, bool BIAS, bool F32OUT>
 __global__ __launch_bounds__(64 * G::FA) void grouped_gemm_reduce(const int32_t *__restrict__ seg, int S,
                                                                   int64_t max_rows, const uint16_t *__restrict__ bias,
@@ -1440,41 +1460,42 @@ __global__ __launch_bounds__(64 * G::FA) void grouped_gemm_reduce(const int32_t 
     const int NT = (N + kL - 1) / kL;
     const int64_t total = (int64_t)tb[S] * NT;
     const TailPlan plan = plan_tail(total, Gsize, K / BKused, true, min_len);
-    const int tile = blockIdx.x / G::NW, wave = blockIdx.x % G::NW;
-    if (plan.rem == 0 || tile >= plan.rem)
-        return;
+    const int wave = blockIdx.x % G::NW;
     const int lane = threadIdx.x & 63, a = threadIdx.x >> 6;
     const int wn = wave % G::WGN_, wm = wave / G::WGN_;
     const int r32 = lane & 31, khalf = lane >> 5;
-    const TileLoc t = locate(tb, seg, S, max_rows, NT, plan.F + tile);
-    const uint16_t *bseg = bias ? bias + (int64_t)t.s * N : nullptr;
-    const TileOut rt = tile_out<F32OUT>(C, t.row0, t.row_end, N);
-    for (int b = 0; b < G::FB; ++b) {
-        const float *src = part_ws + (size_t)tile * plan.sk * (kL * kL) +
-                           (size_t)wave * (G::FA * G::FB * 16 * 64) + (size_t)((a * G::FB + b) * 16) * 64 + lane;
-        float v[16];
+    for (int tile = blockIdx.x / G::NW; tile < plan.rem; tile += gridDim.x / G::NW) {
+        const TileLoc t = locate(tb, seg, S, max_rows, NT, plan.F + tile);
+        const uint16_t *bseg = bias ? bias + (int64_t)t.s * N : nullptr;
+        const TileOut rt = tile_out<F32OUT>(C, t.row0, t.row_end, N);
+        const int nbv = valid_b<G>(t, wm);
+        for (int b = 0; b < nbv; ++b) {
+            const float *src = part_ws + (size_t)tile * plan.sk * (kL * kL) +
+                               (size_t)wave * (G::FA * G::FB * 16 * 64) + (size_t)((a * G::FB + b) * 16) * 64 + lane;
+            float v[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            v[r] = src[(size_t)r * 64];
+            for (int r = 0; r < 16; ++r)
+                v[r] = src[(size_t)r * 64];
 #pragma unroll
-        for (int c = 1; c < 8; ++c) {
-            if (c < plan.sk) {
-                float w[16];
+            for (int c = 1; c < 8; ++c) {
+                if (c < plan.sk) {
+                    float w[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    w[r] = src[(size_t)c * (kL * kL) + (size_t)r * 64];
+                    for (int r = 0; r < 16; ++r)
+                        w[r] = src[(size_t)c * (kL * kL) + (size_t)r * 64];
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    v[r] += w[r];
+                    for (int r = 0; r < 16; ++r)
+                        v[r] += w[r];
+                }
             }
-        }
-        const int64_t row = t.row0 + wm * G::WTM + b * 32 + r32;
-        const bool row_ok = row < t.row_end;
+            const int64_t row = t.row0 + wm * G::WTM + b * 32 + r32;
+            const bool row_ok = row < t.row_end;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int n = t.n0 + wn * G::WTN + a * 32 + 8 * g + 4 * khalf;
-            store4<GELU, BIAS, F32OUT>(rt, bseg, row, row_ok, n, N, v[4 * g], v[4 * g + 1], v[4 * g + 2],
-                                       v[4 * g + 3]);
+            for (int g = 0; g < 4; ++g) {
+                const int n = t.n0 + wn * G::WTN + a * 32 + 8 * g + 4 * khalf;
+                store4<GELU, BIAS, F32OUT>(rt, bseg, row, row_ok, n, N, v[4 * g], v[4 * g + 1], v[4 * g + 2],
+                                           v[4 * g + 3]);
+            }
         }
     }
 }
@@ -1636,7 +1657,7 @@ size_t gemm_ws_bytes()
 {
     int64_t grid = (int64_t)device_cus();
     grid = (grid + kXcds - 1) / kXcds * kXcds;
-    return (size_t)grid * kL * kL * sizeof(float);
+    return (size_t)grid * kTailUnitsPerBlock * kL * kL * sizeof(float);
 }
 
 moe_status_t launch_grouped_gemm(const void *a, const int32_t *seg_offsets, int num_segments, int64_t max_rows,
