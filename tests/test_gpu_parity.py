@@ -407,6 +407,34 @@ def test_dispatch_ignores_out_of_range_ids():
     assert dp["slot_row"][3, 1].item() == -2 and dp["slot_row"][7, 0].item() == -2
 
 
+@pytest.mark.parametrize("T,d,E,k,cf", [
+    (4096, 4096, 8, 2, 0.0),     # single-launch dispatch, grid = CUs: eight-vector row prefetch
+    (5000, 4104, 8, 2, 0.0),     # more blocks than CUs: four-vector prefetch, rest of a ragged row after
+    (8192, 512, 64, 2, 0.0),     # four-vector prefetch longer than the row
+    (8192, 2048, 64, 2, 1.25),   # capped: no prefetch, two blocks per CU
+])
+def test_dispatch_single_launch_grids(T, d, E, k, cf):
+    """The single-launch dispatch in each of its grid regimes (prefetch of the
+    row before the planning or not, one or two blocks per CU) against the
+    oracle's capacity, permutation and x_perm, with Zipf-skewed selections."""
+    rng = np.random.default_rng(T + d)
+    logits = rng.standard_normal((T, E)) + 2.0 * np.log(1.0 / np.arange(1, E + 1))
+    idx = np.argsort(-logits, axis=1, kind="stable")[:, :k].astype(np.int32)
+    x = wl.f32_to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32))
+    xt = torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16)
+    dp = api.moe_dispatch(xt, torch.from_numpy(idx).to(DEV), E, cf)
+    torch.cuda.synchronize()
+    ref = oracle.capacity(idx, E, np.float32(cf))
+    np.testing.assert_array_equal(dp["seg_offsets"].cpu().numpy(), ref.seg_offsets)
+    np.testing.assert_array_equal(dp["kept_count"].cpu().numpy(), ref.kept_count)
+    np.testing.assert_array_equal(dp["slot_row"].cpu().numpy(), ref.slot_row)
+    rows = int(ref.seg_offsets[-1])
+    np.testing.assert_array_equal(dp["row_src"].cpu().numpy()[:rows], ref.row_src)
+    assert int(dp["n_dropped"].item()) == ref.n_dropped
+    got = dp["x_perm"][:rows].view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, expected_xperm(x, ref.row_src, k))
+
+
 def test_pages_dispatch_example_on_gpu():
     import json
     import os

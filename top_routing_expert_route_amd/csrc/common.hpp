@@ -173,6 +173,7 @@ constexpr size_t kCtrlBytes = 256;
 // softmax output, or NULL.
 size_t route_ws_bytes(int64_t T, int d, int E, moe_dtype_t dt);
 size_t gemm_ws_bytes();
+int device_cus(); // compute units of the current device (cached per thread and device)
 moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, const float *b_router,
                           const float *sel_bias, int64_t T, int d, int E, int k, float alpha, int32_t *topk_idx,
                           float *topk_w,

@@ -314,12 +314,16 @@ __device__ __forceinline__ uint64_t match_mask(int l, bool local, int nbits)
 // in the group: the same rank as the multi-kernel path), writes slot_row and
 // row_src, and then each wave copies its token's row of x to the token's kept
 // rows.  With PREFETCH (no cap and the whole layer local: every selection is
-// kept) the first piece of the row is loaded before the planning, so the
-// row read overlaps it.
+// kept) the first piece of the row (U 16-byte vectors per lane) is loaded
+// before the planning, so the row read overlaps it.  The kernel fits 64
+// registers, so that two blocks share a CU when the grid has more blocks than
+// CUs (a second round of blocks would double the time); the prefetch of
+// eight vectors does not, and runs only when the grid fits the CUs (four
+// otherwise).
 constexpr int kDispTB = 16;
 
 template <bool PREFETCH, int U>
-__global__ __launch_bounds__(64 * kDispTB) void dispatch_fused(
+__global__ __launch_bounds__(64 * kDispTB, (PREFETCH && U > 4) ? 1 : 8) void dispatch_fused(
     const int32_t *__restrict__ topk_idx, int64_t T, int k, int e0, int E_loc, int nbits, int64_t cap,
     const u32x4 *__restrict__ x, int64_t units, u32x4 *__restrict__ x_perm, int64_t max_rows,
     int32_t *__restrict__ seg_offsets, int32_t *__restrict__ kept_count, int32_t *__restrict__ n_dropped,
@@ -565,7 +569,11 @@ moe_status_t launch_dispatch(const void *x, moe_dtype_t dt, const int32_t *topk_
         // one launch: every block counts all selections itself
         const int64_t units = x ? (int64_t)d * (dt == MOE_BF16 ? 2 : 4) / 16 : 0;
         const bool prefetch = x_perm && cap < 0 && E_loc == E;
-        if (prefetch)
+        if (prefetch && fused_blocks > device_cus())
+            dispatch_fused<true, 4><<<(unsigned)fused_blocks, 64 * kDispTB, 0, stream>>>(
+                topk_idx, T, k, e0, E_loc, nbits, cap, (const u32x4 *)x, units, (u32x4 *)x_perm, max_rows,
+                seg_offsets, kept_count, n_dropped, slot_row, row_src);
+        else if (prefetch)
             dispatch_fused<true, 8><<<(unsigned)fused_blocks, 64 * kDispTB, 0, stream>>>(
                 topk_idx, T, k, e0, E_loc, nbits, cap, (const u32x4 *)x, units, (u32x4 *)x_perm, max_rows,
                 seg_offsets, kept_count, n_dropped, slot_row, row_src);

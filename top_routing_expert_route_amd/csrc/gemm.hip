@@ -1567,22 +1567,6 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(const float *__restrict_
     }
 }
 
-int device_cus()
-{
-    static thread_local int cached_dev = -1, cached_cus = 0;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess)
-        return 256;
-    if (dev != cached_dev) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            cus = 256;
-        cached_dev = dev;
-        cached_cus = cus;
-    }
-    return cached_cus;
-}
-
 // One block per CU (a multiple of the XCD count).  With a split-K workspace
 // a problem of few tiles still fills the chip (the tail plan cuts their K);
 // without one, blocks beyond the tile count would only idle.
@@ -1652,6 +1636,22 @@ moe_status_t run_bf16(const void *a, const int32_t *seg, int S, int64_t max_rows
 }
 
 } // namespace
+
+int device_cus()
+{
+    static thread_local int cached_dev = -1, cached_cus = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 256;
+    if (dev != cached_dev) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cached_dev = dev;
+        cached_cus = cus;
+    }
+    return cached_cus;
+}
 
 size_t gemm_ws_bytes()
 {
