@@ -541,8 +541,10 @@ def test_route_leaves_workspace_counters_zero():
 
 
 @pytest.mark.parametrize("T,d,E,k,sel", [
-    (8205, 256, 64, 2, "none"),    # two token tiles per block, last block 13 tokens
-    (8223, 520, 16, 4, "gauss"),   # two tiles, ragged K range per wave, selection bias
+    (6007, 256, 64, 2, "none"),    # two token tiles per block, last block 23 tokens
+    (4100, 520, 17, 3, "gauss"),   # two tiles, last block 4 tokens, ragged K range per wave, selection bias
+    (8205, 256, 64, 2, "none"),    # four tiles, last block 13 tokens
+    (8223, 520, 16, 4, "gauss"),   # four tiles, ragged K range per wave, selection bias
     (16421, 200, 33, 3, "none"),   # four tiles, three expert tiles, last block 37 tokens
     (16384, 128, 8, 2, "none"),    # four tiles, whole blocks
     (50000, 64, 64, 8, "gauss"),   # four tiles, 782 blocks: statistics in 28 groups of 28
@@ -550,7 +552,7 @@ def test_route_leaves_workspace_counters_zero():
 ])
 def test_route_multi_tile_blocks(T, d, E, k, sel):
     """The single-launch router's larger blocks (two or four 16-token tiles,
-    taken from 8192 and 16384 tokens on) and its two-level statistics (block
+    taken above 4096 and 8192 tokens on 256 CUs) and its two-level statistics (block
     groups, then the groups) against the oracle on every token, with ragged
     last blocks and groups; bitwise equal on a second call, and the
     workspace's arrival counters back at zero."""

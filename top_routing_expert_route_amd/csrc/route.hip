@@ -833,10 +833,17 @@ static int select_blocks(int64_t T) { return (int)((T + kSelTokensPerBlock - 1) 
 static bool route_is_fused(moe_dtype_t dt, int E) { return dt == MOE_BF16 && E <= 64; }
 
 // Token tiles of 16 per block of the single-launch router.  Every block reads
-// and splits the whole fp32 router weight, so a block scores as many tokens as
-// still leaves a block for each of the 256 compute units: 64 from 16384
-// tokens, 32 from 8192, else 16.
-static int route_tt(int64_t T) { return T >= 256 * 64 ? 4 : (T >= 256 * 32 ? 2 : 1); }
+// and splits the whole fp32 router weight, and one block fills a CU (its
+// registers), so a block scores the fewest tiles that keep the grid within one
+// block per CU (a second round of blocks would double the time): on 256 CUs,
+// 16 tokens up to 4096, 32 up to 8192, else 64.
+static int route_tt(int64_t T)
+{
+    const int64_t cus = device_cus();
+    if (T <= cus * kRouteTB)
+        return 1;
+    return T <= cus * 2 * kRouteTB ? 2 : 4;
+}
 
 // Blocks per group of the single-launch router's two-level statistics: about
 // sqrt(blocks), so that a group's collection and the final one are about as
