@@ -13,8 +13,9 @@
 //     (selections of that expert in earlier chunks) + (earlier in its chunk).
 //  dispatch_count    per-chunk histogram of local experts (LDS atomics: exact
 //                    integer counts, order-free).
-//  dispatch_scan     one block: per-expert exclusive scan over chunks (one
-//                    wave per expert, shuffle scans), capacity, kept counts,
+//  dispatch_scan     one block: per-expert exclusive scan over chunks (two
+//                    coalesced passes over the counts, segment sums scanned
+//                    in LDS), capacity, kept counts,
 //                    the exclusive scan of kept counts (segment offsets) and
 //                    the number of dropped selections.
 //  dispatch_rank     each wave walks its chunk 64 selections at a time; lanes
@@ -85,27 +86,69 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane)
 }
 
 // chunk_count [nchunks][E_loc] is turned in place into the per-chunk bases.
+// The [nchunks][E_loc] counts are read row by row (consecutive threads take
+// consecutive experts, so the accesses coalesce): thread (s, l) owns chunks
+// [s per, (s + 1) per) of expert l, the chunk range cut into S = 1024 / E_loc
+// segments.  Pass one sums the thread's chunks (eight loads in flight); the
+// segment sums are scanned per expert in LDS (a wave per expert); pass two
+// writes the exclusive prefixes over the thread's chunks.  Two rounds of
+// independent loads instead of one dependent round per 64 chunks.
 __global__ __launch_bounds__(1024) void dispatch_scan(int32_t *__restrict__ chunk_cb, int nchunks, int E_loc,
                                                       int64_t cap, int32_t *__restrict__ seg_offsets,
                                                       int32_t *__restrict__ kept_count,
                                                       int32_t *__restrict__ n_dropped)
 {
+    __shared__ int part[1024]; // [S][E_loc]: segment sums, then their exclusive prefixes
     __shared__ int tot[1024];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int l = wave; l < E_loc; l += 16) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int S = max(1, min(nchunks, 1024 / E_loc));
+    const int per = (nchunks + S - 1) / S;
+    const int l = tid % E_loc, s = tid / E_loc;
+    const bool act = s < S;
+    const int c_lo = s * per, c_hi = min(nchunks, c_lo + per);
+    if (act) {
+        int sum = 0;
+        for (int c0 = c_lo; c0 < c_hi; c0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                v[u] = c0 + u < c_hi ? chunk_cb[(int64_t)(c0 + u) * E_loc + l] : 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                sum += v[u];
+        }
+        part[s * E_loc + l] = sum;
+    }
+    __syncthreads();
+    for (int e = wave; e < E_loc; e += 16) {
         int carry = 0;
-        for (int c0 = 0; c0 < nchunks; c0 += 64) {
-            const int c = c0 + lane;
-            const int v = c < nchunks ? chunk_cb[(int64_t)c * E_loc + l] : 0;
+        for (int q0 = 0; q0 < S; q0 += 64) {
+            const int q = q0 + lane;
+            const int v = q < S ? part[q * E_loc + e] : 0;
             const int inc = wave_incl_scan(v, lane);
-            if (c < nchunks)
-                chunk_cb[(int64_t)c * E_loc + l] = carry + inc - v;
+            if (q < S)
+                part[q * E_loc + e] = carry + inc - v;
             carry += __shfl(inc, 63, 64);
         }
         if (lane == 0)
-            tot[l] = carry;
+            tot[e] = carry;
     }
     __syncthreads();
+    if (act) {
+        int carry = part[s * E_loc + l];
+        for (int c0 = c_lo; c0 < c_hi; c0 += 8) {
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                v[u] = c0 + u < c_hi ? chunk_cb[(int64_t)(c0 + u) * E_loc + l] : 0;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (c0 + u < c_hi)
+                    chunk_cb[(int64_t)(c0 + u) * E_loc + l] = carry;
+                carry += v[u];
+            }
+        }
+    }
     if (wave == 0) {
         int carry = 0, drop = 0;
         for (int l0 = 0; l0 < E_loc; l0 += 64) {
