@@ -25,11 +25,11 @@
 //                     dot product (the small fp32 workloads).
 //  route_select       one wave per token: softmax, top-k by (logit desc, id
 //                     asc), routing weights, and per-block partial sums of the
-//                     probabilities and selection counts.
-//  route_reduce_partials / route_finalize
-//                     fixed-order sums of the partials (chunks of rows, then
-//                     the chunk sums in one block) -> counts, f, P and L_aux
-//                     (bitwise reproducible).
+//                     probabilities and selection counts, summed in a fixed
+//                     order by the last blocks to finish (in groups of blocks,
+//                     then over the groups, as in route_fused) -> counts, f, P
+//                     and L_aux (bitwise reproducible).
+//  route_finalize     T = 0: zero counts and statistics.
 #include "common.hpp"
 
 #include <math.h>
@@ -248,19 +248,50 @@ template <class V> __device__ __forceinline__ V collect(const V *p)
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Fixed-order sums of partial rows [r0, r1) (E values each; any blockDim.x >=
-// E): G2 threads per expert take rows r0 + g, r0 + g + G2, ... (four at a time,
-// so that their coherent loads are in flight together) in double and int64,
-// then thread e adds its G2 sums in order into sp[e], sc[e].  Every thread
-// sees sp and sc after the call.
+// Fixed-order sums of partial rows [r0, r1) (E values each): G2 threads per
+// expert take rows r0 + g, r0 + g + G2, ... (four at a time, so that their
+// coherent loads are in flight together) in double and int64, then thread e
+// adds its G2 sums in order into sp[e], sc[e] (rp, rc: G2 x E <= blockDim.x
+// entries).  With more than half as many experts as threads, each thread
+// sums whole rows for experts tid, tid + blockDim.x, ... (the same order as
+// G2 = 1).  Every thread sees sp and sc after the call.
 template <class TP, class TC>
-__device__ void sum_rows(const TP *pp, const TC *pc, int64_t r0, int64_t r1, int E, double *rp, long long *rc,
+__device__ __forceinline__ void sum_rows(const TP *pp, const TC *pc, int64_t r0, int64_t r1, int E, double *rp, long long *rc,
                          double *sp, long long *sc)
 {
     const int nt = blockDim.x, tid = threadIdx.x;
     int G2 = 1;
     while (G2 * 2 * E <= nt)
         G2 *= 2;
+    if (G2 == 1) {
+        for (int q = tid; q < E; q += nt) {
+            double ps = 0.0;
+            long long cs = 0;
+            int64_t b = r0;
+            for (; b + 3 < r1; b += 4) {
+                TP pv[4];
+                TC cv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    pv[u] = collect(pp + (b + u) * E + q);
+                    cv[u] = collect(pc + (b + u) * E + q);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    ps += (double)pv[u];
+                    cs += (long long)cv[u];
+                }
+            }
+            for (; b < r1; ++b) {
+                ps += (double)collect(pp + b * E + q);
+                cs += (long long)collect(pc + b * E + q);
+            }
+            sp[q] = ps;
+            sc[q] = cs;
+        }
+        __syncthreads();
+        return;
+    }
     const int e = tid / G2, g = tid % G2;
     double ps = 0.0;
     long long cs = 0;
@@ -330,7 +361,7 @@ __device__ __forceinline__ bool arrived_last(unsigned *counter, unsigned n, int 
 // reads gsz or ngroups rows instead of one block reading every row.  With one
 // group the last block sums the rows directly.  Every counter is back at zero
 // when the launch completes.
-__device__ void finish_stats(const float *part_p, const int32_t *part_c, int gsz, double *grp_p, long long *grp_c,
+__device__ __forceinline__ void finish_stats(const float *part_p, const int32_t *part_c, int gsz, double *grp_p, long long *grp_c,
                              unsigned *counters, int64_t T, int E, float alpha, int32_t *expert_count, float *f,
                              float *P, float *l_aux, double *rp, long long *rc, double *sp, long long *sc,
                              double *terms, int *s_flag)
@@ -619,10 +650,17 @@ __global__ __launch_bounds__(256) void route_select(const float *__restrict__ lo
                                                     int64_t T, int E, int k,
                                                     int32_t *__restrict__ topk_idx, float *__restrict__ topk_w,
                                                     float *__restrict__ part_p, int32_t *__restrict__ part_c,
-                                                    float *__restrict__ probs)
+                                                    float *__restrict__ probs, int gsz, double *__restrict__ grp_p,
+                                                    long long *__restrict__ grp_c, unsigned *__restrict__ counters,
+                                                    float alpha, int32_t *__restrict__ expert_count,
+                                                    float *__restrict__ f, float *__restrict__ P,
+                                                    float *__restrict__ l_aux)
 {
     __shared__ float sp[4][EPL * 64];
     __shared__ int sc[4][EPL * 64];
+    __shared__ double rp[256], tp[EPL * 64], terms[EPL * 64]; // statistics: E <= 64 EPL
+    __shared__ long long rc[256], tc[EPL * 64];
+    __shared__ int s_flag;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
     float pacc[EPL];
@@ -732,37 +770,16 @@ __global__ __launch_bounds__(256) void route_select(const float *__restrict__ lo
         p += sp[1][e];
         p += sp[2][e];
         p += sp[3][e];
-        part_p[(int64_t)blockIdx.x * E + e] = p;
-        part_c[(int64_t)blockIdx.x * E + e] = sc[0][e] + sc[1][e] + sc[2][e] + sc[3][e];
+        publish(part_p + (int64_t)blockIdx.x * E + e, p);
+        publish(part_c + (int64_t)blockIdx.x * E + e, sc[0][e] + sc[1][e] + sc[2][e] + sc[3][e]);
     }
+    finish_stats(part_p, part_c, gsz, grp_p, grp_c, counters, T, E, alpha, expert_count, f, P, l_aux, rp, rc, tp, tc,
+                 terms, &s_flag);
 }
 
-// First level of the partial-sum reduction: chunk c (one block) sums rows
-// [c R, (c+1) R) of the per-block partials, in row order, for every expert.
-constexpr int kFinRows = 32;
-
-__global__ __launch_bounds__(256) void route_reduce_partials(const float *__restrict__ part_p,
-                                                             const int32_t *__restrict__ part_c, int nblk, int E,
-                                                             double *__restrict__ fin_p, long long *__restrict__ fin_c)
-{
-    const int c = blockIdx.x;
-    const int r0 = c * kFinRows, r1 = min(nblk, r0 + kFinRows);
-    for (int e = threadIdx.x; e < E; e += 256) {
-        double ps = 0.0;
-        long long cs = 0;
-        for (int r = r0; r < r1; ++r) {
-            ps += (double)part_p[(int64_t)r * E + e];
-            cs += part_c[(int64_t)r * E + e];
-        }
-        fin_p[(int64_t)c * E + e] = ps;
-        fin_c[(int64_t)c * E + e] = cs;
-    }
-}
-
-// One block of 1024 threads; G threads per expert sum the chunk sums in a
-// fixed strided order, then the G partial sums are added in order.  DIRECT:
-// the rows are the per-block partials themselves (few blocks: one launch
-// instead of two).
+// One block of 1024 threads; G threads per expert sum the rows in a fixed
+// strided order, then the G partial sums are added in order.  Used for T = 0
+// (no rows: zero counts and statistics).
 __host__ __device__ constexpr int finalize_threads_per_expert(int E)
 {
     int G = 1;
@@ -771,7 +788,7 @@ __host__ __device__ constexpr int finalize_threads_per_expert(int E)
     return G;
 }
 
-template <bool DIRECT, class TP, class TC>
+template <class TP, class TC>
 __global__ __launch_bounds__(1024) void route_finalize(const TP *__restrict__ fin_p, const TC *__restrict__ fin_c,
                                                        int nrows, int64_t T, int E, float alpha,
                                                        int32_t *__restrict__ expert_count, float *__restrict__ f,
@@ -821,8 +838,6 @@ __global__ __launch_bounds__(1024) void route_finalize(const TP *__restrict__ fi
 }
 
 } // namespace
-
-static int fin_chunks(int nblk) { return (nblk + kFinRows - 1) / kFinRows; }
 
 static int select_blocks(int64_t T) { return (int)((T + kSelTokensPerBlock - 1) / kSelTokensPerBlock); }
 
@@ -890,8 +905,9 @@ size_t route_ws_bytes(int64_t T, int d, int E, moe_dtype_t dt)
     // logits, partials, chunk sums, plus the split router weight and the
     // grouped GEMM's tail partials when the logits run on it
     const bool on_gemm = router_on_gemm(dt, d, E);
+    const int gsz = route_group_size(nblk, E);
     size_t b = align_up((size_t)T * E * (on_gemm ? 3 : 1) * sizeof(float)) + parts +
-               2 * align_up((size_t)fin_chunks(nblk) * E * 8);
+               2 * align_up((size_t)((nblk + gsz - 1) / gsz) * E * 8);
     if (on_gemm)
         b += align_up((size_t)E * 3 * d * sizeof(uint16_t)) + align_up(gemm_ws_bytes());
     return b;
@@ -949,7 +965,7 @@ moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, 
 {
     if (T == 0) {
         // no tokens: zero counts and statistics
-        route_finalize<true><<<1, 1024, 0, stream>>>((const float *)nullptr, (const int *)nullptr, 0, T, E, alpha,
+        route_finalize<float, int><<<1, 1024, 0, stream>>>((const float *)nullptr, (const int *)nullptr, 0, T, E, alpha,
                                                      expert_count, f, P, l_aux);
         return check_launch("route_finalize");
     }
@@ -985,8 +1001,9 @@ moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, 
     float *logits = cv.take<float>((size_t)T * E * pieces);
     float *part_p = cv.take<float>((size_t)nblk * E);
     int32_t *part_c = cv.take<int32_t>((size_t)nblk * E);
-    double *fin_p = cv.take<double>((size_t)fin_chunks(nblk) * E);
-    long long *fin_c = cv.take<long long>((size_t)fin_chunks(nblk) * E);
+    const int gsz = route_group_size(nblk, E);
+    double *grp_p = cv.take<double>((size_t)((nblk + gsz - 1) / gsz) * E);
+    long long *grp_c = cv.take<long long>((size_t)((nblk + gsz - 1) / gsz) * E);
     uint16_t *w3 = on_gemm ? cv.take<uint16_t>((size_t)E * 3 * d) : nullptr;
     void *gws = on_gemm ? cv.take<char>(gemm_ws_bytes()) : nullptr;
 
@@ -1009,29 +1026,19 @@ moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, 
         return s;
     const int epl = (E + 63) / 64;
     const dim3 g((unsigned)nblk);
+#define SEL_STATS gsz, grp_p, grp_c, ticket, alpha, expert_count, f, P, l_aux
     switch (epl) {
-    case 1: route_select<1><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs); break;
-    case 2: route_select<2><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs); break;
+    case 1: route_select<1><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs, SEL_STATS); break;
+    case 2: route_select<2><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs, SEL_STATS); break;
     case 3:
-    case 4: route_select<4><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs); break;
+    case 4: route_select<4><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs, SEL_STATS); break;
     case 5: case 6: case 7: case 8:
-        route_select<8><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs); break;
+        route_select<8><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs, SEL_STATS); break;
     default:
-        route_select<16><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs); break;
+        route_select<16><<<g, 256, 0, stream>>>(logits, pieces, b_router, sel_bias, T, E, k, topk_idx, topk_w, part_p, part_c, probs, SEL_STATS); break;
     }
-    if (moe_status_t s = check_launch("route_select"))
-        return s;
-    if (nblk <= 32 * finalize_threads_per_expert(E)) {
-        // at most 32 partial rows per thread: sum them directly
-        route_finalize<true><<<1, 1024, 0, stream>>>(part_p, part_c, nblk, T, E, alpha, expert_count, f, P, l_aux);
-        return check_launch("route_finalize");
-    }
-    const int nfin = fin_chunks(nblk);
-    route_reduce_partials<<<(unsigned)nfin, 256, 0, stream>>>(part_p, part_c, nblk, E, fin_p, fin_c);
-    if (moe_status_t s = check_launch("route_reduce_partials"))
-        return s;
-    route_finalize<false><<<1, 1024, 0, stream>>>(fin_p, fin_c, nfin, T, E, alpha, expert_count, f, P, l_aux);
-    return check_launch("route_finalize");
+#undef SEL_STATS
+    return check_launch("route_select");
 }
 
 } // namespace moe
