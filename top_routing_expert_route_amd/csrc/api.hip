@@ -228,7 +228,8 @@ int64_t moe_max_rows(int64_t T, int E, int k, float capacity_factor, int num_loc
 }
 
 // Route workspaces: the arrival counters in the control bytes, then the
-// partial rows (and, off the single-launch path, logits and chunk sums).
+// statistics' partial and group rows (and, off the single-launch path, the
+// logits).
 static size_t route_ws_total(int64_t T, int d, int E, moe_dtype_t dt)
 {
     return T > 0 ? kCtrlBytes + route_ws_bytes(T, d, E, dt) : 0;

@@ -897,17 +897,16 @@ size_t route_ws_bytes(int64_t T, int d, int E, moe_dtype_t dt)
     if (T <= 0)
         return 0;
     const int nblk = route_blocks(T, E, dt);
-    const size_t parts = 2 * align_up((size_t)nblk * E * sizeof(float));
-    if (route_is_fused(dt, E)) {
-        const int gsz = route_group_size(nblk, E);
-        return parts + 2 * align_up((size_t)((nblk + gsz - 1) / gsz) * E * 8);
-    }
-    // logits, partials, chunk sums, plus the split router weight and the
-    // grouped GEMM's tail partials when the logits run on it
-    const bool on_gemm = router_on_gemm(dt, d, E);
+    // per-block partial rows and per-group rows of the statistics
     const int gsz = route_group_size(nblk, E);
-    size_t b = align_up((size_t)T * E * (on_gemm ? 3 : 1) * sizeof(float)) + parts +
-               2 * align_up((size_t)((nblk + gsz - 1) / gsz) * E * 8);
+    const size_t stats = 2 * align_up((size_t)nblk * E * sizeof(float)) +
+                         2 * align_up((size_t)((nblk + gsz - 1) / gsz) * E * 8);
+    if (route_is_fused(dt, E))
+        return stats;
+    // plus the logits, and the split router weight and the grouped GEMM's
+    // tail partials when the logits run on it
+    const bool on_gemm = router_on_gemm(dt, d, E);
+    size_t b = align_up((size_t)T * E * (on_gemm ? 3 : 1) * sizeof(float)) + stats;
     if (on_gemm)
         b += align_up((size_t)E * 3 * d * sizeof(uint16_t)) + align_up(gemm_ws_bytes());
     return b;
@@ -965,8 +964,8 @@ moe_status_t launch_route(const void *x, moe_dtype_t dt, const float *w_router, 
 {
     if (T == 0) {
         // no tokens: zero counts and statistics
-        route_finalize<float, int><<<1, 1024, 0, stream>>>((const float *)nullptr, (const int *)nullptr, 0, T, E, alpha,
-                                                     expert_count, f, P, l_aux);
+        route_finalize<float, int><<<1, 1024, 0, stream>>>((const float *)nullptr, (const int *)nullptr, 0, T, E,
+                                                           alpha, expert_count, f, P, l_aux);
         return check_launch("route_finalize");
     }
     const int nblk = route_blocks(T, E, dt);
