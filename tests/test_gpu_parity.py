@@ -590,6 +590,9 @@ def test_route_sel_bias_full_size():
     changed = (plain["topk_idx"] != r["topk_idx"]).any(dim=1).float().mean().item()
     assert changed > 0.1, changed  # the bias moved a real share of the selections
     assert torch.equal(plain["P"], r["P"])  # P is the unbiased mean probability
+    # 2048 select blocks: statistics in 45 groups; the arrival counters are back at zero
+    ws = api.workspace(x.device, 0)
+    assert int(ws[:256].count_nonzero().item()) == 0
     print("sel_bias: near ties boundary %d order %d; %.1f%% of tokens re-routed" %
           (nt["boundary"], nt["order"], 100 * changed))
 
