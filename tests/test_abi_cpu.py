@@ -185,3 +185,32 @@ def test_backward_workspace_and_rejections(lib):
     p = api.Problem(1 << 20, 128, 8, 2, 128, 0.0, 0, 0, 0, 0.01, api.MOE_BF16)
     assert call(p, full) == api.MOE_ERR_UNSUPPORTED
     assert b"columns" in lib.moe_last_error()
+
+
+def test_binding_checks_caller_outputs():
+    """The binding's `out=` form checks the caller's tensors before any call
+    reaches the library (which trusts the sizes it is given)."""
+    import torch
+    from top_routing_expert_route_amd import api
+    x = torch.zeros((16, 8), dtype=torch.bfloat16)
+    wr = torch.zeros((4, 8), dtype=torch.float32)
+    good = dict(topk_idx=torch.empty((16, 2), dtype=torch.int32), topk_w=torch.empty((16, 2)),
+                expert_count=torch.empty(4, dtype=torch.int32), f=torch.empty(4), P=torch.empty(4),
+                l_aux=torch.empty(1))
+    for name, bad in (("topk_idx", torch.empty((16, 3), dtype=torch.int32)),
+                      ("topk_w", torch.empty((16, 2), dtype=torch.float64)),
+                      ("P", torch.empty(8)[::2])):
+        out = dict(good, **{name: bad})
+        with pytest.raises(ValueError, match=name):
+            api.moe_route(x, wr, None, 2, out=out)
+    idx = torch.zeros((16, 2), dtype=torch.int32)
+    mr = api.max_rows(16, 4, 2)
+    dgood = dict(seg_offsets=torch.empty(5, dtype=torch.int32), kept_count=torch.empty(4, dtype=torch.int32),
+                 slot_row=torch.empty((16, 2), dtype=torch.int32), row_src=torch.empty(mr, dtype=torch.int32),
+                 n_dropped=torch.empty(1, dtype=torch.int32), x_perm=torch.empty((mr, 8), dtype=torch.bfloat16))
+    for name, bad in (("row_src", torch.empty(mr - 1, dtype=torch.int32)),
+                      ("x_perm", torch.empty((mr, 8), dtype=torch.float32)),
+                      ("seg_offsets", None)):
+        out = dict(dgood, **{name: bad})
+        with pytest.raises(ValueError, match=name):
+            api.moe_dispatch(x, idx, 4, out=out)

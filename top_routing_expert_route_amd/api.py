@@ -166,6 +166,16 @@ def workspace(device, nbytes: int) -> torch.Tensor:
     return buf
 
 
+def _check_out(out: dict, spec: dict, dev) -> None:
+    """Caller-supplied outputs: each named tensor must have the shape, dtype
+    and device the call writes (the library trusts the sizes it is given)."""
+    for name, (shape, dtype) in spec.items():
+        t = out.get(name)
+        if t is None or tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != dev \
+                or not t.is_contiguous():
+            raise ValueError("out[%r]: need a contiguous %s tensor of shape %s on %s" % (name, dtype, shape, dev))
+
+
 def max_rows(T: int, E: int, k: int, capacity_factor: float = 0.0, num_local_experts: int = 0) -> int:
     return int(lib().moe_max_rows(T, E, k, capacity_factor, num_local_experts))
 
@@ -173,16 +183,23 @@ def max_rows(T: int, E: int, k: int, capacity_factor: float = 0.0, num_local_exp
 # ----------------------------------------------------------------- steps --
 
 def moe_route(x: torch.Tensor, w_router: torch.Tensor, b_router: Optional[torch.Tensor], k: int,
-              alpha: float = 0.01, sel_bias: Optional[torch.Tensor] = None) -> dict:
+              alpha: float = 0.01, sel_bias: Optional[torch.Tensor] = None, out: Optional[dict] = None) -> dict:
+    """moe_route; `out` (the dict an earlier call returned, same sizes)
+    receives the results instead of new tensors."""
     T, d = x.shape
     E = w_router.shape[0]
     dev = x.device
-    out = dict(topk_idx=torch.empty((T, k), dtype=torch.int32, device=dev),
-               topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
-               expert_count=torch.empty(E, dtype=torch.int32, device=dev),
-               f=torch.empty(E, dtype=torch.float32, device=dev),
-               P=torch.empty(E, dtype=torch.float32, device=dev),
-               l_aux=torch.empty(1, dtype=torch.float32, device=dev))
+    if out is None:
+        out = dict(topk_idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+                   topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
+                   expert_count=torch.empty(E, dtype=torch.int32, device=dev),
+                   f=torch.empty(E, dtype=torch.float32, device=dev),
+                   P=torch.empty(E, dtype=torch.float32, device=dev),
+                   l_aux=torch.empty(1, dtype=torch.float32, device=dev))
+    else:
+        _check_out(out, dict(topk_idx=((T, k), torch.int32), topk_w=((T, k), torch.float32),
+                             expert_count=((E,), torch.int32), f=((E,), torch.float32), P=((E,), torch.float32),
+                             l_aux=((1,), torch.float32)), dev)
     nb = lib().moe_route_workspace_size(T, d, E)
     ws = workspace(dev, nb)
     check(lib().moe_route(_p(x), _dt(x), _p(w_router), _p(b_router), _p(sel_bias), T, d, E, k, alpha,
@@ -194,22 +211,35 @@ def moe_route(x: torch.Tensor, w_router: torch.Tensor, b_router: Optional[torch.
 def moe_dispatch(x: Optional[torch.Tensor], topk_idx: torch.Tensor, E: int, capacity_factor: float = 0.0,
                  expert_begin: int = 0, num_local_experts: int = 0, with_x_perm: bool = True,
                  rows: Optional[int] = None, dtype: Optional[torch.dtype] = None, d: Optional[int] = None,
-                 noalloc: bool = False) -> dict:
+                 noalloc: bool = False, out: Optional[dict] = None) -> dict:
     """moe_dispatch with a torch workspace; with noalloc, moe_dispatch_noalloc
-    (the library's static scratch, no workspace)."""
+    (the library's static scratch, no workspace).  New outputs have row_src
+    filled with -1 past the kept rows (the library writes rows [0, rows));
+    `out` (the dict an earlier call returned, same sizes) receives the
+    results instead, its rows past the kept ones left as they were."""
     T, k = topk_idx.shape
     dev = topk_idx.device
     E_loc = num_local_experts if num_local_experts > 0 else E
     mr = max_rows(T, E, k, capacity_factor, num_local_experts) if rows is None else rows
     d = x.shape[1] if x is not None else d
     dt = _dt(x) if x is not None else (MOE_BF16 if dtype == torch.bfloat16 else MOE_F32)
-    out = dict(seg_offsets=torch.empty(E_loc + 1, dtype=torch.int32, device=dev),
-               kept_count=torch.empty(E_loc, dtype=torch.int32, device=dev),
-               slot_row=torch.empty((T, k), dtype=torch.int32, device=dev),
-               row_src=torch.full((max(1, mr),), -1, dtype=torch.int32, device=dev),
-               n_dropped=torch.empty(1, dtype=torch.int32, device=dev),
-               x_perm=(torch.empty((max(1, mr), d), dtype=x.dtype, device=dev) if (with_x_perm and x is not None)
-                       else None))
+    if out is None:
+        out = dict(seg_offsets=torch.empty(E_loc + 1, dtype=torch.int32, device=dev),
+                   kept_count=torch.empty(E_loc, dtype=torch.int32, device=dev),
+                   slot_row=torch.empty((T, k), dtype=torch.int32, device=dev),
+                   row_src=torch.full((max(1, mr),), -1, dtype=torch.int32, device=dev),
+                   n_dropped=torch.empty(1, dtype=torch.int32, device=dev),
+                   x_perm=(torch.empty((max(1, mr), d), dtype=x.dtype, device=dev)
+                           if (with_x_perm and x is not None) else None))
+    else:
+        spec = dict(seg_offsets=((E_loc + 1,), torch.int32), kept_count=((E_loc,), torch.int32),
+                    slot_row=((T, k), torch.int32), row_src=((max(1, mr),), torch.int32),
+                    n_dropped=((1,), torch.int32))
+        if out.get("x_perm") is not None:
+            if x is None:
+                raise ValueError("out['x_perm'] needs x")
+            spec["x_perm"] = ((max(1, mr), d), x.dtype)
+        _check_out(out, spec, dev)
     if noalloc:
         check(lib().moe_dispatch_noalloc(_p(x), dt, _p(topk_idx), T, d, E, k, capacity_factor, expert_begin,
                                          num_local_experts, _p(out["seg_offsets"]), _p(out["kept_count"]),
