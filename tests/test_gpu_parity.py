@@ -524,6 +524,33 @@ def test_route_bitwise_reproducible_and_stats_fixed_order():
         assert torch.equal(r1[k], r2[k]), k
 
 
+@pytest.mark.parametrize("name", ["drop-small", "fine-small"])
+def test_route_and_dispatch_into_caller_outputs(name):
+    """The binding's out= form (outputs allocated once and reused, as the
+    bench's stage timing calls them) gives the bits of fresh outputs, call
+    after call, also after another layer's results were written into them."""
+    w = SMALL[name]
+    inp, t = _inputs(w)
+    r0 = api.moe_route(t["x"], t["w_router"], t["b_router"], w.k, w.alpha, sel_bias=t["sel_bias"])
+    d0 = api.moe_dispatch(t["x"], r0["topk_idx"], w.E, w.capacity_factor, w.expert_begin, w.num_local_experts)
+    r_out = {k: torch.full_like(v, 7) for k, v in r0.items()}
+    d_out = {k: (torch.full_like(v, 7) if torch.is_tensor(v) else v) for k, v in d0.items()}
+    _, t2 = _inputs(w, seed=3)
+    for xs in (t2["x"], t["x"], t["x"]):
+        r = api.moe_route(xs, t["w_router"], t["b_router"], w.k, w.alpha, sel_bias=t["sel_bias"], out=r_out)
+        d = api.moe_dispatch(xs, r["topk_idx"], w.E, w.capacity_factor, w.expert_begin, w.num_local_experts,
+                             out=d_out)
+    torch.cuda.synchronize()
+    assert r is r_out and d is d_out
+    for k in r0:
+        assert torch.equal(r[k], r0[k]), k
+    rows = int(d0["seg_offsets"][-1])
+    for k in ("seg_offsets", "kept_count", "slot_row", "n_dropped"):
+        assert torch.equal(d[k], d0[k]), k
+    assert torch.equal(d["row_src"][:rows], d0["row_src"][:rows])
+    assert torch.equal(d["x_perm"][:rows].view(torch.int16), d0["x_perm"][:rows].view(torch.int16))
+
+
 def test_route_leaves_workspace_counters_zero():
     """The single-launch router's arrival counter (the workspace's first 256
     bytes) is zero again after every call, whatever the grid size, so the
