@@ -844,7 +844,7 @@ static int select_blocks(int64_t T) { return (int)((T + kSelTokensPerBlock - 1) 
 // Tokens per block of the fused small-E path.
 // Path of the router: the single-launch kernel for bf16 activations with at
 // most 64 experts, otherwise logits (split-weight grouped GEMM, MFMA or fp32
-// kernel) + route_select + the partial-sum reduction.
+// kernel) + route_select (which also sums the statistics).
 static bool route_is_fused(moe_dtype_t dt, int E) { return dt == MOE_BF16 && E <= 64; }
 
 // Token tiles of 16 per block of the single-launch router.  Every block reads
